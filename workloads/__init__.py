@@ -1,0 +1,207 @@
+"""Seeded synthetic inputs for one decode step of grouped-query attention.
+
+This module only draws random numbers and lays them out; it holds none of the
+method's arithmetic (no rotation, no attention, no rounding rules of its own:
+casting to bfloat16 is torch's round-to-nearest-even). Both the CPU oracle's
+tests and the GPU path's tests/benchmark take their inputs from here, and from
+nowhere else, so that the two sides see byte-identical data.
+
+Workloads (the shapes of the pages' examples, synthetic values N(0, 1)):
+
+* ``tiny_mha``   batch 1, 4 query / 4 KV heads, head dim 16, 5 cached tokens
+                 (+1 appended), fp32, RoPE base 10000.
+* ``gqa_8b``     batch 16, 32 query / 8 KV heads (G = 4), head dim 128, 8192
+                 cached tokens per sequence, bf16, contiguous cache.  The layer
+                 shape of an 8B model with 8 KV groups for 32 heads.
+* ``mqa_ragged`` batch 64, 32 query heads sharing 1 KV head, head dim 128,
+                 cached lengths uniform in [512, 4096], bf16.
+* ``long_gqa``   batch 1, 64 query / 8 KV heads (G = 8), head dim 128, 131072
+                 cached tokens, bf16.
+* ``paged_gqa``  batch 32, 32 / 8 heads, head dim 128, block size 16, cached
+                 lengths uniform in [1024, 16384]; the blocks of all sequences
+                 sit in one shared pool in a seeded random order.
+
+Draw order (one ``torch.Generator`` seeded with the workload's seed):
+cached lengths -> block permutation (paged only) -> K cache -> V cache -> q ->
+k_new -> v_new.  Values are drawn as float32 N(0, 1) and cast to the storage
+dtype.  Every cache slot at or past a sequence's cached length (including the
+slot the append will fill) holds NaN, so a read of an unwritten slot shows up.
+
+The RoPE cos/sin table is an input of the append (the pages do not give the
+rotation frequencies): row p, column i holds cos/sin(p * base^(-2i/d)),
+evaluated in float64 and rounded once to float32.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+import torch
+
+__all__ = ["Workload", "WORKLOADS", "DecodeInputs", "draw", "rotation_table"]
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    seed: int
+    B: int
+    H_q: int
+    H_kv: int
+    d: int
+    dtype: str                 # "f32" or "bf16": storage dtype of q, K, V, out
+    cached_lo: int             # cached tokens per sequence before the step,
+    cached_hi: int             # uniform integers in [lo, hi] (equal => fixed)
+    layout: str = "contiguous"  # or "paged"
+    T_max: int = 0             # contiguous capacity (tokens per (b, kv head))
+    block_size: int = 16       # paged only
+    rope_base: float = 10000.0
+
+    @property
+    def G(self) -> int:
+        return self.H_q // self.H_kv
+
+    @property
+    def paged(self) -> bool:
+        return self.layout == "paged"
+
+    @property
+    def max_attended(self) -> int:
+        return self.cached_hi + 1
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return -(-self.max_attended // self.block_size)
+
+    @property
+    def table_rows(self) -> int:
+        """Positions the rotation table covers (every slot a sequence can use)."""
+        if self.paged:
+            return self.max_blocks_per_seq * self.block_size
+        return self.T_max
+
+    def replace(self, **kw) -> "Workload":
+        """Same structure at another size (for oracle-sized parity cases)."""
+        w = dataclasses.replace(self, **kw)
+        if not w.paged and w.T_max < w.cached_hi + 1:
+            w = dataclasses.replace(w, T_max=_round_up(w.cached_hi + 1, 8))
+        return w
+
+
+def _round_up(x: int, m: int) -> int:
+    return -(-x // m) * m
+
+
+WORKLOADS = {
+    "tiny_mha": Workload("tiny_mha", 0, B=1, H_q=4, H_kv=4, d=16, dtype="f32",
+                         cached_lo=5, cached_hi=5, T_max=8),
+    "gqa_8b": Workload("gqa_8b", 1, B=16, H_q=32, H_kv=8, d=128, dtype="bf16",
+                       cached_lo=8192, cached_hi=8192, T_max=8200),
+    "mqa_ragged": Workload("mqa_ragged", 2, B=64, H_q=32, H_kv=1, d=128, dtype="bf16",
+                           cached_lo=512, cached_hi=4096, T_max=4104),
+    "long_gqa": Workload("long_gqa", 3, B=1, H_q=64, H_kv=8, d=128, dtype="bf16",
+                         cached_lo=131072, cached_hi=131072, T_max=131080),
+    "paged_gqa": Workload("paged_gqa", 4, B=32, H_q=32, H_kv=8, d=128, dtype="bf16",
+                          cached_lo=1024, cached_hi=16384, layout="paged", block_size=16),
+}
+
+
+@dataclasses.dataclass
+class DecodeInputs:
+    """One decode step's inputs, on the CPU, in storage dtype.
+
+    cached      int32 [B]   tokens in the cache before the step (= append slot)
+    k_cache     [B, H_kv, T_max, d]   contiguous layout, or
+                [N_blocks, H_kv, block_size, d]   paged pool
+    v_cache     same shape as k_cache
+    block_table int32 [B, max_blocks_per_seq] (paged; -1 = unused) or None
+    q           [B, H_q, d]   raw (not yet rotated) query of the new token
+    k_new, v_new [B, H_kv, d] raw key and value of the new token
+    rope_cos, rope_sin  float32 [table_rows, d // 2]
+    """
+    workload: Workload
+    cached: torch.Tensor
+    k_cache: torch.Tensor
+    v_cache: torch.Tensor
+    block_table: Optional[torch.Tensor]
+    q: torch.Tensor
+    k_new: torch.Tensor
+    v_new: torch.Tensor
+    rope_cos: torch.Tensor
+    rope_sin: torch.Tensor
+
+    @property
+    def seq_lens(self) -> torch.Tensor:
+        """Attended length after the append (cached + 1)."""
+        return self.cached + 1
+
+
+def _storage(x: torch.Tensor, dtype: str) -> torch.Tensor:
+    if dtype == "f32":
+        return x.contiguous()
+    if dtype == "bf16":
+        return x.to(torch.bfloat16).contiguous()
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def rotation_table(rows: int, d: int, base: float = 10000.0):
+    """cos/sin of p * base^(-2i/d) for p < rows, i < d/2; float64 -> float32 once."""
+    i = np.arange(d // 2, dtype=np.float64)
+    inv_freq = base ** (-2.0 * i / d)
+    ang = np.arange(rows, dtype=np.float64)[:, None] * inv_freq[None, :]
+    return (torch.from_numpy(np.cos(ang).astype(np.float32)),
+            torch.from_numpy(np.sin(ang).astype(np.float32)))
+
+
+def draw(w: Workload) -> DecodeInputs:
+    """Draw the workload's inputs from its seed (deterministic, CPU only)."""
+    g = torch.Generator().manual_seed(w.seed)
+    if w.cached_lo == w.cached_hi:
+        cached = torch.full((w.B,), w.cached_lo, dtype=torch.int32)
+    else:
+        cached = torch.randint(w.cached_lo, w.cached_hi + 1, (w.B,), generator=g,
+                               dtype=torch.int64).to(torch.int32)
+    lens = (cached + 1).tolist()
+
+    block_table = None
+    if w.paged:
+        bs = w.block_size
+        nblk = [-(-L // bs) for L in lens]
+        total = sum(nblk)
+        perm = torch.randperm(total, generator=g).to(torch.int32)
+        block_table = torch.full((w.B, w.max_blocks_per_seq), -1, dtype=torch.int32)
+        off = 0
+        for b, n in enumerate(nblk):
+            block_table[b, :n] = perm[off:off + n]
+            off += n
+        shape = (total, w.H_kv, bs, w.d)
+    else:
+        assert w.T_max >= w.cached_hi + 1, "contiguous capacity must hold cached + 1"
+        shape = (w.B, w.H_kv, w.T_max, w.d)
+
+    k_cache = torch.randn(shape, generator=g, dtype=torch.float32)
+    v_cache = torch.randn(shape, generator=g, dtype=torch.float32)
+    q = torch.randn((w.B, w.H_q, w.d), generator=g, dtype=torch.float32)
+    k_new = torch.randn((w.B, w.H_kv, w.d), generator=g, dtype=torch.float32)
+    v_new = torch.randn((w.B, w.H_kv, w.d), generator=g, dtype=torch.float32)
+
+    k_cache = _storage(k_cache, w.dtype)
+    v_cache = _storage(v_cache, w.dtype)
+    nan = float("nan")
+    for b, c in enumerate(cached.tolist()):
+        if w.paged:
+            bs = w.block_size
+            for p in range(c, -(-lens[b] // bs) * bs):
+                blk = int(block_table[b, p // bs])
+                k_cache[blk, :, p % bs, :] = nan
+                v_cache[blk, :, p % bs, :] = nan
+        else:
+            k_cache[b, :, c:, :] = nan
+            v_cache[b, :, c:, :] = nan
+
+    cos, sin = rotation_table(w.table_rows, w.d, w.rope_base)
+    return DecodeInputs(w, cached, k_cache, v_cache, block_table,
+                        _storage(q, w.dtype), _storage(k_new, w.dtype),
+                        _storage(v_new, w.dtype), cos, sin)
