@@ -1,0 +1,215 @@
+#!/usr/bin/env python3
+"""Benchmark: one decode step (append + grouped-query attention) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gqa_8b]
+
+A step is the whole hot path over one batch: kvc_append (rotate and store the
+new key, store the value, rotate q) followed by kvc_decode_attn (all splits and
+their merge, one kernel).  Inputs are resident in HBM before timing starts.
+To keep the 256 MB Infinity Cache from serving the cache between steps, R
+replicas of the KV cache (R * bytes >= 2 GB) are used in turn.
+
+Prints one JSON line: `value` is the algorithmic KV bytes one step must read
+(sum_b L_b * H_kv * d * 2 * 2 bytes) divided by the measured step time.
+`roofline` rates the decode kernel alone (per-launch time from HIP events
+recorded around each decode launch on its stream) against 8 TB/s.
+`cpu_baseline` is the CPU oracle timed on the host on the same inputs.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
+MALL_DEFEAT_BYTES = 2 << 30
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_gqa_8b_traffic.json")
+DECODE_SRC = os.path.join(ROOT, "mqa_decode_attention_amd", "csrc", "kvc_decode.hip")
+
+
+def kv_read_bytes(seq_lens, H_kv, d, elem_bytes):
+    """Bytes of K and V a decode step must read: sum_b L_b * H_kv * d * 2 * e."""
+    return int(sum(int(L) for L in seq_lens)) * H_kv * d * 2 * elem_bytes
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="gqa_8b")
+    ap.add_argument("--split-tokens", type=int, default=0, help="0 = library heuristic")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-seqs", type=int, default=0,
+                    help="sequences the CPU oracle is timed on (0 = all)")
+    return ap.parse_args()
+
+
+def traffic_for_current_kernel():
+    """HBM bytes per decode launch from committed rocprofv3 counter runs, if they
+    were taken on the current decode kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        src = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
+        if t.get("kernel_source_sha256") == src:
+            return t.get("hbm_bytes_per_launch")
+    except (OSError, ValueError):
+        pass
+    return None
+
+
+def cpu_baseline(x, n_seqs):
+    """Time the CPU oracle (as it stands, one thread) on the same step's inputs."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+    from dataclasses import replace
+
+    w = x.workload
+    B = w.B if n_seqs <= 0 else min(n_seqs, w.B)
+    dt = w.dtype
+
+    def np_store(t):
+        t = t.contiguous()
+        return t.view(__import__("torch").int16).numpy().view(np.uint16) if dt == "bf16" else t.numpy()
+
+    if w.paged:
+        raise NotImplementedError("CPU baseline is timed on contiguous workloads")
+    kc, vc = np_store(x.k_cache[:B]), np_store(x.v_cache[:B])
+    q, kn, vn = np_store(x.q[:B]), np_store(x.k_new[:B]), np_store(x.v_new[:B])
+    cos, sin = x.rope_cos.numpy(), x.rope_sin.numpy()
+    cached = x.cached.numpy()[:B]
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        k2, v2, q2 = O.append_contiguous(kc, vc, cached, kn, vn, cos, sin, dt, q=q)
+        O.decode_attention(q2, k2, v2, cached + 1, dt)
+        sec = time.perf_counter() - t0
+    nbytes = kv_read_bytes(cached + 1, w.H_kv, w.d, 2 if dt == "bf16" else 4)
+    return {"value": round(nbytes / sec / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{B} of {w.B} sequences of {w.name} (append + attention, float64, numpy, one thread), "
+                      f"{sec:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the decode path shards by sequence and KV head with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mqa_decode_attention_amd as kvc
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    kvc.load()   # fails loudly if libkvc.so is missing
+
+    w = W.WORKLOADS[args.workload]
+    x = W.draw(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    e = 2 if w.dtype == "bf16" else 4
+    kv_bytes = kv_read_bytes(x.seq_lens.tolist(), w.H_kv, w.d, e)
+    cache_bytes = x.k_cache.numel() * e * 2
+    R = max(1, -(-MALL_DEFEAT_BYTES // cache_bytes))
+
+    ks = [x.k_cache.to(dev) for _ in range(R)]
+    vs = [x.v_cache.to(dev) for _ in range(R)]
+    q = x.q.to(dev)
+    kn, vn = x.k_new.to(dev), x.v_new.to(dev)
+    pos, lens = x.cached.to(dev), x.seq_lens.to(dev)
+    cos, sin = x.rope_cos.to(dev), x.rope_sin.to(dev)
+    tbl = x.block_table.to(dev) if w.paged else None
+    max_len = int(x.seq_lens.max())
+    out = torch.empty_like(q)
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        r = i % R
+        kvc.append(ks[r], vs[r], pos, kn, vn, cos, sin, q=q, block_table=tbl)
+        if ev is not None:
+            ev[0].record()
+        if w.paged:
+            kvc.decode_attn_paged(q, ks[r], vs[r], tbl, lens, max_len, out=out, split_tokens=args.split_tokens)
+        else:
+            kvc.decode_attn(q, ks[r], vs[r], lens, max_len, out=out, split_tokens=args.split_tokens)
+        if ev is not None:
+            ev[1].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # whole-step timing: K steps between two events, nothing else in between
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(args.steps):
+        step(i)
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = t_start.elapsed_time(t_end) / args.steps
+
+    # per-launch duration of the decode kernel: events around each decode launch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    dec_ms = [a.elapsed_time(b) for a, b in evs]
+    dec_avg_ms = sum(dec_ms) / len(dec_ms)
+    dec_med_ms = sorted(dec_ms)[len(dec_ms) // 2]
+
+    achieved = kv_bytes / (dec_avg_ms * 1e-3) / 1e9
+    value = kv_bytes / (step_ms * 1e-3) / 1e9
+    traffic = traffic_for_current_kernel()
+
+    res = {
+        "metric": "GQA decode-attn KV read GB/s (% of MI355X HBM peak); us per decode step",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1), NaN past each sequence's length)",
+        "config": {"workload": w.name, "batch": w.B, "H_q": w.H_q, "H_kv": w.H_kv, "head_dim": w.d,
+                   "cached_tokens": [w.cached_lo, w.cached_hi], "layout": w.layout,
+                   "kv_bytes_per_step": kv_bytes, "cache_replicas": R,
+                   "split_tokens": args.split_tokens or "auto"},
+        "us_per_step": round(step_ms * 1e3, 2),
+        "decode_us": round(dec_avg_ms * 1e3, 2),
+        "decode_us_median": round(dec_med_ms * 1e3, 2),
+        "hbm_pct_step": round(100 * value / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "decode_split_kernel (split + fused log-sum-exp merge)",
+                     "bytes_per_launch": kv_bytes},
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu_baseline and not w.paged:
+        res["cpu_baseline"] = cpu_baseline(x, args.cpu_sample_seqs)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,167 @@
+/*
+ * kvc.h - C ABI of libkvc: one autoregressive decode step of grouped-query
+ * attention over a KV cache, on an AMD Instinct MI355X (gfx950).
+ *
+ * A decode step is two calls on one stream:
+ *   1. kvc_append: rotate the new token's key (RoPE) and store it, with the
+ *      token's value, as one slice along the token axis of the cache; the same
+ *      call can rotate the token's query in place.
+ *   2. kvc_decode_attn / kvc_decode_attn_paged: every query head h attends over
+ *      the cached keys/values of its group g(h) = floor(h / G), G = H_q / H_kv:
+ *      O_h = softmax(q_h K_g(h)^T * scale) V_g(h).
+ *
+ * Definitions followed (page titles as published):
+ *  - "Grouped-query attention: berbagi KV head di antara grup query" (nalar.dev),
+ *    section "Jumlah head menentukan batas grup": G, g(h), A_h and O_h; section
+ *    "GQA berada di antara MHA dan MQA": H_kv = H_q is MHA, H_kv = 1 is MQA.
+ *  - "KV Cache" explainer (lensaml.com), step 3: the cache is a pair of
+ *    [batch, kv_heads, tokens, head_dim] tensors per layer, each decode step
+ *    writes one slice along the token axis, and keys are rotated by position
+ *    once and stored rotated.
+ *  - "Arsitektur Inferensi LLM: PagedAttention, KV-Cache & Speculative
+ *    Decoding" (tveniu.com), section 4: the cache split into fixed blocks of
+ *    tokens placed anywhere in memory and found through a per-sequence table.
+ *  - "KV Cache 최적화 심층 분석: GQA·MLA·MHA 어텐션 메커니즘과 메모리 효율화 전략"
+ *    (youngju.dev), PagedKVCache listing: pool [n_blocks, n_heads, block_size,
+ *    head_dim], logical block pos / block_size, offset pos % block_size.
+ *
+ * Conventions for every entry point:
+ *  - All tensors are dense, row-major, in DEVICE memory, owned by the caller.
+ *    The library allocates nothing and keeps no per-call state.
+ *  - dtype: KVC_BF16 (bfloat16 q/K/V/out, float32 accumulation) or KVC_F32.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null stream)
+ *    and never synchronise.  Sizes are checked on the host before anything is
+ *    launched: a non-OK status means nothing was enqueued, and kvc_last_error()
+ *    (thread-local) says why.  Values that live in device memory (positions,
+ *    lengths, block ids) cannot be checked on the host; the kernels clamp them
+ *    so that every access stays inside the buffers described by the sizes
+ *    passed in, but the results for out-of-contract values are unspecified.
+ *  - Output buffers must not alias inputs.  Concurrent calls are safe when
+ *    they do not share output or workspace buffers.
+ */
+#ifndef KVC_H_
+#define KVC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVC_ABI_VERSION 1
+
+typedef enum kvc_status {
+    KVC_OK = 0,
+    KVC_ERR_NULL = 1,        /* a required pointer is NULL                       */
+    KVC_ERR_SHAPE = 2,       /* inconsistent sizes (H_q % H_kv, capacity, ...)   */
+    KVC_ERR_UNSUPPORTED = 3, /* valid request this build does not implement      */
+    KVC_ERR_WORKSPACE = 4,   /* workspace missing, too small or misaligned       */
+    KVC_ERR_HIP = 5          /* a HIP runtime call failed                        */
+} kvc_status;
+
+typedef enum kvc_dtype { KVC_F32 = 0, KVC_BF16 = 1 } kvc_dtype;
+
+/* How RoPE pairs the head dimension: (2i, 2i+1), or (i, i + d/2). */
+typedef enum kvc_rope_style { KVC_ROPE_INTERLEAVED = 0, KVC_ROPE_HALF = 1 } kvc_rope_style;
+
+/* KVC_ABI_VERSION of the loaded library. */
+int kvc_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char* kvc_status_string(int status);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char* kvc_last_error(void);
+
+/*
+ * kvc_append - write the new token of every sequence into the cache.
+ *
+ * For sequence b, p = positions[b] is the slot (the number of tokens cached
+ * before this step).  For every KV head j and pair i of the head dimension,
+ * with x0, x1 the pair of k_new[b, j, :] (style picks the pair), c =
+ * rope_cos[p, i], s = rope_sin[p, i], the stored key is
+ *     r0 = (x0*c) - (x1*s),   r1 = (x0*s) + (x1*c)
+ * evaluated in float32 one rounded operation at a time (no fused multiply-add)
+ * and rounded to nearest-even into the storage dtype.  v_new[b, j, :] is copied
+ * bit for bit.  If q_inout is not NULL, q_inout[b, h, :] is rotated in place in
+ * the same way at the same position.  No other cache element changes.
+ *
+ * Cache layout:
+ *   block_table == NULL: contiguous k_cache/v_cache [B, H_kv, T_max, d];
+ *                        the slot is [b, j, p, :].  Requires p < T_max.
+ *   block_table != NULL: pools k_cache/v_cache [num_blocks, H_kv, block_size, d]
+ *                        and int32 block_table [B, max_blocks_per_seq]; the slot
+ *                        is [block_table[b][p / block_size], j, p % block_size, :].
+ *                        Requires p < max_blocks_per_seq * block_size and that
+ *                        table entry in [0, num_blocks).  T_max is ignored.
+ * Positions outside [0, min(capacity, rope_rows)), or a block id outside
+ * [0, num_blocks), make the kernel skip that sequence's writes.
+ *
+ * Arguments: positions int32 [B]; k_new, v_new [B, H_kv, d]; q_inout [B, H_q, d]
+ * or NULL; rope_cos, rope_sin float32 [rope_rows, d/2] (row p holds the
+ * cos/sin of the pair angles at position p).  d must be even.
+ */
+kvc_status kvc_append(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
+                      void* k_cache, void* v_cache, int T_max,
+                      const int32_t* block_table, int block_size, int max_blocks_per_seq,
+                      int num_blocks, const int32_t* positions,
+                      const void* k_new, const void* v_new, void* q_inout,
+                      const float* rope_cos, const float* rope_sin, int rope_rows,
+                      int rope_style, void* stream);
+
+/*
+ * Bytes of workspace kvc_decode_attn / kvc_decode_attn_paged need for these
+ * sizes and this split_tokens (0 = the library's choice).  May be 0.
+ * Returns (size_t)-1 for invalid sizes.
+ *
+ * The workspace holds per-split partial results (running max, sum, weighted
+ * values) and one arrival counter per (sequence, KV head).  It must be
+ * zero-filled before its first use; every completed call leaves it zeroed
+ * again, so one buffer serves any number of later calls (not concurrent ones).
+ */
+size_t kvc_decode_workspace_bytes(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
+                                  int max_seq_len, int split_tokens);
+
+/*
+ * kvc_decode_attn - attention of the new token over a contiguous cache.
+ *
+ * out[b, h, :] = sum_t w_t V[b, g(h), t, :] over t < L_b = seq_lens[b], with
+ * w = softmax_t(scale * <q[b, h, :], K[b, g(h), t, :]>), g(h) = h / (H_q / H_kv).
+ * q is the (already rotated) query [B, H_q, d]; k_cache, v_cache [B, H_kv,
+ * T_max, d]; seq_lens int32 [B] with 0 <= L_b <= max_seq_len <= T_max (L_b = 0
+ * gives zeros); scale <= 0 means 1/sqrt(d); out [B, H_q, d] in dtype.
+ * Slots at or past L_b are never read.
+ *
+ * The token axis is cut into splits of split_tokens tokens (0 = library
+ * heuristic); each split is one workgroup per (sequence, KV head) and the
+ * splits are merged exactly by their log-sum-exp.  The result does not depend
+ * on the split count beyond float32 rounding.
+ */
+kvc_status kvc_decode_attn(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
+                           const void* q, const void* k_cache, const void* v_cache, int T_max,
+                           const int32_t* seq_lens, int max_seq_len, float scale, void* out,
+                           int split_tokens, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
+ * kvc_decode_attn_paged - the same attention over a paged cache.
+ *
+ * k_pool, v_pool [num_blocks, H_kv, block_size, d]; block_table int32
+ * [B, max_blocks_per_seq]: token t of sequence b lives in block
+ * block_table[b][t / block_size] at offset t % block_size.  Entries past
+ * ceil(L_b / block_size) are never read.  Requires max_seq_len <=
+ * max_blocks_per_seq * block_size.  Blocks may be shared between sequences.
+ */
+kvc_status kvc_decode_attn_paged(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
+                                 const void* q, const void* k_pool, const void* v_pool,
+                                 int num_blocks, int block_size, const int32_t* block_table,
+                                 int max_blocks_per_seq, const int32_t* seq_lens,
+                                 int max_seq_len, float scale, void* out, int split_tokens,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H_ */

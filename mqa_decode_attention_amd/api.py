@@ -1,0 +1,180 @@
+"""Python binding of libkvc: argument marshalling only.
+
+Each function checks the torch tensors it is given (device, dtype, layout,
+shape), passes their device pointers and the current HIP stream to the C ABI,
+and raises KvcError on a non-OK status.  All computation happens in the HIP
+kernels; nothing here touches tensor values.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Optional, Tuple
+
+import torch
+
+from . import _lib
+
+KVC_F32, KVC_BF16 = 0, 1
+ROPE_STYLES = {"interleaved": 0, "half": 1}
+
+
+class KvcError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"kvc status {status}: {message}")
+        self.status = status
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return KVC_BF16
+    if t.dtype == torch.float32:
+        return KVC_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+def _stream(device: torch.device, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        lib = _lib.load()
+        raise KvcError(status, lib.kvc_last_error().decode() or lib.kvc_status_string(status).decode())
+
+
+def append(k_cache: torch.Tensor, v_cache: torch.Tensor, positions: torch.Tensor,
+           k_new: torch.Tensor, v_new: torch.Tensor, rope_cos: torch.Tensor,
+           rope_sin: torch.Tensor, q: Optional[torch.Tensor] = None,
+           block_table: Optional[torch.Tensor] = None, rope_style: str = "interleaved",
+           stream=None) -> None:
+    """kvc_append: rotate and store the new token's key, store its value, rotate q in place.
+
+    Contiguous caches are [B, H_kv, T_max, d]; with a block_table [B, max_blocks]
+    (int32) they are pools [num_blocks, H_kv, block_size, d].
+    """
+    lib = _lib.load()
+    dt = _dtype_code(k_new)
+    B, H_kv, d = k_new.shape
+    H_q = q.shape[1] if q is not None else H_kv
+    if rope_cos.dim() != 2 or rope_cos.shape[1] != d // 2:
+        raise ValueError(f"rope_cos must be [rows, {d // 2}], got {tuple(rope_cos.shape)}")
+    if block_table is not None:
+        num_blocks, _, block_size, _ = k_cache.shape
+        T_max = 0
+        mb = block_table.shape[1]
+        tbl = _dev(block_table, "block_table", torch.int32, (B, mb))
+        shape = (num_blocks, H_kv, block_size, d)
+    else:
+        T_max = k_cache.shape[2]
+        tbl, block_size, mb, num_blocks = None, 0, 0, 0
+        shape = (B, H_kv, T_max, d)
+    _check(lib.kvc_append(
+        dt, B, H_q, H_kv, d,
+        _dev(k_cache, "k_cache", k_new.dtype, shape), _dev(v_cache, "v_cache", k_new.dtype, shape), T_max,
+        tbl, block_size, mb, num_blocks,
+        _dev(positions, "positions", torch.int32, (B,)),
+        _dev(k_new, "k_new", k_new.dtype), _dev(v_new, "v_new", k_new.dtype, (B, H_kv, d)),
+        _dev(q, "q", k_new.dtype, (B, H_q, d)) if q is not None else None,
+        _dev(rope_cos, "rope_cos", torch.float32), _dev(rope_sin, "rope_sin", torch.float32, rope_cos.shape),
+        rope_cos.shape[0], ROPE_STYLES[rope_style], _stream(k_new.device, stream)))
+
+
+def workspace_bytes(dtype: torch.dtype, B: int, H_q: int, H_kv: int, d: int, max_seq_len: int,
+                    split_tokens: int = 0) -> int:
+    lib = _lib.load()
+    code = KVC_BF16 if dtype == torch.bfloat16 else KVC_F32
+    n = lib.kvc_decode_workspace_bytes(code, B, H_q, H_kv, d, max_seq_len, split_tokens)
+    if n == (1 << 64) - 1:
+        raise KvcError(2, lib.kvc_last_error().decode() or "invalid sizes for the decode workspace")
+    return n
+
+
+# Zero-filled workspaces kept per (device, stream): the library leaves them
+# zeroed after every completed call, so one buffer serves all later calls
+# issued on the same stream.
+_WORKSPACES: Dict[Tuple[int, int], torch.Tensor] = {}
+
+
+def _workspace(device: torch.device, stream_handle: int, nbytes: int) -> Tuple[Optional[int], int]:
+    if nbytes == 0:
+        return None, 0
+    key = (device.index if device.index is not None else torch.cuda.current_device(), stream_handle)
+    ws = _WORKSPACES.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _WORKSPACES[key] = ws
+    return ws.data_ptr(), ws.numel()
+
+
+def _decode_args(q, out):
+    dt = _dtype_code(q)
+    B, H_q, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    return dt, B, H_q, d, out
+
+
+def decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                seq_lens: torch.Tensor, max_seq_len: int, out: Optional[torch.Tensor] = None,
+                scale: Optional[float] = None, split_tokens: int = 0,
+                workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """kvc_decode_attn over a contiguous cache [B, H_kv, T_max, d]; returns out [B, H_q, d]."""
+    lib = _lib.load()
+    dt, B, H_q, d, out = _decode_args(q, out)
+    _, H_kv, T_max, _ = k_cache.shape
+    st = _stream(q.device, stream)
+    need = workspace_bytes(q.dtype, B, H_q, H_kv, d, max_seq_len, split_tokens)
+    if workspace is not None:
+        ws, wsn = _dev(workspace, "workspace", torch.uint8), workspace.numel()
+    else:
+        ws, wsn = _workspace(q.device, st, need)
+    _check(lib.kvc_decode_attn(
+        dt, B, H_q, H_kv, d, _dev(q, "q", q.dtype),
+        _dev(k_cache, "k_cache", q.dtype, (B, H_kv, T_max, d)),
+        _dev(v_cache, "v_cache", q.dtype, (B, H_kv, T_max, d)), T_max,
+        _dev(seq_lens, "seq_lens", torch.int32, (B,)), int(max_seq_len),
+        float(scale) if scale else 0.0, _dev(out, "out", q.dtype, (B, H_q, d)),
+        int(split_tokens), ws, wsn, st))
+    return out
+
+
+def decode_attn_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                      block_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                      out: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                      split_tokens: int = 0, workspace: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+    """kvc_decode_attn_paged over pools [num_blocks, H_kv, block_size, d]."""
+    lib = _lib.load()
+    dt, B, H_q, d, out = _decode_args(q, out)
+    num_blocks, H_kv, block_size, _ = k_pool.shape
+    st = _stream(q.device, stream)
+    need = workspace_bytes(q.dtype, B, H_q, H_kv, d, max_seq_len, split_tokens)
+    if workspace is not None:
+        ws, wsn = _dev(workspace, "workspace", torch.uint8), workspace.numel()
+    else:
+        ws, wsn = _workspace(q.device, st, need)
+    _check(lib.kvc_decode_attn_paged(
+        dt, B, H_q, H_kv, d, _dev(q, "q", q.dtype),
+        _dev(k_pool, "k_pool", q.dtype, (num_blocks, H_kv, block_size, d)),
+        _dev(v_pool, "v_pool", q.dtype, (num_blocks, H_kv, block_size, d)),
+        num_blocks, block_size, _dev(block_table, "block_table", torch.int32, (B, block_table.shape[1])),
+        block_table.shape[1], _dev(seq_lens, "seq_lens", torch.int32, (B,)), int(max_seq_len),
+        float(scale) if scale else 0.0, _dev(out, "out", q.dtype, (B, H_q, d)),
+        int(split_tokens), ws, wsn, st))
+    return out

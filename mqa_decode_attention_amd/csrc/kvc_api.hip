@@ -1,0 +1,266 @@
+// kvc_api.hip - the C ABI of libkvc (declared in include/kvc.h): argument
+// checks, launch planning and error reporting around the kernels.
+//
+// Every check here runs on the host before any HIP call, so a bad call returns
+// its status without touching the device.
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "kvc_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+kvc_status fail(kvc_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
+kvc_status fail(kvc_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+kvc_status ok() {
+    g_last_error[0] = '\0';
+    return KVC_OK;
+}
+
+kvc_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(KVC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t elem_bytes(kvc_dtype dt) { return dt == KVC_BF16 ? 2 : 4; }
+
+bool dtype_ok(kvc_dtype dt) { return dt == KVC_BF16 || dt == KVC_F32; }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Heads of one group served by one workgroup: the largest of 8, 4, 2, 1 that
+// divides G (larger groups are served in several chunks).
+int heads_per_wg(int G) {
+    for (int c : {8, 4, 2, 1})
+        if (G % c == 0) return c;
+    return 1;
+}
+
+// Workgroups the split heuristic aims for: four per compute unit of an MI355X.
+constexpr int kTargetWorkgroups = 4 * 256;
+
+// Common checks of the head/group sizes.
+kvc_status check_heads(kvc_dtype dt, int B, int H_q, int H_kv, int d) {
+    if (!dtype_ok(dt)) return fail(KVC_ERR_UNSUPPORTED, "unknown dtype %d", static_cast<int>(dt));
+    if (B < 0 || H_q <= 0 || H_kv <= 0 || d <= 0)
+        return fail(KVC_ERR_SHAPE, "sizes must be positive (B=%d H_q=%d H_kv=%d d=%d)", B, H_q, H_kv, d);
+    if (H_q % H_kv != 0)
+        return fail(KVC_ERR_SHAPE, "H_q=%d is not a multiple of H_kv=%d", H_q, H_kv);
+    return KVC_OK;
+}
+
+}  // namespace
+
+namespace kvc {
+
+bool plan_decode(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_len,
+                 int split_tokens, DecodePlan* plan, const char** why) {
+    DecodePlan pl{};
+    const int G = H_q / H_kv;
+    pl.heads_per_wg = heads_per_wg(G);
+    pl.n_chunks = G / pl.heads_per_wg;
+    if (!decode_supported(dtype, d, pl.heads_per_wg)) {
+        *why = "no decode kernel for this dtype and head_dim (head_dim must be 16, 32, 64, 128 or 256)";
+        return false;
+    }
+    const long long units = static_cast<long long>(B) * H_kv * pl.n_chunks;
+    const int tile = decode_tile_tokens(dtype, d);
+    const int L = std::max(max_seq_len, 1);
+    int ts;
+    if (split_tokens > 0) {
+        ts = split_tokens;
+        if ((L + ts - 1) / ts > kMaxSplits) {
+            *why = "split_tokens gives more splits than the merge step supports";
+            return false;
+        }
+    } else {
+        long long want = units > 0 ? (kTargetWorkgroups + units - 1) / units : 1;
+        want = std::max(1LL, std::min<long long>(want, kMaxSplits));
+        ts = static_cast<int>((L + want - 1) / want);
+        ts = (ts + tile - 1) / tile * tile;
+        while ((L + ts - 1) / ts > kMaxSplits) ts += tile;
+    }
+    pl.split_tokens = ts;
+    pl.n_splits = (L + ts - 1) / ts;
+    if (pl.n_splits > 1) {
+        const size_t bh = static_cast<size_t>(B) * H_q;
+        pl.ws_part = 0;
+        pl.ws_ml = align_up(bh * pl.n_splits * d * sizeof(float), 256);
+        pl.ws_count = align_up(pl.ws_ml + bh * pl.n_splits * sizeof(float2), 256);
+        pl.ws_bytes = align_up(pl.ws_count + static_cast<size_t>(units) * sizeof(int), 256);
+    }
+    *plan = pl;
+    return true;
+}
+
+}  // namespace kvc
+
+extern "C" {
+
+int kvc_abi_version(void) { return KVC_ABI_VERSION; }
+
+const char* kvc_status_string(int status) {
+    switch (status) {
+        case KVC_OK: return "ok";
+        case KVC_ERR_NULL: return "null pointer";
+        case KVC_ERR_SHAPE: return "inconsistent sizes";
+        case KVC_ERR_UNSUPPORTED: return "unsupported configuration";
+        case KVC_ERR_WORKSPACE: return "workspace missing or too small";
+        case KVC_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* kvc_last_error(void) { return g_last_error; }
+
+kvc_status kvc_append(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
+                      void* k_cache, void* v_cache, int T_max,
+                      const int32_t* block_table, int block_size, int max_blocks_per_seq,
+                      int num_blocks, const int32_t* positions,
+                      const void* k_new, const void* v_new, void* q_inout,
+                      const float* rope_cos, const float* rope_sin, int rope_rows,
+                      int rope_style, void* stream) {
+    kvc_status st = check_heads(dtype, B, H_q, H_kv, d);
+    if (st != KVC_OK) return st;
+    if (d % 2 != 0) return fail(KVC_ERR_SHAPE, "head_dim %d must be even for the rotation", d);
+    if (rope_style != KVC_ROPE_INTERLEAVED && rope_style != KVC_ROPE_HALF)
+        return fail(KVC_ERR_UNSUPPORTED, "unknown rope_style %d", rope_style);
+    if (rope_rows <= 0) return fail(KVC_ERR_SHAPE, "rope_rows must be positive");
+    if (B == 0) return ok();
+    if (!k_cache || !v_cache || !positions || !k_new || !v_new || !rope_cos || !rope_sin)
+        return fail(KVC_ERR_NULL, "kvc_append: a required pointer is NULL");
+    kvc::AppendParams p{};
+    p.dtype = dtype;
+    p.B = B; p.H_q = H_q; p.H_kv = H_kv; p.d = d;
+    p.k_cache = k_cache; p.v_cache = v_cache; p.T_max = T_max;
+    p.block_table = block_table;
+    p.block_size = block_size; p.max_blocks_per_seq = max_blocks_per_seq; p.num_blocks = num_blocks;
+    if (block_table) {
+        if (block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0)
+            return fail(KVC_ERR_SHAPE, "paged append needs positive block_size, max_blocks_per_seq, num_blocks");
+        const long long cap = static_cast<long long>(block_size) * max_blocks_per_seq;
+        if (cap > 0x7FFFFFFF) return fail(KVC_ERR_SHAPE, "paged capacity exceeds 2^31 tokens");
+        p.capacity = static_cast<int>(cap);
+    } else {
+        if (T_max <= 0) return fail(KVC_ERR_SHAPE, "T_max must be positive");
+        p.capacity = T_max;
+    }
+    p.positions = positions;
+    p.k_new = k_new; p.v_new = v_new; p.q_inout = q_inout;
+    p.rope_cos = rope_cos; p.rope_sin = rope_sin; p.rope_rows = rope_rows;
+    p.rope_style = rope_style;
+    return hip_status(kvc::launch_append(p, static_cast<hipStream_t>(stream)), "kvc_append launch");
+}
+
+size_t kvc_decode_workspace_bytes(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
+                                  int max_seq_len, int split_tokens) {
+    if (check_heads(dtype, B, H_q, H_kv, d) != KVC_OK || max_seq_len < 0 || split_tokens < 0)
+        return static_cast<size_t>(-1);
+    kvc::DecodePlan pl;
+    const char* why = nullptr;
+    if (!kvc::plan_decode(dtype, B, H_q, H_kv, d, max_seq_len, split_tokens, &pl, &why))
+        return static_cast<size_t>(-1);
+    return pl.ws_bytes;
+}
+
+}  // extern "C"
+
+namespace {
+
+kvc_status decode_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const void* q,
+                         const void* k, const void* v, int T_max, int num_blocks, int block_size,
+                         const int32_t* block_table, int max_blocks_per_seq,
+                         const int32_t* seq_lens, int max_seq_len, float scale, void* out,
+                         int split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+    kvc_status st = check_heads(dtype, B, H_q, H_kv, d);
+    if (st != KVC_OK) return st;
+    const bool paged = block_table != nullptr;
+    if (max_seq_len < 0) return fail(KVC_ERR_SHAPE, "max_seq_len must be >= 0");
+    if (split_tokens < 0) return fail(KVC_ERR_SHAPE, "split_tokens must be >= 0");
+    if (paged) {
+        if (block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0)
+            return fail(KVC_ERR_SHAPE, "paged decode needs positive block_size, max_blocks_per_seq, num_blocks");
+        if (static_cast<long long>(max_seq_len) > static_cast<long long>(block_size) * max_blocks_per_seq)
+            return fail(KVC_ERR_SHAPE, "max_seq_len %d exceeds the block table's %lld tokens", max_seq_len,
+                        static_cast<long long>(block_size) * max_blocks_per_seq);
+    } else if (max_seq_len > T_max) {
+        return fail(KVC_ERR_SHAPE, "max_seq_len %d exceeds the cache capacity T_max %d", max_seq_len, T_max);
+    }
+    if (B == 0) return ok();
+    if (!q || !k || !v || !seq_lens || !out)
+        return fail(KVC_ERR_NULL, "decode: a required pointer is NULL");
+    kvc::DecodePlan pl;
+    const char* why = nullptr;
+    if (!kvc::plan_decode(dtype, B, H_q, H_kv, d, max_seq_len, split_tokens, &pl, &why))
+        return fail(KVC_ERR_UNSUPPORTED, "%s", why);
+    if (pl.ws_bytes > 0) {
+        if (!workspace) return fail(KVC_ERR_WORKSPACE, "decode needs %zu bytes of workspace, got NULL", pl.ws_bytes);
+        if (workspace_bytes < pl.ws_bytes)
+            return fail(KVC_ERR_WORKSPACE, "decode needs %zu bytes of workspace, got %zu", pl.ws_bytes, workspace_bytes);
+        if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+            return fail(KVC_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    }
+    const long long n_wg = static_cast<long long>(B) * H_kv * pl.n_chunks * pl.n_splits;
+    if (n_wg > 0x7FFFFFF0LL) return fail(KVC_ERR_SHAPE, "too many workgroups");
+
+    kvc::DecodeParams p{};
+    p.q = q; p.k = k; p.v = v; p.out = out;
+    p.seq_lens = seq_lens;
+    p.block_table = block_table;
+    char* ws = static_cast<char*>(workspace);
+    p.ws_part = pl.ws_bytes ? reinterpret_cast<float*>(ws + pl.ws_part) : nullptr;
+    p.ws_ml = pl.ws_bytes ? reinterpret_cast<float2*>(ws + pl.ws_ml) : nullptr;
+    p.ws_count = pl.ws_bytes ? reinterpret_cast<int*>(ws + pl.ws_count) : nullptr;
+    p.B = B; p.H_q = H_q; p.H_kv = H_kv; p.G = H_q / H_kv; p.n_chunks = pl.n_chunks;
+    p.T_max = T_max; p.block_size = block_size; p.max_blocks_per_seq = max_blocks_per_seq;
+    p.num_blocks = num_blocks;
+    p.max_seq_len = max_seq_len; p.split_tokens = pl.split_tokens; p.n_splits = pl.n_splits;
+    p.n_wg = static_cast<int>(n_wg);
+    p.n_wg_pad = static_cast<int>((n_wg + 7) / 8 * 8);
+    const float sc = scale > 0.0f ? scale : 1.0f / sqrtf(static_cast<float>(d));
+    p.scale_log2 = sc * 1.4426950408889634f;
+    return hip_status(kvc::launch_decode(dtype, d, pl.heads_per_wg, paged, p, static_cast<hipStream_t>(stream)),
+                      "decode launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+kvc_status kvc_decode_attn(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
+                           const void* q, const void* k_cache, const void* v_cache, int T_max,
+                           const int32_t* seq_lens, int max_seq_len, float scale, void* out,
+                           int split_tokens, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+    return decode_common(dtype, B, H_q, H_kv, d, q, k_cache, v_cache, T_max, 0, 0, nullptr, 0, seq_lens,
+                         max_seq_len, scale, out, split_tokens, workspace, workspace_bytes, stream);
+}
+
+kvc_status kvc_decode_attn_paged(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
+                                 const void* q, const void* k_pool, const void* v_pool,
+                                 int num_blocks, int block_size, const int32_t* block_table,
+                                 int max_blocks_per_seq, const int32_t* seq_lens,
+                                 int max_seq_len, float scale, void* out, int split_tokens,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+    if (!block_table) return fail(KVC_ERR_NULL, "kvc_decode_attn_paged: block_table is NULL");
+    return decode_common(dtype, B, H_q, H_kv, d, q, k_pool, v_pool, 0, num_blocks, block_size, block_table,
+                         max_blocks_per_seq, seq_lens, max_seq_len, scale, out, split_tokens, workspace,
+                         workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,123 @@
+// kvc_append.hip - store the new token's rotated key and its value as one
+// slice along the token axis of the cache, and rotate its query in place.
+//
+// The cache layout and the "rotate once, store rotated" rule follow the "KV
+// Cache" explainer (lensaml.com), step 3; the paged slot (block table entry
+// pos / block_size, offset pos % block_size) follows the PagedKVCache listing of
+// "KV Cache 최적화 심층 분석: GQA·MLA·MHA 어텐션 메커니즘과 메모리 효율화 전략"
+// (youngju.dev) and section 4 of "Arsitektur Inferensi LLM: PagedAttention,
+// KV-Cache & Speculative Decoding" (tveniu.com).
+//
+// The rotation of a pair (x0, x1) by (c, s) is the float32 sequence
+//   r0 = (x0*c) - (x1*s),  r1 = (x0*s) + (x1*c)
+// with every operation rounded on its own: this file is compiled with
+// -ffp-contract=off and the pragma below forbids fused multiply-adds, so the
+// stored bits are fixed by the inputs alone.
+
+#include "kvc_internal.h"
+#include "kvc_device.h"
+
+#pragma clang fp contract(off)
+
+namespace kvc {
+
+namespace {
+
+template <typename T>
+struct Store;
+
+template <>
+struct Store<float> {
+    __device__ static float load(const float* p, size_t i) { return p[i]; }
+    __device__ static void store(float* p, size_t i, float x) { p[i] = x; }
+};
+
+template <>
+struct Store<uint16_t> {
+    __device__ static float load(const uint16_t* p, size_t i) { return bf16_bits_to_f32(p[i]); }
+    __device__ static void store(uint16_t* p, size_t i, float x) { p[i] = f32_to_bf16_rne(x); }
+};
+
+// One thread per (sequence, vector, pair).  Vectors of sequence b, in order:
+// the H_kv keys (rotated into the cache), the H_kv values (copied into the
+// cache), then, when q_inout is given, the H_q queries (rotated in place).
+template <typename T>
+__global__ void __launch_bounds__(256) append_kernel(const AppendParams p) {
+    const int half = p.d >> 1;
+    const int nvec = 2 * p.H_kv + (p.q_inout ? p.H_q : 0);
+    const long long total = static_cast<long long>(p.B) * nvec * half;
+    const long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (idx >= total) return;
+    const int i = static_cast<int>(idx % half);
+    const int vec = static_cast<int>((idx / half) % nvec);
+    const int b = static_cast<int>(idx / (static_cast<long long>(half) * nvec));
+
+    const int pos = p.positions[b];
+    if (pos < 0 || pos >= p.capacity || pos >= p.rope_rows) return;
+
+    // slot of (b, head j) in the cache, in elements, for head 0; + j * head stride
+    size_t slot0;
+    size_t head_stride;
+    if (p.block_table) {
+        const int blk = p.block_table[static_cast<size_t>(b) * p.max_blocks_per_seq + pos / p.block_size];
+        if (blk < 0 || blk >= p.num_blocks) return;
+        slot0 = (static_cast<size_t>(blk) * p.H_kv * p.block_size + pos % p.block_size) * p.d;
+        head_stride = static_cast<size_t>(p.block_size) * p.d;
+    } else {
+        slot0 = (static_cast<size_t>(b) * p.H_kv * p.T_max + pos) * p.d;
+        head_stride = static_cast<size_t>(p.T_max) * p.d;
+    }
+
+    int e0, e1;
+    if (p.rope_style == KVC_ROPE_HALF) { e0 = i; e1 = i + half; }
+    else { e0 = 2 * i; e1 = 2 * i + 1; }
+
+    if (vec >= p.H_kv && vec < 2 * p.H_kv) {  // value: bit copy of both elements
+        const int j = vec - p.H_kv;
+        const T* src = static_cast<const T*>(p.v_new) + (static_cast<size_t>(b) * p.H_kv + j) * p.d;
+        T* dst = static_cast<T*>(p.v_cache) + slot0 + j * head_stride;
+        dst[2 * i] = src[2 * i];
+        dst[2 * i + 1] = src[2 * i + 1];
+        return;
+    }
+
+    const float c = p.rope_cos[static_cast<size_t>(pos) * half + i];
+    const float s = p.rope_sin[static_cast<size_t>(pos) * half + i];
+    const T* src;
+    T* dst;
+    if (vec < p.H_kv) {
+        src = static_cast<const T*>(p.k_new) + (static_cast<size_t>(b) * p.H_kv + vec) * p.d;
+        dst = static_cast<T*>(p.k_cache) + slot0 + vec * head_stride;
+    } else {
+        const int h = vec - 2 * p.H_kv;
+        dst = static_cast<T*>(p.q_inout) + (static_cast<size_t>(b) * p.H_q + h) * p.d;
+        src = dst;
+    }
+    const float x0 = Store<T>::load(src, e0);
+    const float x1 = Store<T>::load(src, e1);
+    const float a = x0 * c;
+    const float bb = x1 * s;
+    const float r0 = a - bb;
+    const float e = x0 * s;
+    const float f = x1 * c;
+    const float r1 = e + f;
+    Store<T>::store(dst, e0, r0);
+    Store<T>::store(dst, e1, r1);
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
+    const int nvec = 2 * p.H_kv + (p.q_inout ? p.H_q : 0);
+    const long long total = static_cast<long long>(p.B) * nvec * (p.d / 2);
+    const int threads = 256;
+    const long long blocks = (total + threads - 1) / threads;
+    if (blocks <= 0) return hipSuccess;
+    if (p.dtype == KVC_BF16)
+        hipLaunchKernelGGL(append_kernel<uint16_t>, dim3(static_cast<unsigned>(blocks)), dim3(threads), 0, stream, p);
+    else
+        hipLaunchKernelGGL(append_kernel<float>, dim3(static_cast<unsigned>(blocks)), dim3(threads), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace kvc

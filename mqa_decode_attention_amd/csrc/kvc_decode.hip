@@ -1,0 +1,391 @@
+// kvc_decode.hip - attention of one new token per sequence over its KV cache.
+//
+// What is computed: for query head h of sequence b, with G = H_q / H_kv and
+// KV head j = floor(h / G) ("Grouped-query attention: berbagi KV head di antara
+// grup query", nalar.dev, section "Jumlah head menentukan batas grup"),
+//     out[b, h] = sum_t softmax_t(scale * q[b, h] . K[b, j, t]) V[b, j, t],  t < L_b.
+//
+// How (the pages name the idea - exact attention streamed through on-chip
+// memory with an online softmax, "Arsitektur Inferensi LLM" (tveniu.com),
+// section 5 - but no kernel for this chip):
+//  * One workgroup per (sequence, KV head, query-head chunk, token split).
+//    All query heads of the chunk are scored against each K row as it is
+//    read, so the compact KV of a group is read from HBM once, never expanded
+//    per query head ("Traffic cache tetap bergantung pada implementasi", same
+//    GQA page).
+//  * Each wave streams its own token rows straight into registers with 16-byte
+//    loads: LPT lanes cover one row (head_dim elements), 64 / LPT rows per load
+//    instruction, so every load instruction reads whole contiguous rows.
+//  * Scores: bf16 dot2 (two products per instruction, float32 accumulation)
+//    summed over the LPT lanes of a row with DPP.  Softmax is online in the
+//    log2 domain: running max m, running sum l, rescaled weighted-value sums.
+//  * Waves merge through LDS.  A single split writes the output; otherwise the
+//    split writes (m, l, acc) to the workspace and the last workgroup of its
+//    (sequence, KV head, chunk) to arrive - found with an atomic counter -
+//    merges all splits by their log-sum-exp and writes the output.
+//  * Paged caches: token t of sequence b is read from block
+//    table[b][t / block_size], offset t % block_size (PagedKVCache listing,
+//    youngju.dev; section 4 of the tveniu.com guide).  A 16-token block of one
+//    KV head is 4 KiB contiguous, so rows stay whole.
+
+#include "kvc_internal.h"
+#include "kvc_device.h"
+
+namespace kvc {
+
+namespace {
+
+template <typename T>
+struct Elem;
+template <>
+struct Elem<uint16_t> {  // bfloat16 bits
+    static constexpr int kPerVec = 8;  // elements per 16-byte load
+};
+template <>
+struct Elem<float> {
+    static constexpr int kPerVec = 4;
+};
+
+// Rows of LPT lanes, each lane holding EPL = D / LPT consecutive elements.
+template <typename T, int D>
+struct Layout {
+    static constexpr int EPL = Elem<T>::kPerVec;  // one 16-byte load per lane and row
+    static constexpr int LPT = D / EPL;
+    static constexpr int TPW = 64 / LPT;          // token rows per load instruction
+    static_assert(D % EPL == 0 && LPT >= 1 && LPT <= 64, "unsupported head_dim");
+};
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <typename T>
+__device__ __forceinline__ void store_out(void* out, size_t i, float x);
+template <>
+__device__ __forceinline__ void store_out<uint16_t>(void* out, size_t i, float x) {
+    static_cast<uint16_t*>(out)[i] = f32_to_bf16_rne(x);
+}
+template <>
+__device__ __forceinline__ void store_out<float>(void* out, size_t i, float x) {
+    static_cast<float*>(out)[i] = x;
+}
+
+// Partial dot product of one 16-byte K chunk with one query head's chunk.
+template <typename T>
+struct Dot;
+template <>
+struct Dot<uint16_t> {
+    // q chunk kept as 4 packed bf16 pairs
+    using QReg = uint4;
+    __device__ static QReg load_q(const void* q, size_t off) {
+        return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) + off);
+    }
+    __device__ static float dot(const uint4& k, const QReg& q) {
+        float s = dot2_bf16(k.x, q.x, 0.0f);
+        s = dot2_bf16(k.y, q.y, s);
+        s = dot2_bf16(k.z, q.z, s);
+        return dot2_bf16(k.w, q.w, s);
+    }
+    // the 8 values of a V chunk as float32
+    __device__ static void unpack(const uint4& v, float* f) {
+        f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+        f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+        f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+        f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+    }
+};
+template <>
+struct Dot<float> {
+    using QReg = float4;
+    __device__ static QReg load_q(const void* q, size_t off) {
+        return *reinterpret_cast<const float4*>(static_cast<const float*>(q) + off);
+    }
+    __device__ static float dot(const uint4& k, const QReg& q) {
+        float s = __builtin_bit_cast(float, k.x) * q.x;
+        s = fmaf(__builtin_bit_cast(float, k.y), q.y, s);
+        s = fmaf(__builtin_bit_cast(float, k.z), q.z, s);
+        return fmaf(__builtin_bit_cast(float, k.w), q.w, s);
+    }
+    __device__ static void unpack(const uint4& v, float* f) {
+        f[0] = __builtin_bit_cast(float, v.x); f[1] = __builtin_bit_cast(float, v.y);
+        f[2] = __builtin_bit_cast(float, v.z); f[3] = __builtin_bit_cast(float, v.w);
+    }
+};
+
+template <typename T, int D, int GC, int U, int NW, bool PAGED>
+__global__ void __launch_bounds__(NW * 64)
+decode_split_kernel(const DecodeParams p) {
+    using Lay = Layout<T, D>;
+    constexpr int EPL = Lay::EPL, LPT = Lay::LPT, TPW = Lay::TPW;
+    constexpr int TILE = U * TPW;  // tokens per wave iteration
+    constexpr int NT = NW * 64;
+
+    // The wave merge (sm_acc) and the split merge (sm_w, sm_lw) never overlap in
+    // time (a barrier separates them), so they share one LDS buffer.
+    constexpr int kWaveFloats = NW * GC * D;
+    constexpr int kSplitFloats = 2 * GC * kMaxSplits;
+    __shared__ float smem[kWaveFloats > kSplitFloats ? kWaveFloats : kSplitFloats];
+    __shared__ float sm_m[NW][GC];
+    __shared__ float sm_l[NW][GC];
+    __shared__ float sm_red[GC];
+    __shared__ int sm_last;
+    float (*sm_acc)[GC][D] = reinterpret_cast<float (*)[GC][D]>(smem);
+    float (*sm_w)[kMaxSplits] = reinterpret_cast<float (*)[kMaxSplits]>(smem);
+    float (*sm_lw)[kMaxSplits] = reinterpret_cast<float (*)[kMaxSplits]>(smem + GC * kMaxSplits);
+
+    const int wid = xcd_logical_id(blockIdx.x, p.n_wg, p.n_wg_pad);
+    if (wid < 0) return;
+    const int split = wid % p.n_splits;
+    const int unit = wid / p.n_splits;          // (b, j, chunk)
+    const int chunk = unit % p.n_chunks;
+    const int bj = unit / p.n_chunks;
+    const int b = bj / p.H_kv;
+    const int j = bj % p.H_kv;
+
+    int L = p.seq_lens[b];
+    L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
+    int nsp = (L + p.split_tokens - 1) / p.split_tokens;
+    nsp = nsp < 1 ? 1 : nsp;
+    if (split >= nsp) return;
+    const int t_begin = split * p.split_tokens;
+    const int t_end = min(L, t_begin + p.split_tokens);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int tg = lane / LPT;                  // token row of this lane within a load
+    const int el0 = (lane % LPT) * EPL;         // first head_dim element of this lane
+    const int h0 = j * p.G + chunk * GC;        // first query head of the chunk
+
+    typename Dot<T>::QReg qr[GC];
+#pragma unroll
+    for (int g = 0; g < GC; ++g)
+        qr[g] = Dot<T>::load_q(p.q, (static_cast<size_t>(b) * p.H_q + h0 + g) * D + el0);
+
+    float m[GC], l[GC], acc[GC][EPL];
+#pragma unroll
+    for (int g = 0; g < GC; ++g) {
+        m[g] = -INFINITY;
+        l[g] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[g][e] = 0.0f;
+    }
+
+    const T* kbase = static_cast<const T*>(p.k);
+    const T* vbase = static_cast<const T*>(p.v);
+    const size_t seq_off = PAGED ? 0 : (static_cast<size_t>(b) * p.H_kv + j) * p.T_max * D;
+    const int32_t* table = PAGED ? p.block_table + static_cast<size_t>(b) * p.max_blocks_per_seq : nullptr;
+
+    for (int base = t_begin + wave * TILE; base < t_end; base += NW * TILE) {
+        uint4 kr[U], vr[U];
+        bool valid[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int t = base + u * TPW + tg;
+            valid[u] = t < t_end;
+            const int tc = valid[u] ? t : t_end - 1;   // never touch rows >= L
+            size_t off;
+            if constexpr (PAGED) {
+                int blk = table[tc / p.block_size];
+                blk = blk < 0 ? 0 : (blk >= p.num_blocks ? p.num_blocks - 1 : blk);
+                off = ((static_cast<size_t>(blk) * p.H_kv + j) * p.block_size + tc % p.block_size) * D;
+            } else {
+                off = seq_off + static_cast<size_t>(tc) * D;
+            }
+            kr[u] = *reinterpret_cast<const uint4*>(kbase + off + el0);
+            vr[u] = *reinterpret_cast<const uint4*>(vbase + off + el0);
+        }
+
+        float s[U][GC];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int g = 0; g < GC; ++g) {
+                const float part = Dot<T>::dot(kr[u], qr[g]);
+                const float full = group_sum<LPT>(part) * p.scale_log2;
+                s[u][g] = valid[u] ? full : -INFINITY;
+            }
+
+#pragma unroll
+        for (int g = 0; g < GC; ++g) {
+            float mt = s[0][g];
+#pragma unroll
+            for (int u = 1; u < U; ++u) mt = fmaxf(mt, s[u][g]);
+            mt = across_groups_max<LPT>(mt);
+            const float m_new = fmaxf(m[g], mt);
+            const float alpha = fast_exp2(m[g] - m_new);
+            m[g] = m_new;
+            l[g] *= alpha;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[g][e] *= alpha;
+#pragma unroll
+            for (int u = 0; u < U; ++u) s[u][g] = fast_exp2(s[u][g] - m_new);
+        }
+
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float vf[EPL];
+            Dot<T>::unpack(vr[u], vf);
+#pragma unroll
+            for (int g = 0; g < GC; ++g) {
+                l[g] += s[u][g];
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(s[u][g], vf[e], acc[g][e]);
+            }
+        }
+    }
+
+    // fold the token rows of the wave together (lanes with equal lane % LPT)
+#pragma unroll
+    for (int g = 0; g < GC; ++g) {
+        l[g] = across_groups_sum<LPT>(l[g]);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[g][e] = across_groups_sum<LPT>(acc[g][e]);
+    }
+    if (lane < LPT) {
+#pragma unroll
+        for (int g = 0; g < GC; ++g)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) sm_acc[wave][g][el0 + e] = acc[g][e];
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int g = 0; g < GC; ++g) {
+            sm_m[wave][g] = m[g];
+            sm_l[wave][g] = l[g];
+        }
+    }
+    __syncthreads();
+
+    // merge the waves: split result for each (head, element)
+    for (int idx = tid; idx < GC * D; idx += NT) {
+        const int g = idx / D;
+        const int e = idx % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][g]);
+        float A = 0.0f, Ls = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const float mw = sm_m[w][g];
+            const float f = (mw == -INFINITY) ? 0.0f : fast_exp2(mw - M);
+            A = fmaf(sm_acc[w][g][e], f, A);
+            Ls = fmaf(sm_l[w][g], f, Ls);
+        }
+        const size_t bh = static_cast<size_t>(b) * p.H_q + h0 + g;
+        if (nsp == 1) {
+            store_out<T>(p.out, bh * D + e, Ls > 0.0f ? A / Ls : 0.0f);
+        } else {
+            p.ws_part[(bh * p.n_splits + split) * D + e] = A;
+            if (e == 0) p.ws_ml[bh * p.n_splits + split] = make_float2(M, Ls);
+        }
+    }
+    if (nsp == 1) return;
+
+    // publish this split; the last workgroup of the unit to arrive merges all splits
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) sm_last = (atomicAdd(p.ws_count + unit, 1) == nsp - 1);
+    __syncthreads();
+    if (!sm_last) return;
+    __threadfence();
+
+    for (int idx = tid; idx < GC * nsp; idx += NT) {
+        const int g = idx / nsp;
+        const int sp = idx % nsp;
+        const float2 ml = p.ws_ml[(static_cast<size_t>(b) * p.H_q + h0 + g) * p.n_splits + sp];
+        sm_w[g][sp] = ml.x;
+        sm_lw[g][sp] = ml.y;
+    }
+    __syncthreads();
+    for (int g = wave; g < GC; g += NW) {           // per-head maximum over splits
+        float M = -INFINITY;
+        for (int sp = lane; sp < nsp; sp += 64) M = fmaxf(M, sm_w[g][sp]);
+        M = across_groups_max<1>(M);
+        if (lane == 0) sm_red[g] = M;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < GC * nsp; idx += NT) {
+        const int g = idx / nsp;
+        const int sp = idx % nsp;
+        const float mw = sm_w[g][sp];
+        const float f = (mw == -INFINITY) ? 0.0f : fast_exp2(mw - sm_red[g]);
+        sm_w[g][sp] = f;
+        sm_lw[g][sp] *= f;
+    }
+    __syncthreads();
+    for (int g = wave; g < GC; g += NW) {           // per-head total weight
+        float Ls = 0.0f;
+        for (int sp = lane; sp < nsp; sp += 64) Ls += sm_lw[g][sp];
+        Ls = across_groups_sum<1>(Ls);
+        if (lane == 0) sm_red[g] = Ls;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < GC * D; idx += NT) {
+        const int g = idx / D;
+        const int e = idx % D;
+        const size_t bh = static_cast<size_t>(b) * p.H_q + h0 + g;
+        const float* part = p.ws_part + bh * p.n_splits * D + e;
+        float A = 0.0f;
+        for (int sp = 0; sp < nsp; ++sp) A = fmaf(sm_w[g][sp], part[static_cast<size_t>(sp) * D], A);
+        const float Ls = sm_red[g];
+        store_out<T>(p.out, bh * D + e, Ls > 0.0f ? A / Ls : 0.0f);
+    }
+    if (tid == 0) p.ws_count[unit] = 0;   // ready for the next call
+}
+
+constexpr int kU = 4;
+constexpr int kNW = 4;
+
+template <typename T, int D, int GC>
+hipError_t launch_tdg(bool paged, const DecodeParams& p, hipStream_t stream) {
+    const dim3 grid(p.n_wg_pad), block(kNW * 64);
+    if (paged)
+        hipLaunchKernelGGL((decode_split_kernel<T, D, GC, kU, kNW, true>), grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL((decode_split_kernel<T, D, GC, kU, kNW, false>), grid, block, 0, stream, p);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_td(int gc, bool paged, const DecodeParams& p, hipStream_t stream) {
+    switch (gc) {
+        case 1: return launch_tdg<T, D, 1>(paged, p, stream);
+        case 2: return launch_tdg<T, D, 2>(paged, p, stream);
+        case 4: return launch_tdg<T, D, 4>(paged, p, stream);
+        case 8: return launch_tdg<T, D, 8>(paged, p, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename T>
+hipError_t launch_t(int d, int gc, bool paged, const DecodeParams& p, hipStream_t stream) {
+    switch (d) {
+        case 16: return launch_td<T, 16>(gc, paged, p, stream);
+        case 32: return launch_td<T, 32>(gc, paged, p, stream);
+        case 64: return launch_td<T, 64>(gc, paged, p, stream);
+        case 128: return launch_td<T, 128>(gc, paged, p, stream);
+        case 256: return launch_td<T, 256>(gc, paged, p, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+bool decode_supported(kvc_dtype dtype, int d, int heads_per_wg) {
+    const bool dt_ok = dtype == KVC_BF16 || dtype == KVC_F32;
+    const bool d_ok = d == 16 || d == 32 || d == 64 || d == 128 || d == 256;
+    const bool g_ok = heads_per_wg == 1 || heads_per_wg == 2 || heads_per_wg == 4 || heads_per_wg == 8;
+    return dt_ok && d_ok && g_ok;
+}
+
+int decode_tile_tokens(kvc_dtype dtype, int d) {
+    const int epl = dtype == KVC_BF16 ? 8 : 4;
+    return kU * (64 / (d / epl)) * kNW;
+}
+
+hipError_t launch_decode(kvc_dtype dtype, int d, int heads_per_wg, bool paged,
+                         const DecodeParams& p, hipStream_t stream) {
+    if (dtype == KVC_BF16) return launch_t<uint16_t>(d, heads_per_wg, paged, p, stream);
+    return launch_t<float>(d, heads_per_wg, paged, p, stream);
+}
+
+}  // namespace kvc

@@ -1,0 +1,81 @@
+// kvc_internal.h - parameter blocks and launchers shared by the C ABI layer
+// (kvc_api.hip) and the kernel translation units.  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/kvc.h"
+
+namespace kvc {
+
+struct AppendParams {
+    kvc_dtype dtype;
+    int B, H_q, H_kv, d;
+    void* k_cache;
+    void* v_cache;
+    int T_max;                   // contiguous capacity (tokens)
+    const int32_t* block_table;  // NULL => contiguous
+    int block_size, max_blocks_per_seq, num_blocks;
+    int capacity;                // tokens addressable per sequence
+    const int32_t* positions;
+    const void* k_new;
+    const void* v_new;
+    void* q_inout;
+    const float* rope_cos;
+    const float* rope_sin;
+    int rope_rows;
+    int rope_style;
+};
+
+hipError_t launch_append(const AppendParams& p, hipStream_t stream);
+
+// Split-decode launch plan, a pure function of the sizes (no device query), so
+// that kvc_decode_workspace_bytes and the decode call always agree.
+struct DecodePlan {
+    int heads_per_wg;   // query heads one workgroup serves (a divisor of G)
+    int n_chunks;       // G / heads_per_wg
+    int split_tokens;   // tokens per split
+    int n_splits;       // splits of the longest sequence (>= 1)
+    size_t ws_part;     // byte offsets inside the workspace
+    size_t ws_ml;
+    size_t ws_count;
+    size_t ws_bytes;    // 0 when n_splits == 1
+};
+
+// Largest split count the merge step supports (partials live in LDS).
+constexpr int kMaxSplits = 256;
+
+struct DecodeParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;
+    const int32_t* seq_lens;
+    const int32_t* block_table;  // NULL => contiguous
+    float* ws_part;              // [B*H_q, n_splits, d]   weighted-value partials
+    float2* ws_ml;               // [B*H_q, n_splits]      (running max (log2), sum)
+    int* ws_count;               // [B*H_kv*n_chunks]     arrival counters
+    int B, H_q, H_kv, G, n_chunks;
+    int T_max, block_size, max_blocks_per_seq, num_blocks;
+    int max_seq_len, split_tokens, n_splits;
+    int n_wg, n_wg_pad;          // logical workgroups, padded to a multiple of 8
+    float scale_log2;            // softmax scale * log2(e)
+};
+
+// Returns false (and leaves *plan untouched) when the sizes cannot be planned.
+bool plan_decode(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_len,
+                 int split_tokens, DecodePlan* plan, const char** why);
+
+// Is there a kernel for this (dtype, head dim, heads per workgroup)?
+bool decode_supported(kvc_dtype dtype, int d, int heads_per_wg);
+
+// Tokens one workgroup consumes per pass of all its waves (split sizes are a
+// multiple of this unless the caller fixes them).
+int decode_tile_tokens(kvc_dtype dtype, int d);
+
+hipError_t launch_decode(kvc_dtype dtype, int d, int heads_per_wg, bool paged,
+                         const DecodeParams& p, hipStream_t stream);
+
+}  // namespace kvc

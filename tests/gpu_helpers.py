@@ -1,0 +1,104 @@
+"""Shared steps of the GPU tests: run the HIP path, run the oracle, compare.
+
+The GPU side goes through the Python binding (and so the C ABI); the oracle
+side sees the same seeded inputs and never anything the GPU produced.
+"""
+from __future__ import annotations
+
+import sys
+from typing import Optional
+
+import numpy as np
+import torch
+
+import mqa_decode_attention_amd as kvc
+import oracle as O
+import workloads as W
+
+BF16_TOL = 2e-3      # max-abs bar for bf16 attention outputs (after bf16 rounding of the oracle)
+F32_TOL = 1e-5       # float32 outputs: far inside the same bar
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def store_np(t: torch.Tensor, dtype: str) -> np.ndarray:
+    t = t.detach().cpu().contiguous()
+    if dtype == "bf16":
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.uint8).numpy()
+
+
+class GpuStep:
+    """Inputs on the GPU, the append and the decode call, results back on the CPU."""
+
+    def __init__(self, x: W.DecodeInputs, device: str = "cuda"):
+        self.x = x
+        w = x.workload
+        self.k = x.k_cache.to(device)
+        self.v = x.v_cache.to(device)
+        self.q = x.q.to(device).clone()
+        self.kn = x.k_new.to(device)
+        self.vn = x.v_new.to(device)
+        self.pos = x.cached.to(device)
+        self.lens = x.seq_lens.to(device)
+        self.cos = x.rope_cos.to(device)
+        self.sin = x.rope_sin.to(device)
+        self.tbl = x.block_table.to(device) if w.paged else None
+        self.max_len = int(x.seq_lens.max())
+
+    def append(self, rope_style="interleaved", stream=None):
+        kvc.append(self.k, self.v, self.pos, self.kn, self.vn, self.cos, self.sin, q=self.q,
+                   block_table=self.tbl, rope_style=rope_style, stream=stream)
+
+    def decode(self, split_tokens=0, lens=None, max_len=None, stream=None, out=None):
+        lens = self.lens if lens is None else lens
+        max_len = self.max_len if max_len is None else max_len
+        if self.tbl is not None:
+            return kvc.decode_attn_paged(self.q, self.k, self.v, self.tbl, lens, max_len,
+                                         split_tokens=split_tokens, stream=stream, out=out)
+        return kvc.decode_attn(self.q, self.k, self.v, lens, max_len, split_tokens=split_tokens,
+                               stream=stream, out=out)
+
+
+def oracle_append(x: W.DecodeInputs, rope_style="interleaved"):
+    """Oracle caches and rotated q after the append (numpy storage arrays)."""
+    w = x.workload
+    dt = w.dtype
+    kc, vc = store_np(x.k_cache, dt), store_np(x.v_cache, dt)
+    q, kn, vn = store_np(x.q, dt), store_np(x.k_new, dt), store_np(x.v_new, dt)
+    cos, sin = x.rope_cos.numpy(), x.rope_sin.numpy()
+    cached = x.cached.numpy()
+    if w.paged:
+        return O.append_paged(kc, vc, x.block_table.numpy(), w.block_size, cached, kn, vn, cos, sin,
+                              dt, rope_style, q=q)
+    return O.append_contiguous(kc, vc, cached, kn, vn, cos, sin, dt, rope_style, q=q)
+
+
+def oracle_decode(x: W.DecodeInputs, k2, v2, q2, seq_lens=None):
+    w = x.workload
+    lens = x.seq_lens.numpy() if seq_lens is None else seq_lens
+    if w.paged:
+        o = O.decode_attention_paged(q2, k2, v2, x.block_table.numpy(), w.block_size, lens, w.dtype)
+    else:
+        o = O.decode_attention(q2, k2, v2, lens, w.dtype)
+    return o
+
+
+def compare_out(got: torch.Tensor, ref64: np.ndarray, dtype: str, what: str = ""):
+    """Max-abs error of the GPU output against the oracle rounded to the storage dtype."""
+    g = O.to_f64(store_np(got, dtype), dtype)
+    r = O.to_f64(O.round_store(ref64, dtype), dtype)
+    assert g.shape == r.shape, (g.shape, r.shape)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite GPU output"
+    err = float(np.max(np.abs(g - r))) if g.size else 0.0
+    tol = BF16_TOL if dtype == "bf16" else F32_TOL
+    say(f"  {what}: max|err| = {err:.3g} (tol {tol}), max|out| = {float(np.max(np.abs(r))) if r.size else 0:.3g}")
+    assert err <= tol, f"{what}: max abs error {err} > {tol}"
+    return err

@@ -1,0 +1,126 @@
+"""The C ABI library loads, exports every declared symbol, and rejects bad calls
+on the host before touching a device (CPU only: no compute call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mqa_decode_attention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvc.h")
+
+KVC_OK, KVC_ERR_NULL, KVC_ERR_SHAPE, KVC_ERR_UNSUPPORTED, KVC_ERR_WORKSPACE, KVC_ERR_HIP = range(6)
+F32, BF16 = 0, 1
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails its host checks
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvc_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 7
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES), "binding signatures must mirror the header"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.kvc_abi_version() == 1
+    for s in range(6):
+        assert lib.kvc_status_string(s)
+    assert lib.kvc_status_string(99) == b"unknown status"
+    assert lib.kvc_last_error() is not None
+
+
+def _append(lib, **kw):
+    a = dict(dt=BF16, B=2, H_q=8, H_kv=2, d=128, k=FAKE, v=FAKE, T_max=64, tbl=None, bs=0, mb=0, nb=0,
+             pos=FAKE, kn=FAKE, vn=FAKE, q=None, cos=FAKE, sin=FAKE, rows=64, style=0, stream=None)
+    a.update(kw)
+    return lib.kvc_append(a["dt"], a["B"], a["H_q"], a["H_kv"], a["d"], a["k"], a["v"], a["T_max"],
+                          a["tbl"], a["bs"], a["mb"], a["nb"], a["pos"], a["kn"], a["vn"], a["q"],
+                          a["cos"], a["sin"], a["rows"], a["style"], a["stream"])
+
+
+def test_append_host_checks(lib):
+    assert _append(lib, H_q=6, H_kv=4) == KVC_ERR_SHAPE
+    assert b"multiple" in lib.kvc_last_error()
+    assert _append(lib, d=127) == KVC_ERR_SHAPE
+    assert _append(lib, style=7) == KVC_ERR_UNSUPPORTED
+    assert _append(lib, dt=5) == KVC_ERR_UNSUPPORTED
+    assert _append(lib, k=None) == KVC_ERR_NULL
+    assert _append(lib, pos=None) == KVC_ERR_NULL
+    assert _append(lib, cos=None) == KVC_ERR_NULL
+    assert _append(lib, T_max=0) == KVC_ERR_SHAPE
+    assert _append(lib, tbl=FAKE, bs=0, mb=4, nb=10) == KVC_ERR_SHAPE
+    assert _append(lib, rows=0) == KVC_ERR_SHAPE
+    assert _append(lib, B=0) == KVC_OK           # nothing to do, nothing launched
+
+
+def _decode(lib, **kw):
+    a = dict(dt=BF16, B=2, H_q=8, H_kv=2, d=128, q=FAKE, k=FAKE, v=FAKE, T_max=64, lens=FAKE, L=64,
+             scale=0.0, out=FAKE, split=0, ws=None, wsn=0, stream=None)
+    a.update(kw)
+    return lib.kvc_decode_attn(a["dt"], a["B"], a["H_q"], a["H_kv"], a["d"], a["q"], a["k"], a["v"],
+                               a["T_max"], a["lens"], a["L"], a["scale"], a["out"], a["split"], a["ws"],
+                               a["wsn"], a["stream"])
+
+
+def test_decode_host_checks(lib):
+    assert _decode(lib, H_q=7) == KVC_ERR_SHAPE
+    assert _decode(lib, L=65) == KVC_ERR_SHAPE                  # beyond T_max
+    assert b"T_max" in lib.kvc_last_error()
+    assert _decode(lib, L=-1) == KVC_ERR_SHAPE
+    assert _decode(lib, q=None) == KVC_ERR_NULL
+    assert _decode(lib, out=None) == KVC_ERR_NULL
+    assert _decode(lib, lens=None) == KVC_ERR_NULL
+    assert _decode(lib, d=96) == KVC_ERR_UNSUPPORTED
+    assert _decode(lib, d=2) == KVC_ERR_UNSUPPORTED
+    assert _decode(lib, dt=9) == KVC_ERR_UNSUPPORTED
+    # a long sequence needs splits and therefore a workspace
+    assert _decode(lib, T_max=100000, L=100000) == KVC_ERR_WORKSPACE
+    need = lib.kvc_decode_workspace_bytes(BF16, 2, 8, 2, 128, 100000, 0)
+    assert need > 0
+    assert _decode(lib, T_max=100000, L=100000, ws=FAKE, wsn=need - 1) == KVC_ERR_WORKSPACE
+    assert _decode(lib, T_max=100000, L=100000, ws=ctypes.c_void_p(0x1008), wsn=need) == KVC_ERR_WORKSPACE
+    assert b"aligned" in lib.kvc_last_error()
+    # too many splits for the merge step
+    assert _decode(lib, T_max=100000, L=100000, split=16) == KVC_ERR_UNSUPPORTED
+    assert _decode(lib, B=0) == KVC_OK
+
+
+def test_paged_host_checks(lib):
+    f = lib.kvc_decode_attn_paged
+    args = [BF16, 2, 8, 2, 128, FAKE, FAKE, FAKE, 100, 16, FAKE, 4, FAKE, 64, 0.0, FAKE, 0, None, 0, None]
+    bad = list(args)
+    bad[10] = None
+    assert f(*bad) == KVC_ERR_NULL                                # no block table
+    bad = list(args)
+    bad[13] = 65                                                  # 4 blocks * 16 tokens = 64
+    assert f(*bad) == KVC_ERR_SHAPE
+    bad = list(args)
+    bad[9] = 0
+    assert f(*bad) == KVC_ERR_SHAPE
+
+
+def test_workspace_sizes(lib):
+    ws = lib.kvc_decode_workspace_bytes
+    assert ws(F32, 1, 4, 4, 16, 6, 0) == 0                        # one split, no workspace
+    assert ws(BF16, 16, 32, 8, 128, 8193, 0) > 0
+    # explicit split: partials for B*H_q heads, n_splits each, d + 2 floats, 256-aligned regions
+    n = ws(BF16, 16, 32, 8, 128, 8193, 1024)
+    splits = -(-8193 // 1024)
+    assert n >= 16 * 32 * splits * (128 + 2) * 4 and n % 256 == 0
+    assert ws(BF16, 16, 32, 8, 128, 8193, 8193) == 0
+    assert ws(BF16, 16, 30, 8, 128, 8193, 0) == (1 << 64) - 1     # invalid sizes
+    assert ws(BF16, 1, 64, 8, 128, 131073, 0) > 0

@@ -1,0 +1,197 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Append: bit-exact over the whole cache buffers and the rotated query.
+Attention: max-abs error <= 2e-3 (bf16; the oracle rounded to bf16) and
+<= 1e-5 (float32), at oracle-sized shapes that span many tiles and splits with
+ragged tails, and at the workloads' full sizes on sampled (sequence, KV head)
+groups in the launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from gpu_helpers import GpuStep, bits, compare_out, oracle_append, oracle_decode, say, store_np
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "tiny_mha": W.WORKLOADS["tiny_mha"],
+    "gqa_8b": W.WORKLOADS["gqa_8b"].replace(B=3, cached_lo=300, cached_hi=1100, T_max=1104),
+    "mqa_ragged": W.WORKLOADS["mqa_ragged"].replace(B=5, cached_lo=100, cached_hi=700, T_max=704),
+    "long_gqa": W.WORKLOADS["long_gqa"].replace(cached_lo=3000, cached_hi=3000, T_max=3008),
+    "paged_gqa": W.WORKLOADS["paged_gqa"].replace(B=4, cached_lo=20, cached_hi=400),
+}
+
+
+def _check_append(step: GpuStep, x, style="interleaved"):
+    k2, v2, q2 = oracle_append(x, style)
+    dt = x.workload.dtype
+    assert np.array_equal(bits(step.k), np.ascontiguousarray(k2).view(np.uint8)), "K cache differs from the oracle"
+    assert np.array_equal(bits(step.v), np.ascontiguousarray(v2).view(np.uint8)), "V cache differs from the oracle"
+    assert np.array_equal(store_np(step.q, dt).view(np.uint8), np.ascontiguousarray(q2).view(np.uint8)), \
+        "rotated q differs from the oracle"
+    return k2, v2, q2
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_step_matches_oracle(name):
+    x = W.draw(SMALL[name])
+    say(f"[{name}] B={x.workload.B} lens={x.seq_lens.tolist()[:6]} append+decode")
+    step = GpuStep(x)
+    step.append()
+    torch.cuda.synchronize()
+    k2, v2, q2 = _check_append(step, x)
+    ref = oracle_decode(x, k2, v2, q2)
+    for split in (0, 64, 100, 1 << 20):
+        out = step.decode(split_tokens=split)
+        torch.cuda.synchronize()
+        compare_out(out, ref, x.workload.dtype, f"{name} split_tokens={split}")
+
+
+@pytest.mark.parametrize("name", ["gqa_8b", "paged_gqa", "tiny_mha"])
+def test_half_rotation_style(name):
+    x = W.draw(SMALL[name])
+    say(f"[{name}] rope_style=half")
+    step = GpuStep(x)
+    step.append(rope_style="half")
+    torch.cuda.synchronize()
+    k2, v2, q2 = _check_append(step, x, "half")
+    compare_out(step.decode(), oracle_decode(x, k2, v2, q2), x.workload.dtype, f"{name} half")
+
+
+def test_edge_lengths():
+    """L = 1 (empty cache before the step), L = 0, tile-exact and tile+1 lengths."""
+    base = W.WORKLOADS["gqa_8b"].replace(B=6, cached_lo=511, cached_hi=511, T_max=520)
+    x = W.draw(base)
+    x.cached[:] = torch.tensor([0, 63, 64, 127, 255, 511], dtype=torch.int32)
+    # re-poison so slots >= cached are NaN for the new lengths
+    for b, c in enumerate(x.cached.tolist()):
+        x.k_cache[b, :, c:] = float("nan")
+        x.v_cache[b, :, c:] = float("nan")
+    say(f"[edge] lens={x.seq_lens.tolist()}")
+    step = GpuStep(x)
+    step.append()
+    torch.cuda.synchronize()
+    k2, v2, q2 = _check_append(step, x)
+    ref = oracle_decode(x, k2, v2, q2)
+    for split in (0, 64, 1 << 20):
+        compare_out(step.decode(split_tokens=split), ref, "bf16", f"edge split={split}")
+    # one token: the output is exactly that token's value (a single weight of 1)
+    out = step.decode()
+    torch.cuda.synchronize()
+    vn = store_np(x.v_new, "bf16")
+    assert np.array_equal(store_np(out, "bf16")[0].reshape(8, 4, 128)[:, 0], vn[0])
+    # L = 0 for every sequence: zeros
+    zero = torch.zeros_like(step.lens)
+    out0 = step.decode(lens=zero, max_len=0)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out0.float()) == 0
+
+
+def test_split_invariance_and_determinism():
+    x = W.draw(SMALL["long_gqa"])
+    say("[long_gqa small] split invariance")
+    step = GpuStep(x)
+    step.append()
+    torch.cuda.synchronize()
+    k2, v2, q2 = _check_append(step, x)
+    ref = oracle_decode(x, k2, v2, q2)
+    outs = {}
+    for split in (16, 64, 200, 1500, 3001, 0):
+        outs[split] = step.decode(split_tokens=split).clone()
+        torch.cuda.synchronize()
+        compare_out(outs[split], ref, "bf16", f"split={split}")
+    again = step.decode(split_tokens=64)
+    torch.cuda.synchronize()
+    assert torch.equal(again.view(torch.int16), outs[64].view(torch.int16)), "run-to-run difference"
+
+
+def test_nondefault_stream():
+    x = W.draw(SMALL["gqa_8b"])
+    say("[gqa_8b small] side stream")
+    step = GpuStep(x)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        step.append(stream=s)
+        out = step.decode(stream=s)
+    s.synchronize()
+    k2, v2, q2 = _check_append(step, x)
+    compare_out(out, oracle_decode(x, k2, v2, q2), "bf16", "side stream")
+
+
+def test_paged_equals_contiguous_bitwise():
+    """The same logical cache as a contiguous buffer and as a shuffled block pool."""
+    w = W.WORKLOADS["gqa_8b"].replace(B=4, cached_lo=50, cached_hi=900, T_max=912)
+    x = W.draw(w)
+    say("[paged == contiguous]")
+    step = GpuStep(x)
+    step.append()
+    torch.cuda.synchronize()
+    bs = 16
+    B, H_kv, T, d = step.k.shape
+    nblk = -(-T // bs)
+    g = torch.Generator().manual_seed(11)
+    perm = torch.randperm(B * nblk, generator=g)
+    table = perm.view(B, nblk).to(torch.int32)
+    kp = torch.empty((B * nblk, H_kv, bs, d), dtype=step.k.dtype, device="cuda")
+    vp = torch.empty_like(kp)
+    kpad = torch.nn.functional.pad(step.k, (0, 0, 0, nblk * bs - T))
+    vpad = torch.nn.functional.pad(step.v, (0, 0, 0, nblk * bs - T))
+    kp[table.flatten().long().cuda()] = kpad.view(B, H_kv, nblk, bs, d).permute(0, 2, 1, 3, 4).reshape(-1, H_kv, bs, d)
+    vp[table.flatten().long().cuda()] = vpad.view(B, H_kv, nblk, bs, d).permute(0, 2, 1, 3, 4).reshape(-1, H_kv, bs, d)
+    import mqa_decode_attention_amd as kvc
+    for split in (0, 128):
+        a = kvc.decode_attn(step.q, step.k, step.v, step.lens, step.max_len, split_tokens=split)
+        p = kvc.decode_attn_paged(step.q, kp, vp, table.cuda(), step.lens, step.max_len, split_tokens=split)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), p.view(torch.int16)), f"paged != contiguous (split {split})"
+
+
+# ---------------------------------------------------------------------------
+# full sizes, default launch plan (what the benchmark times)
+# ---------------------------------------------------------------------------
+
+
+def _sample_groups(w, n, seed):
+    rng = np.random.default_rng(seed)
+    pairs = {(0, 0), (w.B - 1, w.H_kv - 1)}
+    while len(pairs) < min(n, w.B * w.H_kv):
+        pairs.add((int(rng.integers(w.B)), int(rng.integers(w.H_kv))))
+    return sorted(pairs)
+
+
+@pytest.mark.parametrize("name", ["gqa_8b", "mqa_ragged", "long_gqa", "paged_gqa"])
+def test_full_size_sampled(name):
+    w = W.WORKLOADS[name]
+    x = W.draw(w)
+    say(f"[{name} full] B={w.B} max_len={int(x.seq_lens.max())}")
+    step = GpuStep(x)
+    step.append()
+    out = step.decode()
+    torch.cuda.synchronize()
+    # the append, over the whole buffers
+    k2, v2, q2 = _check_append(step, x)
+    # attention, on sampled (sequence, KV head) groups computed one by one
+    dt, G = w.dtype, w.G
+    got = store_np(out, dt)
+    lens = x.seq_lens.numpy()
+    worst = 0.0
+    for b, j in _sample_groups(w, 6, seed=w.seed):
+        hs = slice(j * G, (j + 1) * G)
+        qg = q2[b:b + 1, hs]
+        if w.paged:
+            Lb = int(lens[b])
+            kg = O.gather_paged(k2, x.block_table.numpy(), w.block_size, b, Lb)[None, j:j + 1]
+            vg = O.gather_paged(v2, x.block_table.numpy(), w.block_size, b, Lb)[None, j:j + 1]
+        else:
+            kg, vg = k2[b:b + 1, j:j + 1], v2[b:b + 1, j:j + 1]
+        ref = O.decode_attention(qg, kg, vg, lens[b:b + 1], dt)
+        g = O.to_f64(got[b:b + 1, hs], dt)
+        r = O.to_f64(O.round_store(ref, dt), dt)
+        err = float(np.max(np.abs(g - r)))
+        worst = max(worst, err)
+        assert err <= 2e-3, f"{name} (b={b}, j={j}): max abs error {err}"
+    assert np.all(np.isfinite(O.to_f64(got, dt)))
+    say(f"  {name}: sampled max|err| = {worst:.3g}")
