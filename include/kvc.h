@@ -115,10 +115,13 @@ kvc_status kvc_append(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
  * sizes and this split_tokens (0 = the library's choice).  May be 0.
  * Returns (size_t)-1 for invalid sizes.
  *
- * The workspace holds per-split partial results (running max, sum, weighted
- * values) and one arrival counter per (sequence, KV head).  It must be
- * zero-filled before its first use; every completed call leaves it zeroed
- * again, so one buffer serves any number of later calls (not concurrent ones).
+ * The workspace starts with a fixed 256 KiB region of arrival counters (one
+ * per sequence, KV head and head chunk; at most 65536 of them), followed by
+ * the per-split partial results (running max, sum, weighted values).  The
+ * buffer must be zero-filled before its first use.  Every completed call
+ * leaves the counter region zeroed again and never writes partials into it,
+ * so one buffer serves any number of later calls of any shape, one at a time
+ * (calls that overlap in time must not share a workspace).
  */
 size_t kvc_decode_workspace_bytes(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
                                   int max_seq_len, int split_tokens);

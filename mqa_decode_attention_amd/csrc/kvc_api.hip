@@ -98,11 +98,15 @@ bool plan_decode(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_l
     pl.split_tokens = ts;
     pl.n_splits = (L + ts - 1) / ts;
     if (pl.n_splits > 1) {
+        if (units > kMaxUnits) {
+            *why = "more than 65536 (sequence, KV head, head chunk) units need splitting";
+            return false;
+        }
         const size_t bh = static_cast<size_t>(B) * H_q;
-        pl.ws_part = 0;
-        pl.ws_ml = align_up(bh * pl.n_splits * d * sizeof(float), 256);
-        pl.ws_count = align_up(pl.ws_ml + bh * pl.n_splits * sizeof(float2), 256);
-        pl.ws_bytes = align_up(pl.ws_count + static_cast<size_t>(units) * sizeof(int), 256);
+        pl.ws_count = 0;
+        pl.ws_ml = kCounterBytes;
+        pl.ws_part = align_up(pl.ws_ml + bh * pl.n_splits * sizeof(float2), 256);
+        pl.ws_bytes = align_up(pl.ws_part + bh * pl.n_splits * d * sizeof(float), 256);
     }
     *plan = pl;
     return true;

@@ -47,6 +47,14 @@ struct DecodePlan {
 // Largest split count the merge step supports (partials live in LDS).
 constexpr int kMaxSplits = 256;
 
+// The arrival counters sit in a fixed region at the start of every workspace,
+// one int per (sequence, KV head, head chunk), and partial results are only
+// ever written after it.  A counter is therefore never overwritten by another
+// call's partials, and a buffer reused across calls of any shape keeps every
+// counter at zero between calls.
+constexpr int kMaxUnits = 1 << 16;
+constexpr size_t kCounterBytes = sizeof(int) * kMaxUnits;
+
 struct DecodeParams {
     const void* q;
     const void* k;

@@ -195,3 +195,24 @@ def test_full_size_sampled(name):
         assert err <= 2e-3, f"{name} (b={b}, j={j}): max abs error {err}"
     assert np.all(np.isfinite(O.to_f64(got, dt)))
     say(f"  {name}: sampled max|err| = {worst:.3g}")
+
+
+def test_workspace_reuse_across_shapes():
+    """One workspace shared by calls of different shapes (regression: arrival
+    counters must never sit where an earlier call left partial results)."""
+    import mqa_decode_attention_amd as kvc
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    cases = [SMALL["long_gqa"], SMALL["mqa_ragged"], SMALL["gqa_8b"], SMALL["long_gqa"]]
+    for i, w in enumerate(cases):
+        x = W.draw(w)
+        say(f"[workspace reuse {i}] {w.name}")
+        step = GpuStep(x)
+        step.append()
+        for split in (16, 64):
+            out = kvc.decode_attn(step.q, step.k, step.v, step.lens, step.max_len, split_tokens=split,
+                                  workspace=ws)
+            torch.cuda.synchronize()
+            k2, v2, q2 = oracle_append(x)
+            compare_out(out, oracle_decode(x, k2, v2, q2), w.dtype, f"reuse {w.name} split={split}")
+    # every counter is back at zero
+    assert torch.count_nonzero(ws[: 256 << 10]) == 0
