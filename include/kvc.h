@@ -75,6 +75,16 @@ const char* kvc_status_string(int status);
 const char* kvc_last_error(void);
 
 /*
+ * Timing aid.  The next kvc_decode_attn / kvc_decode_attn_paged call made on
+ * this thread records start_event on its stream just before launching its
+ * streaming (split) kernel and stop_event just after it, so that
+ * hipEventElapsedTime gives that kernel's duration.  Both are hipEvent_t
+ * handles owned by the caller (or NULL).  One-shot: the next decode call, even
+ * a failing one, clears them.
+ */
+void kvc_profile_next_decode(void* start_event, void* stop_event);
+
+/*
  * kvc_append - write the new token of every sequence into the cache.
  *
  * For sequence b, p = positions[b] is the slot (the number of tokens cached
@@ -115,13 +125,11 @@ kvc_status kvc_append(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
  * sizes and this split_tokens (0 = the library's choice).  May be 0.
  * Returns (size_t)-1 for invalid sizes.
  *
- * The workspace starts with a fixed 256 KiB region of arrival counters (one
- * per sequence, KV head and head chunk; at most 65536 of them), followed by
- * the per-split partial results (running max, sum, weighted values).  The
- * buffer must be zero-filled before its first use.  Every completed call
- * leaves the counter region zeroed again and never writes partials into it,
- * so one buffer serves any number of later calls of any shape, one at a time
- * (calls that overlap in time must not share a workspace).
+ * The workspace holds the per-split partial results (running max and sum
+ * per query head, weighted value sums) that the split kernel writes and the
+ * merge kernel of the same call reads.  Its contents need no initialisation
+ * and mean nothing between calls; calls that overlap in time must not share
+ * a workspace.
  */
 size_t kvc_decode_workspace_bytes(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
                                   int max_seq_len, int split_tokens);
@@ -137,9 +145,10 @@ size_t kvc_decode_workspace_bytes(kvc_dtype dtype, int B, int H_q, int H_kv, int
  * Slots at or past L_b are never read.
  *
  * The token axis is cut into splits of split_tokens tokens (0 = library
- * heuristic); each split is one workgroup per (sequence, KV head) and the
- * splits are merged exactly by their log-sum-exp.  The result does not depend
- * on the split count beyond float32 rounding.
+ * heuristic); each split is one workgroup per (sequence, KV head) and, when a
+ * sequence has more than one split, a second kernel on the same stream merges
+ * them exactly by their log-sum-exp.  The result does not depend on the split
+ * count beyond float32 rounding.
  */
 kvc_status kvc_decode_attn(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
                            const void* q, const void* k_cache, const void* v_cache, int T_max,

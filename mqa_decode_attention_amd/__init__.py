@@ -8,5 +8,5 @@ include/kvc.h); this package only marshals torch tensors into it:
     decode_attn_paged(q, k_pool, v_pool, block_table, seq_lens, max_seq_len)
 """
 from .api import (KVC_BF16, KVC_F32, KvcError, append, decode_attn, decode_attn_paged,  # noqa: F401
-                  workspace_bytes)
+                  profile_next_decode, workspace_bytes)
 from ._lib import LIB_PATH, load  # noqa: F401

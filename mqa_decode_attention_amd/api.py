@@ -105,9 +105,8 @@ def workspace_bytes(dtype: torch.dtype, B: int, H_q: int, H_kv: int, d: int, max
     return n
 
 
-# Zero-filled workspaces kept per (device, stream): the library leaves them
-# zeroed after every completed call, so one buffer serves all later calls
-# issued on the same stream.
+# Workspaces kept per (device, stream); calls on one stream run one at a time,
+# so they can share one buffer.
 _WORKSPACES: Dict[Tuple[int, int], torch.Tensor] = {}
 
 
@@ -117,9 +116,16 @@ def _workspace(device: torch.device, stream_handle: int, nbytes: int) -> Tuple[O
     key = (device.index if device.index is not None else torch.cuda.current_device(), stream_handle)
     ws = _WORKSPACES.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
         _WORKSPACES[key] = ws
     return ws.data_ptr(), ws.numel()
+
+
+def profile_next_decode(start: "torch.cuda.Event", stop: "torch.cuda.Event") -> None:
+    """Have the next decode call on this thread record `start`/`stop` around its
+    streaming kernel (kvc_profile_next_decode).  The events must exist already
+    (record them once before the first use)."""
+    _lib.load().kvc_profile_next_decode(start.cuda_event, stop.cuda_event)
 
 
 def _decode_args(q, out):

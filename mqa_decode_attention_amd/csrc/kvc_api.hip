@@ -16,6 +16,8 @@
 namespace {
 
 thread_local char g_last_error[512] = "";
+thread_local hipEvent_t g_prof_start = nullptr;   // one-shot timing events (kvc_profile_next_decode)
+thread_local hipEvent_t g_prof_stop = nullptr;
 
 kvc_status fail(kvc_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 
@@ -98,14 +100,9 @@ bool plan_decode(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_l
     pl.split_tokens = ts;
     pl.n_splits = (L + ts - 1) / ts;
     if (pl.n_splits > 1) {
-        if (units > kMaxUnits) {
-            *why = "more than 65536 (sequence, KV head, head chunk) units need splitting";
-            return false;
-        }
         const size_t bh = static_cast<size_t>(B) * H_q;
-        pl.ws_count = 0;
-        pl.ws_ml = kCounterBytes;
-        pl.ws_part = align_up(pl.ws_ml + bh * pl.n_splits * sizeof(float2), 256);
+        pl.ws_ml = 0;
+        pl.ws_part = align_up(bh * pl.n_splits * sizeof(float2), 256);
         pl.ws_bytes = align_up(pl.ws_part + bh * pl.n_splits * d * sizeof(float), 256);
     }
     *plan = pl;
@@ -131,6 +128,11 @@ const char* kvc_status_string(int status) {
 }
 
 const char* kvc_last_error(void) { return g_last_error; }
+
+void kvc_profile_next_decode(void* start_event, void* stop_event) {
+    g_prof_start = static_cast<hipEvent_t>(start_event);
+    g_prof_stop = static_cast<hipEvent_t>(stop_event);
+}
 
 kvc_status kvc_append(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
                       void* k_cache, void* v_cache, int T_max,
@@ -191,6 +193,8 @@ kvc_status decode_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const
                          const int32_t* block_table, int max_blocks_per_seq,
                          const int32_t* seq_lens, int max_seq_len, float scale, void* out,
                          int split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+    const hipEvent_t ev0 = g_prof_start, ev1 = g_prof_stop;   // one-shot, cleared by every call
+    g_prof_start = g_prof_stop = nullptr;
     kvc_status st = check_heads(dtype, B, H_q, H_kv, d);
     if (st != KVC_OK) return st;
     const bool paged = block_table != nullptr;
@@ -229,7 +233,6 @@ kvc_status decode_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const
     char* ws = static_cast<char*>(workspace);
     p.ws_part = pl.ws_bytes ? reinterpret_cast<float*>(ws + pl.ws_part) : nullptr;
     p.ws_ml = pl.ws_bytes ? reinterpret_cast<float2*>(ws + pl.ws_ml) : nullptr;
-    p.ws_count = pl.ws_bytes ? reinterpret_cast<int*>(ws + pl.ws_count) : nullptr;
     p.B = B; p.H_q = H_q; p.H_kv = H_kv; p.G = H_q / H_kv; p.n_chunks = pl.n_chunks;
     p.T_max = T_max; p.block_size = block_size; p.max_blocks_per_seq = max_blocks_per_seq;
     p.num_blocks = num_blocks;
@@ -238,8 +241,22 @@ kvc_status decode_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const
     p.n_wg_pad = static_cast<int>((n_wg + 7) / 8 * 8);
     const float sc = scale > 0.0f ? scale : 1.0f / sqrtf(static_cast<float>(d));
     p.scale_log2 = sc * 1.4426950408889634f;
-    return hip_status(kvc::launch_decode(dtype, d, pl.heads_per_wg, paged, p, static_cast<hipStream_t>(stream)),
-                      "decode launch");
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (ev0) {
+        const hipError_t e = hipEventRecord(ev0, hs);
+        if (e != hipSuccess) return hip_status(e, "profiling start event");
+    }
+    hipError_t e = kvc::launch_decode_split(dtype, d, pl.heads_per_wg, paged, p, hs);
+    if (e != hipSuccess) return hip_status(e, "decode split launch");
+    if (ev1) {
+        e = hipEventRecord(ev1, hs);
+        if (e != hipSuccess) return hip_status(e, "profiling stop event");
+    }
+    if (pl.n_splits > 1) {
+        e = kvc::launch_decode_merge(dtype, d, p, hs);
+        if (e != hipSuccess) return hip_status(e, "decode merge launch");
+    }
+    return ok();
 }
 
 }  // namespace

@@ -19,10 +19,11 @@
 //  * Scores: bf16 dot2 (two products per instruction, float32 accumulation)
 //    summed over the LPT lanes of a row with DPP.  Softmax is online in the
 //    log2 domain: running max m, running sum l, rescaled weighted-value sums.
-//  * Waves merge through LDS.  A single split writes the output; otherwise the
-//    split writes (m, l, acc) to the workspace and the last workgroup of its
-//    (sequence, KV head, chunk) to arrive - found with an atomic counter -
-//    merges all splits by their log-sum-exp and writes the output.
+//  * Waves merge through LDS.  A single split writes the output; otherwise each
+//    split writes (m, l, acc) to the workspace and a second, small kernel
+//    merges the splits of every (sequence, query head) by their log-sum-exp.
+//    (Merging inside the split kernel would need an agent-scope release per
+//    workgroup, an L2 write-back that measured far slower than a launch.)
 //  * Paged caches: token t of sequence b is read from block
 //    table[b][t / block_size], offset t % block_size (PagedKVCache listing,
 //    youngju.dev; section 4 of the tveniu.com guide).  A 16-token block of one
@@ -118,23 +119,14 @@ decode_split_kernel(const DecodeParams p) {
     constexpr int TILE = U * TPW;  // tokens per wave iteration
     constexpr int NT = NW * 64;
 
-    // The wave merge (sm_acc) and the split merge (sm_w, sm_lw) never overlap in
-    // time (a barrier separates them), so they share one LDS buffer.
-    constexpr int kWaveFloats = NW * GC * D;
-    constexpr int kSplitFloats = 2 * GC * kMaxSplits;
-    __shared__ float smem[kWaveFloats > kSplitFloats ? kWaveFloats : kSplitFloats];
+    __shared__ float sm_acc[NW][GC][D];
     __shared__ float sm_m[NW][GC];
     __shared__ float sm_l[NW][GC];
-    __shared__ float sm_red[GC];
-    __shared__ int sm_last;
-    float (*sm_acc)[GC][D] = reinterpret_cast<float (*)[GC][D]>(smem);
-    float (*sm_w)[kMaxSplits] = reinterpret_cast<float (*)[kMaxSplits]>(smem);
-    float (*sm_lw)[kMaxSplits] = reinterpret_cast<float (*)[kMaxSplits]>(smem + GC * kMaxSplits);
 
     const int wid = xcd_logical_id(blockIdx.x, p.n_wg, p.n_wg_pad);
     if (wid < 0) return;
     const int split = wid % p.n_splits;
-    const int unit = wid / p.n_splits;          // (b, j, chunk)
+    const int unit = wid / p.n_splits;          // (b, j, chunk): one query-head chunk of one group
     const int chunk = unit % p.n_chunks;
     const int bj = unit / p.n_chunks;
     const int b = bj / p.H_kv;
@@ -278,58 +270,55 @@ decode_split_kernel(const DecodeParams p) {
             if (e == 0) p.ws_ml[bh * p.n_splits + split] = make_float2(M, Ls);
         }
     }
-    if (nsp == 1) return;
+}
 
-    // publish this split; the last workgroup of the unit to arrive merges all splits
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) sm_last = (atomicAdd(p.ws_count + unit, 1) == nsp - 1);
-    __syncthreads();
-    if (!sm_last) return;
-    __threadfence();
-
-    for (int idx = tid; idx < GC * nsp; idx += NT) {
-        const int g = idx / nsp;
-        const int sp = idx % nsp;
-        const float2 ml = p.ws_ml[(static_cast<size_t>(b) * p.H_q + h0 + g) * p.n_splits + sp];
-        sm_w[g][sp] = ml.x;
-        sm_lw[g][sp] = ml.y;
+// Merge of the splits of every (sequence, query head) by their log-sum-exp:
+// M = max_s m_s, w_s = 2^(m_s - M), out = sum_s w_s acc_s / sum_s w_s l_s.
+// One wave per (sequence, query head); lanes stride over head_dim.
+template <typename T, int D>
+__global__ void __launch_bounds__(256) decode_merge_kernel(const DecodeParams p) {
+    __shared__ float sm_w[4][kMaxSplits];
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const long long bh = static_cast<long long>(blockIdx.x) * 4 + wave;
+    if (bh >= static_cast<long long>(p.B) * p.H_q) return;
+    const int b = static_cast<int>(bh / p.H_q);
+    int L = p.seq_lens[b];
+    L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
+    int nsp = (L + p.split_tokens - 1) / p.split_tokens;
+    if (nsp <= 1) return;                        // written directly by the split kernel
+    const float2* ml = p.ws_ml + bh * p.n_splits;
+    float M = -INFINITY;
+    for (int sp = lane; sp < nsp; sp += 64) M = fmaxf(M, ml[sp].x);
+    M = across_groups_max<1>(M);
+    float Ls = 0.0f;
+    for (int sp = lane; sp < nsp; sp += 64) {
+        const float2 v = ml[sp];
+        const float w = (v.x == -INFINITY) ? 0.0f : fast_exp2(v.x - M);
+        sm_w[wave][sp] = w;
+        Ls = fmaf(w, v.y, Ls);
     }
-    __syncthreads();
-    for (int g = wave; g < GC; g += NW) {           // per-head maximum over splits
-        float M = -INFINITY;
-        for (int sp = lane; sp < nsp; sp += 64) M = fmaxf(M, sm_w[g][sp]);
-        M = across_groups_max<1>(M);
-        if (lane == 0) sm_red[g] = M;
+    Ls = across_groups_sum<1>(Ls);
+    __builtin_amdgcn_wave_barrier();   // sm_w[wave] is private to this wave
+    const float* part = p.ws_part + bh * p.n_splits * D;
+    const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
+    constexpr int EPT = (D + 63) / 64;
+    float acc[EPT];
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) acc[k] = 0.0f;
+    for (int sp = 0; sp < nsp; ++sp) {
+        const float w = sm_w[wave][sp];
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) {
+            const int e = lane + 64 * k;
+            if (e < D) acc[k] = fmaf(w, part[static_cast<size_t>(sp) * D + e], acc[k]);
+        }
     }
-    __syncthreads();
-    for (int idx = tid; idx < GC * nsp; idx += NT) {
-        const int g = idx / nsp;
-        const int sp = idx % nsp;
-        const float mw = sm_w[g][sp];
-        const float f = (mw == -INFINITY) ? 0.0f : fast_exp2(mw - sm_red[g]);
-        sm_w[g][sp] = f;
-        sm_lw[g][sp] *= f;
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+        const int e = lane + 64 * k;
+        if (e < D) store_out<T>(p.out, static_cast<size_t>(bh) * D + e, Ls > 0.0f ? acc[k] * inv : 0.0f);
     }
-    __syncthreads();
-    for (int g = wave; g < GC; g += NW) {           // per-head total weight
-        float Ls = 0.0f;
-        for (int sp = lane; sp < nsp; sp += 64) Ls += sm_lw[g][sp];
-        Ls = across_groups_sum<1>(Ls);
-        if (lane == 0) sm_red[g] = Ls;
-    }
-    __syncthreads();
-    for (int idx = tid; idx < GC * D; idx += NT) {
-        const int g = idx / D;
-        const int e = idx % D;
-        const size_t bh = static_cast<size_t>(b) * p.H_q + h0 + g;
-        const float* part = p.ws_part + bh * p.n_splits * D + e;
-        float A = 0.0f;
-        for (int sp = 0; sp < nsp; ++sp) A = fmaf(sm_w[g][sp], part[static_cast<size_t>(sp) * D], A);
-        const float Ls = sm_red[g];
-        store_out<T>(p.out, bh * D + e, Ls > 0.0f ? A / Ls : 0.0f);
-    }
-    if (tid == 0) p.ws_count[unit] = 0;   // ready for the next call
 }
 
 constexpr int kU = 4;
@@ -343,6 +332,26 @@ hipError_t launch_tdg(bool paged, const DecodeParams& p, hipStream_t stream) {
     else
         hipLaunchKernelGGL((decode_split_kernel<T, D, GC, kU, kNW, false>), grid, block, 0, stream, p);
     return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_merge_td(const DecodeParams& p, hipStream_t stream) {
+    const long long waves = static_cast<long long>(p.B) * p.H_q;
+    const dim3 grid(static_cast<unsigned>((waves + 3) / 4)), block(256);
+    hipLaunchKernelGGL((decode_merge_kernel<T, D>), grid, block, 0, stream, p);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_merge_t(int d, const DecodeParams& p, hipStream_t stream) {
+    switch (d) {
+        case 16: return launch_merge_td<T, 16>(p, stream);
+        case 32: return launch_merge_td<T, 32>(p, stream);
+        case 64: return launch_merge_td<T, 64>(p, stream);
+        case 128: return launch_merge_td<T, 128>(p, stream);
+        case 256: return launch_merge_td<T, 256>(p, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 template <typename T, int D>
@@ -382,10 +391,15 @@ int decode_tile_tokens(kvc_dtype dtype, int d) {
     return kU * (64 / (d / epl)) * kNW;
 }
 
-hipError_t launch_decode(kvc_dtype dtype, int d, int heads_per_wg, bool paged,
-                         const DecodeParams& p, hipStream_t stream) {
+hipError_t launch_decode_split(kvc_dtype dtype, int d, int heads_per_wg, bool paged,
+                               const DecodeParams& p, hipStream_t stream) {
     if (dtype == KVC_BF16) return launch_t<uint16_t>(d, heads_per_wg, paged, p, stream);
     return launch_t<float>(d, heads_per_wg, paged, p, stream);
+}
+
+hipError_t launch_decode_merge(kvc_dtype dtype, int d, const DecodeParams& p, hipStream_t stream) {
+    if (dtype == KVC_BF16) return launch_merge_t<uint16_t>(d, p, stream);
+    return launch_merge_t<float>(d, p, stream);
 }
 
 }  // namespace kvc

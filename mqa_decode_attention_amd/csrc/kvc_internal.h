@@ -38,22 +38,14 @@ struct DecodePlan {
     int n_chunks;       // G / heads_per_wg
     int split_tokens;   // tokens per split
     int n_splits;       // splits of the longest sequence (>= 1)
-    size_t ws_part;     // byte offsets inside the workspace
-    size_t ws_ml;
-    size_t ws_count;
+    size_t ws_ml;       // byte offsets inside the workspace
+    size_t ws_part;
     size_t ws_bytes;    // 0 when n_splits == 1
 };
 
 // Largest split count the merge step supports (partials live in LDS).
 constexpr int kMaxSplits = 256;
 
-// The arrival counters sit in a fixed region at the start of every workspace,
-// one int per (sequence, KV head, head chunk), and partial results are only
-// ever written after it.  A counter is therefore never overwritten by another
-// call's partials, and a buffer reused across calls of any shape keeps every
-// counter at zero between calls.
-constexpr int kMaxUnits = 1 << 16;
-constexpr size_t kCounterBytes = sizeof(int) * kMaxUnits;
 
 struct DecodeParams {
     const void* q;
@@ -64,7 +56,6 @@ struct DecodeParams {
     const int32_t* block_table;  // NULL => contiguous
     float* ws_part;              // [B*H_q, n_splits, d]   weighted-value partials
     float2* ws_ml;               // [B*H_q, n_splits]      (running max (log2), sum)
-    int* ws_count;               // [B*H_kv*n_chunks]     arrival counters
     int B, H_q, H_kv, G, n_chunks;
     int T_max, block_size, max_blocks_per_seq, num_blocks;
     int max_seq_len, split_tokens, n_splits;
@@ -83,7 +74,11 @@ bool decode_supported(kvc_dtype dtype, int d, int heads_per_wg);
 // multiple of this unless the caller fixes them).
 int decode_tile_tokens(kvc_dtype dtype, int d);
 
-hipError_t launch_decode(kvc_dtype dtype, int d, int heads_per_wg, bool paged,
-                         const DecodeParams& p, hipStream_t stream);
+// The streaming kernel: one workgroup per (sequence, KV head, chunk, split).
+hipError_t launch_decode_split(kvc_dtype dtype, int d, int heads_per_wg, bool paged,
+                               const DecodeParams& p, hipStream_t stream);
+
+// The log-sum-exp merge of the splits (only when n_splits > 1).
+hipError_t launch_decode_merge(kvc_dtype dtype, int d, const DecodeParams& p, hipStream_t stream);
 
 }  // namespace kvc

@@ -198,10 +198,10 @@ def test_full_size_sampled(name):
 
 
 def test_workspace_reuse_across_shapes():
-    """One workspace shared by calls of different shapes (regression: arrival
-    counters must never sit where an earlier call left partial results)."""
+    """One workspace buffer shared by calls of different shapes, filled with
+    garbage first: no call may depend on what an earlier call left in it."""
     import mqa_decode_attention_amd as kvc
-    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    ws = torch.full((64 << 20,), 0x7F, dtype=torch.uint8, device="cuda")
     cases = [SMALL["long_gqa"], SMALL["mqa_ragged"], SMALL["gqa_8b"], SMALL["long_gqa"]]
     for i, w in enumerate(cases):
         x = W.draw(w)
@@ -214,5 +214,3 @@ def test_workspace_reuse_across_shapes():
             torch.cuda.synchronize()
             k2, v2, q2 = oracle_append(x)
             compare_out(out, oracle_decode(x, k2, v2, q2), w.dtype, f"reuse {w.name} split={split}")
-    # every counter is back at zero
-    assert torch.count_nonzero(ws[: 256 << 10]) == 0
