@@ -4,8 +4,8 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gqa_8b]
 
 A step is the whole hot path over one batch: kvc_append (rotate and store the
-new key, store the value, rotate q) followed by kvc_decode_attn (all splits and
-their merge, one kernel).  Inputs are resident in HBM before timing starts.
+new key, store the value, rotate q) followed by kvc_decode_attn (the streaming
+split kernel and, when a sequence has several splits, the merge kernel).  Inputs are resident in HBM before timing starts.
 To keep the 256 MB Infinity Cache from serving the cache between steps, R
 replicas of the KV cache (R * bytes >= 2 GB) are used in turn.
 
