@@ -31,6 +31,7 @@ UNITS = {
     "kvc_api.hip": [],
     "kvc_append.hip": ["-ffp-contract=off"],
     "kvc_decode.hip": [],
+    "kvc_decode_mfma.hip": [],
 }
 
 

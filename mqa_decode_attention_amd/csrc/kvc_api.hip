@@ -74,14 +74,15 @@ bool plan_decode(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_l
                  int split_tokens, DecodePlan* plan, const char** why) {
     DecodePlan pl{};
     const int G = H_q / H_kv;
-    pl.heads_per_wg = heads_per_wg(G);
+    pl.mfma = decode_mfma_supported(dtype, d, G);
+    pl.heads_per_wg = pl.mfma ? G : heads_per_wg(G);
     pl.n_chunks = G / pl.heads_per_wg;
-    if (!decode_supported(dtype, d, pl.heads_per_wg)) {
+    if (!pl.mfma && !decode_supported(dtype, d, pl.heads_per_wg)) {
         *why = "no decode kernel for this dtype and head_dim (head_dim must be 16, 32, 64, 128 or 256)";
         return false;
     }
     const long long units = static_cast<long long>(B) * H_kv * pl.n_chunks;
-    const int tile = decode_tile_tokens(dtype, d);
+    const int tile = pl.mfma ? decode_mfma_tile_tokens() : decode_tile_tokens(dtype, d);
     const int L = std::max(max_seq_len, 1);
     int ts;
     if (split_tokens > 0) {
@@ -246,7 +247,8 @@ kvc_status decode_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const
         const hipError_t e = hipEventRecord(ev0, hs);
         if (e != hipSuccess) return hip_status(e, "profiling start event");
     }
-    hipError_t e = kvc::launch_decode_split(dtype, d, pl.heads_per_wg, paged, p, hs);
+    hipError_t e = pl.mfma ? kvc::launch_decode_mfma(d, p.G, paged, p, hs)
+                           : kvc::launch_decode_split(dtype, d, pl.heads_per_wg, paged, p, hs);
     if (e != hipSuccess) return hip_status(e, "decode split launch");
     if (ev1) {
         e = hipEventRecord(ev1, hs);

@@ -1,0 +1,322 @@
+// kvc_decode_mfma.hip - bf16 decode attention on the gfx950 matrix cores.
+//
+// Same contract as the split kernel in kvc_decode.hip (one workgroup per
+// (sequence, KV head, token split); split results merged by their log-sum-exp;
+// scores = scale * q . k and out = softmax-weighted V rows, per query head of
+// the group g(h) = floor(h / G) - "Grouped-query attention: berbagi KV head di
+// antara grup query", nalar.dev, section "Jumlah head menentukan batas grup"),
+// but both products of a 32-token tile run as v_mfma_f32_16x16x32_bf16:
+//
+//   S^T[t, g] = sum_d K[t, d] Q[g, d]        A = K rows (16 tokens x 32 d),
+//                                            B = Q^T (32 d x 16 heads)
+//   O^T[c, g] += sum_t V[t, c] P[g, t]       A = V^T (16 columns x 32 tokens),
+//                                            B = P^T (32 tokens x 16 heads)
+//
+// Operand layouts (16x16x32, wave64): an A operand gives lane l the 8 values of
+// row (l % 16) at reduction slots 8*(l/16) .. +7; a B operand gives lane l the 8
+// values of column (l % 16) at the same slots; the 4 results of lane l are rows
+// 4*(l/16) .. +3 of column (l % 16).  The reduction slots only have to agree
+// between A and B, so any fixed assignment of d (or of tokens) to slots works.
+//
+// * K rows go from HBM straight into the A operand with 16-byte loads.
+// * S^T leaves lane l with one query head (l % 16) and 8 tokens of the tile.
+//   That is exactly the B operand P^T of the second product once the tokens
+//   are mapped to slots as tok(q, e) = 4q + e (e < 4), 16 + 4q + (e - 4) (e >= 4),
+//   q = l / 16, so the probabilities never leave their lane.  The softmax
+//   rescale of O^T is lane-local too: O^T also keeps head (l % 16) in lane l.
+// * V rows are read with whole-row 16-byte loads, stored row-major in this
+//   wave's LDS slice, and read back transposed with ds_read_b64_tr_b16: inside
+//   each 16-lane group, output lane 4a+b receives element b of the 8-byte
+//   chunks addressed by lanes a, a+4, a+8, a+12.  Pointing source lane s at
+//   row tok(q, s/4 [+4]) and columns 16*nb + 4*(s % 4) .. +3 gives each lane 4
+//   tokens of one V column - the A operand V^T - with one instruction.
+// * Query heads beyond G are zero rows of the B operand; more than 16 heads use
+//   several 16-head blocks over the same K/V registers.
+// * The probabilities are rounded to bf16 for the second product; the running
+//   sum l adds those same rounded values, so numerator and denominator agree.
+
+#include "kvc_internal.h"
+#include "kvc_device.h"
+
+namespace kvc {
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ f32x4_t mfma16(const uint4& a, const uint4& b, const f32x4_t& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Two float32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v_t));
+}
+
+// Lanes l, l^16, l^32, l^48 hold the same query head: reduce over them.
+__device__ __forceinline__ float max_same_head(float x) {
+    x = fmaxf(x, __shfl_xor(x, 16, 64));
+    return fmaxf(x, __shfl_xor(x, 32, 64));
+}
+__device__ __forceinline__ float sum_same_head(float x) {
+    x += __shfl_xor(x, 16, 64);
+    return x + __shfl_xor(x, 32, 64);
+}
+
+template <int D, int HB, int NW, bool PAGED>
+__global__ void __launch_bounds__(NW * 64)
+decode_mfma_kernel(const DecodeParams p) {
+    constexpr int KK = D / 32;            // 32-wide d slices per 16-token block
+    constexpr int NB = D / 16;            // 16-column blocks of V
+    constexpr int TT = 32;                // tokens per wave tile
+    constexpr int ROWB = 2 * D + 32;      // LDS bytes per staged V row (padded: no bank conflicts)
+    constexpr int STAGE = TT * ROWB;      // LDS bytes per wave
+    constexpr int MERGE = NW * 16 * D * 4 + 2 * NW * 16 * 4;
+    __shared__ __attribute__((aligned(16))) char smem[NW * STAGE > MERGE ? NW * STAGE : MERGE];
+
+    const int wid = xcd_logical_id(blockIdx.x, p.n_wg, p.n_wg_pad);
+    if (wid < 0) return;
+    const int split = wid % p.n_splits;
+    const int unit = wid / p.n_splits;    // b * H_kv + j
+    const int b = unit / p.H_kv;
+    const int j = unit % p.H_kv;
+    const int G = p.G;
+
+    int L = p.seq_lens[b];
+    L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
+    int nsp = (L + p.split_tokens - 1) / p.split_tokens;
+    nsp = nsp < 1 ? 1 : nsp;
+    if (split >= nsp) return;
+    const int t_begin = split * p.split_tokens;
+    const int t_end = min(L, t_begin + p.split_tokens);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int r16 = lane & 15;            // row/column index inside the operand
+    const int q4 = lane >> 4;             // 16-lane group: reduction slots 8*q4 .. +7
+
+    // B operand Q^T: lane holds head 16*hb + r16, d = 32*kk + 8*q4 .. +7
+    uint4 qb[HB][KK];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+        const int g = 16 * hb + r16;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            qb[hb][kk] = make_uint4(0, 0, 0, 0);
+            if (g < G)
+                qb[hb][kk] = *reinterpret_cast<const uint4*>(
+                    static_cast<const uint16_t*>(p.q) + (static_cast<size_t>(b) * p.H_q + j * G + g) * D +
+                    32 * kk + 8 * q4);
+        }
+    }
+
+    float m[HB], l[HB];
+    f32x4_t o[HB][NB];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+        m[hb] = -INFINITY;
+        l[hb] = 0.0f;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) o[hb][nb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+
+    const uint16_t* kbase = static_cast<const uint16_t*>(p.k);
+    const uint16_t* vbase = static_cast<const uint16_t*>(p.v);
+    const size_t seq_off = PAGED ? 0 : (static_cast<size_t>(b) * p.H_kv + j) * p.T_max * D;
+    const int32_t* table = PAGED ? p.block_table + static_cast<size_t>(b) * p.max_blocks_per_seq : nullptr;
+    auto row_off = [&](int t) -> size_t {   // element offset of token t's row (t < L)
+        if constexpr (PAGED) {
+            int blk = table[t / p.block_size];
+            blk = blk < 0 ? 0 : (blk >= p.num_blocks ? p.num_blocks - 1 : blk);
+            return ((static_cast<size_t>(blk) * p.H_kv + j) * p.block_size + t % p.block_size) * D;
+        } else {
+            return seq_off + static_cast<size_t>(t) * D;
+        }
+    };
+
+    char* stage = smem + wave * STAGE;
+    constexpr int VROWS = 64 * 8 / D;     // V rows covered by one wave-wide 16-byte load
+    constexpr int VLOADS = TT / VROWS;
+    constexpr int LPR = D / 8;            // lanes per V row
+
+    for (int base = t_begin + wave * TT; base < t_end; base += NW * TT) {
+        // ---- issue all loads of the tile: K into A operands, V rows for staging
+        uint4 ka[2][KK];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            int t = base + 16 * kb + r16;
+            t = t < t_end ? t : t_end - 1;
+            const size_t off = row_off(t) + 8 * q4;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+                ka[kb][kk] = *reinterpret_cast<const uint4*>(kbase + off + 32 * kk);
+        }
+        uint4 vr[VLOADS];
+#pragma unroll
+        for (int i = 0; i < VLOADS; ++i) {
+            int t = base + VROWS * i + lane / LPR;
+            t = t < t_end ? t : t_end - 1;
+            vr[i] = *reinterpret_cast<const uint4*>(vbase + row_off(t) + 8 * (lane % LPR));
+        }
+
+        // ---- scores S^T = K Q^T, scaled to log2 units; tokens past t_end masked
+        float s[HB][8];
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) acc = mfma16(ka[kb][kk], qb[hb][kk], acc);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = base + 16 * kb + 4 * q4 + e;
+                    s[hb][4 * kb + e] = t < t_end ? acc[e] * p.scale_log2 : -INFINITY;
+                }
+            }
+
+        // ---- stage V rows in LDS (row-major, padded rows)
+#pragma unroll
+        for (int i = 0; i < VLOADS; ++i) {
+            const int r = VROWS * i + lane / LPR;
+            *reinterpret_cast<uint4*>(stage + r * ROWB + 16 * (lane % LPR)) = vr[i];
+        }
+
+        // ---- online softmax per head; P^T packed as the bf16 B operand
+        uint4 pb[HB];
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
+            float mt = s[hb][0];
+#pragma unroll
+            for (int e = 1; e < 8; ++e) mt = fmaxf(mt, s[hb][e]);
+            mt = max_same_head(mt);
+            const float m_new = fmaxf(m[hb], mt);
+            const float alpha = fast_exp2(m[hb] - m_new);
+            m[hb] = m_new;
+            float pr[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pr[e] = fast_exp2(s[hb][e] - m_new);
+            pb[hb].x = pack2_bf16(pr[0], pr[1]);
+            pb[hb].y = pack2_bf16(pr[2], pr[3]);
+            pb[hb].z = pack2_bf16(pr[4], pr[5]);
+            pb[hb].w = pack2_bf16(pr[6], pr[7]);
+            float ps = bf16_lo(pb[hb].x) + bf16_hi(pb[hb].x) + bf16_lo(pb[hb].y) + bf16_hi(pb[hb].y) +
+                       bf16_lo(pb[hb].z) + bf16_hi(pb[hb].z) + bf16_lo(pb[hb].w) + bf16_hi(pb[hb].w);
+            l[hb] = fmaf(l[hb], alpha, ps);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) o[hb][nb] *= alpha;
+        }
+
+        // ---- O^T += V^T P^T: V^T operands read transposed from LDS
+        const int s16 = lane & 15;
+        const char* src0 = stage + (4 * q4 + s16 / 4) * ROWB + 8 * (s16 % 4);
+        const char* src1 = src0 + 16 * ROWB;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src0 + 32 * nb));
+            const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src1 + 32 * nb));
+            uint4 va;
+            va.x = __builtin_bit_cast(uint2, lo).x;
+            va.y = __builtin_bit_cast(uint2, lo).y;
+            va.z = __builtin_bit_cast(uint2, hi).x;
+            va.w = __builtin_bit_cast(uint2, hi).y;
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb) o[hb][nb] = mfma16(va, pb[hb], o[hb][nb]);
+        }
+    }
+
+    // ---- merge the waves (LDS reused: all waves are past their loops)
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) l[hb] = sum_same_head(l[hb]);
+    __syncthreads();
+    float* sm_o = reinterpret_cast<float*>(smem);                 // [NW][16][D]
+    float* sm_m = sm_o + NW * 16 * D;                               // [NW][16]
+    float* sm_l = sm_m + NW * 16;                                   // [NW][16]
+    const int NT = NW * 64;
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+        const int g = 16 * hb + r16;          // this lane's head
+        // lane holds O^T[c][g] for c = 16*nb + 4*q4 + e
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sm_o[(wave * 16 + r16) * D + 16 * nb + 4 * q4 + e] = o[hb][nb][e];
+        if (q4 == 0) {
+            sm_m[wave * 16 + r16] = m[hb];
+            sm_l[wave * 16 + r16] = l[hb];
+        }
+        __syncthreads();
+        const int heads = min(16, G - 16 * hb);
+        for (int idx = tid; idx < heads * D; idx += NT) {
+            const int gh = idx / D;
+            const int c = idx % D;
+            float M = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w * 16 + gh]);
+            float A = 0.0f, Ls = 0.0f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const float mw = sm_m[w * 16 + gh];
+                const float f = (mw == -INFINITY) ? 0.0f : fast_exp2(mw - M);
+                A = fmaf(sm_o[(w * 16 + gh) * D + c], f, A);
+                Ls = fmaf(sm_l[w * 16 + gh], f, Ls);
+            }
+            const size_t bh = static_cast<size_t>(b) * p.H_q + j * G + 16 * hb + gh;
+            if (nsp == 1) {
+                static_cast<uint16_t*>(p.out)[bh * D + c] = f32_to_bf16_rne(Ls > 0.0f ? A / Ls : 0.0f);
+            } else {
+                p.ws_part[(bh * p.n_splits + split) * D + c] = A;
+                if (c == 0) p.ws_ml[bh * p.n_splits + split] = make_float2(M, Ls);
+            }
+        }
+        (void)g;
+        __syncthreads();
+    }
+}
+
+constexpr int kNWm = 4;
+
+template <int D, int HB>
+hipError_t launch_dh(bool paged, const DecodeParams& p, hipStream_t stream) {
+    const dim3 grid(p.n_wg_pad), block(kNWm * 64);
+    if (paged)
+        hipLaunchKernelGGL((decode_mfma_kernel<D, HB, kNWm, true>), grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL((decode_mfma_kernel<D, HB, kNWm, false>), grid, block, 0, stream, p);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(int G, bool paged, const DecodeParams& p, hipStream_t stream) {
+    if (G <= 16) return launch_dh<D, 1>(paged, p, stream);
+    return launch_dh<D, 2>(paged, p, stream);
+}
+
+}  // namespace
+
+bool decode_mfma_supported(kvc_dtype dtype, int d, int G) {
+    return dtype == KVC_BF16 && (d == 64 || d == 128 || d == 256) && G >= 1 && G <= 32;
+}
+
+int decode_mfma_tile_tokens() { return 32 * kNWm; }
+
+hipError_t launch_decode_mfma(int d, int G, bool paged, const DecodeParams& p, hipStream_t stream) {
+    switch (d) {
+        case 64: return launch_d<64>(G, paged, p, stream);
+        case 128: return launch_d<128>(G, paged, p, stream);
+        case 256: return launch_d<256>(G, paged, p, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace kvc

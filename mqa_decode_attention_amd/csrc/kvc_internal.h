@@ -34,6 +34,7 @@ hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 // Split-decode launch plan, a pure function of the sizes (no device query), so
 // that kvc_decode_workspace_bytes and the decode call always agree.
 struct DecodePlan {
+    bool mfma;          // matrix-core kernel (bf16) rather than the vector kernel
     int heads_per_wg;   // query heads one workgroup serves (a divisor of G)
     int n_chunks;       // G / heads_per_wg
     int split_tokens;   // tokens per split
@@ -77,6 +78,12 @@ int decode_tile_tokens(kvc_dtype dtype, int d);
 // The streaming kernel: one workgroup per (sequence, KV head, chunk, split).
 hipError_t launch_decode_split(kvc_dtype dtype, int d, int heads_per_wg, bool paged,
                                const DecodeParams& p, hipStream_t stream);
+
+// The matrix-core streaming kernel (bf16; head_dim 64/128/256; G <= 32): one
+// workgroup per (sequence, KV head, split) serves all G query heads.
+bool decode_mfma_supported(kvc_dtype dtype, int d, int G);
+int decode_mfma_tile_tokens();
+hipError_t launch_decode_mfma(int d, int G, bool paged, const DecodeParams& p, hipStream_t stream);
 
 // The log-sum-exp merge of the splits (only when n_splits > 1).
 hipError_t launch_decode_merge(kvc_dtype dtype, int d, const DecodeParams& p, hipStream_t stream);

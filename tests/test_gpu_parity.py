@@ -214,3 +214,26 @@ def test_workspace_reuse_across_shapes():
             torch.cuda.synchronize()
             k2, v2, q2 = oracle_append(x)
             compare_out(out, oracle_decode(x, k2, v2, q2), w.dtype, f"reuse {w.name} split={split}")
+
+
+GROUP_CASES = [
+    # (H_q, H_kv, d, dtype): MHA, odd and large groups, every head_dim, both dtypes
+    (8, 8, 128, "bf16"), (12, 4, 128, "bf16"), (16, 1, 128, "bf16"), (24, 1, 128, "bf16"),
+    (48, 2, 128, "bf16"), (8, 2, 64, "bf16"), (8, 2, 256, "bf16"), (64, 2, 256, "bf16"),
+    (8, 2, 32, "bf16"), (4, 4, 16, "bf16"), (16, 4, 128, "f32"), (6, 2, 16, "f32"), (64, 2, 64, "f32"),
+]
+
+
+@pytest.mark.parametrize("H_q,H_kv,d,dtype", GROUP_CASES)
+def test_group_shapes(H_q, H_kv, d, dtype):
+    w = W.Workload("groups", 21, B=3, H_q=H_q, H_kv=H_kv, d=d, dtype=dtype, cached_lo=90, cached_hi=700,
+                   T_max=704)
+    x = W.draw(w)
+    say(f"[groups] H_q={H_q} H_kv={H_kv} d={d} {dtype} lens={x.seq_lens.tolist()}")
+    step = GpuStep(x)
+    step.append()
+    torch.cuda.synchronize()
+    k2, v2, q2 = _check_append(step, x)
+    ref = oracle_decode(x, k2, v2, q2)
+    for split in (0, 96, 1 << 20):
+        compare_out(step.decode(split_tokens=split), ref, dtype, f"G={H_q // H_kv} d={d} {dtype} split={split}")
