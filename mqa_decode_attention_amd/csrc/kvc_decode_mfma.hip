@@ -32,8 +32,10 @@
 //   tokens of one V column - the A operand V^T - with one instruction.
 // * Query heads beyond G are zero rows of the B operand; more than 16 heads use
 //   several 16-head blocks over the same K/V registers.
-// * The probabilities are rounded to bf16 for the second product; the running
-//   sum l adds those same rounded values, so numerator and denominator agree.
+// * The probabilities enter the second product as a pair of bf16 operands
+//   (hi = bf16(p), lo = bf16(p - hi)), two MFMAs, so p carries about 16
+//   significant bits: rounding p once to bf16 alone would leave errors of a
+//   few 1e-4 in the output, enough to move it across a bf16 rounding boundary.
 
 #include "kvc_internal.h"
 #include "kvc_device.h"
@@ -192,8 +194,9 @@ decode_mfma_kernel(const DecodeParams p) {
             *reinterpret_cast<uint4*>(stage + r * ROWB + 16 * (lane % LPR)) = vr[i];
         }
 
-        // ---- online softmax per head; P^T packed as the bf16 B operand
-        uint4 pb[HB];
+        // ---- online softmax per head; P^T as two bf16 B operands, hi + lo = P
+        // to about 16 significant bits, so the weighted sum keeps float32 accuracy
+        uint4 ph[HB], pl[HB];
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb) {
             float mt = s[hb][0];
@@ -203,15 +206,20 @@ decode_mfma_kernel(const DecodeParams p) {
             const float m_new = fmaxf(m[hb], mt);
             const float alpha = fast_exp2(m[hb] - m_new);
             m[hb] = m_new;
-            float pr[8];
+            float pr[8], ps = 0.0f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pr[e] = fast_exp2(s[hb][e] - m_new);
-            pb[hb].x = pack2_bf16(pr[0], pr[1]);
-            pb[hb].y = pack2_bf16(pr[2], pr[3]);
-            pb[hb].z = pack2_bf16(pr[4], pr[5]);
-            pb[hb].w = pack2_bf16(pr[6], pr[7]);
-            float ps = bf16_lo(pb[hb].x) + bf16_hi(pb[hb].x) + bf16_lo(pb[hb].y) + bf16_hi(pb[hb].y) +
-                       bf16_lo(pb[hb].z) + bf16_hi(pb[hb].z) + bf16_lo(pb[hb].w) + bf16_hi(pb[hb].w);
+            for (int e = 0; e < 8; ++e) {
+                pr[e] = fast_exp2(s[hb][e] - m_new);
+                ps += pr[e];
+            }
+            uint32_t hi[4], lo[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                hi[i] = pack2_bf16(pr[2 * i], pr[2 * i + 1]);
+                lo[i] = pack2_bf16(pr[2 * i] - bf16_lo(hi[i]), pr[2 * i + 1] - bf16_hi(hi[i]));
+            }
+            ph[hb] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+            pl[hb] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
             l[hb] = fmaf(l[hb], alpha, ps);
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) o[hb][nb] *= alpha;
@@ -231,7 +239,10 @@ decode_mfma_kernel(const DecodeParams p) {
             va.z = __builtin_bit_cast(uint2, hi).x;
             va.w = __builtin_bit_cast(uint2, hi).y;
 #pragma unroll
-            for (int hb = 0; hb < HB; ++hb) o[hb][nb] = mfma16(va, pb[hb], o[hb][nb]);
+            for (int hb = 0; hb < HB; ++hb) {
+                o[hb][nb] = mfma16(va, ph[hb], o[hb][nb]);
+                o[hb][nb] = mfma16(va, pl[hb], o[hb][nb]);
+            }
         }
     }
 
