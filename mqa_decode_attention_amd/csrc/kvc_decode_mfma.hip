@@ -50,8 +50,13 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// The running max is moved only when a tile exceeds it by more than this many
+// powers of two (so weights stay <= 2^8 and rescales become rare).
+constexpr float kLazy = 8.0f;
 
 __device__ __forceinline__ f32x4_t mfma16(const uint4& a, const uint4& b, const f32x4_t& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -80,10 +85,13 @@ decode_mfma_kernel(const DecodeParams p) {
     constexpr int KK = D / 32;            // 32-wide d slices per 16-token block
     constexpr int NB = D / 16;            // 16-column blocks of V
     constexpr int TT = 32;                // tokens per wave tile
-    constexpr int ROWB = 2 * D + 32;      // LDS bytes per staged V row (padded: no bank conflicts)
-    constexpr int STAGE = TT * ROWB;      // LDS bytes per wave
-    constexpr int MERGE = NW * 16 * D * 4 + 2 * NW * 16 * 4;
-    __shared__ __attribute__((aligned(16))) char smem[NW * STAGE > MERGE ? NW * STAGE : MERGE];
+    constexpr int ROWB = 2 * D;           // LDS bytes per staged V row
+    constexpr int STAGE = TT * ROWB;      // LDS bytes of one V tile
+    // V tiles are double-buffered per wave; two separate arrays, so the
+    // compiler can tell the tile being read from the one being filled.
+    __shared__ __attribute__((aligned(16))) char vbuf0[NW * STAGE];
+    __shared__ __attribute__((aligned(16))) char vbuf1[NW * STAGE];
+    static_assert(NW * STAGE >= NW * 16 * D * 4 && NW * STAGE >= 2 * NW * 16 * 4, "merge area");
 
     const int wid = xcd_logical_id(blockIdx.x, p.n_wg, p.n_wg_pad);
     if (wid < 0) return;
@@ -146,32 +154,70 @@ decode_mfma_kernel(const DecodeParams p) {
         }
     };
 
-    char* stage = smem + wave * STAGE;
-    constexpr int VROWS = 64 * 8 / D;     // V rows covered by one wave-wide 16-byte load
+    constexpr int LPR = D / 8;            // 16-byte chunks (lanes) per V row
+    constexpr int VROWS = 64 / LPR;       // V rows per wave-wide 16-byte load
     constexpr int VLOADS = TT / VROWS;
-    constexpr int LPR = D / 8;            // lanes per V row
+    // Chunk u of tile row r sits at slot u ^ swz(r) of that row in LDS.  With
+    // this XOR swizzle the 16 lanes of a transposed read (4 rows x 32 bytes)
+    // hit 8 distinct 16-byte bank groups, without padding the rows.
+    auto swz = [](int r) { return (2 * r) & (LPR - 1); };
 
-    for (int base = t_begin + wave * TT; base < t_end; base += NW * TT) {
-        // ---- issue all loads of the tile: K into A operands, V rows for staging
-        uint4 ka[2][KK];
+    // Contiguous caches are read through buffer resources whose range ends at
+    // row t_end of this (sequence, KV head): rows past the split read as zeros
+    // without touching memory, so no clamping is needed.  Paged caches clamp
+    // the row to t_end - 1 (always a valid, finite row of this sequence).
+    const size_t rows_bytes = static_cast<size_t>(t_end) * D * 2;
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(kbase + seq_off), 0, static_cast<int>(rows_bytes), 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(vbase + seq_off), 0, static_cast<int>(rows_bytes), 0x00020000);
+
+    // K rows of a tile, straight into A operands (registers)
+    auto load_k = [&](int base, uint4 (&ka)[2][KK]) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            int t = base + 16 * kb + r16;
-            t = t < t_end ? t : t_end - 1;
-            const size_t off = row_off(t) + 8 * q4;
+            const int t = base + 16 * kb + r16;
+            if constexpr (PAGED) {
+                const size_t off = row_off(t < t_end ? t : t_end - 1) + 8 * q4;
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk)
-                ka[kb][kk] = *reinterpret_cast<const uint4*>(kbase + off + 32 * kk);
+                for (int kk = 0; kk < KK; ++kk)
+                    ka[kb][kk] = *reinterpret_cast<const uint4*>(kbase + off + 32 * kk);
+            } else {
+                const int off = (t * D + 8 * q4) * 2;
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk)
+                    ka[kb][kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, off + 64 * kk, 0, 0));
+            }
         }
-        uint4 vr[VLOADS];
+    };
+    // V rows of a tile, HBM -> LDS without passing through registers: lane l
+    // of load i fills LDS bytes [16 l, 16 l + 16) of that load's 1 KiB, i.e. row
+    // VROWS*i + l / LPR, slot l % LPR, so it fetches chunk (slot ^ swz(row)).
+    auto load_v = [&](int base, char* buf) {
+        char* wbuf = buf + wave * STAGE;
 #pragma unroll
         for (int i = 0; i < VLOADS; ++i) {
-            int t = base + VROWS * i + lane / LPR;
-            t = t < t_end ? t : t_end - 1;
-            vr[i] = *reinterpret_cast<const uint4*>(vbase + row_off(t) + 8 * (lane % LPR));
+            const int r = VROWS * i + lane / LPR;
+            const int u = (lane % LPR) ^ swz(r);
+            const int t = base + r;
+            lds_void_t* dst = (lds_void_t*)(wbuf + 1024 * i);
+            if constexpr (PAGED) {
+                const uint16_t* src = vbase + row_off(t < t_end ? t : t_end - 1) + 8 * u;
+                __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+            } else {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, dst, 16, (t * D + 8 * u) * 2, 0, 0, 0);
+            }
         }
+    };
 
-        // ---- scores S^T = K Q^T, scaled to log2 units; tokens past t_end masked
+    // transposed-read source of this lane: row tr_row (+16 for the upper half),
+    // columns 16*nb + 4*(s16 % 4) .. +3 = chunk 2*nb + (s16 % 4) / 2, half s16 & 1
+    const int s16 = lane & 15;
+    const int tr_row = 4 * q4 + s16 / 4;
+
+    auto compute_tile = [&](const uint4 (&ka)[2][KK], const char* buf, int base) {
+        const char* wbuf = buf + wave * STAGE;
+        // scores S^T = K Q^T, scaled to log2 units; tokens past t_end masked
         float s[HB][8];
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb)
@@ -187,15 +233,10 @@ decode_mfma_kernel(const DecodeParams p) {
                 }
             }
 
-        // ---- stage V rows in LDS (row-major, padded rows)
-#pragma unroll
-        for (int i = 0; i < VLOADS; ++i) {
-            const int r = VROWS * i + lane / LPR;
-            *reinterpret_cast<uint4*>(stage + r * ROWB + 16 * (lane % LPR)) = vr[i];
-        }
-
-        // ---- online softmax per head; P^T as two bf16 B operands, hi + lo = P
-        // to about 16 significant bits, so the weighted sum keeps float32 accuracy
+        // online softmax per head.  The reference max m is only moved when the
+        // tile max exceeds it by more than 2^kLazy (then O and l are rescaled);
+        // otherwise p = 2^(s - m) <= 2^kLazy, exact after the final division.
+        // P^T goes in as two bf16 B operands, hi + lo = p to ~16 significant bits.
         uint4 ph[HB], pl[HB];
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb) {
@@ -203,13 +244,19 @@ decode_mfma_kernel(const DecodeParams p) {
 #pragma unroll
             for (int e = 1; e < 8; ++e) mt = fmaxf(mt, s[hb][e]);
             mt = max_same_head(mt);
-            const float m_new = fmaxf(m[hb], mt);
-            const float alpha = fast_exp2(m[hb] - m_new);
-            m[hb] = m_new;
+            const bool move = mt > m[hb] + kLazy;
+            if (__any(move)) {
+                const float m_new = move ? mt : m[hb];
+                const float alpha = fast_exp2(m[hb] - m_new);
+                m[hb] = m_new;
+                l[hb] *= alpha;
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) o[hb][nb] *= alpha;
+            }
             float pr[8], ps = 0.0f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                pr[e] = fast_exp2(s[hb][e] - m_new);
+                pr[e] = fast_exp2(s[hb][e] - m[hb]);
                 ps += pr[e];
             }
             uint32_t hi[4], lo[4];
@@ -220,19 +267,18 @@ decode_mfma_kernel(const DecodeParams p) {
             }
             ph[hb] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
             pl[hb] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-            l[hb] = fmaf(l[hb], alpha, ps);
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) o[hb][nb] *= alpha;
+            l[hb] += ps;
         }
 
-        // ---- O^T += V^T P^T: V^T operands read transposed from LDS
-        const int s16 = lane & 15;
-        const char* src0 = stage + (4 * q4 + s16 / 4) * ROWB + 8 * (s16 % 4);
-        const char* src1 = src0 + 16 * ROWB;
+        // O^T += V^T P^T: V^T operands read transposed from LDS
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src0 + 32 * nb));
-            const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src1 + 32 * nb));
+            const int u = 2 * nb + (s16 % 4) / 2;
+            const int r0 = tr_row, r1 = tr_row + 16;
+            const char* a0 = wbuf + r0 * ROWB + 16 * (u ^ swz(r0)) + 8 * (s16 & 1);
+            const char* a1 = wbuf + r1 * ROWB + 16 * (u ^ swz(r1)) + 8 * (s16 & 1);
+            const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)a0);
+            const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)a1);
             uint4 va;
             va.x = __builtin_bit_cast(uint2, lo).x;
             va.y = __builtin_bit_cast(uint2, lo).y;
@@ -244,14 +290,40 @@ decode_mfma_kernel(const DecodeParams p) {
                 o[hb][nb] = mfma16(va, pl[hb], o[hb][nb]);
             }
         }
+    };
+
+    // Software pipeline: while one tile is computed, the next one's K rows
+    // (registers) and V rows (the other LDS buffer) are in flight.  The next
+    // tile is fetched unconditionally - past the split it reads zeros
+    // (contiguous: outside the buffer range, no memory traffic) or the clamped
+    // last row (paged) - so every path through the loop has the same loads in
+    // flight and the compiler waits only for the tile it is about to use.
+    uint4 ka0[2][KK], ka1[2][KK];
+    constexpr int kStep = NW * TT;
+    int base = t_begin + wave * TT;
+    if (base < t_end) {
+        load_k(base, ka0);
+        load_v(base, vbuf0);
+        for (;;) {
+            load_k(base + kStep, ka1);
+            load_v(base + kStep, vbuf1);
+            compute_tile(ka0, vbuf0, base);
+            base += kStep;
+            if (base >= t_end) break;
+            load_k(base + kStep, ka0);
+            load_v(base + kStep, vbuf0);
+            compute_tile(ka1, vbuf1, base);
+            base += kStep;
+            if (base >= t_end) break;
+        }
     }
 
     // ---- merge the waves (LDS reused: all waves are past their loops)
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) l[hb] = sum_same_head(l[hb]);
     __syncthreads();
-    float* sm_o = reinterpret_cast<float*>(smem);                 // [NW][16][D]
-    float* sm_m = sm_o + NW * 16 * D;                               // [NW][16]
+    float* sm_o = reinterpret_cast<float*>(vbuf0);                // [NW][16][D]
+    float* sm_m = reinterpret_cast<float*>(vbuf1);                // [NW][16]
     float* sm_l = sm_m + NW * 16;                                   // [NW][16]
     const int NT = NW * 64;
 #pragma unroll
