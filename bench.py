@@ -3,16 +3,17 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gqa_8b]
 
-A step is the whole hot path over one batch: kvc_append (rotate and store the
-new key, store the value, rotate q) followed by kvc_decode_attn (the streaming
-split kernel and, when a sequence has several splits, the merge kernel).  Inputs are resident in HBM before timing starts.
+A step is the whole hot path over one batch: kvc_decode_step, i.e. the append
+(rotate and store the new key, store the value, rotate q) and the attention of
+every query head over its group's cache (the streaming kernel, which also does
+the append, and, when a sequence has several splits, the merge kernel).  Inputs are resident in HBM before timing starts.
 To keep the 256 MB Infinity Cache from serving the cache between steps, R
 replicas of the KV cache (R * bytes >= 2 GB) are used in turn.
 
 Prints one JSON line: `value` is the algorithmic KV bytes one step must read
 (sum_b L_b * H_kv * d * 2 * 2 bytes) divided by the measured step time.
-`roofline` rates the streaming decode kernel alone (per-launch time from HIP
-events the library records around that kernel on its stream) against 8 TB/s.
+`roofline` rates the streaming kernel alone (per-launch time from HIP events the
+library attaches to that kernel's launch on its stream) against 8 TB/s.
 `cpu_baseline` is the CPU oracle timed on the host on the same inputs.
 """
 from __future__ import annotations
@@ -136,15 +137,14 @@ def main():
     out = torch.empty_like(q)
     torch.cuda.synchronize()
 
+    q_rot = torch.empty_like(q)
+
     def step(i, ev=None):
         r = i % R
-        kvc.append(ks[r], vs[r], pos, kn, vn, cos, sin, q=q, block_table=tbl)
-        if ev is not None:   # the library records these around its streaming kernel
+        if ev is not None:   # the library attaches these to its streaming kernel
             kvc.profile_next_decode(ev[0], ev[1])
-        if w.paged:
-            kvc.decode_attn_paged(q, ks[r], vs[r], tbl, lens, max_len, out=out, split_tokens=args.split_tokens)
-        else:
-            kvc.decode_attn(q, ks[r], vs[r], lens, max_len, out=out, split_tokens=args.split_tokens)
+        kvc.decode_step(q, ks[r], vs[r], pos, kn, vn, cos, sin, max_len, block_table=tbl, q_rot_out=q_rot,
+                        out=out, split_tokens=args.split_tokens)
 
     for i in range(args.warmup):
         step(i)
@@ -204,7 +204,7 @@ def main():
         "hbm_pct_step": round(100 * value / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "decode_split_kernel (streaming pass; the split merge is a separate small kernel)",
+                     "kernel": "decode_mfma_kernel (streaming pass with the fused append; the split merge is a separate small kernel)",
                      "bytes_per_launch": kv_bytes},
         "wall_s_timed": round(wall, 4),
     }

@@ -2,13 +2,15 @@
  * kvc.h - C ABI of libkvc: one autoregressive decode step of grouped-query
  * attention over a KV cache, on an AMD Instinct MI355X (gfx950).
  *
- * A decode step is two calls on one stream:
+ * A decode step is two operations on one stream:
  *   1. kvc_append: rotate the new token's key (RoPE) and store it, with the
  *      token's value, as one slice along the token axis of the cache; the same
  *      call can rotate the token's query in place.
  *   2. kvc_decode_attn / kvc_decode_attn_paged: every query head h attends over
  *      the cached keys/values of its group g(h) = floor(h / G), G = H_q / H_kv:
  *      O_h = softmax(q_h K_g(h)^T * scale) V_g(h).
+ * kvc_decode_step does both in one call (and, for the common shapes, in one
+ * streaming kernel).
  *
  * Definitions followed (page titles as published):
  *  - "Grouped-query attention: berbagi KV head di antara grup query" (nalar.dev),
@@ -76,9 +78,9 @@ const char* kvc_last_error(void);
 
 /*
  * Timing aid.  The next kvc_decode_attn / kvc_decode_attn_paged call made on
- * this thread records start_event on its stream just before launching its
- * streaming (split) kernel and stop_event just after it, so that
- * hipEventElapsedTime gives that kernel's duration.  Both are hipEvent_t
+ * this thread launches its streaming (split) kernel with start_event and
+ * stop_event attached (hipExtLaunchKernel), so the two events bracket exactly
+ * that kernel and hipEventElapsedTime gives its duration.  Both are hipEvent_t
  * handles owned by the caller (or NULL).  One-shot: the next decode call, even
  * a failing one, clears them.
  */
@@ -171,6 +173,36 @@ kvc_status kvc_decode_attn_paged(kvc_dtype dtype, int B, int H_q, int H_kv, int 
                                  int max_blocks_per_seq, const int32_t* seq_lens,
                                  int max_seq_len, float scale, void* out, int split_tokens,
                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kvc_decode_step - one whole decode step: kvc_append followed by the
+ * attention of the new token, as one call.
+ *
+ * Same result as kvc_append(..., q_inout = copy of q ...) followed by
+ * kvc_decode_attn[_paged] with seq_lens[b] = positions[b] + 1, bit for bit:
+ * the new token's key is rotated and stored with its value at slot
+ * positions[b], the query is rotated at the same position (written to
+ * q_rot_out), and every query head attends over the positions[b] + 1 cached
+ * tokens, the new one included.  For bf16 with head_dim 64/128/256 and
+ * G <= 32 the append runs inside the streaming attention kernel (the
+ * workgroup holding the new token stores it before reading it; q is rotated
+ * in registers); other shapes run the append kernel first.
+ *
+ * q is the raw query [B, H_q, d] (not modified); q_rot_out [B, H_q, d]
+ * (required) receives the rotated query.  Cache arguments as in kvc_append
+ * (block_table == NULL: contiguous [B, H_kv, T_max, d]; else paged pools).
+ * max_seq_len must be >= every positions[b] + 1; a position outside the cache
+ * or the rotation table writes nothing and gives zeros for that sequence.
+ * Workspace as for kvc_decode_attn (kvc_decode_workspace_bytes with the same
+ * sizes and max_seq_len).
+ */
+kvc_status kvc_decode_step(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
+                           const void* q, void* q_rot_out, void* k_cache, void* v_cache, int T_max,
+                           const int32_t* block_table, int block_size, int max_blocks_per_seq,
+                           int num_blocks, const int32_t* positions, const void* k_new,
+                           const void* v_new, const float* rope_cos, const float* rope_sin,
+                           int rope_rows, int rope_style, int max_seq_len, float scale, void* out,
+                           int split_tokens, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

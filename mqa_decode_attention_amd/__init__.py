@@ -6,7 +6,8 @@ include/kvc.h); this package only marshals torch tensors into it:
     append(k_cache, v_cache, positions, k_new, v_new, rope_cos, rope_sin, q=..., block_table=...)
     decode_attn(q, k_cache, v_cache, seq_lens, max_seq_len)
     decode_attn_paged(q, k_pool, v_pool, block_table, seq_lens, max_seq_len)
+    decode_step(q, k_cache, v_cache, positions, k_new, v_new, rope_cos, rope_sin, max_seq_len, ...)
 """
 from .api import (KVC_BF16, KVC_F32, KvcError, append, decode_attn, decode_attn_paged,  # noqa: F401
-                  profile_next_decode, workspace_bytes)
+                  decode_step, profile_next_decode, workspace_bytes)
 from ._lib import LIB_PATH, load  # noqa: F401

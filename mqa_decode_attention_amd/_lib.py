@@ -34,6 +34,12 @@ SIGNATURES = {
                                       c_int, c_int, c_void_p, c_int, c_void_p,
                                       c_int, c_float, c_void_p, c_int,
                                       c_void_p, c_size_t, c_void_p]),
+    "kvc_decode_step": (c_int, [c_int, c_int, c_int, c_int, c_int,
+                                c_void_p, c_void_p, c_void_p, c_void_p, c_int,
+                                c_void_p, c_int, c_int, c_int, c_void_p,
+                                c_void_p, c_void_p, c_void_p, c_void_p,
+                                c_int, c_int, c_int, c_float, c_void_p,
+                                c_int, c_void_p, c_size_t, c_void_p]),
 }
 
 ABI_VERSION = 1

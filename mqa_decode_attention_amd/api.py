@@ -184,3 +184,48 @@ def decode_attn_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tenso
         float(scale) if scale else 0.0, _dev(out, "out", q.dtype, (B, H_q, d)),
         int(split_tokens), ws, wsn, st))
     return out
+
+
+def decode_step(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                positions: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                rope_cos: torch.Tensor, rope_sin: torch.Tensor, max_seq_len: int,
+                block_table: Optional[torch.Tensor] = None, rope_style: str = "interleaved",
+                q_rot_out: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                scale: Optional[float] = None, split_tokens: int = 0,
+                workspace: Optional[torch.Tensor] = None, stream=None):
+    """kvc_decode_step: append the new token and attend, in one call.
+
+    q is the raw query (left unchanged); returns (out, q_rot_out).
+    """
+    lib = _lib.load()
+    dt, B, H_q, d, out = _decode_args(q, out)
+    H_kv = k_new.shape[1]
+    if q_rot_out is None:
+        q_rot_out = torch.empty_like(q)
+    if rope_cos.dim() != 2 or rope_cos.shape[1] != d // 2:
+        raise ValueError(f"rope_cos must be [rows, {d // 2}], got {tuple(rope_cos.shape)}")
+    if block_table is not None:
+        num_blocks, _, block_size, _ = k_cache.shape
+        T_max, mb = 0, block_table.shape[1]
+        tbl = _dev(block_table, "block_table", torch.int32, (B, mb))
+        shape = (num_blocks, H_kv, block_size, d)
+    else:
+        T_max = k_cache.shape[2]
+        tbl, block_size, mb, num_blocks = None, 0, 0, 0
+        shape = (B, H_kv, T_max, d)
+    st = _stream(q.device, stream)
+    need = workspace_bytes(q.dtype, B, H_q, H_kv, d, max_seq_len, split_tokens)
+    if workspace is not None:
+        ws, wsn = _dev(workspace, "workspace", torch.uint8), workspace.numel()
+    else:
+        ws, wsn = _workspace(q.device, st, need)
+    _check(lib.kvc_decode_step(
+        dt, B, H_q, H_kv, d, _dev(q, "q", q.dtype, (B, H_q, d)),
+        _dev(q_rot_out, "q_rot_out", q.dtype, (B, H_q, d)),
+        _dev(k_cache, "k_cache", q.dtype, shape), _dev(v_cache, "v_cache", q.dtype, shape), T_max,
+        tbl, block_size, mb, num_blocks, _dev(positions, "positions", torch.int32, (B,)),
+        _dev(k_new, "k_new", q.dtype, (B, H_kv, d)), _dev(v_new, "v_new", q.dtype, (B, H_kv, d)),
+        _dev(rope_cos, "rope_cos", torch.float32), _dev(rope_sin, "rope_sin", torch.float32, rope_cos.shape),
+        rope_cos.shape[0], ROPE_STYLES[rope_style], int(max_seq_len), float(scale) if scale else 0.0,
+        _dev(out, "out", q.dtype, (B, H_q, d)), int(split_tokens), ws, wsn, st))
+    return out, q_rot_out

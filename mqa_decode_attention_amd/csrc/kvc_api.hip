@@ -189,11 +189,24 @@ size_t kvc_decode_workspace_bytes(kvc_dtype dtype, int B, int H_q, int H_kv, int
 
 namespace {
 
+// The append half of kvc_decode_step (NULL for a plain decode call).
+struct StepArgs {
+    const int32_t* positions;
+    const void* k_new;
+    const void* v_new;
+    void* q_rot_out;
+    const float* rope_cos;
+    const float* rope_sin;
+    int rope_rows;
+    int rope_style;
+};
+
 kvc_status decode_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const void* q,
                          const void* k, const void* v, int T_max, int num_blocks, int block_size,
                          const int32_t* block_table, int max_blocks_per_seq,
                          const int32_t* seq_lens, int max_seq_len, float scale, void* out,
-                         int split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+                         int split_tokens, void* workspace, size_t workspace_bytes, void* stream,
+                         const StepArgs* step) {
     const hipEvent_t ev0 = g_prof_start, ev1 = g_prof_stop;   // one-shot, cleared by every call
     g_prof_start = g_prof_stop = nullptr;
     kvc_status st = check_heads(dtype, B, H_q, H_kv, d);
@@ -210,9 +223,18 @@ kvc_status decode_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const
     } else if (max_seq_len > T_max) {
         return fail(KVC_ERR_SHAPE, "max_seq_len %d exceeds the cache capacity T_max %d", max_seq_len, T_max);
     }
+    if (step) {
+        if (d % 2 != 0) return fail(KVC_ERR_SHAPE, "head_dim %d must be even for the rotation", d);
+        if (step->rope_style != KVC_ROPE_INTERLEAVED && step->rope_style != KVC_ROPE_HALF)
+            return fail(KVC_ERR_UNSUPPORTED, "unknown rope_style %d", step->rope_style);
+        if (step->rope_rows <= 0) return fail(KVC_ERR_SHAPE, "rope_rows must be positive");
+    }
     if (B == 0) return ok();
-    if (!q || !k || !v || !seq_lens || !out)
+    if (!q || !k || !v || !out || (!step && !seq_lens))
         return fail(KVC_ERR_NULL, "decode: a required pointer is NULL");
+    if (step && (!step->positions || !step->k_new || !step->v_new || !step->q_rot_out || !step->rope_cos ||
+                 !step->rope_sin))
+        return fail(KVC_ERR_NULL, "kvc_decode_step: a required pointer is NULL");
     kvc::DecodePlan pl;
     const char* why = nullptr;
     if (!kvc::plan_decode(dtype, B, H_q, H_kv, d, max_seq_len, split_tokens, &pl, &why))
@@ -243,17 +265,46 @@ kvc_status decode_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const
     const float sc = scale > 0.0f ? scale : 1.0f / sqrtf(static_cast<float>(d));
     p.scale_log2 = sc * 1.4426950408889634f;
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    if (ev0) {
-        const hipError_t e = hipEventRecord(ev0, hs);
-        if (e != hipSuccess) return hip_status(e, "profiling start event");
+    kvc::KernelTiming tm;
+    tm.start = ev0;
+    tm.stop = ev1;
+    hipError_t e = hipSuccess;
+    if (step) {
+        p.positions = step->positions;
+        p.k_new = step->k_new;
+        p.v_new = step->v_new;
+        p.q_raw = q;
+        p.q_rot_out = step->q_rot_out;
+        p.rope_cos = step->rope_cos;
+        p.rope_sin = step->rope_sin;
+        p.rope_rows = step->rope_rows;
+        p.rope_style = step->rope_style;
+        p.capacity = paged ? block_size * max_blocks_per_seq : T_max;
+        p.seq_lens = nullptr;
+        if (!pl.mfma) {
+            // no fused kernel for this shape: rotated q into q_rot_out, append, then attend
+            const size_t qbytes = static_cast<size_t>(B) * H_q * d * elem_bytes(dtype);
+            e = hipMemcpyAsync(step->q_rot_out, q, qbytes, hipMemcpyDeviceToDevice, hs);
+            if (e != hipSuccess) return hip_status(e, "kvc_decode_step query copy");
+            kvc::AppendParams ap{};
+            ap.dtype = dtype;
+            ap.B = B; ap.H_q = H_q; ap.H_kv = H_kv; ap.d = d;
+            ap.k_cache = const_cast<void*>(k); ap.v_cache = const_cast<void*>(v); ap.T_max = T_max;
+            ap.block_table = block_table; ap.block_size = block_size;
+            ap.max_blocks_per_seq = max_blocks_per_seq; ap.num_blocks = num_blocks;
+            ap.capacity = p.capacity;
+            ap.positions = step->positions;
+            ap.k_new = step->k_new; ap.v_new = step->v_new; ap.q_inout = step->q_rot_out;
+            ap.rope_cos = step->rope_cos; ap.rope_sin = step->rope_sin;
+            ap.rope_rows = step->rope_rows; ap.rope_style = step->rope_style;
+            e = kvc::launch_append(ap, hs);
+            if (e != hipSuccess) return hip_status(e, "kvc_decode_step append launch");
+            p.q = step->q_rot_out;
+        }
     }
-    hipError_t e = pl.mfma ? kvc::launch_decode_mfma(d, p.G, paged, p, hs)
-                           : kvc::launch_decode_split(dtype, d, pl.heads_per_wg, paged, p, hs);
+    e = pl.mfma ? kvc::launch_decode_mfma(d, p.G, paged, step != nullptr, p, hs, tm)
+                : kvc::launch_decode_split(dtype, d, pl.heads_per_wg, paged, p, hs, tm);
     if (e != hipSuccess) return hip_status(e, "decode split launch");
-    if (ev1) {
-        e = hipEventRecord(ev1, hs);
-        if (e != hipSuccess) return hip_status(e, "profiling stop event");
-    }
     if (pl.n_splits > 1) {
         e = kvc::launch_decode_merge(dtype, d, p, hs);
         if (e != hipSuccess) return hip_status(e, "decode merge launch");
@@ -271,7 +322,7 @@ kvc_status kvc_decode_attn(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
                            int split_tokens, void* workspace, size_t workspace_bytes,
                            void* stream) {
     return decode_common(dtype, B, H_q, H_kv, d, q, k_cache, v_cache, T_max, 0, 0, nullptr, 0, seq_lens,
-                         max_seq_len, scale, out, split_tokens, workspace, workspace_bytes, stream);
+                         max_seq_len, scale, out, split_tokens, workspace, workspace_bytes, stream, nullptr);
 }
 
 kvc_status kvc_decode_attn_paged(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
@@ -283,7 +334,23 @@ kvc_status kvc_decode_attn_paged(kvc_dtype dtype, int B, int H_q, int H_kv, int 
     if (!block_table) return fail(KVC_ERR_NULL, "kvc_decode_attn_paged: block_table is NULL");
     return decode_common(dtype, B, H_q, H_kv, d, q, k_pool, v_pool, 0, num_blocks, block_size, block_table,
                          max_blocks_per_seq, seq_lens, max_seq_len, scale, out, split_tokens, workspace,
-                         workspace_bytes, stream);
+                         workspace_bytes, stream, nullptr);
+}
+
+kvc_status kvc_decode_step(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
+                           const void* q, void* q_rot_out, void* k_cache, void* v_cache, int T_max,
+                           const int32_t* block_table, int block_size, int max_blocks_per_seq,
+                           int num_blocks, const int32_t* positions, const void* k_new,
+                           const void* v_new, const float* rope_cos, const float* rope_sin,
+                           int rope_rows, int rope_style, int max_seq_len, float scale, void* out,
+                           int split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+    StepArgs st{positions, k_new, v_new, q_rot_out, rope_cos, rope_sin, rope_rows, rope_style};
+    if (block_table)
+        return decode_common(dtype, B, H_q, H_kv, d, q, k_cache, v_cache, 0, num_blocks, block_size,
+                             block_table, max_blocks_per_seq, nullptr, max_seq_len, scale, out, split_tokens,
+                             workspace, workspace_bytes, stream, &st);
+    return decode_common(dtype, B, H_q, H_kv, d, q, k_cache, v_cache, T_max, 0, 0, nullptr, 0, nullptr,
+                         max_seq_len, scale, out, split_tokens, workspace, workspace_bytes, stream, &st);
 }
 
 }  // extern "C"

@@ -10,9 +10,9 @@
 //
 // The rotation of a pair (x0, x1) by (c, s) is the float32 sequence
 //   r0 = (x0*c) - (x1*s),  r1 = (x0*s) + (x1*c)
-// with every operation rounded on its own: this file is compiled with
-// -ffp-contract=off and the pragma below forbids fused multiply-adds, so the
-// stored bits are fixed by the inputs alone.
+// with every operation rounded on its own (rope_pair: no fused multiply-add;
+// this file is also compiled with -ffp-contract=off), so the stored bits are
+// fixed by the inputs alone.
 
 #include "kvc_internal.h"
 #include "kvc_device.h"
@@ -95,12 +95,8 @@ __global__ void __launch_bounds__(256) append_kernel(const AppendParams p) {
     }
     const float x0 = Store<T>::load(src, e0);
     const float x1 = Store<T>::load(src, e1);
-    const float a = x0 * c;
-    const float bb = x1 * s;
-    const float r0 = a - bb;
-    const float e = x0 * s;
-    const float f = x1 * c;
-    const float r1 = e + f;
+    float r0, r1;
+    rope_pair(x0, x1, c, s, r0, r1);
     Store<T>::store(dst, e0, r0);
     Store<T>::store(dst, e1, r1);
 }

@@ -132,8 +132,7 @@ decode_split_kernel(const DecodeParams p) {
     const int b = bj / p.H_kv;
     const int j = bj % p.H_kv;
 
-    int L = p.seq_lens[b];
-    L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
+    const int L = attended_len(p, b);
     int nsp = (L + p.split_tokens - 1) / p.split_tokens;
     nsp = nsp < 1 ? 1 : nsp;
     if (split >= nsp) return;
@@ -283,8 +282,7 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(const DecodeParams p)
     const long long bh = static_cast<long long>(blockIdx.x) * 4 + wave;
     if (bh >= static_cast<long long>(p.B) * p.H_q) return;
     const int b = static_cast<int>(bh / p.H_q);
-    int L = p.seq_lens[b];
-    L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
+    const int L = attended_len(p, b);
     int nsp = (L + p.split_tokens - 1) / p.split_tokens;
     if (nsp <= 1) return;                        // written directly by the split kernel
     const float2* ml = p.ws_ml + bh * p.n_splits;
@@ -325,13 +323,10 @@ constexpr int kU = 4;
 constexpr int kNW = 4;
 
 template <typename T, int D, int GC>
-hipError_t launch_tdg(bool paged, const DecodeParams& p, hipStream_t stream) {
+hipError_t launch_tdg(bool paged, const DecodeParams& p, hipStream_t stream, const KernelTiming& tm) {
     const dim3 grid(p.n_wg_pad), block(kNW * 64);
-    if (paged)
-        hipLaunchKernelGGL((decode_split_kernel<T, D, GC, kU, kNW, true>), grid, block, 0, stream, p);
-    else
-        hipLaunchKernelGGL((decode_split_kernel<T, D, GC, kU, kNW, false>), grid, block, 0, stream, p);
-    return hipGetLastError();
+    if (paged) return launch_timed(decode_split_kernel<T, D, GC, kU, kNW, true>, grid, block, stream, tm, p);
+    return launch_timed(decode_split_kernel<T, D, GC, kU, kNW, false>, grid, block, stream, tm, p);
 }
 
 template <typename T, int D>
@@ -355,24 +350,24 @@ hipError_t launch_merge_t(int d, const DecodeParams& p, hipStream_t stream) {
 }
 
 template <typename T, int D>
-hipError_t launch_td(int gc, bool paged, const DecodeParams& p, hipStream_t stream) {
+hipError_t launch_td(int gc, bool paged, const DecodeParams& p, hipStream_t stream, const KernelTiming& tm) {
     switch (gc) {
-        case 1: return launch_tdg<T, D, 1>(paged, p, stream);
-        case 2: return launch_tdg<T, D, 2>(paged, p, stream);
-        case 4: return launch_tdg<T, D, 4>(paged, p, stream);
-        case 8: return launch_tdg<T, D, 8>(paged, p, stream);
+        case 1: return launch_tdg<T, D, 1>(paged, p, stream, tm);
+        case 2: return launch_tdg<T, D, 2>(paged, p, stream, tm);
+        case 4: return launch_tdg<T, D, 4>(paged, p, stream, tm);
+        case 8: return launch_tdg<T, D, 8>(paged, p, stream, tm);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <typename T>
-hipError_t launch_t(int d, int gc, bool paged, const DecodeParams& p, hipStream_t stream) {
+hipError_t launch_t(int d, int gc, bool paged, const DecodeParams& p, hipStream_t stream, const KernelTiming& tm) {
     switch (d) {
-        case 16: return launch_td<T, 16>(gc, paged, p, stream);
-        case 32: return launch_td<T, 32>(gc, paged, p, stream);
-        case 64: return launch_td<T, 64>(gc, paged, p, stream);
-        case 128: return launch_td<T, 128>(gc, paged, p, stream);
-        case 256: return launch_td<T, 256>(gc, paged, p, stream);
+        case 16: return launch_td<T, 16>(gc, paged, p, stream, tm);
+        case 32: return launch_td<T, 32>(gc, paged, p, stream, tm);
+        case 64: return launch_td<T, 64>(gc, paged, p, stream, tm);
+        case 128: return launch_td<T, 128>(gc, paged, p, stream, tm);
+        case 256: return launch_td<T, 256>(gc, paged, p, stream, tm);
         default: return hipErrorInvalidValue;
     }
 }
@@ -392,9 +387,9 @@ int decode_tile_tokens(kvc_dtype dtype, int d) {
 }
 
 hipError_t launch_decode_split(kvc_dtype dtype, int d, int heads_per_wg, bool paged,
-                               const DecodeParams& p, hipStream_t stream) {
-    if (dtype == KVC_BF16) return launch_t<uint16_t>(d, heads_per_wg, paged, p, stream);
-    return launch_t<float>(d, heads_per_wg, paged, p, stream);
+                               const DecodeParams& p, hipStream_t stream, const KernelTiming& tm) {
+    if (dtype == KVC_BF16) return launch_t<uint16_t>(d, heads_per_wg, paged, p, stream, tm);
+    return launch_t<float>(d, heads_per_wg, paged, p, stream, tm);
 }
 
 hipError_t launch_decode_merge(kvc_dtype dtype, int d, const DecodeParams& p, hipStream_t stream) {

@@ -79,7 +79,7 @@ __device__ __forceinline__ float sum_same_head(float x) {
     return x + __shfl_xor(x, 32, 64);
 }
 
-template <int D, int HB, int NW, bool PAGED>
+template <int D, int HB, int NW, bool PAGED, bool FUSED>
 __global__ void __launch_bounds__(NW * 64)
 decode_mfma_kernel(const DecodeParams p) {
     constexpr int KK = D / 32;            // 32-wide d slices per 16-token block
@@ -101,8 +101,7 @@ decode_mfma_kernel(const DecodeParams p) {
     const int j = unit % p.H_kv;
     const int G = p.G;
 
-    int L = p.seq_lens[b];
-    L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
+    const int L = attended_len(p, b);
     int nsp = (L + p.split_tokens - 1) / p.split_tokens;
     nsp = nsp < 1 ? 1 : nsp;
     if (split >= nsp) return;
@@ -117,16 +116,58 @@ decode_mfma_kernel(const DecodeParams p) {
 
     // B operand Q^T: lane holds head 16*hb + r16, d = 32*kk + 8*q4 .. +7
     uint4 qb[HB][KK];
+    const int pos = L - 1;                // slot of the new token (fused step)
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
         const int g = 16 * hb + r16;
+        const size_t qoff = (static_cast<size_t>(b) * p.H_q + j * G + g) * D + 8 * q4;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
             qb[hb][kk] = make_uint4(0, 0, 0, 0);
             if (g < G)
                 qb[hb][kk] = *reinterpret_cast<const uint4*>(
-                    static_cast<const uint16_t*>(p.q) + (static_cast<size_t>(b) * p.H_q + j * G + g) * D +
-                    32 * kk + 8 * q4);
+                    static_cast<const uint16_t*>(FUSED ? p.q_raw : p.q) + qoff + 32 * kk);
+        }
+        if constexpr (FUSED) {
+            // rotate the raw query at the new token's position, exactly as the
+            // append kernel would (float32, one rounding per op, then bf16 RNE)
+            if (g < G && L > 0) {
+                const float* cs = p.rope_cos + static_cast<size_t>(pos) * (D / 2);
+                const float* sn = p.rope_sin + static_cast<size_t>(pos) * (D / 2);
+                if (p.rope_style == KVC_ROPE_HALF) {
+#pragma unroll
+                    for (int kk = 0; kk < KK / 2; ++kk) {
+                        uint32_t* x = reinterpret_cast<uint32_t*>(&qb[hb][kk]);
+                        uint32_t* y = reinterpret_cast<uint32_t*>(&qb[hb][kk + KK / 2]);
+#pragma unroll
+                        for (int w = 0; w < 4; ++w) {
+                            const int i = 32 * kk + 8 * q4 + 2 * w;     // pair indices i, i + 1
+                            float a0, a1, b0, b1;
+                            rope_pair(bf16_lo(x[w]), bf16_lo(y[w]), cs[i], sn[i], a0, b0);
+                            rope_pair(bf16_hi(x[w]), bf16_hi(y[w]), cs[i + 1], sn[i + 1], a1, b1);
+                            x[w] = pack_bf16x2(a0, a1);
+                            y[w] = pack_bf16x2(b0, b1);
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int kk = 0; kk < KK; ++kk) {
+                        uint32_t* x = reinterpret_cast<uint32_t*>(&qb[hb][kk]);
+#pragma unroll
+                        for (int w = 0; w < 4; ++w) {
+                            const int i = (32 * kk + 8 * q4) / 2 + w;    // elements 2i, 2i + 1
+                            float r0, r1;
+                            rope_pair(bf16_lo(x[w]), bf16_hi(x[w]), cs[i], sn[i], r0, r1);
+                            x[w] = pack_bf16x2(r0, r1);
+                        }
+                    }
+                }
+                if (split == 0 && wave == 0 && p.q_rot_out) {
+#pragma unroll
+                    for (int kk = 0; kk < KK; ++kk)
+                        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.q_rot_out) + qoff + 32 * kk) = qb[hb][kk];
+                }
+            }
         }
     }
 
@@ -292,6 +333,47 @@ decode_mfma_kernel(const DecodeParams p) {
         }
     };
 
+    if constexpr (FUSED) {
+        // The split holding the new token stores it (rotated key, raw value)
+        // before any of its waves reads the tile that contains it; other
+        // splits of the sequence never read that slot.
+        if (split == nsp - 1 && L > 0) {
+            uint16_t* kdst = nullptr;
+            uint16_t* vdst = nullptr;
+            if constexpr (PAGED) {
+                const int blk = table[pos / p.block_size];      // clamped like every row read
+                const int bc = blk < 0 ? 0 : (blk >= p.num_blocks ? p.num_blocks - 1 : blk);
+                const size_t off = ((static_cast<size_t>(bc) * p.H_kv + j) * p.block_size + pos % p.block_size) * D;
+                if (blk == bc) {
+                    kdst = static_cast<uint16_t*>(const_cast<void*>(p.k)) + off;
+                    vdst = static_cast<uint16_t*>(const_cast<void*>(p.v)) + off;
+                }
+            } else {
+                kdst = static_cast<uint16_t*>(const_cast<void*>(p.k)) + seq_off + static_cast<size_t>(pos) * D;
+                vdst = static_cast<uint16_t*>(const_cast<void*>(p.v)) + seq_off + static_cast<size_t>(pos) * D;
+            }
+            if (kdst && wave == 0) {
+                const uint16_t* kn = static_cast<const uint16_t*>(p.k_new) + (static_cast<size_t>(b) * p.H_kv + j) * D;
+                const uint16_t* vn = static_cast<const uint16_t*>(p.v_new) + (static_cast<size_t>(b) * p.H_kv + j) * D;
+                const float* cs = p.rope_cos + static_cast<size_t>(pos) * (D / 2);
+                const float* sn = p.rope_sin + static_cast<size_t>(pos) * (D / 2);
+                for (int i = lane; i < D / 2; i += 64) {
+                    int e0, e1;
+                    if (p.rope_style == KVC_ROPE_HALF) { e0 = i; e1 = i + D / 2; }
+                    else { e0 = 2 * i; e1 = 2 * i + 1; }
+                    float r0, r1;
+                    rope_pair(bf16_bits_to_f32(kn[e0]), bf16_bits_to_f32(kn[e1]), cs[i], sn[i], r0, r1);
+                    kdst[e0] = f32_to_bf16_rne(r0);
+                    kdst[e1] = f32_to_bf16_rne(r1);
+                    vdst[2 * i] = vn[2 * i];
+                    vdst[2 * i + 1] = vn[2 * i + 1];
+                }
+            }
+            __threadfence_block();
+            __syncthreads();
+        }
+    }
+
     // Software pipeline: while one tile is computed, the next one's K rows
     // (registers) and V rows (the other LDS buffer) are in flight.  The next
     // tile is fetched unconditionally - past the split it reads zeros
@@ -369,20 +451,19 @@ decode_mfma_kernel(const DecodeParams p) {
 
 constexpr int kNWm = 4;
 
-template <int D, int HB>
-hipError_t launch_dh(bool paged, const DecodeParams& p, hipStream_t stream) {
+template <int D, int HB, bool FUSED>
+hipError_t launch_dhf(bool paged, const DecodeParams& p, hipStream_t stream, const KernelTiming& tm) {
     const dim3 grid(p.n_wg_pad), block(kNWm * 64);
-    if (paged)
-        hipLaunchKernelGGL((decode_mfma_kernel<D, HB, kNWm, true>), grid, block, 0, stream, p);
-    else
-        hipLaunchKernelGGL((decode_mfma_kernel<D, HB, kNWm, false>), grid, block, 0, stream, p);
-    return hipGetLastError();
+    if (paged) return launch_timed(decode_mfma_kernel<D, HB, kNWm, true, FUSED>, grid, block, stream, tm, p);
+    return launch_timed(decode_mfma_kernel<D, HB, kNWm, false, FUSED>, grid, block, stream, tm, p);
 }
 
 template <int D>
-hipError_t launch_d(int G, bool paged, const DecodeParams& p, hipStream_t stream) {
-    if (G <= 16) return launch_dh<D, 1>(paged, p, stream);
-    return launch_dh<D, 2>(paged, p, stream);
+hipError_t launch_d(int G, bool paged, bool fused, const DecodeParams& p, hipStream_t stream,
+                    const KernelTiming& tm) {
+    if (G <= 16)
+        return fused ? launch_dhf<D, 1, true>(paged, p, stream, tm) : launch_dhf<D, 1, false>(paged, p, stream, tm);
+    return fused ? launch_dhf<D, 2, true>(paged, p, stream, tm) : launch_dhf<D, 2, false>(paged, p, stream, tm);
 }
 
 }  // namespace
@@ -393,11 +474,12 @@ bool decode_mfma_supported(kvc_dtype dtype, int d, int G) {
 
 int decode_mfma_tile_tokens() { return 32 * kNWm; }
 
-hipError_t launch_decode_mfma(int d, int G, bool paged, const DecodeParams& p, hipStream_t stream) {
+hipError_t launch_decode_mfma(int d, int G, bool paged, bool fused, const DecodeParams& p,
+                              hipStream_t stream, const KernelTiming& tm) {
     switch (d) {
-        case 64: return launch_d<64>(G, paged, p, stream);
-        case 128: return launch_d<128>(G, paged, p, stream);
-        case 256: return launch_d<256>(G, paged, p, stream);
+        case 64: return launch_d<64>(G, paged, fused, p, stream, tm);
+        case 128: return launch_d<128>(G, paged, fused, p, stream, tm);
+        case 256: return launch_d<256>(G, paged, fused, p, stream, tm);
         default: return hipErrorInvalidValue;
     }
 }

@@ -38,6 +38,22 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 }
 
 // ---------------------------------------------------------------------------
+// RoPE rotation of one pair (x0, x1) by (c, s), every operation rounded to
+// float32 on its own (no fused multiply-add), so the result is fixed by the
+// inputs:  r0 = (x0*c) - (x1*s),  r1 = (x0*s) + (x1*c).
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ void rope_pair(float x0, float x1, float c, float s, float& r0, float& r1) {
+#pragma clang fp contract(off)
+    const float a = x0 * c;
+    const float b = x1 * s;
+    const float e = x0 * s;
+    const float f = x1 * c;
+    r0 = a - b;
+    r1 = e + f;
+}
+
+// ---------------------------------------------------------------------------
 // Cross-lane exchange inside a 64-wide wavefront.
 // DPP controls (GFX9 encoding): quad_perm(a,b,c,d) = a | b<<2 | c<<4 | d<<6,
 // row_mirror = 0x140 (lane i <-> 15-i in a row of 16),

@@ -2,6 +2,7 @@
 // (kvc_api.hip) and the kernel translation units.  Not installed.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -62,7 +63,33 @@ struct DecodeParams {
     int max_seq_len, split_tokens, n_splits;
     int n_wg, n_wg_pad;          // logical workgroups, padded to a multiple of 8
     float scale_log2;            // softmax scale * log2(e)
+
+    // Set for kvc_decode_step: lengths come from positions (L_b = positions[b] + 1)
+    // and, in the fused kernel, the append happens inside the streaming pass.
+    const int32_t* positions;    // [B] slot of the new token, or NULL
+    const void* k_new;           // [B, H_kv, d] raw key / value of the new token
+    const void* v_new;
+    const void* q_raw;           // [B, H_q, d] unrotated query (fused kernel)
+    void* q_rot_out;             // [B, H_q, d] receives the rotated query
+    const float* rope_cos;       // [rope_rows, d/2]
+    const float* rope_sin;
+    int rope_rows, rope_style;
+    int capacity;                // tokens addressable per sequence
 };
+
+// Attended length of sequence b: from positions (a decode step, after its
+// append) or from seq_lens; clamped to [0, max_seq_len].  A step whose slot is
+// outside the cache or the rotation table attends over nothing.
+__device__ __forceinline__ int attended_len(const DecodeParams& p, int b) {
+    int L;
+    if (p.positions) {
+        const int pos = p.positions[b];
+        L = (pos >= 0 && pos < p.capacity && pos < p.rope_rows) ? pos + 1 : 0;
+    } else {
+        L = p.seq_lens[b];
+    }
+    return L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
+}
 
 // Returns false (and leaves *plan untouched) when the sizes cannot be planned.
 bool plan_decode(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_len,
@@ -75,15 +102,32 @@ bool decode_supported(kvc_dtype dtype, int d, int heads_per_wg);
 // multiple of this unless the caller fixes them).
 int decode_tile_tokens(kvc_dtype dtype, int d);
 
+// Optional events recorded by the command processor exactly around one kernel.
+struct KernelTiming {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+
+template <typename Kernel, typename Params>
+inline hipError_t launch_timed(Kernel kernel, dim3 grid, dim3 block, hipStream_t stream,
+                               const KernelTiming& tm, const Params& p) {
+    if (tm.start || tm.stop)
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, tm.start, tm.stop, 0, p);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, 0, stream, p);
+    return hipGetLastError();
+}
+
 // The streaming kernel: one workgroup per (sequence, KV head, chunk, split).
 hipError_t launch_decode_split(kvc_dtype dtype, int d, int heads_per_wg, bool paged,
-                               const DecodeParams& p, hipStream_t stream);
+                               const DecodeParams& p, hipStream_t stream, const KernelTiming& tm);
 
 // The matrix-core streaming kernel (bf16; head_dim 64/128/256; G <= 32): one
 // workgroup per (sequence, KV head, split) serves all G query heads.
 bool decode_mfma_supported(kvc_dtype dtype, int d, int G);
 int decode_mfma_tile_tokens();
-hipError_t launch_decode_mfma(int d, int G, bool paged, const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_mfma(int d, int G, bool paged, bool fused, const DecodeParams& p,
+                              hipStream_t stream, const KernelTiming& tm);
 
 // The log-sum-exp merge of the splits (only when n_splits > 1).
 hipError_t launch_decode_merge(kvc_dtype dtype, int d, const DecodeParams& p, hipStream_t stream);

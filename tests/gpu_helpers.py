@@ -102,3 +102,14 @@ def compare_out(got: torch.Tensor, ref64: np.ndarray, dtype: str, what: str = ""
     say(f"  {what}: max|err| = {err:.3g} (tol {tol}), max|out| = {float(np.max(np.abs(r))) if r.size else 0:.3g}")
     assert err <= tol, f"{what}: max abs error {err} > {tol}"
     return err
+
+
+def run_step(step: "GpuStep", split_tokens=0, rope_style="interleaved", stream=None):
+    """kvc_decode_step on fresh copies of the step's inputs: (k, v, q_rot, out)."""
+    x = step.x
+    k, v = step.k.clone(), step.v.clone()
+    q_raw = x.q.to(step.k.device)
+    out, q_rot = kvc.decode_step(q_raw, k, v, step.pos, step.kn, step.vn, step.cos, step.sin,
+                                 step.max_len, block_table=step.tbl, rope_style=rope_style,
+                                 split_tokens=split_tokens, stream=stream)
+    return k, v, q_rot, out

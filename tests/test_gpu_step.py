@@ -1,0 +1,117 @@
+"""kvc_decode_step (append + attention in one call) on the GPU.
+
+It must give exactly what kvc_append followed by kvc_decode_attn gives (same
+split plan: bitwise equal caches, rotated query and output) and match the
+oracle (bit-exact append, attention within tolerance), also at full size in
+the launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from gpu_helpers import GpuStep, bits, compare_out, oracle_append, oracle_decode, run_step, say, store_np
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "tiny_mha": W.WORKLOADS["tiny_mha"],
+    "gqa_8b": W.WORKLOADS["gqa_8b"].replace(B=3, cached_lo=0, cached_hi=1100, T_max=1104),
+    "mqa_ragged": W.WORKLOADS["mqa_ragged"].replace(B=5, cached_lo=100, cached_hi=700, T_max=704),
+    "long_gqa": W.WORKLOADS["long_gqa"].replace(cached_lo=3000, cached_hi=3000, T_max=3008),
+    "paged_gqa": W.WORKLOADS["paged_gqa"].replace(B=4, cached_lo=0, cached_hi=400),
+    "gqa_d64": W.Workload("gqa_d64", 31, B=3, H_q=16, H_kv=4, d=64, dtype="bf16", cached_lo=10, cached_hi=500,
+                          T_max=504),
+    "mqa_d256": W.Workload("mqa_d256", 32, B=2, H_q=24, H_kv=1, d=256, dtype="bf16", cached_lo=10, cached_hi=500,
+                           T_max=504),
+    "valu_d32": W.Workload("valu_d32", 33, B=2, H_q=8, H_kv=2, d=32, dtype="bf16", cached_lo=10, cached_hi=300,
+                           T_max=304),
+}
+
+
+@pytest.mark.parametrize("style", ["interleaved", "half"])
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_step_equals_append_then_decode(name, style):
+    x = W.draw(CASES[name])
+    say(f"[step {name} {style}] lens={x.seq_lens.tolist()[:6]}")
+    ref = GpuStep(x)
+    for split in (0, 64):
+        k, v, q_rot, out = run_step(ref, split_tokens=split, rope_style=style)
+        a = GpuStep(x)
+        a.append(rope_style=style)
+        out_a = a.decode(split_tokens=split)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(k), bits(a.k)), "K cache differs"
+        assert np.array_equal(bits(v), bits(a.v)), "V cache differs"
+        assert np.array_equal(bits(q_rot), bits(a.q)), "rotated q differs"
+        assert np.array_equal(bits(out), bits(out_a)), f"output differs (split {split})"
+    # and against the oracle
+    k2, v2, q2 = oracle_append(x, style)
+    assert np.array_equal(bits(k), np.ascontiguousarray(k2).view(np.uint8))
+    assert np.array_equal(bits(q_rot), np.ascontiguousarray(q2).view(np.uint8))
+    compare_out(out, oracle_decode(x, k2, v2, q2), x.workload.dtype, f"step {name} {style}")
+
+
+def test_step_out_of_range_positions_write_nothing():
+    w = W.WORKLOADS["gqa_8b"].replace(B=3, cached_lo=50, cached_hi=50, T_max=64)
+    x = W.draw(w)
+    x.cached[:] = torch.tensor([10, 64, -1], dtype=torch.int32)     # 64 == T_max: outside the cache
+    for b, c in enumerate(x.cached.tolist()):
+        if c >= 0:
+            x.k_cache[b, :, c:] = float("nan")
+            x.v_cache[b, :, c:] = float("nan")
+    say("[step] out-of-range positions")
+    s = GpuStep(x)
+    s.max_len = 64                       # the cache capacity; position 64 is outside it
+    k0, v0 = bits(s.k), bits(s.v)
+    k, v, q_rot, out = run_step(s)
+    torch.cuda.synchronize()
+    kb, vb = bits(k).reshape(3, -1), bits(v).reshape(3, -1)
+    assert np.array_equal(kb[1:], k0.reshape(3, -1)[1:]) and np.array_equal(vb[1:], v0.reshape(3, -1)[1:])
+    o = store_np(out, "bf16")
+    assert np.all(o[1:] == 0)
+    k2, v2, q2 = O.append_contiguous(store_np(x.k_cache[:1], "bf16"), store_np(x.v_cache[:1], "bf16"),
+                                     x.cached.numpy()[:1], store_np(x.k_new[:1], "bf16"),
+                                     store_np(x.v_new[:1], "bf16"), x.rope_cos.numpy(), x.rope_sin.numpy(),
+                                     "bf16", q=store_np(x.q[:1], "bf16"))
+    compare_out(out[:1], O.decode_attention(q2, k2, v2, [11], "bf16"), "bf16", "valid sequence")
+
+
+def _sample_groups(w, n, seed):
+    rng = np.random.default_rng(seed)
+    pairs = {(0, 0), (w.B - 1, w.H_kv - 1)}
+    while len(pairs) < min(n, w.B * w.H_kv):
+        pairs.add((int(rng.integers(w.B)), int(rng.integers(w.H_kv))))
+    return sorted(pairs)
+
+
+@pytest.mark.parametrize("name", ["gqa_8b", "mqa_ragged", "long_gqa", "paged_gqa", "tiny_mha"])
+def test_step_full_size(name):
+    """The benchmarked call (kvc_decode_step, default split plan) at full size."""
+    w = W.WORKLOADS[name]
+    x = W.draw(w)
+    say(f"[step {name} full] B={w.B} max_len={int(x.seq_lens.max())}")
+    s = GpuStep(x)
+    k, v, q_rot, out = run_step(s)
+    torch.cuda.synchronize()
+    k2, v2, q2 = oracle_append(x)
+    assert np.array_equal(bits(k), np.ascontiguousarray(k2).view(np.uint8)), "K cache differs from the oracle"
+    assert np.array_equal(bits(v), np.ascontiguousarray(v2).view(np.uint8)), "V cache differs from the oracle"
+    assert np.array_equal(bits(q_rot), np.ascontiguousarray(q2).view(np.uint8)), "rotated q differs"
+    dt, G = w.dtype, w.G
+    got = store_np(out, dt)
+    lens = x.seq_lens.numpy()
+    worst = 0.0
+    for b, j in _sample_groups(w, 6, seed=w.seed + 100):
+        hs = slice(j * G, (j + 1) * G)
+        if w.paged:
+            kg = O.gather_paged(k2, x.block_table.numpy(), w.block_size, b, int(lens[b]))[None, j:j + 1]
+            vg = O.gather_paged(v2, x.block_table.numpy(), w.block_size, b, int(lens[b]))[None, j:j + 1]
+        else:
+            kg, vg = k2[b:b + 1, j:j + 1], v2[b:b + 1, j:j + 1]
+        ref = O.decode_attention(q2[b:b + 1, hs], kg, vg, lens[b:b + 1], dt)
+        err = float(np.max(np.abs(O.to_f64(got[b:b + 1, hs], dt) - O.to_f64(O.round_store(ref, dt), dt))))
+        worst = max(worst, err)
+        assert err <= (2e-3 if dt == "bf16" else 1e-5), f"{name} (b={b}, j={j}): max abs error {err}"
+    say(f"  {name}: sampled max|err| = {worst:.3g}")
