@@ -79,9 +79,14 @@ __device__ __forceinline__ float sum_same_head(float x) {
     return x + __shfl_xor(x, 32, 64);
 }
 
-template <int D, int HB, int NW, bool PAGED, bool FUSED>
+// MODE 0: contiguous cache.  MODE 1: paged, any block size (each row's block
+// looked up per lane).  MODE 2: paged with block_size % 16 == 0 and splits
+// starting on 32-token boundaries, so every 16-row group of a tile lies in one
+// block: one wave-uniform table lookup per group.
+template <int D, int HB, int NW, int MODE, bool FUSED>
 __global__ void __launch_bounds__(NW * 64)
 decode_mfma_kernel(const DecodeParams p) {
+    constexpr bool PAGED = MODE != 0;
     constexpr int KK = D / 32;            // 32-wide d slices per 16-token block
     constexpr int NB = D / 16;            // 16-column blocks of V
     constexpr int TT = 32;                // tokens per wave tile
@@ -110,9 +115,126 @@ decode_mfma_kernel(const DecodeParams p) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15;            // row/column index inside the operand
     const int q4 = lane >> 4;             // 16-lane group: reduction slots 8*q4 .. +7
+
+    float m[HB], l[HB];
+    f32x4_t o[HB][NB];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+        m[hb] = -INFINITY;
+        l[hb] = 0.0f;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) o[hb][nb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+
+    const uint16_t* kbase = static_cast<const uint16_t*>(p.k);
+    const uint16_t* vbase = static_cast<const uint16_t*>(p.v);
+    const size_t seq_off = PAGED ? 0 : (static_cast<size_t>(b) * p.H_kv + j) * p.T_max * D;
+    const int32_t* table = PAGED ? p.block_table + static_cast<size_t>(b) * p.max_blocks_per_seq : nullptr;
+    auto row_off = [&](int t) -> size_t {   // element offset of token t's row (t < L)
+        if constexpr (PAGED) {
+            int blk = table[t / p.block_size];
+            blk = blk < 0 ? 0 : (blk >= p.num_blocks ? p.num_blocks - 1 : blk);
+            return ((static_cast<size_t>(blk) * p.H_kv + j) * p.block_size + t % p.block_size) * D;
+        } else {
+            return seq_off + static_cast<size_t>(t) * D;
+        }
+    };
+
+    constexpr int LPR = D / 8;            // 16-byte chunks (lanes) per V row
+    constexpr int VROWS = 64 / LPR;       // V rows per wave-wide 16-byte load
+    constexpr int VLOADS = TT / VROWS;
+    // Chunk u of tile row r sits at slot u ^ swz(r) of that row in LDS.  With
+    // this XOR swizzle the 16 lanes of a transposed read (4 rows x 32 bytes)
+    // hit 8 distinct 16-byte bank groups, without padding the rows.
+    auto swz = [](int r) { return (2 * r) & (LPR - 1); };
+
+    // Contiguous caches are read through buffer resources whose range ends at
+    // row t_end of this (sequence, KV head): rows past the split read as zeros
+    // without touching memory, so no clamping is needed.  Paged caches clamp
+    // the row to t_end - 1 (always a valid, finite row of this sequence).
+    const size_t rows_bytes = static_cast<size_t>(t_end) * D * 2;
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(kbase + seq_off), 0, static_cast<int>(rows_bytes), 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(vbase + seq_off), 0, static_cast<int>(rows_bytes), 0x00020000);
+
+    // MODE 2: buffer resource of the 16-row group starting at row0 (wave-
+    // uniform, a multiple of 16): its range ends at the last row < t_end, so
+    // rows past the split read as zeros without a table lookup or memory access.
+    auto group_rsrc = [&](const uint16_t* pool, int row0) -> __amdgpu_buffer_rsrc_t {
+        int nvalid = t_end - row0;
+        nvalid = nvalid < 0 ? 0 : (nvalid > 16 ? 16 : nvalid);
+        int blk = 0;
+        if (nvalid > 0) {
+            blk = table[row0 / p.block_size];
+            blk = blk < 0 ? 0 : (blk >= p.num_blocks ? p.num_blocks - 1 : blk);
+        }
+        const uint16_t* g0 = pool + ((static_cast<size_t>(blk) * p.H_kv + j) * p.block_size + row0 % p.block_size) * D;
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(g0), 0, nvalid * D * 2, 0x00020000);
+    };
+
+    // K rows of a tile, straight into A operands (registers)
+    auto load_k = [&](int base, uint4 (&ka)[2][KK]) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const int t = base + 16 * kb + r16;
+            if constexpr (MODE == 2) {
+                const __amdgpu_buffer_rsrc_t rs = group_rsrc(kbase, base + 16 * kb);
+                const int off = (r16 * D + 8 * q4) * 2;
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk)
+                    ka[kb][kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 64 * kk, 0, 0));
+            } else if constexpr (PAGED) {
+                const size_t off = row_off(t < t_end ? t : t_end - 1) + 8 * q4;
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk)
+                    ka[kb][kk] = *reinterpret_cast<const uint4*>(kbase + off + 32 * kk);
+            } else {
+                const int off = (t * D + 8 * q4) * 2;
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk)
+                    ka[kb][kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, off + 64 * kk, 0, 0));
+            }
+        }
+    };
+    // V rows of a tile, HBM -> LDS without passing through registers: lane l
+    // of load i fills LDS bytes [16 l, 16 l + 16) of that load's 1 KiB, i.e. row
+    // VROWS*i + l / LPR, slot l % LPR, so it fetches chunk (slot ^ swz(row)).
+    auto load_v = [&](int base, char* buf) {
+        char* wbuf = buf + wave * STAGE;
+#pragma unroll
+        for (int i = 0; i < VLOADS; ++i) {
+            const int r = VROWS * i + lane / LPR;
+            const int u = (lane % LPR) ^ swz(r);
+            const int t = base + r;
+            lds_void_t* dst = (lds_void_t*)(wbuf + 1024 * i);
+            if constexpr (MODE == 2) {
+                const int row0 = (VROWS * i / 16) * 16;           // this load's 16-row group
+                const __amdgpu_buffer_rsrc_t rs = group_rsrc(vbase, base + row0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, ((r - row0) * D + 8 * u) * 2, 0, 0, 0);
+            } else if constexpr (PAGED) {
+                const uint16_t* src = vbase + row_off(t < t_end ? t : t_end - 1) + 8 * u;
+                __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+            } else {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, dst, 16, (t * D + 8 * u) * 2, 0, 0, 0);
+            }
+        }
+    };
+
+    // The first tile's loads go out before the query is loaded, so the two
+    // latencies overlap - except in the split that stores the new token, whose
+    // tiles may only be read after the store.
+    uint4 ka0[2][KK], ka1[2][KK];
+    constexpr int kStep = NW * TT;
+    int base = t_begin + wave * TT;
+    const bool early = !(FUSED && split == nsp - 1);
+    if (early && base < t_end) {
+        load_k(base, ka0);
+        load_v(base, vbuf0);
+    }
 
     // B operand Q^T: lane holds head 16*hb + r16, d = 32*kk + 8*q4 .. +7
     uint4 qb[HB][KK];
@@ -171,85 +293,46 @@ decode_mfma_kernel(const DecodeParams p) {
         }
     }
 
-    float m[HB], l[HB];
-    f32x4_t o[HB][NB];
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
-        m[hb] = -INFINITY;
-        l[hb] = 0.0f;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) o[hb][nb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (FUSED) {
+        // The split holding the new token stores it (rotated key, raw value)
+        // before any of its waves reads the tile that contains it; other
+        // splits of the sequence never read that slot.
+        if (split == nsp - 1 && L > 0) {
+            uint16_t* kdst = nullptr;
+            uint16_t* vdst = nullptr;
+            if constexpr (PAGED) {
+                const int blk = table[pos / p.block_size];      // clamped like every row read
+                const int bc = blk < 0 ? 0 : (blk >= p.num_blocks ? p.num_blocks - 1 : blk);
+                const size_t off = ((static_cast<size_t>(bc) * p.H_kv + j) * p.block_size + pos % p.block_size) * D;
+                if (blk == bc) {
+                    kdst = static_cast<uint16_t*>(const_cast<void*>(p.k)) + off;
+                    vdst = static_cast<uint16_t*>(const_cast<void*>(p.v)) + off;
+                }
+            } else {
+                kdst = static_cast<uint16_t*>(const_cast<void*>(p.k)) + seq_off + static_cast<size_t>(pos) * D;
+                vdst = static_cast<uint16_t*>(const_cast<void*>(p.v)) + seq_off + static_cast<size_t>(pos) * D;
+            }
+            if (kdst && wave == 0) {
+                const uint16_t* kn = static_cast<const uint16_t*>(p.k_new) + (static_cast<size_t>(b) * p.H_kv + j) * D;
+                const uint16_t* vn = static_cast<const uint16_t*>(p.v_new) + (static_cast<size_t>(b) * p.H_kv + j) * D;
+                const float* cs = p.rope_cos + static_cast<size_t>(pos) * (D / 2);
+                const float* sn = p.rope_sin + static_cast<size_t>(pos) * (D / 2);
+                for (int i = lane; i < D / 2; i += 64) {
+                    int e0, e1;
+                    if (p.rope_style == KVC_ROPE_HALF) { e0 = i; e1 = i + D / 2; }
+                    else { e0 = 2 * i; e1 = 2 * i + 1; }
+                    float r0, r1;
+                    rope_pair(bf16_bits_to_f32(kn[e0]), bf16_bits_to_f32(kn[e1]), cs[i], sn[i], r0, r1);
+                    kdst[e0] = f32_to_bf16_rne(r0);
+                    kdst[e1] = f32_to_bf16_rne(r1);
+                    vdst[2 * i] = vn[2 * i];
+                    vdst[2 * i + 1] = vn[2 * i + 1];
+                }
+            }
+            __threadfence_block();
+            __syncthreads();
+        }
     }
-
-    const uint16_t* kbase = static_cast<const uint16_t*>(p.k);
-    const uint16_t* vbase = static_cast<const uint16_t*>(p.v);
-    const size_t seq_off = PAGED ? 0 : (static_cast<size_t>(b) * p.H_kv + j) * p.T_max * D;
-    const int32_t* table = PAGED ? p.block_table + static_cast<size_t>(b) * p.max_blocks_per_seq : nullptr;
-    auto row_off = [&](int t) -> size_t {   // element offset of token t's row (t < L)
-        if constexpr (PAGED) {
-            int blk = table[t / p.block_size];
-            blk = blk < 0 ? 0 : (blk >= p.num_blocks ? p.num_blocks - 1 : blk);
-            return ((static_cast<size_t>(blk) * p.H_kv + j) * p.block_size + t % p.block_size) * D;
-        } else {
-            return seq_off + static_cast<size_t>(t) * D;
-        }
-    };
-
-    constexpr int LPR = D / 8;            // 16-byte chunks (lanes) per V row
-    constexpr int VROWS = 64 / LPR;       // V rows per wave-wide 16-byte load
-    constexpr int VLOADS = TT / VROWS;
-    // Chunk u of tile row r sits at slot u ^ swz(r) of that row in LDS.  With
-    // this XOR swizzle the 16 lanes of a transposed read (4 rows x 32 bytes)
-    // hit 8 distinct 16-byte bank groups, without padding the rows.
-    auto swz = [](int r) { return (2 * r) & (LPR - 1); };
-
-    // Contiguous caches are read through buffer resources whose range ends at
-    // row t_end of this (sequence, KV head): rows past the split read as zeros
-    // without touching memory, so no clamping is needed.  Paged caches clamp
-    // the row to t_end - 1 (always a valid, finite row of this sequence).
-    const size_t rows_bytes = static_cast<size_t>(t_end) * D * 2;
-    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(kbase + seq_off), 0, static_cast<int>(rows_bytes), 0x00020000);
-    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(vbase + seq_off), 0, static_cast<int>(rows_bytes), 0x00020000);
-
-    // K rows of a tile, straight into A operands (registers)
-    auto load_k = [&](int base, uint4 (&ka)[2][KK]) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const int t = base + 16 * kb + r16;
-            if constexpr (PAGED) {
-                const size_t off = row_off(t < t_end ? t : t_end - 1) + 8 * q4;
-#pragma unroll
-                for (int kk = 0; kk < KK; ++kk)
-                    ka[kb][kk] = *reinterpret_cast<const uint4*>(kbase + off + 32 * kk);
-            } else {
-                const int off = (t * D + 8 * q4) * 2;
-#pragma unroll
-                for (int kk = 0; kk < KK; ++kk)
-                    ka[kb][kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, off + 64 * kk, 0, 0));
-            }
-        }
-    };
-    // V rows of a tile, HBM -> LDS without passing through registers: lane l
-    // of load i fills LDS bytes [16 l, 16 l + 16) of that load's 1 KiB, i.e. row
-    // VROWS*i + l / LPR, slot l % LPR, so it fetches chunk (slot ^ swz(row)).
-    auto load_v = [&](int base, char* buf) {
-        char* wbuf = buf + wave * STAGE;
-#pragma unroll
-        for (int i = 0; i < VLOADS; ++i) {
-            const int r = VROWS * i + lane / LPR;
-            const int u = (lane % LPR) ^ swz(r);
-            const int t = base + r;
-            lds_void_t* dst = (lds_void_t*)(wbuf + 1024 * i);
-            if constexpr (PAGED) {
-                const uint16_t* src = vbase + row_off(t < t_end ? t : t_end - 1) + 8 * u;
-                __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
-            } else {
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, dst, 16, (t * D + 8 * u) * 2, 0, 0, 0);
-            }
-        }
-    };
 
     // transposed-read source of this lane: row tr_row (+16 for the upper half),
     // columns 16*nb + 4*(s16 % 4) .. +3 = chunk 2*nb + (s16 % 4) / 2, half s16 & 1
@@ -333,59 +416,17 @@ decode_mfma_kernel(const DecodeParams p) {
         }
     };
 
-    if constexpr (FUSED) {
-        // The split holding the new token stores it (rotated key, raw value)
-        // before any of its waves reads the tile that contains it; other
-        // splits of the sequence never read that slot.
-        if (split == nsp - 1 && L > 0) {
-            uint16_t* kdst = nullptr;
-            uint16_t* vdst = nullptr;
-            if constexpr (PAGED) {
-                const int blk = table[pos / p.block_size];      // clamped like every row read
-                const int bc = blk < 0 ? 0 : (blk >= p.num_blocks ? p.num_blocks - 1 : blk);
-                const size_t off = ((static_cast<size_t>(bc) * p.H_kv + j) * p.block_size + pos % p.block_size) * D;
-                if (blk == bc) {
-                    kdst = static_cast<uint16_t*>(const_cast<void*>(p.k)) + off;
-                    vdst = static_cast<uint16_t*>(const_cast<void*>(p.v)) + off;
-                }
-            } else {
-                kdst = static_cast<uint16_t*>(const_cast<void*>(p.k)) + seq_off + static_cast<size_t>(pos) * D;
-                vdst = static_cast<uint16_t*>(const_cast<void*>(p.v)) + seq_off + static_cast<size_t>(pos) * D;
-            }
-            if (kdst && wave == 0) {
-                const uint16_t* kn = static_cast<const uint16_t*>(p.k_new) + (static_cast<size_t>(b) * p.H_kv + j) * D;
-                const uint16_t* vn = static_cast<const uint16_t*>(p.v_new) + (static_cast<size_t>(b) * p.H_kv + j) * D;
-                const float* cs = p.rope_cos + static_cast<size_t>(pos) * (D / 2);
-                const float* sn = p.rope_sin + static_cast<size_t>(pos) * (D / 2);
-                for (int i = lane; i < D / 2; i += 64) {
-                    int e0, e1;
-                    if (p.rope_style == KVC_ROPE_HALF) { e0 = i; e1 = i + D / 2; }
-                    else { e0 = 2 * i; e1 = 2 * i + 1; }
-                    float r0, r1;
-                    rope_pair(bf16_bits_to_f32(kn[e0]), bf16_bits_to_f32(kn[e1]), cs[i], sn[i], r0, r1);
-                    kdst[e0] = f32_to_bf16_rne(r0);
-                    kdst[e1] = f32_to_bf16_rne(r1);
-                    vdst[2 * i] = vn[2 * i];
-                    vdst[2 * i + 1] = vn[2 * i + 1];
-                }
-            }
-            __threadfence_block();
-            __syncthreads();
-        }
-    }
-
     // Software pipeline: while one tile is computed, the next one's K rows
     // (registers) and V rows (the other LDS buffer) are in flight.  The next
     // tile is fetched unconditionally - past the split it reads zeros
     // (contiguous: outside the buffer range, no memory traffic) or the clamped
     // last row (paged) - so every path through the loop has the same loads in
     // flight and the compiler waits only for the tile it is about to use.
-    uint4 ka0[2][KK], ka1[2][KK];
-    constexpr int kStep = NW * TT;
-    int base = t_begin + wave * TT;
     if (base < t_end) {
-        load_k(base, ka0);
-        load_v(base, vbuf0);
+        if (!early) {
+            load_k(base, ka0);
+            load_v(base, vbuf0);
+        }
         for (;;) {
             load_k(base + kStep, ka1);
             load_v(base + kStep, vbuf1);
@@ -454,8 +495,10 @@ constexpr int kNWm = 4;
 template <int D, int HB, bool FUSED>
 hipError_t launch_dhf(bool paged, const DecodeParams& p, hipStream_t stream, const KernelTiming& tm) {
     const dim3 grid(p.n_wg_pad), block(kNWm * 64);
-    if (paged) return launch_timed(decode_mfma_kernel<D, HB, kNWm, true, FUSED>, grid, block, stream, tm, p);
-    return launch_timed(decode_mfma_kernel<D, HB, kNWm, false, FUSED>, grid, block, stream, tm, p);
+    if (!paged) return launch_timed(decode_mfma_kernel<D, HB, kNWm, 0, FUSED>, grid, block, stream, tm, p);
+    if (p.block_size % 16 == 0 && p.split_tokens % 32 == 0)
+        return launch_timed(decode_mfma_kernel<D, HB, kNWm, 2, FUSED>, grid, block, stream, tm, p);
+    return launch_timed(decode_mfma_kernel<D, HB, kNWm, 1, FUSED>, grid, block, stream, tm, p);
 }
 
 template <int D>
