@@ -69,6 +69,16 @@ __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v_t));
 }
 
+// Buffer resource from values that are the same in every lane; readfirstlane
+// keeps them in scalar registers, so the compiler never needs a loop over lanes.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_uniform_rsrc(const void* base, int bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+    void* ua = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(ua, 0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
 // Lanes l, l^16, l^32, l^48 hold the same query head: reduce over them.
 __device__ __forceinline__ float max_same_head(float x) {
     x = fmaxf(x, __shfl_xor(x, 16, 64));
@@ -85,7 +95,9 @@ __device__ __forceinline__ float sum_same_head(float x) {
 // block: one wave-uniform table lookup per group.
 template <int D, int HB, int NW, int MODE, bool FUSED>
 __global__ void __launch_bounds__(NW * 64)
-decode_mfma_kernel(const DecodeParams p) {
+decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table) {
+    // (the block table as its own restrict argument: nothing this kernel stores
+    // can alias it, so its wave-uniform reads may use scalar loads)
     constexpr bool PAGED = MODE != 0;
     constexpr int KK = D / 32;            // 32-wide d slices per 16-token block
     constexpr int NB = D / 16;            // 16-column blocks of V
@@ -132,7 +144,7 @@ decode_mfma_kernel(const DecodeParams p) {
     const uint16_t* kbase = static_cast<const uint16_t*>(p.k);
     const uint16_t* vbase = static_cast<const uint16_t*>(p.v);
     const size_t seq_off = PAGED ? 0 : (static_cast<size_t>(b) * p.H_kv + j) * p.T_max * D;
-    const int32_t* table = PAGED ? p.block_table + static_cast<size_t>(b) * p.max_blocks_per_seq : nullptr;
+    const int32_t* table = PAGED ? block_table + static_cast<size_t>(b) * p.max_blocks_per_seq : nullptr;
     auto row_off = [&](int t) -> size_t {   // element offset of token t's row (t < L)
         if constexpr (PAGED) {
             int blk = table[t / p.block_size];
@@ -156,24 +168,28 @@ decode_mfma_kernel(const DecodeParams p) {
     // without touching memory, so no clamping is needed.  Paged caches clamp
     // the row to t_end - 1 (always a valid, finite row of this sequence).
     const size_t rows_bytes = static_cast<size_t>(t_end) * D * 2;
-    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(kbase + seq_off), 0, static_cast<int>(rows_bytes), 0x00020000);
-    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(vbase + seq_off), 0, static_cast<int>(rows_bytes), 0x00020000);
+    const __amdgpu_buffer_rsrc_t krs = make_uniform_rsrc(kbase + seq_off, static_cast<int>(rows_bytes));
+    const __amdgpu_buffer_rsrc_t vrs = make_uniform_rsrc(vbase + seq_off, static_cast<int>(rows_bytes));
 
     // MODE 2: buffer resource of the 16-row group starting at row0 (wave-
     // uniform, a multiple of 16): its range ends at the last row < t_end, so
     // rows past the split read as zeros without a table lookup or memory access.
-    auto group_rsrc = [&](const uint16_t* pool, int row0) -> __amdgpu_buffer_rsrc_t {
-        int nvalid = t_end - row0;
+    auto group_rsrc = [&](const uint16_t* pool, int row0_) -> __amdgpu_buffer_rsrc_t {
+        // wave-uniform by construction; readfirstlane lets the compiler see it
+        const int row0 = __builtin_amdgcn_readfirstlane(row0_);
+        int nvalid = __builtin_amdgcn_readfirstlane(t_end) - row0;
         nvalid = nvalid < 0 ? 0 : (nvalid > 16 ? 16 : nvalid);
+        // (a division leaves its result in a vector register: readfirstlane
+        // returns it to a scalar one, so the table read is a scalar load)
+        const int lb = __builtin_amdgcn_readfirstlane(row0 / p.block_size);
+        const int in_blk = row0 - lb * p.block_size;
         int blk = 0;
         if (nvalid > 0) {
-            blk = table[row0 / p.block_size];
+            blk = __builtin_amdgcn_readfirstlane(table[lb]);
             blk = blk < 0 ? 0 : (blk >= p.num_blocks ? p.num_blocks - 1 : blk);
         }
-        const uint16_t* g0 = pool + ((static_cast<size_t>(blk) * p.H_kv + j) * p.block_size + row0 % p.block_size) * D;
-        return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(g0), 0, nvalid * D * 2, 0x00020000);
+        const uint16_t* g0 = pool + ((static_cast<size_t>(blk) * p.H_kv + j) * p.block_size + in_blk) * D;
+        return make_uniform_rsrc(g0, nvalid * D * 2);
     };
 
     // K rows of a tile, straight into A operands (registers)
@@ -224,14 +240,15 @@ decode_mfma_kernel(const DecodeParams p) {
         }
     };
 
-    // The first tile's loads go out before the query is loaded, so the two
-    // latencies overlap - except in the split that stores the new token, whose
-    // tiles may only be read after the store.
+    // Plain decode: the first tile's loads go out before the query is loaded,
+    // so the two latencies overlap.  The fused step loads the first tile after
+    // the query rotation and the append (the split storing the new token may
+    // only read it after the store), the same way in every split so that all
+    // paths into the pipeline have the same loads in flight.
     uint4 ka0[2][KK], ka1[2][KK];
     constexpr int kStep = NW * TT;
     int base = t_begin + wave * TT;
-    const bool early = !(FUSED && split == nsp - 1);
-    if (early && base < t_end) {
+    if (!FUSED && base < t_end) {
         load_k(base, ka0);
         load_v(base, vbuf0);
     }
@@ -261,12 +278,17 @@ decode_mfma_kernel(const DecodeParams p) {
                     for (int kk = 0; kk < KK / 2; ++kk) {
                         uint32_t* x = reinterpret_cast<uint32_t*>(&qb[hb][kk]);
                         uint32_t* y = reinterpret_cast<uint32_t*>(&qb[hb][kk + KK / 2]);
+                        const int i0 = 32 * kk + 8 * q4;                  // pairs i0 .. i0 + 7
+                        float c8[8], s8[8];
+                        *reinterpret_cast<float4*>(c8) = *reinterpret_cast<const float4*>(cs + i0);
+                        *reinterpret_cast<float4*>(c8 + 4) = *reinterpret_cast<const float4*>(cs + i0 + 4);
+                        *reinterpret_cast<float4*>(s8) = *reinterpret_cast<const float4*>(sn + i0);
+                        *reinterpret_cast<float4*>(s8 + 4) = *reinterpret_cast<const float4*>(sn + i0 + 4);
 #pragma unroll
                         for (int w = 0; w < 4; ++w) {
-                            const int i = 32 * kk + 8 * q4 + 2 * w;     // pair indices i, i + 1
                             float a0, a1, b0, b1;
-                            rope_pair(bf16_lo(x[w]), bf16_lo(y[w]), cs[i], sn[i], a0, b0);
-                            rope_pair(bf16_hi(x[w]), bf16_hi(y[w]), cs[i + 1], sn[i + 1], a1, b1);
+                            rope_pair(bf16_lo(x[w]), bf16_lo(y[w]), c8[2 * w], s8[2 * w], a0, b0);
+                            rope_pair(bf16_hi(x[w]), bf16_hi(y[w]), c8[2 * w + 1], s8[2 * w + 1], a1, b1);
                             x[w] = pack_bf16x2(a0, a1);
                             y[w] = pack_bf16x2(b0, b1);
                         }
@@ -275,11 +297,15 @@ decode_mfma_kernel(const DecodeParams p) {
 #pragma unroll
                     for (int kk = 0; kk < KK; ++kk) {
                         uint32_t* x = reinterpret_cast<uint32_t*>(&qb[hb][kk]);
+                        const int i0 = (32 * kk + 8 * q4) / 2;            // pairs i0 .. i0 + 3
+                        const float4 c4 = *reinterpret_cast<const float4*>(cs + i0);
+                        const float4 s4 = *reinterpret_cast<const float4*>(sn + i0);
+                        const float cw[4] = {c4.x, c4.y, c4.z, c4.w};
+                        const float sw[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
                         for (int w = 0; w < 4; ++w) {
-                            const int i = (32 * kk + 8 * q4) / 2 + w;    // elements 2i, 2i + 1
                             float r0, r1;
-                            rope_pair(bf16_lo(x[w]), bf16_hi(x[w]), cs[i], sn[i], r0, r1);
+                            rope_pair(bf16_lo(x[w]), bf16_hi(x[w]), cw[w], sw[w], r0, r1);
                             x[w] = pack_bf16x2(r0, r1);
                         }
                     }
@@ -332,6 +358,10 @@ decode_mfma_kernel(const DecodeParams p) {
             __threadfence_block();
             __syncthreads();
         }
+        // Every path (split 0 stores the rotated query, the last split stores
+        // the new token) enters the tile pipeline with nothing in flight, so
+        // the pipeline's waits stay exact.
+        __builtin_amdgcn_s_waitcnt(0);
     }
 
     // transposed-read source of this lane: row tr_row (+16 for the upper half),
@@ -423,7 +453,7 @@ decode_mfma_kernel(const DecodeParams p) {
     // last row (paged) - so every path through the loop has the same loads in
     // flight and the compiler waits only for the tile it is about to use.
     if (base < t_end) {
-        if (!early) {
+        if (FUSED) {
             load_k(base, ka0);
             load_v(base, vbuf0);
         }
@@ -495,10 +525,11 @@ constexpr int kNWm = 4;
 template <int D, int HB, bool FUSED>
 hipError_t launch_dhf(bool paged, const DecodeParams& p, hipStream_t stream, const KernelTiming& tm) {
     const dim3 grid(p.n_wg_pad), block(kNWm * 64);
-    if (!paged) return launch_timed(decode_mfma_kernel<D, HB, kNWm, 0, FUSED>, grid, block, stream, tm, p);
+    const int32_t* tbl = p.block_table;
+    if (!paged) return launch_timed(decode_mfma_kernel<D, HB, kNWm, 0, FUSED>, grid, block, stream, tm, p, tbl);
     if (p.block_size % 16 == 0 && p.split_tokens % 32 == 0)
-        return launch_timed(decode_mfma_kernel<D, HB, kNWm, 2, FUSED>, grid, block, stream, tm, p);
-    return launch_timed(decode_mfma_kernel<D, HB, kNWm, 1, FUSED>, grid, block, stream, tm, p);
+        return launch_timed(decode_mfma_kernel<D, HB, kNWm, 2, FUSED>, grid, block, stream, tm, p, tbl);
+    return launch_timed(decode_mfma_kernel<D, HB, kNWm, 1, FUSED>, grid, block, stream, tm, p, tbl);
 }
 
 template <int D>

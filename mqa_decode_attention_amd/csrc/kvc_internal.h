@@ -108,13 +108,13 @@ struct KernelTiming {
     hipEvent_t stop = nullptr;
 };
 
-template <typename Kernel, typename Params>
+template <typename Kernel, typename... Args>
 inline hipError_t launch_timed(Kernel kernel, dim3 grid, dim3 block, hipStream_t stream,
-                               const KernelTiming& tm, const Params& p) {
+                               const KernelTiming& tm, const Args&... args) {
     if (tm.start || tm.stop)
-        hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, tm.start, tm.stop, 0, p);
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, tm.start, tm.stop, 0, args...);
     else
-        hipLaunchKernelGGL(kernel, grid, block, 0, stream, p);
+        hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
     return hipGetLastError();
 }
 
