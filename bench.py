@@ -31,7 +31,10 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
 MALL_DEFEAT_BYTES = 2 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_gqa_8b_traffic.json")
-DECODE_SRC = os.path.join(ROOT, "mqa_decode_attention_amd", "csrc", "kvc_decode.hip")
+# the streaming kernel is built from these sources; counters taken on other
+# versions of them do not describe the current kernel
+KERNEL_SOURCES = [os.path.join(ROOT, "mqa_decode_attention_amd", "csrc", f)
+                  for f in ("kvc_decode_mfma.hip", "kvc_device.h", "kvc_internal.h")]
 
 
 def kv_read_bytes(seq_lens, H_kv, d, elem_bytes):
@@ -49,21 +52,43 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seqs", type=int, default=0,
                     help="sequences the CPU oracle is timed on (0 = all)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (counter calibration)")
+    ap.add_argument("--read-probe", action="store_true",
+                    help="only measure the streaming-read ceiling (kvc_hbm_read_probe)")
     return ap.parse_args()
 
 
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
 def traffic_for_current_kernel():
-    """HBM bytes per decode launch from committed rocprofv3 counter runs, if they
-    were taken on the current decode kernel source; else None."""
+    """HBM bytes per launch of the streaming kernel from the committed rocprofv3
+    counter runs, if they were taken on the current kernel sources; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
-        src = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()
-        if t.get("kernel_source_sha256") == src:
+        if t.get("kernel_sources_sha256") == kernel_source_hash():
             return t.get("hbm_bytes_per_launch")
     except (OSError, ValueError):
         pass
     return None
+
+
+def calibrate_copy(nbytes: int) -> None:
+    """A plain device copy of known size (read nbytes, write nbytes), five times:
+    what FETCH_SIZE / WRITE_SIZE report for it scales the counters of the kernel."""
+    import torch
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes": nbytes, "copies": 5}))
 
 
 def cpu_baseline(x, n_seqs):
@@ -99,8 +124,43 @@ def cpu_baseline(x, n_seqs):
                       f"{sec:.2f} s"}
 
 
+def read_probe(gib: int = 4, reps: int = 10) -> dict:
+    """Streaming-read rate of kvc_hbm_read_probe over a 4 GiB buffer (far beyond
+    the 256 MB Infinity Cache), best of several grid sizes."""
+    import ctypes
+
+    import torch
+
+    import mqa_decode_attention_amd as kvc
+
+    lib = kvc.load()
+    nbytes = gib << 30
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    best = {}
+    for wgs in (1024, 2048, 4096, 8192):
+        sink = torch.zeros(wgs, dtype=torch.int32, device="cuda")
+        st = torch.cuda.current_stream().cuda_stream
+        rc = lib.kvc_hbm_read_probe(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()), wgs, st)
+        assert rc == 0, lib.kvc_last_error()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            lib.kvc_hbm_read_probe(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()), wgs, st)
+        b.record()
+        torch.cuda.synchronize()
+        gbs = nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+        best[wgs] = round(gbs, 1)
+    return {"read_probe_gbs": best, "read_probe_best_gbs": max(best.values()), "buffer_gib": gib}
+
+
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
+    if args.read_probe:
+        print(json.dumps(read_probe()), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the decode path shards by sequence and KV head with no exchange; see the design notes)",
@@ -208,6 +268,11 @@ def main():
                      "bytes_per_launch": kv_bytes},
         "wall_s_timed": round(wall, 4),
     }
+    del ks, vs
+    torch.cuda.empty_cache()
+    probe = read_probe(reps=5)
+    res["read_ceiling"] = {"probe": "kvc_hbm_read_probe, 4 GiB, best grid", "gbs": probe["read_probe_best_gbs"],
+                           "kernel_frac_of_ceiling": round(achieved / probe["read_probe_best_gbs"], 4)}
     if not args.no_cpu_baseline and not w.paged:
         res["cpu_baseline"] = cpu_baseline(x, args.cpu_sample_seqs)
     print(json.dumps(res), flush=True)

@@ -19,6 +19,7 @@ SIGNATURES = {
     "kvc_status_string": (c_char_p, [c_int]),
     "kvc_last_error": (c_char_p, []),
     "kvc_profile_next_decode": (None, [c_void_p, c_void_p]),
+    "kvc_hbm_read_probe": (c_int, [c_void_p, c_size_t, c_void_p, c_int, c_void_p]),
     "kvc_append": (c_int, [c_int, c_int, c_int, c_int, c_int,
                            c_void_p, c_void_p, c_int,
                            c_void_p, c_int, c_int, c_int, c_void_p,

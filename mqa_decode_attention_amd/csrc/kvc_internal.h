@@ -132,4 +132,8 @@ hipError_t launch_decode_mfma(int d, int G, bool paged, bool fused, const Decode
 // The log-sum-exp merge of the splits (only when n_splits > 1).
 hipError_t launch_decode_merge(kvc_dtype dtype, int d, const DecodeParams& p, hipStream_t stream);
 
+// Streaming-read probe (kvc_hbm_read_probe).
+hipError_t launch_read_probe(const void* buf, size_t bytes, unsigned* sink, int workgroups,
+                             hipStream_t stream);
+
 }  // namespace kvc
