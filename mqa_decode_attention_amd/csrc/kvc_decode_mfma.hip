@@ -48,6 +48,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -67,6 +68,16 @@ __device__ __forceinline__ f32x4_t mfma16(const uint4& a, const uint4& b, const 
 __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
     const f32x2_t v = {lo, hi};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v_t));
+}
+
+// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector
+// memory operations are outstanding and leaves the other counters alone.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// c ? a : b on values (a conditional between two uint4 lvalues would select
+// an address, which forces register arrays into memory).
+__device__ __forceinline__ uint4 select4(bool c, const uint4& a, const uint4& b) {
+    return make_uint4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
 }
 
 // Buffer resource from values that are the same in every lane; readfirstlane
@@ -118,7 +129,9 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     const int j = unit % p.H_kv;
     const int G = p.G;
 
-    const int L = attended_len(p, b);
+    // fused step: slot of the new token (read once; it also gives L)
+    const int pos = FUSED ? p.positions[b] : 0;
+    const int L = FUSED ? len_from_position(p, pos) : attended_len(p, b);
     int nsp = (L + p.split_tokens - 1) / p.split_tokens;
     nsp = nsp < 1 ? 1 : nsp;
     if (split >= nsp) return;
@@ -193,7 +206,7 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     };
 
     // K rows of a tile, straight into A operands (registers)
-    auto load_k = [&](int base, uint4 (&ka)[2][KK]) {
+    auto load_k = [&](int base, uint4 (&ka)[2][KK]) __attribute__((always_inline)) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             const int t = base + 16 * kb + r16;
@@ -219,7 +232,7 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     // V rows of a tile, HBM -> LDS without passing through registers: lane l
     // of load i fills LDS bytes [16 l, 16 l + 16) of that load's 1 KiB, i.e. row
     // VROWS*i + l / LPR, slot l % LPR, so it fetches chunk (slot ^ swz(row)).
-    auto load_v = [&](int base, char* buf) {
+    auto load_v = [&](int base, char* buf) __attribute__((always_inline)) {
         char* wbuf = buf + wave * STAGE;
 #pragma unroll
         for (int i = 0; i < VLOADS; ++i) {
@@ -240,128 +253,132 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
         }
     };
 
-    // Plain decode: the first tile's loads go out before the query is loaded,
-    // so the two latencies overlap.  The fused step loads the first tile after
-    // the query rotation and the append (the split storing the new token may
-    // only read it after the store), the same way in every split so that all
-    // paths into the pipeline have the same loads in flight.
+    // The first tile's loads go out before anything else, so their latency
+    // overlaps the loads of the query (and, in the fused step, of the new
+    // token and its rotation table row).
     uint4 ka0[2][KK], ka1[2][KK];
     constexpr int kStep = NW * TT;
     int base = t_begin + wave * TT;
-    if (!FUSED && base < t_end) {
+    if (base < t_end) {
         load_k(base, ka0);
         load_v(base, vbuf0);
     }
 
-    // B operand Q^T: lane holds head 16*hb + r16, d = 32*kk + 8*q4 .. +7
+    // B operand Q^T: lane holds head 16*hb + r16, d = 32*kk + 8*q4 .. +7.  The
+    // group's G query rows are read through a buffer resource covering exactly
+    // them, so lanes of heads >= G read zeros.
+    const size_t qgrp = (static_cast<size_t>(b) * p.H_q + static_cast<size_t>(j) * G) * D;
+    const __amdgpu_buffer_rsrc_t qrs =
+        make_uniform_rsrc(static_cast<const uint16_t*>(FUSED ? p.q_raw : p.q) + qgrp, G * D * 2);
     uint4 qb[HB][KK];
-    const int pos = L - 1;                // slot of the new token (fused step)
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
-        const int g = 16 * hb + r16;
-        const size_t qoff = (static_cast<size_t>(b) * p.H_q + j * G + g) * D + 8 * q4;
+    for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+            qb[hb][kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                qrs, ((16 * hb + r16) * D + 32 * kk + 8 * q4) * 2, 0, 0));
+
+    // Fused step.  The new token sits at slot pos of sequence b; the last
+    // split of (b, j) stores it (rotated key, raw value) and, since its own
+    // tile loads may run before or after that store, patches the token into
+    // the tile it loaded instead of reading it back: the key row in the K
+    // registers, the value row in the staged V tile.  Every wave issues the
+    // same memory instructions whatever its role; a role it does not have
+    // gets a buffer range of zero bytes (loads read zeros, stores are
+    // dropped), so the waits of the tile pipeline stay exact.
+    int patch_row = -1;                   // token index of the patched row, or -1
+    size_t slot = 0;                      // element offset of the new token's row
+    bool slot_ok = false;                 // this split stores the new token
+    uint4 kn[KK];                         // rotated new key, A-operand layout
+    uint4 vn = make_uint4(0, 0, 0, 0);    // raw new value, 16-byte chunk lane % LPR
+    if constexpr (FUSED) {
+        const bool pos_ok = pos >= 0 && pos < p.capacity && pos < p.rope_rows;
+        const bool own = pos_ok && split == nsp - 1;
+        const size_t kv_in = (static_cast<size_t>(b) * p.H_kv + j) * D;
+        const __amdgpu_buffer_rsrc_t knrs =
+            make_uniform_rsrc(static_cast<const uint16_t*>(p.k_new) + kv_in, own ? D * 2 : 0);
+        const __amdgpu_buffer_rsrc_t vnrs =
+            make_uniform_rsrc(static_cast<const uint16_t*>(p.v_new) + kv_in, own ? D * 2 : 0);
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+            kn[kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                knrs, (32 * kk + 8 * q4) * 2, 0, 0));
+        vn = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vnrs, (lane % LPR) * 16, 0, 0));
+
+        // cos/sin of the pairs this lane's chunks hold.  Adjacent pairs: chunk
+        // kk holds pairs 16*kk + 4*q4 .. +3.  Split halves: chunks m and
+        // m + KK/2 pair up element by element, pairs 32*m + 8*q4 .. +7, kept
+        // as cw[2m], cw[2m + 1].  (Row 0 stands in when the position is
+        // invalid: the query is then left as it is and nothing is stored.)
+        // (the table row is read through buffer resources, like every other
+        // load here)
+        const bool half = p.rope_style == KVC_ROPE_HALF;
+        const size_t trow = static_cast<size_t>(pos_ok ? pos : 0) * (D / 2);
+        const __amdgpu_buffer_rsrc_t crs = make_uniform_rsrc(p.rope_cos + trow, D * 2);
+        const __amdgpu_buffer_rsrc_t srs = make_uniform_rsrc(p.rope_sin + trow, D * 2);
+        float4 cw[KK], sw[KK];
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-            qb[hb][kk] = make_uint4(0, 0, 0, 0);
-            if (g < G)
-                qb[hb][kk] = *reinterpret_cast<const uint4*>(
-                    static_cast<const uint16_t*>(FUSED ? p.q_raw : p.q) + qoff + 32 * kk);
+            const int i0 = half ? 32 * (kk >> 1) + 8 * q4 + 4 * (kk & 1) : 16 * kk + 4 * q4;
+            cw[kk] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(crs, i0 * 4, 0, 0));
+            sw[kk] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(srs, i0 * 4, 0, 0));
         }
-        if constexpr (FUSED) {
-            // rotate the raw query at the new token's position, exactly as the
-            // append kernel would (float32, one rounding per op, then bf16 RNE)
-            if (g < G && L > 0) {
-                const float* cs = p.rope_cos + static_cast<size_t>(pos) * (D / 2);
-                const float* sn = p.rope_sin + static_cast<size_t>(pos) * (D / 2);
-                if (p.rope_style == KVC_ROPE_HALF) {
+        auto fget = [](const float4& v, int i) __attribute__((always_inline)) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; };
+        // rotate one vector held as KK chunks, exactly as the append kernel
+        // does (float32, one rounding per operation, then bf16 RNE)
+        auto rotate = [&](uint4 (&x)[KK]) __attribute__((always_inline)) {
+            if (half) {
 #pragma unroll
-                    for (int kk = 0; kk < KK / 2; ++kk) {
-                        uint32_t* x = reinterpret_cast<uint32_t*>(&qb[hb][kk]);
-                        uint32_t* y = reinterpret_cast<uint32_t*>(&qb[hb][kk + KK / 2]);
-                        const int i0 = 32 * kk + 8 * q4;                  // pairs i0 .. i0 + 7
-                        float c8[8], s8[8];
-                        *reinterpret_cast<float4*>(c8) = *reinterpret_cast<const float4*>(cs + i0);
-                        *reinterpret_cast<float4*>(c8 + 4) = *reinterpret_cast<const float4*>(cs + i0 + 4);
-                        *reinterpret_cast<float4*>(s8) = *reinterpret_cast<const float4*>(sn + i0);
-                        *reinterpret_cast<float4*>(s8 + 4) = *reinterpret_cast<const float4*>(sn + i0 + 4);
+                for (int m = 0; m < KK / 2; ++m) {
+                    uint32_t* xa = reinterpret_cast<uint32_t*>(&x[m]);
+                    uint32_t* ya = reinterpret_cast<uint32_t*>(&x[m + KK / 2]);
 #pragma unroll
-                        for (int w = 0; w < 4; ++w) {
-                            float a0, a1, b0, b1;
-                            rope_pair(bf16_lo(x[w]), bf16_lo(y[w]), c8[2 * w], s8[2 * w], a0, b0);
-                            rope_pair(bf16_hi(x[w]), bf16_hi(y[w]), c8[2 * w + 1], s8[2 * w + 1], a1, b1);
-                            x[w] = pack_bf16x2(a0, a1);
-                            y[w] = pack_bf16x2(b0, b1);
-                        }
+                    for (int w = 0; w < 4; ++w) {
+                        const int e0 = 2 * w, e1 = 2 * w + 1;     // elements of this dword
+                        float a0, a1, b0, b1;
+                        rope_pair(bf16_lo(xa[w]), bf16_lo(ya[w]), fget(cw[2 * m + e0 / 4], e0 % 4),
+                                  fget(sw[2 * m + e0 / 4], e0 % 4), a0, b0);
+                        rope_pair(bf16_hi(xa[w]), bf16_hi(ya[w]), fget(cw[2 * m + e1 / 4], e1 % 4),
+                                  fget(sw[2 * m + e1 / 4], e1 % 4), a1, b1);
+                        xa[w] = pack_bf16x2(a0, a1);
+                        ya[w] = pack_bf16x2(b0, b1);
                     }
-                } else {
-#pragma unroll
-                    for (int kk = 0; kk < KK; ++kk) {
-                        uint32_t* x = reinterpret_cast<uint32_t*>(&qb[hb][kk]);
-                        const int i0 = (32 * kk + 8 * q4) / 2;            // pairs i0 .. i0 + 3
-                        const float4 c4 = *reinterpret_cast<const float4*>(cs + i0);
-                        const float4 s4 = *reinterpret_cast<const float4*>(sn + i0);
-                        const float cw[4] = {c4.x, c4.y, c4.z, c4.w};
-                        const float sw[4] = {s4.x, s4.y, s4.z, s4.w};
-#pragma unroll
-                        for (int w = 0; w < 4; ++w) {
-                            float r0, r1;
-                            rope_pair(bf16_lo(x[w]), bf16_hi(x[w]), cw[w], sw[w], r0, r1);
-                            x[w] = pack_bf16x2(r0, r1);
-                        }
-                    }
-                }
-                if (split == 0 && wave == 0 && p.q_rot_out) {
-#pragma unroll
-                    for (int kk = 0; kk < KK; ++kk)
-                        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.q_rot_out) + qoff + 32 * kk) = qb[hb][kk];
-                }
-            }
-        }
-    }
-
-    if constexpr (FUSED) {
-        // The split holding the new token stores it (rotated key, raw value)
-        // before any of its waves reads the tile that contains it; other
-        // splits of the sequence never read that slot.
-        if (split == nsp - 1 && L > 0) {
-            uint16_t* kdst = nullptr;
-            uint16_t* vdst = nullptr;
-            if constexpr (PAGED) {
-                const int blk = table[pos / p.block_size];      // clamped like every row read
-                const int bc = blk < 0 ? 0 : (blk >= p.num_blocks ? p.num_blocks - 1 : blk);
-                const size_t off = ((static_cast<size_t>(bc) * p.H_kv + j) * p.block_size + pos % p.block_size) * D;
-                if (blk == bc) {
-                    kdst = static_cast<uint16_t*>(const_cast<void*>(p.k)) + off;
-                    vdst = static_cast<uint16_t*>(const_cast<void*>(p.v)) + off;
                 }
             } else {
-                kdst = static_cast<uint16_t*>(const_cast<void*>(p.k)) + seq_off + static_cast<size_t>(pos) * D;
-                vdst = static_cast<uint16_t*>(const_cast<void*>(p.v)) + seq_off + static_cast<size_t>(pos) * D;
-            }
-            if (kdst && wave == 0) {
-                const uint16_t* kn = static_cast<const uint16_t*>(p.k_new) + (static_cast<size_t>(b) * p.H_kv + j) * D;
-                const uint16_t* vn = static_cast<const uint16_t*>(p.v_new) + (static_cast<size_t>(b) * p.H_kv + j) * D;
-                const float* cs = p.rope_cos + static_cast<size_t>(pos) * (D / 2);
-                const float* sn = p.rope_sin + static_cast<size_t>(pos) * (D / 2);
-                for (int i = lane; i < D / 2; i += 64) {
-                    int e0, e1;
-                    if (p.rope_style == KVC_ROPE_HALF) { e0 = i; e1 = i + D / 2; }
-                    else { e0 = 2 * i; e1 = 2 * i + 1; }
-                    float r0, r1;
-                    rope_pair(bf16_bits_to_f32(kn[e0]), bf16_bits_to_f32(kn[e1]), cs[i], sn[i], r0, r1);
-                    kdst[e0] = f32_to_bf16_rne(r0);
-                    kdst[e1] = f32_to_bf16_rne(r1);
-                    vdst[2 * i] = vn[2 * i];
-                    vdst[2 * i + 1] = vn[2 * i + 1];
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) {
+                    uint32_t* xa = reinterpret_cast<uint32_t*>(&x[kk]);
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        float r0, r1;
+                        rope_pair(bf16_lo(xa[w]), bf16_hi(xa[w]), fget(cw[kk], w), fget(sw[kk], w), r0, r1);
+                        xa[w] = pack_bf16x2(r0, r1);
+                    }
                 }
             }
-            __threadfence_block();
-            __syncthreads();
+        };
+        if (pos_ok) {
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb) rotate(qb[hb]);
         }
-        // Every path (split 0 stores the rotated query, the last split stores
-        // the new token) enters the tile pipeline with nothing in flight, so
-        // the pipeline's waits stay exact.
-        __builtin_amdgcn_s_waitcnt(0);
+        rotate(kn);
+
+        // the new token's slot (a clamped table entry would be another
+        // sequence's block: then nothing is stored)
+        if constexpr (PAGED) {
+            if (own) {
+                const int blk = table[pos / p.block_size];
+                slot_ok = blk >= 0 && blk < p.num_blocks;
+                slot = ((static_cast<size_t>(slot_ok ? blk : 0) * p.H_kv + j) * p.block_size + pos % p.block_size) * D;
+            }
+        } else {
+            slot_ok = own;
+            slot = seq_off + static_cast<size_t>(own ? pos : 0) * D;
+        }
+
+        // the token is attended over (pos < t_end) only when max_seq_len
+        // covers it; only the wave whose tile holds it patches
+        patch_row = __builtin_amdgcn_readfirstlane(slot_ok && pos < t_end ? pos : -1);
     }
 
     // transposed-read source of this lane: row tr_row (+16 for the upper half),
@@ -369,8 +386,32 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     const int s16 = lane & 15;
     const int tr_row = 4 * q4 + s16 / 4;
 
-    auto compute_tile = [&](const uint4 (&ka)[2][KK], const char* buf, int base) {
-        const char* wbuf = buf + wave * STAGE;
+    // Vector memory operations one tile issues: K rows into registers, V rows
+    // into LDS (paged caches with other block sizes add table reads, which
+    // only make the wait below more conservative).
+    constexpr int kTileLoads = 2 * KK + VLOADS;
+    static_assert(kTileLoads < 64, "vmcnt range");
+
+    auto compute_tile = [&](uint4 (&ka)[2][KK], char* buf, int base) __attribute__((always_inline)) {
+        char* wbuf = buf + wave * STAGE;
+        // the tile holding the new token (fused step): its key row goes into
+        // the K operand here, its value row over the staged one below
+        const bool patch = FUSED && static_cast<unsigned>(patch_row - base) < static_cast<unsigned>(TT);
+        const int rt = patch_row - base;
+        if constexpr (FUSED) {
+            if (patch) {
+                // lanes of row rt % 16 of block rt / 16; both blocks written
+                // through value selects (selecting between arrays would take
+                // their addresses)
+                const bool mine0 = rt < 16 && r16 == rt;
+                const bool mine1 = rt >= 16 && r16 == rt - 16;
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) {
+                    ka[0][kk] = select4(mine0, kn[kk], ka[0][kk]);
+                    ka[1][kk] = select4(mine1, kn[kk], ka[1][kk]);
+                }
+            }
+        }
         // scores S^T = K Q^T, scaled to log2 units; tokens past t_end masked
         float s[HB][8];
 #pragma unroll
@@ -424,6 +465,19 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
             l[hb] += ps;
         }
 
+        // This tile's loads were issued before the next tile's kTileLoads
+        // loads, and loads complete in order, so waiting until at most
+        // kTileLoads are outstanding means its V rows are in LDS.  The wait
+        // is explicit: the compiler's own tracking of direct-to-LDS loads
+        // was seen to drop it when the first tile is loaded before the loop
+        // (the transposed reads then ran ahead of the data from the second
+        // iteration on).
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kTileLoads));
+        if constexpr (FUSED) {
+            // (every lane writes; lanes l, l + LPR, ... write the same chunk)
+            if (patch) *reinterpret_cast<uint4*>(wbuf + rt * ROWB + 16 * ((lane % LPR) ^ swz(rt))) = vn;
+        }
+
         // O^T += V^T P^T: V^T operands read transposed from LDS
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
@@ -453,10 +507,6 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     // last row (paged) - so every path through the loop has the same loads in
     // flight and the compiler waits only for the tile it is about to use.
     if (base < t_end) {
-        if (FUSED) {
-            load_k(base, ka0);
-            load_v(base, vbuf0);
-        }
         for (;;) {
             load_k(base + kStep, ka1);
             load_v(base + kStep, vbuf1);
@@ -471,10 +521,36 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
         }
     }
 
-    // ---- merge the waves (LDS reused: all waves are past their loops)
+    // ---- merge the waves (LDS reused: all waves are past their loops, and
+    // the last prefetch into LDS must have landed before it is overwritten)
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) l[hb] = sum_same_head(l[hb]);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
+
+    if constexpr (FUSED) {
+        // Results of the append: the rotated query (split 0) and the new
+        // token's rotated key and raw value (the split that holds it),
+        // stored once every load of this workgroup has completed.  Nothing in
+        // this kernel reads them back (the holding split patched the token
+        // into its tile), so they can wait until here.
+        const bool qout = split == 0 && wave == 0 && p.q_rot_out != nullptr;
+        const __amdgpu_buffer_rsrc_t qors =
+            make_uniform_rsrc(qout ? static_cast<uint16_t*>(p.q_rot_out) + qgrp : p.q_rot_out, qout ? G * D * 2 : 0);
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, qb[hb][kk]), qors,
+                                                       ((16 * hb + r16) * D + 32 * kk + 8 * q4) * 2, 0, 0);
+        const bool st = slot_ok && wave == 0;
+        const __amdgpu_buffer_rsrc_t ksrs = make_uniform_rsrc(static_cast<const uint16_t*>(p.k) + slot, st ? D * 2 : 0);
+        const __amdgpu_buffer_rsrc_t vsrs = make_uniform_rsrc(static_cast<const uint16_t*>(p.v) + slot, st ? D * 2 : 0);
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, kn[kk]), ksrs, (32 * kk + 8 * q4) * 2, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, vn), vsrs, (lane % LPR) * 16, 0, 0);
+    }
     float* sm_o = reinterpret_cast<float*>(vbuf0);                // [NW][16][D]
     float* sm_m = reinterpret_cast<float*>(vbuf1);                // [NW][16]
     float* sm_l = sm_m + NW * 16;                                   // [NW][16]

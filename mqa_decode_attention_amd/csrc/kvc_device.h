@@ -20,11 +20,12 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
 
 // Round float32 to the nearest bfloat16, ties to even (integer form, so the
 // result never depends on a hardware rounding mode).  NaN stays a quiet NaN.
+// (Written as a select, so no divergent branch is generated.)
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-    uint32_t u = __builtin_bit_cast(uint32_t, f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return static_cast<uint16_t>((u >> 16) | 0x0040u);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
+    const uint32_t u = __builtin_bit_cast(uint32_t, f);
+    const uint32_t rounded = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t quiet = (u >> 16) | 0x0040u;
+    return static_cast<uint16_t>(((u & 0x7FFFFFFFu) > 0x7F800000u) ? quiet : rounded);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {

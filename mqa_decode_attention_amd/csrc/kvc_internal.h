@@ -80,14 +80,14 @@ struct DecodeParams {
 // Attended length of sequence b: from positions (a decode step, after its
 // append) or from seq_lens; clamped to [0, max_seq_len].  A step whose slot is
 // outside the cache or the rotation table attends over nothing.
+__device__ __forceinline__ int len_from_position(const DecodeParams& p, int pos) {
+    const int L = (pos >= 0 && pos < p.capacity && pos < p.rope_rows) ? pos + 1 : 0;
+    return L > p.max_seq_len ? p.max_seq_len : L;
+}
+
 __device__ __forceinline__ int attended_len(const DecodeParams& p, int b) {
-    int L;
-    if (p.positions) {
-        const int pos = p.positions[b];
-        L = (pos >= 0 && pos < p.capacity && pos < p.rope_rows) ? pos + 1 : 0;
-    } else {
-        L = p.seq_lens[b];
-    }
+    if (p.positions) return len_from_position(p, p.positions[b]);
+    const int L = p.seq_lens[b];
     return L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
 }
 
