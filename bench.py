@@ -257,7 +257,9 @@ def main():
         "config": {"workload": w.name, "batch": w.B, "H_q": w.H_q, "H_kv": w.H_kv, "head_dim": w.d,
                    "cached_tokens": [w.cached_lo, w.cached_hi], "layout": w.layout,
                    "kv_bytes_per_step": kv_bytes, "cache_replicas": R,
-                   "split_tokens": args.split_tokens or "auto"},
+                   "split_tokens": kvc.split_tokens(x.q.dtype, w.B, w.H_q, w.H_kv, w.d, max_len, args.split_tokens,
+                                                    pool_tokens=x.k_cache.shape[0] * w.block_size if w.paged else 0),
+                   "split_choice": "explicit" if args.split_tokens else "library"},
         "us_per_step": round(step_ms * 1e3, 2),
         "decode_us": round(dec_avg_ms * 1e3, 2),
         "decode_us_median": round(dec_med_ms * 1e3, 2),

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 1
+#define KVC_ABI_VERSION 2
 
 typedef enum kvc_status {
     KVC_OK = 0,
@@ -132,9 +132,13 @@ kvc_status kvc_append(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
                       int rope_style, void* stream);
 
 /*
- * Bytes of workspace kvc_decode_attn / kvc_decode_attn_paged need for these
- * sizes and this split_tokens (0 = the library's choice).  May be 0.
- * Returns (size_t)-1 for invalid sizes.
+ * Bytes of workspace kvc_decode_attn / kvc_decode_attn_paged / kvc_decode_step
+ * need for these sizes and this split_tokens (0 = the library's choice).  May
+ * be 0.  Returns (size_t)-1 for invalid sizes (kvc_last_error says why).
+ *
+ * pool_tokens is num_blocks * block_size for a paged cache (the pool's token
+ * capacity, which the library's split choice takes into account) and 0 for a
+ * contiguous cache; pass the same sizes as the decode call.
  *
  * The workspace holds the per-split partial results (running max and sum
  * per query head, weighted value sums) that the split kernel writes and the
@@ -143,7 +147,22 @@ kvc_status kvc_append(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
  * a workspace.
  */
 size_t kvc_decode_workspace_bytes(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
-                                  int max_seq_len, int split_tokens);
+                                  int max_seq_len, long long pool_tokens, int split_tokens);
+
+/*
+ * The split length (tokens per workgroup) a decode call with these sizes
+ * uses: split_tokens itself when it is positive, else the library's choice.
+ * Arguments as for kvc_decode_workspace_bytes; returns -1 for invalid sizes.
+ *
+ * The library's choice: one round of workgroups that occupies every compute
+ * unit equally (as many workgroups as the device holds at once for this
+ * kernel, spread over B * H_kv sequence-head pairs); for a paged pool much
+ * smaller than B * max_seq_len (ragged lengths), about four rounds of
+ * shorter splits; never fewer than 32 * (H_q / H_kv) tokens, so that the
+ * partial results stay a few percent of the bytes read.
+ */
+int kvc_decode_split_tokens(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_len,
+                            long long pool_tokens, int split_tokens);
 
 /*
  * kvc_decode_attn - attention of the new token over a contiguous cache.
@@ -193,9 +212,11 @@ kvc_status kvc_decode_attn_paged(kvc_dtype dtype, int B, int H_q, int H_kv, int 
  * positions[b], the query is rotated at the same position (written to
  * q_rot_out), and every query head attends over the positions[b] + 1 cached
  * tokens, the new one included.  For bf16 with head_dim 64/128/256 and
- * G <= 32 the append runs inside the streaming attention kernel (the
- * workgroup holding the new token stores it before reading it; q is rotated
- * in registers); other shapes run the append kernel first.
+ * G <= 32 the append runs inside the streaming attention kernel (q is
+ * rotated in registers; the workgroup whose split holds the new token uses
+ * the rotated key and the value from registers for that token and stores
+ * them to the cache after its pass); other shapes run the append kernel
+ * first.
  *
  * q is the raw query [B, H_q, d] (not modified); q_rot_out [B, H_q, d]
  * (required) receives the rotated query.  Cache arguments as in kvc_append
@@ -203,7 +224,7 @@ kvc_status kvc_decode_attn_paged(kvc_dtype dtype, int B, int H_q, int H_kv, int 
  * max_seq_len must be >= every positions[b] + 1; a position outside the cache
  * or the rotation table writes nothing and gives zeros for that sequence.
  * Workspace as for kvc_decode_attn (kvc_decode_workspace_bytes with the same
- * sizes and max_seq_len).
+ * sizes, max_seq_len and pool_tokens).
  */
 kvc_status kvc_decode_step(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
                            const void* q, void* q_rot_out, void* k_cache, void* v_cache, int T_max,

@@ -9,5 +9,5 @@ include/kvc.h); this package only marshals torch tensors into it:
     decode_step(q, k_cache, v_cache, positions, k_new, v_new, rope_cos, rope_sin, max_seq_len, ...)
 """
 from .api import (KVC_BF16, KVC_F32, KvcError, append, decode_attn, decode_attn_paged,  # noqa: F401
-                  decode_step, profile_next_decode, workspace_bytes)
+                  decode_step, profile_next_decode, split_tokens, workspace_bytes)
 from ._lib import LIB_PATH, load  # noqa: F401

@@ -10,8 +10,8 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvc.so")
 
-c_int, c_size_t, c_float, c_void_p, c_char_p = (ctypes.c_int, ctypes.c_size_t, ctypes.c_float,
-                                                 ctypes.c_void_p, ctypes.c_char_p)
+c_int, c_longlong, c_size_t, c_float, c_void_p, c_char_p = (ctypes.c_int, ctypes.c_longlong, ctypes.c_size_t,
+                                                             ctypes.c_float, ctypes.c_void_p, ctypes.c_char_p)
 
 # name -> (restype, argtypes); mirrors include/kvc.h
 SIGNATURES = {
@@ -25,7 +25,8 @@ SIGNATURES = {
                            c_void_p, c_int, c_int, c_int, c_void_p,
                            c_void_p, c_void_p, c_void_p,
                            c_void_p, c_void_p, c_int, c_int, c_void_p]),
-    "kvc_decode_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int, c_int, c_int]),
+    "kvc_decode_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int, c_int, c_longlong, c_int]),
+    "kvc_decode_split_tokens": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_longlong, c_int]),
     "kvc_decode_attn": (c_int, [c_int, c_int, c_int, c_int, c_int,
                                 c_void_p, c_void_p, c_void_p, c_int,
                                 c_void_p, c_int, c_float, c_void_p,
@@ -43,7 +44,7 @@ SIGNATURES = {
                                 c_int, c_void_p, c_size_t, c_void_p]),
 }
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 _lib = None
 

@@ -96,12 +96,24 @@ def append(k_cache: torch.Tensor, v_cache: torch.Tensor, positions: torch.Tensor
 
 
 def workspace_bytes(dtype: torch.dtype, B: int, H_q: int, H_kv: int, d: int, max_seq_len: int,
-                    split_tokens: int = 0) -> int:
+                    split_tokens: int = 0, pool_tokens: int = 0) -> int:
+    """kvc_decode_workspace_bytes; pool_tokens = num_blocks * block_size for a paged cache."""
     lib = _lib.load()
     code = KVC_BF16 if dtype == torch.bfloat16 else KVC_F32
-    n = lib.kvc_decode_workspace_bytes(code, B, H_q, H_kv, d, max_seq_len, split_tokens)
+    n = lib.kvc_decode_workspace_bytes(code, B, H_q, H_kv, d, max_seq_len, pool_tokens, split_tokens)
     if n == (1 << 64) - 1:
         raise KvcError(2, lib.kvc_last_error().decode() or "invalid sizes for the decode workspace")
+    return n
+
+
+def split_tokens(dtype: torch.dtype, B: int, H_q: int, H_kv: int, d: int, max_seq_len: int,
+                 split_tokens: int = 0, pool_tokens: int = 0) -> int:
+    """kvc_decode_split_tokens: the split length a decode call with these sizes uses."""
+    lib = _lib.load()
+    code = KVC_BF16 if dtype == torch.bfloat16 else KVC_F32
+    n = lib.kvc_decode_split_tokens(code, B, H_q, H_kv, d, max_seq_len, pool_tokens, split_tokens)
+    if n < 0:
+        raise KvcError(2, lib.kvc_last_error().decode() or "invalid sizes")
     return n
 
 
@@ -170,7 +182,8 @@ def decode_attn_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tenso
     dt, B, H_q, d, out = _decode_args(q, out)
     num_blocks, H_kv, block_size, _ = k_pool.shape
     st = _stream(q.device, stream)
-    need = workspace_bytes(q.dtype, B, H_q, H_kv, d, max_seq_len, split_tokens)
+    need = workspace_bytes(q.dtype, B, H_q, H_kv, d, max_seq_len, split_tokens,
+                           pool_tokens=num_blocks * block_size)
     if workspace is not None:
         ws, wsn = _dev(workspace, "workspace", torch.uint8), workspace.numel()
     else:
@@ -214,7 +227,8 @@ def decode_step(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         tbl, block_size, mb, num_blocks = None, 0, 0, 0
         shape = (B, H_kv, T_max, d)
     st = _stream(q.device, stream)
-    need = workspace_bytes(q.dtype, B, H_q, H_kv, d, max_seq_len, split_tokens)
+    need = workspace_bytes(q.dtype, B, H_q, H_kv, d, max_seq_len, split_tokens,
+                           pool_tokens=num_blocks * block_size if block_table is not None else 0)
     if workspace is not None:
         ws, wsn = _dev(workspace, "workspace", torch.uint8), workspace.numel()
     else:

@@ -10,6 +10,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "kvc_internal.h"
 
@@ -53,8 +54,29 @@ int heads_per_wg(int G) {
     return 1;
 }
 
-// Workgroups the split heuristic aims for: four per compute unit of an MI355X.
+// Workgroups the split heuristic of the VALU kernel aims for: four per
+// compute unit of an MI355X.
 constexpr int kTargetWorkgroups = 4 * 256;
+
+// Compute units of the current device (256 on an MI355X, also the answer
+// when no device can be queried, e.g. when sizing a workspace on a host
+// without a GPU).  Cached per device.
+int cu_count() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+        (void)hipGetLastError();
+        n = 256;
+    }
+    cached[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
 
 // Common checks of the head/group sizes.
 kvc_status check_heads(kvc_dtype dt, int B, int H_q, int H_kv, int d) {
@@ -71,7 +93,7 @@ kvc_status check_heads(kvc_dtype dt, int B, int H_q, int H_kv, int d) {
 namespace kvc {
 
 bool plan_decode(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_len,
-                 int split_tokens, DecodePlan* plan, const char** why) {
+                 long long pool_tokens, int split_tokens, DecodePlan* plan, const char** why) {
     DecodePlan pl{};
     const int G = H_q / H_kv;
     pl.mfma = decode_mfma_supported(dtype, d, G);
@@ -84,22 +106,41 @@ bool plan_decode(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_l
     const long long units = static_cast<long long>(B) * H_kv * pl.n_chunks;
     const int tile = pl.mfma ? decode_mfma_tile_tokens() : decode_tile_tokens(dtype, d);
     const int L = std::max(max_seq_len, 1);
-    int ts;
+    long long ts;
     if (split_tokens > 0) {
         ts = split_tokens;
         if ((L + ts - 1) / ts > kMaxSplits) {
             *why = "split_tokens gives more splits than the merge step supports";
             return false;
         }
+    } else if (pl.mfma) {
+        // One round of workgroups that fills every compute unit equally
+        // streams best: fewer leave CUs idle, a partial second round leaves
+        // a tail.  A paged pool holding much less than B * L tokens means
+        // ragged lengths, where about four rounds of shorter splits even out
+        // the per-sequence work.  Each split also writes G partial rows
+        // (about G / split_tokens of the bytes it reads): at least 32 * G
+        // tokens per split keeps that near 3 %.
+        const long long slots = static_cast<long long>(cu_count()) * decode_mfma_wgs_per_cu(d, G);
+        const long long full = units * L;
+        if (pool_tokens > 0 && pool_tokens * H_kv * 10 < full * 9) {
+            ts = (pool_tokens * H_kv + 4 * slots - 1) / (4 * slots);
+        } else {
+            const long long S = std::max(1LL, slots / std::max(1LL, units));
+            ts = (L + S - 1) / S;
+        }
+        ts = std::max<long long>(ts, 32LL * G);
+        ts = (ts + tile - 1) / tile * tile;
+        while ((L + ts - 1) / ts > kMaxSplits) ts += tile;
     } else {
         long long want = units > 0 ? (kTargetWorkgroups + units - 1) / units : 1;
         want = std::max(1LL, std::min<long long>(want, kMaxSplits));
-        ts = static_cast<int>((L + want - 1) / want);
+        ts = (L + want - 1) / want;
         ts = (ts + tile - 1) / tile * tile;
         while ((L + ts - 1) / ts > kMaxSplits) ts += tile;
     }
-    pl.split_tokens = ts;
-    pl.n_splits = (L + ts - 1) / ts;
+    pl.split_tokens = static_cast<int>(std::min<long long>(ts, 0x7FFFFFFF));
+    pl.n_splits = static_cast<int>((L + ts - 1) / ts);
     if (pl.n_splits > 1) {
         const size_t bh = static_cast<size_t>(B) * H_q;
         pl.ws_ml = 0;
@@ -184,14 +225,34 @@ kvc_status kvc_append(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
 }
 
 size_t kvc_decode_workspace_bytes(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
-                                  int max_seq_len, int split_tokens) {
-    if (check_heads(dtype, B, H_q, H_kv, d) != KVC_OK || max_seq_len < 0 || split_tokens < 0)
+                                  int max_seq_len, long long pool_tokens, int split_tokens) {
+    if (check_heads(dtype, B, H_q, H_kv, d) != KVC_OK || max_seq_len < 0 || split_tokens < 0 ||
+        pool_tokens < 0) {
+        fail(KVC_ERR_SHAPE, "invalid sizes for the decode workspace");
         return static_cast<size_t>(-1);
+    }
     kvc::DecodePlan pl;
     const char* why = nullptr;
-    if (!kvc::plan_decode(dtype, B, H_q, H_kv, d, max_seq_len, split_tokens, &pl, &why))
+    if (!kvc::plan_decode(dtype, B, H_q, H_kv, d, max_seq_len, pool_tokens, split_tokens, &pl, &why)) {
+        fail(KVC_ERR_UNSUPPORTED, "%s", why);
         return static_cast<size_t>(-1);
+    }
+    ok();
     return pl.ws_bytes;
+}
+
+int kvc_decode_split_tokens(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_len,
+                            long long pool_tokens, int split_tokens) {
+    if (check_heads(dtype, B, H_q, H_kv, d) != KVC_OK || max_seq_len < 0 || split_tokens < 0 ||
+        pool_tokens < 0)
+        return -1;
+    kvc::DecodePlan pl;
+    const char* why = nullptr;
+    if (!kvc::plan_decode(dtype, B, H_q, H_kv, d, max_seq_len, pool_tokens, split_tokens, &pl, &why)) {
+        fail(KVC_ERR_UNSUPPORTED, "%s", why);
+        return -1;
+    }
+    return pl.split_tokens;
 }
 
 }  // extern "C"
@@ -246,7 +307,8 @@ kvc_status decode_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const
         return fail(KVC_ERR_NULL, "kvc_decode_step: a required pointer is NULL");
     kvc::DecodePlan pl;
     const char* why = nullptr;
-    if (!kvc::plan_decode(dtype, B, H_q, H_kv, d, max_seq_len, split_tokens, &pl, &why))
+    const long long pool_tokens = paged ? static_cast<long long>(num_blocks) * block_size : 0;
+    if (!kvc::plan_decode(dtype, B, H_q, H_kv, d, max_seq_len, pool_tokens, split_tokens, &pl, &why))
         return fail(KVC_ERR_UNSUPPORTED, "%s", why);
     if (pl.ws_bytes > 0) {
         if (!workspace) return fail(KVC_ERR_WORKSPACE, "decode needs %zu bytes of workspace, got NULL", pl.ws_bytes);

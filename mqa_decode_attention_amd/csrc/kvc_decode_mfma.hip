@@ -624,6 +624,17 @@ bool decode_mfma_supported(kvc_dtype dtype, int d, int G) {
 
 int decode_mfma_tile_tokens() { return 32 * kNWm; }
 
+int decode_mfma_wgs_per_cu(int d, int G) {
+    // Per workgroup: 4 waves and 2 * 32 * d * 2 * 4 bytes of LDS (two staged
+    // V tiles per wave).  Registers per lane (compiled, VGPR + AGPR): d = 64
+    // about 150 (one 16-head block) / 220 (two); d = 128 about 250 / 380;
+    // d = 256 over 256.  A SIMD holds 512 per lane, a CU 160 KiB of LDS.
+    const bool two_blocks = G > 16;
+    if (d <= 64) return two_blocks ? 2 : 3;
+    if (d <= 128) return two_blocks ? 1 : 2;
+    return 1;
+}
+
 hipError_t launch_decode_mfma(int d, int G, bool paged, bool fused, const DecodeParams& p,
                               hipStream_t stream, const KernelTiming& tm) {
     switch (d) {

@@ -92,8 +92,10 @@ __device__ __forceinline__ int attended_len(const DecodeParams& p, int b) {
 }
 
 // Returns false (and leaves *plan untouched) when the sizes cannot be planned.
+// pool_tokens: token capacity of a paged pool (num_blocks * block_size), which
+// bounds the tokens all sequences attend over together; 0 for a contiguous cache.
 bool plan_decode(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_len,
-                 int split_tokens, DecodePlan* plan, const char** why);
+                 long long pool_tokens, int split_tokens, DecodePlan* plan, const char** why);
 
 // Is there a kernel for this (dtype, head dim, heads per workgroup)?
 bool decode_supported(kvc_dtype dtype, int d, int heads_per_wg);
@@ -126,6 +128,9 @@ hipError_t launch_decode_split(kvc_dtype dtype, int d, int heads_per_wg, bool pa
 // workgroup per (sequence, KV head, split) serves all G query heads.
 bool decode_mfma_supported(kvc_dtype dtype, int d, int G);
 int decode_mfma_tile_tokens();
+// Workgroups of the MFMA decode kernel one compute unit holds at once (set by
+// its registers and LDS at this head dim and group size).
+int decode_mfma_wgs_per_cu(int d, int G);
 hipError_t launch_decode_mfma(int d, int G, bool paged, bool fused, const DecodeParams& p,
                               hipStream_t stream, const KernelTiming& tm);
 

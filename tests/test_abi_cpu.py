@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kvc_abi_version() == 1
+    assert lib.kvc_abi_version() == _lib.ABI_VERSION == 2
     for s in range(6):
         assert lib.kvc_status_string(s)
     assert lib.kvc_status_string(99) == b"unknown status"
@@ -89,7 +89,7 @@ def test_decode_host_checks(lib):
     assert _decode(lib, dt=9) == KVC_ERR_UNSUPPORTED
     # a long sequence needs splits and therefore a workspace
     assert _decode(lib, T_max=100000, L=100000) == KVC_ERR_WORKSPACE
-    need = lib.kvc_decode_workspace_bytes(BF16, 2, 8, 2, 128, 100000, 0)
+    need = lib.kvc_decode_workspace_bytes(BF16, 2, 8, 2, 128, 100000, 0, 0)
     assert need > 0
     assert _decode(lib, T_max=100000, L=100000, ws=FAKE, wsn=need - 1) == KVC_ERR_WORKSPACE
     assert _decode(lib, T_max=100000, L=100000, ws=ctypes.c_void_p(0x1008), wsn=need) == KVC_ERR_WORKSPACE
@@ -115,12 +115,35 @@ def test_paged_host_checks(lib):
 
 def test_workspace_sizes(lib):
     ws = lib.kvc_decode_workspace_bytes
-    assert ws(F32, 1, 4, 4, 16, 6, 0) == 0                        # one split, no workspace
-    assert ws(BF16, 16, 32, 8, 128, 8193, 0) > 0
+    assert ws(F32, 1, 4, 4, 16, 6, 0, 0) == 0                     # one split, no workspace
+    assert ws(BF16, 16, 32, 8, 128, 8193, 0, 0) > 0
     # explicit split: partials for B*H_q heads, n_splits each, d + 2 floats, 256-aligned regions
-    n = ws(BF16, 16, 32, 8, 128, 8193, 1024)
+    n = ws(BF16, 16, 32, 8, 128, 8193, 0, 1024)
     splits = -(-8193 // 1024)
     assert n >= 16 * 32 * splits * (128 + 2) * 4 and n % 256 == 0
-    assert ws(BF16, 16, 32, 8, 128, 8193, 8193) == 0
-    assert ws(BF16, 16, 30, 8, 128, 8193, 0) == (1 << 64) - 1     # invalid sizes
-    assert ws(BF16, 1, 64, 8, 128, 131073, 0) > 0
+    assert ws(BF16, 16, 32, 8, 128, 8193, 0, 8193) == 0
+    assert ws(BF16, 16, 30, 8, 128, 8193, 0, 0) == (1 << 64) - 1  # invalid sizes
+    assert ws(BF16, 16, 32, 8, 128, 8193, -1, 0) == (1 << 64) - 1
+    assert ws(BF16, 1, 64, 8, 128, 131073, 0, 0) > 0
+
+
+def test_split_choice(lib):
+    """The library's split length: one balanced round of workgroups, a floor of
+    32 * G tokens, shorter splits for ragged paged pools, multiples of the
+    128-token tile.  (The device count is 256 compute units when no GPU can be
+    queried, as here.)"""
+    st = lib.kvc_decode_split_tokens
+    assert st(BF16, 16, 32, 8, 128, 8193, 0, 0) == 2176         # 128 units, 512 slots: 4 splits
+    assert st(BF16, 1, 64, 8, 128, 131073, 0, 0) == 2176        # 8 units: 64 splits
+    assert st(BF16, 64, 32, 1, 128, 4097, 0, 0) == 1152         # G = 32: 256 slots, >= 1024 tokens
+    assert st(BF16, 16, 32, 8, 128, 8193, 0, 1000) == 1000      # explicit split kept
+    # paged pool holding about half of B * max_seq_len tokens: ~4 rounds of splits
+    pool = 17408 * 16
+    ts = st(BF16, 32, 32, 8, 128, 16385, pool, 0)
+    assert ts % 128 == 0 and 1024 <= ts <= 1280
+    # a pool as large as B * max_seq_len is treated like a contiguous cache
+    assert st(BF16, 32, 32, 8, 128, 16385, 32 * 16385, 0) == st(BF16, 32, 32, 8, 128, 16385, 0, 0)
+    for args in [(BF16, 16, 32, 8, 128, 8193), (BF16, 3, 12, 4, 64, 700), (BF16, 2, 24, 1, 256, 500)]:
+        t = st(*args, 0, 0)
+        assert t > 0 and t % 128 == 0 and t >= 32 * (args[2] // args[3])
+    assert st(BF16, 16, 30, 8, 128, 8193, 0, 0) == -1
