@@ -126,7 +126,8 @@ def cpu_baseline(x, n_seqs):
 
 def read_probe(gib: int = 4, reps: int = 10) -> dict:
     """Streaming-read rate of kvc_hbm_read_probe over a 4 GiB buffer (far beyond
-    the 256 MB Infinity Cache), best of several grid sizes."""
+    the 256 MB Infinity Cache), best of several grid sizes, with the default and
+    with the non-temporal cache policy (the one the decode kernels use)."""
     import ctypes
 
     import torch
@@ -136,21 +137,25 @@ def read_probe(gib: int = 4, reps: int = 10) -> dict:
     lib = kvc.load()
     nbytes = gib << 30
     buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
-    best = {}
-    for wgs in (1024, 2048, 4096, 8192):
-        sink = torch.zeros(wgs, dtype=torch.int32, device="cuda")
-        st = torch.cuda.current_stream().cuda_stream
-        rc = lib.kvc_hbm_read_probe(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()), wgs, st)
-        assert rc == 0, lib.kvc_last_error()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(reps):
-            lib.kvc_hbm_read_probe(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()), wgs, st)
-        b.record()
-        torch.cuda.synchronize()
-        gbs = nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
-        best[wgs] = round(gbs, 1)
-    return {"read_probe_gbs": best, "read_probe_best_gbs": max(best.values()), "buffer_gib": gib}
+    st = torch.cuda.current_stream().cuda_stream
+    res = {}
+    for nt in (0, 1):
+        best = {}
+        for wgs in (1024, 2048, 4096, 8192):
+            sink = torch.zeros(wgs, dtype=torch.int32, device="cuda")
+            args = (ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()), wgs, nt, st)
+            rc = lib.kvc_hbm_read_probe(*args)
+            assert rc == 0, lib.kvc_last_error()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                lib.kvc_hbm_read_probe(*args)
+            b.record()
+            torch.cuda.synchronize()
+            best[wgs] = round(nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9, 1)
+        res["nontemporal" if nt else "default"] = {"gbs": best, "best_gbs": max(best.values())}
+    res["buffer_gib"] = gib
+    return res
 
 
 def main():
@@ -273,8 +278,10 @@ def main():
     del ks, vs
     torch.cuda.empty_cache()
     probe = read_probe(reps=5)
-    res["read_ceiling"] = {"probe": "kvc_hbm_read_probe, 4 GiB, best grid", "gbs": probe["read_probe_best_gbs"],
-                           "kernel_frac_of_ceiling": round(achieved / probe["read_probe_best_gbs"], 4)}
+    ceil_nt = probe["nontemporal"]["best_gbs"]
+    res["read_ceiling"] = {"probe": "kvc_hbm_read_probe, 4 GiB, best grid",
+                           "default_policy_gbs": probe["default"]["best_gbs"], "nontemporal_gbs": ceil_nt,
+                           "kernel_frac_of_ceiling": round(achieved / ceil_nt, 4)}
     if not args.no_cpu_baseline and not w.paged:
         res["cpu_baseline"] = cpu_baseline(x, args.cpu_sample_seqs)
     print(json.dumps(res), flush=True)

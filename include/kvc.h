@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 2
+#define KVC_ABI_VERSION 3
 
 typedef enum kvc_status {
     KVC_OK = 0,
@@ -89,11 +89,14 @@ void kvc_profile_next_decode(void* start_event, void* stop_event);
 /*
  * Measurement aid: a plain streaming read of `bytes` (a multiple of 16) from
  * device buffer `buf` by `workgroups` workgroups of 256 threads, each reading
- * one contiguous slice with 16-byte loads.  Its rate is the practical HBM read
- * ceiling that a read-bound kernel such as decode attention can approach.
- * `sink` is a device buffer of `workgroups` uint32 (written almost never).
+ * one contiguous slice with 16-byte loads, with the default cache policy or,
+ * when `nontemporal` is nonzero, the non-temporal one (the policy of the
+ * decode kernels' K/V loads).  Its rate is the practical HBM read ceiling
+ * that a read-bound kernel such as decode attention can approach.  `sink` is
+ * a device buffer of `workgroups` uint32 (written almost never).
  */
-kvc_status kvc_hbm_read_probe(const void* buf, size_t bytes, void* sink, int workgroups, void* stream);
+kvc_status kvc_hbm_read_probe(const void* buf, size_t bytes, void* sink, int workgroups, int nontemporal,
+                              void* stream);
 
 /*
  * kvc_append - write the new token of every sequence into the cache.

@@ -19,7 +19,7 @@ SIGNATURES = {
     "kvc_status_string": (c_char_p, [c_int]),
     "kvc_last_error": (c_char_p, []),
     "kvc_profile_next_decode": (None, [c_void_p, c_void_p]),
-    "kvc_hbm_read_probe": (c_int, [c_void_p, c_size_t, c_void_p, c_int, c_void_p]),
+    "kvc_hbm_read_probe": (c_int, [c_void_p, c_size_t, c_void_p, c_int, c_int, c_void_p]),
     "kvc_append": (c_int, [c_int, c_int, c_int, c_int, c_int,
                            c_void_p, c_void_p, c_int,
                            c_void_p, c_int, c_int, c_int, c_void_p,
@@ -44,7 +44,7 @@ SIGNATURES = {
                                 c_int, c_void_p, c_size_t, c_void_p]),
 }
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _lib = None
 

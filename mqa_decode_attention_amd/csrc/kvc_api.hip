@@ -171,12 +171,13 @@ const char* kvc_status_string(int status) {
 
 const char* kvc_last_error(void) { return g_last_error; }
 
-kvc_status kvc_hbm_read_probe(const void* buf, size_t bytes, void* sink, int workgroups, void* stream) {
+kvc_status kvc_hbm_read_probe(const void* buf, size_t bytes, void* sink, int workgroups, int nontemporal,
+                              void* stream) {
     if (!buf || !sink) return fail(KVC_ERR_NULL, "kvc_hbm_read_probe: a required pointer is NULL");
     if (bytes < 16 || workgroups <= 0)
         return fail(KVC_ERR_SHAPE, "kvc_hbm_read_probe: need bytes >= 16 and workgroups > 0");
     return hip_status(kvc::launch_read_probe(buf, bytes, static_cast<unsigned*>(sink), workgroups,
-                                             static_cast<hipStream_t>(stream)),
+                                             nontemporal != 0, static_cast<hipStream_t>(stream)),
                       "kvc_hbm_read_probe launch");
 }
 

@@ -273,49 +273,81 @@ decode_split_kernel(const DecodeParams p) {
 
 // Merge of the splits of every (sequence, query head) by their log-sum-exp:
 // M = max_s m_s, w_s = 2^(m_s - M), out = sum_s w_s acc_s / sum_s w_s l_s.
-// One wave per (sequence, query head); lanes stride over head_dim.
+// One wave per (sequence, query head).  Lane l reads 16 bytes (columns
+// 4 * (l % C4) .. +3, C4 = D / 4) of split pass * SPL + l / C4, so one
+// wave-wide load covers SPL = 256 / D splits; the (m, l) pairs and the
+// partial rows of the first KU passes are requested together, so a merge of
+// up to KU * SPL splits waits for memory once.  Lanes holding the same
+// columns are summed at the end (fixed order: the result is deterministic).
 template <typename T, int D>
 __global__ void __launch_bounds__(256) decode_merge_kernel(const DecodeParams p) {
-    __shared__ float sm_w[4][kMaxSplits];
-    const int wave = threadIdx.x >> 6;
+    constexpr int C4 = D / 4;
+    constexpr int SPL = 64 / C4;
+    constexpr int KU = 4;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const long long bh = static_cast<long long>(blockIdx.x) * 4 + wave;
     if (bh >= static_cast<long long>(p.B) * p.H_q) return;
     const int b = static_cast<int>(bh / p.H_q);
     const int L = attended_len(p, b);
-    int nsp = (L + p.split_tokens - 1) / p.split_tokens;
+    const int nsp = (L + p.split_tokens - 1) / p.split_tokens;
     if (nsp <= 1) return;                        // written directly by the split kernel
     const float2* ml = p.ws_ml + bh * p.n_splits;
+    const float4* part = reinterpret_cast<const float4*>(p.ws_part + bh * p.n_splits * D);
+    const int c4 = lane % C4;
+    const int sub = lane / C4;
+
+    // (split indices past the last are clamped and their weight zeroed, so
+    // every load is unconditional and all of them are in flight together)
+    float4 pv[KU];
+    float2 mv[KU];
+    bool live[KU];
+    auto fetch = [&](int pass0) {
+#pragma unroll
+        for (int u = 0; u < KU; ++u) {
+            const int sp = (pass0 + u) * SPL + sub;
+            live[u] = sp < nsp;
+            const int spc = live[u] ? sp : nsp - 1;
+            pv[u] = part[static_cast<size_t>(spc) * C4 + c4];
+            mv[u] = ml[spc];
+        }
+    };
+    fetch(0);
     float M = -INFINITY;
-    for (int sp = lane; sp < nsp; sp += 64) M = fmaxf(M, ml[sp].x);
+    for (int sp = lane; sp < nsp + 63; sp += 64) M = fmaxf(M, ml[sp < nsp ? sp : nsp - 1].x);
     M = across_groups_max<1>(M);
+
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     float Ls = 0.0f;
-    for (int sp = lane; sp < nsp; sp += 64) {
-        const float2 v = ml[sp];
-        const float w = (v.x == -INFINITY) ? 0.0f : fast_exp2(v.x - M);
-        sm_w[wave][sp] = w;
-        Ls = fmaf(w, v.y, Ls);
+    for (int pass0 = 0;;) {
+#pragma unroll
+        for (int u = 0; u < KU; ++u) {
+            const float w = (!live[u] || mv[u].x == -INFINITY) ? 0.0f : fast_exp2(mv[u].x - M);
+            acc.x = fmaf(w, pv[u].x, acc.x);
+            acc.y = fmaf(w, pv[u].y, acc.y);
+            acc.z = fmaf(w, pv[u].z, acc.z);
+            acc.w = fmaf(w, pv[u].w, acc.w);
+            if (c4 == 0) Ls = fmaf(w, mv[u].y, Ls);
+        }
+        pass0 += KU;
+        if (pass0 * SPL >= nsp) break;
+        fetch(pass0);
+    }
+#pragma unroll
+    for (int off = C4; off < 64; off <<= 1) {
+        acc.x += __shfl_xor(acc.x, off, 64);
+        acc.y += __shfl_xor(acc.y, off, 64);
+        acc.z += __shfl_xor(acc.z, off, 64);
+        acc.w += __shfl_xor(acc.w, off, 64);
     }
     Ls = across_groups_sum<1>(Ls);
-    __builtin_amdgcn_wave_barrier();   // sm_w[wave] is private to this wave
-    const float* part = p.ws_part + bh * p.n_splits * D;
-    const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
-    constexpr int EPT = (D + 63) / 64;
-    float acc[EPT];
-#pragma unroll
-    for (int k = 0; k < EPT; ++k) acc[k] = 0.0f;
-    for (int sp = 0; sp < nsp; ++sp) {
-        const float w = sm_w[wave][sp];
-#pragma unroll
-        for (int k = 0; k < EPT; ++k) {
-            const int e = lane + 64 * k;
-            if (e < D) acc[k] = fmaf(w, part[static_cast<size_t>(sp) * D + e], acc[k]);
-        }
-    }
-#pragma unroll
-    for (int k = 0; k < EPT; ++k) {
-        const int e = lane + 64 * k;
-        if (e < D) store_out<T>(p.out, static_cast<size_t>(bh) * D + e, Ls > 0.0f ? acc[k] * inv : 0.0f);
+    if (sub == 0) {
+        const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
+        const size_t o = static_cast<size_t>(bh) * D + 4 * c4;
+        store_out<T>(p.out, o + 0, acc.x * inv);
+        store_out<T>(p.out, o + 1, acc.y * inv);
+        store_out<T>(p.out, o + 2, acc.z * inv);
+        store_out<T>(p.out, o + 3, acc.w * inv);
     }
 }
 

@@ -139,6 +139,6 @@ hipError_t launch_decode_merge(kvc_dtype dtype, int d, const DecodeParams& p, hi
 
 // Streaming-read probe (kvc_hbm_read_probe).
 hipError_t launch_read_probe(const void* buf, size_t bytes, unsigned* sink, int workgroups,
-                             hipStream_t stream);
+                             bool nontemporal, hipStream_t stream);
 
 }  // namespace kvc
