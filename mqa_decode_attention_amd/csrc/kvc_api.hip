@@ -121,7 +121,7 @@ bool plan_decode(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_l
         // the per-sequence work.  Each split also writes G partial rows
         // (about G / split_tokens of the bytes it reads): at least 32 * G
         // tokens per split keeps that near 3 %.
-        const long long slots = static_cast<long long>(cu_count()) * decode_mfma_wgs_per_cu(d, G);
+        const long long slots = static_cast<long long>(cu_count()) * decode_mfma_wgs_per_cu(d, G, pool_tokens > 0);
         const long long full = units * L;
         if (pool_tokens > 0 && pool_tokens * H_kv * 10 < full * 9) {
             ts = (pool_tokens * H_kv + 4 * slots - 1) / (4 * slots);

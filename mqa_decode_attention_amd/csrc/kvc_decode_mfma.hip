@@ -37,6 +37,8 @@
 //   significant bits: rounding p once to bf16 alone would leave errors of a
 //   few 1e-4 in the output, enough to move it across a bf16 rounding boundary.
 
+#include <type_traits>
+
 #include "kvc_internal.h"
 #include "kvc_device.h"
 
@@ -125,6 +127,16 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     // compiler can tell the tile being read from the one being filled.
     __shared__ __attribute__((aligned(16))) char vbuf0[NW * STAGE];
     __shared__ __attribute__((aligned(16))) char vbuf1[NW * STAGE];
+    // K tiles of a contiguous cache are staged the same way up to d = 128: a
+    // direct load moves whole 256-byte rows, while loading K straight into
+    // the MFMA operand moves 64-byte pieces of 16 rows per instruction, which
+    // streamed about 4 % slower.  (At d = 256 the four buffers would not fit
+    // in LDS.  Paged caches keep K in registers: their per-group table reads
+    // would double with K staged, and the halved occupancy could not hide
+    // them - measured twice as slow.)
+    constexpr bool KLDS = D <= 128 && MODE == 0;
+    __shared__ __attribute__((aligned(16))) char kbuf0[KLDS ? NW * STAGE : 16];
+    __shared__ __attribute__((aligned(16))) char kbuf1[KLDS ? NW * STAGE : 16];
     static_assert(NW * STAGE >= NW * 16 * D * 4 && NW * STAGE >= 2 * NW * 16 * 4, "merge area");
 
     const int wid = xcd_logical_id(blockIdx.x, p.n_wg, p.n_wg_pad);
@@ -181,6 +193,9 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     // this XOR swizzle the 16 lanes of a transposed read (4 rows x 32 bytes)
     // hit 8 distinct 16-byte bank groups, without padding the rows.
     auto swz = [](int r) { return (2 * r) & (LPR - 1); };
+    // K rows: chunk c at slot c ^ (r % LPR), so the 16 lanes reading one
+    // chunk of 16 consecutive rows for the MFMA operand hit distinct banks
+    auto swzk = [](int r) { return r & (LPR - 1); };
 
     // Contiguous caches are read through buffer resources whose range ends at
     // row t_end of this (sequence, KV head): rows past the split read as zeros
@@ -236,27 +251,48 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
             }
         }
     };
-    // V rows of a tile, HBM -> LDS without passing through registers: lane l
-    // of load i fills LDS bytes [16 l, 16 l + 16) of that load's 1 KiB, i.e. row
-    // VROWS*i + l / LPR, slot l % LPR, so it fetches chunk (slot ^ swz(row)).
-    auto load_v = [&](int base, char* buf) __attribute__((always_inline)) {
+    // Rows of a tile (V, and K when KLDS), HBM -> LDS without passing through
+    // registers: lane l of load i fills LDS bytes [16 l, 16 l + 16) of that
+    // load's 1 KiB, i.e. row VROWS*i + l / LPR, slot l % LPR, so it fetches
+    // chunk (slot ^ swizzle(row)).
+    auto load_rows = [&](auto is_k, int base, char* buf) __attribute__((always_inline)) {
+        constexpr bool ISK = decltype(is_k)::value;
+        const uint16_t* pool = ISK ? kbase : vbase;
         char* wbuf = buf + wave * STAGE;
 #pragma unroll
         for (int i = 0; i < VLOADS; ++i) {
             const int r = VROWS * i + lane / LPR;
-            const int u = (lane % LPR) ^ swz(r);
+            const int u = (lane % LPR) ^ (ISK ? swzk(r) : swz(r));
             const int t = base + r;
             lds_void_t* dst = (lds_void_t*)(wbuf + 1024 * i);
             if constexpr (MODE == 2) {
                 const int row0 = (VROWS * i / 16) * 16;           // this load's 16-row group
-                const __amdgpu_buffer_rsrc_t rs = group_rsrc(vbase, base + row0);
+                const __amdgpu_buffer_rsrc_t rs = group_rsrc(pool, base + row0);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, ((r - row0) * D + 8 * u) * 2, 0, 0, kNT);
             } else if constexpr (PAGED) {
-                const uint16_t* src = vbase + row_off(t < t_end ? t : t_end - 1) + 8 * u;
+                const uint16_t* src = pool + row_off(t < t_end ? t : t_end - 1) + 8 * u;
                 __builtin_amdgcn_global_load_lds(src, dst, 16, 0, kNT);
             } else {
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, dst, 16, (t * D + 8 * u) * 2, 0, 0, kNT);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ISK ? krs : vrs, dst, 16, (t * D + 8 * u) * 2, 0, 0, kNT);
             }
+        }
+    };
+    // one tile: K (LDS or registers), then V
+    auto load_tile = [&](int base, uint4 (&ka)[2][KK], char* kb, char* vb) __attribute__((always_inline)) {
+        if constexpr (KLDS) load_rows(std::true_type{}, base, kb);
+        else load_k(base, ka);
+        load_rows(std::false_type{}, base, vb);
+    };
+    // K operand of a tile staged in LDS: lane (r16, q4) takes 16-byte chunk
+    // 4*kk + q4 of rows r16 and 16 + r16 (the layout load_k produces)
+    auto read_k = [&](const char* kb, uint4 (&ka)[2][KK]) __attribute__((always_inline)) {
+        const char* wk = kb + wave * STAGE;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int r = 16 * h + r16;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+                ka[h][kk] = *reinterpret_cast<const uint4*>(wk + r * ROWB + 16 * ((4 * kk + q4) ^ swzk(r)));
         }
     };
 
@@ -267,8 +303,7 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     constexpr int kStep = NW * TT;
     int base = t_begin + wave * TT;
     if (base < t_end) {
-        load_k(base, ka0);
-        load_v(base, vbuf0);
+        load_tile(base, ka0, kbuf0, vbuf0);
     }
 
     // B operand Q^T: lane holds head 16*hb + r16, d = 32*kk + 8*q4 .. +7.  The
@@ -393,14 +428,21 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     const int s16 = lane & 15;
     const int tr_row = 4 * q4 + s16 / 4;
 
-    // Vector memory operations one tile issues: K rows into registers, V rows
-    // into LDS (paged caches with other block sizes add table reads, which
-    // only make the wait below more conservative).
-    constexpr int kTileLoads = 2 * KK + VLOADS;
-    static_assert(kTileLoads < 64, "vmcnt range");
+    // Vector memory operations one tile issues: K rows (into LDS, or into
+    // registers at d = 256), then V rows into LDS (paged caches with other
+    // block sizes add table reads, which only make the waits below more
+    // conservative).
+    constexpr int kTileLoads = (KLDS ? VLOADS : 2 * KK) + VLOADS;
+    static_assert(VLOADS + kTileLoads < 64, "vmcnt range");
 
-    auto compute_tile = [&](uint4 (&ka)[2][KK], char* buf, int base) __attribute__((always_inline)) {
+    auto compute_tile = [&](uint4 (&ka)[2][KK], const char* kb, char* buf, int base) __attribute__((always_inline)) {
         char* wbuf = buf + wave * STAGE;
+        if constexpr (KLDS) {
+            // this tile's K rows were loaded before its V rows and the next
+            // tile's kTileLoads loads: at most VLOADS + kTileLoads outstanding
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(VLOADS + kTileLoads));
+            read_k(kb, ka);
+        }
         // the tile holding the new token (fused step): its key row goes into
         // the K operand here, its value row over the staged one below
         const bool patch = FUSED && static_cast<unsigned>(patch_row - base) < static_cast<unsigned>(TT);
@@ -515,14 +557,14 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     // flight and the compiler waits only for the tile it is about to use.
     if (base < t_end) {
         for (;;) {
-            load_k(base + kStep, ka1);
-            load_v(base + kStep, vbuf1);
-            compute_tile(ka0, vbuf0, base);
+            load_tile(base + kStep, ka1, kbuf1, vbuf1);
+            compute_tile(ka0, kbuf0, vbuf0, base);
             base += kStep;
             if (base >= t_end) break;
-            load_k(base + kStep, ka0);
-            load_v(base + kStep, vbuf0);
-            compute_tile(ka1, vbuf1, base);
+            load_tile(base + kStep, ka0, kbuf0, vbuf0);
+            // (with K staged in LDS, one operand array serves both stages)
+            if constexpr (KLDS) compute_tile(ka0, kbuf1, vbuf1, base);
+            else compute_tile(ka1, kbuf1, vbuf1, base);
             base += kStep;
             if (base >= t_end) break;
         }
@@ -631,12 +673,16 @@ bool decode_mfma_supported(kvc_dtype dtype, int d, int G) {
 
 int decode_mfma_tile_tokens() { return 32 * kNWm; }
 
-int decode_mfma_wgs_per_cu(int d, int G) {
-    // Per workgroup: 4 waves and 2 * 32 * d * 2 * 4 bytes of LDS (two staged
-    // V tiles per wave).  Registers per lane (compiled, VGPR + AGPR): d = 64
-    // about 150 (one 16-head block) / 220 (two); d = 128 about 250 / 380;
-    // d = 256 over 256.  A SIMD holds 512 per lane, a CU 160 KiB of LDS.
+int decode_mfma_wgs_per_cu(int d, int G, bool paged) {
+    // Per workgroup: 4 waves; LDS 32 * 2d bytes per staged tile, two V tiles
+    // per wave and, for a contiguous cache up to d = 128, two K tiles: 64 KiB
+    // at d = 64 and 128 KiB at d = 128 contiguous, 32 / 64 / 128 KiB at
+    // d = 64 / 128 / 256 paged, of the 160 KiB a CU has.  Registers (VGPR +
+    // AGPR per lane, compiled): paged d = 128 about 250 with one 16-head block
+    // (two waves per SIMD), about 380 with two (one); d = 64 paged about 150
+    // / 210 (three / two).
     const bool two_blocks = G > 16;
+    if (!paged) return d <= 64 ? 2 : 1;
     if (d <= 64) return two_blocks ? 2 : 3;
     if (d <= 128) return two_blocks ? 1 : 2;
     return 1;

@@ -129,8 +129,8 @@ hipError_t launch_decode_split(kvc_dtype dtype, int d, int heads_per_wg, bool pa
 bool decode_mfma_supported(kvc_dtype dtype, int d, int G);
 int decode_mfma_tile_tokens();
 // Workgroups of the MFMA decode kernel one compute unit holds at once (set by
-// its registers and LDS at this head dim and group size).
-int decode_mfma_wgs_per_cu(int d, int G);
+// its registers and LDS at this head dim, group size and cache layout).
+int decode_mfma_wgs_per_cu(int d, int G, bool paged);
 hipError_t launch_decode_mfma(int d, int G, bool paged, bool fused, const DecodeParams& p,
                               hipStream_t stream, const KernelTiming& tm);
 

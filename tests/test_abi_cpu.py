@@ -133,16 +133,18 @@ def test_split_choice(lib):
     128-token tile.  (The device count is 256 compute units when no GPU can be
     queried, as here.)"""
     st = lib.kvc_decode_split_tokens
-    assert st(BF16, 16, 32, 8, 128, 8193, 0, 0) == 2176         # 128 units, 512 slots: 4 splits
-    assert st(BF16, 1, 64, 8, 128, 131073, 0, 0) == 2176        # 8 units: 64 splits
-    assert st(BF16, 64, 32, 1, 128, 4097, 0, 0) == 1152         # G = 32: 256 slots, >= 1024 tokens
+    # contiguous d = 128: one workgroup per CU, 256 slots
+    assert st(BF16, 16, 32, 8, 128, 8193, 0, 0) == 4224         # 128 units: 2 splits
+    assert st(BF16, 1, 64, 8, 128, 131073, 0, 0) == 4224        # 8 units: 32 splits
+    assert st(BF16, 64, 32, 1, 128, 4097, 0, 0) == 1152         # G = 32: 4 splits, >= 1024 tokens
+    assert st(BF16, 16, 32, 8, 64, 8193, 0, 0) == 2176          # d = 64: two per CU, 512 slots
     assert st(BF16, 16, 32, 8, 128, 8193, 0, 1000) == 1000      # explicit split kept
     # paged pool holding about half of B * max_seq_len tokens: ~4 rounds of splits
     pool = 17408 * 16
     ts = st(BF16, 32, 32, 8, 128, 16385, pool, 0)
     assert ts % 128 == 0 and 1024 <= ts <= 1280
-    # a pool as large as B * max_seq_len is treated like a contiguous cache
-    assert st(BF16, 32, 32, 8, 128, 16385, 32 * 16385, 0) == st(BF16, 32, 32, 8, 128, 16385, 0, 0)
+    # a pool as large as B * max_seq_len gets one round: 256 units on 512 paged slots (two per CU)
+    assert st(BF16, 32, 32, 8, 128, 16385, 32 * 16385, 0) == 8320
     for args in [(BF16, 16, 32, 8, 128, 8193), (BF16, 3, 12, 4, 64, 700), (BF16, 2, 24, 1, 256, 500)]:
         t = st(*args, 0, 0)
         assert t > 0 and t % 128 == 0 and t >= 32 * (args[2] // args[3])
