@@ -67,6 +67,9 @@ constexpr int kNT = 2;
 // powers of two (so weights stay <= 2^8 and rescales become rare).
 constexpr float kLazy = 8.0f;
 
+// Start of the running max (the largest finite float): below every real score.
+constexpr float kNoMax = 3.402823466e38f;
+
 __device__ __forceinline__ f32x4_t mfma16(const uint4& a, const uint4& b, const f32x4_t& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
@@ -166,7 +169,9 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     f32x4_t o[HB][NB];
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
-        m[hb] = -INFINITY;
+        // finite start: a tile whose rows are all masked (possible with the
+        // interleaved rows) then gives weights 2^(-inf - m) = 0, not NaN
+        m[hb] = -kNoMax;
         l[hb] = 0.0f;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) o[hb][nb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -196,6 +201,19 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     // K rows: chunk c at slot c ^ (r % LPR), so the 16 lanes reading one
     // chunk of 16 consecutive rows for the MFMA operand hit distinct banks
     auto swzk = [](int r) { return r & (LPR - 1); };
+
+    // Token of row r of this wave's tile at step base.  With K staged in LDS
+    // the waves interleave: in every 16-token group, wave w takes 4 tokens
+    // (row r -> base + 16 * (r / 4) + 4 * w + r % 4), so one load instruction
+    // of each of the 4 waves covers 16 consecutive rows and the workgroup
+    // reads its K and V as two sequential streams (a wave streaming its own
+    // 32-row block was measurably slower).  Otherwise each wave takes 32
+    // consecutive tokens from its own base.
+    constexpr bool ILV = KLDS;
+    static_assert(!ILV || NW == 4, "interleaved rows assume four waves");
+    auto tok = [&](int base, int r) __attribute__((always_inline)) {
+        return ILV ? base + 16 * (r >> 2) + 4 * wave + (r & 3) : base + r;
+    };
 
     // Contiguous caches are read through buffer resources whose range ends at
     // row t_end of this (sequence, KV head): rows past the split read as zeros
@@ -230,7 +248,7 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     auto load_k = [&](int base, uint4 (&ka)[2][KK]) __attribute__((always_inline)) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            const int t = base + 16 * kb + r16;
+            const int t = tok(base, 16 * kb + r16);
             if constexpr (MODE == 2) {
                 const __amdgpu_buffer_rsrc_t rs = group_rsrc(kbase, base + 16 * kb);
                 const int off = (r16 * D + 8 * q4) * 2;
@@ -263,7 +281,7 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
         for (int i = 0; i < VLOADS; ++i) {
             const int r = VROWS * i + lane / LPR;
             const int u = (lane % LPR) ^ (ISK ? swzk(r) : swz(r));
-            const int t = base + r;
+            const int t = tok(base, r);
             lds_void_t* dst = (lds_void_t*)(wbuf + 1024 * i);
             if constexpr (MODE == 2) {
                 const int row0 = (VROWS * i / 16) * 16;           // this load's 16-row group
@@ -301,7 +319,7 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     // token and its rotation table row).
     uint4 ka0[2][KK], ka1[2][KK];
     constexpr int kStep = NW * TT;
-    int base = t_begin + wave * TT;
+    int base = t_begin + (ILV ? 0 : wave * TT);   // step base: the workgroup's, or this wave's
     if (base < t_end) {
         load_tile(base, ka0, kbuf0, vbuf0);
     }
@@ -445,8 +463,11 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
         }
         // the tile holding the new token (fused step): its key row goes into
         // the K operand here, its value row over the staged one below
-        const bool patch = FUSED && static_cast<unsigned>(patch_row - base) < static_cast<unsigned>(TT);
-        const int rt = patch_row - base;
+        const int dp = patch_row - base;                    // new token relative to the step
+        const bool patch = FUSED && (ILV ? static_cast<unsigned>(dp) < static_cast<unsigned>(kStep) &&
+                                               ((dp >> 2) & 3) == wave
+                                         : static_cast<unsigned>(dp) < static_cast<unsigned>(TT));
+        const int rt = ILV ? 4 * (dp >> 4) + (dp & 3) : dp;  // its row in this wave's tile
         if constexpr (FUSED) {
             if (patch) {
                 // lanes of row rt % 16 of block rt / 16; both blocks written
@@ -472,7 +493,7 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
                 for (int kk = 0; kk < KK; ++kk) acc = mfma16(ka[kb][kk], qb[hb][kk], acc);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int t = base + 16 * kb + 4 * q4 + e;
+                    const int t = tok(base, 16 * kb + 4 * q4 + e);
                     s[hb][4 * kb + e] = t < t_end ? acc[e] * p.scale_log2 : -INFINITY;
                 }
             }
@@ -628,7 +649,7 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
 #pragma unroll
             for (int w = 0; w < NW; ++w) {
                 const float mw = sm_m[w * 16 + gh];
-                const float f = (mw == -INFINITY) ? 0.0f : fast_exp2(mw - M);
+                const float f = (mw == -kNoMax) ? 0.0f : fast_exp2(mw - M);
                 A = fmaf(sm_o[(w * 16 + gh) * D + c], f, A);
                 Ls = fmaf(sm_l[w * 16 + gh], f, Ls);
             }

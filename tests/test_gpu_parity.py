@@ -121,8 +121,18 @@ def test_nondefault_stream():
     compare_out(out, oracle_decode(x, k2, v2, q2), "bf16", "side stream")
 
 
-def test_paged_equals_contiguous_bitwise():
-    """The same logical cache as a contiguous buffer and as a shuffled block pool."""
+def test_paged_equals_contiguous():
+    """The same logical cache as a contiguous buffer and as a shuffled block pool.
+
+    The two kernels add the tokens in different orders (the contiguous one
+    spreads each 16-token group over its four waves, the paged one gives each
+    wave 32 consecutive tokens), so they agree to float32 rounding: after the
+    bf16 store most outputs are equal, and the rest differ where the float32
+    result lies near a bf16 rounding midpoint - one step, two across a power
+    of two - or where the output is a cancellation far below its terms (there
+    float32 rounding of terms of size ~0.1 is a few 1e-8, several bf16 steps of
+    a 1e-5 output).  A wrong block or row gives errors far larger and far more
+    frequent.  Both are also checked against the oracle elsewhere."""
     w = W.WORKLOADS["gqa_8b"].replace(B=4, cached_lo=50, cached_hi=900, T_max=912)
     x = W.draw(w)
     say("[paged == contiguous]")
@@ -146,7 +156,16 @@ def test_paged_equals_contiguous_bitwise():
         a = kvc.decode_attn(step.q, step.k, step.v, step.lens, step.max_len, split_tokens=split)
         p = kvc.decode_attn_paged(step.q, kp, vp, table.cuda(), step.lens, step.max_len, split_tokens=split)
         torch.cuda.synchronize()
-        assert torch.equal(a.view(torch.int16), p.view(torch.int16)), f"paged != contiguous (split {split})"
+        af, pf = a.float(), p.float()
+        big = torch.maximum(af.abs(), pf.abs()).clamp(min=2.0 ** -126)
+        step_ = big.frexp().exponent.float().sub(8).exp2()        # one bf16 step at the larger magnitude
+        diff = (af - pf).abs()
+        same = float((diff == 0).float().mean())
+        say(f"  split {split}: equal {same:.4f}, max diff {float(diff.max()):.3g}, mean diff {float(diff.mean()):.3g}")
+        bad = diff > 2 * step_ + 2e-6
+        assert not bool(bad.any()), f"paged vs contiguous (split {split}): {int(bad.sum())} outputs differ beyond rounding"
+        assert float(diff.mean()) < 1e-5, f"paged vs contiguous (split {split}): mean diff {float(diff.mean())}"
+        assert same > 0.95, f"paged vs contiguous (split {split}): only {same:.3f} of outputs equal"
 
 
 # ---------------------------------------------------------------------------
