@@ -134,6 +134,7 @@ def test_split_choice(lib):
     queried, as here.)"""
     st = lib.kvc_decode_split_tokens
     # contiguous d = 128: one workgroup per CU, 256 slots
+    # (splits are whole 128-token steps)
     assert st(BF16, 16, 32, 8, 128, 8193, 0, 0) == 4224         # 128 units: 2 splits
     assert st(BF16, 1, 64, 8, 128, 131073, 0, 0) == 4224        # 8 units: 32 splits
     assert st(BF16, 64, 32, 1, 128, 4097, 0, 0) == 1152         # G = 32: 4 splits, >= 1024 tokens
