@@ -75,6 +75,13 @@ __device__ __forceinline__ f32x4_t mfma16(const uint4& a, const uint4& b, const 
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// v_mfma_f32_16x16x16_bf16: A gives lane l the 4 values of row (l % 16) at
+// reduction slots 4*(l/16) .. +3, B the 4 values of column (l % 16) at the
+// same slots; the results land as in the 16x16x32 product.
+__device__ __forceinline__ f32x4_t mfma16k16(const s16x4_t& a, const uint2& b, const f32x4_t& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
+}
+
 // Two float32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
     const f32x2_t v = {lo, hi};
@@ -123,7 +130,13 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     constexpr bool PAGED = MODE != 0;
     constexpr int KK = D / 32;            // 32-wide d slices per 16-token block
     constexpr int NB = D / 16;            // 16-column blocks of V
-    constexpr int TT = 32;                // tokens per wave tile
+    // Tokens per wave tile: 16 where K is staged in LDS (contiguous cache,
+    // d <= 128), else 32.  Half-height tiles keep 8 KiB per wave (32 KiB per
+    // CU) in flight while a wave waits, the amount a plain streaming read
+    // needed for its best rate on this part; 32-row tiles doubled that and
+    // were slower.
+    constexpr int TT = (MODE == 0 && D <= 128) ? 16 : 32;
+    constexpr int KB = TT / 16;           // 16-row K blocks per tile
     constexpr int ROWB = 2 * D;           // LDS bytes per staged V row
     constexpr int STAGE = TT * ROWB;      // LDS bytes of one V tile
     // V tiles are double-buffered per wave; two separate arrays, so the
@@ -140,7 +153,7 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     constexpr bool KLDS = D <= 128 && MODE == 0;
     __shared__ __attribute__((aligned(16))) char kbuf0[KLDS ? NW * STAGE : 16];
     __shared__ __attribute__((aligned(16))) char kbuf1[KLDS ? NW * STAGE : 16];
-    static_assert(NW * STAGE >= NW * 16 * D * 4 && NW * STAGE >= 2 * NW * 16 * 4, "merge area");
+    static_assert(NW * STAGE >= 2 * NW * 16 * 4, "merge area (m, l)");
 
     const int wid = xcd_logical_id(blockIdx.x, p.n_wg, p.n_wg_pad);
     if (wid < 0) return;
@@ -245,9 +258,9 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     };
 
     // K rows of a tile, straight into A operands (registers)
-    auto load_k = [&](int base, uint4 (&ka)[2][KK]) __attribute__((always_inline)) {
+    auto load_k = [&](int base, uint4 (&ka)[KB][KK]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < KB; ++kb) {
             const int t = tok(base, 16 * kb + r16);
             if constexpr (MODE == 2) {
                 const __amdgpu_buffer_rsrc_t rs = group_rsrc(kbase, base + 16 * kb);
@@ -296,17 +309,17 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
         }
     };
     // one tile: K (LDS or registers), then V
-    auto load_tile = [&](int base, uint4 (&ka)[2][KK], char* kb, char* vb) __attribute__((always_inline)) {
+    auto load_tile = [&](int base, uint4 (&ka)[KB][KK], char* kb, char* vb) __attribute__((always_inline)) {
         if constexpr (KLDS) load_rows(std::true_type{}, base, kb);
         else load_k(base, ka);
         load_rows(std::false_type{}, base, vb);
     };
     // K operand of a tile staged in LDS: lane (r16, q4) takes 16-byte chunk
     // 4*kk + q4 of rows r16 and 16 + r16 (the layout load_k produces)
-    auto read_k = [&](const char* kb, uint4 (&ka)[2][KK]) __attribute__((always_inline)) {
+    auto read_k = [&](const char* kb, uint4 (&ka)[KB][KK]) __attribute__((always_inline)) {
         const char* wk = kb + wave * STAGE;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int h = 0; h < KB; ++h) {
             const int r = 16 * h + r16;
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk)
@@ -317,7 +330,7 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     // The first tile's loads go out before anything else, so their latency
     // overlaps the loads of the query (and, in the fused step, of the new
     // token and its rotation table row).
-    uint4 ka0[2][KK], ka1[2][KK];
+    uint4 ka0[KB][KK], ka1[KB][KK];
     constexpr int kStep = NW * TT;
     int base = t_begin + (ILV ? 0 : wave * TT);   // step base: the workgroup's, or this wave's
     if (base < t_end) {
@@ -453,7 +466,7 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     constexpr int kTileLoads = (KLDS ? VLOADS : 2 * KK) + VLOADS;
     static_assert(VLOADS + kTileLoads < 64, "vmcnt range");
 
-    auto compute_tile = [&](uint4 (&ka)[2][KK], const char* kb, char* buf, int base) __attribute__((always_inline)) {
+    auto compute_tile = [&](uint4 (&ka)[KB][KK], const char* kb, char* buf, int base) __attribute__((always_inline)) {
         char* wbuf = buf + wave * STAGE;
         if constexpr (KLDS) {
             // this tile's K rows were loaded before its V rows and the next
@@ -470,24 +483,24 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
         const int rt = ILV ? 4 * (dp >> 4) + (dp & 3) : dp;  // its row in this wave's tile
         if constexpr (FUSED) {
             if (patch) {
-                // lanes of row rt % 16 of block rt / 16; both blocks written
+                // lanes of row rt % 16 of block rt / 16; every block written
                 // through value selects (selecting between arrays would take
                 // their addresses)
-                const bool mine0 = rt < 16 && r16 == rt;
-                const bool mine1 = rt >= 16 && r16 == rt - 16;
 #pragma unroll
-                for (int kk = 0; kk < KK; ++kk) {
-                    ka[0][kk] = select4(mine0, kn[kk], ka[0][kk]);
-                    ka[1][kk] = select4(mine1, kn[kk], ka[1][kk]);
+                for (int h = 0; h < KB; ++h) {
+                    const bool mine = (rt >> 4) == h && r16 == (rt & 15);
+#pragma unroll
+                    for (int kk = 0; kk < KK; ++kk) ka[h][kk] = select4(mine, kn[kk], ka[h][kk]);
                 }
             }
         }
         // scores S^T = K Q^T, scaled to log2 units; tokens past t_end masked
-        float s[HB][8];
+        constexpr int NS = 4 * KB;            // scores per lane and head
+        float s[HB][NS];
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+            for (int kb = 0; kb < KB; ++kb) {
                 f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int kk = 0; kk < KK; ++kk) acc = mfma16(ka[kb][kk], qb[hb][kk], acc);
@@ -502,12 +515,12 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
         // tile max exceeds it by more than 2^kLazy (then O and l are rescaled);
         // otherwise p = 2^(s - m) <= 2^kLazy, exact after the final division.
         // P^T goes in as two bf16 B operands, hi + lo = p to ~16 significant bits.
-        uint4 ph[HB], pl[HB];
+        uint32_t ph[HB][NS / 2], pl[HB][NS / 2];
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb) {
             float mt = s[hb][0];
 #pragma unroll
-            for (int e = 1; e < 8; ++e) mt = fmaxf(mt, s[hb][e]);
+            for (int e = 1; e < NS; ++e) mt = fmaxf(mt, s[hb][e]);
             mt = max_same_head(mt);
             const bool move = mt > m[hb] + kLazy;
             if (__any(move)) {
@@ -518,20 +531,17 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) o[hb][nb] *= alpha;
             }
-            float pr[8], ps = 0.0f;
+            float pr[NS], ps = 0.0f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
+            for (int e = 0; e < NS; ++e) {
                 pr[e] = fast_exp2(s[hb][e] - m[hb]);
                 ps += pr[e];
             }
-            uint32_t hi[4], lo[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                hi[i] = pack2_bf16(pr[2 * i], pr[2 * i + 1]);
-                lo[i] = pack2_bf16(pr[2 * i] - bf16_lo(hi[i]), pr[2 * i + 1] - bf16_hi(hi[i]));
+            for (int i = 0; i < NS / 2; ++i) {
+                ph[hb][i] = pack2_bf16(pr[2 * i], pr[2 * i + 1]);
+                pl[hb][i] = pack2_bf16(pr[2 * i] - bf16_lo(ph[hb][i]), pr[2 * i + 1] - bf16_hi(ph[hb][i]));
             }
-            ph[hb] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-            pl[hb] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
             l[hb] += ps;
         }
 
@@ -548,24 +558,36 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
             if (patch) *reinterpret_cast<uint4*>(wbuf + rt * ROWB + 16 * ((lane % LPR) ^ swz(rt))) = vn;
         }
 
-        // O^T += V^T P^T: V^T operands read transposed from LDS
+        // O^T += V^T P^T: V^T operands read transposed from LDS.  A 32-row
+        // tile is one 16x16x32 product per column block (tokens of rows
+        // tr_row and tr_row + 16); a 16-row tile one 16x16x16 product, whose
+        // operands are exactly the low halves of those.
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             const int u = 2 * nb + (s16 % 4) / 2;
-            const int r0 = tr_row, r1 = tr_row + 16;
+            const int r0 = tr_row;
             const char* a0 = wbuf + r0 * ROWB + 16 * (u ^ swz(r0)) + 8 * (s16 & 1);
-            const char* a1 = wbuf + r1 * ROWB + 16 * (u ^ swz(r1)) + 8 * (s16 & 1);
             const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)a0);
-            const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)a1);
-            uint4 va;
-            va.x = __builtin_bit_cast(uint2, lo).x;
-            va.y = __builtin_bit_cast(uint2, lo).y;
-            va.z = __builtin_bit_cast(uint2, hi).x;
-            va.w = __builtin_bit_cast(uint2, hi).y;
+            if constexpr (KB == 2) {
+                const int r1 = tr_row + 16;
+                const char* a1 = wbuf + r1 * ROWB + 16 * (u ^ swz(r1)) + 8 * (s16 & 1);
+                const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)a1);
+                uint4 va;
+                va.x = __builtin_bit_cast(uint2, lo).x;
+                va.y = __builtin_bit_cast(uint2, lo).y;
+                va.z = __builtin_bit_cast(uint2, hi).x;
+                va.w = __builtin_bit_cast(uint2, hi).y;
 #pragma unroll
-            for (int hb = 0; hb < HB; ++hb) {
-                o[hb][nb] = mfma16(va, ph[hb], o[hb][nb]);
-                o[hb][nb] = mfma16(va, pl[hb], o[hb][nb]);
+                for (int hb = 0; hb < HB; ++hb) {
+                    o[hb][nb] = mfma16(va, make_uint4(ph[hb][0], ph[hb][1], ph[hb][2], ph[hb][3]), o[hb][nb]);
+                    o[hb][nb] = mfma16(va, make_uint4(pl[hb][0], pl[hb][1], pl[hb][2], pl[hb][3]), o[hb][nb]);
+                }
+            } else {
+#pragma unroll
+                for (int hb = 0; hb < HB; ++hb) {
+                    o[hb][nb] = mfma16k16(lo, make_uint2(ph[hb][0], ph[hb][1]), o[hb][nb]);
+                    o[hb][nb] = mfma16k16(lo, make_uint2(pl[hb][0], pl[hb][1]), o[hb][nb]);
+                }
             }
         }
     };
@@ -621,48 +643,57 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, kn[kk]), ksrs, (32 * kk + 8 * q4) * 2, 0, 0);
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, vn), vsrs, (lane % LPR) * 16, 0, 0);
     }
-    float* sm_o = reinterpret_cast<float*>(vbuf0);                // [NW][16][D]
+    // The waves' partial O go through LDS in column passes of CW columns:
+    // [NW][16][CW] floats fit in one V buffer (all of D for 32-row tiles,
+    // half of it for 16-row tiles).
+    constexpr int CW = (STAGE / 64) < D ? (STAGE / 64) : D;
+    constexpr int CP = D / CW;
+    static_assert(NW * 16 * CW * 4 <= NW * STAGE && CW % 16 == 0, "merge area");
+    float* sm_o = reinterpret_cast<float*>(vbuf0);                // [NW][16][CW]
     float* sm_m = reinterpret_cast<float*>(vbuf1);                // [NW][16]
     float* sm_l = sm_m + NW * 16;                                   // [NW][16]
     const int NT = NW * 64;
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
-        const int g = 16 * hb + r16;          // this lane's head
-        // lane holds O^T[c][g] for c = 16*nb + 4*q4 + e
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sm_o[(wave * 16 + r16) * D + 16 * nb + 4 * q4 + e] = o[hb][nb][e];
         if (q4 == 0) {
             sm_m[wave * 16 + r16] = m[hb];
             sm_l[wave * 16 + r16] = l[hb];
         }
-        __syncthreads();
         const int heads = min(16, G - 16 * hb);
-        for (int idx = tid; idx < heads * D; idx += NT) {
-            const int gh = idx / D;
-            const int c = idx % D;
-            float M = -INFINITY;
 #pragma unroll
-            for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w * 16 + gh]);
-            float A = 0.0f, Ls = 0.0f;
+        for (int cp = 0; cp < CP; ++cp) {
+            // lane holds O^T[c][g] for c = 16*nb + 4*q4 + e, g = 16*hb + r16
 #pragma unroll
-            for (int w = 0; w < NW; ++w) {
-                const float mw = sm_m[w * 16 + gh];
-                const float f = (mw == -kNoMax) ? 0.0f : fast_exp2(mw - M);
-                A = fmaf(sm_o[(w * 16 + gh) * D + c], f, A);
-                Ls = fmaf(sm_l[w * 16 + gh], f, Ls);
+            for (int nb = cp * (CW / 16); nb < (cp + 1) * (CW / 16); ++nb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    sm_o[(wave * 16 + r16) * CW + 16 * nb - cp * CW + 4 * q4 + e] = o[hb][nb][e];
+            __syncthreads();
+            for (int idx = tid; idx < heads * CW; idx += NT) {
+                const int gh = idx / CW;
+                const int cc = idx % CW;
+                const int c = cp * CW + cc;
+                float M = -INFINITY;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w * 16 + gh]);
+                float A = 0.0f, Ls = 0.0f;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) {
+                    const float mw = sm_m[w * 16 + gh];
+                    const float f = (mw == -kNoMax) ? 0.0f : fast_exp2(mw - M);
+                    A = fmaf(sm_o[(w * 16 + gh) * CW + cc], f, A);
+                    Ls = fmaf(sm_l[w * 16 + gh], f, Ls);
+                }
+                const size_t bh = static_cast<size_t>(b) * p.H_q + j * G + 16 * hb + gh;
+                if (nsp == 1) {
+                    static_cast<uint16_t*>(p.out)[bh * D + c] = f32_to_bf16_rne(Ls > 0.0f ? A / Ls : 0.0f);
+                } else {
+                    p.ws_part[(bh * p.n_splits + split) * D + c] = A;
+                    if (c == 0) p.ws_ml[bh * p.n_splits + split] = make_float2(M, Ls);
+                }
             }
-            const size_t bh = static_cast<size_t>(b) * p.H_q + j * G + 16 * hb + gh;
-            if (nsp == 1) {
-                static_cast<uint16_t*>(p.out)[bh * D + c] = f32_to_bf16_rne(Ls > 0.0f ? A / Ls : 0.0f);
-            } else {
-                p.ws_part[(bh * p.n_splits + split) * D + c] = A;
-                if (c == 0) p.ws_ml[bh * p.n_splits + split] = make_float2(M, Ls);
-            }
+            __syncthreads();
         }
-        (void)g;
-        __syncthreads();
     }
 }
 
