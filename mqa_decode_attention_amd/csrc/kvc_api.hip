@@ -104,7 +104,7 @@ bool plan_decode(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_l
         return false;
     }
     const long long units = static_cast<long long>(B) * H_kv * pl.n_chunks;
-    const int tile = pl.mfma ? decode_mfma_tile_tokens() : decode_tile_tokens(dtype, d);
+    const int tile = pl.mfma ? decode_mfma_step_tokens(d, pool_tokens > 0) : decode_tile_tokens(dtype, d);
     const int L = std::max(max_seq_len, 1);
     long long ts;
     if (split_tokens > 0) {
@@ -130,9 +130,9 @@ bool plan_decode(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_l
             ts = (L + S - 1) / S;
         }
         ts = std::max<long long>(ts, 32LL * G);
-        // Whole 128-token steps: splits that start off a step boundary
-        // (e.g. balanced 4112 + 4081 for 8193 tokens instead of 4224 + 3969)
-        // streamed 2-13 % slower.
+        // Whole loop steps of the kernel (64 or 128 tokens): splits that
+        // start off a step boundary (e.g. balanced 4112 + 4081 for 8193
+        // tokens with 128-token steps) streamed 2-13 % slower.
         ts = (ts + tile - 1) / tile * tile;
         while ((L + ts - 1) / ts > kMaxSplits) ts += tile;
     } else {

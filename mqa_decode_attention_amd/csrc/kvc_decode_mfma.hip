@@ -91,6 +91,8 @@ __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
 // s_waitcnt immediate (gfx9 encoding) that waits until at most n vector
 // memory operations are outstanding and leaves the other counters alone.
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+// ... and one that waits for every LDS (and scalar memory) operation.
+constexpr int kLgkmZero = 15 | (3 << 14) | (7 << 4);
 
 // c ? a : b on values (a conditional between two uint4 lvalues would select
 // an address, which forces register arrays into memory).
@@ -593,18 +595,26 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     };
 
     // Software pipeline: while one tile is computed, the next one's K rows
-    // (registers) and V rows (the other LDS buffer) are in flight.  The next
-    // tile is fetched unconditionally - past the split it reads zeros
-    // (contiguous: outside the buffer range, no memory traffic) or the clamped
-    // last row (paged) - so every path through the loop has the same loads in
-    // flight and the compiler waits only for the tile it is about to use.
+    // (LDS or registers) and V rows (the other LDS buffers) are in flight.
+    // The next tile is fetched unconditionally - past the split it reads
+    // zeros (contiguous: outside the buffer range, no memory traffic) or the
+    // clamped last row (paged) - so every path through the loop has the same
+    // loads in flight and the waits stay exact.  A stage is refilled only
+    // once every LDS read of it has completed: a direct load writes LDS when
+    // its data returns, outside the order of the wave's own LDS
+    // instructions, so a read still queued could see the new tile (a load
+    // past the split returns almost at once).
+    auto refill = [&](int at, uint4 (&ka)[KB][KK], char* kb, char* vb) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(kLgkmZero);
+        load_tile(at, ka, kb, vb);
+    };
     if (base < t_end) {
         for (;;) {
-            load_tile(base + kStep, ka1, kbuf1, vbuf1);
+            refill(base + kStep, ka1, kbuf1, vbuf1);
             compute_tile(ka0, kbuf0, vbuf0, base);
             base += kStep;
             if (base >= t_end) break;
-            load_tile(base + kStep, ka0, kbuf0, vbuf0);
+            refill(base + kStep, ka0, kbuf0, vbuf0);
             // (with K staged in LDS, one operand array serves both stages)
             if constexpr (KLDS) compute_tile(ka0, kbuf1, vbuf1, base);
             else compute_tile(ka1, kbuf1, vbuf1, base);
@@ -723,13 +733,16 @@ bool decode_mfma_supported(kvc_dtype dtype, int d, int G) {
     return dtype == KVC_BF16 && (d == 64 || d == 128 || d == 256) && G >= 1 && G <= 32;
 }
 
-int decode_mfma_tile_tokens() { return 32 * kNWm; }
+int decode_mfma_step_tokens(int d, bool paged) { return kNWm * ((!paged && d <= 128) ? 16 : 32); }
 
 int decode_mfma_wgs_per_cu(int d, int G, bool paged) {
-    // Per workgroup: 4 waves; LDS 32 * 2d bytes per staged tile, two V tiles
-    // per wave and, for a contiguous cache up to d = 128, two K tiles: 64 KiB
-    // at d = 64 and 128 KiB at d = 128 contiguous, 32 / 64 / 128 KiB at
-    // d = 64 / 128 / 256 paged, of the 160 KiB a CU has.  Registers (VGPR +
+    // Per workgroup: 4 waves; LDS TT * 2d bytes per staged tile, two V tiles
+    // per wave and, for a contiguous cache up to d = 128 (TT = 16), two K
+    // tiles: 32 KiB at d = 64 and 64 KiB at d = 128 contiguous (one
+    // workgroup per CU at d = 128 still streamed best: it keeps the 32 KiB
+    // per CU in flight a plain read needs), 32 / 64 / 128 KiB at d = 64 /
+    // 128 / 256 paged and 128 KiB at d = 256 contiguous (TT = 32), of the
+    // 160 KiB a CU has.  Registers (VGPR +
     // AGPR per lane, compiled): paged d = 128 about 250 with one 16-head block
     // (two waves per SIMD), about 380 with two (one); d = 64 paged about 150
     // / 210 (three / two).

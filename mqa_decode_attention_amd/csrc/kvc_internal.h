@@ -127,7 +127,9 @@ hipError_t launch_decode_split(kvc_dtype dtype, int d, int heads_per_wg, bool pa
 // The matrix-core streaming kernel (bf16; head_dim 64/128/256; G <= 32): one
 // workgroup per (sequence, KV head, split) serves all G query heads.
 bool decode_mfma_supported(kvc_dtype dtype, int d, int G);
-int decode_mfma_tile_tokens();
+// Tokens one workgroup of that kernel covers per loop step (four waves'
+// tiles); splits of a whole number of steps stream fastest.
+int decode_mfma_step_tokens(int d, bool paged);
 // Workgroups of the MFMA decode kernel one compute unit holds at once (set by
 // its registers and LDS at this head dim, group size and cache layout).
 int decode_mfma_wgs_per_cu(int d, int G, bool paged);

@@ -6,8 +6,16 @@ hipcc cross-compiles; nothing runs on a GPU).
   the last direct-to-LDS load before it.  The V rows reach LDS by direct
   loads; a build whose compiler-placed waits missed this read stale tiles
   from the second loop iteration on, so the kernels place the wait
-  themselves, and this guards it.  (Straight-line scan in layout order.)
+  themselves, and this guards it.
+* No direct-to-LDS load may be issued while an LDS read may still be
+  outstanding (an s_waitcnt lgkmcnt(0) must come between them).  A direct
+  load writes LDS when its data returns, outside the order of the wave's DS
+  instructions; a build that let the compiler move a stage's refill in among
+  the previous tile's reads of that stage gave wrong results where the refill
+  lay past the split (such loads return almost at once).
 * The kernels used at head_dim 64 / 128 must not spill to scratch.
+
+(Straight-line scans in layout order.)
 """
 import os
 import re
@@ -40,26 +48,34 @@ def asm(tmp_path_factory):
 
 
 def kernels(text):
-    """(mangled name, head_dim, instruction lines) of each streaming decode kernel."""
+    """(mangled name, head_dim, cache mode, instruction lines) of each streaming
+    decode kernel (template arguments: head_dim, head blocks, waves, mode, fused)."""
     lines = text.split("\n")
     for i, l in enumerate(lines):
-        m = re.match(r"^(_ZN3kvc\S*decode_mfma_kernelILi(\d+)E\S*):", l)
+        m = re.match(r"^(_ZN3kvc\S*decode_mfma_kernelILi(\d+)ELi\d+ELi\d+ELi(\d+)E\S*):", l)
         if m:
             end = next(k for k in range(i, len(lines)) if "s_endpgm" in lines[k])
-            yield m.group(1), int(m.group(2)), [x.split(";")[0].strip() for x in lines[i:end]]
+            yield m.group(1), int(m.group(2)), int(m.group(3)), [x.split(";")[0].strip() for x in lines[i:end]]
 
 
-def tile_loads(d):
-    """K-row loads + V-row direct loads of one 32-token tile of one wave."""
-    kk = d // 32                     # 16-byte K chunks per row and lane group
-    vloads = 32 // (64 // (d // 8))  # wave-wide 16-byte V loads per tile
-    return 2 * kk + vloads
+def tile_loads(d, mode):
+    """Vector memory operations of one wave's tile: a contiguous cache up to
+    d = 128 stages 16-row tiles, K and V both by direct loads; otherwise
+    32-row tiles, K into registers (two 16-row blocks of d / 32 chunks)."""
+    lanes_per_row = d // 8
+    if mode == 0 and d <= 128:
+        return 2 * (16 * lanes_per_row // 64)
+    return 2 * (d // 32) + 32 * lanes_per_row // 64
+
+
+def is_lds_dma(ins):
+    return ("buffer_load" in ins and ins.endswith(" lds")) or "global_load_lds" in ins
 
 
 def unguarded_transposed_reads(body, limit):
     pending, bad = False, []
     for ins in body:
-        if ("buffer_load" in ins and ins.endswith(" lds")) or "global_load_lds" in ins:
+        if is_lds_dma(ins):
             pending = True
         elif ins.startswith("s_waitcnt"):
             m = re.search(r"vmcnt\((\d+)\)", ins)
@@ -70,13 +86,36 @@ def unguarded_transposed_reads(body, limit):
     return bad
 
 
+def refills_over_pending_reads(body):
+    pending, bad = False, []
+    for ins in body:
+        if ins.startswith("ds_read"):
+            pending = True
+        elif ins.startswith("s_waitcnt"):
+            m = re.search(r"lgkmcnt\((\d+)\)", ins)
+            if m and int(m.group(1)) == 0:
+                pending = False
+        elif is_lds_dma(ins) and pending:
+            bad.append(ins)
+    return bad
+
+
 def test_transposed_reads_wait_for_their_tile(asm):
     seen = 0
-    for name, d, body in kernels(asm):
+    for name, d, mode, body in kernels(asm):
         seen += 1
-        bad = unguarded_transposed_reads(body, tile_loads(d))
+        bad = unguarded_transposed_reads(body, tile_loads(d, mode))
         assert not bad, f"{name}: transposed V reads with no wait for their tile's loads: {bad[:2]}"
     assert seen >= 12, "expected the decode kernel instantiations in the assembly"
+
+
+def test_no_refill_while_lds_reads_pending(asm):
+    seen = 0
+    for name, d, mode, body in kernels(asm):
+        seen += 1
+        bad = refills_over_pending_reads(body)
+        assert not bad, f"{name}: direct-to-LDS loads issued while LDS reads may be outstanding: {bad[:2]}"
+    assert seen >= 12
 
 
 def test_no_scratch_at_common_head_dims(asm):
