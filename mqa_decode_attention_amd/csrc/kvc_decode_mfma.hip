@@ -141,20 +141,23 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     constexpr int KB = TT / 16;           // 16-row K blocks per tile
     constexpr int ROWB = 2 * D;           // LDS bytes per staged V row
     constexpr int STAGE = TT * ROWB;      // LDS bytes of one V tile
-    // V tiles are double-buffered per wave; two separate arrays, so the
-    // compiler can tell the tile being read from the one being filled.
-    __shared__ __attribute__((aligned(16))) char vbuf0[NW * STAGE];
-    __shared__ __attribute__((aligned(16))) char vbuf1[NW * STAGE];
-    // K tiles of a contiguous cache are staged the same way up to d = 128: a
-    // direct load moves whole 256-byte rows, while loading K straight into
-    // the MFMA operand moves 64-byte pieces of 16 rows per instruction, which
-    // streamed about 4 % slower.  (At d = 256 the four buffers would not fit
-    // in LDS.  Paged caches keep K in registers: their per-group table reads
-    // would double with K staged, and the halved occupancy could not hide
-    // them - measured twice as slow.)
+    // K tiles of a contiguous cache are staged in LDS up to d = 128: a direct
+    // load moves whole 256-byte rows, while loading K straight into the MFMA
+    // operand moves 64-byte pieces of 16 rows per instruction, which streamed
+    // about 4 % slower.  (Paged caches keep K in registers: their per-group
+    // table reads would double with K staged, and the halved occupancy could
+    // not hide them - measured twice as slow.)
     constexpr bool KLDS = D <= 128 && MODE == 0;
-    __shared__ __attribute__((aligned(16))) char kbuf0[KLDS ? NW * STAGE : 16];
-    __shared__ __attribute__((aligned(16))) char kbuf1[KLDS ? NW * STAGE : 16];
+    // With K staged, each wave has one K and one V stage, each refilled as
+    // soon as the tile's computation is done with it (K after its operand
+    // reads, V after the PV product): at most one tile's K and V in flight,
+    // which streamed about 2 % faster than two full stages.  With K in
+    // registers, V is double-buffered per wave in two separate arrays (so
+    // the compiler can tell the tile being read from the one being filled)
+    // and K uses two operand arrays.
+    __shared__ __attribute__((aligned(16))) char vbuf0[NW * STAGE];
+    __shared__ __attribute__((aligned(16))) char vbuf1[KLDS ? 16 : NW * STAGE];
+    __shared__ __attribute__((aligned(16))) char kbuf[KLDS ? NW * STAGE : 16];
     static_assert(NW * STAGE >= 2 * NW * 16 * 4, "merge area (m, l)");
 
     const int wid = xcd_logical_id(blockIdx.x, p.n_wg, p.n_wg_pad);
@@ -336,7 +339,7 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     constexpr int kStep = NW * TT;
     int base = t_begin + (ILV ? 0 : wave * TT);   // step base: the workgroup's, or this wave's
     if (base < t_end) {
-        load_tile(base, ka0, kbuf0, vbuf0);
+        load_tile(base, ka0, kbuf, vbuf0);
     }
 
     // B operand Q^T: lane holds head 16*hb + r16, d = 32*kk + 8*q4 .. +7.  The
@@ -462,19 +465,31 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     const int tr_row = 4 * q4 + s16 / 4;
 
     // Vector memory operations one tile issues: K rows (into LDS, or into
-    // registers at d = 256), then V rows into LDS (paged caches with other
-    // block sizes add table reads, which only make the waits below more
-    // conservative).
+    // registers at d = 256 and for paged caches), then V rows into LDS (paged
+    // caches with other block sizes add table reads, which only make the
+    // waits below more conservative).
     constexpr int kTileLoads = (KLDS ? VLOADS : 2 * KK) + VLOADS;
     static_assert(VLOADS + kTileLoads < 64, "vmcnt range");
+    // Loads issued after this tile's V rows, before its V wait: the next
+    // tile's K rows (staged K), or the whole next tile.
+    constexpr int kAfterV = KLDS ? VLOADS : kTileLoads;
 
-    auto compute_tile = [&](uint4 (&ka)[KB][KK], const char* kb, char* buf, int base) __attribute__((always_inline)) {
+    // A stage is refilled only once every LDS read of it has completed: a
+    // direct load writes LDS when its data returns, outside the order of the
+    // wave's own LDS instructions, so a read still queued could see the new
+    // tile (a load past the split returns almost at once).  The wait also
+    // keeps the compiler from moving the refill in among those reads.
+    auto compute_tile = [&](uint4 (&ka)[KB][KK], char* kb, char* buf, int base) __attribute__((always_inline)) {
         char* wbuf = buf + wave * STAGE;
         if constexpr (KLDS) {
-            // this tile's K rows were loaded before its V rows and the next
-            // tile's kTileLoads loads: at most VLOADS + kTileLoads outstanding
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(VLOADS + kTileLoads));
+            // this tile's K rows were issued before its V rows and nothing
+            // after those: at most VLOADS outstanding
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(VLOADS));
             read_k(kb, ka);
+            // the K stage is free once those reads are done: the next
+            // tile's K rows go out now (past the split: zeros, no traffic)
+            __builtin_amdgcn_s_waitcnt(kLgkmZero);
+            load_rows(std::true_type{}, base + kStep, kb);
         }
         // the tile holding the new token (fused step): its key row goes into
         // the K operand here, its value row over the staged one below
@@ -547,14 +562,13 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
             l[hb] += ps;
         }
 
-        // This tile's loads were issued before the next tile's kTileLoads
-        // loads, and loads complete in order, so waiting until at most
-        // kTileLoads are outstanding means its V rows are in LDS.  The wait
-        // is explicit: the compiler's own tracking of direct-to-LDS loads
-        // was seen to drop it when the first tile is loaded before the loop
-        // (the transposed reads then ran ahead of the data from the second
-        // iteration on).
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kTileLoads));
+        // This tile's V rows were issued before kAfterV later loads, and
+        // loads complete in order, so waiting until at most kAfterV are
+        // outstanding means they are in LDS.  The wait is explicit: the
+        // compiler's own tracking of direct-to-LDS loads was seen to drop it
+        // when the first tile is loaded before the loop (the transposed
+        // reads then ran ahead of the data from the second iteration on).
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kAfterV));
         if constexpr (FUSED) {
             // (every lane writes; lanes l, l + LPR, ... write the same chunk)
             if (patch) *reinterpret_cast<uint4*>(wbuf + rt * ROWB + 16 * ((lane % LPR) ^ swz(rt))) = vn;
@@ -592,34 +606,42 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
                 }
             }
         }
+        if constexpr (KLDS) {
+            // the V stage is free: the next tile's V rows go out
+            __builtin_amdgcn_s_waitcnt(kLgkmZero);
+            load_rows(std::false_type{}, base + kStep, buf);
+        }
     };
 
-    // Software pipeline: while one tile is computed, the next one's K rows
-    // (LDS or registers) and V rows (the other LDS buffers) are in flight.
+    // Software pipeline.  Staged K: the tile computation itself issues the
+    // next tile's loads.  K in registers: while one tile is computed, the
+    // next one's K rows and V rows (the other LDS buffer) are in flight.
     // The next tile is fetched unconditionally - past the split it reads
     // zeros (contiguous: outside the buffer range, no memory traffic) or the
     // clamped last row (paged) - so every path through the loop has the same
-    // loads in flight and the waits stay exact.  A stage is refilled only
-    // once every LDS read of it has completed: a direct load writes LDS when
-    // its data returns, outside the order of the wave's own LDS
-    // instructions, so a read still queued could see the new tile (a load
-    // past the split returns almost at once).
-    auto refill = [&](int at, uint4 (&ka)[KB][KK], char* kb, char* vb) __attribute__((always_inline)) {
-        __builtin_amdgcn_s_waitcnt(kLgkmZero);
-        load_tile(at, ka, kb, vb);
-    };
+    // loads in flight and the waits stay exact.
     if (base < t_end) {
-        for (;;) {
-            refill(base + kStep, ka1, kbuf1, vbuf1);
-            compute_tile(ka0, kbuf0, vbuf0, base);
-            base += kStep;
-            if (base >= t_end) break;
-            refill(base + kStep, ka0, kbuf0, vbuf0);
-            // (with K staged in LDS, one operand array serves both stages)
-            if constexpr (KLDS) compute_tile(ka0, kbuf1, vbuf1, base);
-            else compute_tile(ka1, kbuf1, vbuf1, base);
-            base += kStep;
-            if (base >= t_end) break;
+        if constexpr (KLDS) {
+            for (;;) {
+                compute_tile(ka0, kbuf, vbuf0, base);
+                base += kStep;
+                if (base >= t_end) break;
+            }
+        } else {
+            auto refill = [&](int at, uint4 (&ka)[KB][KK], char* vb) __attribute__((always_inline)) {
+                __builtin_amdgcn_s_waitcnt(kLgkmZero);
+                load_tile(at, ka, kbuf, vb);
+            };
+            for (;;) {
+                refill(base + kStep, ka1, vbuf1);
+                compute_tile(ka0, kbuf, vbuf0, base);
+                base += kStep;
+                if (base >= t_end) break;
+                refill(base + kStep, ka0, vbuf0);
+                compute_tile(ka1, kbuf, vbuf1, base);
+                base += kStep;
+                if (base >= t_end) break;
+            }
         }
     }
 
@@ -660,7 +682,7 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     constexpr int CP = D / CW;
     static_assert(NW * 16 * CW * 4 <= NW * STAGE && CW % 16 == 0, "merge area");
     float* sm_o = reinterpret_cast<float*>(vbuf0);                // [NW][16][CW]
-    float* sm_m = reinterpret_cast<float*>(vbuf1);                // [NW][16]
+    float* sm_m = reinterpret_cast<float*>(KLDS ? kbuf : vbuf1);  // [NW][16]
     float* sm_l = sm_m + NW * 16;                                   // [NW][16]
     const int NT = NW * 64;
 #pragma unroll
@@ -736,13 +758,13 @@ bool decode_mfma_supported(kvc_dtype dtype, int d, int G) {
 int decode_mfma_step_tokens(int d, bool paged) { return kNWm * ((!paged && d <= 128) ? 16 : 32); }
 
 int decode_mfma_wgs_per_cu(int d, int G, bool paged) {
-    // Per workgroup: 4 waves; LDS TT * 2d bytes per staged tile, two V tiles
-    // per wave and, for a contiguous cache up to d = 128 (TT = 16), two K
-    // tiles: 32 KiB at d = 64 and 64 KiB at d = 128 contiguous (one
-    // workgroup per CU at d = 128 still streamed best: it keeps the 32 KiB
-    // per CU in flight a plain read needs), 32 / 64 / 128 KiB at d = 64 /
-    // 128 / 256 paged and 128 KiB at d = 256 contiguous (TT = 32), of the
-    // 160 KiB a CU has.  Registers (VGPR +
+    // Per workgroup: 4 waves; LDS TT * 2d bytes per staged tile.  Contiguous
+    // up to d = 128 (TT = 16): one K and one V tile per wave, 16 KiB at
+    // d = 64 and 32 KiB at d = 128 (one workgroup per CU at d = 128 still
+    // streamed best - its 32 KiB in flight is what a plain streaming read
+    // needs; two per CU measured about 1.5 % slower).  Otherwise two V
+    // tiles per wave (TT = 32): 32 / 64 / 128 KiB at d = 64 / 128 / 256, of
+    // the 160 KiB a CU has.  Registers (VGPR +
     // AGPR per lane, compiled): paged d = 128 about 250 with one 16-head block
     // (two waves per SIMD), about 380 with two (one); d = 64 paged about 150
     // / 210 (three / two).
