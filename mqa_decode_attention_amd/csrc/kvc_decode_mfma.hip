@@ -332,15 +332,13 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
         }
     };
 
-    // The first tile's loads go out before anything else, so their latency
-    // overlaps the loads of the query (and, in the fused step, of the new
-    // token and its rotation table row).
-    uint4 ka0[KB][KK], ka1[KB][KK];
+    // Prologue.  The small loads go out first (the query and, in the fused
+    // step, the new token and its rotation table row), then the first tile:
+    // loads complete in order, so the rotation waits for the small loads
+    // only and runs while the tile is in flight.
     constexpr int kStep = NW * TT;
     int base = t_begin + (ILV ? 0 : wave * TT);   // step base: the workgroup's, or this wave's
-    if (base < t_end) {
-        load_tile(base, ka0, kbuf, vbuf0);
-    }
+    uint4 ka0[KB][KK], ka1[KB][KK];
 
     // B operand Q^T: lane holds head 16*hb + r16, d = 32*kk + 8*q4 .. +7.  The
     // group's G query rows are read through a buffer resource covering exactly
@@ -360,18 +358,17 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     // split of (b, j) stores it (rotated key, raw value) and, since its own
     // tile loads may run before or after that store, patches the token into
     // the tile it loaded instead of reading it back: the key row in the K
-    // registers, the value row in the staged V tile.  Every wave issues the
+    // operand, the value row in the staged V tile.  Every wave issues the
     // same memory instructions whatever its role; a role it does not have
     // gets a buffer range of zero bytes (loads read zeros, stores are
     // dropped), so the waits of the tile pipeline stay exact.
-    int patch_row = -1;                   // token index of the patched row, or -1
-    size_t slot = 0;                      // element offset of the new token's row
-    bool slot_ok = false;                 // this split stores the new token
+    const bool pos_ok = FUSED && pos >= 0 && pos < p.capacity && pos < p.rope_rows;
+    const bool own = pos_ok && split == nsp - 1;
+    const bool half = FUSED && p.rope_style == KVC_ROPE_HALF;
     uint4 kn[KK];                         // rotated new key, A-operand layout
     uint4 vn = make_uint4(0, 0, 0, 0);    // raw new value, 16-byte chunk lane % LPR
+    float4 cw[KK], sw[KK];                // cos/sin of the pairs this lane's chunks hold
     if constexpr (FUSED) {
-        const bool pos_ok = pos >= 0 && pos < p.capacity && pos < p.rope_rows;
-        const bool own = pos_ok && split == nsp - 1;
         const size_t kv_in = (static_cast<size_t>(b) * p.H_kv + j) * D;
         const __amdgpu_buffer_rsrc_t knrs =
             make_uniform_rsrc(static_cast<const uint16_t*>(p.k_new) + kv_in, own ? D * 2 : 0);
@@ -383,24 +380,32 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
                 knrs, (32 * kk + 8 * q4) * 2, 0, 0));
         vn = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vnrs, (lane % LPR) * 16, 0, 0));
 
-        // cos/sin of the pairs this lane's chunks hold.  Adjacent pairs: chunk
-        // kk holds pairs 16*kk + 4*q4 .. +3.  Split halves: chunks m and
-        // m + KK/2 pair up element by element, pairs 32*m + 8*q4 .. +7, kept
-        // as cw[2m], cw[2m + 1].  (Row 0 stands in when the position is
-        // invalid: the query is then left as it is and nothing is stored.)
-        // (the table row is read through buffer resources, like every other
-        // load here)
-        const bool half = p.rope_style == KVC_ROPE_HALF;
+        // Adjacent pairs: chunk kk holds pairs 16*kk + 4*q4 .. +3.  Split
+        // halves: chunks m and m + KK/2 pair up element by element, pairs
+        // 32*m + 8*q4 .. +7, kept as cw[2m], cw[2m + 1].  (Row 0 stands in
+        // when the position is invalid: the query is then left as it is and
+        // nothing is stored.)
         const size_t trow = static_cast<size_t>(pos_ok ? pos : 0) * (D / 2);
         const __amdgpu_buffer_rsrc_t crs = make_uniform_rsrc(p.rope_cos + trow, D * 2);
         const __amdgpu_buffer_rsrc_t srs = make_uniform_rsrc(p.rope_sin + trow, D * 2);
-        float4 cw[KK], sw[KK];
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
             const int i0 = half ? 32 * (kk >> 1) + 8 * q4 + 4 * (kk & 1) : 16 * kk + 4 * q4;
             cw[kk] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(crs, i0 * 4, 0, 0));
             sw[kk] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(srs, i0 * 4, 0, 0));
         }
+    }
+
+    // (unconditional, like every tile load: a wave with nothing to do reads
+    // zeros or the clamped last row.  Behind a branch, the compiler's own
+    // waits for the small loads would assume the path without these loads
+    // and wait for the tile as well.)
+    load_tile(base, ka0, kbuf, vbuf0);
+
+    int patch_row = -1;                   // token index of the patched row, or -1
+    size_t slot = 0;                      // element offset of the new token's row
+    bool slot_ok = false;                 // this split stores the new token
+    if constexpr (FUSED) {
         auto fget = [](const float4& v, int i) __attribute__((always_inline)) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; };
         // rotate one vector held as KK chunks, exactly as the append kernel
         // does (float32, one rounding per operation, then bf16 RNE)
@@ -675,13 +680,17 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, kn[kk]), ksrs, (32 * kk + 8 * q4) * 2, 0, 0);
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, vn), vsrs, (lane % LPR) * 16, 0, 0);
     }
-    // The waves' partial O go through LDS in column passes of CW columns:
-    // [NW][16][CW] floats fit in one V buffer (all of D for 32-row tiles,
-    // half of it for 16-row tiles).
-    constexpr int CW = (STAGE / 64) < D ? (STAGE / 64) : D;
-    constexpr int CP = D / CW;
-    static_assert(NW * 16 * CW * 4 <= NW * STAGE && CW % 16 == 0, "merge area");
-    float* sm_o = reinterpret_cast<float*>(vbuf0);                // [NW][16][CW]
+    // The waves' partial results go through LDS, RB head rows at a time:
+    // [NW][RB][D] floats of O fit in one V buffer (RB = 8 for 16-row tiles,
+    // 16 for 32-row tiles), so up to 8 heads take one pass.  Rows are D
+    // floats apart, a multiple of the bank count: the 16-byte chunks of row
+    // r are XOR-swizzled by 4r, so the lanes writing one column block of
+    // several rows hit distinct banks.
+    constexpr int RB = (STAGE / (4 * D)) < 16 ? (STAGE / (4 * D)) : 16;
+    constexpr int NCH = D / 4;            // 16-byte chunks per row
+    static_assert(NW * RB * D * 4 <= NW * STAGE && RB >= 4, "merge area");
+    auto chunk_at = [](int row, int ch) { return ch ^ ((4 * row) & (NCH - 1)); };
+    float* sm_o = reinterpret_cast<float*>(vbuf0);                // [NW][RB][D]
     float* sm_m = reinterpret_cast<float*>(KLDS ? kbuf : vbuf1);  // [NW][16]
     float* sm_l = sm_m + NW * 16;                                   // [NW][16]
     const int NT = NW * 64;
@@ -692,19 +701,23 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
             sm_l[wave * 16 + r16] = l[hb];
         }
         const int heads = min(16, G - 16 * hb);
-#pragma unroll
-        for (int cp = 0; cp < CP; ++cp) {
+        for (int r0 = 0; r0 < heads; r0 += RB) {
             // lane holds O^T[c][g] for c = 16*nb + 4*q4 + e, g = 16*hb + r16
+            const int row = r16 - r0;
+            if (row >= 0 && row < RB && r16 < heads) {
+                float* dst = sm_o + (wave * RB + row) * D;
 #pragma unroll
-            for (int nb = cp * (CW / 16); nb < (cp + 1) * (CW / 16); ++nb)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    sm_o[(wave * 16 + r16) * CW + 16 * nb - cp * CW + 4 * q4 + e] = o[hb][nb][e];
+                for (int nb = 0; nb < NB; ++nb)
+                    *reinterpret_cast<float4*>(dst + 4 * chunk_at(row, 4 * nb + q4)) =
+                        make_float4(o[hb][nb][0], o[hb][nb][1], o[hb][nb][2], o[hb][nb][3]);
+            }
             __syncthreads();
-            for (int idx = tid; idx < heads * CW; idx += NT) {
-                const int gh = idx / CW;
-                const int cc = idx % CW;
-                const int c = cp * CW + cc;
+            const int rows = min(RB, heads - r0);
+            for (int idx = tid; idx < rows * D; idx += NT) {
+                const int gr = idx / D;
+                const int c = idx % D;
+                const int gh = r0 + gr;
+                const int at = 4 * chunk_at(gr, c / 4) + (c & 3);
                 float M = -INFINITY;
 #pragma unroll
                 for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w * 16 + gh]);
@@ -713,7 +726,7 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
                 for (int w = 0; w < NW; ++w) {
                     const float mw = sm_m[w * 16 + gh];
                     const float f = (mw == -kNoMax) ? 0.0f : fast_exp2(mw - M);
-                    A = fmaf(sm_o[(w * 16 + gh) * CW + cc], f, A);
+                    A = fmaf(sm_o[(w * RB + gr) * D + at], f, A);
                     Ls = fmaf(sm_l[w * 16 + gh], f, Ls);
                 }
                 const size_t bh = static_cast<size_t>(b) * p.H_q + j * G + 16 * hb + gh;

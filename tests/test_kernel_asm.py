@@ -15,7 +15,8 @@ hipcc cross-compiles; nothing runs on a GPU).
   lay past the split (such loads return almost at once).
 * The kernels used at head_dim 64 / 128 must not spill to scratch.
 
-(Straight-line scans in layout order.)
+Both waits are checked on every path through each kernel's control-flow
+graph (basic blocks from the labels and branches of the assembly).
 """
 import os
 import re
@@ -48,14 +49,15 @@ def asm(tmp_path_factory):
 
 
 def kernels(text):
-    """(mangled name, head_dim, cache mode, instruction lines) of each streaming
-    decode kernel (template arguments: head_dim, head blocks, waves, mode, fused)."""
+    """(mangled name, head_dim, cache mode, lines) of each streaming decode kernel
+    (template arguments: head_dim, head blocks, waves, mode, fused), from its
+    label to the end of the function (blocks may follow an s_endpgm)."""
     lines = text.split("\n")
     for i, l in enumerate(lines):
         m = re.match(r"^(_ZN3kvc\S*decode_mfma_kernelILi(\d+)ELi\d+ELi\d+ELi(\d+)E\S*):", l)
         if m:
-            end = next(k for k in range(i, len(lines)) if "s_endpgm" in lines[k])
-            yield m.group(1), int(m.group(2)), int(m.group(3)), [x.split(";")[0].strip() for x in lines[i:end]]
+            end = next(k for k in range(i, len(lines)) if lines[k].startswith(".Lfunc_end"))
+            yield m.group(1), int(m.group(2)), int(m.group(3)), [x.split(";")[0].strip() for x in lines[i + 1:end]]
 
 
 def tile_loads(d, mode):
@@ -72,32 +74,96 @@ def is_lds_dma(ins):
     return ("buffer_load" in ins and ins.endswith(" lds")) or "global_load_lds" in ins
 
 
-def unguarded_transposed_reads(body, limit):
-    pending, bad = False, []
-    for ins in body:
-        if is_lds_dma(ins):
-            pending = True
-        elif ins.startswith("s_waitcnt"):
-            m = re.search(r"vmcnt\((\d+)\)", ins)
-            if m and int(m.group(1)) <= limit:
-                pending = False
-        elif ins.startswith("ds_read_b64_tr_b16") and pending:
-            bad.append(ins)
+def basic_blocks(body):
+    """[(label, instructions, successor labels)] in layout order.  A block ends
+    at a label or after a branch or s_endpgm (blocks reached only by falling
+    through a conditional branch have no label in the assembly)."""
+    raw, label, ins = [], "entry", []
+    for line in body:
+        if re.match(r"^\.LBB\S*:$", line):
+            raw.append((label, ins))
+            label, ins = line[:-1], []
+        elif line and not line.startswith(".") and not line.startswith("%"):
+            ins.append(line)
+            if re.match(r"s_(c?branch|endpgm)", line):
+                raw.append((label, ins))
+                label, ins = f"fallthrough{len(raw)}", []
+    raw.append((label, ins))
+    out = []
+    for k, (lab, ins) in enumerate(raw):
+        succ = []
+        last = ins[-1] if ins else ""
+        m = re.match(r"s_(c?)branch\S*\s+(\.LBB\S+)", last)
+        if m:
+            succ.append(m.group(2))
+        if not (last.startswith("s_branch") or last.startswith("s_endpgm")) and k + 1 < len(raw):
+            succ.append(raw[k + 1][0])
+        out.append((lab, ins, succ))
+    return out
+
+
+def flagged(body, sets, clears, check):
+    """Instructions satisfying `check` that some path reaches with a `sets`
+    instruction after the last `clears` one (forward dataflow, OR at joins)."""
+    bl = basic_blocks(body)
+    idx = {lab: k for k, (lab, _, _) in enumerate(bl)}
+    state_in = [False] * len(bl)
+
+    def run(k, report=None):
+        st = state_in[k]
+        for i in bl[k][1]:
+            if report is not None and check(i) and st:
+                report.append(i)
+            if sets(i):
+                st = True
+            elif clears(i):
+                st = False
+        return st
+
+    changed = True
+    while changed:
+        changed = False
+        for k in range(len(bl)):
+            if run(k):
+                for s in bl[k][2]:
+                    j = idx.get(s)
+                    if j is not None and not state_in[j]:
+                        state_in[j] = changed = True
+    bad = []
+    for k in range(len(bl)):
+        run(k, bad)
     return bad
+
+
+def waitcnt_field(ins, field):
+    m = re.search(field + r"\((\d+)\)", ins) if ins.startswith("s_waitcnt") else None
+    return int(m.group(1)) if m else None
+
+
+def unguarded_transposed_reads(body, limit):
+    def clears(i):
+        v = waitcnt_field(i, "vmcnt")
+        return v is not None and v <= limit
+    return flagged(body, is_lds_dma, clears, lambda i: i.startswith("ds_read_b64_tr_b16"))
 
 
 def refills_over_pending_reads(body):
-    pending, bad = False, []
-    for ins in body:
-        if ins.startswith("ds_read"):
-            pending = True
-        elif ins.startswith("s_waitcnt"):
-            m = re.search(r"lgkmcnt\((\d+)\)", ins)
-            if m and int(m.group(1)) == 0:
-                pending = False
-        elif is_lds_dma(ins) and pending:
-            bad.append(ins)
-    return bad
+    return flagged(body, lambda i: i.startswith("ds_read"), lambda i: waitcnt_field(i, "lgkmcnt") == 0, is_lds_dma)
+
+
+def test_dataflow_sees_waits_on_back_edges():
+    """The checker itself: a wait placed on the loop's back edge, laid out after
+    the read it guards, counts; a path that skips it does not."""
+    loop = [".LBB0_1:", "ds_read_b64_tr_b16 v[0:1], v2", "buffer_load_dwordx4 v3, s[0:3], 0 offen lds",
+            "s_waitcnt vmcnt(4)", "s_cbranch_scc1 .LBB0_1", "s_endpgm"]
+    pre = ["buffer_load_dwordx4 v3, s[0:3], 0 offen lds", "s_waitcnt vmcnt(0)"]
+    assert unguarded_transposed_reads(pre + loop, 4) == []
+    skip = ["buffer_load_dwordx4 v3, s[0:3], 0 offen lds", "s_cbranch_vccz .LBB0_2", "s_waitcnt vmcnt(0)",
+            ".LBB0_2:", "ds_read_b64_tr_b16 v[0:1], v2", "s_endpgm"]
+    assert unguarded_transposed_reads(skip, 4) == ["ds_read_b64_tr_b16 v[0:1], v2"]
+    refill = ["ds_read_b128 v[0:3], v4", "s_cbranch_vccz .LBB0_3", "s_waitcnt lgkmcnt(0)", ".LBB0_3:",
+              "buffer_load_dwordx4 v3, s[0:3], 0 offen lds", "s_endpgm"]
+    assert refills_over_pending_reads(refill) == ["buffer_load_dwordx4 v3, s[0:3], 0 offen lds"]
 
 
 def test_transposed_reads_wait_for_their_tile(asm):
