@@ -63,6 +63,10 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // access pattern, measured with the library's read probe).
 constexpr int kNT = 2;
 
+// Block-table entries of one split that the paged kernel with staged tiles
+// (MODE 3) keeps in LDS (4 KiB): splits spanning more blocks use MODE 2.
+constexpr int kTblMax = 1024;
+
 // The running max is moved only when a tile exceeds it by more than this many
 // powers of two (so weights stay <= 2^8 and rescales become rare).
 constexpr float kLazy = 8.0f;
@@ -123,7 +127,10 @@ __device__ __forceinline__ float sum_same_head(float x) {
 // MODE 0: contiguous cache.  MODE 1: paged, any block size (each row's block
 // looked up per lane).  MODE 2: paged with block_size % 16 == 0 and splits
 // starting on 32-token boundaries, so every 16-row group of a tile lies in one
-// block: one wave-uniform table lookup per group.
+// block: one wave-uniform table lookup per group.  MODE 3: paged, d <= 128,
+// block_size % 16 == 0, splits starting on 16-token boundaries and spanning at
+// most kTblMax blocks: the split's slice of the block table is staged in LDS
+// once, and K and V tiles are staged like those of a contiguous cache.
 template <int D, int HB, int NW, int MODE, bool FUSED>
 __global__ void __launch_bounds__(NW * 64)
 decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table) {
@@ -132,22 +139,21 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     constexpr bool PAGED = MODE != 0;
     constexpr int KK = D / 32;            // 32-wide d slices per 16-token block
     constexpr int NB = D / 16;            // 16-column blocks of V
-    // Tokens per wave tile: 16 where K is staged in LDS (contiguous cache,
-    // d <= 128), else 32.  Half-height tiles keep 8 KiB per wave (32 KiB per
-    // CU) in flight while a wave waits, the amount a plain streaming read
-    // needed for its best rate on this part; 32-row tiles doubled that and
-    // were slower.
-    constexpr int TT = (MODE == 0 && D <= 128) ? 16 : 32;
+    // K tiles are staged in LDS up to d = 128 (contiguous caches, and paged
+    // ones in MODE 3): a direct load moves whole 256-byte rows, while loading
+    // K straight into the MFMA operand moves 64-byte pieces of 16 rows per
+    // instruction, which streamed about 4 % slower.  (MODE 2 keeps K in
+    // registers: there, staging K doubled its per-group scalar table reads,
+    // which the halved occupancy could not hide - measured twice as slow.)
+    constexpr bool KLDS = D <= 128 && (MODE == 0 || MODE == 3);
+    // Tokens per wave tile: 16 where K is staged, else 32.  Half-height tiles
+    // keep 8 KiB per wave (32 KiB per CU) in flight while a wave waits, the
+    // amount a plain streaming read needed for its best rate on this part;
+    // 32-row tiles doubled that and were slower.
+    constexpr int TT = KLDS ? 16 : 32;
     constexpr int KB = TT / 16;           // 16-row K blocks per tile
     constexpr int ROWB = 2 * D;           // LDS bytes per staged V row
     constexpr int STAGE = TT * ROWB;      // LDS bytes of one V tile
-    // K tiles of a contiguous cache are staged in LDS up to d = 128: a direct
-    // load moves whole 256-byte rows, while loading K straight into the MFMA
-    // operand moves 64-byte pieces of 16 rows per instruction, which streamed
-    // about 4 % slower.  (Paged caches keep K in registers: their per-group
-    // table reads would double with K staged, and the halved occupancy could
-    // not hide them - measured twice as slow.)
-    constexpr bool KLDS = D <= 128 && MODE == 0;
     // With K staged, each wave has one K and one V stage, each refilled as
     // soon as the tile's computation is done with it (K after its operand
     // reads, V after the PV product): at most one tile's K and V in flight,
@@ -158,9 +164,15 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     __shared__ __attribute__((aligned(16))) char vbuf0[NW * STAGE];
     __shared__ __attribute__((aligned(16))) char vbuf1[KLDS ? 16 : NW * STAGE];
     __shared__ __attribute__((aligned(16))) char kbuf[KLDS ? NW * STAGE : 16];
+    __shared__ int tbl_lds[MODE == 3 ? kTblMax : 1];
     static_assert(NW * STAGE >= 2 * NW * 16 * 4, "merge area (m, l)");
 
-    const int wid = xcd_logical_id(blockIdx.x, p.n_wg, p.n_wg_pad);
+    // Workgroups in launch order: the splits of one (sequence, KV head) are
+    // neighbours, and the hardware deals consecutive workgroups to the XCDs
+    // in turn.  (Grouping each unit's splits on one XCD gains nothing for a
+    // stream without reuse, and with ragged lengths it left some XCDs with
+    // far more work than others: the paged workload ran 2.4 % slower.)
+    const int wid = blockIdx.x < static_cast<unsigned>(p.n_wg) ? static_cast<int>(blockIdx.x) : -1;
     if (wid < 0) return;
     const int split = wid % p.n_splits;
     const int unit = wid / p.n_splits;    // b * H_kv + j
@@ -227,7 +239,9 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     // reads its K and V as two sequential streams (a wave streaming its own
     // 32-row block was measurably slower).  Otherwise each wave takes 32
     // consecutive tokens from its own base.
-    constexpr bool ILV = KLDS;
+    // (Paged tiles are not interleaved: each wave's 16 rows then lie in one
+    // block, found with one table lookup.)
+    constexpr bool ILV = KLDS && MODE == 0;
     static_assert(!ILV || NW == 4, "interleaved rows assume four waves");
     auto tok = [&](int base, int r) __attribute__((always_inline)) {
         return ILV ? base + 16 * (r >> 2) + 4 * wave + (r & 3) : base + r;
@@ -258,6 +272,24 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
             blk = __builtin_amdgcn_readfirstlane(table[lb]);
             blk = blk < 0 ? 0 : (blk >= p.num_blocks ? p.num_blocks - 1 : blk);
         }
+        const uint16_t* g0 = pool + ((static_cast<size_t>(blk) * p.H_kv + j) * p.block_size + in_blk) * D;
+        return make_uniform_rsrc(g0, nvalid * D * 2);
+    };
+
+    // MODE 3: buffer resource of the wave's 16-row tile at row0 (wave-uniform,
+    // a multiple of 16, so the rows lie in one block), its block id read from
+    // the staged table slice; its range ends at the last row < t_end, so rows
+    // past the split read as zeros without a memory access.
+    const int fb = PAGED ? t_begin / p.block_size : 0;   // first block index of the split
+    auto tile_rsrc = [&](const uint16_t* pool, int row0_) -> __amdgpu_buffer_rsrc_t {
+        const int row0 = __builtin_amdgcn_readfirstlane(row0_);
+        int nvalid = __builtin_amdgcn_readfirstlane(t_end) - row0;
+        nvalid = nvalid < 0 ? 0 : (nvalid > 16 ? 16 : nvalid);
+        const int lb = row0 / p.block_size;
+        int ti = lb - fb;
+        ti = ti < 0 ? 0 : (ti >= kTblMax ? kTblMax - 1 : ti);
+        const int blk = __builtin_amdgcn_readfirstlane(nvalid > 0 ? tbl_lds[ti] : 0);
+        const int in_blk = row0 - lb * p.block_size;
         const uint16_t* g0 = pool + ((static_cast<size_t>(blk) * p.H_kv + j) * p.block_size + in_blk) * D;
         return make_uniform_rsrc(g0, nvalid * D * 2);
     };
@@ -301,7 +333,10 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
             const int u = (lane % LPR) ^ (ISK ? swzk(r) : swz(r));
             const int t = tok(base, r);
             lds_void_t* dst = (lds_void_t*)(wbuf + 1024 * i);
-            if constexpr (MODE == 2) {
+            if constexpr (MODE == 3) {
+                const __amdgpu_buffer_rsrc_t rs = tile_rsrc(pool, base);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, (r * D + 8 * u) * 2, 0, 0, kNT);
+            } else if constexpr (MODE == 2) {
                 const int row0 = (VROWS * i / 16) * 16;           // this load's 16-row group
                 const __amdgpu_buffer_rsrc_t rs = group_rsrc(pool, base + row0);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, ((r - row0) * D + 8 * u) * 2, 0, 0, kNT);
@@ -339,6 +374,20 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     constexpr int kStep = NW * TT;
     int base = t_begin + (ILV ? 0 : wave * TT);   // step base: the workgroup's, or this wave's
     uint4 ka0[KB][KK], ka1[KB][KK];
+
+    // MODE 3: the table entries of the blocks this split spans (read first:
+    // the first tile's addresses depend on them).  Indices past the split are
+    // clamped to its first entry, so every read stays in this sequence's row.
+    constexpr int kTblPer = kTblMax / (NW * 64);
+    int tv[kTblPer];
+    const int nblk = PAGED ? (t_end - 1) / p.block_size - fb + 1 : 0;
+    if constexpr (MODE == 3) {
+#pragma unroll
+        for (int k = 0; k < kTblPer; ++k) {
+            const int i = tid + k * NW * 64;
+            tv[k] = table[fb + (i < nblk ? i : 0)];
+        }
+    }
 
     // B operand Q^T: lane holds head 16*hb + r16, d = 32*kk + 8*q4 .. +7.  The
     // group's G query rows are read through a buffer resource covering exactly
@@ -400,6 +449,17 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     // zeros or the clamped last row.  Behind a branch, the compiler's own
     // waits for the small loads would assume the path without these loads
     // and wait for the tile as well.)
+    if constexpr (MODE == 3) {
+        // (ids out of range are clamped into the pool, so no access leaves
+        // it; in-range ids are the caller's contract)
+#pragma unroll
+        for (int k = 0; k < kTblPer; ++k) {
+            const int i = tid + k * NW * 64;
+            const int blk = tv[k] < 0 ? 0 : (tv[k] >= p.num_blocks ? p.num_blocks - 1 : tv[k]);
+            if (i < nblk) tbl_lds[i] = blk;
+        }
+        __syncthreads();
+    }
     load_tile(base, ka0, kbuf, vbuf0);
 
     int patch_row = -1;                   // token index of the patched row, or -1
@@ -749,6 +809,10 @@ hipError_t launch_dhf(bool paged, const DecodeParams& p, hipStream_t stream, con
     const dim3 grid(p.n_wg_pad), block(kNWm * 64);
     const int32_t* tbl = p.block_table;
     if (!paged) return launch_timed(decode_mfma_kernel<D, HB, kNWm, 0, FUSED>, grid, block, stream, tm, p, tbl);
+    if constexpr (D <= 128) {
+        if (p.block_size % 16 == 0 && p.split_tokens % 16 == 0 && p.split_tokens / p.block_size + 2 <= kTblMax)
+            return launch_timed(decode_mfma_kernel<D, HB, kNWm, 3, FUSED>, grid, block, stream, tm, p, tbl);
+    }
     if (p.block_size % 16 == 0 && p.split_tokens % 32 == 0)
         return launch_timed(decode_mfma_kernel<D, HB, kNWm, 2, FUSED>, grid, block, stream, tm, p, tbl);
     return launch_timed(decode_mfma_kernel<D, HB, kNWm, 1, FUSED>, grid, block, stream, tm, p, tbl);
@@ -768,23 +832,21 @@ bool decode_mfma_supported(kvc_dtype dtype, int d, int G) {
     return dtype == KVC_BF16 && (d == 64 || d == 128 || d == 256) && G >= 1 && G <= 32;
 }
 
-int decode_mfma_step_tokens(int d, bool paged) { return kNWm * ((!paged && d <= 128) ? 16 : 32); }
+int decode_mfma_step_tokens(int d, bool /*paged*/) { return kNWm * (d <= 128 ? 16 : 32); }
 
 int decode_mfma_wgs_per_cu(int d, int G, bool paged) {
-    // Per workgroup: 4 waves; LDS TT * 2d bytes per staged tile.  Contiguous
-    // up to d = 128 (TT = 16): one K and one V tile per wave, 16 KiB at
-    // d = 64 and 32 KiB at d = 128 (one workgroup per CU at d = 128 still
-    // streamed best - its 32 KiB in flight is what a plain streaming read
-    // needs; two per CU measured about 1.5 % slower).  Otherwise two V
-    // tiles per wave (TT = 32): 32 / 64 / 128 KiB at d = 64 / 128 / 256, of
-    // the 160 KiB a CU has.  Registers (VGPR +
-    // AGPR per lane, compiled): paged d = 128 about 250 with one 16-head block
-    // (two waves per SIMD), about 380 with two (one); d = 64 paged about 150
-    // / 210 (three / two).
+    // Per workgroup: 4 waves; LDS TT * 2d bytes per staged tile.  Up to
+    // d = 128 (TT = 16): one K and one V tile per wave, 16 KiB at d = 64 and
+    // 32 KiB at d = 128, plus 4 KiB of block table when paged.  A contiguous
+    // cache at d = 128 still streamed best with one workgroup per CU (its
+    // 32 KiB in flight is what a plain streaming read needs; two measured
+    // about 1.5 % slower); a ragged paged pool, whose many short splits each
+    // pay a prologue, with three (registers: about 168 per lane with one
+    // 16-head block, three waves per SIMD; about 260 with two, one).  At
+    // d = 256 (TT = 32, K in registers): two V tiles per wave, 128 KiB.
     const bool two_blocks = G > 16;
-    if (!paged) return d <= 64 ? 2 : 1;
-    if (d <= 64) return two_blocks ? 2 : 3;
-    if (d <= 128) return two_blocks ? 1 : 2;
+    if (d <= 64) return two_blocks ? 2 : (paged ? 3 : 2);
+    if (d <= 128) return two_blocks ? 1 : (paged ? 3 : 1);
     return 1;
 }
 
