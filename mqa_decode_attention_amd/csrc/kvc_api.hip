@@ -118,18 +118,24 @@ bool plan_decode(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_l
         // streams best: fewer leave CUs idle, a partial second round leaves
         // a tail.  A paged pool holding much less than B * L tokens means
         // ragged lengths, where about four rounds of shorter splits even out
-        // the per-sequence work.  Each split also writes G partial rows
-        // (about G / split_tokens of the bytes it reads): at least 32 * G
-        // tokens per split keeps that near 3 %.
+        // the per-sequence work.  Groups of more than 16 heads (two head
+        // blocks per wave, two waves per SIMD) do several times the work per
+        // tile and wait on latency more than on bandwidth: about three
+        // workgroups per slot (ragged 64-sequence MQA: 27 us at 384-token
+        // splits, 30-31 us at one round of 1088).  Each split also writes G
+        // partial rows, about G / split_tokens of the bytes it reads: at
+        // least 32 * G tokens per split keeps that near 3 %, 12 * G (for
+        // the large groups) near 8 %.
         const long long slots = static_cast<long long>(cu_count()) * decode_mfma_wgs_per_cu(d, G, pool_tokens > 0);
         const long long full = units * L;
+        const bool large_group = G > 16;
         if (pool_tokens > 0 && pool_tokens * H_kv * 10 < full * 9) {
             ts = (pool_tokens * H_kv + 4 * slots - 1) / (4 * slots);
         } else {
-            const long long S = std::max(1LL, slots / std::max(1LL, units));
+            const long long S = std::max(1LL, (large_group ? 3 : 1) * slots / std::max(1LL, units));
             ts = (L + S - 1) / S;
         }
-        ts = std::max<long long>(ts, 32LL * G);
+        ts = std::max<long long>(ts, (large_group ? 12LL : 32LL) * G);
         // Whole loop steps of the kernel (64 or 128 tokens): splits that
         // start off a step boundary (e.g. balanced 4112 + 4081 for 8193
         // tokens with 128-token steps) streamed 2-13 % slower.

@@ -128,16 +128,17 @@ def test_workspace_sizes(lib):
 
 
 def test_split_choice(lib):
-    """The library's split length: one balanced round of workgroups, a floor of
-    32 * G tokens, shorter splits for ragged paged pools, whole loop steps of
-    the kernel (64 tokens up to d = 128, else 128).  (The device count is 256 compute units when no GPU can be
-    queried, as here.)"""
+    """The library's split length: one balanced round of workgroups (about three
+    per slot for groups of more than 16 heads), a floor of 32 * G tokens (12 * G
+    for those groups), shorter splits for ragged paged pools, whole loop steps
+    of the kernel (64 tokens up to d = 128, else 128).  (The device count is
+    256 compute units when no GPU can be queried, as here.)"""
     st = lib.kvc_decode_split_tokens
     # contiguous d = 128: one workgroup per CU, 256 slots
     # (splits are whole 64-token steps)
     assert st(BF16, 16, 32, 8, 128, 8193, 0, 0) == 4160         # 128 units: 2 splits
     assert st(BF16, 1, 64, 8, 128, 131073, 0, 0) == 4160        # 8 units: 32 splits
-    assert st(BF16, 64, 32, 1, 128, 4097, 0, 0) == 1088         # G = 32: 4 splits, >= 1024 tokens
+    assert st(BF16, 64, 32, 1, 128, 4097, 0, 0) == 384          # G = 32: ~3 per slot, >= 12 * G tokens
     assert st(BF16, 16, 32, 8, 64, 8193, 0, 0) == 2112          # d = 64: two per CU, 512 slots
     assert st(BF16, 16, 32, 8, 128, 8193, 0, 1000) == 1000      # explicit split kept
     # paged pool holding about half of B * max_seq_len tokens: ~4 rounds of
@@ -149,5 +150,6 @@ def test_split_choice(lib):
     for args in [(BF16, 16, 32, 8, 128, 8193), (BF16, 3, 12, 4, 64, 700), (BF16, 2, 24, 1, 256, 500)]:
         t = st(*args, 0, 0)
         step = 64 if args[4] <= 128 else 128
-        assert t > 0 and t % step == 0 and t >= 32 * (args[2] // args[3])
+        G = args[2] // args[3]
+        assert t > 0 and t % step == 0 and t >= (12 if G > 16 else 32) * G
     assert st(BF16, 16, 30, 8, 128, 8193, 0, 0) == -1
