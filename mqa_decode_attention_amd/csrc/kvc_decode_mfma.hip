@@ -131,8 +131,10 @@ __device__ __forceinline__ float sum_same_head(float x) {
 // block_size % 16 == 0, splits starting on 16-token boundaries and spanning at
 // most kTblMax blocks: the split's slice of the block table is staged in LDS
 // once, and K and V tiles are staged like those of a contiguous cache.
+// (The paged kernel with staged tiles and one head block is planned at three
+// workgroups per CU: its registers are held to three waves per SIMD.)
 template <int D, int HB, int NW, int MODE, bool FUSED>
-__global__ void __launch_bounds__(NW * 64)
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((MODE == 3 && HB == 1) ? 3 : 1, 8)))
 decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table) {
     // (the block table as its own restrict argument: nothing this kernel stores
     // can alias it, so its wave-uniform reads may use scalar loads)
@@ -772,29 +774,41 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
                         make_float4(o[hb][nb][0], o[hb][nb][1], o[hb][nb][2], o[hb][nb][3]);
             }
             __syncthreads();
+            // one 16-byte column chunk of one head row per thread
             const int rows = min(RB, heads - r0);
-            for (int idx = tid; idx < rows * D; idx += NT) {
-                const int gr = idx / D;
-                const int c = idx % D;
+            for (int idx = tid; idx < rows * NCH; idx += NT) {
+                const int gr = idx / NCH;
+                const int ch = idx % NCH;
                 const int gh = r0 + gr;
-                const int at = 4 * chunk_at(gr, c / 4) + (c & 3);
+                const int at = 4 * chunk_at(gr, ch);
                 float M = -INFINITY;
 #pragma unroll
                 for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w * 16 + gh]);
-                float A = 0.0f, Ls = 0.0f;
+                float4 A = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                float Ls = 0.0f;
 #pragma unroll
                 for (int w = 0; w < NW; ++w) {
                     const float mw = sm_m[w * 16 + gh];
                     const float f = (mw == -kNoMax) ? 0.0f : fast_exp2(mw - M);
-                    A = fmaf(sm_o[(w * RB + gr) * D + at], f, A);
+                    const float4 ow = *reinterpret_cast<const float4*>(sm_o + (w * RB + gr) * D + at);
+                    A.x = fmaf(ow.x, f, A.x);
+                    A.y = fmaf(ow.y, f, A.y);
+                    A.z = fmaf(ow.z, f, A.z);
+                    A.w = fmaf(ow.w, f, A.w);
                     Ls = fmaf(sm_l[w * 16 + gh], f, Ls);
                 }
                 const size_t bh = static_cast<size_t>(b) * p.H_q + j * G + 16 * hb + gh;
+                const int c = 4 * ch;
                 if (nsp == 1) {
-                    static_cast<uint16_t*>(p.out)[bh * D + c] = f32_to_bf16_rne(Ls > 0.0f ? A / Ls : 0.0f);
+                    uint2 packed;
+                    packed.x = static_cast<uint32_t>(f32_to_bf16_rne(Ls > 0.0f ? A.x / Ls : 0.0f)) |
+                               (static_cast<uint32_t>(f32_to_bf16_rne(Ls > 0.0f ? A.y / Ls : 0.0f)) << 16);
+                    packed.y = static_cast<uint32_t>(f32_to_bf16_rne(Ls > 0.0f ? A.z / Ls : 0.0f)) |
+                               (static_cast<uint32_t>(f32_to_bf16_rne(Ls > 0.0f ? A.w / Ls : 0.0f)) << 16);
+                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + bh * D + c) = packed;
                 } else {
-                    p.ws_part[(bh * p.n_splits + split) * D + c] = A;
-                    if (c == 0) p.ws_ml[bh * p.n_splits + split] = make_float2(M, Ls);
+                    *reinterpret_cast<float4*>(p.ws_part + (bh * p.n_splits + split) * D + c) = A;
+                    if (ch == 0) p.ws_ml[bh * p.n_splits + split] = make_float2(M, Ls);
                 }
             }
             __syncthreads();
