@@ -61,7 +61,7 @@ import numpy as np
 
 __all__ = [
     "DTYPES", "bf16_round_bits", "bf16_to_f32", "to_f32", "to_f64", "round_store",
-    "rope_table", "rope_rotate", "append_contiguous", "append_paged",
+    "rope_table", "rope_rotate", "rope_rotate_f32", "append_contiguous", "append_paged",
     "decode_attention", "decode_attention_paged", "decode_attention_weights",
     "gather_paged", "causal_attention_full", "kv_elements_per_layer",
     "kv_bytes_per_token", "kv_cache_bytes", "paged_location", "paged_blocks",
@@ -179,7 +179,14 @@ def _fl(x64: np.ndarray) -> np.ndarray:
 
 def rope_rotate(x: np.ndarray, dtype: str, cos_row: np.ndarray, sin_row: np.ndarray,
                 style: str = "interleaved") -> np.ndarray:
-    """Rotate the last axis (head_dim) of stored vectors x by one table row.
+    """Rotate the last axis (head_dim) of stored vectors x by one table row, then
+    round once into the storage dtype."""
+    return round_store(rope_rotate_f32(x, dtype, cos_row, sin_row, style), dtype)
+
+
+def rope_rotate_f32(x: np.ndarray, dtype: str, cos_row: np.ndarray, sin_row: np.ndarray,
+                    style: str = "interleaved") -> np.ndarray:
+    """The rotation before its final rounding: float32 values (held as float64).
 
     Each op is evaluated in float64 on float32 operands and rounded to float32;
     with 53 >= 2*24 + 2 mantissa bits this is exactly IEEE float32 arithmetic.
@@ -195,7 +202,7 @@ def rope_rotate(x: np.ndarray, dtype: str, cos_row: np.ndarray, sin_row: np.ndar
     r = np.empty_like(xf)
     r[..., i0] = r0
     r[..., i1] = r1
-    return round_store(r, dtype)
+    return r
 
 
 # ---------------------------------------------------------------------------
