@@ -25,7 +25,9 @@
  *    tokens placed anywhere in memory and found through a per-sequence table.
  *  - "KV Cache 최적화 심층 분석: GQA·MLA·MHA 어텐션 메커니즘과 메모리 효율화 전략"
  *    (youngju.dev), PagedKVCache listing: pool [n_blocks, n_heads, block_size,
- *    head_dim], logical block pos / block_size, offset pos % block_size.
+ *    head_dim], logical block pos / block_size, offset pos % block_size; and
+ *    its QuantizedKVCache listing (the *_u8 entry points): uint8 codes with a
+ *    per-vector step and zero point.
  *
  * Conventions for every entry point:
  *  - All tensors are dense, row-major, in DEVICE memory, owned by the caller.
@@ -51,7 +53,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 3
+#define KVC_ABI_VERSION 4
 
 typedef enum kvc_status {
     KVC_OK = 0,
@@ -62,7 +64,10 @@ typedef enum kvc_status {
     KVC_ERR_HIP = 5          /* a HIP runtime call failed                        */
 } kvc_status;
 
-typedef enum kvc_dtype { KVC_F32 = 0, KVC_BF16 = 1 } kvc_dtype;
+/* KVC_U8 names the quantized cache of kvc_append_u8 / kvc_decode_attn*_u8
+ * (uint8 codes, bf16 queries and outputs); only kvc_decode_workspace_bytes and
+ * kvc_decode_split_tokens take it as a dtype. */
+typedef enum kvc_dtype { KVC_F32 = 0, KVC_BF16 = 1, KVC_U8 = 2 } kvc_dtype;
 
 /* How RoPE pairs the head dimension: (2i, 2i+1), or (i, i + d/2). */
 typedef enum kvc_rope_style { KVC_ROPE_INTERLEAVED = 0, KVC_ROPE_HALF = 1 } kvc_rope_style;
@@ -236,6 +241,61 @@ kvc_status kvc_decode_step(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
                            const void* v_new, const float* rope_cos, const float* rope_sin,
                            int rope_rows, int rope_style, int max_seq_len, float scale, void* out,
                            int split_tokens, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Quantized cache (uint8 codes).  Each cached key or value vector (one
+ * sequence, KV head and token) is d uint8 codes c plus a float32 pair
+ * (step, zero point) = sz[.., 0:2], and stands for the values
+ * (c - zero point) * step.  Contiguous: codes [B, H_kv, T_max, d], pairs
+ * [B, H_kv, T_max, 2]; paged: codes [num_blocks, H_kv, block_size, d], pairs
+ * [num_blocks, H_kv, block_size, 2], through the block table as above.  Half
+ * the bytes of a bf16 cache per token plus 16 bytes per token and KV head.
+ */
+
+/*
+ * kvc_append_u8 - kvc_append for a quantized cache.  The key is rotated as in
+ * kvc_append (float32, one rounding per operation) and quantized from that
+ * float32 result, the value from its dtype converted to float32, following
+ * the QuantizedKVCache listing with one pair per vector, in float32 with one
+ * rounding per operation and round-to-nearest-even:
+ *     step = (max - min) / 255   (taken as 1 when it is 0)
+ *     zero point = clamp(round(-min / step), 0, 255)
+ *     code = clamp(round(x / step + zero point), 0, 255)
+ * over the d elements of the vector.  q_inout (if not NULL) is rotated in
+ * place exactly as kvc_append does.  dtype is that of k_new, v_new and q_inout
+ * (KVC_BF16 or KVC_F32); d even and <= 256.  Position and table rules as for
+ * kvc_append.
+ */
+kvc_status kvc_append_u8(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
+                         void* k_codes, float* k_sz, void* v_codes, float* v_sz, int T_max,
+                         const int32_t* block_table, int block_size, int max_blocks_per_seq,
+                         int num_blocks, const int32_t* positions,
+                         const void* k_new, const void* v_new, void* q_inout,
+                         const float* rope_cos, const float* rope_sin, int rope_rows,
+                         int rope_style, void* stream);
+
+/*
+ * kvc_decode_attn_u8 - kvc_decode_attn over a quantized contiguous cache: the
+ * same attention, each cached vector taken as (c - zero point) * step.  q and
+ * out are bf16 [B, H_q, d]; head_dim 64 or 128; H_q / H_kv <= 32.  Workspace
+ * and split rules as for kvc_decode_attn, with kvc_decode_workspace_bytes /
+ * kvc_decode_split_tokens called with dtype KVC_U8.
+ */
+kvc_status kvc_decode_attn_u8(int B, int H_q, int H_kv, int d, const void* q, const void* k_codes,
+                              const float* k_sz, const void* v_codes, const float* v_sz, int T_max,
+                              const int32_t* seq_lens, int max_seq_len, float scale, void* out,
+                              int split_tokens, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kvc_decode_attn_paged_u8 - the same over quantized pools.  Requires
+ * block_size a multiple of 16, split_tokens (when given) a multiple of 16, and
+ * splits spanning at most 1022 blocks (KVC_ERR_UNSUPPORTED otherwise).
+ */
+kvc_status kvc_decode_attn_paged_u8(int B, int H_q, int H_kv, int d, const void* q, const void* k_codes,
+                                    const float* k_sz, const void* v_codes, const float* v_sz, int num_blocks,
+                                    int block_size, const int32_t* block_table, int max_blocks_per_seq,
+                                    const int32_t* seq_lens, int max_seq_len, float scale, void* out,
+                                    int split_tokens, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

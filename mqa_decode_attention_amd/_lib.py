@@ -42,9 +42,23 @@ SIGNATURES = {
                                 c_void_p, c_void_p, c_void_p, c_void_p,
                                 c_int, c_int, c_int, c_float, c_void_p,
                                 c_int, c_void_p, c_size_t, c_void_p]),
+    "kvc_append_u8": (c_int, [c_int, c_int, c_int, c_int, c_int,
+                              c_void_p, c_void_p, c_void_p, c_void_p, c_int,
+                              c_void_p, c_int, c_int, c_int, c_void_p,
+                              c_void_p, c_void_p, c_void_p,
+                              c_void_p, c_void_p, c_int, c_int, c_void_p]),
+    "kvc_decode_attn_u8": (c_int, [c_int, c_int, c_int, c_int, c_void_p,
+                                   c_void_p, c_void_p, c_void_p, c_void_p, c_int,
+                                   c_void_p, c_int, c_float, c_void_p,
+                                   c_int, c_void_p, c_size_t, c_void_p]),
+    "kvc_decode_attn_paged_u8": (c_int, [c_int, c_int, c_int, c_int, c_void_p,
+                                         c_void_p, c_void_p, c_void_p, c_void_p, c_int,
+                                         c_int, c_void_p, c_int,
+                                         c_void_p, c_int, c_float, c_void_p,
+                                         c_int, c_void_p, c_size_t, c_void_p]),
 }
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 _lib = None
 

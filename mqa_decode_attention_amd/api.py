@@ -14,7 +14,7 @@ import torch
 
 from . import _lib
 
-KVC_F32, KVC_BF16 = 0, 1
+KVC_F32, KVC_BF16, KVC_U8 = 0, 1, 2
 ROPE_STYLES = {"interleaved": 0, "half": 1}
 
 
@@ -95,11 +95,19 @@ def append(k_cache: torch.Tensor, v_cache: torch.Tensor, positions: torch.Tensor
         rope_cos.shape[0], ROPE_STYLES[rope_style], _stream(k_new.device, stream)))
 
 
+def _cache_code(dtype) -> int:
+    """dtype of the cache: torch.bfloat16, torch.float32, or torch.uint8 (quantized)."""
+    if dtype == torch.uint8:
+        return KVC_U8
+    return KVC_BF16 if dtype == torch.bfloat16 else KVC_F32
+
+
 def workspace_bytes(dtype: torch.dtype, B: int, H_q: int, H_kv: int, d: int, max_seq_len: int,
                     split_tokens: int = 0, pool_tokens: int = 0) -> int:
-    """kvc_decode_workspace_bytes; pool_tokens = num_blocks * block_size for a paged cache."""
+    """kvc_decode_workspace_bytes; pool_tokens = num_blocks * block_size for a paged
+    cache; dtype torch.uint8 for the quantized cache."""
     lib = _lib.load()
-    code = KVC_BF16 if dtype == torch.bfloat16 else KVC_F32
+    code = _cache_code(dtype)
     n = lib.kvc_decode_workspace_bytes(code, B, H_q, H_kv, d, max_seq_len, pool_tokens, split_tokens)
     if n == (1 << 64) - 1:
         raise KvcError(2, lib.kvc_last_error().decode() or "invalid sizes for the decode workspace")
@@ -110,7 +118,7 @@ def split_tokens(dtype: torch.dtype, B: int, H_q: int, H_kv: int, d: int, max_se
                  split_tokens: int = 0, pool_tokens: int = 0) -> int:
     """kvc_decode_split_tokens: the split length a decode call with these sizes uses."""
     lib = _lib.load()
-    code = KVC_BF16 if dtype == torch.bfloat16 else KVC_F32
+    code = _cache_code(dtype)
     n = lib.kvc_decode_split_tokens(code, B, H_q, H_kv, d, max_seq_len, pool_tokens, split_tokens)
     if n < 0:
         raise KvcError(2, lib.kvc_last_error().decode() or "invalid sizes")
@@ -243,3 +251,98 @@ def decode_step(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         rope_cos.shape[0], ROPE_STYLES[rope_style], int(max_seq_len), float(scale) if scale else 0.0,
         _dev(out, "out", q.dtype, (B, H_q, d)), int(split_tokens), ws, wsn, st))
     return out, q_rot_out
+
+
+# ---------------------------------------------------------------------------
+# quantized cache: uint8 codes [.., d] with a float32 (step, zero point) pair
+# [.., 2] per cached vector
+# ---------------------------------------------------------------------------
+
+
+def append_u8(k_codes: torch.Tensor, k_sz: torch.Tensor, v_codes: torch.Tensor, v_sz: torch.Tensor,
+              positions: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, rope_cos: torch.Tensor,
+              rope_sin: torch.Tensor, q: Optional[torch.Tensor] = None,
+              block_table: Optional[torch.Tensor] = None, rope_style: str = "interleaved",
+              stream=None) -> None:
+    """kvc_append_u8: quantize the rotated new key and the new value into the
+    code / pair arrays; rotate q (bf16 or f32, as k_new) in place if given."""
+    lib = _lib.load()
+    dt = _dtype_code(k_new)
+    B, H_kv, d = k_new.shape
+    H_q = q.shape[1] if q is not None else H_kv
+    if rope_cos.dim() != 2 or rope_cos.shape[1] != d // 2:
+        raise ValueError(f"rope_cos must be [rows, {d // 2}], got {tuple(rope_cos.shape)}")
+    if block_table is not None:
+        num_blocks, _, block_size, _ = k_codes.shape
+        T_max, mb = 0, block_table.shape[1]
+        tbl = _dev(block_table, "block_table", torch.int32, (B, mb))
+        lead = (num_blocks, H_kv, block_size)
+    else:
+        T_max = k_codes.shape[2]
+        tbl, block_size, mb, num_blocks = None, 0, 0, 0
+        lead = (B, H_kv, T_max)
+    _check(lib.kvc_append_u8(
+        dt, B, H_q, H_kv, d,
+        _dev(k_codes, "k_codes", torch.uint8, lead + (d,)), _dev(k_sz, "k_sz", torch.float32, lead + (2,)),
+        _dev(v_codes, "v_codes", torch.uint8, lead + (d,)), _dev(v_sz, "v_sz", torch.float32, lead + (2,)), T_max,
+        tbl, block_size, mb, num_blocks,
+        _dev(positions, "positions", torch.int32, (B,)),
+        _dev(k_new, "k_new", k_new.dtype), _dev(v_new, "v_new", k_new.dtype, (B, H_kv, d)),
+        _dev(q, "q", k_new.dtype, (B, H_q, d)) if q is not None else None,
+        _dev(rope_cos, "rope_cos", torch.float32), _dev(rope_sin, "rope_sin", torch.float32, rope_cos.shape),
+        rope_cos.shape[0], ROPE_STYLES[rope_style], _stream(k_new.device, stream)))
+
+
+def decode_attn_u8(q: torch.Tensor, k_codes: torch.Tensor, k_sz: torch.Tensor, v_codes: torch.Tensor,
+                   v_sz: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                   out: Optional[torch.Tensor] = None, scale: Optional[float] = None, split_tokens: int = 0,
+                   workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """kvc_decode_attn_u8 over a quantized contiguous cache [B, H_kv, T_max, d];
+    q and out bf16 [B, H_q, d]."""
+    lib = _lib.load()
+    B, H_q, d = q.shape
+    out = torch.empty_like(q) if out is None else out
+    _, H_kv, T_max, _ = k_codes.shape
+    st = _stream(q.device, stream)
+    need = workspace_bytes(torch.uint8, B, H_q, H_kv, d, max_seq_len, split_tokens)
+    if workspace is not None:
+        ws, wsn = _dev(workspace, "workspace", torch.uint8), workspace.numel()
+    else:
+        ws, wsn = _workspace(q.device, st, need)
+    lead = (B, H_kv, T_max)
+    _check(lib.kvc_decode_attn_u8(
+        B, H_q, H_kv, d, _dev(q, "q", torch.bfloat16),
+        _dev(k_codes, "k_codes", torch.uint8, lead + (d,)), _dev(k_sz, "k_sz", torch.float32, lead + (2,)),
+        _dev(v_codes, "v_codes", torch.uint8, lead + (d,)), _dev(v_sz, "v_sz", torch.float32, lead + (2,)), T_max,
+        _dev(seq_lens, "seq_lens", torch.int32, (B,)), int(max_seq_len), float(scale) if scale else 0.0,
+        _dev(out, "out", torch.bfloat16, (B, H_q, d)), int(split_tokens), ws, wsn, st))
+    return out
+
+
+def decode_attn_paged_u8(q: torch.Tensor, k_codes: torch.Tensor, k_sz: torch.Tensor, v_codes: torch.Tensor,
+                         v_sz: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                         out: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                         split_tokens: int = 0, workspace: Optional[torch.Tensor] = None,
+                         stream=None) -> torch.Tensor:
+    """kvc_decode_attn_paged_u8 over quantized pools [num_blocks, H_kv, block_size, d]."""
+    lib = _lib.load()
+    B, H_q, d = q.shape
+    out = torch.empty_like(q) if out is None else out
+    num_blocks, H_kv, block_size, _ = k_codes.shape
+    st = _stream(q.device, stream)
+    need = workspace_bytes(torch.uint8, B, H_q, H_kv, d, max_seq_len, split_tokens,
+                           pool_tokens=num_blocks * block_size)
+    if workspace is not None:
+        ws, wsn = _dev(workspace, "workspace", torch.uint8), workspace.numel()
+    else:
+        ws, wsn = _workspace(q.device, st, need)
+    lead = (num_blocks, H_kv, block_size)
+    _check(lib.kvc_decode_attn_paged_u8(
+        B, H_q, H_kv, d, _dev(q, "q", torch.bfloat16),
+        _dev(k_codes, "k_codes", torch.uint8, lead + (d,)), _dev(k_sz, "k_sz", torch.float32, lead + (2,)),
+        _dev(v_codes, "v_codes", torch.uint8, lead + (d,)), _dev(v_sz, "v_sz", torch.float32, lead + (2,)),
+        num_blocks, block_size, _dev(block_table, "block_table", torch.int32, (B, block_table.shape[1])),
+        block_table.shape[1], _dev(seq_lens, "seq_lens", torch.int32, (B,)), int(max_seq_len),
+        float(scale) if scale else 0.0, _dev(out, "out", torch.bfloat16, (B, H_q, d)),
+        int(split_tokens), ws, wsn, st))
+    return out

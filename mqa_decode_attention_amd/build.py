@@ -32,6 +32,7 @@ UNITS = {
     "kvc_append.hip": ["-ffp-contract=off"],
     "kvc_decode.hip": [],
     "kvc_decode_mfma.hip": [],
+    "kvc_decode_u8.hip": [],
     "kvc_probe.hip": [],
 }
 

@@ -96,7 +96,12 @@ bool plan_decode(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_l
                  long long pool_tokens, int split_tokens, DecodePlan* plan, const char** why) {
     DecodePlan pl{};
     const int G = H_q / H_kv;
-    pl.mfma = decode_mfma_supported(dtype, d, G);
+    const bool u8 = dtype == KVC_U8;      // quantized cache: its own matrix-core kernel
+    if (u8 && !decode_u8_supported(d, G)) {
+        *why = "the quantized-cache kernel needs head_dim 64 or 128 and H_q / H_kv <= 32";
+        return false;
+    }
+    pl.mfma = u8 || decode_mfma_supported(dtype, d, G);
     pl.heads_per_wg = pl.mfma ? G : heads_per_wg(G);
     pl.n_chunks = G / pl.heads_per_wg;
     if (!pl.mfma && !decode_supported(dtype, d, pl.heads_per_wg)) {
@@ -104,7 +109,8 @@ bool plan_decode(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_l
         return false;
     }
     const long long units = static_cast<long long>(B) * H_kv * pl.n_chunks;
-    const int tile = pl.mfma ? decode_mfma_step_tokens(d, pool_tokens > 0) : decode_tile_tokens(dtype, d);
+    const int tile = u8 ? decode_u8_step_tokens()
+                        : (pl.mfma ? decode_mfma_step_tokens(d, pool_tokens > 0) : decode_tile_tokens(dtype, d));
     const int L = std::max(max_seq_len, 1);
     long long ts;
     if (split_tokens > 0) {
@@ -126,7 +132,8 @@ bool plan_decode(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_l
         // partial rows, about G / split_tokens of the bytes it reads: at
         // least 32 * G tokens per split keeps that near 3 %, 12 * G (for
         // the large groups) near 8 %.
-        const long long slots = static_cast<long long>(cu_count()) * decode_mfma_wgs_per_cu(d, G, pool_tokens > 0);
+        const long long slots = static_cast<long long>(cu_count()) *
+                                (u8 ? decode_u8_wgs_per_cu(d, G) : decode_mfma_wgs_per_cu(d, G, pool_tokens > 0));
         const long long full = units * L;
         const bool large_group = G > 16;
         if (pool_tokens > 0 && pool_tokens * H_kv * 10 < full * 9) {
@@ -234,9 +241,48 @@ kvc_status kvc_append(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
     return hip_status(kvc::launch_append(p, static_cast<hipStream_t>(stream)), "kvc_append launch");
 }
 
+kvc_status kvc_append_u8(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
+                         void* k_codes, float* k_sz, void* v_codes, float* v_sz, int T_max,
+                         const int32_t* block_table, int block_size, int max_blocks_per_seq,
+                         int num_blocks, const int32_t* positions,
+                         const void* k_new, const void* v_new, void* q_inout,
+                         const float* rope_cos, const float* rope_sin, int rope_rows,
+                         int rope_style, void* stream) {
+    kvc_status st = check_heads(dtype, B, H_q, H_kv, d);
+    if (st != KVC_OK) return st;
+    if (d % 2 != 0 || d > 256) return fail(KVC_ERR_SHAPE, "head_dim %d must be even and at most 256", d);
+    if (rope_style != KVC_ROPE_INTERLEAVED && rope_style != KVC_ROPE_HALF)
+        return fail(KVC_ERR_UNSUPPORTED, "unknown rope_style %d", rope_style);
+    if (rope_rows <= 0) return fail(KVC_ERR_SHAPE, "rope_rows must be positive");
+    if (B == 0) return ok();
+    if (!k_codes || !k_sz || !v_codes || !v_sz || !positions || !k_new || !v_new || !rope_cos || !rope_sin)
+        return fail(KVC_ERR_NULL, "kvc_append_u8: a required pointer is NULL");
+    kvc::AppendParams p{};
+    p.dtype = dtype;
+    p.B = B; p.H_q = H_q; p.H_kv = H_kv; p.d = d;
+    p.k_cache = k_codes; p.v_cache = v_codes; p.k_sz = k_sz; p.v_sz = v_sz; p.T_max = T_max;
+    p.block_table = block_table;
+    p.block_size = block_size; p.max_blocks_per_seq = max_blocks_per_seq; p.num_blocks = num_blocks;
+    if (block_table) {
+        if (block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0)
+            return fail(KVC_ERR_SHAPE, "paged append needs positive block_size, max_blocks_per_seq, num_blocks");
+        const long long cap = static_cast<long long>(block_size) * max_blocks_per_seq;
+        if (cap > 0x7FFFFFFF) return fail(KVC_ERR_SHAPE, "paged capacity exceeds 2^31 tokens");
+        p.capacity = static_cast<int>(cap);
+    } else {
+        if (T_max <= 0) return fail(KVC_ERR_SHAPE, "T_max must be positive");
+        p.capacity = T_max;
+    }
+    p.positions = positions;
+    p.k_new = k_new; p.v_new = v_new; p.q_inout = q_inout;
+    p.rope_cos = rope_cos; p.rope_sin = rope_sin; p.rope_rows = rope_rows;
+    p.rope_style = rope_style;
+    return hip_status(kvc::launch_append_u8(p, static_cast<hipStream_t>(stream)), "kvc_append_u8 launch");
+}
+
 size_t kvc_decode_workspace_bytes(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
                                   int max_seq_len, long long pool_tokens, int split_tokens) {
-    if (check_heads(dtype, B, H_q, H_kv, d) != KVC_OK || max_seq_len < 0 || split_tokens < 0 ||
+    if (check_heads(dtype == KVC_U8 ? KVC_BF16 : dtype, B, H_q, H_kv, d) != KVC_OK || max_seq_len < 0 || split_tokens < 0 ||
         pool_tokens < 0) {
         fail(KVC_ERR_SHAPE, "invalid sizes for the decode workspace");
         return static_cast<size_t>(-1);
@@ -253,7 +299,7 @@ size_t kvc_decode_workspace_bytes(kvc_dtype dtype, int B, int H_q, int H_kv, int
 
 int kvc_decode_split_tokens(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_len,
                             long long pool_tokens, int split_tokens) {
-    if (check_heads(dtype, B, H_q, H_kv, d) != KVC_OK || max_seq_len < 0 || split_tokens < 0 ||
+    if (check_heads(dtype == KVC_U8 ? KVC_BF16 : dtype, B, H_q, H_kv, d) != KVC_OK || max_seq_len < 0 || split_tokens < 0 ||
         pool_tokens < 0)
         return -1;
     kvc::DecodePlan pl;
@@ -281,16 +327,19 @@ struct StepArgs {
     int rope_style;
 };
 
+// dtype KVC_U8: k / v are uint8 codes with pairs k_sz / v_sz (q and out bf16).
 kvc_status decode_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const void* q,
                          const void* k, const void* v, int T_max, int num_blocks, int block_size,
                          const int32_t* block_table, int max_blocks_per_seq,
                          const int32_t* seq_lens, int max_seq_len, float scale, void* out,
                          int split_tokens, void* workspace, size_t workspace_bytes, void* stream,
-                         const StepArgs* step) {
+                         const StepArgs* step, const float* k_sz = nullptr, const float* v_sz = nullptr) {
     const hipEvent_t ev0 = g_prof_start, ev1 = g_prof_stop;   // one-shot, cleared by every call
     g_prof_start = g_prof_stop = nullptr;
-    kvc_status st = check_heads(dtype, B, H_q, H_kv, d);
+    const bool u8 = dtype == KVC_U8;
+    kvc_status st = check_heads(u8 ? KVC_BF16 : dtype, B, H_q, H_kv, d);
     if (st != KVC_OK) return st;
+    if (u8 && B > 0 && (!k_sz || !v_sz)) return fail(KVC_ERR_NULL, "quantized decode: k_sz or v_sz is NULL");
     const bool paged = block_table != nullptr;
     if (max_seq_len < 0) return fail(KVC_ERR_SHAPE, "max_seq_len must be >= 0");
     if (split_tokens < 0) return fail(KVC_ERR_SHAPE, "split_tokens must be >= 0");
@@ -320,6 +369,15 @@ kvc_status decode_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const
     const long long pool_tokens = paged ? static_cast<long long>(num_blocks) * block_size : 0;
     if (!kvc::plan_decode(dtype, B, H_q, H_kv, d, max_seq_len, pool_tokens, split_tokens, &pl, &why))
         return fail(KVC_ERR_UNSUPPORTED, "%s", why);
+    if (u8 && paged) {
+        // 32-token tiles of 16-row groups, each inside one block, found in a
+        // staged slice of at most kTblMax table entries
+        if (pl.split_tokens % 16 != 0)
+            return fail(KVC_ERR_UNSUPPORTED, "the quantized paged kernel needs split_tokens a multiple of 16");
+        if (std::min(pl.split_tokens, std::max(max_seq_len, 1)) / block_size + 2 > kvc::kTblMax)
+            return fail(KVC_ERR_UNSUPPORTED, "a split of the quantized paged kernel spans more than %d blocks",
+                        kvc::kTblMax - 2);
+    }
     if (pl.ws_bytes > 0) {
         if (!workspace) return fail(KVC_ERR_WORKSPACE, "decode needs %zu bytes of workspace, got NULL", pl.ws_bytes);
         if (workspace_bytes < pl.ws_bytes)
@@ -383,11 +441,12 @@ kvc_status decode_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const
             p.q = step->q_rot_out;
         }
     }
-    e = pl.mfma ? kvc::launch_decode_mfma(d, p.G, paged, step != nullptr, p, hs, tm)
-                : kvc::launch_decode_split(dtype, d, pl.heads_per_wg, paged, p, hs, tm);
+    if (u8) e = kvc::launch_decode_u8(d, p.G, paged, p, k_sz, v_sz, hs, tm);
+    else e = pl.mfma ? kvc::launch_decode_mfma(d, p.G, paged, step != nullptr, p, hs, tm)
+                     : kvc::launch_decode_split(dtype, d, pl.heads_per_wg, paged, p, hs, tm);
     if (e != hipSuccess) return hip_status(e, "decode split launch");
     if (pl.n_splits > 1) {
-        e = kvc::launch_decode_merge(dtype, d, p, hs);
+        e = kvc::launch_decode_merge(u8 ? KVC_BF16 : dtype, d, p, hs);
         if (e != hipSuccess) return hip_status(e, "decode merge launch");
     }
     return ok();
@@ -432,6 +491,28 @@ kvc_status kvc_decode_step(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
                              workspace, workspace_bytes, stream, &st);
     return decode_common(dtype, B, H_q, H_kv, d, q, k_cache, v_cache, T_max, 0, 0, nullptr, 0, nullptr,
                          max_seq_len, scale, out, split_tokens, workspace, workspace_bytes, stream, &st);
+}
+
+kvc_status kvc_decode_attn_u8(int B, int H_q, int H_kv, int d, const void* q, const void* k_codes,
+                              const float* k_sz, const void* v_codes, const float* v_sz, int T_max,
+                              const int32_t* seq_lens, int max_seq_len, float scale, void* out,
+                              int split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+    return decode_common(KVC_U8, B, H_q, H_kv, d, q, k_codes, v_codes, T_max, 0, 0, nullptr, 0, seq_lens,
+                         max_seq_len, scale, out, split_tokens, workspace, workspace_bytes, stream, nullptr,
+                         k_sz, v_sz);
+}
+
+kvc_status kvc_decode_attn_paged_u8(int B, int H_q, int H_kv, int d, const void* q, const void* k_codes,
+                                    const float* k_sz, const void* v_codes, const float* v_sz, int num_blocks,
+                                    int block_size, const int32_t* block_table, int max_blocks_per_seq,
+                                    const int32_t* seq_lens, int max_seq_len, float scale, void* out,
+                                    int split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!block_table) return fail(KVC_ERR_NULL, "kvc_decode_attn_paged_u8: block_table is NULL");
+    if (block_size % 16 != 0)
+        return fail(KVC_ERR_UNSUPPORTED, "the quantized paged kernel needs block_size a multiple of 16");
+    return decode_common(KVC_U8, B, H_q, H_kv, d, q, k_codes, v_codes, 0, num_blocks, block_size, block_table,
+                         max_blocks_per_seq, seq_lens, max_seq_len, scale, out, split_tokens, workspace,
+                         workspace_bytes, stream, nullptr, k_sz, v_sz);
 }
 
 }  // extern "C"

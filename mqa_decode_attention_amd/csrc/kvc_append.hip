@@ -101,7 +101,127 @@ __global__ void __launch_bounds__(256) append_kernel(const AppendParams p) {
     Store<T>::store(dst, e1, r1);
 }
 
+// Quantized cache: the new key (rotated as above, kept in float32) and value
+// of each (sequence, KV head) become uint8 codes with one (step, zero point)
+// pair, following the QuantizedKVCache listing of "KV Cache 최적화 심층 분석:
+// GQA·MLA·MHA 어텐션 메커니즘과 메모리 효율화 전략" (youngju.dev) with a pair per
+// vector: over the vector, step = (max - min) / 255 (taken as 1 when it is 0),
+// zero point = -min / step rounded to nearest-even and clamped to [0, 255],
+// code = x / step + zero point rounded and clamped to [0, 255]; float32, one
+// rounding per operation.  One wave per vector: the H_kv keys, the H_kv
+// values, then (q_inout given) the H_q queries, rotated in place as above.
+template <typename T>
+__global__ void __launch_bounds__(256) append_u8_kernel(const AppendParams p) {
+    const int lane = threadIdx.x & 63;
+    const int nvec = 2 * p.H_kv + (p.q_inout ? p.H_q : 0);
+    const long long gw = static_cast<long long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (gw >= static_cast<long long>(p.B) * nvec) return;
+    const int vec = static_cast<int>(gw % nvec);
+    const int b = static_cast<int>(gw / nvec);
+    const int pos = p.positions[b];
+    if (pos < 0 || pos >= p.capacity || pos >= p.rope_rows) return;
+    const int half = p.d >> 1;
+
+    // row index (in vectors of d elements) of (b, head 0) at slot pos, and the
+    // stride between heads
+    size_t row0, head_rows;
+    if (p.block_table) {
+        const int blk = p.block_table[static_cast<size_t>(b) * p.max_blocks_per_seq + pos / p.block_size];
+        if (blk < 0 || blk >= p.num_blocks) return;
+        row0 = static_cast<size_t>(blk) * p.H_kv * p.block_size + pos % p.block_size;
+        head_rows = p.block_size;
+    } else {
+        row0 = static_cast<size_t>(b) * p.H_kv * p.T_max + pos;
+        head_rows = p.T_max;
+    }
+
+    // lane handles pairs i = lane and lane + 64 (d <= 256)
+    float x[4];
+    int el[4];
+    bool has[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int i = lane + 64 * k;
+        has[k] = i < half;
+        el[2 * k] = p.rope_style == KVC_ROPE_HALF ? i : 2 * i;
+        el[2 * k + 1] = p.rope_style == KVC_ROPE_HALF ? i + half : 2 * i + 1;
+    }
+    const bool is_key = vec < p.H_kv;
+    const bool is_query = vec >= 2 * p.H_kv;
+    const int j = is_key ? vec : vec - p.H_kv;
+    const T* src;
+    if (is_query) src = static_cast<const T*>(p.q_inout) + (static_cast<size_t>(b) * p.H_q + vec - 2 * p.H_kv) * p.d;
+    else src = static_cast<const T*>(is_key ? p.k_new : p.v_new) + (static_cast<size_t>(b) * p.H_kv + j) * p.d;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        x[2 * k] = 0.0f;
+        x[2 * k + 1] = 0.0f;
+        if (!has[k]) continue;
+        const float x0 = Store<T>::load(src, el[2 * k]);
+        const float x1 = Store<T>::load(src, el[2 * k + 1]);
+        if (is_query || is_key) {
+            const int i = lane + 64 * k;
+            const float c = p.rope_cos[static_cast<size_t>(pos) * half + i];
+            const float s = p.rope_sin[static_cast<size_t>(pos) * half + i];
+            rope_pair(x0, x1, c, s, x[2 * k], x[2 * k + 1]);
+        } else {
+            x[2 * k] = x0;
+            x[2 * k + 1] = x1;
+        }
+    }
+    if (is_query) {
+        T* dst = static_cast<T*>(p.q_inout) + (static_cast<size_t>(b) * p.H_q + vec - 2 * p.H_kv) * p.d;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            if (!has[k]) continue;
+            Store<T>::store(dst, el[2 * k], x[2 * k]);
+            Store<T>::store(dst, el[2 * k + 1], x[2 * k + 1]);
+        }
+        return;
+    }
+
+    float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        if (!has[k]) continue;
+        mn = fminf(mn, fminf(x[2 * k], x[2 * k + 1]));
+        mx = fmaxf(mx, fmaxf(x[2 * k], x[2 * k + 1]));
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        mn = fminf(mn, __shfl_xor(mn, off, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+    }
+    float step = (mx - mn) / 255.0f;
+    step = step == 0.0f ? 1.0f : step;
+    const float zp = fminf(fmaxf(rintf(-mn / step), 0.0f), 255.0f);
+
+    const size_t row = row0 + static_cast<size_t>(j) * head_rows;
+    uint8_t* codes = static_cast<uint8_t*>(is_key ? p.k_cache : p.v_cache) + row * p.d;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        if (!has[k >> 1]) continue;
+        codes[el[k]] = static_cast<uint8_t>(fminf(fmaxf(rintf(x[k] / step + zp), 0.0f), 255.0f));
+    }
+    if (lane == 0) {
+        float* sz = (is_key ? p.k_sz : p.v_sz) + row * 2;
+        sz[0] = step;
+        sz[1] = zp;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_append_u8(const AppendParams& p, hipStream_t stream) {
+    const int nvec = 2 * p.H_kv + (p.q_inout ? p.H_q : 0);
+    const long long blocks = (static_cast<long long>(p.B) * nvec + 3) / 4;
+    if (blocks <= 0) return hipSuccess;
+    if (p.dtype == KVC_BF16)
+        hipLaunchKernelGGL(append_u8_kernel<uint16_t>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL(append_u8_kernel<float>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
 
 hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
     const int nvec = 2 * p.H_kv + (p.q_inout ? p.H_q : 0);

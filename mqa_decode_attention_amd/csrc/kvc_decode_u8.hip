@@ -1,0 +1,506 @@
+// kvc_decode_u8.hip - decode attention over a uint8 quantized KV cache on the
+// gfx950 matrix cores.
+//
+// Cache: each cached key or value vector is d uint8 codes c plus one float
+// (step, zero point) pair, and reads back as (c - zp) * step - the
+// QuantizedKVCache listing of "KV Cache 최적화 심층 분석: GQA·MLA·MHA 어텐션
+// 메커니즘과 메모리 효율화 전략" (youngju.dev), with a pair kept per vector.
+// Attention is the unquantized one ("Grouped-query attention: berbagi KV head di
+// antara grup query", nalar.dev, section "Jumlah head menentukan batas grup")
+// over those values.  The affine map stays out of the two products: the codes
+// are exact in bf16, and
+//     q . k_t          = step_t * (q . c_t - zp_t * sum(q))
+//     sum_t p_t v_t[c] = sum_t (p_t * step_t) c_t[c] - sum_t p_t * step_t * zp_t
+// so both MFMA products take the raw codes; each score gets one multiply-add,
+// each weight one multiply, and each head one running correction that is
+// subtracted from O at the end.
+//
+// Structure (as the bf16 kernel's staged-tile path): one workgroup of four
+// waves per (sequence, KV head, split); each wave streams 32-token tiles.  Per
+// tile the K codes, V codes and both pair rows go from HBM to LDS by direct
+// loads (buffer ranges ending at the split, so nothing past it is read); the K
+// operand is read from LDS as 8 codes per lane and converted to bf16; the V
+// tile is converted to a bf16 copy in LDS and read back transposed
+// (ds_read_b64_tr_b16) as the A operand V^T, exactly as for a bf16 cache.
+// Each stage is refilled as soon as the tile is done with it (K after its
+// operand reads, V after its conversion), after every LDS read of it has
+// completed.  MODE 0: contiguous codes [B, H_kv, T_max, d], pairs
+// [B, H_kv, T_max, 2].  MODE 3: pools [N_blk, H_kv, bs, d] / [.., bs, 2] with
+// bs % 16 == 0; the split's slice of the block table is staged in LDS.
+
+#include <type_traits>
+
+#include "kvc_internal.h"
+#include "kvc_device.h"
+#include "kvc_mfma_common.h"
+
+namespace kvc {
+
+namespace {
+
+using namespace mfma;
+
+constexpr int kNWq = 4;      // waves per workgroup
+constexpr int kTTq = 32;     // tokens per wave tile
+
+// Eight uint8 codes -> eight bf16 values (exact: integers below 256 need 8
+// significant bits): convert each byte to float32 (v_cvt_f32_ubyteN), keep
+// the upper halves.
+__device__ __forceinline__ float byte_f32(uint32_t w, int k) { return static_cast<float>((w >> (8 * k)) & 0xFFu); }
+__device__ __forceinline__ uint4 codes8_to_bf16(uint2 c) {
+    uint4 r;
+    const float f0 = byte_f32(c.x, 0), f1 = byte_f32(c.x, 1), f2 = byte_f32(c.x, 2), f3 = byte_f32(c.x, 3);
+    const float f4 = byte_f32(c.y, 0), f5 = byte_f32(c.y, 1), f6 = byte_f32(c.y, 2), f7 = byte_f32(c.y, 3);
+    r.x = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, f1), __builtin_bit_cast(uint32_t, f0), 0x07060302u);
+    r.y = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, f3), __builtin_bit_cast(uint32_t, f2), 0x07060302u);
+    r.z = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, f5), __builtin_bit_cast(uint32_t, f4), 0x07060302u);
+    r.w = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, f7), __builtin_bit_cast(uint32_t, f6), 0x07060302u);
+    return r;
+}
+
+template <int D, int HB, int MODE>
+__global__ void __launch_bounds__(kNWq * 64)
+decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, const float* __restrict__ k_sz,
+                 const float* __restrict__ v_sz) {
+    constexpr bool PAGED = MODE == 3;
+    constexpr int NW = kNWq;
+    constexpr int TT = kTTq;
+    constexpr int KB = TT / 16;           // 16-row blocks per tile
+    constexpr int KK = D / 32;            // 32-wide d slices of the score product
+    constexpr int NB = D / 16;            // 16-column blocks of V
+    constexpr int CROW = D;               // bytes per code row
+    constexpr int CLPR = D / 16;          // 16-byte chunks per code row
+    constexpr int CROWS = 64 / CLPR;      // code rows per wave-wide 16-byte load
+    constexpr int CLOADS = TT / CROWS;    // such loads per tile and tensor
+    constexpr int CSTAGE = TT * CROW;     // LDS bytes of one code tile
+    constexpr int ROWB = 2 * D;           // bytes per row of the bf16 V copy
+    constexpr int STAGE = TT * ROWB;      // LDS bytes of the bf16 V copy
+    constexpr int LPR = D / 8;            // 16-byte chunks per bf16 row
+    // pair rows: 32 tokens x 8 bytes, one load (contiguous) or one per 16-row
+    // block (paged: the halves may lie in different blocks)
+    constexpr int SZLOADS = PAGED ? 2 : 1;
+    constexpr int SZROWS = TT / SZLOADS;  // rows per pair load
+    static_assert(CROWS <= 16 && TT % CROWS == 0, "code rows per load");
+
+    __shared__ __attribute__((aligned(16))) char kc_lds[NW * CSTAGE];
+    __shared__ __attribute__((aligned(16))) char vc_lds[NW * CSTAGE];
+    __shared__ __attribute__((aligned(16))) char vb_lds[NW * STAGE];
+    __shared__ __attribute__((aligned(16))) char ksz_lds[NW * TT * 8];
+    __shared__ __attribute__((aligned(16))) char vsz_lds[NW * TT * 8];
+    __shared__ int tbl_lds[PAGED ? kTblMax : 1];
+    static_assert(NW * STAGE >= 2 * NW * 16 * 4 && NW * CSTAGE >= 2 * NW * 16 * 4, "merge area");
+
+    const int wid = blockIdx.x < static_cast<unsigned>(p.n_wg) ? static_cast<int>(blockIdx.x) : -1;
+    if (wid < 0) return;
+    const int split = wid % p.n_splits;
+    const int unit = wid / p.n_splits;    // b * H_kv + j
+    const int b = unit / p.H_kv;
+    const int j = unit % p.H_kv;
+    const int G = p.G;
+    const int L = attended_len(p, b);
+    int nsp = (L + p.split_tokens - 1) / p.split_tokens;
+    nsp = nsp < 1 ? 1 : nsp;
+    if (split >= nsp) return;
+    const int t_begin = split * p.split_tokens;
+    const int t_end = min(L, t_begin + p.split_tokens);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r16 = lane & 15;
+    const int q4 = lane >> 4;
+
+    float m[HB], l[HB], corr[HB];
+    f32x4_t o[HB][NB];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+        m[hb] = -kNoMax;
+        l[hb] = 0.0f;
+        corr[hb] = 0.0f;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) o[hb][nb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+
+    const uint8_t* kcodes = static_cast<const uint8_t*>(p.k);
+    const uint8_t* vcodes = static_cast<const uint8_t*>(p.v);
+    const size_t seq_rows = PAGED ? 0 : (static_cast<size_t>(b) * p.H_kv + j) * p.T_max;
+    const int32_t* table = PAGED ? block_table + static_cast<size_t>(b) * p.max_blocks_per_seq : nullptr;
+    const int fb = PAGED ? t_begin / p.block_size : 0;
+
+    // buffer resource of rows [row0, row0 + n) of one vector array (codes of
+    // `width` bytes per row, or pairs of 8), its range cut at t_end: rows past
+    // the split read as zeros without a memory access.  Contiguous: rows of
+    // this (sequence, KV head); paged: the 16-row group at row0 (a multiple
+    // of 16) lies in one block, found in the staged table.
+    auto rows_rsrc = [&](const void* base_ptr, int width, int row0_, int n) -> __amdgpu_buffer_rsrc_t {
+        const int row0 = __builtin_amdgcn_readfirstlane(row0_);
+        int nvalid = __builtin_amdgcn_readfirstlane(t_end) - row0;
+        nvalid = nvalid < 0 ? 0 : (nvalid > n ? n : nvalid);
+        size_t first;
+        if constexpr (PAGED) {
+            const int lb = row0 / p.block_size;
+            int ti = lb - fb;
+            ti = ti < 0 ? 0 : (ti >= kTblMax ? kTblMax - 1 : ti);
+            const int blk = __builtin_amdgcn_readfirstlane(nvalid > 0 ? tbl_lds[ti] : 0);
+            first = (static_cast<size_t>(blk) * p.H_kv + j) * p.block_size + (row0 - lb * p.block_size);
+        } else {
+            first = seq_rows + static_cast<size_t>(row0);
+        }
+        return make_uniform_rsrc(static_cast<const char*>(base_ptr) + first * width, nvalid * width);
+    };
+
+    // one tensor's tile at row base: codes (CLOADS loads) then pairs (SZLOADS)
+    // into this wave's LDS slices.  Codes: lane l of load i fills bytes
+    // [16 l, 16 l + 16) of that load's 1 KiB, i.e. row CROWS*i + l / CLPR,
+    // slot l % CLPR; K rows hold chunk (slot ^ (row % CLPR)) there (so the
+    // 16 lanes reading one chunk of 16 rows for the operand spread over the
+    // banks), V rows are stored as they come.
+    auto load_tensor = [&](auto is_k, int base) __attribute__((always_inline)) {
+        constexpr bool ISK = decltype(is_k)::value;
+        const uint8_t* codes = ISK ? kcodes : vcodes;
+        const float* sz = ISK ? k_sz : v_sz;
+        char* cbuf = (ISK ? kc_lds : vc_lds) + wave * CSTAGE;
+        char* sbuf = (ISK ? ksz_lds : vsz_lds) + wave * TT * 8;
+#pragma unroll
+        for (int i = 0; i < CLOADS; ++i) {
+            const int r = CROWS * i + lane / CLPR;
+            const int u = ISK ? ((lane % CLPR) ^ (r % CLPR)) : (lane % CLPR);
+            const int g0 = (CROWS * i / 16) * 16;                 // this load's 16-row group
+            const __amdgpu_buffer_rsrc_t rs = rows_rsrc(codes, CROW, base + (PAGED ? g0 : 0), PAGED ? 16 : TT);
+            const int row_in = PAGED ? r - g0 : r;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(cbuf + 1024 * i), 16,
+                                                     row_in * CROW + 16 * u, 0, 0, kNT);
+        }
+#pragma unroll
+        for (int i = 0; i < SZLOADS; ++i) {
+            // SZROWS rows of 8 bytes are SZROWS / 2 lanes of 16 bytes; the other
+            // lanes stay idle, so the load writes only those bytes of LDS (the
+            // instruction is still issued once per wave: the wait counts hold)
+            const __amdgpu_buffer_rsrc_t rs = rows_rsrc(sz, 8, base + SZROWS * i, SZROWS);
+            if (lane < SZROWS / 2)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(sbuf + 8 * SZROWS * i), 16, 16 * lane, 0,
+                                                         0, kNT);
+        }
+    };
+    constexpr int kTensorLoads = CLOADS + SZLOADS;
+
+    // pair (step, zero point) of tile row r from a staged pair slice
+    auto pair_at = [&](const char* sbuf, int r) __attribute__((always_inline)) {
+        return *reinterpret_cast<const float2*>(sbuf + 8 * r);
+    };
+
+    // Prologue: the table slice (paged), then the query, then the first tile.
+    constexpr int kStep = NW * TT;
+    int base = t_begin + wave * TT;
+    constexpr int kTblPer = kTblMax / (NW * 64);
+    int tv[kTblPer];
+    const int nblk = PAGED ? (t_end - 1) / p.block_size - fb + 1 : 0;
+    if constexpr (PAGED) {
+#pragma unroll
+        for (int k = 0; k < kTblPer; ++k) {
+            const int i = tid + k * NW * 64;
+            tv[k] = table[fb + (i < nblk ? i : 0)];
+        }
+    }
+    const size_t qgrp = (static_cast<size_t>(b) * p.H_q + static_cast<size_t>(j) * G) * D;
+    const __amdgpu_buffer_rsrc_t qrs = make_uniform_rsrc(static_cast<const uint16_t*>(p.q) + qgrp, G * D * 2);
+    uint4 qb[HB][KK];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+            qb[hb][kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                qrs, ((16 * hb + r16) * D + 32 * kk + 8 * q4) * 2, 0, 0));
+    if constexpr (PAGED) {
+#pragma unroll
+        for (int k = 0; k < kTblPer; ++k) {
+            const int i = tid + k * NW * 64;
+            const int blk = tv[k] < 0 ? 0 : (tv[k] >= p.num_blocks ? p.num_blocks - 1 : tv[k]);
+            if (i < nblk) tbl_lds[i] = blk;
+        }
+        __syncthreads();
+    }
+    load_tensor(std::true_type{}, base);
+    load_tensor(std::false_type{}, base);
+
+    // sum over d of each query head (the zero-point term of the scores): this
+    // lane's 8*KK elements, then the four lanes of the head
+    float qsum[HB];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            const uint32_t* w = reinterpret_cast<const uint32_t*>(&qb[hb][kk]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc += bf16_lo(w[i]) + bf16_hi(w[i]);
+        }
+        qsum[hb] = sum_same_head(acc);
+    }
+
+    const int s16 = lane & 15;
+    const int tr_row = 4 * q4 + s16 / 4;
+    auto swz = [](int r) { return (2 * r) & (LPR - 1); };
+
+    auto compute_tile = [&](int base) __attribute__((always_inline)) {
+        const char* kc = kc_lds + wave * CSTAGE;
+        const char* vc = vc_lds + wave * CSTAGE;
+        char* vb = vb_lds + wave * STAGE;
+        const char* ks = ksz_lds + wave * TT * 8;
+        const char* vs = vsz_lds + wave * TT * 8;
+
+        // K codes and pairs were issued before this tile's V loads and nothing
+        // after them: at most kTensorLoads outstanding
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kTensorLoads));
+        uint4 ka[KB][KK];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const int r = 16 * kb + r16;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                const int c8 = 4 * kk + q4;                         // 8-byte piece of the row
+                const char* a = kc + r * CROW + 16 * ((c8 / 2) ^ (r % CLPR)) + 8 * (c8 % 2);
+                ka[kb][kk] = codes8_to_bf16(*reinterpret_cast<const uint2*>(a));
+            }
+        }
+        float2 kp[KB][4];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) kp[kb][e] = pair_at(ks, 16 * kb + 4 * q4 + e);
+        // the K stage is free once those reads are done: the next tile's K
+        __builtin_amdgcn_s_waitcnt(kLgkmZero);
+        load_tensor(std::true_type{}, base + kStep);
+
+        // scores: step * (q . c - zp * sum(q)), in log2 units; past t_end masked
+        constexpr int NS = 4 * KB;
+        float s[HB][NS];
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) acc = mfma16(ka[kb][kk], qb[hb][kk], acc);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = base + 16 * kb + 4 * q4 + e;
+                    const float2 sz = kp[kb][e];
+                    s[hb][4 * kb + e] = t < t_end ? (acc[e] - sz.y * qsum[hb]) * (sz.x * p.scale_log2) : -INFINITY;
+                }
+            }
+
+        // V codes and pairs: issued before the K loads just above
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kTensorLoads));
+        float vstep[NS], vzp[NS];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float2 sz = pair_at(vs, 16 * kb + 4 * q4 + e);
+                vstep[4 * kb + e] = sz.x;
+                vzp[4 * kb + e] = sz.y;
+            }
+
+        // online softmax per head (lazy reference max, as in the bf16 kernel);
+        // the PV weights are p * step_v, entered as bf16 hi + lo, and the
+        // correction sums (hi + lo) * zp_v, rescaled with O and l
+        uint32_t ph[HB][NS / 2], pl[HB][NS / 2];
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
+            float mt = s[hb][0];
+#pragma unroll
+            for (int e = 1; e < NS; ++e) mt = fmaxf(mt, s[hb][e]);
+            mt = max_same_head(mt);
+            const bool move = mt > m[hb] + kLazy;
+            if (__any(move)) {
+                const float m_new = move ? mt : m[hb];
+                const float alpha = fast_exp2(m[hb] - m_new);
+                m[hb] = m_new;
+                l[hb] *= alpha;
+                corr[hb] *= alpha;
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) o[hb][nb] *= alpha;
+            }
+            float pw[NS], ps = 0.0f;
+#pragma unroll
+            for (int e = 0; e < NS; ++e) {
+                const float pr = fast_exp2(s[hb][e] - m[hb]);
+                ps += pr;
+                pw[e] = pr * vstep[e];
+            }
+#pragma unroll
+            for (int i = 0; i < NS / 2; ++i) {
+                ph[hb][i] = pack2_bf16(pw[2 * i], pw[2 * i + 1]);
+                pl[hb][i] = pack2_bf16(pw[2 * i] - bf16_lo(ph[hb][i]), pw[2 * i + 1] - bf16_hi(ph[hb][i]));
+                corr[hb] = fmaf(bf16_lo(ph[hb][i]) + bf16_lo(pl[hb][i]), vzp[2 * i], corr[hb]);
+                corr[hb] = fmaf(bf16_hi(ph[hb][i]) + bf16_hi(pl[hb][i]), vzp[2 * i + 1], corr[hb]);
+            }
+            l[hb] += ps;
+        }
+
+        // the V codes to a bf16 copy laid out as the bf16 kernel stages V rows
+        // (chunk u of row r at slot u ^ swz(r)): each lane converts 16-byte
+        // pieces of the code tile
+#pragma unroll
+        for (int m8 = 0; m8 < CSTAGE / 1024; ++m8) {
+            const int ci = 64 * m8 + lane;
+            const int r = ci / CLPR;
+            const int u = ci % CLPR;
+            const uint4 c = *reinterpret_cast<const uint4*>(vc + 16 * ci);
+            const uint4 lo = codes8_to_bf16(make_uint2(c.x, c.y));
+            const uint4 hi = codes8_to_bf16(make_uint2(c.z, c.w));
+            *reinterpret_cast<uint4*>(vb + r * ROWB + 16 * ((2 * u) ^ swz(r))) = lo;
+            *reinterpret_cast<uint4*>(vb + r * ROWB + 16 * ((2 * u + 1) ^ swz(r))) = hi;
+        }
+        // the V stage is free once its reads are done: the next tile's V
+        __builtin_amdgcn_s_waitcnt(kLgkmZero);
+        load_tensor(std::false_type{}, base + kStep);
+
+        // O^T += V^T P^T, V^T read transposed from the bf16 copy (two 16-row
+        // halves per column block, one 16x16x32 product)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int u = 2 * nb + (s16 % 4) / 2;
+            const int r0 = tr_row, r1 = tr_row + 16;
+            const char* a0 = vb + r0 * ROWB + 16 * (u ^ swz(r0)) + 8 * (s16 & 1);
+            const char* a1 = vb + r1 * ROWB + 16 * (u ^ swz(r1)) + 8 * (s16 & 1);
+            const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)a0);
+            const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)a1);
+            uint4 va;
+            va.x = __builtin_bit_cast(uint2, lo).x;
+            va.y = __builtin_bit_cast(uint2, lo).y;
+            va.z = __builtin_bit_cast(uint2, hi).x;
+            va.w = __builtin_bit_cast(uint2, hi).y;
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb) {
+                o[hb][nb] = mfma16(va, make_uint4(ph[hb][0], ph[hb][1], ph[hb][2], ph[hb][3]), o[hb][nb]);
+                o[hb][nb] = mfma16(va, make_uint4(pl[hb][0], pl[hb][1], pl[hb][2], pl[hb][3]), o[hb][nb]);
+            }
+        }
+    };
+
+    // Tiles past the split are loaded anyway (zero range: no memory access), so
+    // every path has the same loads in flight and the waits stay exact.
+    if (base < t_end) {
+        for (;;) {
+            compute_tile(base);
+            base += kStep;
+            if (base >= t_end) break;
+        }
+    }
+
+    // ---- apply the zero-point correction and merge the waves (LDS reused
+    // once every load of this workgroup has landed)
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+        l[hb] = sum_same_head(l[hb]);
+        const float c = sum_same_head(corr[hb]);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) o[hb][nb] -= c;
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+
+    // O rows of the group's heads through LDS, RB rows per pass (chunks of row
+    // r XOR-swizzled by 4r); one thread per 16-byte column chunk of a row
+    constexpr int RB = (NW * STAGE / (NW * 4 * D)) < 16 ? (NW * STAGE / (NW * 4 * D)) : 16;
+    constexpr int NCH = D / 4;
+    static_assert(RB >= 4, "merge area");
+    auto chunk_at = [](int row, int ch) { return ch ^ ((4 * row) & (NCH - 1)); };
+    float* sm_o = reinterpret_cast<float*>(vb_lds);               // [NW][RB][D]
+    float* sm_m = reinterpret_cast<float*>(kc_lds);               // [NW][16]
+    float* sm_l = sm_m + NW * 16;                                   // [NW][16]
+    const int NT = NW * 64;
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+        if (q4 == 0) {
+            sm_m[wave * 16 + r16] = m[hb];
+            sm_l[wave * 16 + r16] = l[hb];
+        }
+        const int heads = min(16, G - 16 * hb);
+        for (int r0 = 0; r0 < heads; r0 += RB) {
+            const int row = r16 - r0;
+            if (row >= 0 && row < RB && r16 < heads) {
+                float* dst = sm_o + (wave * RB + row) * D;
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    *reinterpret_cast<float4*>(dst + 4 * chunk_at(row, 4 * nb + q4)) =
+                        make_float4(o[hb][nb][0], o[hb][nb][1], o[hb][nb][2], o[hb][nb][3]);
+            }
+            __syncthreads();
+            const int rows = min(RB, heads - r0);
+            for (int idx = tid; idx < rows * NCH; idx += NT) {
+                const int gr = idx / NCH;
+                const int ch = idx % NCH;
+                const int gh = r0 + gr;
+                const int at = 4 * chunk_at(gr, ch);
+                float M = -INFINITY;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w * 16 + gh]);
+                float4 A = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                float Ls = 0.0f;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) {
+                    const float mw = sm_m[w * 16 + gh];
+                    const float f = (mw == -kNoMax) ? 0.0f : fast_exp2(mw - M);
+                    const float4 ow = *reinterpret_cast<const float4*>(sm_o + (w * RB + gr) * D + at);
+                    A.x = fmaf(ow.x, f, A.x);
+                    A.y = fmaf(ow.y, f, A.y);
+                    A.z = fmaf(ow.z, f, A.z);
+                    A.w = fmaf(ow.w, f, A.w);
+                    Ls = fmaf(sm_l[w * 16 + gh], f, Ls);
+                }
+                const size_t bh = static_cast<size_t>(b) * p.H_q + j * G + 16 * hb + gh;
+                const int c = 4 * ch;
+                if (nsp == 1) {
+                    uint2 packed;
+                    packed.x = static_cast<uint32_t>(f32_to_bf16_rne(Ls > 0.0f ? A.x / Ls : 0.0f)) |
+                               (static_cast<uint32_t>(f32_to_bf16_rne(Ls > 0.0f ? A.y / Ls : 0.0f)) << 16);
+                    packed.y = static_cast<uint32_t>(f32_to_bf16_rne(Ls > 0.0f ? A.z / Ls : 0.0f)) |
+                               (static_cast<uint32_t>(f32_to_bf16_rne(Ls > 0.0f ? A.w / Ls : 0.0f)) << 16);
+                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + bh * D + c) = packed;
+                } else {
+                    *reinterpret_cast<float4*>(p.ws_part + (bh * p.n_splits + split) * D + c) = A;
+                    if (ch == 0) p.ws_ml[bh * p.n_splits + split] = make_float2(M, Ls);
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+template <int D, int HB>
+hipError_t launch_dh(bool paged, const DecodeParams& p, const float* k_sz, const float* v_sz, hipStream_t stream,
+                     const KernelTiming& tm) {
+    const dim3 grid(p.n_wg_pad), block(kNWq * 64);
+    if (paged) return launch_timed(decode_u8_kernel<D, HB, 3>, grid, block, stream, tm, p, p.block_table, k_sz, v_sz);
+    return launch_timed(decode_u8_kernel<D, HB, 0>, grid, block, stream, tm, p, p.block_table, k_sz, v_sz);
+}
+
+}  // namespace
+
+bool decode_u8_supported(int d, int G) { return (d == 64 || d == 128) && G >= 1 && G <= 32; }
+
+int decode_u8_step_tokens() { return kNWq * kTTq; }
+
+int decode_u8_wgs_per_cu(int d, int G) {
+    // LDS per workgroup: code tiles 2 * 4 * 32 * d, the bf16 V copy 4 * 32 * 2d,
+    // pair rows 2 KiB (+ 4 KiB of table when paged): 66-70 KiB at d = 128, so
+    // two per CU; registers (about 180 per lane with one 16-head block, 280
+    // with two) allow two waves per SIMD, or one.
+    (void)d;
+    return G > 16 ? 1 : 2;
+}
+
+hipError_t launch_decode_u8(int d, int G, bool paged, const DecodeParams& p, const float* k_sz, const float* v_sz,
+                            hipStream_t stream, const KernelTiming& tm) {
+    const bool two = G > 16;
+    switch (d) {
+        case 64: return two ? launch_dh<64, 2>(paged, p, k_sz, v_sz, stream, tm) : launch_dh<64, 1>(paged, p, k_sz, v_sz, stream, tm);
+        case 128: return two ? launch_dh<128, 2>(paged, p, k_sz, v_sz, stream, tm) : launch_dh<128, 1>(paged, p, k_sz, v_sz, stream, tm);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace kvc

@@ -28,9 +28,14 @@ struct AppendParams {
     const float* rope_sin;
     int rope_rows;
     int rope_style;
+    // uint8 quantized cache (launch_append_u8): k_cache / v_cache hold the
+    // codes [.., d] and these the float (step, zero point) pair of each vector
+    float* k_sz;
+    float* v_sz;
 };
 
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
+hipError_t launch_append_u8(const AppendParams& p, hipStream_t stream);
 
 // Split-decode launch plan, a pure function of the sizes (no device query), so
 // that kvc_decode_workspace_bytes and the decode call always agree.
@@ -47,6 +52,11 @@ struct DecodePlan {
 
 // Largest split count the merge step supports (partials live in LDS).
 constexpr int kMaxSplits = 256;
+
+// Block-table entries of one split that the paged kernels with staged tiles
+// keep in LDS (4 KiB).  The bf16 kernel falls back to per-group table reads
+// for splits spanning more blocks; the quantized one needs splits within it.
+constexpr int kTblMax = 1024;
 
 
 struct DecodeParams {
@@ -135,6 +145,15 @@ int decode_mfma_step_tokens(int d, bool paged);
 int decode_mfma_wgs_per_cu(int d, int G, bool paged);
 hipError_t launch_decode_mfma(int d, int G, bool paged, bool fused, const DecodeParams& p,
                               hipStream_t stream, const KernelTiming& tm);
+
+// The matrix-core streaming kernel over a uint8 quantized cache (bf16 q and
+// out; head_dim 64/128; G <= 32); k_sz / v_sz hold the (step, zero point)
+// pair of each cached vector.
+bool decode_u8_supported(int d, int G);
+int decode_u8_step_tokens();
+int decode_u8_wgs_per_cu(int d, int G);
+hipError_t launch_decode_u8(int d, int G, bool paged, const DecodeParams& p, const float* k_sz,
+                            const float* v_sz, hipStream_t stream, const KernelTiming& tm);
 
 // The log-sum-exp merge of the splits (only when n_splits > 1).
 hipError_t launch_decode_merge(kvc_dtype dtype, int d, const DecodeParams& p, hipStream_t stream);

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kvc.h")
 
 KVC_OK, KVC_ERR_NULL, KVC_ERR_SHAPE, KVC_ERR_UNSUPPORTED, KVC_ERR_WORKSPACE, KVC_ERR_HIP = range(6)
-F32, BF16 = 0, 1
+F32, BF16, U8 = 0, 1, 2
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails its host checks
 
 
@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kvc_abi_version() == _lib.ABI_VERSION == 3
+    assert lib.kvc_abi_version() == _lib.ABI_VERSION == 4
     for s in range(6):
         assert lib.kvc_status_string(s)
     assert lib.kvc_status_string(99) == b"unknown status"
@@ -153,3 +153,67 @@ def test_split_choice(lib):
         G = args[2] // args[3]
         assert t > 0 and t % step == 0 and t >= (12 if G > 16 else 32) * G
     assert st(BF16, 16, 30, 8, 128, 8193, 0, 0) == -1
+
+def test_quantized_cache_host_checks(lib):
+    """The uint8-cache entry points check on the host: missing pair arrays, head
+    dims without a kernel, paged block sizes that are not a multiple of 16,
+    splits spanning more blocks than the staged table slice, sizes."""
+    dec = lib.kvc_decode_attn_u8
+    #       B  H_q H_kv d    q     kc    ks    vc    vs    T   lens  L   scale out  split ws wsn stream
+    args = [2, 8, 2, 128, FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, 64, 0.0, FAKE, 0, None, 0, None]
+    bad = list(args)
+    bad[6] = None
+    assert dec(*bad) == KVC_ERR_NULL                                  # no K pairs
+    bad = list(args)
+    bad[8] = None
+    assert dec(*bad) == KVC_ERR_NULL                                  # no V pairs
+    bad = list(args)
+    bad[3] = 256
+    assert dec(*bad) == KVC_ERR_UNSUPPORTED                           # head_dim 256: no quantized kernel
+    bad = list(args)
+    bad[1] = 7
+    assert dec(*bad) == KVC_ERR_SHAPE
+    bad = list(args)
+    bad[11] = 65
+    assert dec(*bad) == KVC_ERR_SHAPE                                 # beyond T_max
+    bad = list(args)
+    bad[0] = 0
+    assert dec(*bad) == KVC_OK
+    pg = lib.kvc_decode_attn_paged_u8
+    #        B  H_q H_kv d    q     kc    ks    vc    vs    nblk bs  tbl  mb lens  L   scale out  split ws  wsn stream
+    pargs = [2, 8, 2, 128, FAKE, FAKE, FAKE, FAKE, FAKE, 100, 16, FAKE, 4, FAKE, 64, 0.0, FAKE, 0, None, 0, None]
+    bad = list(pargs)
+    bad[10] = 8
+    assert pg(*bad) == KVC_ERR_UNSUPPORTED                            # block size 8
+    bad = list(pargs)
+    bad[11] = None
+    assert pg(*bad) == KVC_ERR_NULL
+    bad = list(pargs)
+    bad[17] = 40
+    assert pg(*bad) == KVC_ERR_UNSUPPORTED                            # split of 40 tokens
+    big = list(pargs)
+    big[12], big[14], big[17] = 2000, 32000, 1 << 20                 # a split over 2000 blocks
+    assert pg(*big) == KVC_ERR_UNSUPPORTED
+    app = lib.kvc_append_u8
+    #        dt   B  H_q H_kv d    kc    ks    vc    vs    T   tbl  bs mb nblk pos   kn    vn    q     cos   sin   rows style stream
+    aargs = [BF16, 2, 8, 2, 128, FAKE, FAKE, FAKE, FAKE, 64, None, 0, 0, 0, FAKE, FAKE, FAKE, None, FAKE, FAKE, 64, 0, None]
+    bad = list(aargs)
+    bad[6] = None
+    assert app(*bad) == KVC_ERR_NULL
+    bad = list(aargs)
+    bad[4] = 258
+    assert app(*bad) == KVC_ERR_SHAPE                                 # more than 256 elements
+    bad = list(aargs)
+    bad[1] = 0
+    assert app(*bad) == KVC_OK
+
+
+def test_quantized_cache_split_choice(lib):
+    """The quantized kernel's plan: 128-token steps, two workgroups per CU (one
+    for groups of more than 16 heads), the same floors and ragged-pool rule."""
+    st = lib.kvc_decode_split_tokens
+    assert st(U8, 16, 32, 8, 128, 8193, 0, 0) == 2176                # 512 slots over 128 units: 4 splits
+    assert st(U8, 64, 32, 1, 128, 4097, 0, 0) == 384                 # G = 32
+    assert st(U8, 32, 32, 8, 128, 16385, 17408 * 16, 0) == 1152      # ragged pool: ~4 rounds
+    assert st(U8, 16, 32, 8, 256, 8193, 0, 0) == -1                  # no quantized kernel at d = 256
+    assert lib.kvc_decode_workspace_bytes(U8, 16, 32, 8, 128, 8193, 0, 0) > 0

@@ -27,6 +27,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "mqa_decode_attention_amd", "csrc", "kvc_decode_mfma.hip")
+SRC_U8 = os.path.join(ROOT, "mqa_decode_attention_amd", "csrc", "kvc_decode_u8.hip")
 
 
 def _hipcc():
@@ -36,16 +37,35 @@ def _hipcc():
     return None
 
 
-@pytest.fixture(scope="module")
-def asm(tmp_path_factory):
+def _compile(tmp_path_factory, src, name):
     cc = _hipcc()
     if cc is None:
         pytest.skip("hipcc not available")
-    out = tmp_path_factory.mktemp("asm") / "decode_mfma.s"
+    out = tmp_path_factory.mktemp("asm") / name
     subprocess.run([cc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Xclang", "-target-feature",
                     "-Xclang", "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "--cuda-device-only", "-S",
-                    SRC, "-o", str(out)], check=True, stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL)
+                    src, "-o", str(out)], check=True, stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL)
     return out.read_text()
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    return _compile(tmp_path_factory, SRC, "decode_mfma.s")
+
+
+@pytest.fixture(scope="module")
+def asm_u8(tmp_path_factory):
+    return _compile(tmp_path_factory, SRC_U8, "decode_u8.s")
+
+
+def kernels_u8(text):
+    """(mangled name, head_dim, mode, lines) of each quantized-cache decode kernel."""
+    lines = text.split("\n")
+    for i, l in enumerate(lines):
+        m = re.match(r"^(_ZN3kvc\S*decode_u8_kernelILi(\d+)ELi\d+ELi(\d+)E\S*):", l)
+        if m:
+            end = next(k for k in range(i, len(lines)) if lines[k].startswith(".Lfunc_end"))
+            yield m.group(1), int(m.group(2)), int(m.group(3)), [x.split(";")[0].strip() for x in lines[i + 1:end]]
 
 
 def kernels(text):
@@ -188,5 +208,43 @@ def test_no_scratch_at_common_head_dims(asm):
     for m in re.finditer(r"\.amdhsa_kernel (\S+)(.*?)\.end_amdhsa_kernel", asm, re.S):
         name, body = m.group(1), m.group(2)
         if "decode_mfma_kernelILi64E" in name or "decode_mfma_kernelILi128E" in name:
+            scratch = int(re.search(r"\.amdhsa_private_segment_fixed_size\s+(\d+)", body).group(1))
+            assert scratch == 0, f"{name} spills {scratch} bytes per lane"
+
+
+def test_u8_no_refill_while_lds_reads_pending(asm_u8):
+    seen = 0
+    for name, d, mode, body in kernels_u8(asm_u8):
+        seen += 1
+        bad = refills_over_pending_reads(body)
+        assert not bad, f"{name}: direct-to-LDS loads issued while LDS reads may be outstanding: {bad[:2]}"
+    assert seen >= 8
+
+
+def test_u8_staged_reads_wait_for_their_loads(asm_u8):
+    """Reads of staged codes and pairs (64/128-bit LDS reads) come after a wait
+    that leaves at most one tensor's tile loads outstanding (codes d / 32 loads
+    plus 1 or 2 pair loads).  Excluded: the transposed reads, which read the
+    wave's own bf16 copy (written by its LDS stores), and 32-bit reads (table
+    entries and the merge's scalars)."""
+    def staged_read(i):
+        return (i.startswith("ds_read") and "tr_b16" not in i and not re.match(r"ds_read2?(st64)?_b32", i)
+                and not i.startswith("ds_read_u") and not i.startswith("ds_read_i"))
+    seen = 0
+    for name, d, mode, body in kernels_u8(asm_u8):
+        seen += 1
+        limit = d // 32 + (2 if mode == 3 else 1)
+        def clears(i, limit=limit):
+            v = waitcnt_field(i, "vmcnt")
+            return v is not None and v <= limit
+        bad = flagged(body, is_lds_dma, clears, staged_read)
+        assert not bad, f"{name}: staged reads with no wait for their loads: {bad[:2]}"
+    assert seen >= 8
+
+
+def test_u8_no_scratch(asm_u8):
+    for m in re.finditer(r"\.amdhsa_kernel (\S+)(.*?)\.end_amdhsa_kernel", asm_u8, re.S):
+        name, body = m.group(1), m.group(2)
+        if "decode_u8_kernel" in name:
             scratch = int(re.search(r"\.amdhsa_private_segment_fixed_size\s+(\d+)", body).group(1))
             assert scratch == 0, f"{name} spills {scratch} bytes per lane"

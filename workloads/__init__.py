@@ -30,6 +30,18 @@ slot the append will fill) holds NaN, so a read of an unwritten slot shows up.
 The RoPE cos/sin table is an input of the append (the pages do not give the
 rotation frequencies): row p, column i holds cos/sin(p * base^(-2i/d)),
 evaluated in float64 and rounded once to float32.
+
+Quantized cache (``draw_quantized``): the same workload's layout with uint8
+codes in place of the K and V values and a float32 (step, zero point) pair per
+cached vector, drawn directly (this module does no quantizing), with the
+statistics such a cache of N(0, 1) vectors has: steps uniform in
+[0.015, 0.03) (the range (max - min) / 255 takes for vectors of a few hundred
+elements), zero points integers uniform in [100, 155], and codes a normal
+sample around the zero point with spread 1 / step, rounded to an integer and
+kept in [0, 255] - so each vector reads back as roughly N(0, 1) values.  From a
+second generator seeded with seed + 7919, in the order K pairs -> V pairs ->
+K codes -> V codes, so the unquantized draws stay unchanged.  Slots at or past
+a sequence's cached length hold code 0 and NaN pairs.
 """
 from __future__ import annotations
 
@@ -40,7 +52,7 @@ from typing import Optional
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "DecodeInputs", "draw", "rotation_table"]
+__all__ = ["Workload", "WORKLOADS", "DecodeInputs", "QuantCache", "draw", "draw_quantized", "rotation_table"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -205,3 +217,52 @@ def draw(w: Workload) -> DecodeInputs:
     return DecodeInputs(w, cached, k_cache, v_cache, block_table,
                         _storage(q, w.dtype), _storage(k_new, w.dtype),
                         _storage(v_new, w.dtype), cos, sin)
+
+
+@dataclasses.dataclass
+class QuantCache:
+    """A quantized cache of a workload's layout, on the CPU.
+
+    k_codes, v_codes  uint8 [B, H_kv, T_max, d] or [N_blocks, H_kv, block_size, d]
+    k_sz, v_sz        float32 [..., 2]: (step, zero point) of each cached vector
+    """
+    k_codes: torch.Tensor
+    k_sz: torch.Tensor
+    v_codes: torch.Tensor
+    v_sz: torch.Tensor
+
+
+def draw_quantized(x: DecodeInputs) -> QuantCache:
+    """Draw a quantized cache in the layout of x (same lengths and block table)."""
+    w = x.workload
+    g = torch.Generator().manual_seed(w.seed + 7919)
+    shape = tuple(x.k_cache.shape)
+    lead = shape[:-1]
+    pairs = []
+    for _ in range(2):
+        step = 0.015 + 0.015 * torch.rand(lead, generator=g, dtype=torch.float32)
+        zp = torch.randint(100, 156, lead, generator=g, dtype=torch.int64).to(torch.float32)
+        pairs.append(torch.stack([step, zp], dim=-1).contiguous())
+    k_sz, v_sz = pairs
+    codes = []
+    for sz in (k_sz, v_sz):
+        c = torch.randn(shape, generator=g, dtype=torch.float32) / sz[..., :1] + sz[..., 1:]
+        codes.append(torch.round(c).clamp(0, 255).to(torch.uint8).contiguous())
+    k_codes, v_codes = codes
+    nan = float("nan")
+    lens = (x.cached + 1).tolist()
+    for b, c in enumerate(x.cached.tolist()):
+        if w.paged:
+            bs = w.block_size
+            for pos in range(c, -(-lens[b] // bs) * bs):
+                blk = int(x.block_table[b, pos // bs])
+                for t in (k_codes, v_codes):
+                    t[blk, :, pos % bs, :] = 0
+                for t in (k_sz, v_sz):
+                    t[blk, :, pos % bs, :] = nan
+        else:
+            for t in (k_codes, v_codes):
+                t[b, :, c:, :] = 0
+            for t in (k_sz, v_sz):
+                t[b, :, c:, :] = nan
+    return QuantCache(k_codes, k_sz, v_codes, v_sz)
