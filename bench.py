@@ -30,16 +30,27 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
 MALL_DEFEAT_BYTES = 2 << 30
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_gqa_8b_traffic.json")
-# the streaming kernel is built from these sources; counters taken on other
-# versions of them do not describe the current kernel
-KERNEL_SOURCES = [os.path.join(ROOT, "mqa_decode_attention_amd", "csrc", f)
-                  for f in ("kvc_decode_mfma.hip", "kvc_device.h", "kvc_internal.h")]
+# committed rocprofv3 counter runs per (cache kind, workload), and the sources
+# the streaming kernel is built from: counters taken on other versions of them
+# do not describe the current kernel
+_CSRC = os.path.join(ROOT, "mqa_decode_attention_amd", "csrc")
+TRAFFIC = {
+    ("native", "gqa_8b"): ("decode_gqa_8b_traffic.json",
+                           ("kvc_decode_mfma.hip", "kvc_mfma_common.h", "kvc_device.h", "kvc_internal.h")),
+    ("u8", "gqa_8b"): ("decode_u8_gqa_8b_traffic.json",
+                       ("kvc_decode_u8.hip", "kvc_mfma_common.h", "kvc_device.h", "kvc_internal.h")),
+}
 
 
 def kv_read_bytes(seq_lens, H_kv, d, elem_bytes):
     """Bytes of K and V a decode step must read: sum_b L_b * H_kv * d * 2 * e."""
     return int(sum(int(L) for L in seq_lens)) * H_kv * d * 2 * elem_bytes
+
+
+def kv_read_bytes_u8(seq_lens, H_kv, d):
+    """The same for the quantized cache: d codes plus an 8-byte (step, zero
+    point) pair per token, KV head and tensor."""
+    return int(sum(int(L) for L in seq_lens)) * H_kv * (d + 8) * 2
 
 
 def parse():
@@ -49,6 +60,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="gqa_8b")
     ap.add_argument("--split-tokens", type=int, default=0, help="0 = library heuristic")
+    ap.add_argument("--kv-cache", choices=("native", "u8"), default="native",
+                    help="native: the workload's dtype (kvc_decode_step); u8: the quantized cache "
+                         "(kvc_append_u8 + kvc_decode_attn[_paged]_u8 on codes drawn by workloads.draw_quantized)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seqs", type=int, default=0,
                     help="sequences the CPU oracle is timed on (0 = all)")
@@ -59,20 +73,24 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        h.update(open(f, "rb").read())
+    for f in sources:
+        h.update(open(os.path.join(_CSRC, f), "rb").read())
     return h.hexdigest()
 
 
-def traffic_for_current_kernel():
+def traffic_for_current_kernel(kind: str, workload: str):
     """HBM bytes per launch of the streaming kernel from the committed rocprofv3
-    counter runs, if they were taken on the current kernel sources; else None."""
+    counter runs of this workload, if they were taken on the current kernel
+    sources; else None."""
+    if (kind, workload) not in TRAFFIC:
+        return None
+    name, sources = TRAFFIC[(kind, workload)]
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(os.path.join(ROOT, "profiles", name)) as f:
             t = json.load(f)
-        if t.get("kernel_sources_sha256") == kernel_source_hash():
+        if t.get("kernel_sources_sha256") == kernel_source_hash(sources):
             return t.get("hbm_bytes_per_launch")
     except (OSError, ValueError):
         pass
@@ -122,6 +140,39 @@ def cpu_baseline(x, n_seqs):
     return {"value": round(nbytes / sec / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{B} of {w.B} sequences of {w.name} (append + attention, float64, numpy, one thread), "
                       f"{sec:.2f} s"}
+
+
+def cpu_baseline_u8(x, qc, n_seqs):
+    """Time the quantized-cache oracle (as it stands, one thread) on the same step."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle.kvc_quant_oracle as QO
+
+    w = x.workload
+    B = w.B if n_seqs <= 0 else min(n_seqs, w.B)
+    dt = w.dtype
+    import torch
+
+    def np_store(t):
+        t = t.contiguous()
+        return t.view(torch.int16).numpy().view(np.uint16) if dt == "bf16" else t.numpy()
+
+    if w.paged:
+        raise NotImplementedError("CPU baseline is timed on contiguous workloads")
+    arrs = [a[:B].numpy() for a in (qc.k_codes, qc.k_sz, qc.v_codes, qc.v_sz)]
+    q, kn, vn = np_store(x.q[:B]), np_store(x.k_new[:B]), np_store(x.v_new[:B])
+    cos, sin = x.rope_cos.numpy(), x.rope_sin.numpy()
+    cached = x.cached.numpy()[:B]
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        kc, ks, vc, vs, q2 = QO.append_contiguous_u8(*arrs, cached, kn, vn, cos, sin, dt, q=q)
+        QO.decode_attention_u8(q2, kc, ks, vc, vs, cached + 1, dt)
+        sec = time.perf_counter() - t0
+    nbytes = kv_read_bytes_u8(cached + 1, w.H_kv, w.d)
+    return {"value": round(nbytes / sec / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{B} of {w.B} sequences of {w.name}, uint8 cache (append + attention, float64, numpy, "
+                      f"one thread), {sec:.2f} s"}
 
 
 def read_probe(gib: int = 4, reps: int = 10) -> dict:
@@ -186,13 +237,23 @@ def main():
     x = W.draw(w)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    u8 = args.kv_cache == "u8"
     e = 2 if w.dtype == "bf16" else 4
-    kv_bytes = kv_read_bytes(x.seq_lens.tolist(), w.H_kv, w.d, e)
-    cache_bytes = x.k_cache.numel() * e * 2
+    if u8:
+        qc = W.draw_quantized(x)
+        kv_bytes = kv_read_bytes_u8(x.seq_lens.tolist(), w.H_kv, w.d)
+        cache_bytes = (qc.k_codes.numel() + qc.k_sz.numel() * 4) * 2
+    else:
+        kv_bytes = kv_read_bytes(x.seq_lens.tolist(), w.H_kv, w.d, e)
+        cache_bytes = x.k_cache.numel() * e * 2
     R = max(1, min(64, -(-MALL_DEFEAT_BYTES // cache_bytes)))
 
-    ks = [x.k_cache.to(dev) for _ in range(R)]
-    vs = [x.v_cache.to(dev) for _ in range(R)]
+    if u8:
+        ks = [(qc.k_codes.to(dev), qc.k_sz.to(dev)) for _ in range(R)]
+        vs = [(qc.v_codes.to(dev), qc.v_sz.to(dev)) for _ in range(R)]
+    else:
+        ks = [x.k_cache.to(dev) for _ in range(R)]
+        vs = [x.v_cache.to(dev) for _ in range(R)]
     q = x.q.to(dev)
     kn, vn = x.k_new.to(dev), x.v_new.to(dev)
     pos, lens = x.cached.to(dev), x.seq_lens.to(dev)
@@ -203,9 +264,21 @@ def main():
     torch.cuda.synchronize()
 
     q_rot = torch.empty_like(q)
+    q_work = q.clone()    # u8 step: the append rotates the query in place (rotation keeps its norm)
 
     def step(i, ev=None):
         r = i % R
+        if u8:
+            (kc, ksz), (vc, vsz) = ks[r], vs[r]
+            kvc.append_u8(kc, ksz, vc, vsz, pos, kn, vn, cos, sin, q=q_work, block_table=tbl)
+            if ev is not None:
+                kvc.profile_next_decode(ev[0], ev[1])
+            if tbl is not None:
+                kvc.decode_attn_paged_u8(q_work, kc, ksz, vc, vsz, tbl, lens, max_len, out=out,
+                                         split_tokens=args.split_tokens)
+            else:
+                kvc.decode_attn_u8(q_work, kc, ksz, vc, vsz, lens, max_len, out=out, split_tokens=args.split_tokens)
+            return
         if ev is not None:   # the library attaches these to its streaming kernel
             kvc.profile_next_decode(ev[0], ev[1])
         kvc.decode_step(q, ks[r], vs[r], pos, kn, vn, cos, sin, max_len, block_table=tbl, q_rot_out=q_rot,
@@ -244,7 +317,8 @@ def main():
 
     achieved = kv_bytes / (dec_avg_ms * 1e-3) / 1e9
     value = kv_bytes / (step_ms * 1e-3) / 1e9
-    traffic = traffic_for_current_kernel()
+    traffic = traffic_for_current_kernel(args.kv_cache, w.name)
+    pool_tokens = x.k_cache.shape[0] * w.block_size if w.paged else 0
 
     res = {
         "metric": "GQA decode-attn KV read GB/s (% of MI355X HBM peak); us per decode step",
@@ -258,12 +332,15 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
-        "data": "synthetic (seeded N(0,1), NaN past each sequence's length)",
-        "config": {"workload": w.name, "batch": w.B, "H_q": w.H_q, "H_kv": w.H_kv, "head_dim": w.d,
-                   "cached_tokens": [w.cached_lo, w.cached_hi], "layout": w.layout,
+        "data": ("synthetic (seeded uint8 codes and per-vector (step, zero point) pairs of N(0,1)-like "
+                 "vectors, NaN pairs past each sequence's length)") if u8 else
+                "synthetic (seeded N(0,1), NaN past each sequence's length)",
+        "config": {"workload": w.name + ("_u8" if u8 else ""), "batch": w.B, "H_q": w.H_q, "H_kv": w.H_kv,
+                   "head_dim": w.d, "cached_tokens": [w.cached_lo, w.cached_hi], "layout": w.layout,
+                   "kv_cache": "uint8 codes + float32 (step, zero point) per vector" if u8 else w.dtype,
                    "kv_bytes_per_step": kv_bytes, "cache_replicas": R,
-                   "split_tokens": kvc.split_tokens(x.q.dtype, w.B, w.H_q, w.H_kv, w.d, max_len, args.split_tokens,
-                                                    pool_tokens=x.k_cache.shape[0] * w.block_size if w.paged else 0),
+                   "split_tokens": kvc.split_tokens(torch.uint8 if u8 else x.q.dtype, w.B, w.H_q, w.H_kv, w.d,
+                                                    max_len, args.split_tokens, pool_tokens=pool_tokens),
                    "split_choice": "explicit" if args.split_tokens else "library"},
         "us_per_step": round(step_ms * 1e3, 2),
         "decode_us": round(dec_avg_ms * 1e3, 2),
@@ -271,7 +348,9 @@ def main():
         "hbm_pct_step": round(100 * value / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "decode_mfma_kernel (streaming pass with the fused append; the split merge is a separate small kernel)",
+                     "kernel": ("decode_u8_kernel (streaming pass over the codes; the append and the split merge "
+                                "are separate small kernels)") if u8 else
+                               "decode_mfma_kernel (streaming pass with the fused append; the split merge is a separate small kernel)",
                      "bytes_per_launch": kv_bytes},
         "wall_s_timed": round(wall, 4),
     }
@@ -283,7 +362,8 @@ def main():
                            "default_policy_gbs": probe["default"]["best_gbs"], "nontemporal_gbs": ceil_nt,
                            "kernel_frac_of_ceiling": round(achieved / ceil_nt, 4)}
     if not args.no_cpu_baseline and not w.paged:
-        res["cpu_baseline"] = cpu_baseline(x, args.cpu_sample_seqs)
+        res["cpu_baseline"] = cpu_baseline_u8(x, qc, args.cpu_sample_seqs) if u8 else \
+            cpu_baseline(x, args.cpu_sample_seqs)
     print(json.dumps(res), flush=True)
 
 
