@@ -27,7 +27,8 @@
  *    (youngju.dev), PagedKVCache listing: pool [n_blocks, n_heads, block_size,
  *    head_dim], logical block pos / block_size, offset pos % block_size; and
  *    its QuantizedKVCache listing (the *_u8 entry points): uint8 codes with a
- *    per-vector step and zero point.
+ *    per-vector step and zero point; its SlidingWindowAttention listing (the
+ *    *_window and *_ring entry points): attention over the last W tokens.
  *
  * Conventions for every entry point:
  *  - All tensors are dense, row-major, in DEVICE memory, owned by the caller.
@@ -53,7 +54,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 4
+#define KVC_ABI_VERSION 5
 
 typedef enum kvc_status {
     KVC_OK = 0,
@@ -241,6 +242,75 @@ kvc_status kvc_decode_step(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
                            const void* v_new, const float* rope_cos, const float* rope_sin,
                            int rope_rows, int rope_style, int max_seq_len, float scale, void* out,
                            int split_tokens, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Sliding window: the new token attends only the last `window` tokens of its
+ * sequence, itself included - the SlidingWindowAttention listing of "KV Cache
+ * 최적화 심층 분석: GQA·MLA·MHA 어텐션 메커니즘과 메모리 효율화 전략"
+ * (youngju.dev), which concatenates the new key and value and cuts the cache
+ * to its last window_size tokens.  That cut cache is held either as
+ *   - a full cache (contiguous, or paged through a block table, laid out as
+ *     for kvc_decode_attn[_paged]): a sequence holding L tokens attends tokens
+ *     [max(0, L - window), L); the older ones stay stored and are never read
+ *     (window 0: no window); or
+ *   - a ring (contiguous only, ring = 1): k/v [B, H_kv, T_max, d], token t in
+ *     slot t % T_max, written by kvc_append_ring; the window is T_max (pass
+ *     window 0 or T_max) and the slots [0, min(L, T_max)) are attended.
+ *     Attention does not depend on the order of the tokens, so this equals
+ *     the window over a full cache.
+ */
+
+/*
+ * kvc_append_ring - kvc_append into a contiguous ring of T_max slots: the new
+ * token of position p = positions[b] goes to slot p % T_max (replacing the
+ * token p - T_max, which has left the window); its key and q_inout (if not
+ * NULL) are rotated at position p itself.  Positions must be in [0,
+ * rope_rows) (others write nothing); they may exceed T_max.
+ */
+kvc_status kvc_append_ring(kvc_dtype dtype, int B, int H_q, int H_kv, int d, void* k_ring, void* v_ring,
+                           int T_max, const int32_t* positions, const void* k_new, const void* v_new,
+                           void* q_inout, const float* rope_cos, const float* rope_sin, int rope_rows,
+                           int rope_style, void* stream);
+
+/*
+ * The token span the splits of a windowed call cover: min(max_seq_len,
+ * T_max) for a ring, min(max_seq_len, window + 15) for a window over a full
+ * cache (the paged kernels start their splits at a multiple of 16 tokens),
+ * max_seq_len without either.  Pass it as max_seq_len to
+ * kvc_decode_workspace_bytes / kvc_decode_split_tokens when sizing the
+ * workspace of kvc_decode_attn_window / kvc_decode_step_window.  -1 for
+ * invalid sizes.
+ */
+int kvc_window_span(int max_seq_len, int window, int ring, int T_max);
+
+/*
+ * kvc_decode_attn_window - kvc_decode_attn (block_table == NULL) or
+ * kvc_decode_attn_paged over the window described above.  Arguments as for
+ * those calls, plus window (>= 0) and ring (0 or 1; contiguous only; then
+ * max_seq_len may exceed T_max).  seq_lens are the sequences' full lengths L
+ * (tokens ever appended, the new one included).
+ */
+kvc_status kvc_decode_attn_window(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const void* q,
+                                  const void* k_cache, const void* v_cache, int T_max, const int32_t* block_table,
+                                  int block_size, int max_blocks_per_seq, int num_blocks, const int32_t* seq_lens,
+                                  int max_seq_len, int window, int ring, float scale, void* out, int split_tokens,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kvc_decode_step_window - kvc_decode_step with a window: the same append
+ * (kvc_append_ring's slot when ring = 1) and the attention of the new token
+ * over its window, with L = positions[b] + 1.  Bit for bit the result of the
+ * append followed by kvc_decode_attn_window.  For bf16 with head_dim
+ * 64/128/256 and G <= 32 over a full cache the append runs inside the
+ * streaming kernel; a ring runs the append kernel first.
+ */
+kvc_status kvc_decode_step_window(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const void* q, void* q_rot_out,
+                                  void* k_cache, void* v_cache, int T_max, const int32_t* block_table,
+                                  int block_size, int max_blocks_per_seq, int num_blocks, const int32_t* positions,
+                                  const void* k_new, const void* v_new, const float* rope_cos,
+                                  const float* rope_sin, int rope_rows, int rope_style, int max_seq_len,
+                                  int window, int ring, float scale, void* out, int split_tokens, void* workspace,
+                                  size_t workspace_bytes, void* stream);
 
 /*
  * Quantized cache (uint8 codes).  Each cached key or value vector (one

@@ -42,6 +42,22 @@ SIGNATURES = {
                                 c_void_p, c_void_p, c_void_p, c_void_p,
                                 c_int, c_int, c_int, c_float, c_void_p,
                                 c_int, c_void_p, c_size_t, c_void_p]),
+    "kvc_append_ring": (c_int, [c_int, c_int, c_int, c_int, c_int,
+                                c_void_p, c_void_p, c_int, c_void_p,
+                                c_void_p, c_void_p, c_void_p,
+                                c_void_p, c_void_p, c_int, c_int, c_void_p]),
+    "kvc_window_span": (c_int, [c_int, c_int, c_int, c_int]),
+    "kvc_decode_attn_window": (c_int, [c_int, c_int, c_int, c_int, c_int,
+                                       c_void_p, c_void_p, c_void_p, c_int,
+                                       c_void_p, c_int, c_int, c_int, c_void_p,
+                                       c_int, c_int, c_int, c_float, c_void_p,
+                                       c_int, c_void_p, c_size_t, c_void_p]),
+    "kvc_decode_step_window": (c_int, [c_int, c_int, c_int, c_int, c_int,
+                                       c_void_p, c_void_p, c_void_p, c_void_p, c_int,
+                                       c_void_p, c_int, c_int, c_int, c_void_p,
+                                       c_void_p, c_void_p, c_void_p, c_void_p,
+                                       c_int, c_int, c_int, c_int, c_int, c_float, c_void_p,
+                                       c_int, c_void_p, c_size_t, c_void_p]),
     "kvc_append_u8": (c_int, [c_int, c_int, c_int, c_int, c_int,
                               c_void_p, c_void_p, c_void_p, c_void_p, c_int,
                               c_void_p, c_int, c_int, c_int, c_void_p,
@@ -58,7 +74,7 @@ SIGNATURES = {
                                          c_int, c_void_p, c_size_t, c_void_p]),
 }
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 _lib = None
 

@@ -254,6 +254,113 @@ def decode_step(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
 
 
 # ---------------------------------------------------------------------------
+# sliding window: attend the last `window` tokens (full cache or a ring)
+# ---------------------------------------------------------------------------
+
+
+def window_span(max_seq_len: int, window: int, ring: bool = False, T_max: int = 0) -> int:
+    """kvc_window_span: the max_seq_len that sizes a windowed call's splits and workspace."""
+    n = _lib.load().kvc_window_span(int(max_seq_len), int(window), int(bool(ring)), int(T_max))
+    if n < 0:
+        raise KvcError(2, "invalid window sizes")
+    return n
+
+
+def append_ring(k_ring: torch.Tensor, v_ring: torch.Tensor, positions: torch.Tensor, k_new: torch.Tensor,
+                v_new: torch.Tensor, rope_cos: torch.Tensor, rope_sin: torch.Tensor,
+                q: Optional[torch.Tensor] = None, rope_style: str = "interleaved", stream=None) -> None:
+    """kvc_append_ring: position p goes to slot p % T_max of a ring [B, H_kv, T_max, d]."""
+    lib = _lib.load()
+    dt = _dtype_code(k_new)
+    B, H_kv, d = k_new.shape
+    H_q = q.shape[1] if q is not None else H_kv
+    if rope_cos.dim() != 2 or rope_cos.shape[1] != d // 2:
+        raise ValueError(f"rope_cos must be [rows, {d // 2}], got {tuple(rope_cos.shape)}")
+    T_max = k_ring.shape[2]
+    shape = (B, H_kv, T_max, d)
+    _check(lib.kvc_append_ring(
+        dt, B, H_q, H_kv, d, _dev(k_ring, "k_ring", k_new.dtype, shape), _dev(v_ring, "v_ring", k_new.dtype, shape),
+        T_max, _dev(positions, "positions", torch.int32, (B,)),
+        _dev(k_new, "k_new", k_new.dtype), _dev(v_new, "v_new", k_new.dtype, (B, H_kv, d)),
+        _dev(q, "q", k_new.dtype, (B, H_q, d)) if q is not None else None,
+        _dev(rope_cos, "rope_cos", torch.float32), _dev(rope_sin, "rope_sin", torch.float32, rope_cos.shape),
+        rope_cos.shape[0], ROPE_STYLES[rope_style], _stream(k_new.device, stream)))
+
+
+def _cache_geometry(k_cache, block_table, B, H_kv, d):
+    if block_table is not None:
+        num_blocks, _, block_size, _ = k_cache.shape
+        mb = block_table.shape[1]
+        return (0, _dev(block_table, "block_table", torch.int32, (B, mb)), block_size, mb, num_blocks,
+                (num_blocks, H_kv, block_size, d))
+    T_max = k_cache.shape[2]
+    return T_max, None, 0, 0, 0, (B, H_kv, T_max, d)
+
+
+def decode_attn_window(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_lens: torch.Tensor,
+                       max_seq_len: int, window: int, ring: bool = False,
+                       block_table: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                       scale: Optional[float] = None, split_tokens: int = 0,
+                       workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """kvc_decode_attn_window: attention over the last `window` tokens of a full
+    cache (contiguous, or pools with a block_table), or over a ring (ring=True)."""
+    lib = _lib.load()
+    dt, B, H_q, d, out = _decode_args(q, out)
+    H_kv = k_cache.shape[1]
+    T_max, tbl, block_size, mb, num_blocks, shape = _cache_geometry(k_cache, block_table, B, H_kv, d)
+    st = _stream(q.device, stream)
+    need = workspace_bytes(q.dtype, B, H_q, H_kv, d, window_span(max_seq_len, window, ring, T_max), split_tokens,
+                           pool_tokens=num_blocks * block_size)
+    if workspace is not None:
+        ws, wsn = _dev(workspace, "workspace", torch.uint8), workspace.numel()
+    else:
+        ws, wsn = _workspace(q.device, st, need)
+    _check(lib.kvc_decode_attn_window(
+        dt, B, H_q, H_kv, d, _dev(q, "q", q.dtype),
+        _dev(k_cache, "k_cache", q.dtype, shape), _dev(v_cache, "v_cache", q.dtype, shape), T_max,
+        tbl, block_size, mb, num_blocks, _dev(seq_lens, "seq_lens", torch.int32, (B,)), int(max_seq_len),
+        int(window), int(bool(ring)), float(scale) if scale else 0.0, _dev(out, "out", q.dtype, (B, H_q, d)),
+        int(split_tokens), ws, wsn, st))
+    return out
+
+
+def decode_step_window(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, positions: torch.Tensor,
+                       k_new: torch.Tensor, v_new: torch.Tensor, rope_cos: torch.Tensor, rope_sin: torch.Tensor,
+                       max_seq_len: int, window: int, ring: bool = False,
+                       block_table: Optional[torch.Tensor] = None, rope_style: str = "interleaved",
+                       q_rot_out: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                       scale: Optional[float] = None, split_tokens: int = 0,
+                       workspace: Optional[torch.Tensor] = None, stream=None):
+    """kvc_decode_step_window: append the new token (ring slot when ring=True)
+    and attend over its window, in one call; returns (out, q_rot_out)."""
+    lib = _lib.load()
+    dt, B, H_q, d, out = _decode_args(q, out)
+    H_kv = k_new.shape[1]
+    if q_rot_out is None:
+        q_rot_out = torch.empty_like(q)
+    if rope_cos.dim() != 2 or rope_cos.shape[1] != d // 2:
+        raise ValueError(f"rope_cos must be [rows, {d // 2}], got {tuple(rope_cos.shape)}")
+    T_max, tbl, block_size, mb, num_blocks, shape = _cache_geometry(k_cache, block_table, B, H_kv, d)
+    st = _stream(q.device, stream)
+    need = workspace_bytes(q.dtype, B, H_q, H_kv, d, window_span(max_seq_len, window, ring, T_max), split_tokens,
+                           pool_tokens=num_blocks * block_size)
+    if workspace is not None:
+        ws, wsn = _dev(workspace, "workspace", torch.uint8), workspace.numel()
+    else:
+        ws, wsn = _workspace(q.device, st, need)
+    _check(lib.kvc_decode_step_window(
+        dt, B, H_q, H_kv, d, _dev(q, "q", q.dtype, (B, H_q, d)),
+        _dev(q_rot_out, "q_rot_out", q.dtype, (B, H_q, d)),
+        _dev(k_cache, "k_cache", q.dtype, shape), _dev(v_cache, "v_cache", q.dtype, shape), T_max,
+        tbl, block_size, mb, num_blocks, _dev(positions, "positions", torch.int32, (B,)),
+        _dev(k_new, "k_new", q.dtype, (B, H_kv, d)), _dev(v_new, "v_new", q.dtype, (B, H_kv, d)),
+        _dev(rope_cos, "rope_cos", torch.float32), _dev(rope_sin, "rope_sin", torch.float32, rope_cos.shape),
+        rope_cos.shape[0], ROPE_STYLES[rope_style], int(max_seq_len), int(window), int(bool(ring)),
+        float(scale) if scale else 0.0, _dev(out, "out", q.dtype, (B, H_q, d)), int(split_tokens), ws, wsn, st))
+    return out, q_rot_out
+
+
+# ---------------------------------------------------------------------------
 # quantized cache: uint8 codes [.., d] with a float32 (step, zero point) pair
 # [.., 2] per cached vector
 # ---------------------------------------------------------------------------

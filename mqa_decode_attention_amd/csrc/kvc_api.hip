@@ -202,13 +202,15 @@ void kvc_profile_next_decode(void* start_event, void* stop_event) {
     g_prof_stop = static_cast<hipEvent_t>(stop_event);
 }
 
-kvc_status kvc_append(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
-                      void* k_cache, void* v_cache, int T_max,
-                      const int32_t* block_table, int block_size, int max_blocks_per_seq,
-                      int num_blocks, const int32_t* positions,
-                      const void* k_new, const void* v_new, void* q_inout,
-                      const float* rope_cos, const float* rope_sin, int rope_rows,
-                      int rope_style, void* stream) {
+}  // extern "C"
+
+namespace {
+
+kvc_status append_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, void* k_cache, void* v_cache,
+                         int T_max, const int32_t* block_table, int block_size, int max_blocks_per_seq,
+                         int num_blocks, const int32_t* positions, const void* k_new, const void* v_new,
+                         void* q_inout, const float* rope_cos, const float* rope_sin, int rope_rows,
+                         int rope_style, bool ring, void* stream) {
     kvc_status st = check_heads(dtype, B, H_q, H_kv, d);
     if (st != KVC_OK) return st;
     if (d % 2 != 0) return fail(KVC_ERR_SHAPE, "head_dim %d must be even for the rotation", d);
@@ -232,13 +234,45 @@ kvc_status kvc_append(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
         p.capacity = static_cast<int>(cap);
     } else {
         if (T_max <= 0) return fail(KVC_ERR_SHAPE, "T_max must be positive");
-        p.capacity = T_max;
+        p.capacity = ring ? 0x7FFFFFFF : T_max;    // a ring takes any position
     }
+    p.ring = ring ? 1 : 0;
     p.positions = positions;
     p.k_new = k_new; p.v_new = v_new; p.q_inout = q_inout;
     p.rope_cos = rope_cos; p.rope_sin = rope_sin; p.rope_rows = rope_rows;
     p.rope_style = rope_style;
     return hip_status(kvc::launch_append(p, static_cast<hipStream_t>(stream)), "kvc_append launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+kvc_status kvc_append(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
+                      void* k_cache, void* v_cache, int T_max,
+                      const int32_t* block_table, int block_size, int max_blocks_per_seq,
+                      int num_blocks, const int32_t* positions,
+                      const void* k_new, const void* v_new, void* q_inout,
+                      const float* rope_cos, const float* rope_sin, int rope_rows,
+                      int rope_style, void* stream) {
+    return append_common(dtype, B, H_q, H_kv, d, k_cache, v_cache, T_max, block_table, block_size,
+                         max_blocks_per_seq, num_blocks, positions, k_new, v_new, q_inout, rope_cos, rope_sin,
+                         rope_rows, rope_style, false, stream);
+}
+
+kvc_status kvc_append_ring(kvc_dtype dtype, int B, int H_q, int H_kv, int d, void* k_ring, void* v_ring,
+                           int T_max, const int32_t* positions, const void* k_new, const void* v_new,
+                           void* q_inout, const float* rope_cos, const float* rope_sin, int rope_rows,
+                           int rope_style, void* stream) {
+    return append_common(dtype, B, H_q, H_kv, d, k_ring, v_ring, T_max, nullptr, 0, 0, 0, positions, k_new,
+                         v_new, q_inout, rope_cos, rope_sin, rope_rows, rope_style, true, stream);
+}
+
+int kvc_window_span(int max_seq_len, int window, int ring, int T_max) {
+    if (max_seq_len < 0 || window < 0 || (ring && T_max <= 0)) return -1;
+    if (ring) return std::min(max_seq_len, T_max);
+    if (window > 0) return static_cast<int>(std::min<long long>(max_seq_len, static_cast<long long>(window) + 15));
+    return max_seq_len;
 }
 
 kvc_status kvc_append_u8(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
@@ -333,7 +367,8 @@ kvc_status decode_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const
                          const int32_t* block_table, int max_blocks_per_seq,
                          const int32_t* seq_lens, int max_seq_len, float scale, void* out,
                          int split_tokens, void* workspace, size_t workspace_bytes, void* stream,
-                         const StepArgs* step, const float* k_sz = nullptr, const float* v_sz = nullptr) {
+                         const StepArgs* step, const float* k_sz = nullptr, const float* v_sz = nullptr,
+                         int window = 0, int ring = 0) {
     const hipEvent_t ev0 = g_prof_start, ev1 = g_prof_stop;   // one-shot, cleared by every call
     g_prof_start = g_prof_stop = nullptr;
     const bool u8 = dtype == KVC_U8;
@@ -343,12 +378,20 @@ kvc_status decode_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const
     const bool paged = block_table != nullptr;
     if (max_seq_len < 0) return fail(KVC_ERR_SHAPE, "max_seq_len must be >= 0");
     if (split_tokens < 0) return fail(KVC_ERR_SHAPE, "split_tokens must be >= 0");
+    if (window < 0) return fail(KVC_ERR_SHAPE, "window must be >= 0");
+    if (ring && paged) return fail(KVC_ERR_UNSUPPORTED, "a ring cache is contiguous (no block table)");
+    if (ring && window != 0 && window != T_max)
+        return fail(KVC_ERR_SHAPE, "a ring of T_max = %d slots attends all of them: window must be 0 or %d", T_max,
+                    T_max);
+    if (u8 && (window || ring)) return fail(KVC_ERR_UNSUPPORTED, "no sliding window for the quantized cache");
     if (paged) {
         if (block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0)
             return fail(KVC_ERR_SHAPE, "paged decode needs positive block_size, max_blocks_per_seq, num_blocks");
         if (static_cast<long long>(max_seq_len) > static_cast<long long>(block_size) * max_blocks_per_seq)
             return fail(KVC_ERR_SHAPE, "max_seq_len %d exceeds the block table's %lld tokens", max_seq_len,
                         static_cast<long long>(block_size) * max_blocks_per_seq);
+    } else if (ring) {
+        if (T_max <= 0) return fail(KVC_ERR_SHAPE, "T_max must be positive");
     } else if (max_seq_len > T_max) {
         return fail(KVC_ERR_SHAPE, "max_seq_len %d exceeds the cache capacity T_max %d", max_seq_len, T_max);
     }
@@ -367,7 +410,10 @@ kvc_status decode_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const
     kvc::DecodePlan pl;
     const char* why = nullptr;
     const long long pool_tokens = paged ? static_cast<long long>(num_blocks) * block_size : 0;
-    if (!kvc::plan_decode(dtype, B, H_q, H_kv, d, max_seq_len, pool_tokens, split_tokens, &pl, &why))
+    // splits cover the attended span of a sequence (a window's tokens, or the
+    // ring's slots), which kvc_window_span gives
+    const int span = kvc_window_span(max_seq_len, window, ring, T_max);
+    if (!kvc::plan_decode(dtype, B, H_q, H_kv, d, span, pool_tokens, split_tokens, &pl, &why))
         return fail(KVC_ERR_UNSUPPORTED, "%s", why);
     if (u8 && paged) {
         // 32-token tiles of 16-row groups, each inside one block, found in a
@@ -399,6 +445,9 @@ kvc_status decode_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const
     p.T_max = T_max; p.block_size = block_size; p.max_blocks_per_seq = max_blocks_per_seq;
     p.num_blocks = num_blocks;
     p.max_seq_len = max_seq_len; p.split_tokens = pl.split_tokens; p.n_splits = pl.n_splits;
+    p.window = ring ? 0 : window;
+    p.ring = ring ? 1 : 0;
+    p.align = paged ? 16 : 1;
     p.n_wg = static_cast<int>(n_wg);
     p.n_wg_pad = static_cast<int>((n_wg + 7) / 8 * 8);
     const float sc = scale > 0.0f ? scale : 1.0f / sqrtf(static_cast<float>(d));
@@ -408,6 +457,9 @@ kvc_status decode_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const
     tm.start = ev0;
     tm.stop = ev1;
     hipError_t e = hipSuccess;
+    // the append runs inside the matrix-core kernel, except for a ring (the new
+    // token's slot is not the last attended row there)
+    const bool fused = step != nullptr && pl.mfma && !ring;
     if (step) {
         p.positions = step->positions;
         p.k_new = step->k_new;
@@ -418,10 +470,11 @@ kvc_status decode_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const
         p.rope_sin = step->rope_sin;
         p.rope_rows = step->rope_rows;
         p.rope_style = step->rope_style;
-        p.capacity = paged ? block_size * max_blocks_per_seq : T_max;
+        p.capacity = paged ? block_size * max_blocks_per_seq : (ring ? 0x7FFFFFFF : T_max);
         p.seq_lens = nullptr;
-        if (!pl.mfma) {
-            // no fused kernel for this shape: rotated q into q_rot_out, append, then attend
+        if (!fused) {
+            // no fused kernel for this shape (or a ring cache): rotated q into
+            // q_rot_out, append, then attend
             const size_t qbytes = static_cast<size_t>(B) * H_q * d * elem_bytes(dtype);
             e = hipMemcpyAsync(step->q_rot_out, q, qbytes, hipMemcpyDeviceToDevice, hs);
             if (e != hipSuccess) return hip_status(e, "kvc_decode_step query copy");
@@ -436,13 +489,14 @@ kvc_status decode_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const
             ap.k_new = step->k_new; ap.v_new = step->v_new; ap.q_inout = step->q_rot_out;
             ap.rope_cos = step->rope_cos; ap.rope_sin = step->rope_sin;
             ap.rope_rows = step->rope_rows; ap.rope_style = step->rope_style;
+            ap.ring = p.ring;
             e = kvc::launch_append(ap, hs);
             if (e != hipSuccess) return hip_status(e, "kvc_decode_step append launch");
             p.q = step->q_rot_out;
         }
     }
     if (u8) e = kvc::launch_decode_u8(d, p.G, paged, p, k_sz, v_sz, hs, tm);
-    else e = pl.mfma ? kvc::launch_decode_mfma(d, p.G, paged, step != nullptr, p, hs, tm)
+    else e = pl.mfma ? kvc::launch_decode_mfma(d, p.G, paged, fused, p, hs, tm)
                      : kvc::launch_decode_split(dtype, d, pl.heads_per_wg, paged, p, hs, tm);
     if (e != hipSuccess) return hip_status(e, "decode split launch");
     if (pl.n_splits > 1) {
@@ -491,6 +545,37 @@ kvc_status kvc_decode_step(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
                              workspace, workspace_bytes, stream, &st);
     return decode_common(dtype, B, H_q, H_kv, d, q, k_cache, v_cache, T_max, 0, 0, nullptr, 0, nullptr,
                          max_seq_len, scale, out, split_tokens, workspace, workspace_bytes, stream, &st);
+}
+
+kvc_status kvc_decode_attn_window(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const void* q,
+                                  const void* k_cache, const void* v_cache, int T_max, const int32_t* block_table,
+                                  int block_size, int max_blocks_per_seq, int num_blocks, const int32_t* seq_lens,
+                                  int max_seq_len, int window, int ring, float scale, void* out, int split_tokens,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+    if (block_table)
+        return decode_common(dtype, B, H_q, H_kv, d, q, k_cache, v_cache, 0, num_blocks, block_size, block_table,
+                             max_blocks_per_seq, seq_lens, max_seq_len, scale, out, split_tokens, workspace,
+                             workspace_bytes, stream, nullptr, nullptr, nullptr, window, ring);
+    return decode_common(dtype, B, H_q, H_kv, d, q, k_cache, v_cache, T_max, 0, 0, nullptr, 0, seq_lens,
+                         max_seq_len, scale, out, split_tokens, workspace, workspace_bytes, stream, nullptr, nullptr,
+                         nullptr, window, ring);
+}
+
+kvc_status kvc_decode_step_window(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const void* q, void* q_rot_out,
+                                  void* k_cache, void* v_cache, int T_max, const int32_t* block_table,
+                                  int block_size, int max_blocks_per_seq, int num_blocks, const int32_t* positions,
+                                  const void* k_new, const void* v_new, const float* rope_cos,
+                                  const float* rope_sin, int rope_rows, int rope_style, int max_seq_len,
+                                  int window, int ring, float scale, void* out, int split_tokens, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+    StepArgs st{positions, k_new, v_new, q_rot_out, rope_cos, rope_sin, rope_rows, rope_style};
+    if (block_table)
+        return decode_common(dtype, B, H_q, H_kv, d, q, k_cache, v_cache, 0, num_blocks, block_size,
+                             block_table, max_blocks_per_seq, nullptr, max_seq_len, scale, out, split_tokens,
+                             workspace, workspace_bytes, stream, &st, nullptr, nullptr, window, ring);
+    return decode_common(dtype, B, H_q, H_kv, d, q, k_cache, v_cache, T_max, 0, 0, nullptr, 0, nullptr,
+                         max_seq_len, scale, out, split_tokens, workspace, workspace_bytes, stream, &st, nullptr,
+                         nullptr, window, ring);
 }
 
 kvc_status kvc_decode_attn_u8(int B, int H_q, int H_kv, int d, const void* q, const void* k_codes,

@@ -64,7 +64,8 @@ __global__ void __launch_bounds__(256) append_kernel(const AppendParams p) {
         slot0 = (static_cast<size_t>(blk) * p.H_kv * p.block_size + pos % p.block_size) * p.d;
         head_stride = static_cast<size_t>(p.block_size) * p.d;
     } else {
-        slot0 = (static_cast<size_t>(b) * p.H_kv * p.T_max + pos) * p.d;
+        // (a ring of T_max slots keeps position pos in slot pos % T_max)
+        slot0 = (static_cast<size_t>(b) * p.H_kv * p.T_max + (p.ring ? pos % p.T_max : pos)) * p.d;
         head_stride = static_cast<size_t>(p.T_max) * p.d;
     }
 
@@ -131,7 +132,7 @@ __global__ void __launch_bounds__(256) append_u8_kernel(const AppendParams p) {
         row0 = static_cast<size_t>(blk) * p.H_kv * p.block_size + pos % p.block_size;
         head_rows = p.block_size;
     } else {
-        row0 = static_cast<size_t>(b) * p.H_kv * p.T_max + pos;
+        row0 = static_cast<size_t>(b) * p.H_kv * p.T_max + (p.ring ? pos % p.T_max : pos);
         head_rows = p.T_max;
     }
 

@@ -132,12 +132,12 @@ decode_split_kernel(const DecodeParams p) {
     const int b = bj / p.H_kv;
     const int j = bj % p.H_kv;
 
-    const int L = attended_len(p, b);
-    int nsp = (L + p.split_tokens - 1) / p.split_tokens;
-    nsp = nsp < 1 ? 1 : nsp;
+    const TokenRange tr = token_range(p, attended_len(p, b));
+    const int nsp = split_count(p, tr);
     if (split >= nsp) return;
-    const int t_begin = split * p.split_tokens;
-    const int t_end = min(L, t_begin + p.split_tokens);
+    const int t_begin = tr.org + split * p.split_tokens;
+    const int t_end = min(tr.hi, t_begin + p.split_tokens);
+    const int t_lo = tr.lo;                     // rows before it (window) are masked, never read
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -171,8 +171,8 @@ decode_split_kernel(const DecodeParams p) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int t = base + u * TPW + tg;
-            valid[u] = t < t_end;
-            const int tc = valid[u] ? t : t_end - 1;   // never touch rows >= L
+            valid[u] = t >= t_lo && t < t_end;
+            const int tc = t < t_lo ? t_lo : (t < t_end ? t : t_end - 1);   // only attended rows
             size_t off;
             if constexpr (PAGED) {
                 int blk = table[tc / p.block_size];
@@ -289,8 +289,7 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(const DecodeParams p)
     const long long bh = static_cast<long long>(blockIdx.x) * 4 + wave;
     if (bh >= static_cast<long long>(p.B) * p.H_q) return;
     const int b = static_cast<int>(bh / p.H_q);
-    const int L = attended_len(p, b);
-    const int nsp = (L + p.split_tokens - 1) / p.split_tokens;
+    const int nsp = split_count(p, token_range(p, attended_len(p, b)));
     if (nsp <= 1) return;                        // written directly by the split kernel
     const float2* ml = p.ws_ml + bh * p.n_splits;
     const float4* part = reinterpret_cast<const float4*>(p.ws_part + bh * p.n_splits * D);

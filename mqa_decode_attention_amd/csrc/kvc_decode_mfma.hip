@@ -110,11 +110,15 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     // fused step: slot of the new token (read once; it also gives L)
     const int pos = FUSED ? p.positions[b] : 0;
     const int L = FUSED ? len_from_position(p, pos) : attended_len(p, b);
-    int nsp = (L + p.split_tokens - 1) / p.split_tokens;
-    nsp = nsp < 1 ? 1 : nsp;
+    // attended tokens [t_lo, hi) (a sliding window starts past 0); the paged
+    // modes start their splits at t_lo rounded down to 16 and read the rows
+    // before t_lo as zeros (out-of-range offsets) or as row t_lo, masked
+    const TokenRange tr = token_range(p, L);
+    const int nsp = split_count(p, tr);
     if (split >= nsp) return;
-    const int t_begin = split * p.split_tokens;
-    const int t_end = min(L, t_begin + p.split_tokens);
+    const int t_begin = tr.org + split * p.split_tokens;
+    const int t_end = min(tr.hi, t_begin + p.split_tokens);
+    const int t_lo = tr.lo;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -228,12 +232,12 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
             const int t = tok(base, 16 * kb + r16);
             if constexpr (MODE == 2) {
                 const __amdgpu_buffer_rsrc_t rs = group_rsrc(kbase, base + 16 * kb);
-                const int off = (r16 * D + 8 * q4) * 2;
+                const int off = ((t < t_lo ? 16 : r16) * D + 8 * q4) * 2;   // rows before the window: past the range
 #pragma unroll
                 for (int kk = 0; kk < KK; ++kk)
                     ka[kb][kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 64 * kk, 0, kNT));
             } else if constexpr (PAGED) {
-                const size_t off = row_off(t < t_end ? t : t_end - 1) + 8 * q4;
+                const size_t off = row_off(t < t_lo ? t_lo : (t < t_end ? t : t_end - 1)) + 8 * q4;
 #pragma unroll
                 for (int kk = 0; kk < KK; ++kk)
                     ka[kb][kk] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(
@@ -260,15 +264,19 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
             const int u = (lane % LPR) ^ (ISK ? swzk(r) : swz(r));
             const int t = tok(base, r);
             lds_void_t* dst = (lds_void_t*)(wbuf + 1024 * i);
+            // (rows before the window's first token get an offset past the
+            // 16-row range, so they read as zeros without a memory access)
             if constexpr (MODE == 3) {
                 const __amdgpu_buffer_rsrc_t rs = tile_rsrc(pool, base);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, (r * D + 8 * u) * 2, 0, 0, kNT);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, ((t < t_lo ? 16 : r) * D + 8 * u) * 2, 0, 0,
+                                                         kNT);
             } else if constexpr (MODE == 2) {
                 const int row0 = (VROWS * i / 16) * 16;           // this load's 16-row group
                 const __amdgpu_buffer_rsrc_t rs = group_rsrc(pool, base + row0);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, ((r - row0) * D + 8 * u) * 2, 0, 0, kNT);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, ((t < t_lo ? 16 : r - row0) * D + 8 * u) * 2, 0,
+                                                         0, kNT);
             } else if constexpr (PAGED) {
-                const uint16_t* src = pool + row_off(t < t_end ? t : t_end - 1) + 8 * u;
+                const uint16_t* src = pool + row_off(t < t_lo ? t_lo : (t < t_end ? t : t_end - 1)) + 8 * u;
                 __builtin_amdgcn_global_load_lds(src, dst, 16, 0, kNT);
             } else {
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(ISK ? krs : vrs, dst, 16, (t * D + 8 * u) * 2, 0, 0, kNT);
@@ -516,7 +524,8 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int t = tok(base, 16 * kb + 4 * q4 + e);
-                    s[hb][4 * kb + e] = t < t_end ? acc[e] * p.scale_log2 : -INFINITY;
+                    const bool in = (PAGED ? t >= t_lo : true) && t < t_end;   // contiguous splits start at t_lo
+                    s[hb][4 * kb + e] = in ? acc[e] * p.scale_log2 : -INFINITY;
                 }
             }
 

@@ -97,6 +97,7 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
     const int b = unit / p.H_kv;
     const int j = unit % p.H_kv;
     const int G = p.G;
+    // (the quantized entry points have no window: the range is [0, L))
     const int L = attended_len(p, b);
     int nsp = (L + p.split_tokens - 1) / p.split_tokens;
     nsp = nsp < 1 ? 1 : nsp;

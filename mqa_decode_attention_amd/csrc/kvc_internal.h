@@ -28,6 +28,7 @@ struct AppendParams {
     const float* rope_sin;
     int rope_rows;
     int rope_style;
+    int ring;                    // contiguous ring of T_max slots: position p -> slot p % T_max
     // uint8 quantized cache (launch_append_u8): k_cache / v_cache hold the
     // codes [.., d] and these the float (step, zero point) pair of each vector
     float* k_sz;
@@ -85,6 +86,12 @@ struct DecodeParams {
     const float* rope_sin;
     int rope_rows, rope_style;
     int capacity;                // tokens addressable per sequence
+
+    // Sliding window: a sequence holding L tokens attends [max(0, L - window), L)
+    // (window 0: all of them); ring: the cache is a ring of T_max slots (token t
+    // in slot t % T_max) and the slots [0, min(L, T_max)) are attended.
+    int window, ring;
+    int align;                   // split origins are multiples of this (a power of two)
 };
 
 // Attended length of sequence b: from positions (a decode step, after its
@@ -99,6 +106,32 @@ __device__ __forceinline__ int attended_len(const DecodeParams& p, int b) {
     if (p.positions) return len_from_position(p, p.positions[b]);
     const int L = p.seq_lens[b];
     return L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
+}
+
+// Tokens a decode of a sequence holding L tokens attends, [lo, hi), and the
+// origin org of its splits: split s covers [org + s * split_tokens, ...) up to
+// hi.  org is lo rounded down to p.align (16 for the paged kernels, whose tiles
+// are 16-row groups of one block); those kernels mask the rows in [org, lo)
+// and do not read them.
+struct TokenRange {
+    int lo, hi, org;
+};
+__device__ __forceinline__ TokenRange token_range(const DecodeParams& p, int L) {
+    TokenRange r;
+    if (p.ring) {
+        r.lo = 0;
+        r.hi = L < p.T_max ? L : p.T_max;
+    } else {
+        r.hi = L;
+        r.lo = (p.window > 0 && L > p.window) ? L - p.window : 0;
+    }
+    r.org = r.lo & ~(p.align - 1);
+    return r;
+}
+// Splits of that range (at least 1).
+__device__ __forceinline__ int split_count(const DecodeParams& p, const TokenRange& r) {
+    const int n = (r.hi - r.org + p.split_tokens - 1) / p.split_tokens;
+    return n < 1 ? 1 : n;
 }
 
 // Returns false (and leaves *plan untouched) when the sizes cannot be planned.

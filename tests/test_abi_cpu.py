@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kvc_abi_version() == _lib.ABI_VERSION == 4
+    assert lib.kvc_abi_version() == _lib.ABI_VERSION == 5
     for s in range(6):
         assert lib.kvc_status_string(s)
     assert lib.kvc_status_string(99) == b"unknown status"
@@ -111,6 +111,52 @@ def test_paged_host_checks(lib):
     bad = list(args)
     bad[9] = 0
     assert f(*bad) == KVC_ERR_SHAPE
+
+
+def _window(lib, **kw):
+    a = dict(dt=BF16, B=2, H_q=8, H_kv=2, d=128, q=FAKE, k=FAKE, v=FAKE, T_max=64, tbl=None, bs=0, mb=0, nb=0,
+             lens=FAKE, L=64, window=16, ring=0, scale=0.0, out=FAKE, split=0, ws=None, wsn=0, stream=None)
+    a.update(kw)
+    return lib.kvc_decode_attn_window(a["dt"], a["B"], a["H_q"], a["H_kv"], a["d"], a["q"], a["k"], a["v"],
+                                      a["T_max"], a["tbl"], a["bs"], a["mb"], a["nb"], a["lens"], a["L"],
+                                      a["window"], a["ring"], a["scale"], a["out"], a["split"], a["ws"], a["wsn"],
+                                      a["stream"])
+
+
+def test_window_host_checks(lib):
+    """Sliding-window calls: a negative window, a ring with a block table or a
+    window other than its T_max slots, a full cache shorter than max_seq_len,
+    and the token span that sizes the workspace."""
+    span = lib.kvc_window_span
+    assert span(5000, 4096, 0, 0) == 4096 + 15
+    assert span(100, 4096, 0, 0) == 100
+    assert span(5000, 0, 0, 0) == 5000
+    assert span(5000, 0, 1, 4096) == 4096
+    assert span(100, 4096, 1, 4096) == 100
+    assert span(-1, 16, 0, 0) == -1 and span(10, -1, 0, 0) == -1 and span(10, 0, 1, 0) == -1
+    assert _window(lib, window=-1) == KVC_ERR_SHAPE
+    assert _window(lib, ring=1, tbl=FAKE, bs=16, mb=4, nb=8) == KVC_ERR_UNSUPPORTED
+    assert _window(lib, ring=1, window=16) == KVC_ERR_SHAPE            # a ring of 64 slots
+    assert b"T_max" in lib.kvc_last_error()
+    assert _window(lib, L=65) == KVC_ERR_SHAPE                         # a full cache holds max_seq_len
+    assert _window(lib, q=None) == KVC_ERR_NULL
+    assert _window(lib, ring=1, window=64, L=100000, q=None) == KVC_ERR_NULL   # a ring takes any length
+    # the splits of a window cover its span, not the whole sequence
+    assert _window(lib, T_max=100000, L=100000, window=512, B=0) == KVC_OK
+    wsb = lib.kvc_decode_workspace_bytes
+    assert 0 < wsb(BF16, 2, 8, 2, 128, span(100000, 512, 0, 0), 0, 0) < wsb(BF16, 2, 8, 2, 128, 100000, 0, 0)
+    assert _window(lib, dt=U8) == KVC_ERR_UNSUPPORTED or _window(lib, dt=U8) == KVC_ERR_NULL
+    ar = lib.kvc_append_ring
+    args = [BF16, 2, 8, 2, 128, FAKE, FAKE, 64, FAKE, FAKE, FAKE, None, FAKE, FAKE, 64, 0, None]
+    bad = list(args)
+    bad[7] = 0
+    assert ar(*bad) == KVC_ERR_SHAPE                                   # T_max
+    bad = list(args)
+    bad[5] = None
+    assert ar(*bad) == KVC_ERR_NULL
+    bad = list(args)
+    bad[1] = 0
+    assert ar(*bad) == KVC_OK
 
 
 def test_workspace_sizes(lib):
