@@ -47,6 +47,11 @@ def kv_read_bytes(seq_lens, H_kv, d, elem_bytes):
     return int(sum(int(L) for L in seq_lens)) * H_kv * d * 2 * elem_bytes
 
 
+def attended(seq_lens, window):
+    """Tokens each sequence attends: all of them, or the last `window`."""
+    return [min(int(L), window) if window > 0 else int(L) for L in seq_lens]
+
+
 def kv_read_bytes_u8(seq_lens, H_kv, d):
     """The same for the quantized cache: d codes plus an 8-byte (step, zero
     point) pair per token, KV head and tensor."""
@@ -60,6 +65,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="gqa_8b")
     ap.add_argument("--split-tokens", type=int, default=0, help="0 = library heuristic")
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding window of W tokens (kvc_decode_step_window over the full cache; 0 = none)")
+    ap.add_argument("--ring", action="store_true",
+                    help="with --window: the cache is a ring of W slots holding each sequence's window")
     ap.add_argument("--kv-cache", choices=("native", "u8"), default="native",
                     help="native: the workload's dtype (kvc_decode_step); u8: the quantized cache "
                          "(kvc_append_u8 + kvc_decode_attn[_paged]_u8 on codes drawn by workloads.draw_quantized)")
@@ -109,8 +118,9 @@ def calibrate_copy(nbytes: int) -> None:
     print(json.dumps({"calibration_copy_bytes": nbytes, "copies": 5}))
 
 
-def cpu_baseline(x, n_seqs):
-    """Time the CPU oracle (as it stands, one thread) on the same step's inputs."""
+def cpu_baseline(x, n_seqs, window=0):
+    """Time the CPU oracle (as it stands, one thread) on the same step's inputs
+    (with a window: the sliding-window oracle over the full cache)."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -134,12 +144,16 @@ def cpu_baseline(x, n_seqs):
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         k2, v2, q2 = O.append_contiguous(kc, vc, cached, kn, vn, cos, sin, dt, q=q)
-        O.decode_attention(q2, k2, v2, cached + 1, dt)
+        if window:
+            import oracle.kvc_window_oracle as WO
+            WO.decode_attention_window(q2, k2, v2, cached + 1, window, dt)
+        else:
+            O.decode_attention(q2, k2, v2, cached + 1, dt)
         sec = time.perf_counter() - t0
-    nbytes = kv_read_bytes(cached + 1, w.H_kv, w.d, 2 if dt == "bf16" else 4)
+    nbytes = kv_read_bytes(attended(cached + 1, window), w.H_kv, w.d, 2 if dt == "bf16" else 4)
+    what = f"append + attention over the last {window} tokens" if window else "append + attention"
     return {"value": round(nbytes / sec / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{B} of {w.B} sequences of {w.name} (append + attention, float64, numpy, one thread), "
-                      f"{sec:.2f} s"}
+            "sample": f"{B} of {w.B} sequences of {w.name} ({what}, float64, numpy, one thread), {sec:.2f} s"}
 
 
 def cpu_baseline_u8(x, qc, n_seqs):
@@ -238,19 +252,36 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     u8 = args.kv_cache == "u8"
+    win = args.window
+    if (win or args.ring) and (u8 or w.paged and args.ring or args.ring and win <= 0):
+        print("--window applies to the native cache; --ring needs --window and a contiguous workload",
+              file=sys.stderr)
+        sys.exit(2)
     e = 2 if w.dtype == "bf16" else 4
     if u8:
         qc = W.draw_quantized(x)
         kv_bytes = kv_read_bytes_u8(x.seq_lens.tolist(), w.H_kv, w.d)
         cache_bytes = (qc.k_codes.numel() + qc.k_sz.numel() * 4) * 2
     else:
-        kv_bytes = kv_read_bytes(x.seq_lens.tolist(), w.H_kv, w.d, e)
+        kv_bytes = kv_read_bytes(attended(x.seq_lens.tolist(), win), w.H_kv, w.d, e)
         cache_bytes = x.k_cache.numel() * e * 2
     R = max(1, min(64, -(-MALL_DEFEAT_BYTES // cache_bytes)))
 
     if u8:
         ks = [(qc.k_codes.to(dev), qc.k_sz.to(dev)) for _ in range(R)]
         vs = [(qc.v_codes.to(dev), qc.v_sz.to(dev)) for _ in range(R)]
+    elif args.ring:
+        # a ring of W slots holding the window each sequence has before the
+        # step (token t in slot t % W; slots never written stay NaN)
+        rk = torch.full((w.B, w.H_kv, win, w.d), float("nan"), dtype=x.k_cache.dtype)
+        rv = rk.clone()
+        for b, c in enumerate(x.cached.tolist()):
+            for t in range(max(0, c - win + 1), c):
+                rk[b, :, t % win] = x.k_cache[b, :, t]
+                rv[b, :, t % win] = x.v_cache[b, :, t]
+        R = max(1, min(64, -(-MALL_DEFEAT_BYTES // (rk.numel() * e * 2))))
+        ks = [rk.to(dev) for _ in range(R)]
+        vs = [rv.to(dev) for _ in range(R)]
     else:
         ks = [x.k_cache.to(dev) for _ in range(R)]
         vs = [x.v_cache.to(dev) for _ in range(R)]
@@ -281,6 +312,10 @@ def main():
             return
         if ev is not None:   # the library attaches these to its streaming kernel
             kvc.profile_next_decode(ev[0], ev[1])
+        if win:
+            kvc.decode_step_window(q, ks[r], vs[r], pos, kn, vn, cos, sin, max_len, win, ring=args.ring,
+                                   block_table=tbl, q_rot_out=q_rot, out=out, split_tokens=args.split_tokens)
+            return
         kvc.decode_step(q, ks[r], vs[r], pos, kn, vn, cos, sin, max_len, block_table=tbl, q_rot_out=q_rot,
                         out=out, split_tokens=args.split_tokens)
 
@@ -317,7 +352,7 @@ def main():
 
     achieved = kv_bytes / (dec_avg_ms * 1e-3) / 1e9
     value = kv_bytes / (step_ms * 1e-3) / 1e9
-    traffic = traffic_for_current_kernel(args.kv_cache, w.name)
+    traffic = None if win else traffic_for_current_kernel(args.kv_cache, w.name)
     pool_tokens = x.k_cache.shape[0] * w.block_size if w.paged else 0
 
     res = {
@@ -335,12 +370,15 @@ def main():
         "data": ("synthetic (seeded uint8 codes and per-vector (step, zero point) pairs of N(0,1)-like "
                  "vectors, NaN pairs past each sequence's length)") if u8 else
                 "synthetic (seeded N(0,1), NaN past each sequence's length)",
-        "config": {"workload": w.name + ("_u8" if u8 else ""), "batch": w.B, "H_q": w.H_q, "H_kv": w.H_kv,
+        "config": {"workload": w.name + ("_u8" if u8 else "") + (f"_window{win}" if win else "") +
+                               ("_ring" if args.ring else ""), "batch": w.B, "H_q": w.H_q, "H_kv": w.H_kv,
                    "head_dim": w.d, "cached_tokens": [w.cached_lo, w.cached_hi], "layout": w.layout,
                    "kv_cache": "uint8 codes + float32 (step, zero point) per vector" if u8 else w.dtype,
                    "kv_bytes_per_step": kv_bytes, "cache_replicas": R,
+                   "window": win, "ring": bool(args.ring),
                    "split_tokens": kvc.split_tokens(torch.uint8 if u8 else x.q.dtype, w.B, w.H_q, w.H_kv, w.d,
-                                                    max_len, args.split_tokens, pool_tokens=pool_tokens),
+                                                    kvc.window_span(max_len, win, args.ring, win if args.ring else 0),
+                                                    args.split_tokens, pool_tokens=pool_tokens),
                    "split_choice": "explicit" if args.split_tokens else "library"},
         "us_per_step": round(step_ms * 1e3, 2),
         "decode_us": round(dec_avg_ms * 1e3, 2),
@@ -363,7 +401,7 @@ def main():
                            "kernel_frac_of_ceiling": round(achieved / ceil_nt, 4)}
     if not args.no_cpu_baseline and not w.paged:
         res["cpu_baseline"] = cpu_baseline_u8(x, qc, args.cpu_sample_seqs) if u8 else \
-            cpu_baseline(x, args.cpu_sample_seqs)
+            cpu_baseline(x, args.cpu_sample_seqs, win)
     print(json.dumps(res), flush=True)
 
 
