@@ -29,6 +29,10 @@
  *    its QuantizedKVCache listing (the *_u8 entry points): uint8 codes with a
  *    per-vector step and zero point; its SlidingWindowAttention listing (the
  *    *_window and *_ring entry points): attention over the last W tokens.
+ *  - "Arsitektur Inferensi LLM: PagedAttention, KV-Cache & Speculative
+ *    Decoding" (tveniu.com), sections 6 and 7 (the *_multi entry points):
+ *    several new tokens per sequence in one pass - the target model checking
+ *    gamma drafted tokens, or a prompt chunk - each attending causally.
  *
  * Conventions for every entry point:
  *  - All tensors are dense, row-major, in DEVICE memory, owned by the caller.
@@ -54,7 +58,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 5
+#define KVC_ABI_VERSION 6
 
 typedef enum kvc_status {
     KVC_OK = 0,
@@ -311,6 +315,53 @@ kvc_status kvc_decode_step_window(kvc_dtype dtype, int B, int H_q, int H_kv, int
                                   const float* rope_sin, int rope_rows, int rope_style, int max_seq_len,
                                   int window, int ring, float scale, void* out, int split_tokens, void* workspace,
                                   size_t workspace_bytes, void* stream);
+
+/*
+ * Several new tokens per sequence (speculative verification of drafted
+ * tokens, chunked prefill): token i (0 <= i < n) of sequence b takes position
+ * positions[b] + i; its query attends the cache and the new tokens up to
+ * itself (causal), i.e. tokens [lo_i, L_b - n + i + 1) with L_b = seq_lens[b]
+ * (the length after the append, so L_b >= n) and lo_i = max(0, L_b - n + i +
+ * 1 - window) (window 0: lo_i = 0).  Layouts are token-major:
+ * k_new, v_new [B, n, H_kv, d]; q, q_inout, out [B, n, H_q, d].  n = 1 is the
+ * single-token step.  Decode: bf16 only, head_dim 64, 128 or 256; the G * n
+ * query rows of a KV group are served 32 at a time from one pass over its
+ * cache (ceil(G * n / 32) passes).
+ */
+
+/*
+ * kvc_append_multi - kvc_append for n tokens per sequence: token i goes to
+ * slot positions[b] + i (contiguous, or through the block table), its key
+ * and q_inout[b, i] (if not NULL) rotated at that position.  Tokens whose
+ * position is outside the cache or the table write nothing.
+ */
+kvc_status kvc_append_multi(kvc_dtype dtype, int B, int n, int H_q, int H_kv, int d, void* k_cache, void* v_cache,
+                            int T_max, const int32_t* block_table, int block_size, int max_blocks_per_seq,
+                            int num_blocks, const int32_t* positions, const void* k_new, const void* v_new,
+                            void* q_inout, const float* rope_cos, const float* rope_sin, int rope_rows,
+                            int rope_style, void* stream);
+
+/*
+ * Workspace bytes and split length of kvc_decode_attn_multi with these sizes
+ * (as kvc_decode_workspace_bytes / kvc_decode_split_tokens; pool_tokens as
+ * there).  (size_t)-1 / -1 for invalid or unsupported sizes.
+ */
+size_t kvc_decode_multi_workspace_bytes(kvc_dtype dtype, int B, int n, int H_q, int H_kv, int d, int max_seq_len,
+                                        int window, long long pool_tokens, int split_tokens);
+int kvc_decode_multi_split_tokens(kvc_dtype dtype, int B, int n, int H_q, int H_kv, int d, int max_seq_len,
+                                  int window, long long pool_tokens, int split_tokens);
+
+/*
+ * kvc_decode_attn_multi - the attention of the n new tokens of every sequence
+ * (after kvc_append_multi) over a contiguous cache (block_table == NULL) or a
+ * paged one, with an optional window (>= 0).  Other arguments as for
+ * kvc_decode_attn[_paged]; max_seq_len bounds seq_lens.
+ */
+kvc_status kvc_decode_attn_multi(kvc_dtype dtype, int B, int n, int H_q, int H_kv, int d, const void* q,
+                                 const void* k_cache, const void* v_cache, int T_max, const int32_t* block_table,
+                                 int block_size, int max_blocks_per_seq, int num_blocks, const int32_t* seq_lens,
+                                 int max_seq_len, int window, float scale, void* out, int split_tokens,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Quantized cache (uint8 codes).  Each cached key or value vector (one

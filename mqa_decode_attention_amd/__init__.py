@@ -14,13 +14,19 @@ with a sliding window (the last `window` tokens of a full cache, or a ring of sl
     decode_attn_window(q, k_cache, v_cache, seq_lens, max_seq_len, window, ring=..., block_table=...)
     decode_step_window(q, k_cache, v_cache, positions, k_new, v_new, rope_cos, rope_sin, max_seq_len, window, ...)
 
+several new tokens per sequence (speculative verification, chunked prefill):
+
+    append_multi(k_cache, v_cache, positions, k_new, v_new, rope_cos, rope_sin, q=..., block_table=...)
+    decode_attn_multi(q, k_cache, v_cache, seq_lens, max_seq_len, window=..., block_table=...)
+
 and, for a uint8 quantized cache (codes plus a (step, zero point) pair per vector):
 
     append_u8(k_codes, k_sz, v_codes, v_sz, positions, k_new, v_new, rope_cos, rope_sin, ...)
     decode_attn_u8(q, k_codes, k_sz, v_codes, v_sz, seq_lens, max_seq_len)
     decode_attn_paged_u8(q, k_codes, k_sz, v_codes, v_sz, block_table, seq_lens, max_seq_len)
 """
-from .api import (KVC_BF16, KVC_F32, KVC_U8, KvcError, append, append_ring, append_u8, decode_attn,  # noqa: F401
-                  decode_attn_paged, decode_attn_paged_u8, decode_attn_u8, decode_attn_window, decode_step,
-                  decode_step_window, profile_next_decode, split_tokens, window_span, workspace_bytes)
+from .api import (KVC_BF16, KVC_F32, KVC_U8, KvcError, append, append_multi, append_ring, append_u8,  # noqa: F401
+                  decode_attn, decode_attn_multi, decode_attn_paged, decode_attn_paged_u8, decode_attn_u8,
+                  decode_attn_window, decode_step, decode_step_window, multi_split_tokens, multi_workspace_bytes,
+                  profile_next_decode, split_tokens, window_span, workspace_bytes)
 from ._lib import LIB_PATH, load  # noqa: F401

@@ -58,6 +58,20 @@ SIGNATURES = {
                                        c_void_p, c_void_p, c_void_p, c_void_p,
                                        c_int, c_int, c_int, c_int, c_int, c_float, c_void_p,
                                        c_int, c_void_p, c_size_t, c_void_p]),
+    "kvc_append_multi": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int,
+                                 c_void_p, c_void_p, c_int,
+                                 c_void_p, c_int, c_int, c_int, c_void_p,
+                                 c_void_p, c_void_p, c_void_p,
+                                 c_void_p, c_void_p, c_int, c_int, c_void_p]),
+    "kvc_decode_multi_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
+                                                    c_longlong, c_int]),
+    "kvc_decode_multi_split_tokens": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
+                                              c_longlong, c_int]),
+    "kvc_decode_attn_multi": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int,
+                                      c_void_p, c_void_p, c_void_p, c_int,
+                                      c_void_p, c_int, c_int, c_int, c_void_p,
+                                      c_int, c_int, c_float, c_void_p,
+                                      c_int, c_void_p, c_size_t, c_void_p]),
     "kvc_append_u8": (c_int, [c_int, c_int, c_int, c_int, c_int,
                               c_void_p, c_void_p, c_void_p, c_void_p, c_int,
                               c_void_p, c_int, c_int, c_int, c_void_p,
@@ -74,7 +88,7 @@ SIGNATURES = {
                                          c_int, c_void_p, c_size_t, c_void_p]),
 }
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 _lib = None
 

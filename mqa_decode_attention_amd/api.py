@@ -361,6 +361,84 @@ def decode_step_window(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
 
 
 # ---------------------------------------------------------------------------
+# several new tokens per sequence (speculative verification, chunked prefill):
+# k_new / v_new [B, n, H_kv, d], q / out [B, n, H_q, d]
+# ---------------------------------------------------------------------------
+
+
+def append_multi(k_cache: torch.Tensor, v_cache: torch.Tensor, positions: torch.Tensor, k_new: torch.Tensor,
+                 v_new: torch.Tensor, rope_cos: torch.Tensor, rope_sin: torch.Tensor,
+                 q: Optional[torch.Tensor] = None, block_table: Optional[torch.Tensor] = None,
+                 rope_style: str = "interleaved", stream=None) -> None:
+    """kvc_append_multi: token i of sequence b at slot positions[b] + i."""
+    lib = _lib.load()
+    dt = _dtype_code(k_new)
+    B, n, H_kv, d = k_new.shape
+    H_q = q.shape[2] if q is not None else H_kv
+    if rope_cos.dim() != 2 or rope_cos.shape[1] != d // 2:
+        raise ValueError(f"rope_cos must be [rows, {d // 2}], got {tuple(rope_cos.shape)}")
+    T_max, tbl, block_size, mb, num_blocks, shape = _cache_geometry(k_cache, block_table, B, H_kv, d)
+    _check(lib.kvc_append_multi(
+        dt, B, n, H_q, H_kv, d,
+        _dev(k_cache, "k_cache", k_new.dtype, shape), _dev(v_cache, "v_cache", k_new.dtype, shape), T_max,
+        tbl, block_size, mb, num_blocks, _dev(positions, "positions", torch.int32, (B,)),
+        _dev(k_new, "k_new", k_new.dtype), _dev(v_new, "v_new", k_new.dtype, (B, n, H_kv, d)),
+        _dev(q, "q", k_new.dtype, (B, n, H_q, d)) if q is not None else None,
+        _dev(rope_cos, "rope_cos", torch.float32), _dev(rope_sin, "rope_sin", torch.float32, rope_cos.shape),
+        rope_cos.shape[0], ROPE_STYLES[rope_style], _stream(k_new.device, stream)))
+
+
+def multi_workspace_bytes(dtype: torch.dtype, B: int, n: int, H_q: int, H_kv: int, d: int, max_seq_len: int,
+                          window: int = 0, split_tokens: int = 0, pool_tokens: int = 0) -> int:
+    """kvc_decode_multi_workspace_bytes."""
+    lib = _lib.load()
+    nb = lib.kvc_decode_multi_workspace_bytes(_cache_code(dtype), B, n, H_q, H_kv, d, max_seq_len, window,
+                                              pool_tokens, split_tokens)
+    if nb == (1 << 64) - 1:
+        raise KvcError(3, lib.kvc_last_error().decode() or "unsupported sizes")
+    return nb
+
+
+def multi_split_tokens(dtype: torch.dtype, B: int, n: int, H_q: int, H_kv: int, d: int, max_seq_len: int,
+                       window: int = 0, split_tokens: int = 0, pool_tokens: int = 0) -> int:
+    """kvc_decode_multi_split_tokens."""
+    lib = _lib.load()
+    ts = lib.kvc_decode_multi_split_tokens(_cache_code(dtype), B, n, H_q, H_kv, d, max_seq_len, window,
+                                           pool_tokens, split_tokens)
+    if ts < 0:
+        raise KvcError(3, lib.kvc_last_error().decode() or "unsupported sizes")
+    return ts
+
+
+def decode_attn_multi(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, seq_lens: torch.Tensor,
+                      max_seq_len: int, window: int = 0, block_table: Optional[torch.Tensor] = None,
+                      out: Optional[torch.Tensor] = None, scale: Optional[float] = None, split_tokens: int = 0,
+                      workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """kvc_decode_attn_multi: q [B, n, H_q, d] (rotated), seq_lens after the append;
+    returns out [B, n, H_q, d]."""
+    lib = _lib.load()
+    dt = _dtype_code(q)
+    B, n, H_q, d = q.shape
+    out = torch.empty_like(q) if out is None else out
+    H_kv = k_cache.shape[1]
+    T_max, tbl, block_size, mb, num_blocks, shape = _cache_geometry(k_cache, block_table, B, H_kv, d)
+    st = _stream(q.device, stream)
+    need = multi_workspace_bytes(q.dtype, B, n, H_q, H_kv, d, max_seq_len, window, split_tokens,
+                                 pool_tokens=num_blocks * block_size)
+    if workspace is not None:
+        ws, wsn = _dev(workspace, "workspace", torch.uint8), workspace.numel()
+    else:
+        ws, wsn = _workspace(q.device, st, need)
+    _check(lib.kvc_decode_attn_multi(
+        dt, B, n, H_q, H_kv, d, _dev(q, "q", q.dtype, (B, n, H_q, d)),
+        _dev(k_cache, "k_cache", q.dtype, shape), _dev(v_cache, "v_cache", q.dtype, shape), T_max,
+        tbl, block_size, mb, num_blocks, _dev(seq_lens, "seq_lens", torch.int32, (B,)), int(max_seq_len),
+        int(window), float(scale) if scale else 0.0, _dev(out, "out", q.dtype, (B, n, H_q, d)),
+        int(split_tokens), ws, wsn, st))
+    return out
+
+
+# ---------------------------------------------------------------------------
 # quantized cache: uint8 codes [.., d] with a float32 (step, zero point) pair
 # [.., 2] per cached vector
 # ---------------------------------------------------------------------------

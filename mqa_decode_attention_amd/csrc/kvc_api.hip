@@ -93,17 +93,30 @@ kvc_status check_heads(kvc_dtype dt, int B, int H_q, int H_kv, int d) {
 namespace kvc {
 
 bool plan_decode(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_len,
-                 long long pool_tokens, int split_tokens, DecodePlan* plan, const char** why) {
+                 long long pool_tokens, int split_tokens, DecodePlan* plan, const char** why, int qlen) {
     DecodePlan pl{};
     const int G = H_q / H_kv;
+    if (qlen > 1 && (dtype != KVC_BF16 || !decode_mfma_supported(dtype, d, 1))) {
+        *why = "several new tokens per sequence need bf16 and head_dim 64, 128 or 256";
+        return false;
+    }
     const bool u8 = dtype == KVC_U8;      // quantized cache: its own matrix-core kernel
     if (u8 && !decode_u8_supported(d, G)) {
         *why = "the quantized-cache kernel needs head_dim 64 or 128 and H_q / H_kv <= 32";
         return false;
     }
     pl.mfma = u8 || decode_mfma_supported(dtype, d, G);
-    pl.heads_per_wg = pl.mfma ? G : heads_per_wg(G);
-    pl.n_chunks = G / pl.heads_per_wg;
+    // query rows of a KV group: G, or G * qlen for several new tokens, served
+    // in chunks of 16 or 32 rows (one or two 16-row head blocks)
+    const int rows = G * std::max(qlen, 1);
+    if (qlen > 1) {
+        pl.heads_per_wg = rows <= 16 ? rows : 32;
+        pl.n_chunks = (rows + pl.heads_per_wg - 1) / pl.heads_per_wg;
+        pl.heads_per_wg = std::min(rows, pl.heads_per_wg);
+    } else {
+        pl.heads_per_wg = pl.mfma ? G : heads_per_wg(G);
+        pl.n_chunks = G / pl.heads_per_wg;
+    }
     if (!pl.mfma && !decode_supported(dtype, d, pl.heads_per_wg)) {
         *why = "no decode kernel for this dtype and head_dim (head_dim must be 16, 32, 64, 128 or 256)";
         return false;
@@ -133,16 +146,18 @@ bool plan_decode(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_l
         // least 32 * G tokens per split keeps that near 3 %, 12 * G (for
         // the large groups) near 8 %.
         const long long slots = static_cast<long long>(cu_count()) *
-                                (u8 ? decode_u8_wgs_per_cu(d, G) : decode_mfma_wgs_per_cu(d, G, pool_tokens > 0));
+                                (u8 ? decode_u8_wgs_per_cu(d, G)
+                                    : decode_mfma_wgs_per_cu(d, pl.heads_per_wg, pool_tokens > 0));
         const long long full = units * L;
-        const bool large_group = G > 16;
+        const int rpw = pl.heads_per_wg;      // query rows per workgroup
+        const bool large_group = rpw > 16;
         if (pool_tokens > 0 && pool_tokens * H_kv * 10 < full * 9) {
             ts = (pool_tokens * H_kv + 4 * slots - 1) / (4 * slots);
         } else {
             const long long S = std::max(1LL, (large_group ? 3 : 1) * slots / std::max(1LL, units));
             ts = (L + S - 1) / S;
         }
-        ts = std::max<long long>(ts, (large_group ? 12LL : 32LL) * G);
+        ts = std::max<long long>(ts, (large_group ? 12LL : 32LL) * rpw);
         // Whole loop steps of the kernel (64 or 128 tokens): splits that
         // start off a step boundary (e.g. balanced 4112 + 4081 for 8193
         // tokens with 128-token steps) streamed 2-13 % slower.
@@ -158,7 +173,7 @@ bool plan_decode(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_l
     pl.split_tokens = static_cast<int>(std::min<long long>(ts, 0x7FFFFFFF));
     pl.n_splits = static_cast<int>((L + ts - 1) / ts);
     if (pl.n_splits > 1) {
-        const size_t bh = static_cast<size_t>(B) * H_q;
+        const size_t bh = static_cast<size_t>(B) * H_q * std::max(qlen, 1);   // output rows
         pl.ws_ml = 0;
         pl.ws_part = align_up(bh * pl.n_splits * sizeof(float2), 256);
         pl.ws_bytes = align_up(pl.ws_part + bh * pl.n_splits * d * sizeof(float), 256);
@@ -210,7 +225,7 @@ kvc_status append_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, void*
                          int T_max, const int32_t* block_table, int block_size, int max_blocks_per_seq,
                          int num_blocks, const int32_t* positions, const void* k_new, const void* v_new,
                          void* q_inout, const float* rope_cos, const float* rope_sin, int rope_rows,
-                         int rope_style, bool ring, void* stream) {
+                         int rope_style, bool ring, void* stream, int qlen = 1) {
     kvc_status st = check_heads(dtype, B, H_q, H_kv, d);
     if (st != KVC_OK) return st;
     if (d % 2 != 0) return fail(KVC_ERR_SHAPE, "head_dim %d must be even for the rotation", d);
@@ -237,6 +252,7 @@ kvc_status append_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, void*
         p.capacity = ring ? 0x7FFFFFFF : T_max;    // a ring takes any position
     }
     p.ring = ring ? 1 : 0;
+    p.qlen = qlen;
     p.positions = positions;
     p.k_new = k_new; p.v_new = v_new; p.q_inout = q_inout;
     p.rope_cos = rope_cos; p.rope_sin = rope_sin; p.rope_rows = rope_rows;
@@ -266,6 +282,17 @@ kvc_status kvc_append_ring(kvc_dtype dtype, int B, int H_q, int H_kv, int d, voi
                            int rope_style, void* stream) {
     return append_common(dtype, B, H_q, H_kv, d, k_ring, v_ring, T_max, nullptr, 0, 0, 0, positions, k_new,
                          v_new, q_inout, rope_cos, rope_sin, rope_rows, rope_style, true, stream);
+}
+
+kvc_status kvc_append_multi(kvc_dtype dtype, int B, int n, int H_q, int H_kv, int d, void* k_cache, void* v_cache,
+                            int T_max, const int32_t* block_table, int block_size, int max_blocks_per_seq,
+                            int num_blocks, const int32_t* positions, const void* k_new, const void* v_new,
+                            void* q_inout, const float* rope_cos, const float* rope_sin, int rope_rows,
+                            int rope_style, void* stream) {
+    if (n < 1) return fail(KVC_ERR_SHAPE, "tokens per sequence must be >= 1");
+    return append_common(dtype, B, H_q, H_kv, d, k_cache, v_cache, T_max, block_table, block_size,
+                         max_blocks_per_seq, num_blocks, positions, k_new, v_new, q_inout, rope_cos, rope_sin,
+                         rope_rows, rope_style, false, stream, n);
 }
 
 int kvc_window_span(int max_seq_len, int window, int ring, int T_max) {
@@ -345,6 +372,41 @@ int kvc_decode_split_tokens(kvc_dtype dtype, int B, int H_q, int H_kv, int d, in
     return pl.split_tokens;
 }
 
+namespace {
+// plan of a multi-token call (sizes as kvc_decode_attn_multi's); false if invalid
+bool plan_multi(kvc_dtype dtype, int B, int n, int H_q, int H_kv, int d, int max_seq_len, int window,
+                long long pool_tokens, int split_tokens, kvc::DecodePlan* pl) {
+    if (n < 1 || window < 0 || check_heads(dtype, B, H_q, H_kv, d) != KVC_OK || max_seq_len < 0 ||
+        split_tokens < 0 || pool_tokens < 0) {
+        fail(KVC_ERR_SHAPE, "invalid sizes for a multi-token decode");
+        return false;
+    }
+    const char* why = nullptr;
+    const int span = kvc_window_span(max_seq_len, window > 0 ? window + n - 1 : 0, 0, 0);
+    if (!kvc::plan_decode(dtype, B, H_q, H_kv, d, span, pool_tokens, split_tokens, pl, &why, n)) {
+        fail(KVC_ERR_UNSUPPORTED, "%s", why);
+        return false;
+    }
+    return true;
+}
+}  // namespace
+
+size_t kvc_decode_multi_workspace_bytes(kvc_dtype dtype, int B, int n, int H_q, int H_kv, int d, int max_seq_len,
+                                        int window, long long pool_tokens, int split_tokens) {
+    kvc::DecodePlan pl;
+    if (!plan_multi(dtype, B, n, H_q, H_kv, d, max_seq_len, window, pool_tokens, split_tokens, &pl))
+        return static_cast<size_t>(-1);
+    ok();
+    return pl.ws_bytes;
+}
+
+int kvc_decode_multi_split_tokens(kvc_dtype dtype, int B, int n, int H_q, int H_kv, int d, int max_seq_len,
+                                  int window, long long pool_tokens, int split_tokens) {
+    kvc::DecodePlan pl;
+    if (!plan_multi(dtype, B, n, H_q, H_kv, d, max_seq_len, window, pool_tokens, split_tokens, &pl)) return -1;
+    return pl.split_tokens;
+}
+
 }  // extern "C"
 
 namespace {
@@ -368,7 +430,11 @@ kvc_status decode_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const
                          const int32_t* seq_lens, int max_seq_len, float scale, void* out,
                          int split_tokens, void* workspace, size_t workspace_bytes, void* stream,
                          const StepArgs* step, const float* k_sz = nullptr, const float* v_sz = nullptr,
-                         int window = 0, int ring = 0) {
+                         int window = 0, int ring = 0, int qlen = 0) {
+    // qlen: 0 for the single-token entry points; n >= 1 for kvc_decode_attn_multi
+    // (whose matrix-core launches use the multi-token rows even for n = 1)
+    const bool multi = qlen > 0;
+    qlen = multi ? qlen : 1;
     const hipEvent_t ev0 = g_prof_start, ev1 = g_prof_stop;   // one-shot, cleared by every call
     g_prof_start = g_prof_stop = nullptr;
     const bool u8 = dtype == KVC_U8;
@@ -384,6 +450,8 @@ kvc_status decode_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const
         return fail(KVC_ERR_SHAPE, "a ring of T_max = %d slots attends all of them: window must be 0 or %d", T_max,
                     T_max);
     if (u8 && (window || ring)) return fail(KVC_ERR_UNSUPPORTED, "no sliding window for the quantized cache");
+    if (multi && (u8 || ring || step))
+        return fail(KVC_ERR_UNSUPPORTED, "several new tokens: bf16 over a full cache, append first");
     if (paged) {
         if (block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0)
             return fail(KVC_ERR_SHAPE, "paged decode needs positive block_size, max_blocks_per_seq, num_blocks");
@@ -412,8 +480,9 @@ kvc_status decode_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const
     const long long pool_tokens = paged ? static_cast<long long>(num_blocks) * block_size : 0;
     // splits cover the attended span of a sequence (a window's tokens, or the
     // ring's slots), which kvc_window_span gives
-    const int span = kvc_window_span(max_seq_len, window, ring, T_max);
-    if (!kvc::plan_decode(dtype, B, H_q, H_kv, d, span, pool_tokens, split_tokens, &pl, &why))
+    // (several new tokens: the first one's window starts qlen - 1 tokens earlier)
+    const int span = kvc_window_span(max_seq_len, window > 0 ? window + qlen - 1 : 0, ring, T_max);
+    if (!kvc::plan_decode(dtype, B, H_q, H_kv, d, span, pool_tokens, split_tokens, &pl, &why, qlen))
         return fail(KVC_ERR_UNSUPPORTED, "%s", why);
     if (u8 && paged) {
         // 32-token tiles of 16-row groups, each inside one block, found in a
@@ -448,6 +517,7 @@ kvc_status decode_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const
     p.window = ring ? 0 : window;
     p.ring = ring ? 1 : 0;
     p.align = paged ? 16 : 1;
+    p.qlen = qlen;
     p.n_wg = static_cast<int>(n_wg);
     p.n_wg_pad = static_cast<int>((n_wg + 7) / 8 * 8);
     const float sc = scale > 0.0f ? scale : 1.0f / sqrtf(static_cast<float>(d));
@@ -496,7 +566,7 @@ kvc_status decode_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const
         }
     }
     if (u8) e = kvc::launch_decode_u8(d, p.G, paged, p, k_sz, v_sz, hs, tm);
-    else e = pl.mfma ? kvc::launch_decode_mfma(d, p.G, paged, fused, p, hs, tm)
+    else e = pl.mfma ? kvc::launch_decode_mfma(d, qlen > 1 ? pl.heads_per_wg : p.G, paged, fused, multi, p, hs, tm)
                      : kvc::launch_decode_split(dtype, d, pl.heads_per_wg, paged, p, hs, tm);
     if (e != hipSuccess) return hip_status(e, "decode split launch");
     if (pl.n_splits > 1) {
@@ -576,6 +646,21 @@ kvc_status kvc_decode_step_window(kvc_dtype dtype, int B, int H_q, int H_kv, int
     return decode_common(dtype, B, H_q, H_kv, d, q, k_cache, v_cache, T_max, 0, 0, nullptr, 0, nullptr,
                          max_seq_len, scale, out, split_tokens, workspace, workspace_bytes, stream, &st, nullptr,
                          nullptr, window, ring);
+}
+
+kvc_status kvc_decode_attn_multi(kvc_dtype dtype, int B, int n, int H_q, int H_kv, int d, const void* q,
+                                 const void* k_cache, const void* v_cache, int T_max, const int32_t* block_table,
+                                 int block_size, int max_blocks_per_seq, int num_blocks, const int32_t* seq_lens,
+                                 int max_seq_len, int window, float scale, void* out, int split_tokens,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+    if (n < 1) return fail(KVC_ERR_SHAPE, "tokens per sequence must be >= 1");
+    if (block_table)
+        return decode_common(dtype, B, H_q, H_kv, d, q, k_cache, v_cache, 0, num_blocks, block_size, block_table,
+                             max_blocks_per_seq, seq_lens, max_seq_len, scale, out, split_tokens, workspace,
+                             workspace_bytes, stream, nullptr, nullptr, nullptr, window, 0, n);
+    return decode_common(dtype, B, H_q, H_kv, d, q, k_cache, v_cache, T_max, 0, 0, nullptr, 0, seq_lens,
+                         max_seq_len, scale, out, split_tokens, workspace, workspace_bytes, stream, nullptr, nullptr,
+                         nullptr, window, 0, n);
 }
 
 kvc_status kvc_decode_attn_u8(int B, int H_q, int H_kv, int d, const void* q, const void* k_codes,

@@ -38,22 +38,27 @@ struct Store<uint16_t> {
     __device__ static void store(uint16_t* p, size_t i, float x) { p[i] = f32_to_bf16_rne(x); }
 };
 
-// One thread per (sequence, vector, pair).  Vectors of sequence b, in order:
-// the H_kv keys (rotated into the cache), the H_kv values (copied into the
-// cache), then, when q_inout is given, the H_q queries (rotated in place).
+// One thread per (sequence, new token, vector, pair).  Vectors of token bt =
+// b * qlen + t, in order: the H_kv keys (rotated into the cache), the H_kv
+// values (copied into the cache), then, when q_inout is given, the H_q
+// queries (rotated in place).  Token t of sequence b takes position
+// positions[b] + t.
 template <typename T>
 __global__ void __launch_bounds__(256) append_kernel(const AppendParams p) {
     const int half = p.d >> 1;
+    const int qlen = p.qlen > 0 ? p.qlen : 1;
     const int nvec = 2 * p.H_kv + (p.q_inout ? p.H_q : 0);
-    const long long total = static_cast<long long>(p.B) * nvec * half;
+    const long long total = static_cast<long long>(p.B) * qlen * nvec * half;
     const long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (idx >= total) return;
     const int i = static_cast<int>(idx % half);
     const int vec = static_cast<int>((idx / half) % nvec);
-    const int b = static_cast<int>(idx / (static_cast<long long>(half) * nvec));
+    const int bt = static_cast<int>(idx / (static_cast<long long>(half) * nvec));
+    const int b = bt / qlen;
 
-    const int pos = p.positions[b];
-    if (pos < 0 || pos >= p.capacity || pos >= p.rope_rows) return;
+    const long long pos_ll = static_cast<long long>(p.positions[b]) + (bt - b * qlen);
+    if (pos_ll < 0 || pos_ll >= p.capacity || pos_ll >= p.rope_rows) return;
+    const int pos = static_cast<int>(pos_ll);
 
     // slot of (b, head j) in the cache, in elements, for head 0; + j * head stride
     size_t slot0;
@@ -75,7 +80,7 @@ __global__ void __launch_bounds__(256) append_kernel(const AppendParams p) {
 
     if (vec >= p.H_kv && vec < 2 * p.H_kv) {  // value: bit copy of both elements
         const int j = vec - p.H_kv;
-        const T* src = static_cast<const T*>(p.v_new) + (static_cast<size_t>(b) * p.H_kv + j) * p.d;
+        const T* src = static_cast<const T*>(p.v_new) + (static_cast<size_t>(bt) * p.H_kv + j) * p.d;
         T* dst = static_cast<T*>(p.v_cache) + slot0 + j * head_stride;
         dst[2 * i] = src[2 * i];
         dst[2 * i + 1] = src[2 * i + 1];
@@ -87,11 +92,11 @@ __global__ void __launch_bounds__(256) append_kernel(const AppendParams p) {
     const T* src;
     T* dst;
     if (vec < p.H_kv) {
-        src = static_cast<const T*>(p.k_new) + (static_cast<size_t>(b) * p.H_kv + vec) * p.d;
+        src = static_cast<const T*>(p.k_new) + (static_cast<size_t>(bt) * p.H_kv + vec) * p.d;
         dst = static_cast<T*>(p.k_cache) + slot0 + vec * head_stride;
     } else {
         const int h = vec - 2 * p.H_kv;
-        dst = static_cast<T*>(p.q_inout) + (static_cast<size_t>(b) * p.H_q + h) * p.d;
+        dst = static_cast<T*>(p.q_inout) + (static_cast<size_t>(bt) * p.H_q + h) * p.d;
         src = dst;
     }
     const float x0 = Store<T>::load(src, e0);
@@ -226,7 +231,7 @@ hipError_t launch_append_u8(const AppendParams& p, hipStream_t stream) {
 
 hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
     const int nvec = 2 * p.H_kv + (p.q_inout ? p.H_q : 0);
-    const long long total = static_cast<long long>(p.B) * nvec * (p.d / 2);
+    const long long total = static_cast<long long>(p.B) * (p.qlen > 0 ? p.qlen : 1) * nvec * (p.d / 2);
     const int threads = 256;
     const long long blocks = (total + threads - 1) / threads;
     if (blocks <= 0) return hipSuccess;

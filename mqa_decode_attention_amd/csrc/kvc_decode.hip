@@ -287,8 +287,9 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(const DecodeParams p)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const long long bh = static_cast<long long>(blockIdx.x) * 4 + wave;
-    if (bh >= static_cast<long long>(p.B) * p.H_q) return;
-    const int b = static_cast<int>(bh / p.H_q);
+    // output row bh = (b * qlen + i) * H_q + h
+    if (bh >= static_cast<long long>(p.B) * p.qlen * p.H_q) return;
+    const int b = static_cast<int>(bh / (static_cast<long long>(p.qlen) * p.H_q));
     const int nsp = split_count(p, token_range(p, attended_len(p, b)));
     if (nsp <= 1) return;                        // written directly by the split kernel
     const float2* ml = p.ws_ml + bh * p.n_splits;
@@ -362,7 +363,7 @@ hipError_t launch_tdg(bool paged, const DecodeParams& p, hipStream_t stream, con
 
 template <typename T, int D>
 hipError_t launch_merge_td(const DecodeParams& p, hipStream_t stream) {
-    const long long waves = static_cast<long long>(p.B) * p.H_q;
+    const long long waves = static_cast<long long>(p.B) * p.qlen * p.H_q;   // output rows
     const dim3 grid(static_cast<unsigned>((waves + 3) / 4)), block(256);
     hipLaunchKernelGGL((decode_merge_kernel<T, D>), grid, block, 0, stream, p);
     return hipGetLastError();

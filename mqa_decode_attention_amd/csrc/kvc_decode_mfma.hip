@@ -58,7 +58,7 @@ using namespace mfma;
 // once, and K and V tiles are staged like those of a contiguous cache.
 // (The paged kernel with staged tiles and one head block is planned at three
 // workgroups per CU: its registers are held to three waves per SIMD.)
-template <int D, int HB, int NW, int MODE, bool FUSED>
+template <int D, int HB, int NW, int MODE, bool FUSED, bool MQ>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((MODE == 3 && HB == 1) ? 3 : 1, 8)))
 decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table) {
     // (the block table as its own restrict argument: nothing this kernel stores
@@ -102,10 +102,13 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     const int wid = blockIdx.x < static_cast<unsigned>(p.n_wg) ? static_cast<int>(blockIdx.x) : -1;
     if (wid < 0) return;
     const int split = wid % p.n_splits;
-    const int unit = wid / p.n_splits;    // b * H_kv + j
-    const int b = unit / p.H_kv;
-    const int j = unit % p.H_kv;
+    const int unit = wid / p.n_splits;    // b * H_kv + j (MQ: (b * H_kv + j) * n_chunks + chunk)
+    const int chunk = MQ ? unit % p.n_chunks : 0;
+    const int bj = MQ ? unit / p.n_chunks : unit;
+    const int b = bj / p.H_kv;
+    const int j = bj % p.H_kv;
     const int G = p.G;
+    static_assert(!(MQ && FUSED), "several new tokens: the append runs first");
 
     // fused step: slot of the new token (read once; it also gives L)
     const int pos = FUSED ? p.positions[b] : 0;
@@ -329,14 +332,47 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     // them, so lanes of heads >= G read zeros.
     const size_t qgrp = (static_cast<size_t>(b) * p.H_q + static_cast<size_t>(j) * G) * D;
     const __amdgpu_buffer_rsrc_t qrs =
-        make_uniform_rsrc(static_cast<const uint16_t*>(FUSED ? p.q_raw : p.q) + qgrp, G * D * 2);
+        MQ ? make_uniform_rsrc(static_cast<const uint16_t*>(p.q) + static_cast<size_t>(b) * p.qlen * p.H_q * D,
+                               p.qlen * p.H_q * D * 2)
+           : make_uniform_rsrc(static_cast<const uint16_t*>(FUSED ? p.q_raw : p.q) + qgrp, G * D * 2);
+    // MQ: this lane's query row of each head block is row rho of the group's
+    // G * qlen rows (new token i = rho / G, head g = rho % G) at
+    // q[b, i, j * G + g]; rows past the last read zeros (offset past the range)
+    int qoff[HB];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+        if constexpr (MQ) {
+            const int rho = chunk * 16 * HB + 16 * hb + r16;
+            const int qi = rho / G;
+            qoff[hb] = rho < G * p.qlen ? (qi * p.H_q + j * G + (rho - qi * G)) * D : p.qlen * p.H_q * D;
+        } else {
+            qoff[hb] = (16 * hb + r16) * D;
+        }
+    }
     uint4 qb[HB][KK];
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk)
             qb[hb][kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                qrs, ((16 * hb + r16) * D + 32 * kk + 8 * q4) * 2, 0, 0));
+                qrs, (qoff[hb] + 32 * kk + 8 * q4) * 2, 0, 0));
+    // MQ: tokens this lane's query rows attend, [row_lo, row_hi) within the
+    // split: causal among the new tokens (token i sees up to L - qlen + i),
+    // and its own window start
+    int row_lo[HB], row_hi[HB];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+        if constexpr (MQ) {
+            const int rho = chunk * 16 * HB + 16 * hb + r16;
+            const int hi = L - p.qlen + rho / G + 1;
+            const int lo = p.window > 0 ? max(0, hi - p.window) : 0;
+            row_hi[hb] = min(t_end, hi);
+            row_lo[hb] = max(t_lo, lo);
+        } else {
+            row_hi[hb] = t_end;
+            row_lo[hb] = t_lo;
+        }
+    }
 
     // Fused step.  The new token sits at slot pos of sequence b; the last
     // split of (b, j) stores it (rotated key, raw value) and, since its own
@@ -524,7 +560,9 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int t = tok(base, 16 * kb + 4 * q4 + e);
-                    const bool in = (PAGED ? t >= t_lo : true) && t < t_end;   // contiguous splits start at t_lo
+                    // (contiguous single-token splits start at t_lo)
+                    const bool in = MQ ? (t >= row_lo[hb] && t < row_hi[hb])
+                                       : ((PAGED ? t >= t_lo : true) && t < t_end);
                     s[hb][4 * kb + e] = in ? acc[e] * p.scale_log2 : -INFINITY;
                 }
             }
@@ -696,7 +734,8 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
             sm_m[wave * 16 + r16] = m[hb];
             sm_l[wave * 16 + r16] = l[hb];
         }
-        const int heads = min(16, G - 16 * hb);
+        // query rows of this head block (MQ: of this chunk of the G * qlen rows)
+        const int heads = MQ ? min(16, G * p.qlen - chunk * 16 * HB - 16 * hb) : min(16, G - 16 * hb);
         for (int r0 = 0; r0 < heads; r0 += RB) {
             // lane holds O^T[c][g] for c = 16*nb + 4*q4 + e, g = 16*hb + r16
             const int row = r16 - r0;
@@ -731,7 +770,14 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
                     A.w = fmaf(ow.w, f, A.w);
                     Ls = fmaf(sm_l[w * 16 + gh], f, Ls);
                 }
-                const size_t bh = static_cast<size_t>(b) * p.H_q + j * G + 16 * hb + gh;
+                size_t bh;                // output row: (b, h), or (b, i, h) for several new tokens
+                if constexpr (MQ) {
+                    const int rho = chunk * 16 * HB + 16 * hb + gh;
+                    const int qi = rho / G;
+                    bh = (static_cast<size_t>(b) * p.qlen + qi) * p.H_q + j * G + (rho - qi * G);
+                } else {
+                    bh = static_cast<size_t>(b) * p.H_q + j * G + 16 * hb + gh;
+                }
                 const int c = 4 * ch;
                 if (nsp == 1) {
                     uint2 packed;
@@ -752,26 +798,33 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
 
 constexpr int kNWm = 4;
 
-template <int D, int HB, bool FUSED>
+template <int D, int HB, bool FUSED, bool MQ>
 hipError_t launch_dhf(bool paged, const DecodeParams& p, hipStream_t stream, const KernelTiming& tm) {
     const dim3 grid(p.n_wg_pad), block(kNWm * 64);
     const int32_t* tbl = p.block_table;
-    if (!paged) return launch_timed(decode_mfma_kernel<D, HB, kNWm, 0, FUSED>, grid, block, stream, tm, p, tbl);
+    if (!paged) return launch_timed(decode_mfma_kernel<D, HB, kNWm, 0, FUSED, MQ>, grid, block, stream, tm, p, tbl);
     if constexpr (D <= 128) {
         if (p.block_size % 16 == 0 && p.split_tokens % 16 == 0 && p.split_tokens / p.block_size + 2 <= kTblMax)
-            return launch_timed(decode_mfma_kernel<D, HB, kNWm, 3, FUSED>, grid, block, stream, tm, p, tbl);
+            return launch_timed(decode_mfma_kernel<D, HB, kNWm, 3, FUSED, MQ>, grid, block, stream, tm, p, tbl);
     }
     if (p.block_size % 16 == 0 && p.split_tokens % 32 == 0)
-        return launch_timed(decode_mfma_kernel<D, HB, kNWm, 2, FUSED>, grid, block, stream, tm, p, tbl);
-    return launch_timed(decode_mfma_kernel<D, HB, kNWm, 1, FUSED>, grid, block, stream, tm, p, tbl);
+        return launch_timed(decode_mfma_kernel<D, HB, kNWm, 2, FUSED, MQ>, grid, block, stream, tm, p, tbl);
+    return launch_timed(decode_mfma_kernel<D, HB, kNWm, 1, FUSED, MQ>, grid, block, stream, tm, p, tbl);
 }
 
+// rows: query rows one workgroup serves (G, or a chunk of the G * qlen rows
+// of several new tokens), in one or two 16-row head blocks
 template <int D>
-hipError_t launch_d(int G, bool paged, bool fused, const DecodeParams& p, hipStream_t stream,
+hipError_t launch_d(int rows, bool paged, bool fused, bool multi, const DecodeParams& p, hipStream_t stream,
                     const KernelTiming& tm) {
-    if (G <= 16)
-        return fused ? launch_dhf<D, 1, true>(paged, p, stream, tm) : launch_dhf<D, 1, false>(paged, p, stream, tm);
-    return fused ? launch_dhf<D, 2, true>(paged, p, stream, tm) : launch_dhf<D, 2, false>(paged, p, stream, tm);
+    if (multi)
+        return rows <= 16 ? launch_dhf<D, 1, false, true>(paged, p, stream, tm)
+                          : launch_dhf<D, 2, false, true>(paged, p, stream, tm);
+    if (rows <= 16)
+        return fused ? launch_dhf<D, 1, true, false>(paged, p, stream, tm)
+                     : launch_dhf<D, 1, false, false>(paged, p, stream, tm);
+    return fused ? launch_dhf<D, 2, true, false>(paged, p, stream, tm)
+                 : launch_dhf<D, 2, false, false>(paged, p, stream, tm);
 }
 
 }  // namespace
@@ -798,12 +851,12 @@ int decode_mfma_wgs_per_cu(int d, int G, bool paged) {
     return 1;
 }
 
-hipError_t launch_decode_mfma(int d, int G, bool paged, bool fused, const DecodeParams& p,
+hipError_t launch_decode_mfma(int d, int rows, bool paged, bool fused, bool multi, const DecodeParams& p,
                               hipStream_t stream, const KernelTiming& tm) {
     switch (d) {
-        case 64: return launch_d<64>(G, paged, fused, p, stream, tm);
-        case 128: return launch_d<128>(G, paged, fused, p, stream, tm);
-        case 256: return launch_d<256>(G, paged, fused, p, stream, tm);
+        case 64: return launch_d<64>(rows, paged, fused, multi, p, stream, tm);
+        case 128: return launch_d<128>(rows, paged, fused, multi, p, stream, tm);
+        case 256: return launch_d<256>(rows, paged, fused, multi, p, stream, tm);
         default: return hipErrorInvalidValue;
     }
 }

@@ -29,6 +29,7 @@ struct AppendParams {
     int rope_rows;
     int rope_style;
     int ring;                    // contiguous ring of T_max slots: position p -> slot p % T_max
+    int qlen;                    // new tokens per sequence (token i at position positions[b] + i; 0 means 1)
     // uint8 quantized cache (launch_append_u8): k_cache / v_cache hold the
     // codes [.., d] and these the float (step, zero point) pair of each vector
     float* k_sz;
@@ -92,6 +93,12 @@ struct DecodeParams {
     // in slot t % T_max) and the slots [0, min(L, T_max)) are attended.
     int window, ring;
     int align;                   // split origins are multiples of this (a power of two)
+
+    // New tokens per sequence (1 for a single-token step).  With qlen > 1, q
+    // and out are [B, qlen, H_q, d] and query token i of a sequence holding L
+    // tokens attends [.., L - qlen + i + 1) (causal among the new tokens); the
+    // G * qlen query rows of a KV group are cut into n_chunks chunks.
+    int qlen;
 };
 
 // Attended length of sequence b: from positions (a decode step, after its
@@ -122,8 +129,10 @@ __device__ __forceinline__ TokenRange token_range(const DecodeParams& p, int L) 
         r.lo = 0;
         r.hi = L < p.T_max ? L : p.T_max;
     } else {
+        // (with several new tokens the first one's window starts earliest)
+        const int first_hi = L - p.qlen + 1;
         r.hi = L;
-        r.lo = (p.window > 0 && L > p.window) ? L - p.window : 0;
+        r.lo = (p.window > 0 && first_hi > p.window) ? first_hi - p.window : 0;
     }
     r.org = r.lo & ~(p.align - 1);
     return r;
@@ -137,8 +146,9 @@ __device__ __forceinline__ int split_count(const DecodeParams& p, const TokenRan
 // Returns false (and leaves *plan untouched) when the sizes cannot be planned.
 // pool_tokens: token capacity of a paged pool (num_blocks * block_size), which
 // bounds the tokens all sequences attend over together; 0 for a contiguous cache.
+// qlen: new tokens per sequence (query rows G * qlen per KV group).
 bool plan_decode(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_len,
-                 long long pool_tokens, int split_tokens, DecodePlan* plan, const char** why);
+                 long long pool_tokens, int split_tokens, DecodePlan* plan, const char** why, int qlen = 1);
 
 // Is there a kernel for this (dtype, head dim, heads per workgroup)?
 bool decode_supported(kvc_dtype dtype, int d, int heads_per_wg);
@@ -176,7 +186,9 @@ int decode_mfma_step_tokens(int d, bool paged);
 // Workgroups of the MFMA decode kernel one compute unit holds at once (set by
 // its registers and LDS at this head dim, group size and cache layout).
 int decode_mfma_wgs_per_cu(int d, int G, bool paged);
-hipError_t launch_decode_mfma(int d, int G, bool paged, bool fused, const DecodeParams& p,
+// rows: query rows per workgroup (G; with several new tokens, up to 32 of the
+// G * qlen rows, multi = true).
+hipError_t launch_decode_mfma(int d, int rows, bool paged, bool fused, bool multi, const DecodeParams& p,
                               hipStream_t stream, const KernelTiming& tm);
 
 // The matrix-core streaming kernel over a uint8 quantized cache (bf16 q and

@@ -27,7 +27,8 @@ def test_shapes_and_determinism(name):
                            y.view(torch.uint8) if y.dtype != torch.int32 else y), f
     want = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     assert a.q.dtype == want and a.k_cache.dtype == want
-    assert a.q.shape == (w.B, w.H_q, w.d) and a.k_new.shape == (w.B, w.H_kv, w.d)
+    tok = (w.new_tokens,) if w.new_tokens > 1 else ()
+    assert a.q.shape == (w.B,) + tok + (w.H_q, w.d) and a.k_new.shape == (w.B,) + tok + (w.H_kv, w.d)
     assert a.rope_cos.shape == (w.table_rows, w.d // 2)
     assert int(a.cached.min()) >= w.cached_lo and int(a.cached.max()) <= w.cached_hi
     if w.paged:
@@ -48,7 +49,7 @@ def test_poison_exactly_past_cached_length(name):
     for b, c in enumerate(x.cached.tolist()):
         if w.paged:
             bs = w.block_size
-            for p in range(0, -(-(c + 1) // bs) * bs):
+            for p in range(0, -(-(c + w.new_tokens) // bs) * bs):
                 blk = int(x.block_table[b, p // bs])
                 row = x.k_cache[blk, :, p % bs].float()
                 assert bool(torch.isnan(row).all()) == (p >= c)

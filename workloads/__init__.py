@@ -20,6 +20,14 @@ Workloads (the shapes of the pages' examples, synthetic values N(0, 1)):
 * ``paged_gqa``  batch 32, 32 / 8 heads, head dim 128, block size 16, cached
                  lengths uniform in [1024, 16384]; the blocks of all sequences
                  sit in one shared pool in a seeded random order.
+* ``spec_gqa``   gqa_8b's shape with 6 new tokens per sequence: the target
+                 model checking gamma = 5 drafted tokens in one pass, the
+                 worked example of speculative decoding in "Arsitektur
+                 Inferensi LLM" (tveniu.com), section 7.
+
+A workload with ``new_tokens`` = n > 1 draws q [B, n, H_q, d] and k_new,
+v_new [B, n, H_kv, d] (token-major); the cache then has room for, and NaN in,
+the n slots the append fills.
 
 Draw order (one ``torch.Generator`` seeded with the workload's seed):
 cached lengths -> block permutation (paged only) -> K cache -> V cache -> q ->
@@ -69,6 +77,7 @@ class Workload:
     layout: str = "contiguous"  # or "paged"
     T_max: int = 0             # contiguous capacity (tokens per (b, kv head))
     block_size: int = 16       # paged only
+    new_tokens: int = 1        # tokens appended (and queries attending) per sequence
     rope_base: float = 10000.0
 
     @property
@@ -81,7 +90,7 @@ class Workload:
 
     @property
     def max_attended(self) -> int:
-        return self.cached_hi + 1
+        return self.cached_hi + self.new_tokens
 
     @property
     def max_blocks_per_seq(self) -> int:
@@ -97,8 +106,8 @@ class Workload:
     def replace(self, **kw) -> "Workload":
         """Same structure at another size (for oracle-sized parity cases)."""
         w = dataclasses.replace(self, **kw)
-        if not w.paged and w.T_max < w.cached_hi + 1:
-            w = dataclasses.replace(w, T_max=_round_up(w.cached_hi + 1, 8))
+        if not w.paged and w.T_max < w.cached_hi + w.new_tokens:
+            w = dataclasses.replace(w, T_max=_round_up(w.cached_hi + w.new_tokens, 8))
         return w
 
 
@@ -117,6 +126,8 @@ WORKLOADS = {
                          cached_lo=131072, cached_hi=131072, T_max=131080),
     "paged_gqa": Workload("paged_gqa", 4, B=32, H_q=32, H_kv=8, d=128, dtype="bf16",
                           cached_lo=1024, cached_hi=16384, layout="paged", block_size=16),
+    "spec_gqa": Workload("spec_gqa", 5, B=16, H_q=32, H_kv=8, d=128, dtype="bf16",
+                         cached_lo=8192, cached_hi=8192, T_max=8200, new_tokens=6),
 }
 
 
@@ -130,7 +141,8 @@ class DecodeInputs:
     v_cache     same shape as k_cache
     block_table int32 [B, max_blocks_per_seq] (paged; -1 = unused) or None
     q           [B, H_q, d]   raw (not yet rotated) query of the new token
-    k_new, v_new [B, H_kv, d] raw key and value of the new token
+                ([B, n, H_q, d] for n = new_tokens > 1)
+    k_new, v_new [B, H_kv, d] raw key and value of the new token ([B, n, H_kv, d])
     rope_cos, rope_sin  float32 [table_rows, d // 2]
     """
     workload: Workload
@@ -146,8 +158,8 @@ class DecodeInputs:
 
     @property
     def seq_lens(self) -> torch.Tensor:
-        """Attended length after the append (cached + 1)."""
-        return self.cached + 1
+        """Length after the append (cached + new tokens)."""
+        return self.cached + self.workload.new_tokens
 
 
 def _storage(x: torch.Tensor, dtype: str) -> torch.Tensor:
@@ -175,7 +187,8 @@ def draw(w: Workload) -> DecodeInputs:
     else:
         cached = torch.randint(w.cached_lo, w.cached_hi + 1, (w.B,), generator=g,
                                dtype=torch.int64).to(torch.int32)
-    lens = (cached + 1).tolist()
+    n_new = w.new_tokens
+    lens = (cached + n_new).tolist()
 
     block_table = None
     if w.paged:
@@ -190,14 +203,15 @@ def draw(w: Workload) -> DecodeInputs:
             off += n
         shape = (total, w.H_kv, bs, w.d)
     else:
-        assert w.T_max >= w.cached_hi + 1, "contiguous capacity must hold cached + 1"
+        assert w.T_max >= w.cached_hi + n_new, "contiguous capacity must hold the cached and new tokens"
         shape = (w.B, w.H_kv, w.T_max, w.d)
 
     k_cache = torch.randn(shape, generator=g, dtype=torch.float32)
     v_cache = torch.randn(shape, generator=g, dtype=torch.float32)
-    q = torch.randn((w.B, w.H_q, w.d), generator=g, dtype=torch.float32)
-    k_new = torch.randn((w.B, w.H_kv, w.d), generator=g, dtype=torch.float32)
-    v_new = torch.randn((w.B, w.H_kv, w.d), generator=g, dtype=torch.float32)
+    tok = (n_new,) if n_new > 1 else ()
+    q = torch.randn((w.B,) + tok + (w.H_q, w.d), generator=g, dtype=torch.float32)
+    k_new = torch.randn((w.B,) + tok + (w.H_kv, w.d), generator=g, dtype=torch.float32)
+    v_new = torch.randn((w.B,) + tok + (w.H_kv, w.d), generator=g, dtype=torch.float32)
 
     k_cache = _storage(k_cache, w.dtype)
     v_cache = _storage(v_cache, w.dtype)
