@@ -156,6 +156,40 @@ def cpu_baseline(x, n_seqs, window=0):
             "sample": f"{B} of {w.B} sequences of {w.name} ({what}, float64, numpy, one thread), {sec:.2f} s"}
 
 
+def cpu_baseline_multi(x, n_seqs, window=0):
+    """Time the multi-token oracle (as it stands, one thread) on the same step."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import oracle.kvc_multi_oracle as MO
+
+    w = x.workload
+    B = w.B if n_seqs <= 0 else min(n_seqs, w.B)
+    dt = w.dtype
+
+    def np_store(t):
+        t = t.contiguous()
+        return t.view(torch.int16).numpy().view(np.uint16) if dt == "bf16" else t.numpy()
+
+    if w.paged:
+        raise NotImplementedError("CPU baseline is timed on contiguous workloads")
+    kc, vc = np_store(x.k_cache[:B]), np_store(x.v_cache[:B])
+    q, kn, vn = np_store(x.q[:B]), np_store(x.k_new[:B]), np_store(x.v_new[:B])
+    cos, sin = x.rope_cos.numpy(), x.rope_sin.numpy()
+    cached = x.cached.numpy()[:B]
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        k2, v2, q2 = MO.append_multi(kc, vc, cached, kn, vn, cos, sin, dt, q=q)
+        MO.decode_attention_multi(q2, k2, v2, cached + w.new_tokens, dt, window)
+        sec = time.perf_counter() - t0
+    nbytes = kv_read_bytes(attended(cached + w.new_tokens, window + w.new_tokens - 1 if window else 0), w.H_kv, w.d,
+                           2 if dt == "bf16" else 4)
+    return {"value": round(nbytes / sec / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{B} of {w.B} sequences of {w.name} (append of {w.new_tokens} tokens + their attention, "
+                      f"float64, numpy, one thread), {sec:.2f} s"}
+
+
 def cpu_baseline_u8(x, qc, n_seqs):
     """Time the quantized-cache oracle (as it stands, one thread) on the same step."""
     import numpy as np
@@ -253,6 +287,10 @@ def main():
     torch.cuda.set_device(dev)
     u8 = args.kv_cache == "u8"
     win = args.window
+    multi = w.new_tokens > 1          # several new tokens per sequence: append_multi + decode_attn_multi
+    if multi and (u8 or args.ring):
+        print("multi-token workloads run on the native full cache", file=sys.stderr)
+        sys.exit(2)
     if (win or args.ring) and (u8 or w.paged and args.ring or args.ring and win <= 0):
         print("--window applies to the native cache; --ring needs --window and a contiguous workload",
               file=sys.stderr)
@@ -263,7 +301,7 @@ def main():
         kv_bytes = kv_read_bytes_u8(x.seq_lens.tolist(), w.H_kv, w.d)
         cache_bytes = (qc.k_codes.numel() + qc.k_sz.numel() * 4) * 2
     else:
-        kv_bytes = kv_read_bytes(attended(x.seq_lens.tolist(), win), w.H_kv, w.d, e)
+        kv_bytes = kv_read_bytes(attended(x.seq_lens.tolist(), win + w.new_tokens - 1 if win else 0), w.H_kv, w.d, e)
         cache_bytes = x.k_cache.numel() * e * 2
     R = max(1, min(64, -(-MALL_DEFEAT_BYTES // cache_bytes)))
 
@@ -310,8 +348,13 @@ def main():
             else:
                 kvc.decode_attn_u8(q_work, kc, ksz, vc, vsz, lens, max_len, out=out, split_tokens=args.split_tokens)
             return
-        if ev is not None:   # the library attaches these to its streaming kernel
-            kvc.profile_next_decode(ev[0], ev[1])
+        if multi:
+            kvc.append_multi(ks[r], vs[r], pos, kn, vn, cos, sin, q=q_work, block_table=tbl)
+            if ev is not None:
+                kvc.profile_next_decode(ev[0], ev[1])
+            kvc.decode_attn_multi(q_work, ks[r], vs[r], lens, max_len, win, block_table=tbl, out=out,
+                                  split_tokens=args.split_tokens)
+            return
         if win:
             kvc.decode_step_window(q, ks[r], vs[r], pos, kn, vn, cos, sin, max_len, win, ring=args.ring,
                                    block_table=tbl, q_rot_out=q_rot, out=out, split_tokens=args.split_tokens)
@@ -352,7 +395,7 @@ def main():
 
     achieved = kv_bytes / (dec_avg_ms * 1e-3) / 1e9
     value = kv_bytes / (step_ms * 1e-3) / 1e9
-    traffic = None if win else traffic_for_current_kernel(args.kv_cache, w.name)
+    traffic = None if (win or multi) else traffic_for_current_kernel(args.kv_cache, w.name)
     pool_tokens = x.k_cache.shape[0] * w.block_size if w.paged else 0
 
     res = {
@@ -375,10 +418,13 @@ def main():
                    "head_dim": w.d, "cached_tokens": [w.cached_lo, w.cached_hi], "layout": w.layout,
                    "kv_cache": "uint8 codes + float32 (step, zero point) per vector" if u8 else w.dtype,
                    "kv_bytes_per_step": kv_bytes, "cache_replicas": R,
-                   "window": win, "ring": bool(args.ring),
-                   "split_tokens": kvc.split_tokens(torch.uint8 if u8 else x.q.dtype, w.B, w.H_q, w.H_kv, w.d,
-                                                    kvc.window_span(max_len, win, args.ring, win if args.ring else 0),
-                                                    args.split_tokens, pool_tokens=pool_tokens),
+                   "window": win, "ring": bool(args.ring), "new_tokens": w.new_tokens,
+                   "split_tokens": (kvc.multi_split_tokens(x.q.dtype, w.B, w.new_tokens, w.H_q, w.H_kv, w.d, max_len,
+                                                           win, args.split_tokens, pool_tokens=pool_tokens)
+                                    if multi else
+                                    kvc.split_tokens(torch.uint8 if u8 else x.q.dtype, w.B, w.H_q, w.H_kv, w.d,
+                                                     kvc.window_span(max_len, win, args.ring, win if args.ring else 0),
+                                                     args.split_tokens, pool_tokens=pool_tokens)),
                    "split_choice": "explicit" if args.split_tokens else "library"},
         "us_per_step": round(step_ms * 1e3, 2),
         "decode_us": round(dec_avg_ms * 1e3, 2),
@@ -388,6 +434,8 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": ("decode_u8_kernel (streaming pass over the codes; the append and the split merge "
                                 "are separate small kernels)") if u8 else
+                               ("decode_mfma_kernel, multi-token rows (one pass over the cache for all new tokens' "
+                                "queries; the append and the split merge are separate small kernels)") if multi else
                                "decode_mfma_kernel (streaming pass with the fused append; the split merge is a separate small kernel)",
                      "bytes_per_launch": kv_bytes},
         "wall_s_timed": round(wall, 4),
@@ -401,7 +449,7 @@ def main():
                            "kernel_frac_of_ceiling": round(achieved / ceil_nt, 4)}
     if not args.no_cpu_baseline and not w.paged:
         res["cpu_baseline"] = cpu_baseline_u8(x, qc, args.cpu_sample_seqs) if u8 else \
-            cpu_baseline(x, args.cpu_sample_seqs, win)
+            cpu_baseline_multi(x, args.cpu_sample_seqs, win) if multi else cpu_baseline(x, args.cpu_sample_seqs, win)
     print(json.dumps(res), flush=True)
 
 
