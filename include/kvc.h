@@ -33,6 +33,10 @@
  *    Decoding" (tveniu.com), sections 6 and 7 (the *_multi entry points):
  *    several new tokens per sequence in one pass - the target model checking
  *    gamma drafted tokens, or a prompt chunk - each attending causally.
+ *  - "KV Cache 최적화 심층 분석" (youngju.dev), MultiHeadLatentAttention listing
+ *    (the *_mla entry points): a latent cache of one [c_kv | k_rope] row per
+ *    token, keys and values recovered per head by the up-projections W_uk,
+ *    W_uv.
  *
  * Conventions for every entry point:
  *  - All tensors are dense, row-major, in DEVICE memory, owned by the caller.
@@ -58,7 +62,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 6
+#define KVC_ABI_VERSION 7
 
 typedef enum kvc_status {
     KVC_OK = 0,
@@ -417,6 +421,81 @@ kvc_status kvc_decode_attn_paged_u8(int B, int H_q, int H_kv, int d, const void*
                                     int block_size, const int32_t* block_table, int max_blocks_per_seq,
                                     const int32_t* seq_lens, int max_seq_len, float scale, void* out,
                                     int split_tokens, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Latent cache (multi-head latent attention), following the
+ * MultiHeadLatentAttention listing of "KV Cache 최적화 심층 분석: GQA·MLA·MHA
+ * 어텐션 메커니즘과 메모리 효율화 전략" (youngju.dev).  Each token is cached as
+ * one row of d_latent + rope_dim values, [c_kv | k_rope]; the cache is
+ * [B, T_max, d_latent + rope_dim] (one layer; the listing's (c_kv, k_rope)
+ * pair packed along the last axis).  Head h's key and value of token t are
+ * the up-projections of its latent:
+ *     k_h,t = W_uk[h*d_k : (h+1)*d_k, :] c_t + b_uk[h*d_k : (h+1)*d_k]
+ *     v_h,t = W_uv[h*d_k : (h+1)*d_k, :] c_t + b_uv[h*d_k : (h+1)*d_k]
+ * (W [n_heads * d_k, d_latent] and b [n_heads * d_k], nn.Linear's layout),
+ * and out_h = softmax(q_h . k_h,t * scale) v_h over the attended tokens.  As
+ * in the listing, k_rope is stored but not attended.  bf16 only.
+ *
+ * The library computes this in the absorbed form, an exact rewrite:
+ *     scores  q~_h . c_t * scale with q~_h = W_uk,h^T q_h (the key bias adds
+ *             q_h . b_uk,h to every score of head h, which the softmax removes,
+ *             so it is not an argument);
+ *     out_h = W_uv,h (sum_t p_t c_t) + b_uv,h      (the weights p_t sum to 1),
+ * so the cache is read once, as d_latent values per token, for all heads.
+ */
+
+/*
+ * kvc_append_mla - store the new token's row [c_kv_new[b] | k_rope_new[b]]
+ * (bit copies, nothing rotated: the listing rotates neither) at slot
+ * positions[b] of sequence b.  c_kv_new [B, d_latent], k_rope_new
+ * [B, rope_dim] (NULL when rope_dim == 0), dtype KVC_BF16 or KVC_F32 (of
+ * every buffer).  d_latent + rope_dim must be a multiple of 8 (16-byte rows
+ * in bf16).  A position outside [0, T_max) writes nothing.
+ */
+kvc_status kvc_append_mla(kvc_dtype dtype, int B, int d_latent, int rope_dim, void* cache, int T_max,
+                          const int32_t* positions, const void* c_kv_new, const void* k_rope_new, void* stream);
+
+/*
+ * Workspace bytes (256-byte aligned, no initialisation needed) and split
+ * length of kvc_decode_attn_mla with these sizes (max_seq_len bounds the
+ * attended lengths; split_tokens 0 = the library's choice, else a multiple of
+ * 32).  (size_t)-1 / -1 for invalid or unsupported sizes.  The workspace holds
+ * the absorbed queries and the latent context, [B, H, d_latent] float32 each,
+ * and the split partials.
+ */
+size_t kvc_decode_mla_workspace_bytes(int B, int H, int d_latent, int max_seq_len, int split_tokens);
+int kvc_decode_mla_split_tokens(int B, int H, int d_latent, int max_seq_len, int split_tokens);
+
+/*
+ * kvc_decode_attn_mla - attention of one new query per sequence over the
+ * first seq_lens[b] tokens of its latent cache.
+ *   q      bf16 [B, H, d_k]          query heads (d_k a multiple of 32, <= 512)
+ *   cache  bf16 [B, T_max, d_latent + rope_dim], d_latent 128, 256 or 512
+ *   w_uk, w_uv  bf16 [H * d_k, d_latent];  b_uv bf16 [H * d_k] or NULL (zero)
+ *   scale  <= 0: 1 / sqrt(d_k)
+ *   out    float32 [B, H, d_k]  (float32: the result of the value
+ *          up-projection, before any rounding to a storage type)
+ * seq_lens[b] in [0, max_seq_len], max_seq_len <= T_max; a sequence of length
+ * 0 gives zeros.  Four launches: absorbed queries, the streaming pass over the
+ * cache (one workgroup per sequence, 32-head chunk and token split), the merge
+ * of the splits, the value up-projection.
+ */
+kvc_status kvc_decode_attn_mla(int B, int H, int d_k, int d_latent, int rope_dim, const void* q,
+                               const void* cache, int T_max, const int32_t* seq_lens, int max_seq_len,
+                               const void* w_uk, const void* w_uv, const void* b_uv, float scale, float* out,
+                               int split_tokens, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kvc_decode_step_mla - kvc_append_mla then kvc_decode_attn_mla in one call:
+ * the new row is stored at slot positions[b] and sequence b attends
+ * positions[b] + 1 tokens (0 when the position is outside [0, T_max)).
+ * max_seq_len bounds positions[b] + 1.  The append rides in the first launch.
+ */
+kvc_status kvc_decode_step_mla(int B, int H, int d_k, int d_latent, int rope_dim, const void* q, void* cache,
+                               int T_max, const int32_t* positions, const void* c_kv_new,
+                               const void* k_rope_new, int max_seq_len, const void* w_uk, const void* w_uv,
+                               const void* b_uv, float scale, float* out, int split_tokens, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -24,9 +24,17 @@ and, for a uint8 quantized cache (codes plus a (step, zero point) pair per vecto
     append_u8(k_codes, k_sz, v_codes, v_sz, positions, k_new, v_new, rope_cos, rope_sin, ...)
     decode_attn_u8(q, k_codes, k_sz, v_codes, v_sz, seq_lens, max_seq_len)
     decode_attn_paged_u8(q, k_codes, k_sz, v_codes, v_sz, block_table, seq_lens, max_seq_len)
+
+and for a latent cache (multi-head latent attention, one [c_kv | k_rope] row per token):
+
+    append_mla(cache, positions, c_kv_new, k_rope_new)
+    decode_attn_mla(q, cache, seq_lens, max_seq_len, w_uk, w_uv, b_uv)
+    decode_step_mla(q, cache, positions, c_kv_new, k_rope_new, max_seq_len, w_uk, w_uv, b_uv)
 """
 from .api import (KVC_BF16, KVC_F32, KVC_U8, KvcError, append, append_multi, append_ring, append_u8,  # noqa: F401
                   decode_attn, decode_attn_multi, decode_attn_paged, decode_attn_paged_u8, decode_attn_u8,
                   decode_attn_window, decode_step, decode_step_window, multi_split_tokens, multi_workspace_bytes,
                   profile_next_decode, split_tokens, window_span, workspace_bytes)
+from .api import (append_mla, decode_attn_mla, decode_step_mla, mla_split_tokens,  # noqa: F401
+                  mla_workspace_bytes)
 from ._lib import LIB_PATH, load  # noqa: F401

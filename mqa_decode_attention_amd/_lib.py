@@ -86,9 +86,21 @@ SIGNATURES = {
                                          c_int, c_void_p, c_int,
                                          c_void_p, c_int, c_float, c_void_p,
                                          c_int, c_void_p, c_size_t, c_void_p]),
+    "kvc_append_mla": (c_int, [c_int, c_int, c_int, c_int, c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "kvc_decode_mla_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int]),
+    "kvc_decode_mla_split_tokens": (c_int, [c_int, c_int, c_int, c_int, c_int]),
+    "kvc_decode_attn_mla": (c_int, [c_int, c_int, c_int, c_int, c_int, c_void_p,
+                                    c_void_p, c_int, c_void_p, c_int,
+                                    c_void_p, c_void_p, c_void_p, c_float, c_void_p,
+                                    c_int, c_void_p, c_size_t, c_void_p]),
+    "kvc_decode_step_mla": (c_int, [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p,
+                                    c_int, c_void_p, c_void_p,
+                                    c_void_p, c_int, c_void_p, c_void_p,
+                                    c_void_p, c_float, c_void_p, c_int, c_void_p,
+                                    c_size_t, c_void_p]),
 }
 
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 _lib = None
 

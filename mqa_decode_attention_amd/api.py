@@ -531,3 +531,99 @@ def decode_attn_paged_u8(q: torch.Tensor, k_codes: torch.Tensor, k_sz: torch.Ten
         float(scale) if scale else 0.0, _dev(out, "out", torch.bfloat16, (B, H_q, d)),
         int(split_tokens), ws, wsn, st))
     return out
+
+
+# ---------------------------------------------------------------------------
+# Latent cache (multi-head latent attention): cache [B, T_max, d_latent + rope_dim]
+# ---------------------------------------------------------------------------
+
+def append_mla(cache: torch.Tensor, positions: torch.Tensor, c_kv_new: torch.Tensor,
+               k_rope_new: Optional[torch.Tensor] = None, stream=None) -> None:
+    """kvc_append_mla: store [c_kv_new[b] | k_rope_new[b]] at slot positions[b] of each sequence."""
+    lib = _lib.load()
+    dt = _dtype_code(cache)
+    B, T_max, row = cache.shape
+    d_latent = c_kv_new.shape[-1]
+    rope_dim = row - d_latent
+    st = _stream(cache.device, stream)
+    _check(lib.kvc_append_mla(
+        dt, B, d_latent, rope_dim, _dev(cache, "cache", cache.dtype), T_max,
+        _dev(positions, "positions", torch.int32, (B,)),
+        _dev(c_kv_new, "c_kv_new", cache.dtype, (B, d_latent)),
+        _dev(k_rope_new, "k_rope_new", cache.dtype, (B, rope_dim)) if rope_dim > 0 else None, st))
+
+
+def mla_workspace_bytes(B: int, H: int, d_latent: int, max_seq_len: int, split_tokens: int = 0) -> int:
+    """kvc_decode_mla_workspace_bytes."""
+    lib = _lib.load()
+    n = lib.kvc_decode_mla_workspace_bytes(B, H, d_latent, max_seq_len, split_tokens)
+    if n == (1 << 64) - 1:
+        raise KvcError(2, lib.kvc_last_error().decode() or "invalid sizes for the latent-cache workspace")
+    return int(n)
+
+
+def mla_split_tokens(B: int, H: int, d_latent: int, max_seq_len: int, split_tokens: int = 0) -> int:
+    """kvc_decode_mla_split_tokens: tokens per split the latent-cache decode uses."""
+    lib = _lib.load()
+    n = lib.kvc_decode_mla_split_tokens(B, H, d_latent, max_seq_len, split_tokens)
+    if n < 0:
+        raise KvcError(2, lib.kvc_last_error().decode() or "invalid sizes for the latent-cache decode")
+    return int(n)
+
+
+def _mla_args(q, cache, w_uk, w_uv, b_uv, out):
+    B, H, d_k = q.shape
+    _, T_max, row = cache.shape
+    d_latent = w_uk.shape[1]
+    if out is None:
+        out = torch.empty((B, H, d_k), dtype=torch.float32, device=q.device)
+    ptrs = (_dev(w_uk, "w_uk", torch.bfloat16, (H * d_k, d_latent)),
+            _dev(w_uv, "w_uv", torch.bfloat16, (H * d_k, d_latent)),
+            _dev(b_uv, "b_uv", torch.bfloat16, (H * d_k,)) if b_uv is not None else None)
+    return B, H, d_k, d_latent, row - d_latent, T_max, out, ptrs
+
+
+def decode_attn_mla(q: torch.Tensor, cache: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                    w_uk: torch.Tensor, w_uv: torch.Tensor, b_uv: Optional[torch.Tensor] = None,
+                    out: Optional[torch.Tensor] = None, scale: Optional[float] = None, split_tokens: int = 0,
+                    workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """kvc_decode_attn_mla: q bf16 [B, H, d_k] over a latent cache [B, T_max, d_latent + rope_dim];
+    returns out float32 [B, H, d_k]."""
+    lib = _lib.load()
+    B, H, d_k, d_latent, rope_dim, T_max, out, (wk, wv, bv) = _mla_args(q, cache, w_uk, w_uv, b_uv, out)
+    st = _stream(q.device, stream)
+    need = mla_workspace_bytes(B, H, d_latent, max_seq_len, split_tokens)
+    if workspace is not None:
+        ws, wsn = _dev(workspace, "workspace", torch.uint8), workspace.numel()
+    else:
+        ws, wsn = _workspace(q.device, st, need)
+    _check(lib.kvc_decode_attn_mla(
+        B, H, d_k, d_latent, rope_dim, _dev(q, "q", torch.bfloat16), _dev(cache, "cache", torch.bfloat16), T_max,
+        _dev(seq_lens, "seq_lens", torch.int32, (B,)), int(max_seq_len), wk, wv, bv,
+        float(scale) if scale else 0.0, _dev(out, "out", torch.float32, (B, H, d_k)), int(split_tokens),
+        ws, wsn, st))
+    return out
+
+
+def decode_step_mla(q: torch.Tensor, cache: torch.Tensor, positions: torch.Tensor, c_kv_new: torch.Tensor,
+                    k_rope_new: Optional[torch.Tensor], max_seq_len: int, w_uk: torch.Tensor, w_uv: torch.Tensor,
+                    b_uv: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                    scale: Optional[float] = None, split_tokens: int = 0,
+                    workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """kvc_decode_step_mla: append the new rows, then attend positions[b] + 1 tokens."""
+    lib = _lib.load()
+    B, H, d_k, d_latent, rope_dim, T_max, out, (wk, wv, bv) = _mla_args(q, cache, w_uk, w_uv, b_uv, out)
+    st = _stream(q.device, stream)
+    need = mla_workspace_bytes(B, H, d_latent, max_seq_len, split_tokens)
+    if workspace is not None:
+        ws, wsn = _dev(workspace, "workspace", torch.uint8), workspace.numel()
+    else:
+        ws, wsn = _workspace(q.device, st, need)
+    _check(lib.kvc_decode_step_mla(
+        B, H, d_k, d_latent, rope_dim, _dev(q, "q", torch.bfloat16), _dev(cache, "cache", torch.bfloat16), T_max,
+        _dev(positions, "positions", torch.int32, (B,)),
+        _dev(c_kv_new, "c_kv_new", torch.bfloat16, (B, d_latent)),
+        _dev(k_rope_new, "k_rope_new", torch.bfloat16, (B, rope_dim)) if rope_dim > 0 else None,
+        int(max_seq_len), wk, wv, bv, float(scale) if scale else 0.0,
+        _dev(out, "out", torch.float32, (B, H, d_k)), int(split_tokens), ws, wsn, st))
+    return out

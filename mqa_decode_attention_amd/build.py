@@ -33,6 +33,7 @@ UNITS = {
     "kvc_decode.hip": [],
     "kvc_decode_mfma.hip": [],
     "kvc_decode_u8.hip": [],
+    "kvc_mla.hip": [],
     "kvc_probe.hip": [],
 }
 

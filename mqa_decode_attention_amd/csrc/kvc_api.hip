@@ -182,6 +182,47 @@ bool plan_decode(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_l
     return true;
 }
 
+bool plan_mla(int B, int H, int d_latent, int max_seq_len, int split_tokens, MlaPlan* plan, const char** why) {
+    MlaPlan pl{};
+    pl.n_chunks = (H + kMlaHeads - 1) / kMlaHeads;
+    const long long units = static_cast<long long>(B) * pl.n_chunks;
+    const int L = std::max(max_seq_len, 1);
+    long long ts;
+    if (split_tokens > 0) {
+        if (split_tokens % kMlaTile != 0) {
+            *why = "split_tokens must be a multiple of 32 for the latent-cache kernel";
+            return false;
+        }
+        ts = split_tokens;
+    } else {
+        // One workgroup per compute unit (its LDS holds two 32-token stages
+        // of d_latent-wide rows).  Each split writes H * d_latent float32
+        // partials - a 32-head chunk at d_latent 512 writes 64 KiB, an eighth
+        // of what a 256-token split reads - so splits stay at least 256
+        // tokens long.
+        const long long slots = cu_count();
+        const long long S = std::max(1LL, slots / std::max(1LL, units));
+        ts = (L + S - 1) / S;
+        ts = std::max<long long>(ts, 256);
+        ts = (ts + kMlaTile - 1) / kMlaTile * kMlaTile;
+    }
+    while ((L + ts - 1) / ts > kMaxSplits) ts += kMlaTile;
+    if (ts > 0x7FFFFFFF) {
+        *why = "split too long";
+        return false;
+    }
+    pl.split_tokens = static_cast<int>(ts);
+    pl.n_splits = static_cast<int>((L + ts - 1) / ts);
+    const size_t rows = static_cast<size_t>(B) * H;
+    pl.qt = 0;
+    pl.ctx = align_up(rows * d_latent * sizeof(float), 256);
+    pl.ws_ml = pl.ctx + align_up(rows * d_latent * sizeof(float), 256);
+    pl.ws_part = pl.ws_ml + align_up(rows * pl.n_splits * sizeof(float2), 256);
+    pl.ws_bytes = pl.ws_part + (pl.n_splits > 1 ? align_up(rows * pl.n_splits * d_latent * sizeof(float), 256) : 0);
+    *plan = pl;
+    return true;
+}
+
 }  // namespace kvc
 
 extern "C" {
@@ -683,6 +724,147 @@ kvc_status kvc_decode_attn_paged_u8(int B, int H_q, int H_kv, int d, const void*
     return decode_common(KVC_U8, B, H_q, H_kv, d, q, k_codes, v_codes, 0, num_blocks, block_size, block_table,
                          max_blocks_per_seq, seq_lens, max_seq_len, scale, out, split_tokens, workspace,
                          workspace_bytes, stream, nullptr, k_sz, v_sz);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Latent cache (multi-head latent attention)
+// ---------------------------------------------------------------------------
+
+namespace {
+
+kvc_status check_mla_sizes(int B, int H, int d_latent, int rope_dim, int max_seq_len, int split_tokens) {
+    if (B < 0 || H <= 0 || rope_dim < 0 || max_seq_len < 0 || split_tokens < 0)
+        return fail(KVC_ERR_SHAPE, "latent cache: invalid sizes (B=%d H=%d rope_dim=%d max_seq_len=%d)", B, H,
+                    rope_dim, max_seq_len);
+    if (d_latent != 128 && d_latent != 256 && d_latent != 512)
+        return fail(KVC_ERR_UNSUPPORTED, "latent cache: d_latent %d must be 128, 256 or 512", d_latent);
+    if ((d_latent + rope_dim) % 8 != 0)
+        return fail(KVC_ERR_SHAPE, "latent cache: d_latent + rope_dim = %d must be a multiple of 8",
+                    d_latent + rope_dim);
+    return KVC_OK;
+}
+
+kvc_status mla_common(int B, int H, int d_k, int d_latent, int rope_dim, const void* q, void* cache, int T_max,
+                      const int32_t* seq_lens, const int32_t* positions, const void* c_new, const void* r_new,
+                      int max_seq_len, const void* w_uk, const void* w_uv, const void* b_uv, float scale,
+                      float* out, int split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+    const hipEvent_t ev0 = g_prof_start, ev1 = g_prof_stop;   // one-shot, cleared by every call
+    g_prof_start = g_prof_stop = nullptr;
+    kvc_status st = check_mla_sizes(B, H, d_latent, rope_dim, max_seq_len, split_tokens);
+    if (st != KVC_OK) return st;
+    if (d_k <= 0 || d_k % 32 != 0 || d_k > 512)
+        return fail(KVC_ERR_UNSUPPORTED, "latent cache: d_k %d must be a positive multiple of 32, at most 512", d_k);
+    if (T_max <= 0) return fail(KVC_ERR_SHAPE, "T_max must be positive");
+    if (max_seq_len > T_max)
+        return fail(KVC_ERR_SHAPE, "max_seq_len %d exceeds the cache capacity T_max %d", max_seq_len, T_max);
+    const int row = d_latent + rope_dim;
+    if (static_cast<long long>(T_max) * row * 2 + 2LL * kvc::kMlaTile * row * 2 >= 0x7FFFFFFFLL)
+        return fail(KVC_ERR_SHAPE, "latent cache: one sequence's rows exceed 2 GiB");
+    if (B == 0) return ok();
+    if (!q || !cache || !w_uk || !w_uv || !out || (!positions && !seq_lens))
+        return fail(KVC_ERR_NULL, "latent-cache decode: a required pointer is NULL");
+    if (positions && (!c_new || (rope_dim > 0 && !r_new)))
+        return fail(KVC_ERR_NULL, "kvc_decode_step_mla: c_kv_new or k_rope_new is NULL");
+    kvc::MlaPlan pl;
+    const char* why = nullptr;
+    if (!kvc::plan_mla(B, H, d_latent, max_seq_len, split_tokens, &pl, &why))
+        return fail(KVC_ERR_UNSUPPORTED, "%s", why);
+    if (!workspace) return fail(KVC_ERR_WORKSPACE, "latent-cache decode needs %zu bytes of workspace, got NULL",
+                                pl.ws_bytes);
+    if (workspace_bytes < pl.ws_bytes)
+        return fail(KVC_ERR_WORKSPACE, "latent-cache decode needs %zu bytes of workspace, got %zu", pl.ws_bytes,
+                    workspace_bytes);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+        return fail(KVC_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    const long long n_wg = static_cast<long long>(B) * pl.n_chunks * pl.n_splits;
+    if (n_wg > 0x7FFFFFF0LL) return fail(KVC_ERR_SHAPE, "too many workgroups");
+    kvc::MlaParams p{};
+    p.q = q; p.cache = cache; p.seq_lens = seq_lens; p.positions = positions;
+    p.c_new = positions ? c_new : nullptr;
+    p.r_new = r_new;
+    p.w_uk = w_uk; p.w_uv = w_uv; p.b_uv = b_uv; p.out = out;
+    char* ws = static_cast<char*>(workspace);
+    p.qt = reinterpret_cast<float*>(ws + pl.qt);
+    p.ctx = reinterpret_cast<float*>(ws + pl.ctx);
+    p.ws_ml = reinterpret_cast<float2*>(ws + pl.ws_ml);
+    p.ws_part = pl.n_splits > 1 ? reinterpret_cast<float*>(ws + pl.ws_part) : nullptr;
+    p.B = B; p.H = H; p.d_k = d_k; p.d_latent = d_latent; p.rope_dim = rope_dim; p.row = row;
+    p.T_max = T_max; p.max_seq_len = max_seq_len;
+    p.split_tokens = pl.split_tokens; p.n_splits = pl.n_splits; p.n_chunks = pl.n_chunks;
+    p.n_wg = static_cast<int>(n_wg);
+    const float sc = scale > 0.0f ? scale : 1.0f / sqrtf(static_cast<float>(d_k));
+    p.scale_log2 = sc * 1.4426950408889634f;
+    kvc::KernelTiming tm;
+    tm.start = ev0;
+    tm.stop = ev1;
+    return hip_status(kvc::launch_mla(p, static_cast<hipStream_t>(stream), tm), "latent-cache decode launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+kvc_status kvc_append_mla(kvc_dtype dtype, int B, int d_latent, int rope_dim, void* cache, int T_max,
+                          const int32_t* positions, const void* c_kv_new, const void* k_rope_new, void* stream) {
+    if (dtype != KVC_BF16 && dtype != KVC_F32) return fail(KVC_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+    if (B < 0 || d_latent <= 0 || rope_dim < 0 || T_max <= 0)
+        return fail(KVC_ERR_SHAPE, "kvc_append_mla: invalid sizes (B=%d d_latent=%d rope_dim=%d T_max=%d)", B,
+                    d_latent, rope_dim, T_max);
+    if ((d_latent + rope_dim) % 8 != 0)
+        return fail(KVC_ERR_SHAPE, "kvc_append_mla: d_latent + rope_dim = %d must be a multiple of 8",
+                    d_latent + rope_dim);
+    if (B == 0) return ok();
+    if (!cache || !positions || !c_kv_new || (rope_dim > 0 && !k_rope_new))
+        return fail(KVC_ERR_NULL, "kvc_append_mla: a required pointer is NULL");
+    return hip_status(kvc::launch_append_mla(static_cast<int>(elem_bytes(dtype)), B, d_latent, rope_dim, cache,
+                                             T_max, positions, c_kv_new, k_rope_new,
+                                             static_cast<hipStream_t>(stream)),
+                      "kvc_append_mla launch");
+}
+
+size_t kvc_decode_mla_workspace_bytes(int B, int H, int d_latent, int max_seq_len, int split_tokens) {
+    if (check_mla_sizes(B, H, d_latent, 0, max_seq_len, split_tokens) != KVC_OK) return static_cast<size_t>(-1);
+    kvc::MlaPlan pl;
+    const char* why = nullptr;
+    if (!kvc::plan_mla(B, H, d_latent, max_seq_len, split_tokens, &pl, &why)) {
+        fail(KVC_ERR_UNSUPPORTED, "%s", why);
+        return static_cast<size_t>(-1);
+    }
+    ok();
+    return pl.ws_bytes;
+}
+
+int kvc_decode_mla_split_tokens(int B, int H, int d_latent, int max_seq_len, int split_tokens) {
+    if (check_mla_sizes(B, H, d_latent, 0, max_seq_len, split_tokens) != KVC_OK) return -1;
+    kvc::MlaPlan pl;
+    const char* why = nullptr;
+    if (!kvc::plan_mla(B, H, d_latent, max_seq_len, split_tokens, &pl, &why)) {
+        fail(KVC_ERR_UNSUPPORTED, "%s", why);
+        return -1;
+    }
+    return pl.split_tokens;
+}
+
+kvc_status kvc_decode_attn_mla(int B, int H, int d_k, int d_latent, int rope_dim, const void* q,
+                               const void* cache, int T_max, const int32_t* seq_lens, int max_seq_len,
+                               const void* w_uk, const void* w_uv, const void* b_uv, float scale, float* out,
+                               int split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+    if (B > 0 && !seq_lens) return fail(KVC_ERR_NULL, "kvc_decode_attn_mla: seq_lens is NULL");
+    return mla_common(B, H, d_k, d_latent, rope_dim, q, const_cast<void*>(cache), T_max, seq_lens, nullptr,
+                      nullptr, nullptr, max_seq_len, w_uk, w_uv, b_uv, scale, out, split_tokens, workspace,
+                      workspace_bytes, stream);
+}
+
+kvc_status kvc_decode_step_mla(int B, int H, int d_k, int d_latent, int rope_dim, const void* q, void* cache,
+                               int T_max, const int32_t* positions, const void* c_kv_new,
+                               const void* k_rope_new, int max_seq_len, const void* w_uk, const void* w_uv,
+                               const void* b_uv, float scale, float* out, int split_tokens, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    if (B > 0 && !positions) return fail(KVC_ERR_NULL, "kvc_decode_step_mla: positions is NULL");
+    return mla_common(B, H, d_k, d_latent, rope_dim, q, cache, T_max, nullptr, positions, c_kv_new, k_rope_new,
+                      max_seq_len, w_uk, w_uv, b_uv, scale, out, split_tokens, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

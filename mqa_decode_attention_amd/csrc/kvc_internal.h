@@ -203,6 +203,50 @@ hipError_t launch_decode_u8(int d, int G, bool paged, const DecodeParams& p, con
 // The log-sum-exp merge of the splits (only when n_splits > 1).
 hipError_t launch_decode_merge(kvc_dtype dtype, int d, const DecodeParams& p, hipStream_t stream);
 
+// ---------------------------------------------------------------------------
+// Latent cache (multi-head latent attention), absorbed form.
+// ---------------------------------------------------------------------------
+
+struct MlaParams {
+    const void* q;               // bf16 [B, H, d_k]
+    void* cache;                 // bf16 [B, T_max, row], row = d_latent + rope_dim
+    const int32_t* seq_lens;     // [B] attended lengths, or NULL when positions is set
+    const int32_t* positions;    // step: the new row goes to slot positions[b], L = positions[b] + 1
+    const void* c_new;           // step: [B, d_latent] new latent (NULL: no append)
+    const void* r_new;           // step: [B, rope_dim] new rope part (NULL when rope_dim == 0)
+    const void* w_uk;            // bf16 [H * d_k, d_latent]
+    const void* w_uv;            // bf16 [H * d_k, d_latent]
+    const void* b_uv;            // bf16 [H * d_k] or NULL
+    float* out;                  // [B, H, d_k]
+    float* qt;                   // [B, H, d_latent] absorbed queries (workspace)
+    float* ctx;                  // [B, H, d_latent] softmax-weighted latents (workspace)
+    float2* ws_ml;               // [B * H, n_splits] (running max (log2), sum)
+    float* ws_part;              // [B * H, n_splits, d_latent]
+    int B, H, d_k, d_latent, rope_dim, row, T_max, max_seq_len;
+    int split_tokens, n_splits, n_chunks, n_wg;
+    float scale_log2;
+};
+
+struct MlaPlan {
+    int split_tokens, n_splits, n_chunks;
+    size_t qt, ctx, ws_ml, ws_part, ws_bytes;   // byte offsets / total
+};
+
+// Tokens of one tile of the latent-cache kernel (split lengths are multiples).
+constexpr int kMlaTile = 32;
+// Query heads one workgroup of that kernel serves (larger H: several chunks).
+constexpr int kMlaHeads = 32;
+
+bool plan_mla(int B, int H, int d_latent, int max_seq_len, int split_tokens, MlaPlan* plan, const char** why);
+
+// Bit copy of the new rows [c_kv | k_rope] into a latent cache (elem_bytes 2 or 4).
+hipError_t launch_append_mla(int elem_bytes, int B, int d_latent, int rope_dim, void* cache, int T_max,
+                             const int32_t* positions, const void* c_new, const void* r_new, hipStream_t stream);
+
+// The four launches of a latent-cache decode (the append rides in the first
+// when p.c_new is set); tm times the streaming kernel.
+hipError_t launch_mla(const MlaParams& p, hipStream_t stream, const KernelTiming& tm);
+
 // Streaming-read probe (kvc_hbm_read_probe).
 hipError_t launch_read_probe(const void* buf, size_t bytes, unsigned* sink, int workgroups,
                              bool nontemporal, hipStream_t stream);

@@ -38,7 +38,8 @@ import numpy as np
 
 from . import kvc_oracle as O
 
-__all__ = ["append_mla", "up_project", "decode_attention_mla", "mla_cache_bytes_per_token"]
+__all__ = ["append_mla", "up_project", "decode_attention_mla", "decode_attention_mla_heads",
+           "mla_cache_bytes_per_token"]
 
 
 def append_mla(cache, cached, c_kv_new, k_rope_new):
@@ -80,6 +81,27 @@ def decode_attention_mla(q, cache, seq_lens, W_uk, b_uk, W_uv, b_uv, d_latent: i
         V = up_project(c, Wv, bv, H, d_k)
         for h in range(H):
             out[b, h], _ = O._head_attention(qf[b, h], K[h], V[h], sc)
+    return out
+
+
+def decode_attention_mla_heads(q, cache, seq_lens, W_uk, b_uk, W_uv, b_uv, d_latent: int, dtype, pairs,
+                               scale: Optional[float] = None):
+    """Float64 [len(pairs), d_k]: decode_attention_mla's output at the listed
+    (b, h) pairs only.  Head h's keys and values come from its own d_k rows
+    of W_uk and W_uv (the rows the listing's view(S, n_heads, d_k) gives it),
+    so a long cache is up-projected for the sampled heads alone."""
+    d_k = q.shape[2]
+    sc = (1.0 / math.sqrt(d_k)) if scale is None else float(scale)
+    out = np.zeros((len(pairs), d_k))
+    cached = {}
+    for n, (b, h) in enumerate(pairs):
+        L = int(seq_lens[b])
+        if b not in cached:
+            cached[b] = O.to_f64(cache[b, 0:L, 0:d_latent], dtype)
+        rows = slice(h * d_k, (h + 1) * d_k)
+        K = up_project(cached[b], O.to_f64(W_uk[rows], dtype), O.to_f64(b_uk[rows], dtype), 1, d_k)[0]
+        V = up_project(cached[b], O.to_f64(W_uv[rows], dtype), O.to_f64(b_uv[rows], dtype), 1, d_k)[0]
+        out[n], _ = O._head_attention(O.to_f64(q[b, h], dtype), K, V, sc)
     return out
 
 

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kvc_abi_version() == _lib.ABI_VERSION == 6
+    assert lib.kvc_abi_version() == _lib.ABI_VERSION == 7
     for s in range(6):
         assert lib.kvc_status_string(s)
     assert lib.kvc_status_string(99) == b"unknown status"
@@ -263,3 +263,56 @@ def test_quantized_cache_split_choice(lib):
     assert st(U8, 32, 32, 8, 128, 16385, 17408 * 16, 0) == 1152      # ragged pool: ~4 rounds
     assert st(U8, 16, 32, 8, 256, 8193, 0, 0) == -1                  # no quantized kernel at d = 256
     assert lib.kvc_decode_workspace_bytes(U8, 16, 32, 8, 128, 8193, 0, 0) > 0
+
+
+def _mla(lib, **kw):
+    a = dict(B=2, H=32, dk=128, dl=512, rd=64, q=FAKE, cache=FAKE, T_max=64, lens=FAKE, max_len=64, wk=FAKE,
+             wv=FAKE, bv=None, scale=0.0, out=FAKE, split=0, ws=FAKE, wsn=1 << 30, stream=None)
+    a.update(kw)
+    return lib.kvc_decode_attn_mla(a["B"], a["H"], a["dk"], a["dl"], a["rd"], a["q"], a["cache"], a["T_max"],
+                                   a["lens"], a["max_len"], a["wk"], a["wv"], a["bv"], a["scale"], a["out"],
+                                   a["split"], a["ws"], a["wsn"], a["stream"])
+
+
+def test_latent_cache_host_checks(lib):
+    """The latent-cache entry points check sizes, pointers and the workspace on
+    the host (every call here fails before a launch)."""
+    assert _mla(lib, dl=384) == KVC_ERR_UNSUPPORTED                # no kernel for this latent width
+    assert b"d_latent" in lib.kvc_last_error()
+    assert _mla(lib, dk=48) == KVC_ERR_UNSUPPORTED                 # d_k not a multiple of 32
+    assert _mla(lib, rd=3) == KVC_ERR_SHAPE                        # rows not 16-byte multiples
+    assert _mla(lib, max_len=65) == KVC_ERR_SHAPE                  # beyond T_max
+    assert _mla(lib, split=40) == KVC_ERR_UNSUPPORTED              # split not a multiple of 32
+    assert _mla(lib, q=None) == KVC_ERR_NULL
+    assert _mla(lib, lens=None) == KVC_ERR_NULL
+    assert _mla(lib, ws=None) == KVC_ERR_WORKSPACE
+    assert _mla(lib, wsn=1024) == KVC_ERR_WORKSPACE
+    assert _mla(lib, ws=ctypes.c_void_p(0x1010)) == KVC_ERR_WORKSPACE   # not 256-byte aligned
+    assert _mla(lib, B=0) == KVC_OK                                # nothing to do
+    st = lib.kvc_decode_step_mla
+    assert st(2, 32, 128, 512, 64, FAKE, FAKE, 64, FAKE, None, FAKE, 64, FAKE, FAKE, None, 0.0, FAKE, 0, FAKE,
+              1 << 30, None) == KVC_ERR_NULL                        # no new latent rows
+    app = lib.kvc_append_mla
+    assert app(BF16, 2, 512, 60, FAKE, 64, FAKE, FAKE, FAKE, None) == KVC_ERR_SHAPE
+    assert app(BF16, 2, 512, 64, FAKE, 64, FAKE, FAKE, None, None) == KVC_ERR_NULL
+    assert app(U8, 2, 512, 64, FAKE, 64, FAKE, FAKE, FAKE, None) == KVC_ERR_UNSUPPORTED
+
+
+def test_latent_cache_plan(lib):
+    """Splits of the latent-cache decode: about one workgroup per compute unit
+    over the sequences and 32-head chunks, at least 256 tokens, whole 32-token
+    tiles; the workspace holds the absorbed queries, the latent context and
+    the partials."""
+    st, ws = lib.kvc_decode_mla_split_tokens, lib.kvc_decode_mla_workspace_bytes
+    assert st(16, 32, 512, 8193, 0) == 544                         # 16 sequences: 16 splits each
+    assert st(1, 32, 512, 131073, 0) == 544                        # 241 splits (513 -> whole tiles)
+    assert st(64, 32, 512, 4097, 0) == 1056                       # 4 splits (1025 -> whole tiles)
+    assert st(2, 64, 512, 300, 0) == 256                           # floor of 256 tokens
+    assert st(16, 32, 512, 8193, 96) == 96
+    rows = 16 * 32
+    splits = -(-8193 // 544)
+    n = ws(16, 32, 512, 8193, 0)
+    assert n >= 2 * rows * 512 * 4 + rows * splits * (512 + 2) * 4 and n % 256 == 0
+    one = ws(16, 32, 512, 200, 0)                                  # one split: no partials
+    assert one < 2 * rows * 512 * 4 + rows * 8 + 4096
+    assert ws(16, 32, 384, 8193, 0) == (1 << 64) - 1

@@ -143,7 +143,17 @@ def check_append(M) -> bool:
     return ok
 
 
-CHECKS = [check_brute_force, check_absorbed, check_closed_forms, check_rope_part_unread, check_append]
+def check_heads_subset(M) -> bool:
+    rng = np.random.default_rng(56)
+    cache, q, Wk, bk, Wv, bv = _case(rng, B=3, H=4, d_k=8, dl=16, rd=4, T=12, dtype="bf16")
+    L = [12, 5, 1]
+    full = M.decode_attention_mla(q, cache, L, Wk, bk, Wv, bv, 16, "bf16")
+    pairs = [(0, 3), (1, 0), (2, 2), (0, 1)]
+    sub = M.decode_attention_mla_heads(q, cache, L, Wk, bk, Wv, bv, 16, "bf16", pairs)
+    return all(np.array_equal(sub[n], full[b, h]) for n, (b, h) in enumerate(pairs))
+
+
+CHECKS = [check_heads_subset, check_brute_force, check_absorbed, check_closed_forms, check_rope_part_unread, check_append]
 
 
 @pytest.mark.parametrize("chk", CHECKS, ids=lambda c: c.__name__)

@@ -50,6 +50,17 @@ kept in [0, 255] - so each vector reads back as roughly N(0, 1) values.  From a
 second generator seeded with seed + 7919, in the order K pairs -> V pairs ->
 K codes -> V codes, so the unquantized draws stay unchanged.  Slots at or past
 a sequence's cached length hold code 0 and NaN pairs.
+
+Latent cache (``MLA_WORKLOADS``, ``draw_mla``): the cache layout of the
+MultiHeadLatentAttention listing in "KV Cache 최적화 심층 분석" (youngju.dev),
+one row [c_kv | k_rope] of d_latent + rope_dim values per token, [B, T_max,
+d_latent + rope_dim].  Values N(0, 1) as above (NaN at and past each cached
+length); q [B, n_heads, d_k] N(0, 1); the new token's c_kv [B, d_latent] and
+k_rope [B, rope_dim] N(0, 1); the up-projections W_uk, W_uv [n_heads * d_k,
+d_latent] and their biases [n_heads * d_k] drawn as torch's nn.Linear
+initialises them, uniform in +-1/sqrt(d_latent).  Draw order: cached lengths
+-> cache -> q -> c_kv -> k_rope -> W_uk -> b_uk -> W_uv -> b_uv.  There are no
+trained weights anywhere: these only give the products realistic scales.
 """
 from __future__ import annotations
 
@@ -60,7 +71,8 @@ from typing import Optional
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "DecodeInputs", "QuantCache", "draw", "draw_quantized", "rotation_table"]
+__all__ = ["Workload", "WORKLOADS", "DecodeInputs", "QuantCache", "draw", "draw_quantized", "rotation_table",
+           "MlaWorkload", "MLA_WORKLOADS", "MlaInputs", "draw_mla"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -280,3 +292,92 @@ def draw_quantized(x: DecodeInputs) -> QuantCache:
             for t in (k_sz, v_sz):
                 t[b, :, c:, :] = nan
     return QuantCache(k_codes, k_sz, v_codes, v_sz)
+
+
+@dataclasses.dataclass(frozen=True)
+class MlaWorkload:
+    """A decode step over a latent cache: n_heads query heads of width d_k,
+    each token cached as one row of d_latent + rope_dim values."""
+    name: str
+    seed: int
+    B: int
+    H: int                     # query heads (n_heads)
+    d_k: int                   # per-head width of q and of the output
+    d_latent: int
+    rope_dim: int
+    dtype: str                 # "bf16": storage dtype of the cache, q and weights
+    cached_lo: int
+    cached_hi: int
+    T_max: int = 0
+
+    @property
+    def row(self) -> int:
+        return self.d_latent + self.rope_dim
+
+    @property
+    def max_attended(self) -> int:
+        return self.cached_hi + 1
+
+    def replace(self, **kw) -> "MlaWorkload":
+        w = dataclasses.replace(self, **kw)
+        if w.T_max < w.cached_hi + 1:
+            w = dataclasses.replace(w, T_max=_round_up(w.cached_hi + 1, 8))
+        return w
+
+
+MLA_WORKLOADS = {
+    # the 8B-class layer of gqa_8b (32 heads of 128, batch 16, 8192 cached
+    # tokens) with a 512-wide latent and the listing's default rope_dim 64
+    "mla_latent": MlaWorkload("mla_latent", 6, B=16, H=32, d_k=128, d_latent=512, rope_dim=64, dtype="bf16",
+                              cached_lo=8192, cached_hi=8192, T_max=8200),
+}
+
+
+@dataclasses.dataclass
+class MlaInputs:
+    """One latent-cache decode step's inputs, on the CPU, in storage dtype.
+
+    cached   int32 [B]                tokens cached before the step (= append slot)
+    cache    [B, T_max, d_latent + rope_dim]
+    q        [B, H, d_k]
+    c_kv_new [B, d_latent], k_rope_new [B, rope_dim]
+    w_uk, w_uv [H * d_k, d_latent];  b_uk, b_uv [H * d_k]
+    """
+    workload: MlaWorkload
+    cached: torch.Tensor
+    cache: torch.Tensor
+    q: torch.Tensor
+    c_kv_new: torch.Tensor
+    k_rope_new: torch.Tensor
+    w_uk: torch.Tensor
+    b_uk: torch.Tensor
+    w_uv: torch.Tensor
+    b_uv: torch.Tensor
+
+    @property
+    def seq_lens(self) -> torch.Tensor:
+        return self.cached + 1
+
+
+def draw_mla(w: MlaWorkload) -> MlaInputs:
+    """Draw a latent-cache workload's inputs from its seed (deterministic, CPU only)."""
+    g = torch.Generator().manual_seed(w.seed)
+    if w.cached_lo == w.cached_hi:
+        cached = torch.full((w.B,), w.cached_lo, dtype=torch.int32)
+    else:
+        cached = torch.randint(w.cached_lo, w.cached_hi + 1, (w.B,), generator=g,
+                               dtype=torch.int64).to(torch.int32)
+    assert w.T_max >= w.cached_hi + 1, "the cache must hold the cached and the new token"
+    cache = torch.randn((w.B, w.T_max, w.row), generator=g, dtype=torch.float32)
+    q = torch.randn((w.B, w.H, w.d_k), generator=g, dtype=torch.float32)
+    c_kv = torch.randn((w.B, w.d_latent), generator=g, dtype=torch.float32)
+    k_rope = torch.randn((w.B, w.rope_dim), generator=g, dtype=torch.float32)
+    bound = 1.0 / math.sqrt(w.d_latent)
+    uni = lambda *shape: (torch.rand(shape, generator=g, dtype=torch.float32) * 2.0 - 1.0) * bound
+    w_uk, b_uk = uni(w.H * w.d_k, w.d_latent), uni(w.H * w.d_k)
+    w_uv, b_uv = uni(w.H * w.d_k, w.d_latent), uni(w.H * w.d_k)
+    cache = _storage(cache, w.dtype)
+    for b, c in enumerate(cached.tolist()):
+        cache[b, c:, :] = float("nan")
+    st = lambda t: _storage(t, w.dtype)
+    return MlaInputs(w, cached, cache, st(q), st(c_kv), st(k_rope), st(w_uk), st(b_uk), st(w_uv), st(b_uv))
