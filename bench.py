@@ -63,7 +63,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="gqa_8b")
+    ap.add_argument("--workload", default="gqa_8b",
+                    help="gqa_8b (default), mqa_ragged, long_gqa, paged_gqa, tiny_mha, spec_gqa, or the latent "
+                         "cache mla_latent")
     ap.add_argument("--split-tokens", type=int, default=0, help="0 = library heuristic")
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window of W tokens (kvc_decode_step_window over the full cache; 0 = none)")
@@ -223,6 +225,133 @@ def cpu_baseline_u8(x, qc, n_seqs):
                       f"one thread), {sec:.2f} s"}
 
 
+def latent_read_bytes(seq_lens, d_latent, elem_bytes):
+    """Bytes of the latent cache a step must read: sum_b L_b * d_latent * e (the
+    rope part of each row is stored but not attended)."""
+    return int(sum(int(L) for L in seq_lens)) * d_latent * elem_bytes
+
+
+def cpu_baseline_mla(x, n_seqs):
+    """Time the latent-cache oracle (as it stands, one thread: the listing's
+    per-head up-projection of every cached latent, then the attention) on the
+    first n_seqs sequences of the same step."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import oracle.kvc_mla_oracle as MO
+
+    w = x.workload
+    B = min(max(n_seqs, 1), w.B)
+
+    def np_store(t):
+        return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    cache = np_store(x.cache[:B])
+    n = {k: np_store(getattr(x, k)) for k in ("w_uk", "b_uk", "w_uv", "b_uv")}
+    q, ckv, kr = np_store(x.q[:B]), np_store(x.c_kv_new[:B]), np_store(x.k_rope_new[:B])
+    cached = x.cached.numpy()[:B]
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        c2 = MO.append_mla(cache, cached, ckv, kr)
+        MO.decode_attention_mla(q, c2, cached + 1, n["w_uk"], n["b_uk"], n["w_uv"], n["b_uv"], w.d_latent, w.dtype)
+        sec = time.perf_counter() - t0
+    nbytes = latent_read_bytes(cached + 1, w.d_latent, 2)
+    return {"value": round(nbytes / sec / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{B} of {w.B} sequences of {w.name} (append + per-head up-projection of the latents + "
+                      f"attention, float64, numpy, one thread), {sec:.2f} s"}
+
+
+def bench_mla(args, W) -> dict:
+    """One decode step over a latent cache: kvc_decode_step_mla (append + absorbed
+    queries, the streaming pass, the split merge, the value up-projection)."""
+    import torch
+
+    import mqa_decode_attention_amd as kvc
+
+    w = W.MLA_WORKLOADS[args.workload]
+    x = W.draw_mla(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    e = 2
+    kv_bytes = latent_read_bytes(x.seq_lens.tolist(), w.d_latent, e)
+    weight_bytes = 2 * w.H * w.d_k * w.d_latent * e
+    cache_bytes = x.cache.numel() * e
+    R = max(1, min(64, -(-MALL_DEFEAT_BYTES // cache_bytes)))
+    caches = [x.cache.to(dev) for _ in range(R)]
+    q, ckv, kr = x.q.to(dev), x.c_kv_new.to(dev), x.k_rope_new.to(dev)
+    wk, wv, bv = x.w_uk.to(dev), x.w_uv.to(dev), x.b_uv.to(dev)
+    pos = x.cached.to(dev)
+    max_len = int(x.seq_lens.max())
+    out = torch.empty((w.B, w.H, w.d_k), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        if ev is not None:
+            kvc.profile_next_decode(ev[0], ev[1])
+        kvc.decode_step_mla(q, caches[i % R], pos, ckv, kr, max_len, wk, wv, bv, out=out,
+                            split_tokens=args.split_tokens)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(args.steps):
+        step(i)
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = t_start.elapsed_time(t_end) / args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in evs:
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    dec_ms = [a.elapsed_time(b) for a, b in evs]
+    dec_avg_ms = sum(dec_ms) / len(dec_ms)
+    achieved = kv_bytes / (dec_avg_ms * 1e-3) / 1e9
+    value = kv_bytes / (step_ms * 1e-3) / 1e9
+    res = {
+        "metric": "GQA decode-attn KV read GB/s (% of MI355X HBM peak); us per decode step",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) latents and queries, NaN past each sequence's length; up-projections "
+                "drawn as nn.Linear initialises them)",
+        "config": {"workload": w.name, "batch": w.B, "heads": w.H, "d_k": w.d_k, "d_latent": w.d_latent,
+                   "rope_dim": w.rope_dim, "cached_tokens": [w.cached_lo, w.cached_hi], "layout": "contiguous",
+                   "kv_bytes_per_step": kv_bytes, "weight_bytes_per_step": weight_bytes, "cache_replicas": R,
+                   "split_tokens": kvc.mla_split_tokens(w.B, w.H, w.d_latent, max_len, args.split_tokens),
+                   "split_choice": "explicit" if args.split_tokens else "library"},
+        "us_per_step": round(step_ms * 1e3, 2),
+        "decode_us": round(dec_avg_ms * 1e3, 2),
+        "decode_us_median": round(sorted(dec_ms)[len(dec_ms) // 2] * 1e3, 2),
+        "hbm_pct_step": round(100 * value / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_for_current_kernel("native", w.name),
+                     "kernel": "mla_decode_kernel (streaming pass over the latent rows; the absorbed queries with "
+                               "the append, the split merge and the value up-projection are separate small kernels)",
+                     "bytes_per_launch": kv_bytes},
+        "wall_s_timed": round(wall, 4),
+    }
+    del caches
+    torch.cuda.empty_cache()
+    probe = read_probe(reps=5)
+    ceil_nt = probe["nontemporal"]["best_gbs"]
+    res["read_ceiling"] = {"probe": "kvc_hbm_read_probe, 4 GiB, best grid",
+                           "default_policy_gbs": probe["default"]["best_gbs"], "nontemporal_gbs": ceil_nt,
+                           "kernel_frac_of_ceiling": round(achieved / ceil_nt, 4)}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_mla(x, args.cpu_sample_seqs or 4)
+    return res
+
+
 def read_probe(gib: int = 4, reps: int = 10) -> dict:
     """Streaming-read rate of kvc_hbm_read_probe over a 4 GiB buffer (far beyond
     the 256 MB Infinity Cache), best of several grid sizes, with the default and
@@ -281,6 +410,12 @@ def main():
         sys.exit(1)
     kvc.load()   # fails loudly if libkvc.so is missing
 
+    if args.workload in W.MLA_WORKLOADS:
+        if args.window or args.ring or args.kv_cache != "native":
+            print("the latent-cache workload has no window or quantized variant", file=sys.stderr)
+            sys.exit(2)
+        print(json.dumps(bench_mla(args, W)), flush=True)
+        return
     w = W.WORKLOADS[args.workload]
     x = W.draw(w)
     dev = torch.device("cuda:0")

@@ -460,8 +460,9 @@ kvc_status kvc_append_mla(kvc_dtype dtype, int B, int d_latent, int rope_dim, vo
  * length of kvc_decode_attn_mla with these sizes (max_seq_len bounds the
  * attended lengths; split_tokens 0 = the library's choice, else a multiple of
  * 32).  (size_t)-1 / -1 for invalid or unsupported sizes.  The workspace holds
- * the absorbed queries and the latent context, [B, H, d_latent] float32 each,
- * and the split partials.
+ * the absorbed queries and the merged latent context, [B, H, d_latent]
+ * float32 each, and the split partials, [B, H, splits] (max, sum) pairs and
+ * [B, H, splits, d_latent] float32.
  */
 size_t kvc_decode_mla_workspace_bytes(int B, int H, int d_latent, int max_seq_len, int split_tokens);
 int kvc_decode_mla_split_tokens(int B, int H, int d_latent, int max_seq_len, int split_tokens);
@@ -476,9 +477,9 @@ int kvc_decode_mla_split_tokens(int B, int H, int d_latent, int max_seq_len, int
  *   out    float32 [B, H, d_k]  (float32: the result of the value
  *          up-projection, before any rounding to a storage type)
  * seq_lens[b] in [0, max_seq_len], max_seq_len <= T_max; a sequence of length
- * 0 gives zeros.  Four launches: absorbed queries, the streaming pass over the
- * cache (one workgroup per sequence, 32-head chunk and token split), the merge
- * of the splits, the value up-projection.
+ * 0 gives zeros.  Four launches: absorbed queries, the streaming pass over
+ * the cache (one workgroup per sequence, 32-head chunk and token split), the
+ * merge of the splits, the value up-projection.
  */
 kvc_status kvc_decode_attn_mla(int B, int H, int d_k, int d_latent, int rope_dim, const void* q,
                                const void* cache, int T_max, const int32_t* seq_lens, int max_seq_len,

@@ -218,7 +218,7 @@ bool plan_mla(int B, int H, int d_latent, int max_seq_len, int split_tokens, Mla
     pl.ctx = align_up(rows * d_latent * sizeof(float), 256);
     pl.ws_ml = pl.ctx + align_up(rows * d_latent * sizeof(float), 256);
     pl.ws_part = pl.ws_ml + align_up(rows * pl.n_splits * sizeof(float2), 256);
-    pl.ws_bytes = pl.ws_part + (pl.n_splits > 1 ? align_up(rows * pl.n_splits * d_latent * sizeof(float), 256) : 0);
+    pl.ws_bytes = pl.ws_part + align_up(rows * pl.n_splits * d_latent * sizeof(float), 256);
     *plan = pl;
     return true;
 }
@@ -789,7 +789,7 @@ kvc_status mla_common(int B, int H, int d_k, int d_latent, int rope_dim, const v
     p.qt = reinterpret_cast<float*>(ws + pl.qt);
     p.ctx = reinterpret_cast<float*>(ws + pl.ctx);
     p.ws_ml = reinterpret_cast<float2*>(ws + pl.ws_ml);
-    p.ws_part = pl.n_splits > 1 ? reinterpret_cast<float*>(ws + pl.ws_part) : nullptr;
+    p.ws_part = reinterpret_cast<float*>(ws + pl.ws_part);
     p.B = B; p.H = H; p.d_k = d_k; p.d_latent = d_latent; p.rope_dim = rope_dim; p.row = row;
     p.T_max = T_max; p.max_seq_len = max_seq_len;
     p.split_tokens = pl.split_tokens; p.n_splits = pl.n_splits; p.n_chunks = pl.n_chunks;

@@ -47,7 +47,6 @@ namespace {
 
 using namespace mfma;
 
-constexpr int kNW = 4;   // waves per workgroup
 
 // Attended length of sequence b, clamped to [0, max_seq_len]; a step whose
 // slot lies outside the cache attends over nothing.
@@ -89,54 +88,69 @@ __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "mem
 // w takes 16 of the columns for every sequence, 16 sequences per product:
 //   q~^T[l, b] = sum_i W_uk[h d_k + i, l] q[b, h, i]   A = W_uk,h^T (16 l x 32 i),
 //                                                      B = q^T (32 i x 16 b)
-// W_uk,h's 64 columns are staged in LDS as rows of i and read transposed.
+// W_uk,h's 64 columns (rows of i, read transposed) and the 16 sequences'
+// query rows are staged in LDS together, so the products wait on one round
+// of global loads.
 // ---------------------------------------------------------------------------
 template <int DL>
 __global__ void __launch_bounds__(256) mla_absorb_kernel(const MlaParams p) {
     const int tid = threadIdx.x;
-    if (p.c_new) {
-        // the new token's row [c_kv | k_rope] at slot positions[b] (bit copies)
-        const uint16_t* cn = static_cast<const uint16_t*>(p.c_new);
-        const uint16_t* rn = static_cast<const uint16_t*>(p.r_new);
-        uint16_t* cache = static_cast<uint16_t*>(p.cache);
-        for (int b = blockIdx.x; b < p.B; b += gridDim.x) {
-            const int pos = p.positions[b];
-            if (pos < 0 || pos >= p.T_max) continue;
-            uint16_t* dst = cache + (static_cast<size_t>(b) * p.T_max + pos) * p.row;
-            for (int e = tid; e < p.row; e += blockDim.x)
-                dst[e] = e < DL ? cn[static_cast<size_t>(b) * DL + e] : rn[static_cast<size_t>(b) * p.rope_dim + e - DL];
-        }
-    }
     constexpr int NLB = DL / 64;
     const int h = blockIdx.x / NLB;
-    if (h >= p.H) return;
+    if (h >= p.H) {
+        // workgroups past the products (decode step): the new token's row
+        // [c_kv | k_rope] of sequence b at slot positions[b] (bit copies)
+        const int b = blockIdx.x - p.H * NLB;
+        if (!p.c_new || b >= p.B) return;
+        const int pos = p.positions[b];
+        if (pos < 0 || pos >= p.T_max) return;
+        const uint16_t* cn = static_cast<const uint16_t*>(p.c_new);
+        const uint16_t* rn = static_cast<const uint16_t*>(p.r_new);
+        uint16_t* dst = static_cast<uint16_t*>(p.cache) + (static_cast<size_t>(b) * p.T_max + pos) * p.row;
+        for (int e = tid; e < p.row; e += blockDim.x)
+            dst[e] = e < DL ? cn[static_cast<size_t>(b) * DL + e] : rn[static_cast<size_t>(b) * p.rope_dim + e - DL];
+        return;
+    }
     const int l0 = 64 * (blockIdx.x % NLB);
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int r16 = lane & 15, q4 = lane >> 4;
 
-    // W_uk[h d_k + i, l0 .. l0 + 63]: d_k rows of 128 bytes
+    // W_uk[h d_k + i, l0 .. l0 + 63]: d_k rows of 128 bytes; query rows of 16
+    // sequences, d_k bf16 each, one 16-byte chunk of padding per row (so the
+    // 16 rows read at one offset fall in distinct banks)
     __shared__ uint4 wt[512 * 8];
+    __shared__ uint4 qs[16 * 65];
+    const int dk8 = p.d_k / 8;
+    const int qp = dk8 + 1;               // row pitch of qs in 16-byte chunks
     const uint16_t* wk = static_cast<const uint16_t*>(p.w_uk) + static_cast<size_t>(h) * p.d_k * DL + l0;
-    for (int idx = tid; idx < p.d_k * 8; idx += 256) {
-        const int i = idx >> 3, c = idx & 7;
-        wt[idx] = *reinterpret_cast<const uint4*>(wk + static_cast<size_t>(i) * DL + 8 * c);
-    }
-    __syncthreads();
-
+    const uint16_t* qb = static_cast<const uint16_t*>(p.q);
+    const char* wtb = reinterpret_cast<const char*>(wt);
+    const char* qsb = reinterpret_cast<const char*>(qs);
     // transposed-read source of this lane: row (i) 4*q4 + s16/4 (+16), columns
     // 16*wave + 4*(s16 % 4) .. +3
-    const char* wtb = reinterpret_cast<const char*>(wt);
     const int s16 = lane & 15;
     const int trow = 4 * q4 + s16 / 4;
     const int tcol = 16 * wave + 4 * (s16 % 4);
     const int KK = p.d_k / 32;
-    const uint16_t* qb = static_cast<const uint16_t*>(p.q);
     for (int b0 = 0; b0 < p.B; b0 += 16) {
-        const int bq = b0 + r16;
-        const bool bok = bq < p.B;
-        const uint16_t* qrow = qb + (static_cast<size_t>(bok ? bq : 0) * p.H + h) * p.d_k;
+        if (b0 > 0) __syncthreads();      // the previous block's reads of qs are done
+        if (b0 == 0) {
+            for (int idx = tid; idx < p.d_k * 8; idx += 256) {
+                const int i = idx >> 3, c = idx & 7;
+                wt[idx] = *reinterpret_cast<const uint4*>(wk + static_cast<size_t>(i) * DL + 8 * c);
+            }
+        }
+        for (int idx = tid; idx < 16 * dk8; idx += 256) {
+            const int r = idx / dk8, c = idx - (idx / dk8) * dk8;
+            const int bq = b0 + r;
+            qs[r * qp + c] = bq < p.B ? *reinterpret_cast<const uint4*>(
+                                            qb + (static_cast<size_t>(bq) * p.H + h) * p.d_k + 8 * c)
+                                      : make_uint4(0, 0, 0, 0);
+        }
+        __syncthreads();
         f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        const char* qrow = qsb + r16 * qp * 16;
         for (int kk = 0; kk < KK; ++kk) {
             const int r0 = 32 * kk + trow;
             const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(wtb + r0 * 128 + 2 * tcol));
@@ -148,38 +162,55 @@ __global__ void __launch_bounds__(256) mla_absorb_kernel(const MlaParams p) {
             va.z = __builtin_bit_cast(uint2, hi).x;
             va.w = __builtin_bit_cast(uint2, hi).y;
             // B operand: q[b, h, i] for i = 32 kk + 4 q4 + (0..3) and 16 + that
-            uint2 qa = *reinterpret_cast<const uint2*>(qrow + 32 * kk + 4 * q4);
-            uint2 qc = *reinterpret_cast<const uint2*>(qrow + 32 * kk + 16 + 4 * q4);
-            if (!bok) qa = qc = make_uint2(0, 0);
+            const uint2 qa = *reinterpret_cast<const uint2*>(qrow + 2 * (32 * kk + 4 * q4));
+            const uint2 qc = *reinterpret_cast<const uint2*>(qrow + 2 * (32 * kk + 16 + 4 * q4));
             acc = mfma16(va, make_uint4(qa.x, qa.y, qc.x, qc.y), acc);
         }
-        // lane holds q~^T rows l0 + 16 wave + 4 q4 + e of column b
-        if (bok)
+        // lane holds q~^T rows l0 + 16 wave + 4 q4 + e of column b; stored
+        // times the softmax scale in log2 units (the streaming pass then
+        // computes scores ready for exp2)
+        const int bq = b0 + r16;
+        const float sc = p.scale_log2;
+        if (bq < p.B)
             *reinterpret_cast<float4*>(p.qt + (static_cast<size_t>(bq) * p.H + h) * DL + l0 + 16 * wave + 4 * q4) =
-                make_float4(acc[0], acc[1], acc[2], acc[3]);
+                make_float4(acc[0] * sc, acc[1] * sc, acc[2] * sc, acc[3] * sc);
     }
 }
 
 // ---------------------------------------------------------------------------
-// The streaming pass (see the top of the file).
+// The streaming pass.  One workgroup of NWV waves (two per SIMD) per
+// (sequence, chunk of up to 32 heads, token split); the split's rows pass
+// through LDS in 32-token tiles (direct loads, NST stages).  Wave w takes
+// head block hb = w % HB (16 heads) and column slice cs = w / HB of width
+// DW = d_latent / (NWV / HB):
+//   * scores: the wave multiplies its column slice of the tile by the same
+//     slice of its heads' absorbed queries (S^T = C Q~^T, 16 tokens x 16
+//     heads per 16x16x32 product) and leaves the partial sums in LDS; after
+//     a barrier the waves of a head block add the partials in slice order,
+//     so they hold bit-identical scores and run the same online softmax;
+//   * PV: the wave accumulates its heads' X^T over its columns, X^T += C^T
+//     P^T, C^T read transposed from the staged tile (ds_read_b64_tr_b16).
 // ---------------------------------------------------------------------------
-template <int DL, int HB, int NST>
-__global__ void __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
+template <int DL, int HB, int NST, int NWV>
+__global__ void __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(NWV / 4, NWV / 4)))
 mla_decode_kernel(const MlaParams p) {
     constexpr int TT = kMlaTile;          // tokens per tile
-    constexpr int DW = DL / kNW;          // latent columns per wave
+    constexpr int WPH = NWV / HB;         // waves sharing one 16-head block (column slices)
+    constexpr int DW = DL / WPH;          // latent columns per wave
     constexpr int KKW = DW / 32;          // 32-wide reduction steps of a wave's slice
     constexpr int NBW = DW / 16;          // 16-column blocks of a wave's slice
     constexpr int ROWB = 2 * DL;          // LDS bytes per staged row
     constexpr int STAGE = TT * ROWB;
     constexpr int CPR = DL / 8;           // 16-byte chunks per row
     constexpr int RPI = 64 / CPR;         // rows per wave-wide 16-byte load
-    constexpr int LOADS = TT / (kNW * RPI);   // direct loads per thread per tile
-    static_assert(CPR >= 16 && LOADS >= 1, "d_latent 128, 256 or 512");
+    constexpr int LOADS = TT / (NWV * RPI);   // direct loads per thread per tile
+    static_assert(CPR >= 16 && LOADS >= 1 && KKW >= 1, "d_latent 128, 256 or 512");
+    static_assert(NST == 2 || NST == 3, "two or three stages");
+    static_assert(NWV == 4 || NWV == 8, "four or eight waves");
     __shared__ __attribute__((aligned(16))) char st0[STAGE];
     __shared__ __attribute__((aligned(16))) char st1[STAGE];
     __shared__ __attribute__((aligned(16))) char st2[NST > 2 ? STAGE : 16];
-    __shared__ f32x4_t sbuf[kNW * HB * 2 * 64];   // partial scores [wave][hb][kb][lane]
+    __shared__ f32x4_t sbuf[NWV * 2 * 64];   // partial scores [wave][kb][lane]
 
     const int wid = blockIdx.x;
     if (wid >= p.n_wg) return;
@@ -189,22 +220,30 @@ mla_decode_kernel(const MlaParams p) {
     const int b = unit / p.n_chunks;
     const int L = mla_len(p, b);
     const int nsp = L > 0 ? (L + p.split_tokens - 1) / p.split_tokens : 1;
-    if (split >= nsp) return;
+    const int tid = threadIdx.x;
+    const int h0 = chunk * kMlaHeads;     // first head of the chunk
+    const int nh = min(kMlaHeads, p.H - h0);
+    if (split >= nsp) {
+        // a split past the sequence's end: (m, l) = (-inf, 0), a weight of 0
+        // in the merge, which therefore needs no lengths
+        if (tid < nh) p.ws_ml[(static_cast<size_t>(b) * p.H + h0 + tid) * p.n_splits + split] = make_float2(-INFINITY, 0.0f);
+        return;
+    }
     const int t_begin = split * p.split_tokens;
     const int t_end = min(L, t_begin + p.split_tokens);
 
-    const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hbw = wave % HB;            // this wave's head block
+    const int cs = wave / HB;             // ... and column slice
     const int r16 = lane & 15;
     const int q4 = lane >> 4;
-    const int h0 = chunk * kMlaHeads;     // first head of the chunk
-    const int nh = min(kMlaHeads, p.H - h0);
 
-    // Chunk u of tile row r sits at slot u ^ swz(r) of that row in LDS.  The
-    // 16 lanes reading one chunk of 16 consecutive rows (score operands) and
-    // the 16 lanes of a transposed read (4 rows x 32 bytes) both hit distinct
-    // 16-byte bank groups.
+    // Chunk u of tile row r sits at slot u ^ swz(r) of that row in LDS: the 16
+    // lanes reading one chunk of 16 consecutive rows (score operands) and the
+    // 16 lanes of a transposed read (4 rows x 32 bytes) hit distinct 16-byte
+    // bank groups.  (A swizzle spreading 8-row groups instead measured twice
+    // the bank-conflict cycles.)
     auto swz = [](int r) { return (2 * r + ((r >> 3) & 1)) & 15; };
 
     // The sequence's rows through a buffer resource ending at row t_end: rows
@@ -214,7 +253,7 @@ mla_decode_kernel(const MlaParams p) {
     auto load_tile = [&](int base, char* st) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
-            const int j = kNW * i + wave;                 // this load's 1 KiB of the stage
+            const int j = NWV * i + wave;                 // this load's 1 KiB of the stage
             const int rr = RPI * j + lane / CPR;          // row in the tile
             const int u = (lane % CPR) ^ swz(rr);
             lds_void_t* dst = (lds_void_t*)(st + 1024 * j);
@@ -222,38 +261,33 @@ mla_decode_kernel(const MlaParams p) {
         }
     };
 
-    // Absorbed queries of the chunk's heads, this wave's columns, as hi + lo
-    // B operands: lane holds head 16 hb + r16, columns DW*wave + 32 kk + 8 q4 .. +7.
-    // Heads past the chunk read zeros.
+    // Absorbed queries (already scaled to log2 units) of the wave's head block
+    // and columns, as hi + lo B operands: lane holds head 16 hbw + r16,
+    // columns DW*cs + 32 kk + 8 q4 .. +7.  Heads past the chunk read zeros.
     const __amdgpu_buffer_rsrc_t qrs =
         make_uniform_rsrc(p.qt + (static_cast<size_t>(b) * p.H + h0) * DL, nh * DL * 4);
-    uint4 qh[HB][KKW], ql[HB][KKW];
+    uint4 qh[KKW], ql[KKW];
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-        for (int kk = 0; kk < KKW; ++kk) {
-            const int off = ((16 * hb + r16) * DL + DW * wave + 32 * kk + 8 * q4) * 4;
-            const float4 a = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0));
-            const float4 c = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(qrs, off + 16, 0, 0));
-            split8(a, c, qh[hb][kk], ql[hb][kk]);
-        }
-
-    float m[HB], l[HB];
-    f32x4_t o[HB][NBW];
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
-        m[hb] = -kNoMax;
-        l[hb] = 0.0f;
-#pragma unroll
-        for (int nb = 0; nb < NBW; ++nb) o[hb][nb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int kk = 0; kk < KKW; ++kk) {
+        const int off = ((16 * hbw + r16) * DL + DW * cs + 32 * kk + 8 * q4) * 4;
+        const float4 a = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0));
+        const float4 c = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(qrs, off + 16, 0, 0));
+        split8(a, c, qh[kk], ql[kk]);
     }
+
+    // Running max m (log2 units) and sum l of the lane's head; X^T accumulators.
+    // The score products start from -m (in the first column slice), so they
+    // produce s - m directly; m starts at 0 and is set by the first tile.
+    float m = 0.0f, l = 0.0f;
+    f32x4_t o[NBW];
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) o[nb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
     const int s16 = lane & 15;
     const int tr_row = 4 * q4 + s16 / 4;
-    f32x4_t* sw = sbuf + wave * HB * 2 * 64 + lane;
 
     // One tile: cur holds it; refill receives the tile NST - 1 steps ahead.
-    auto body = [&](const char* cur, char* refill, int base) __attribute__((always_inline)) {
+    auto body = [&](const char* cur, char* refill, int base, bool first) __attribute__((always_inline)) {
         // this thread's loads of the tile have landed (at most NST - 2 later
         // tiles outstanding) and its LDS reads of the previous tile are done;
         // after the barrier that holds for every thread, so the stage the last
@@ -262,85 +296,84 @@ mla_decode_kernel(const MlaParams p) {
         wg_barrier();
         load_tile(base + (NST - 1) * TT, refill);
 
-        // partial scores over this wave's columns
-        uint4 ka[2][KKW];
+        // partial scores (minus m) over this wave's columns
+        f32x4_t acc[2];
+        const float init = cs == 0 ? -m : 0.0f;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb) {
+            acc[kb] = f32x4_t{init, init, init, init};
+            const int r = 16 * kb + r16;
 #pragma unroll
             for (int kk = 0; kk < KKW; ++kk) {
-                const int r = 16 * kb + r16;
-                const int u = (DW / 8) * wave + 4 * kk + q4;
-                ka[kb][kk] = *reinterpret_cast<const uint4*>(cur + r * ROWB + 16 * (u ^ swz(r)));
+                const int u = (DW / 8) * cs + 4 * kk + q4;
+                const uint4 ka = *reinterpret_cast<const uint4*>(cur + r * ROWB + 16 * (u ^ swz(r)));
+                acc[kb] = mfma16(ka, qh[kk], acc[kb]);
+                acc[kb] = mfma16(ka, ql[kk], acc[kb]);
             }
+        }
 #pragma unroll
-        for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                for (int kk = 0; kk < KKW; ++kk) {
-                    acc = mfma16(ka[kb][kk], qh[hb][kk], acc);
-                    acc = mfma16(ka[kb][kk], ql[hb][kk], acc);
-                }
-                sw[(hb * 2 + kb) * 64] = acc;
-            }
+        for (int kb = 0; kb < 2; ++kb) sbuf[(wave * 2 + kb) * 64 + lane] = acc[kb];
         __builtin_amdgcn_s_waitcnt(kLgkmZero);
         wg_barrier();
 
-        // full scores (the four partials added in wave order), scaled to log2
-        // units; tokens past the split masked
-        float s[HB][8];
+        // full scores s - m: the slices' partials added in slice order (the
+        // wave's own from its registers), bit-identical in all WPH waves
+        float s[8];
 #pragma unroll
-        for (int hb = 0; hb < HB; ++hb)
+        for (int kb = 0; kb < 2; ++kb) {
+            f32x4_t a = cs == 0 ? acc[kb] : sbuf[((0 * HB + hbw) * 2 + kb) * 64 + lane];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const f32x4_t* sp = sbuf + (hb * 2 + kb) * 64 + lane;
-                f32x4_t a = sp[0];
+            for (int c = 1; c < WPH; ++c) a += cs == c ? acc[kb] : sbuf[((c * HB + hbw) * 2 + kb) * 64 + lane];
 #pragma unroll
-                for (int w = 1; w < kNW; ++w) a += sp[w * HB * 2 * 64];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t = base + 16 * kb + 4 * q4 + e;
-                    s[hb][4 * kb + e] = t < t_end ? a[e] * p.scale_log2 : -INFINITY;
-                }
-            }
-
-        // online softmax, as in the grouped-query kernel: the reference max is
-        // moved only when a tile exceeds it by more than 2^kLazy
-        uint32_t ph[HB][4], pl[HB][4];
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb) {
-            float mt = s[hb][0];
-#pragma unroll
-            for (int e = 1; e < 8; ++e) mt = fmaxf(mt, s[hb][e]);
-            mt = max_same_head(mt);
-            const bool move = mt > m[hb] + kLazy;
-            if (__any(move)) {
-                const float m_new = move ? mt : m[hb];
-                const float alpha = fast_exp2(m[hb] - m_new);
-                m[hb] = m_new;
-                l[hb] *= alpha;
-#pragma unroll
-                for (int nb = 0; nb < NBW; ++nb) o[hb][nb] *= alpha;
-            }
-            float pr[8], ps = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                pr[e] = fast_exp2(s[hb][e] - m[hb]);
-                ps += pr[e];
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                ph[hb][i] = pack2_bf16(pr[2 * i], pr[2 * i + 1]);
-                pl[hb][i] = pack2_bf16(pr[2 * i] - bf16_lo(ph[hb][i]), pr[2 * i + 1] - bf16_hi(ph[hb][i]));
-            }
-            l[hb] += ps;
+            for (int e = 0; e < 4; ++e) s[4 * kb + e] = a[e];
         }
+        if (base + TT > t_end) {          // last tile: rows past the split masked
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (base + 16 * kb + 4 * q4 + e >= t_end) s[4 * kb + e] = -INFINITY;
+        }
+
+        // online softmax.  m moves (and X, l are rescaled) only on the first
+        // tile or when a tile exceeds it by more than 2^kLazy
+        float mt = s[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) mt = fmaxf(mt, s[e]);
+        mt = max_same_head(mt);
+        const bool move = first || mt > kLazy;
+        if (__any(move)) {
+            const float d = move ? mt : 0.0f;
+            m += d;
+            if (!first) {
+                const float alpha = fast_exp2(-d);
+                l *= alpha;
+#pragma unroll
+                for (int nb = 0; nb < NBW; ++nb) o[nb] *= alpha;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s[e] -= d;
+        }
+        float pr[8], ps = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            pr[e] = fast_exp2(s[e]);
+            ps += pr[e];
+        }
+        l += ps;
+        uint32_t ph[4], pl[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            ph[i] = pack2_bf16(pr[2 * i], pr[2 * i + 1]);
+            pl[i] = pack2_bf16(pr[2 * i] - bf16_lo(ph[i]), pr[2 * i + 1] - bf16_hi(ph[i]));
+        }
+        const uint4 pb_hi = make_uint4(ph[0], ph[1], ph[2], ph[3]);
+        const uint4 pb_lo = make_uint4(pl[0], pl[1], pl[2], pl[3]);
 
         // X^T += C^T P^T over this wave's column blocks
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb) {
-            const int u = (DW / 8) * wave + 2 * nb + (s16 % 4) / 2;
+            const int u = (DW / 8) * cs + 2 * nb + (s16 % 4) / 2;
             const int r0 = tr_row, r1 = tr_row + 16;
             const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (lds_s16x4_t*)(cur + r0 * ROWB + 16 * (u ^ swz(r0)) + 8 * (s16 & 1)));
@@ -351,11 +384,8 @@ mla_decode_kernel(const MlaParams p) {
             va.y = __builtin_bit_cast(uint2, lo).y;
             va.z = __builtin_bit_cast(uint2, hi).x;
             va.w = __builtin_bit_cast(uint2, hi).y;
-#pragma unroll
-            for (int hb = 0; hb < HB; ++hb) {
-                o[hb][nb] = mfma16(va, make_uint4(ph[hb][0], ph[hb][1], ph[hb][2], ph[hb][3]), o[hb][nb]);
-                o[hb][nb] = mfma16(va, make_uint4(pl[hb][0], pl[hb][1], pl[hb][2], pl[hb][3]), o[hb][nb]);
-            }
+            o[nb] = mfma16(va, pb_hi, o[nb]);
+            o[nb] = mfma16(va, pb_lo, o[nb]);
         }
     };
 
@@ -366,24 +396,22 @@ mla_decode_kernel(const MlaParams p) {
     load_tile(base, st0);
     if constexpr (NST > 2) load_tile(base + TT, st1);
     if (base < t_end) {
+        bool first = true;
         for (;;) {
             if constexpr (NST == 2) {
-                body(st0, st1, base);
-                base += TT;
-                if (base >= t_end) break;
-                body(st1, st0, base);
-                base += TT;
-                if (base >= t_end) break;
+                body(st0, st1, base, first);
+                first = false;
+                if ((base += TT) >= t_end) break;
+                body(st1, st0, base, false);
+                if ((base += TT) >= t_end) break;
             } else {
-                body(st0, st2, base);
-                base += TT;
-                if (base >= t_end) break;
-                body(st1, st0, base);
-                base += TT;
-                if (base >= t_end) break;
-                body(st2, st1, base);
-                base += TT;
-                if (base >= t_end) break;
+                body(st0, st2, base, first);
+                first = false;
+                if ((base += TT) >= t_end) break;
+                body(st1, st0, base, false);
+                if ((base += TT) >= t_end) break;
+                body(st2, st1, base, false);
+                if ((base += TT) >= t_end) break;
             }
         }
     }
@@ -391,83 +419,86 @@ mla_decode_kernel(const MlaParams p) {
     // handed to the next workgroup)
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
-    // Epilogue: a whole sequence in one split writes x = X / l; several
-    // splits write their (m, l, X) partials.  The wave writes its columns.
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
-        l[hb] = sum_same_head(l[hb]);
-        const int hh = 16 * hb + r16;
-        if (hh >= nh) continue;
+    // Epilogue: the split's (m, l, X) partials, each wave its columns of its
+    // head block (a split that saw no token leaves m = 0, l = 0, X = 0).
+    l = sum_same_head(l);
+    const int hh = 16 * hbw + r16;
+    if (hh < nh) {
         const size_t bh = static_cast<size_t>(b) * p.H + h0 + hh;
-        if (nsp == 1) {
-            const float inv = l[hb] > 0.0f ? 1.0f / l[hb] : 0.0f;
-            float* dst = p.ctx + bh * DL + DW * wave + 4 * q4;
+        float* dst = p.ws_part + (bh * p.n_splits + split) * DL + DW * cs + 4 * q4;
 #pragma unroll
-            for (int nb = 0; nb < NBW; ++nb)
-                *reinterpret_cast<float4*>(dst + 16 * nb) =
-                    make_float4(o[hb][nb][0] * inv, o[hb][nb][1] * inv, o[hb][nb][2] * inv, o[hb][nb][3] * inv);
-        } else {
-            float* dst = p.ws_part + (bh * p.n_splits + split) * DL + DW * wave + 4 * q4;
-#pragma unroll
-            for (int nb = 0; nb < NBW; ++nb)
-                *reinterpret_cast<float4*>(dst + 16 * nb) =
-                    make_float4(o[hb][nb][0], o[hb][nb][1], o[hb][nb][2], o[hb][nb][3]);
-            if (wave == 0 && q4 == 0) p.ws_ml[bh * p.n_splits + split] = make_float2(m[hb], l[hb]);
-        }
+        for (int nb = 0; nb < NBW; ++nb)
+            *reinterpret_cast<float4*>(dst + 16 * nb) = make_float4(o[nb][0], o[nb][1], o[nb][2], o[nb][3]);
+        if (cs == 0 && q4 == 0) p.ws_ml[bh * p.n_splits + split] = make_float2(m, l);
     }
 }
 
 // ---------------------------------------------------------------------------
-// Log-sum-exp merge of the splits of one (sequence, head): x = sum_s 2^(m_s -
-// M) X_s / sum_s 2^(m_s - M) l_s.  One thread per 4 latent columns.
+// Log-sum-exp merge of the splits: x[b, h, :] = sum_s 2^(m_s - M) X_s /
+// sum_s 2^(m_s - M) l_s, one workgroup of d_latent / 4 threads per (sequence,
+// head), 4 columns per thread.  Each chunk of 16 splits' (m, l) pairs and
+// partials is requested at once; splits past a sequence's end carry m = -inf
+// (weight 0) and are skipped by a select (their partials are not written and
+// may hold anything).
 // ---------------------------------------------------------------------------
 template <int DL>
 __global__ void __launch_bounds__(DL / 4) mla_merge_kernel(const MlaParams p) {
-    const int bh = blockIdx.x;
-    const int b = bh / p.H;
-    const int L = mla_len(p, b);
-    const int nsp = L > 0 ? (L + p.split_tokens - 1) / p.split_tokens : 1;
-    if (nsp <= 1) return;                 // written by the streaming pass
-    const float2* ml = p.ws_ml + static_cast<size_t>(bh) * p.n_splits;
-    float M = -INFINITY;
-    for (int s = 0; s < nsp; ++s) M = fmaxf(M, ml[s].x);
+    const size_t bh = blockIdx.x;
     const int c = 4 * threadIdx.x;
+    const float2* ml = p.ws_ml + bh * p.n_splits;
+    const float* part = p.ws_part + bh * p.n_splits * DL + c;
+    float M = -INFINITY, lam = 0.0f;
     float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    float lam = 0.0f;
-    const float* part = p.ws_part + static_cast<size_t>(bh) * p.n_splits * DL + c;
-    for (int s = 0; s < nsp; ++s) {
-        const float2 v = ml[s];
-        const float f = fast_exp2(v.x - M);
-        const float4 x = *reinterpret_cast<const float4*>(part + static_cast<size_t>(s) * DL);
-        acc.x = fmaf(x.x, f, acc.x);
-        acc.y = fmaf(x.y, f, acc.y);
-        acc.z = fmaf(x.z, f, acc.z);
-        acc.w = fmaf(x.w, f, acc.w);
-        lam = fmaf(v.y, f, lam);
+    for (int s0 = 0; s0 < p.n_splits; s0 += 16) {
+        float2 v[16];
+        float4 xp[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const bool in = s0 + j < p.n_splits;
+            v[j] = in ? ml[s0 + j] : make_float2(-INFINITY, 0.0f);
+            xp[j] = in ? *reinterpret_cast<const float4*>(part + static_cast<size_t>(s0 + j) * DL)
+                       : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+        float Mc = M;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) Mc = fmaxf(Mc, v[j].x);
+        const float a = Mc > M ? fast_exp2(M - Mc) : 1.0f;   // rescale of the earlier chunks
+        acc.x *= a; acc.y *= a; acc.z *= a; acc.w *= a;
+        lam *= a;
+        M = Mc;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const float f = fast_exp2(v[j].x - M);
+            const bool use = f > 0.0f;
+            acc.x = use ? fmaf(xp[j].x, f, acc.x) : acc.x;
+            acc.y = use ? fmaf(xp[j].y, f, acc.y) : acc.y;
+            acc.z = use ? fmaf(xp[j].z, f, acc.z) : acc.z;
+            acc.w = use ? fmaf(xp[j].w, f, acc.w) : acc.w;
+            lam = use ? fmaf(v[j].y, f, lam) : lam;
+        }
     }
     const float inv = lam > 0.0f ? 1.0f / lam : 0.0f;
-    *reinterpret_cast<float4*>(p.ctx + static_cast<size_t>(bh) * DL + c) =
-        make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    *reinterpret_cast<float4*>(p.ctx + bh * DL + c) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
 }
 
 // ---------------------------------------------------------------------------
 // Value up-projection, out[b, h, i] = W_uv[h d_k + i, :] . x[b, h, :] +
-// b_uv[h d_k + i].  One workgroup per (head, 64 rows of d_k); wave w takes 16
-// rows for every sequence, 16 sequences per product:
+// b_uv[h d_k + i].  One single-wave workgroup per (head, 16 rows of d_k),
+// 16 sequences per product:
 //   out^T[i, b] = sum_l W_uv[h d_k + i, l] x[b, h, l]   A = W_uv rows (16 i x 32 l),
 //                                                       B = x^T (32 l x 16 b), hi + lo
+// so each row of W_uv is read once per step; the reduction runs in two
+// independent accumulator chains.
 // ---------------------------------------------------------------------------
 template <int DL>
-__global__ void __launch_bounds__(256) mla_up_kernel(const MlaParams p) {
+__global__ void __launch_bounds__(64) mla_up_kernel(const MlaParams p) {
     constexpr int KK = DL / 32;
-    const int nib = (p.d_k + 63) / 64;
+    const int nib = p.d_k / 16;
     const int h = blockIdx.x / nib;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int lane = threadIdx.x;
     const int r16 = lane & 15, q4 = lane >> 4;
-    const int i0 = 64 * (blockIdx.x % nib) + 16 * wave;
-    if (h >= p.H || i0 >= p.d_k) return;
+    const int i0 = 16 * (blockIdx.x - h * nib);
+    if (h >= p.H) return;
     const uint16_t* wrow = static_cast<const uint16_t*>(p.w_uv) + (static_cast<size_t>(h) * p.d_k + i0 + r16) * DL + 8 * q4;
     uint4 wa[KK];
 #pragma unroll
@@ -479,26 +510,26 @@ __global__ void __launch_bounds__(256) mla_up_kernel(const MlaParams p) {
     for (int b0 = 0; b0 < p.B; b0 += 16) {
         const int bq = b0 + r16;
         const bool bok = bq < p.B;
+        const bool empty = !bok || mla_len_lane(p, bok ? bq : b0) == 0;   // length 0: zeros
         const float* xr = p.ctx + (static_cast<size_t>(bok ? bq : 0) * p.H + h) * DL + 8 * q4;
-        f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        f32x4_t acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
             float4 a = *reinterpret_cast<const float4*>(xr + 32 * kk);
             float4 c = *reinterpret_cast<const float4*>(xr + 32 * kk + 4);
             if (!bok) a = c = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            uint4 hi, lo;
-            split8(a, c, hi, lo);
-            acc = mfma16(wa[kk], hi, acc);
-            acc = mfma16(wa[kk], lo, acc);
+            uint4 xh, xl;
+            split8(a, c, xh, xl);
+            acc[kk & 1] = mfma16(wa[kk], xh, acc[kk & 1]);
+            acc[kk & 1] = mfma16(wa[kk], xl, acc[kk & 1]);
         }
+        const f32x4_t r4 = acc[0] + acc[1];
         if (bok) {
-            // a sequence that attends over nothing gives zeros
-            const bool empty = mla_len_lane(p, bq) == 0;
             float4 r;
-            r.x = empty ? 0.0f : acc[0] + bias[0];
-            r.y = empty ? 0.0f : acc[1] + bias[1];
-            r.z = empty ? 0.0f : acc[2] + bias[2];
-            r.w = empty ? 0.0f : acc[3] + bias[3];
+            r.x = empty ? 0.0f : r4[0] + bias[0];
+            r.y = empty ? 0.0f : r4[1] + bias[1];
+            r.z = empty ? 0.0f : r4[2] + bias[2];
+            r.w = empty ? 0.0f : r4[3] + bias[3];
             *reinterpret_cast<float4*>(p.out + (static_cast<size_t>(bq) * p.H + h) * p.d_k + i0 + 4 * q4) = r;
         }
     }
@@ -518,23 +549,30 @@ __global__ void __launch_bounds__(256) mla_append_kernel(int B, int DL, int rd, 
         dst[e] = e < DL ? cn[static_cast<size_t>(b) * DL + e] : rn[static_cast<size_t>(b) * rd + e - DL];
 }
 
+// The streaming kernel: eight waves (two per SIMD), or four where an
+// eighth of the latent width would be narrower than one 32-wide step; two
+// stages (a third measured no faster, as did four waves at d_latent 512).
+template <int DL, int HB>
+hipError_t launch_main(const MlaParams& p, hipStream_t stream, const KernelTiming& tm) {
+    const dim3 grid(p.n_wg);
+    if constexpr (DL / (8 / HB) >= 32)
+        return launch_timed(mla_decode_kernel<DL, HB, 2, 8>, grid, dim3(8 * 64), stream, tm, p);
+    else
+        return launch_timed(mla_decode_kernel<DL, HB, 2, 4>, grid, dim3(4 * 64), stream, tm, p);
+}
+
 template <int DL>
 hipError_t launch_dl(const MlaParams& p, hipStream_t stream, const KernelTiming& tm) {
-    hipLaunchKernelGGL(mla_absorb_kernel<DL>, dim3(p.H * (DL / 64)), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(mla_absorb_kernel<DL>, dim3(p.H * (DL / 64) + (p.c_new ? p.B : 0)), dim3(256), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 grid(p.n_wg), block(kNW * 64);
-    constexpr int NST = 2;
     const int rows = min(p.H, kMlaHeads);
-    e = rows <= 16 ? launch_timed(mla_decode_kernel<DL, 1, NST>, grid, block, stream, tm, p)
-                   : launch_timed(mla_decode_kernel<DL, 2, NST>, grid, block, stream, tm, p);
+    e = rows <= 16 ? launch_main<DL, 1>(p, stream, tm) : launch_main<DL, 2>(p, stream, tm);
     if (e != hipSuccess) return e;
-    if (p.n_splits > 1) {
-        hipLaunchKernelGGL(mla_merge_kernel<DL>, dim3(p.B * p.H), dim3(DL / 4), 0, stream, p);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(mla_up_kernel<DL>, dim3(p.H * ((p.d_k + 63) / 64)), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(mla_merge_kernel<DL>, dim3(p.B * p.H), dim3(DL / 4), 0, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(mla_up_kernel<DL>, dim3(p.H * (p.d_k / 16)), dim3(64), 0, stream, p);
     return hipGetLastError();
 }
 

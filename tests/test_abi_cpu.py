@@ -301,7 +301,7 @@ def test_latent_cache_host_checks(lib):
 def test_latent_cache_plan(lib):
     """Splits of the latent-cache decode: about one workgroup per compute unit
     over the sequences and 32-head chunks, at least 256 tokens, whole 32-token
-    tiles; the workspace holds the absorbed queries, the latent context and
+    tiles; the workspace holds the absorbed queries, the merged context and
     the partials."""
     st, ws = lib.kvc_decode_mla_split_tokens, lib.kvc_decode_mla_workspace_bytes
     assert st(16, 32, 512, 8193, 0) == 544                         # 16 sequences: 16 splits each
@@ -313,6 +313,6 @@ def test_latent_cache_plan(lib):
     splits = -(-8193 // 544)
     n = ws(16, 32, 512, 8193, 0)
     assert n >= 2 * rows * 512 * 4 + rows * splits * (512 + 2) * 4 and n % 256 == 0
-    one = ws(16, 32, 512, 200, 0)                                  # one split: no partials
-    assert one < 2 * rows * 512 * 4 + rows * 8 + 4096
+    one = ws(16, 32, 512, 200, 0)                                  # one split: one partial per head
+    assert 2 * rows * 512 * 4 + rows * (512 + 2) * 4 <= one < 2 * rows * 512 * 4 + rows * (512 + 2) * 4 + 1024
     assert ws(16, 32, 384, 8193, 0) == (1 << 64) - 1
