@@ -39,6 +39,8 @@ TRAFFIC = {
                            ("kvc_decode_mfma.hip", "kvc_mfma_common.h", "kvc_device.h", "kvc_internal.h")),
     ("u8", "gqa_8b"): ("decode_u8_gqa_8b_traffic.json",
                        ("kvc_decode_u8.hip", "kvc_mfma_common.h", "kvc_device.h", "kvc_internal.h")),
+    ("native", "mla_latent"): ("decode_mla_latent_traffic.json",
+                               ("kvc_mla.hip", "kvc_mfma_common.h", "kvc_device.h", "kvc_internal.h")),
 }
 
 
