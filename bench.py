@@ -317,6 +317,7 @@ def bench_mla(args, W) -> dict:
     dec_ms = [a.elapsed_time(b) for a, b in evs]
     dec_avg_ms = sum(dec_ms) / len(dec_ms)
     achieved = kv_bytes / (dec_avg_ms * 1e-3) / 1e9
+    check_kernel_timing(achieved, w.name)
     value = kv_bytes / (step_ms * 1e-3) / 1e9
     res = {
         "metric": "GQA decode-attn KV read GB/s (% of MI355X HBM peak); us per decode step",
@@ -352,6 +353,16 @@ def bench_mla(args, W) -> dict:
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_mla(x, args.cpu_sample_seqs or 4)
     return res
+
+
+def check_kernel_timing(achieved_gbs: float, what: str) -> None:
+    """The per-launch events must bracket the streaming kernel: a rate above the
+    HBM peak means they did not (e.g. a step path that never asked the library
+    for them) and the figure would be meaningless."""
+    if achieved_gbs > 1.05 * HBM_PEAK_GBS:
+        print(f"bench.py: {what}: {achieved_gbs:.0f} GB/s exceeds the HBM peak; the per-launch timing events "
+              "did not bracket the streaming kernel", file=sys.stderr)
+        sys.exit(3)
 
 
 def read_probe(gib: int = 4, reps: int = 10) -> dict:
@@ -492,6 +503,8 @@ def main():
             kvc.decode_attn_multi(q_work, ks[r], vs[r], lens, max_len, win, block_table=tbl, out=out,
                                   split_tokens=args.split_tokens)
             return
+        if ev is not None:
+            kvc.profile_next_decode(ev[0], ev[1])
         if win:
             kvc.decode_step_window(q, ks[r], vs[r], pos, kn, vn, cos, sin, max_len, win, ring=args.ring,
                                    block_table=tbl, q_rot_out=q_rot, out=out, split_tokens=args.split_tokens)
@@ -531,6 +544,7 @@ def main():
     dec_med_ms = sorted(dec_ms)[len(dec_ms) // 2]
 
     achieved = kv_bytes / (dec_avg_ms * 1e-3) / 1e9
+    check_kernel_timing(achieved, w.name)
     value = kv_bytes / (step_ms * 1e-3) / 1e9
     traffic = None if (win or multi) else traffic_for_current_kernel(args.kv_cache, w.name)
     pool_tokens = x.k_cache.shape[0] * w.block_size if w.paged else 0
