@@ -59,7 +59,7 @@ using namespace mfma;
 // (The paged kernel with staged tiles and one head block is planned at three
 // workgroups per CU: its registers are held to three waves per SIMD.)
 template <int D, int HB, int NW, int MODE, bool FUSED, bool MQ>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((MODE == 3 && HB == 1) ? 3 : 1, 8)))
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((MODE == 3 && HB == 1) ? 3 : ((MQ && HB == 2 && MODE == 0 && D <= 128) ? 2 : 1), 8)))
 decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table) {
     // (the block table as its own restrict argument: nothing this kernel stores
     // can alias it, so its wave-uniform reads may use scalar loads)
@@ -73,6 +73,13 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     // registers: there, staging K doubled its per-group scalar table reads,
     // which the halved occupancy could not hide - measured twice as slow.)
     constexpr bool KLDS = D <= 128 && (MODE == 0 || MODE == 3);
+    // Stages per wave of staged K and V tiles.  The 32 query rows of several
+    // new tokens do twice the matrix and softmax work per tile of a 16-row
+    // head block, which a single stage's refill latency then adds to: over a
+    // contiguous cache they get two stages (tile i + 2 loads while tile i is
+    // computed; spec_gqa 100.9 -> 91.3 us).  (A single-token group of 32
+    // heads, whose fused prologue leaves fewer registers, measured slower so.)
+    constexpr int NSTG = (KLDS && MQ && HB == 2 && MODE == 0) ? 2 : 1;
     // Tokens per wave tile: 16 where K is staged, else 32.  Half-height tiles
     // keep 8 KiB per wave (32 KiB per CU) in flight while a wave waits, the
     // amount a plain streaming read needed for its best rate on this part;
@@ -89,8 +96,9 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     // the compiler can tell the tile being read from the one being filled)
     // and K uses two operand arrays.
     __shared__ __attribute__((aligned(16))) char vbuf0[NW * STAGE];
-    __shared__ __attribute__((aligned(16))) char vbuf1[KLDS ? 16 : NW * STAGE];
+    __shared__ __attribute__((aligned(16))) char vbuf1[(KLDS && NSTG == 1) ? 16 : NW * STAGE];
     __shared__ __attribute__((aligned(16))) char kbuf[KLDS ? NW * STAGE : 16];
+    __shared__ __attribute__((aligned(16))) char kbuf1[NSTG == 2 ? NW * STAGE : 16];
     __shared__ int tbl_lds[MODE == 3 ? kTblMax : 1];
     static_assert(NW * STAGE >= 2 * NW * 16 * 4, "merge area (m, l)");
 
@@ -432,6 +440,7 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
         __syncthreads();
     }
     load_tile(base, ka0, kbuf, vbuf0);
+    if constexpr (NSTG == 2) load_tile(base + kStep, ka0, kbuf1, vbuf1);
 
     int patch_row = -1;                   // token index of the patched row, or -1
     size_t slot = 0;                      // element offset of the new token's row
@@ -507,8 +516,10 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     constexpr int kTileLoads = (KLDS ? VLOADS : 2 * KK) + VLOADS;
     static_assert(VLOADS + kTileLoads < 64, "vmcnt range");
     // Loads issued after this tile's V rows, before its V wait: the next
-    // tile's K rows (staged K), or the whole next tile.
-    constexpr int kAfterV = KLDS ? VLOADS : kTileLoads;
+    // tile's K rows (staged K; with two stages, also the following tile's V
+    // and the one after's K), or the whole next tile.
+    constexpr int kAfterV = KLDS ? (2 * NSTG - 1) * VLOADS : kTileLoads;
+    static_assert(kAfterV < 64, "vmcnt range");
 
     // A stage is refilled only once every LDS read of it has completed: a
     // direct load writes LDS when its data returns, outside the order of the
@@ -519,13 +530,15 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
         char* wbuf = buf + wave * STAGE;
         if constexpr (KLDS) {
             // this tile's K rows were issued before its V rows and nothing
-            // after those: at most VLOADS outstanding
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(VLOADS));
+            // after those (two stages: and the next tile's K and V): at most
+            // (2 NSTG - 1) VLOADS outstanding
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm((2 * NSTG - 1) * VLOADS));
             read_k(kb, ka);
-            // the K stage is free once those reads are done: the next
-            // tile's K rows go out now (past the split: zeros, no traffic)
+            // the K stage is free once those reads are done: the K rows of
+            // the tile NSTG steps ahead go out now (past the split: zeros,
+            // no traffic)
             __builtin_amdgcn_s_waitcnt(kLgkmZero);
-            load_rows(std::true_type{}, base + kStep, kb);
+            load_rows(std::true_type{}, base + NSTG * kStep, kb);
         }
         // the tile holding the new token (fused step): its key row goes into
         // the K operand here, its value row over the staged one below
@@ -646,9 +659,9 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
             }
         }
         if constexpr (KLDS) {
-            // the V stage is free: the next tile's V rows go out
+            // the V stage is free: the V rows of the tile NSTG steps ahead go out
             __builtin_amdgcn_s_waitcnt(kLgkmZero);
-            load_rows(std::false_type{}, base + kStep, buf);
+            load_rows(std::false_type{}, base + NSTG * kStep, buf);
         }
     };
 
@@ -660,7 +673,16 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     // clamped last row (paged) - so every path through the loop has the same
     // loads in flight and the waits stay exact.
     if (base < t_end) {
-        if constexpr (KLDS) {
+        if constexpr (KLDS && NSTG == 2) {
+            for (;;) {
+                compute_tile(ka0, kbuf, vbuf0, base);
+                base += kStep;
+                if (base >= t_end) break;
+                compute_tile(ka0, kbuf1, vbuf1, base);
+                base += kStep;
+                if (base >= t_end) break;
+            }
+        } else if constexpr (KLDS) {
             for (;;) {
                 compute_tile(ka0, kbuf, vbuf0, base);
                 base += kStep;

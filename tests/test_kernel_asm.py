@@ -68,25 +68,32 @@ def kernels_u8(text):
             yield m.group(1), int(m.group(2)), int(m.group(3)), [x.split(";")[0].strip() for x in lines[i + 1:end]]
 
 
-def kernels(text):
+def kernels(text, with_hb=False):
     """(mangled name, head_dim, cache mode, lines) of each streaming decode kernel
     (template arguments: head_dim, head blocks, waves, mode, fused), from its
-    label to the end of the function (blocks may follow an s_endpgm)."""
+    label to the end of the function (blocks may follow an s_endpgm); with
+    with_hb, (name, head_dim, mode, (head blocks, several new tokens), lines)."""
     lines = text.split("\n")
     for i, l in enumerate(lines):
-        m = re.match(r"^(_ZN3kvc\S*decode_mfma_kernelILi(\d+)ELi\d+ELi\d+ELi(\d+)E\S*):", l)
+        m = re.match(r"^(_ZN3kvc\S*decode_mfma_kernelILi(\d+)ELi(\d+)ELi\d+ELi(\d+)ELb\dELb(\d)E\S*):", l)
         if m:
             end = next(k for k in range(i, len(lines)) if lines[k].startswith(".Lfunc_end"))
-            yield m.group(1), int(m.group(2)), int(m.group(3)), [x.split(";")[0].strip() for x in lines[i + 1:end]]
+            body = [x.split(";")[0].strip() for x in lines[i + 1:end]]
+            if with_hb:
+                yield m.group(1), int(m.group(2)), int(m.group(4)), (int(m.group(3)), m.group(5) == "1"), body
+            else:
+                yield m.group(1), int(m.group(2)), int(m.group(4)), body
 
 
-def tile_loads(d, mode):
-    """Vector memory operations of one wave's tile: a contiguous cache up to
-    d = 128 stages 16-row tiles, K and V both by direct loads; otherwise
-    32-row tiles, K into registers (two 16-row blocks of d / 32 chunks)."""
+def tile_loads(d, mode, hb=1, mq=False):
+    """Vector memory operations one wave may have outstanding at a transposed
+    read: a contiguous cache up to d = 128 stages 16-row tiles, K and V both by
+    direct loads, one tile ahead (two head blocks of several new tokens' rows:
+    two tiles ahead); otherwise 32-row tiles, K into registers (two 16-row
+    blocks of d / 32 chunks)."""
     lanes_per_row = d // 8
     if mode == 0 and d <= 128:
-        return 2 * (16 * lanes_per_row // 64)
+        return 2 * (16 * lanes_per_row // 64) * (2 if hb == 2 and mq else 1)
     return 2 * (d // 32) + 32 * lanes_per_row // 64
 
 
@@ -188,9 +195,9 @@ def test_dataflow_sees_waits_on_back_edges():
 
 def test_transposed_reads_wait_for_their_tile(asm):
     seen = 0
-    for name, d, mode, body in kernels(asm):
+    for name, d, mode, (hb, mq), body in kernels(asm, with_hb=True):
         seen += 1
-        bad = unguarded_transposed_reads(body, tile_loads(d, mode))
+        bad = unguarded_transposed_reads(body, tile_loads(d, mode, hb, mq))
         assert not bad, f"{name}: transposed V reads with no wait for their tile's loads: {bad[:2]}"
     assert seen >= 12, "expected the decode kernel instantiations in the assembly"
 
