@@ -297,15 +297,7 @@ def bench_mla(args, W) -> dict:
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    t_start.record()
-    for i in range(args.steps):
-        step(i)
-    t_end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    step_ms = t_start.elapsed_time(t_end) / args.steps
+    step_ms, batch_stats, wall = timed_steps(step, args.steps)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for a, b in evs:
         a.record()
@@ -332,8 +324,13 @@ def bench_mla(args, W) -> dict:
                    "split_tokens": kvc.mla_split_tokens(w.B, w.H, w.d_latent, max_len, args.split_tokens),
                    "split_choice": "explicit" if args.split_tokens else "library"},
         "us_per_step": round(step_ms * 1e3, 2),
+        "step_ms_batches": batch_stats,
         "decode_us": round(dec_avg_ms * 1e3, 2),
         "decode_us_median": round(sorted(dec_ms)[len(dec_ms) // 2] * 1e3, 2),
+        # the absorbed form's score and PV multiply-adds: 4 * d_latent per
+        # (head, token)
+        "decode_tflops": round(4 * w.H * w.d_latent * int(x.seq_lens.sum()) / (dec_avg_ms * 1e-3) / 1e12, 2),
+        "flops_per_step": 4 * w.H * w.d_latent * int(x.seq_lens.sum()),
         "hbm_pct_step": round(100 * value / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -353,6 +350,31 @@ def bench_mla(args, W) -> dict:
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_mla(x, args.cpu_sample_seqs or 4)
     return res
+
+
+def timed_steps(step, steps: int, batches: int = 5):
+    """Time `steps` back-to-back steps between two events on the current
+    stream, with events at batch boundaries inside: (ms per step over all of
+    them, {median, min, max} ms per step over the batches)."""
+    import torch
+
+    n = max(1, min(batches, steps))
+    bounds = [round(k * steps / n) for k in range(n + 1)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    evs[0].record()
+    for k in range(n):
+        for i in range(bounds[k], bounds[k + 1]):
+            step(i)
+        evs[k + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    per = sorted(evs[k].elapsed_time(evs[k + 1]) / max(1, bounds[k + 1] - bounds[k]) for k in range(n))
+    total = evs[0].elapsed_time(evs[n]) / steps
+    stats = {"batches": n, "median_ms": round(per[len(per) // 2], 5), "min_ms": round(per[0], 5),
+             "max_ms": round(per[-1], 5)}
+    return total, stats, wall
 
 
 def check_kernel_timing(achieved_gbs: float, what: str) -> None:
@@ -516,17 +538,9 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # whole-step timing: K steps between two events, nothing else in between
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record()
-    for i in range(args.steps):
-        step(i)
-    t_end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    step_ms = t_start.elapsed_time(t_end) / args.steps
+    # whole-step timing: K steps back to back between two events (batch
+    # boundaries marked inside), nothing else in between
+    step_ms, batch_stats, wall = timed_steps(step, args.steps)
 
     # per-launch duration of the streaming decode kernel: events the library
     # records on its stream right before and after that kernel
@@ -547,6 +561,10 @@ def main():
     check_kernel_timing(achieved, w.name)
     value = kv_bytes / (step_ms * 1e-3) / 1e9
     traffic = None if (win or multi) else traffic_for_current_kernel(args.kv_cache, w.name)
+    # algorithmic flops: score and PV multiply-adds, 4 * d per (query head,
+    # attended token), for every new token's query
+    att = attended(x.seq_lens.tolist(), win + w.new_tokens - 1 if win else 0)
+    flops = 4 * w.d * w.H_q * w.new_tokens * int(sum(att))
     pool_tokens = x.k_cache.shape[0] * w.block_size if w.paged else 0
 
     res = {
@@ -578,8 +596,11 @@ def main():
                                                      args.split_tokens, pool_tokens=pool_tokens)),
                    "split_choice": "explicit" if args.split_tokens else "library"},
         "us_per_step": round(step_ms * 1e3, 2),
+        "step_ms_batches": batch_stats,
         "decode_us": round(dec_avg_ms * 1e3, 2),
         "decode_us_median": round(dec_med_ms * 1e3, 2),
+        "decode_tflops": round(flops / (dec_avg_ms * 1e-3) / 1e12, 2),
+        "flops_per_step": flops,
         "hbm_pct_step": round(100 * value / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
