@@ -218,7 +218,7 @@ struct MlaParams {
     const void* w_uv;            // bf16 [H * d_k, d_latent]
     const void* b_uv;            // bf16 [H * d_k] or NULL
     float* out;                  // [B, H, d_k]
-    float* qt;                   // [B, H, d_latent] absorbed queries times the scale (workspace)
+    float* qt;                   // absorbed queries times the scale as bf16 hi + lo planes, [2][B, H, d_latent] (workspace)
     float* ctx;                  // [B, H, d_latent] softmax-weighted latents (workspace)
     float2* ws_ml;               // [B * H, n_splits] (running max (log2), sum)
     float* ws_part;              // [B * H, n_splits, d_latent]

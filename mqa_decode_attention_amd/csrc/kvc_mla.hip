@@ -168,12 +168,23 @@ __global__ void __launch_bounds__(256) mla_absorb_kernel(const MlaParams p) {
         }
         // lane holds q~^T rows l0 + 16 wave + 4 q4 + e of column b; stored
         // times the softmax scale in log2 units (the streaming pass then
-        // computes scores ready for exp2)
+        // computes scores ready for exp2), already split into the hi + lo
+        // bf16 pair that pass feeds to the matrix cores (two planes: every
+        // hi part, then every lo part)
         const int bq = b0 + r16;
         const float sc = p.scale_log2;
-        if (bq < p.B)
-            *reinterpret_cast<float4*>(p.qt + (static_cast<size_t>(bq) * p.H + h) * DL + l0 + 16 * wave + 4 * q4) =
-                make_float4(acc[0] * sc, acc[1] * sc, acc[2] * sc, acc[3] * sc);
+        if (bq < p.B) {
+            const float v0 = acc[0] * sc, v1 = acc[1] * sc, v2 = acc[2] * sc, v3 = acc[3] * sc;
+            uint2 hi, lo;
+            hi.x = pack2_bf16(v0, v1);
+            hi.y = pack2_bf16(v2, v3);
+            lo.x = pack2_bf16(v0 - bf16_lo(hi.x), v1 - bf16_hi(hi.x));
+            lo.y = pack2_bf16(v2 - bf16_lo(hi.y), v3 - bf16_hi(hi.y));
+            uint16_t* qth = reinterpret_cast<uint16_t*>(p.qt);
+            const size_t at = (static_cast<size_t>(bq) * p.H + h) * DL + l0 + 16 * wave + 4 * q4;
+            *reinterpret_cast<uint2*>(qth + at) = hi;
+            *reinterpret_cast<uint2*>(qth + static_cast<size_t>(p.B) * p.H * DL + at) = lo;
+        }
     }
 }
 
@@ -261,18 +272,19 @@ mla_decode_kernel(const MlaParams p) {
         }
     };
 
-    // Absorbed queries (already scaled to log2 units) of the wave's head block
-    // and columns, as hi + lo B operands: lane holds head 16 hbw + r16,
-    // columns DW*cs + 32 kk + 8 q4 .. +7.  Heads past the chunk read zeros.
-    const __amdgpu_buffer_rsrc_t qrs =
-        make_uniform_rsrc(p.qt + (static_cast<size_t>(b) * p.H + h0) * DL, nh * DL * 4);
+    // Absorbed queries (already scaled to log2 units and split into hi + lo
+    // planes) of the wave's head block and columns, as B operands: lane holds
+    // head 16 hbw + r16, columns DW*cs + 32 kk + 8 q4 .. +7.  Heads past the
+    // chunk read zeros.
+    const uint16_t* qth = reinterpret_cast<const uint16_t*>(p.qt) + (static_cast<size_t>(b) * p.H + h0) * DL;
+    const __amdgpu_buffer_rsrc_t qhr = make_uniform_rsrc(qth, nh * DL * 2);
+    const __amdgpu_buffer_rsrc_t qlr = make_uniform_rsrc(qth + static_cast<size_t>(p.B) * p.H * DL, nh * DL * 2);
     uint4 qh[KKW], ql[KKW];
 #pragma unroll
     for (int kk = 0; kk < KKW; ++kk) {
-        const int off = ((16 * hbw + r16) * DL + DW * cs + 32 * kk + 8 * q4) * 4;
-        const float4 a = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0));
-        const float4 c = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(qrs, off + 16, 0, 0));
-        split8(a, c, qh[kk], ql[kk]);
+        const int off = ((16 * hbw + r16) * DL + DW * cs + 32 * kk + 8 * q4) * 2;
+        qh[kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(qhr, off, 0, 0));
+        ql[kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(qlr, off, 0, 0));
     }
 
     // Running max m (log2 units) and sum l of the lane's head; X^T accumulators.
