@@ -122,9 +122,18 @@ def calibrate_copy(nbytes: int) -> None:
     print(json.dumps({"calibration_copy_bytes": nbytes, "copies": 5}))
 
 
-def cpu_baseline(x, n_seqs, window=0):
-    """Time the CPU oracle (as it stands, one thread) on the same step's inputs
-    (with a window: the sliding-window oracle over the full cache)."""
+def cpu_threads() -> int:
+    """Host threads for the all-cores oracle figure: the CPUs this process may
+    run on, at most OMP_NUM_THREADS (the share of the host one GPU gets)."""
+    n = len(os.sched_getaffinity(0))
+    cap = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    return max(1, min(n, cap) if cap > 0 else n)
+
+
+def cpu_baseline(x, n_seqs, window=0, threads=1):
+    """Time the CPU oracle (as it stands; numpy with `threads` BLAS threads) on
+    the same step's inputs (with a window: the sliding-window oracle over the
+    full cache)."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -145,7 +154,7 @@ def cpu_baseline(x, n_seqs, window=0):
     q, kn, vn = np_store(x.q[:B]), np_store(x.k_new[:B]), np_store(x.v_new[:B])
     cos, sin = x.rope_cos.numpy(), x.rope_sin.numpy()
     cached = x.cached.numpy()[:B]
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=threads):
         t0 = time.perf_counter()
         k2, v2, q2 = O.append_contiguous(kc, vc, cached, kn, vn, cos, sin, dt, q=q)
         if window:
@@ -156,8 +165,9 @@ def cpu_baseline(x, n_seqs, window=0):
         sec = time.perf_counter() - t0
     nbytes = kv_read_bytes(attended(cached + 1, window), w.H_kv, w.d, 2 if dt == "bf16" else 4)
     what = f"append + attention over the last {window} tokens" if window else "append + attention"
-    return {"value": round(nbytes / sec / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{B} of {w.B} sequences of {w.name} ({what}, float64, numpy, one thread), {sec:.2f} s"}
+    how = "one thread" if threads == 1 else f"{threads} BLAS threads"
+    return {"value": round(nbytes / sec / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{B} of {w.B} sequences of {w.name} ({what}, float64, numpy, {how}), {sec:.2f} s"}
 
 
 def cpu_baseline_multi(x, n_seqs, window=0):
@@ -622,6 +632,9 @@ def main():
     if not args.no_cpu_baseline and not w.paged:
         res["cpu_baseline"] = cpu_baseline_u8(x, qc, args.cpu_sample_seqs) if u8 else \
             cpu_baseline_multi(x, args.cpu_sample_seqs, win) if multi else cpu_baseline(x, args.cpu_sample_seqs, win)
+        if not u8 and not multi and cpu_threads() > 1:
+            # the same oracle with the host's cores for its BLAS calls (information)
+            res["cpu_baseline_threads"] = cpu_baseline(x, args.cpu_sample_seqs, win, threads=cpu_threads())
     print(json.dumps(res), flush=True)
 
 
