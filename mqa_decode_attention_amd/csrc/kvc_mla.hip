@@ -132,39 +132,66 @@ __global__ void __launch_bounds__(256) mla_absorb_kernel(const MlaParams p) {
     const int s16 = lane & 15;
     const int trow = 4 * q4 + s16 / 4;
     const int tcol = 16 * wave + 4 * (s16 % 4);
-    const int KK = p.d_k / 32;
+    const int KK = p.d_k / 32;            // <= 16; also the W_uk loads per thread
+    const int nq = 16 * dk8;              // 16-byte chunks of 16 query rows (<= 4 per thread)
     for (int b0 = 0; b0 < p.B; b0 += 16) {
         if (b0 > 0) __syncthreads();      // the previous block's reads of qs are done
+        // Every global load of the block is issued before the first LDS
+        // store (loops with a run-time trip count would wait for each load
+        // in turn): the W_uk tile (first block only), then the query rows.
+        // (W_uk through a buffer resource ending at row d_k: the loads need no
+        // guard, and those past it return zeros without a memory access)
+        uint4 wv[16], qv[4];
         if (b0 == 0) {
-            for (int idx = tid; idx < p.d_k * 8; idx += 256) {
-                const int i = idx >> 3, c = idx & 7;
-                wt[idx] = *reinterpret_cast<const uint4*>(wk + static_cast<size_t>(i) * DL + 8 * c);
+            const __amdgpu_buffer_rsrc_t wrs = make_uniform_rsrc(wk, ((p.d_k - 1) * DL + 64) * 2);
+#pragma unroll
+            for (int it = 0; it < 16; ++it) {
+                const int idx = tid + 256 * it;
+                wv[it] = __builtin_bit_cast(
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(wrs, ((idx >> 3) * DL + 8 * (idx & 7)) * 2, 0, 0));
             }
         }
-        for (int idx = tid; idx < 16 * dk8; idx += 256) {
-            const int r = idx / dk8, c = idx - (idx / dk8) * dk8;
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int idx = tid + 256 * it;
+            const int r = idx / dk8, c = idx - r * dk8;
             const int bq = b0 + r;
-            qs[r * qp + c] = bq < p.B ? *reinterpret_cast<const uint4*>(
-                                            qb + (static_cast<size_t>(bq) * p.H + h) * p.d_k + 8 * c)
-                                      : make_uint4(0, 0, 0, 0);
+            qv[it] = (idx < nq && bq < p.B)
+                         ? *reinterpret_cast<const uint4*>(qb + (static_cast<size_t>(bq) * p.H + h) * p.d_k + 8 * c)
+                         : make_uint4(0, 0, 0, 0);
+        }
+        if (b0 == 0) {
+#pragma unroll
+            for (int it = 0; it < 16; ++it)
+                if (it < KK) wt[tid + 256 * it] = wv[it];
+        }
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int idx = tid + 256 * it;
+            const int r = idx / dk8, c = idx - r * dk8;
+            if (idx < nq) qs[r * qp + c] = qv[it];
         }
         __syncthreads();
         f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
         const char* qrow = qsb + r16 * qp * 16;
-        for (int kk = 0; kk < KK; ++kk) {
-            const int r0 = 32 * kk + trow;
-            const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(wtb + r0 * 128 + 2 * tcol));
-            const s16x4_t hi =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(wtb + (r0 + 16) * 128 + 2 * tcol));
-            uint4 va;
-            va.x = __builtin_bit_cast(uint2, lo).x;
-            va.y = __builtin_bit_cast(uint2, lo).y;
-            va.z = __builtin_bit_cast(uint2, hi).x;
-            va.w = __builtin_bit_cast(uint2, hi).y;
-            // B operand: q[b, h, i] for i = 32 kk + 4 q4 + (0..3) and 16 + that
-            const uint2 qa = *reinterpret_cast<const uint2*>(qrow + 2 * (32 * kk + 4 * q4));
-            const uint2 qc = *reinterpret_cast<const uint2*>(qrow + 2 * (32 * kk + 16 + 4 * q4));
-            acc = mfma16(va, make_uint4(qa.x, qa.y, qc.x, qc.y), acc);
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+            if (kk < KK) {
+                const int r0 = 32 * kk + trow;
+                const s16x4_t lo =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(wtb + r0 * 128 + 2 * tcol));
+                const s16x4_t hi =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(wtb + (r0 + 16) * 128 + 2 * tcol));
+                uint4 va;
+                va.x = __builtin_bit_cast(uint2, lo).x;
+                va.y = __builtin_bit_cast(uint2, lo).y;
+                va.z = __builtin_bit_cast(uint2, hi).x;
+                va.w = __builtin_bit_cast(uint2, hi).y;
+                // B operand: q[b, h, i] for i = 32 kk + 4 q4 + (0..3) and 16 + that
+                const uint2 qa = *reinterpret_cast<const uint2*>(qrow + 2 * (32 * kk + 4 * q4));
+                const uint2 qc = *reinterpret_cast<const uint2*>(qrow + 2 * (32 * kk + 16 + 4 * q4));
+                acc = mfma16(va, make_uint4(qa.x, qa.y, qc.x, qc.y), acc);
+            }
         }
         // lane holds q~^T rows l0 + 16 wave + 4 q4 + e of column b; stored
         // times the softmax scale in log2 units (the streaming pass then
@@ -515,20 +542,29 @@ __global__ void __launch_bounds__(64) mla_up_kernel(const MlaParams p) {
     uint4 wa[KK];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) wa[kk] = *reinterpret_cast<const uint4*>(wrow + 32 * kk);
-    float bias[4];
+    // the bias, read unconditionally (from W_uv when there is none, then
+    // replaced by 0) so that no branch separates the loads from each other
     const uint16_t* bv = static_cast<const uint16_t*>(p.b_uv);
+    const uint16_t* bsrc = bv ? bv + static_cast<size_t>(h) * p.d_k + i0 + 4 * q4 : wrow;
+    uint16_t braw[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) bias[e] = bv ? bf16_bits_to_f32(bv[static_cast<size_t>(h) * p.d_k + i0 + 4 * q4 + e]) : 0.0f;
+    for (int e = 0; e < 4; ++e) braw[e] = bsrc[e];
     for (int b0 = 0; b0 < p.B; b0 += 16) {
         const int bq = b0 + r16;
         const bool bok = bq < p.B;
-        const bool empty = !bok || mla_len_lane(p, bok ? bq : b0) == 0;   // length 0: zeros
         const float* xr = p.ctx + (static_cast<size_t>(bok ? bq : 0) * p.H + h) * DL + 8 * q4;
+        // all of the block's x rows requested at once, then its length
+        float4 xa[KK], xc[KK];
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            xa[kk] = *reinterpret_cast<const float4*>(xr + 32 * kk);
+            xc[kk] = *reinterpret_cast<const float4*>(xr + 32 * kk + 4);
+        }
+        const bool empty = !bok || mla_len_lane(p, bok ? bq : b0) == 0;   // length 0: zeros
         f32x4_t acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-            float4 a = *reinterpret_cast<const float4*>(xr + 32 * kk);
-            float4 c = *reinterpret_cast<const float4*>(xr + 32 * kk + 4);
+            float4 a = xa[kk], c = xc[kk];
             if (!bok) a = c = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             uint4 xh, xl;
             split8(a, c, xh, xl);
@@ -536,6 +572,9 @@ __global__ void __launch_bounds__(64) mla_up_kernel(const MlaParams p) {
             acc[kk & 1] = mfma16(wa[kk], xl, acc[kk & 1]);
         }
         const f32x4_t r4 = acc[0] + acc[1];
+        float bias[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bias[e] = bv ? bf16_bits_to_f32(braw[e]) : 0.0f;
         if (bok) {
             float4 r;
             r.x = empty ? 0.0f : r4[0] + bias[0];
