@@ -584,11 +584,8 @@ kvc_status decode_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const
         p.capacity = paged ? block_size * max_blocks_per_seq : (ring ? 0x7FFFFFFF : T_max);
         p.seq_lens = nullptr;
         if (!fused) {
-            // no fused kernel for this shape (or a ring cache): rotated q into
-            // q_rot_out, append, then attend
-            const size_t qbytes = static_cast<size_t>(B) * H_q * d * elem_bytes(dtype);
-            e = hipMemcpyAsync(step->q_rot_out, q, qbytes, hipMemcpyDeviceToDevice, hs);
-            if (e != hipSuccess) return hip_status(e, "kvc_decode_step query copy");
+            // no fused kernel for this shape (or a ring cache): the append
+            // (which also rotates q into q_rot_out), then the attention
             kvc::AppendParams ap{};
             ap.dtype = dtype;
             ap.B = B; ap.H_q = H_q; ap.H_kv = H_kv; ap.d = d;
@@ -597,7 +594,7 @@ kvc_status decode_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const
             ap.max_blocks_per_seq = max_blocks_per_seq; ap.num_blocks = num_blocks;
             ap.capacity = p.capacity;
             ap.positions = step->positions;
-            ap.k_new = step->k_new; ap.v_new = step->v_new; ap.q_inout = step->q_rot_out;
+            ap.k_new = step->k_new; ap.v_new = step->v_new; ap.q_inout = step->q_rot_out; ap.q_in = q;
             ap.rope_cos = step->rope_cos; ap.rope_sin = step->rope_sin;
             ap.rope_rows = step->rope_rows; ap.rope_style = step->rope_style;
             ap.ring = p.ring;

@@ -41,8 +41,8 @@ struct Store<uint16_t> {
 // One thread per (sequence, new token, vector, pair).  Vectors of token bt =
 // b * qlen + t, in order: the H_kv keys (rotated into the cache), the H_kv
 // values (copied into the cache), then, when q_inout is given, the H_q
-// queries (rotated in place).  Token t of sequence b takes position
-// positions[b] + t.
+// queries (rotated in place, or from q_in into q_inout).  Token t of
+// sequence b takes position positions[b] + t.
 template <typename T>
 __global__ void __launch_bounds__(256) append_kernel(const AppendParams p) {
     const int half = p.d >> 1;
@@ -56,8 +56,26 @@ __global__ void __launch_bounds__(256) append_kernel(const AppendParams p) {
     const int bt = static_cast<int>(idx / (static_cast<long long>(half) * nvec));
     const int b = bt / qlen;
 
+    int e0, e1;
+    if (p.rope_style == KVC_ROPE_HALF) { e0 = i; e1 = i + half; }
+    else { e0 = 2 * i; e1 = 2 * i + 1; }
+
+    // A token whose slot is invalid stores nothing; a query read from q_in
+    // still reaches q_inout, unrotated (as a copy rotated in place is left).
+    auto pass_query = [&]() {
+        if (p.q_in && vec >= 2 * p.H_kv) {
+            const size_t off = (static_cast<size_t>(bt) * p.H_q + (vec - 2 * p.H_kv)) * p.d;
+            const T* src = static_cast<const T*>(p.q_in) + off;
+            T* dst = static_cast<T*>(p.q_inout) + off;
+            dst[e0] = src[e0];
+            dst[e1] = src[e1];
+        }
+    };
     const long long pos_ll = static_cast<long long>(p.positions[b]) + (bt - b * qlen);
-    if (pos_ll < 0 || pos_ll >= p.capacity || pos_ll >= p.rope_rows) return;
+    if (pos_ll < 0 || pos_ll >= p.capacity || pos_ll >= p.rope_rows) {
+        pass_query();
+        return;
+    }
     const int pos = static_cast<int>(pos_ll);
 
     // slot of (b, head j) in the cache, in elements, for head 0; + j * head stride
@@ -65,7 +83,10 @@ __global__ void __launch_bounds__(256) append_kernel(const AppendParams p) {
     size_t head_stride;
     if (p.block_table) {
         const int blk = p.block_table[static_cast<size_t>(b) * p.max_blocks_per_seq + pos / p.block_size];
-        if (blk < 0 || blk >= p.num_blocks) return;
+        if (blk < 0 || blk >= p.num_blocks) {
+            pass_query();
+            return;
+        }
         slot0 = (static_cast<size_t>(blk) * p.H_kv * p.block_size + pos % p.block_size) * p.d;
         head_stride = static_cast<size_t>(p.block_size) * p.d;
     } else {
@@ -73,10 +94,6 @@ __global__ void __launch_bounds__(256) append_kernel(const AppendParams p) {
         slot0 = (static_cast<size_t>(b) * p.H_kv * p.T_max + (p.ring ? pos % p.T_max : pos)) * p.d;
         head_stride = static_cast<size_t>(p.T_max) * p.d;
     }
-
-    int e0, e1;
-    if (p.rope_style == KVC_ROPE_HALF) { e0 = i; e1 = i + half; }
-    else { e0 = 2 * i; e1 = 2 * i + 1; }
 
     if (vec >= p.H_kv && vec < 2 * p.H_kv) {  // value: bit copy of both elements
         const int j = vec - p.H_kv;
@@ -96,8 +113,9 @@ __global__ void __launch_bounds__(256) append_kernel(const AppendParams p) {
         dst = static_cast<T*>(p.k_cache) + slot0 + vec * head_stride;
     } else {
         const int h = vec - 2 * p.H_kv;
-        dst = static_cast<T*>(p.q_inout) + (static_cast<size_t>(bt) * p.H_q + h) * p.d;
-        src = dst;
+        const size_t off = (static_cast<size_t>(bt) * p.H_q + h) * p.d;
+        dst = static_cast<T*>(p.q_inout) + off;
+        src = p.q_in ? static_cast<const T*>(p.q_in) + off : dst;
     }
     const float x0 = Store<T>::load(src, e0);
     const float x1 = Store<T>::load(src, e1);
@@ -156,7 +174,8 @@ __global__ void __launch_bounds__(256) append_u8_kernel(const AppendParams p) {
     const bool is_query = vec >= 2 * p.H_kv;
     const int j = is_key ? vec : vec - p.H_kv;
     const T* src;
-    if (is_query) src = static_cast<const T*>(p.q_inout) + (static_cast<size_t>(b) * p.H_q + vec - 2 * p.H_kv) * p.d;
+    if (is_query)
+        src = static_cast<const T*>(p.q_in ? p.q_in : p.q_inout) + (static_cast<size_t>(b) * p.H_q + vec - 2 * p.H_kv) * p.d;
     else src = static_cast<const T*>(is_key ? p.k_new : p.v_new) + (static_cast<size_t>(b) * p.H_kv + j) * p.d;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {

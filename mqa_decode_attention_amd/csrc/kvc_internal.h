@@ -24,6 +24,7 @@ struct AppendParams {
     const void* k_new;
     const void* v_new;
     void* q_inout;
+    const void* q_in;            // NULL: q_inout is rotated in place; else read from here, rotated into q_inout
     const float* rope_cos;
     const float* rope_sin;
     int rope_rows;

@@ -85,6 +85,32 @@ def test_step_out_of_range_positions_write_nothing():
     compare_out(out[:1], O.decode_attention(q2, k2, v2, [11], "bf16"), "bf16", "valid sequence")
 
 
+def test_step_append_kernel_path_out_of_range_positions():
+    """The step through the separate append kernel (float32 here): the query of
+    a sequence whose slot is outside the cache reaches q_rot_out unrotated,
+    as the documented append-on-a-copy would leave it; the others rotated."""
+    w = W.WORKLOADS["tiny_mha"].replace(B=3, cached_lo=5, cached_hi=5, T_max=8)
+    x = W.draw(w)
+    x.cached[:] = torch.tensor([5, 8, -1], dtype=torch.int32)       # 8 == T_max: outside the cache
+    say("[step tiny f32] out-of-range positions")
+    s = GpuStep(x)
+    s.max_len = 8
+    k0, v0 = bits(s.k), bits(s.v)
+    k, v, q_rot, out = run_step(s)
+    torch.cuda.synchronize()
+    qb = bits(q_rot).reshape(3, -1)
+    assert np.array_equal(qb[1:], bits(x.q).reshape(3, -1)[1:]), "unrotated query expected"
+    kb, vb = bits(k).reshape(3, -1), bits(v).reshape(3, -1)
+    assert np.array_equal(kb[1:], k0.reshape(3, -1)[1:]) and np.array_equal(vb[1:], v0.reshape(3, -1)[1:])
+    assert np.all(store_np(out, "f32")[1:] == 0)
+    k2, v2, q2 = O.append_contiguous(store_np(x.k_cache[:1], "f32"), store_np(x.v_cache[:1], "f32"),
+                                     x.cached.numpy()[:1], store_np(x.k_new[:1], "f32"),
+                                     store_np(x.v_new[:1], "f32"), x.rope_cos.numpy(), x.rope_sin.numpy(),
+                                     "f32", q=store_np(x.q[:1], "f32"))
+    assert np.array_equal(qb[:1], np.ascontiguousarray(q2).view(np.uint8).reshape(1, -1)), "rotated q differs"
+    compare_out(out[:1], O.decode_attention(q2, k2, v2, [6], "f32"), "f32", "valid sequence")
+
+
 def _sample_groups(w, n, seed):
     rng = np.random.default_rng(seed)
     pairs = {(0, 0), (w.B - 1, w.H_kv - 1)}
