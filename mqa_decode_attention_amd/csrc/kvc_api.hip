@@ -571,6 +571,8 @@ kvc_status decode_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const
     // the append runs inside the matrix-core kernel, except for a ring (the new
     // token's slot is not the last attended row there)
     const bool fused = step != nullptr && pl.mfma && !ring;
+    // ... and inside the vector kernel for a contiguous cache (one new token)
+    const bool valu_step = step != nullptr && !pl.mfma && !ring && !paged && qlen <= 1;
     if (step) {
         p.positions = step->positions;
         p.k_new = step->k_new;
@@ -583,7 +585,8 @@ kvc_status decode_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const
         p.rope_style = step->rope_style;
         p.capacity = paged ? block_size * max_blocks_per_seq : (ring ? 0x7FFFFFFF : T_max);
         p.seq_lens = nullptr;
-        if (!fused) {
+        p.valu_step = valu_step ? 1 : 0;
+        if (!fused && !valu_step) {
             // no fused kernel for this shape (or a ring cache): the append
             // (which also rotates q into q_rot_out), then the attention
             kvc::AppendParams ap{};

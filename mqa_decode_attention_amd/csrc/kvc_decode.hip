@@ -69,6 +69,21 @@ __device__ __forceinline__ void store_out<float>(void* out, size_t i, float x) {
     static_cast<float*>(out)[i] = x;
 }
 
+// One element of the storage type as float32, and back (round to nearest
+// even for bf16), as the append kernel reads and writes them.
+template <typename T>
+struct Store;
+template <>
+struct Store<float> {
+    __device__ static float load(const float* a, size_t i) { return a[i]; }
+    __device__ static void store(float* a, size_t i, float x) { a[i] = x; }
+};
+template <>
+struct Store<uint16_t> {
+    __device__ static float load(const uint16_t* a, size_t i) { return bf16_bits_to_f32(a[i]); }
+    __device__ static void store(uint16_t* a, size_t i, float x) { a[i] = f32_to_bf16_rne(x); }
+};
+
 // Partial dot product of one 16-byte K chunk with one query head's chunk.
 template <typename T>
 struct Dot;
@@ -122,6 +137,11 @@ decode_split_kernel(const DecodeParams p) {
     __shared__ float sm_acc[NW][GC][D];
     __shared__ float sm_m[NW][GC];
     __shared__ float sm_l[NW][GC];
+    // decode step (p.valu_step): the chunk's rotated queries and the new
+    // token's rotated key and value, in the storage type
+    __shared__ __attribute__((aligned(16))) T sm_q[GC * D];
+    __shared__ __attribute__((aligned(16))) T sm_kn[D];
+    __shared__ __attribute__((aligned(16))) T sm_vn[D];
 
     const int wid = xcd_logical_id(blockIdx.x, p.n_wg, p.n_wg_pad);
     if (wid < 0) return;
@@ -146,10 +166,77 @@ decode_split_kernel(const DecodeParams p) {
     const int el0 = (lane % LPT) * EPL;         // first head_dim element of this lane
     const int h0 = j * p.G + chunk * GC;        // first query head of the chunk
 
+    // Decode step without a separate append: the workgroup rotates its
+    // chunk's queries, and the split holding the new token's slot also that
+    // token's key, with the append's operation sequence and rounding (into
+    // LDS).  That split reads the new row from LDS in place of the cache
+    // row, whose store (chunk 0) nothing in this launch reads back; split 0
+    // stores the rotated queries.  A slot outside the cache or the rotation
+    // table stores nothing and passes the query through unrotated.
+    int pos = -1;
+    bool holds = false;
+    if (p.valu_step) {
+        constexpr int HALF = D / 2;
+        pos = p.positions[b];
+        const bool pos_ok = pos >= 0 && pos < p.capacity && pos < p.rope_rows;
+        holds = pos_ok && pos >= t_begin && pos < t_end;
+        auto ld = [](const T* a, int i) { return Store<T>::load(a, i); };
+        auto pair_at = [&](int i, int& e0, int& e1) {
+            if (p.rope_style == KVC_ROPE_HALF) { e0 = i; e1 = i + HALF; }
+            else { e0 = 2 * i; e1 = 2 * i + 1; }
+        };
+        const T* qsrc = static_cast<const T*>(p.q_raw) + (static_cast<size_t>(b) * p.H_q + h0) * D;
+        for (int idx = tid; idx < GC * HALF; idx += NT) {
+            const int g = idx / HALF, i = idx % HALF;
+            int e0, e1;
+            pair_at(i, e0, e1);
+            const float x0 = ld(qsrc + g * D, e0), x1 = ld(qsrc + g * D, e1);
+            float r0 = x0, r1 = x1;
+            if (pos_ok)
+                rope_pair(x0, x1, p.rope_cos[static_cast<size_t>(pos) * HALF + i],
+                          p.rope_sin[static_cast<size_t>(pos) * HALF + i], r0, r1);
+            Store<T>::store(sm_q + g * D, e0, r0);
+            Store<T>::store(sm_q + g * D, e1, r1);
+        }
+        if (holds) {
+            const T* ksrc = static_cast<const T*>(p.k_new) + (static_cast<size_t>(b) * p.H_kv + j) * D;
+            const T* vsrc = static_cast<const T*>(p.v_new) + (static_cast<size_t>(b) * p.H_kv + j) * D;
+            for (int i = tid; i < HALF; i += NT) {
+                int e0, e1;
+                pair_at(i, e0, e1);
+                float r0, r1;
+                rope_pair(ld(ksrc, e0), ld(ksrc, e1), p.rope_cos[static_cast<size_t>(pos) * HALF + i],
+                          p.rope_sin[static_cast<size_t>(pos) * HALF + i], r0, r1);
+                Store<T>::store(sm_kn, e0, r0);
+                Store<T>::store(sm_kn, e1, r1);
+            }
+            for (int e = tid; e < D; e += NT) sm_vn[e] = vsrc[e];
+        }
+        __syncthreads();
+        if (split == 0 && p.q_rot_out) {
+            T* qdst = static_cast<T*>(p.q_rot_out) + (static_cast<size_t>(b) * p.H_q + h0) * D;
+            for (int idx = tid; idx < GC * D; idx += NT) qdst[idx] = sm_q[idx];
+        }
+        if (holds && chunk == 0) {
+            const size_t slot = ((static_cast<size_t>(b) * p.H_kv + j) * p.T_max + pos) * D;
+            for (int e = tid; e < D; e += NT) {
+                static_cast<T*>(const_cast<void*>(p.k))[slot + e] = sm_kn[e];
+                static_cast<T*>(const_cast<void*>(p.v))[slot + e] = sm_vn[e];
+            }
+        }
+    }
+
     typename Dot<T>::QReg qr[GC];
 #pragma unroll
     for (int g = 0; g < GC; ++g)
-        qr[g] = Dot<T>::load_q(p.q, (static_cast<size_t>(b) * p.H_q + h0 + g) * D + el0);
+        qr[g] = p.valu_step ? Dot<T>::load_q(sm_q, static_cast<size_t>(g) * D + el0)
+                            : Dot<T>::load_q(p.q, (static_cast<size_t>(b) * p.H_q + h0 + g) * D + el0);
+    // the new row, for the split that holds it
+    uint4 k_new_row = make_uint4(0, 0, 0, 0), v_new_row = make_uint4(0, 0, 0, 0);
+    if (holds) {
+        k_new_row = *reinterpret_cast<const uint4*>(sm_kn + el0);
+        v_new_row = *reinterpret_cast<const uint4*>(sm_vn + el0);
+    }
 
     float m[GC], l[GC], acc[GC][EPL];
 #pragma unroll
@@ -183,6 +270,10 @@ decode_split_kernel(const DecodeParams p) {
             }
             kr[u] = *reinterpret_cast<const uint4*>(kbase + off + el0);
             vr[u] = *reinterpret_cast<const uint4*>(vbase + off + el0);
+            if (holds && tc == pos) {
+                kr[u] = k_new_row;
+                vr[u] = v_new_row;
+            }
         }
 
         float s[U][GC];

@@ -88,6 +88,7 @@ struct DecodeParams {
     const float* rope_sin;
     int rope_rows, rope_style;
     int capacity;                // tokens addressable per sequence
+    int valu_step;               // the vector kernel does the step's append itself (contiguous cache)
 
     // Sliding window: a sequence holding L tokens attends [max(0, L - window), L)
     // (window 0: all of them); ring: the cache is a ring of T_max slots (token t
