@@ -232,8 +232,10 @@ kvc_status kvc_decode_attn_paged(kvc_dtype dtype, int B, int H_q, int H_kv, int 
  * G <= 32 the append runs inside the streaming attention kernel (q is
  * rotated in registers; the workgroup whose split holds the new token uses
  * the rotated key and the value from registers for that token and stores
- * them to the cache after its pass); other shapes run the append kernel
- * first.
+ * them to the cache after its pass).  Over a contiguous cache the vector
+ * kernel of the other shapes does the same (queries and the new key rotated
+ * in LDS).  A paged cache without the matrix-core kernel, and a ring, run
+ * the append kernel first.
  *
  * q is the raw query [B, H_q, d] (not modified); q_rot_out [B, H_q, d]
  * (required) receives the rotated query.  Cache arguments as in kvc_append
