@@ -381,8 +381,6 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(const DecodeParams p)
     // output row bh = (b * qlen + i) * H_q + h
     if (bh >= static_cast<long long>(p.B) * p.qlen * p.H_q) return;
     const int b = static_cast<int>(bh / (static_cast<long long>(p.qlen) * p.H_q));
-    const int nsp = split_count(p, token_range(p, attended_len(p, b)));
-    if (nsp <= 1) return;                        // written directly by the split kernel
     const float2* ml = p.ws_ml + bh * p.n_splits;
     const float4* part = reinterpret_cast<const float4*>(p.ws_part + bh * p.n_splits * D);
     const int c4 = lane % C4;
@@ -393,17 +391,30 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(const DecodeParams p)
     float4 pv[KU];
     float2 mv[KU];
     bool live[KU];
-    auto fetch = [&](int pass0) {
+    auto fetch = [&](int pass0, int n) {
 #pragma unroll
         for (int u = 0; u < KU; ++u) {
             const int sp = (pass0 + u) * SPL + sub;
-            live[u] = sp < nsp;
-            const int spc = live[u] ? sp : nsp - 1;
+            live[u] = sp < n;
+            const int spc = live[u] ? sp : n - 1;
             pv[u] = part[static_cast<size_t>(spc) * C4 + c4];
             mv[u] = ml[spc];
         }
     };
-    fetch(0);
+    // The first passes are requested before the sequence's length is known
+    // (over all n_splits slots of the workspace; those past the sequence's
+    // splits are masked once it is), so the two round trips overlap.
+    fetch(0, p.n_splits);
+    const int nsp = split_count(p, token_range(p, attended_len(p, b)));
+    if (nsp <= 1) return;                        // written directly by the split kernel
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+        live[u] = u * SPL + sub < nsp;
+        if (!live[u]) {                          // (unwritten slots may hold anything)
+            pv[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            mv[u] = make_float2(-INFINITY, 0.0f);
+        }
+    }
     float M = -INFINITY;
     for (int sp = lane; sp < nsp + 63; sp += 64) M = fmaxf(M, ml[sp < nsp ? sp : nsp - 1].x);
     M = across_groups_max<1>(M);
@@ -422,7 +433,7 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(const DecodeParams p)
         }
         pass0 += KU;
         if (pass0 * SPL >= nsp) break;
-        fetch(pass0);
+        fetch(pass0, nsp);
     }
 #pragma unroll
     for (int off = C4; off < 64; off <<= 1) {
