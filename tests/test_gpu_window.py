@@ -172,10 +172,11 @@ def test_ring_append_and_decode(dtype):
         compare_out(out, ref, dtype, f"ring {dtype} split={split}")
 
 
-@pytest.mark.parametrize("name", ["gqa_8b", "paged_gqa", "mqa_ragged"])
+@pytest.mark.parametrize("name", ["gqa_8b", "paged_gqa", "mqa_ragged", "gqa_f32"])
 def test_step_window(name):
     """The fused step with a window == oracle append + windowed decode, and ==
-    kvc_append + kvc_decode_attn_window bit for bit."""
+    kvc_append + kvc_decode_attn_window bit for bit (gqa_f32: the vector
+    kernel, which does the append itself over a contiguous cache)."""
     window = 100
     x = W.draw(SMALL[name])
     poison_before_window(x, window)
