@@ -77,6 +77,25 @@ __device__ __forceinline__ void split8(const float4& a, const float4& b, uint4& 
     lo.w = pack2_bf16(b.z - bf16_lo(hi.w), b.w - bf16_hi(hi.w));
 }
 
+// Bit copy of one new row [c_kv | k_rope] (row = DL + rd elements) into dst by
+// nt threads: each pass requests four elements per thread before storing any
+// (indices clamped to the row, so the loads need no branch).
+template <typename T>
+__device__ __forceinline__ void copy_new_row(T* dst, const T* cn, const T* rn, int DL, int rd, int tid, int nt) {
+    const int row = DL + rd;
+    for (int e0 = tid; e0 < row; e0 += 4 * nt) {
+        T v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int e = min(e0 + k * nt, row - 1);
+            v[k] = *(e < DL ? cn + e : rn + (e - DL));
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (e0 + k * nt < row) dst[e0 + k * nt] = v[k];
+    }
+}
+
 // Workgroup barrier that orders nothing by itself: the callers wait for their
 // own LDS and direct-load traffic explicitly first.  (The memory clobber keeps
 // the compiler from moving memory operations across it.)
@@ -104,11 +123,10 @@ __global__ void __launch_bounds__(256) mla_absorb_kernel(const MlaParams p) {
         if (!p.c_new || b >= p.B) return;
         const int pos = p.positions[b];
         if (pos < 0 || pos >= p.T_max) return;
-        const uint16_t* cn = static_cast<const uint16_t*>(p.c_new);
-        const uint16_t* rn = static_cast<const uint16_t*>(p.r_new);
+        const uint16_t* cn = static_cast<const uint16_t*>(p.c_new) + static_cast<size_t>(b) * DL;
+        const uint16_t* rn = static_cast<const uint16_t*>(p.r_new) + static_cast<size_t>(b) * p.rope_dim;
         uint16_t* dst = static_cast<uint16_t*>(p.cache) + (static_cast<size_t>(b) * p.T_max + pos) * p.row;
-        for (int e = tid; e < p.row; e += blockDim.x)
-            dst[e] = e < DL ? cn[static_cast<size_t>(b) * DL + e] : rn[static_cast<size_t>(b) * p.rope_dim + e - DL];
+        copy_new_row(dst, cn, rn, DL, p.rope_dim, tid, static_cast<int>(blockDim.x));
         return;
     }
     const int l0 = 64 * (blockIdx.x % NLB);
@@ -594,10 +612,9 @@ __global__ void __launch_bounds__(256) mla_append_kernel(int B, int DL, int rd, 
     if (b >= B) return;
     const int pos = positions[b];
     if (pos < 0 || pos >= T_max) return;
-    const int row = DL + rd;
-    T* dst = cache + (static_cast<size_t>(b) * T_max + pos) * row;
-    for (int e = threadIdx.x; e < row; e += blockDim.x)
-        dst[e] = e < DL ? cn[static_cast<size_t>(b) * DL + e] : rn[static_cast<size_t>(b) * rd + e - DL];
+    T* dst = cache + (static_cast<size_t>(b) * T_max + pos) * (DL + rd);
+    copy_new_row(dst, cn + static_cast<size_t>(b) * DL, rn + static_cast<size_t>(b) * rd, DL, rd,
+                 static_cast<int>(threadIdx.x), static_cast<int>(blockDim.x));
 }
 
 // The streaming kernel: eight waves (two per SIMD), or four where an
