@@ -43,21 +43,38 @@ from . import kvc_oracle as O
 __all__ = ["quantize_u8", "dequantize_u8", "append_contiguous_u8", "append_paged_u8",
            "decode_attention_u8", "decode_attention_paged_u8", "decode_kv_read_bytes_u8"]
 
-_F255 = np.float32(255.0)
+# An 8-bit affine grid has 256 codes, so 255 steps between its end points.
+_STEPS = np.float32(255.0)
+_TOP_CODE = 255
+
+
+def _affine_grid(lo: np.ndarray, hi: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Step and zero code of the 256-code grid whose end codes sit at the
+    vector's extremes lo and hi (float32 arrays, one entry per vector).
+
+    The step is the span over 255 steps; the zero code is the code nearest to
+    the value 0, kept on the grid.  A vector with no span gets step 1 (the page
+    divides by its zero step there).
+    """
+    step = (hi - lo) / _STEPS
+    step = np.where(step == 0, np.float32(1.0), step).astype(np.float32)
+    zero = np.clip(np.rint(np.negative(lo) / step), 0, _TOP_CODE).astype(np.float32)
+    return step, zero
+
+
+def _encode(x: np.ndarray, step: np.ndarray, zero: np.ndarray) -> np.ndarray:
+    """Code of each value: its distance from the zero code in steps, rounded
+    to the nearest code (ties to even) and kept on the grid."""
+    return np.clip(np.rint(x / step + zero), 0, _TOP_CODE).astype(np.uint8)
 
 
 def quantize_u8(x) -> Tuple[np.ndarray, np.ndarray]:
-    """uint8 codes and float32 [..., 2] (step, zero point) of each vector along
-    the last axis of x (float32 values), in the listing's order of operations."""
-    x = np.asarray(x, dtype=np.float32)
-    mn = x.min(axis=-1, keepdims=True)
-    mx = x.max(axis=-1, keepdims=True)
-    step = (mx - mn) / _F255
-    step = np.where(step == 0, np.float32(1.0), step).astype(np.float32)
-    zp = np.clip(np.rint(-mn / step), 0, 255).astype(np.float32)
-    codes = np.clip(np.rint(x / step + zp), 0, 255).astype(np.uint8)
-    sz = np.concatenate([step, zp], axis=-1).astype(np.float32)
-    return codes, sz
+    """uint8 codes and float32 [..., 2] (step, zero point) pairs of the vectors
+    along the last axis of x.  Every operation is one float32 operation,
+    rounded once (the precision the page's float tensors have)."""
+    v = np.asarray(x, dtype=np.float32)
+    step, zero = _affine_grid(np.min(v, axis=-1, keepdims=True), np.max(v, axis=-1, keepdims=True))
+    return _encode(v, step, zero), np.concatenate([step, zero], axis=-1).astype(np.float32)
 
 
 def dequantize_u8(codes, sz) -> np.ndarray:

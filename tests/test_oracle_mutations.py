@@ -115,6 +115,34 @@ def check_table(M) -> bool:
                 and s[5, 7] == np.float32(math.sin(5 * th)))
 
 
+def check_rope_f32(M) -> bool:
+    """The rotation against native float32 arithmetic (numpy: every operation
+    rounded once, nothing fused), bit for bit."""
+    d, P = 64, 40
+    c, s = M.rope_table(P, d)
+    x = np.random.default_rng(9).standard_normal((P, 4, d)).astype(np.float32)
+    ok = True
+    for style in ("interleaved", "half"):
+        i = np.arange(d // 2)
+        i0, i1 = (2 * i, 2 * i + 1) if style == "interleaved" else (i, i + d // 2)
+        for p in range(P):
+            x0, x1 = x[p][:, i0], x[p][:, i1]
+            want = np.empty_like(x[p])
+            want[:, i0] = x0 * c[p] - x1 * s[p]
+            want[:, i1] = x0 * s[p] + x1 * c[p]
+            ok &= bool(np.array_equal(M.rope_rotate(x[p], "f32", c[p], s[p], style), want))
+    return ok
+
+
+def check_bf16_exact(M) -> bool:
+    """One rounding from float64 to bfloat16 against exact rational rounding,
+    on midpoints and values a hair beside them."""
+    from test_oracle_pins import bf16_exact_inputs, bf16_rne_exact
+    x = bf16_exact_inputs(np.random.default_rng(10), 300)
+    want = np.array([bf16_rne_exact(float(v)) for v in x], dtype=np.uint16)
+    return bool(np.array_equal(M.bf16_round_bits(x), want))
+
+
 def _passes(chk, M) -> bool:
     """A check that raises (e.g. an index out of range) counts as failed."""
     try:
@@ -123,7 +151,8 @@ def _passes(chk, M) -> bool:
         return False
 
 
-CHECKS = [check_sdpa, check_rope_complex, check_incremental, check_sizes, check_paged, check_bf16, check_table]
+CHECKS = [check_sdpa, check_rope_complex, check_incremental, check_sizes, check_paged, check_bf16, check_table,
+          check_rope_f32, check_bf16_exact]
 
 MUTATIONS = {
     "modular_head_map": ("for h in range(j * G, (j + 1) * G):\n                out[b, h], _ = _head_attention(qf[b, h], K, V, sc)\n    return out\n\n\ndef decode_attention_weights",
@@ -141,6 +170,12 @@ MUTATIONS = {
     "kv_factor_two_dropped": ("return 2 * n_layers * n_kv_heads * d_head * elem_bytes", "return n_layers * n_kv_heads * d_head * elem_bytes"),
     "paged_offset": ("return pos // block_size, pos % block_size", "return pos // block_size, (pos + 1) % block_size"),
     "bf16_ties_to_odd": ("even = (cand & 1) == 0", "even = (cand & 1) == 1"),
+    # the rotation with one rounding per output (what a fused multiply-add gives)
+    "rope_single_rounding": ("r0 = _fl(_fl(x0 * c) - _fl(x1 * s))\n    r1 = _fl(_fl(x0 * s) + _fl(x1 * c))",
+                             "r0 = _fl(x0 * c - x1 * s)\n    r1 = _fl(x0 * s + x1 * c)"),
+    # float64 rounded to float32 first, then to bfloat16 (two roundings)
+    "bf16_double_rounding": ("        _nearest_bf16(flat, mag, sign, best, best_d)",
+                             "        _nearest_bf16(f32.astype(np.float64), mag, sign, best, best_d)"),
     "rope_frequency": ("theta = base ** (-(2.0 * i) / d)", "theta = base ** (-(1.0 * i) / d)"),
 }
 

@@ -60,6 +60,62 @@ def test_bf16_rounding_of_float64_is_single_rounding():
     assert O.bf16_to_f32(np.uint16(0x3F80)) == 1.0
 
 
+def bf16_rne_exact(x: float) -> int:
+    """Round-to-nearest-even of a float64 value to bfloat16 bits, from the
+    definition in exact rational arithmetic: bfloat16 keeps 8 significant bits
+    (exponent range of float32, subnormals below 2^-126), the nearer
+    representable neighbour wins, a tie goes to the even significand, and a
+    value at or past halfway above the largest finite one becomes infinity."""
+    from fractions import Fraction
+    import struct
+    sign = 0x8000 if math.copysign(1.0, x) < 0 else 0
+    if math.isinf(x):
+        return sign | 0x7F80
+    a = Fraction(abs(x))
+    if a == 0:
+        return sign
+    e = math.frexp(abs(x))[1] - 1              # 2^e <= |x| < 2^(e+1)
+    e = max(e, -126)                           # subnormals share the last normal binade's spacing
+    ulp = Fraction(2) ** (e - 7)
+    n, rem = divmod(a, ulp)
+    if 2 * rem > ulp or (2 * rem == ulp and n % 2 == 1):
+        n += 1
+    v = n * ulp
+    if v >= Fraction(2) ** 128:
+        return sign | 0x7F80
+    bits = struct.unpack("<I", struct.pack("<f", float(v)))[0]   # v is a bfloat16 value: exact in float32
+    return sign | (bits >> 16)
+
+
+def bf16_exact_inputs(rng, n: int) -> np.ndarray:
+    """float64 values across the whole range, with many exactly halfway between
+    two bfloat16 values and many a hair (far below a float32 ulp) to either
+    side of such a midpoint, where rounding through float32 first goes wrong."""
+    mags = 10.0 ** rng.uniform(-44, 38.5, n)
+    plain = mags * rng.choice([-1.0, 1.0], n)
+    hi = rng.integers(0x0001, 0x7F7F, n).astype(np.uint32)
+    lower = (hi << 16).view(np.float32).astype(np.float64)
+    upper = ((hi + 1) << 16).view(np.float32).astype(np.float64)
+    mid = (lower + upper) / 2                                    # exact in float64
+    hair = (upper - lower) * 2.0 ** -35
+    sgn = rng.choice([-1.0, 1.0], n)
+    return np.concatenate([plain, sgn * mid, sgn * (mid + hair), sgn * (mid - hair),
+                           [2.0 ** 128 * (1 - 2.0 ** -9), 2.0 ** 128 * (1 - 2.0 ** -10), 2.0 ** -133, 2.0 ** -134,
+                            3 * 2.0 ** -135, 0.0, -0.0, np.inf, -np.inf]])
+
+
+def test_bf16_rounding_of_float64_matches_exact_rational_rounding():
+    """One rounding from float64, checked against exact rational arithmetic on
+    random values of every magnitude, on exact midpoints and just beside them,
+    at the overflow threshold and in the subnormal range."""
+    r = np.random.default_rng(77)
+    x = bf16_exact_inputs(r, 4000)
+    want = np.array([bf16_rne_exact(float(v)) for v in x], dtype=np.uint16)
+    got = O.bf16_round_bits(x)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(float(x[i]), hex(int(got[i])), hex(int(want[i]))) for i in bad[:5]]
+
+
 # ---------------------------------------------------------------------------
 # RoPE table and rotation
 # ---------------------------------------------------------------------------
@@ -125,6 +181,47 @@ def test_rope_matches_complex_multiplication(style):
     n0 = np.abs(z)
     n1 = np.hypot(re.astype(np.float64), im)
     np.testing.assert_allclose(n1, n0, rtol=1e-6, atol=1e-6)
+
+
+def _to_f32_torch(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Storage values as float32 through torch's own conversion."""
+    if dtype == "f32":
+        return np.asarray(x, np.float32)
+    return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).float().numpy()
+
+
+@pytest.mark.parametrize("style", ["interleaved", "half"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_rope_is_the_float32_operation_sequence(style, dtype):
+    """The rotation, bit for bit, against the same operation sequence in native
+    IEEE single precision (numpy float32 arithmetic: every product and sum
+    rounded once, nothing fused), then stored through torch's own conversion.
+    A single rounding of the whole expression (a fused multiply-add) differs
+    from it in the last bit of most outputs."""
+    d, P = 128, 300
+    c, s = O.rope_table(P, d)
+    x = _rand_store((P, 3, d), dtype)
+    xf = _to_f32_torch(x, dtype)
+    half = d // 2
+    i = np.arange(half)
+    i0, i1 = (2 * i, 2 * i + 1) if style == "interleaved" else (i, i + half)
+    n_diff_fused = 0
+    for p in range(P):
+        x0, x1 = xf[p][:, i0], xf[p][:, i1]
+        cc, ss = c[p][None, :], s[p][None, :]
+        r0 = x0 * cc - x1 * ss                  # float32 * float32 -> float32, then float32 - float32
+        r1 = x0 * ss + x1 * cc
+        want = np.empty_like(xf[p])
+        want[:, i0], want[:, i1] = r0, r1
+        got = O.rope_rotate_f32(x[p], dtype, c[p], s[p], style)
+        assert got.dtype == np.float64 and np.array_equal(got.astype(np.float32), want)
+        assert np.array_equal(got.astype(np.float32).astype(np.float64), got)    # float32 values
+        stored = O.rope_rotate(x[p], dtype, c[p], s[p], style)
+        ref = want if dtype == "f32" else _bf16_from_torch(want)
+        assert np.array_equal(stored, ref)
+        fused = (x0.astype(np.float64) * cc - x1.astype(np.float64) * ss).astype(np.float32)
+        n_diff_fused += int(np.count_nonzero(fused != r0))
+    assert n_diff_fused > 0     # the check can tell the two apart on these inputs
 
 
 def test_rope_scores_depend_only_on_relative_position():

@@ -15,6 +15,7 @@ import types
 
 import numpy as np
 import pytest
+import torch
 
 import oracle.kvc_oracle as O
 import oracle.kvc_quant_oracle as QO
@@ -140,8 +141,46 @@ def check_paged(M) -> bool:
     return bool(np.array_equal(a, p))
 
 
+def _torch_affine_u8(x: np.ndarray):
+    """The affine 8-bit grid of each vector evaluated with torch float32 CPU
+    tensors (IEEE single precision, every operation rounded once; torch.round
+    takes ties to even): step = span / 255, zero code = -min / step rounded and
+    clamped to [0, 255], codes = x / step + zero code rounded and clamped."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    lo, hi = torch.aminmax(t, dim=-1, keepdim=True)
+    step = torch.div(hi - lo, 255.0)
+    step = torch.where(step == 0, torch.ones_like(step), step)
+    zero = torch.clamp(torch.round(torch.div(-lo, step)), 0.0, 255.0)
+    codes = torch.clamp(torch.round(torch.div(t, step) + zero), 0.0, 255.0).to(torch.uint8)
+    return codes.numpy(), step[..., 0].numpy(), zero[..., 0].numpy()
+
+
+def _tie_vectors() -> np.ndarray:
+    """Vectors whose codes (and zero points) fall exactly halfway between two
+    codes: step 1 with values k + 1/2, and zero points of exactly 127.5."""
+    k = np.arange(0, 255, dtype=np.float32)
+    a = np.concatenate([[0.0, 255.0], k[:62] + 0.5]).astype(np.float32)          # step 1, zero 0
+    b = np.concatenate([[-127.5, 127.5], k[:62] - 127.0]).astype(np.float32)     # step 1, zero rint(127.5)
+    c = np.concatenate([[-1.5, 253.5], k[:62] * 3 + 0.5]).astype(np.float32)     # step 1, zero rint(1.5)
+    return np.stack([a, b, c])
+
+
+def check_float32_torch(M) -> bool:
+    """Bit-exact agreement with the grid evaluated in torch float32 (the precision
+    the page's float tensors carry) on 65536 N(0, 1) vectors of 128 and on
+    vectors built to land on rounding ties."""
+    rng = np.random.default_rng(16)
+    ok = True
+    for x in (rng.standard_normal((1 << 16, 128)).astype(np.float32),
+              (rng.standard_normal((512, 64)) * 1e3 + 7).astype(np.float32), _tie_vectors()):
+        codes, sz = M.quantize_u8(x)
+        tc, ts, tz = _torch_affine_u8(x)
+        ok &= bool(np.array_equal(codes, tc) and np.array_equal(sz[..., 0], ts) and np.array_equal(sz[..., 1], tz))
+    return ok
+
+
 CHECKS = [check_grid_exact, check_half_step, check_clamp_example, check_decode_grid, check_append_half_step,
-          check_paged]
+          check_paged, check_float32_torch]
 
 
 @pytest.mark.parametrize("chk", CHECKS, ids=lambda c: c.__name__)
@@ -177,12 +216,16 @@ def test_code_bytes_per_token_match_the_page():
 # --- planted mistakes -------------------------------------------------------
 
 MUTATIONS = {
-    "step over 256": ("(mx - mn) / _F255", "(mx - mn) / np.float32(256.0)"),
-    "zero point truncated": ("np.rint(-mn / step)", "np.floor(-mn / step)"),
-    "codes truncated": ("np.rint(x / step + zp)", "np.floor(x / step + zp)"),
-    "zero point not clamped": ("np.clip(np.rint(-mn / step), 0, 255)", "np.rint(-mn / step)"),
-    "range over the whole tensor": ("mn = x.min(axis=-1, keepdims=True)",
-                                    "mn = np.full(x.shape[:-1] + (1,), x.min(), np.float32)"),
+    "step over 256": ("_STEPS = np.float32(255.0)", "_STEPS = np.float32(256.0)"),
+    "zero point truncated": ("np.rint(np.negative(lo) / step)", "np.floor(np.negative(lo) / step)"),
+    "codes truncated": ("np.rint(x / step + zero)", "np.floor(x / step + zero)"),
+    "zero point not clamped": ("np.clip(np.rint(np.negative(lo) / step), 0, _TOP_CODE)", "np.rint(np.negative(lo) / step)"),
+    "range over the whole tensor": ("np.min(v, axis=-1, keepdims=True), np.max(v, axis=-1, keepdims=True)",
+                                    "np.full(v.shape[:-1] + (1,), v.min(), np.float32), np.max(v, axis=-1, keepdims=True)"),
+    # the same steps evaluated in float64 (rounded to float32 only when stored)
+    "quantizer in float64": ("v = np.asarray(x, dtype=np.float32)", "v = np.asarray(x, dtype=np.float64)"),
+    # the division by the step replaced by a product with its reciprocal
+    "codes via reciprocal": ("np.rint(x / step + zero)", "np.rint(x * (np.float32(1.0) / step) + zero)"),
     "dequantize without zero point": ("(np.asarray(codes).astype(np.float32) - zp) * step",
                                       "np.asarray(codes).astype(np.float32) * step"),
     "values read with the key pairs": ("v[b, :, :L] = dequantize_u8(v_codes[b, :, :L], v_sz[b, :, :L])",
