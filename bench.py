@@ -77,8 +77,6 @@ def parse():
                     help="native: the workload's dtype (kvc_decode_step); u8: the quantized cache "
                          "(kvc_append_u8 + kvc_decode_attn[_paged]_u8 on codes drawn by workloads.draw_quantized)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-seqs", type=int, default=0,
-                    help="sequences the CPU oracle is timed on (0 = all)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
     ap.add_argument("--read-probe", action="store_true",
@@ -123,155 +121,164 @@ def calibrate_copy(nbytes: int) -> None:
 
 
 def cpu_threads() -> int:
-    """Host threads for the all-cores oracle figure: the CPUs this process may
+    """Host cores for the all-cores oracle figure: the CPUs this process may
     run on, at most OMP_NUM_THREADS (the share of the host one GPU gets)."""
     n = len(os.sched_getaffinity(0))
     cap = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
     return max(1, min(n, cap) if cap > 0 else n)
 
 
-def cpu_baseline(x, n_seqs, window=0, threads=1):
-    """Time the CPU oracle (as it stands; numpy with `threads` BLAS threads) on
-    the same step's inputs (with a window: the sliding-window oracle over the
-    full cache)."""
-    import numpy as np
+# The task the forked oracle workers run (set before the pool forks, so each
+# worker inherits it with the step's inputs; nothing large is sent to them).
+_CPU_TASK = None
+
+
+def _cpu_task(i):
+    _CPU_TASK(i)
+    return 0
+
+
+def _cpu_noop(_):
+    return 0
+
+
+def time_cpu_tasks(task, n_tasks: int, procs: int) -> float:
+    """Seconds to run task(0), ..., task(n_tasks - 1): in this process when
+    procs == 1, else spread over `procs` forked worker processes (started
+    before the clock runs).  One BLAS thread per process either way.  Must run
+    before this process touches the GPU: a forked copy of a process holding a
+    GPU context must not exist."""
+    global _CPU_TASK
     from threadpoolctl import threadpool_limits
+
+    _CPU_TASK = task
+    with threadpool_limits(limits=1):
+        if procs <= 1:
+            t0 = time.perf_counter()
+            for i in range(n_tasks):
+                task(i)
+            return time.perf_counter() - t0
+        import multiprocessing as mp
+        with mp.get_context("fork").Pool(procs) as pool:
+            pool.map(_cpu_noop, range(4 * procs))
+            t0 = time.perf_counter()
+            pool.map(_cpu_task, range(n_tasks), chunksize=1)
+            return time.perf_counter() - t0
+
+
+def _np_store(t, dt):
+    import numpy as np
+    import torch
+    t = t.contiguous()
+    return t.view(torch.int16).numpy().view(np.uint16) if dt == "bf16" else t.numpy()
+
+
+def oracle_tasks(x, kind: str, window: int = 0, qc=None):
+    """The step's CPU oracle as independent (sequence, KV head) tasks: each
+    appends the group's new token(s) and attends its G query heads, on its own
+    slices of the inputs (a paged cache: the sequence's rows gathered through
+    its block table first).  Returns (task, n_tasks, kv_bytes, what)."""
+    import numpy as np
 
     import oracle as O
-    from dataclasses import replace
 
     w = x.workload
-    B = w.B if n_seqs <= 0 else min(n_seqs, w.B)
-    dt = w.dtype
-
-    def np_store(t):
-        t = t.contiguous()
-        return t.view(__import__("torch").int16).numpy().view(np.uint16) if dt == "bf16" else t.numpy()
-
-    if w.paged:
-        raise NotImplementedError("CPU baseline is timed on contiguous workloads")
-    kc, vc = np_store(x.k_cache[:B]), np_store(x.v_cache[:B])
-    q, kn, vn = np_store(x.q[:B]), np_store(x.k_new[:B]), np_store(x.v_new[:B])
+    dt, G, H_kv = w.dtype, w.G, w.H_kv
+    e = 2 if dt == "bf16" else 4
     cos, sin = x.rope_cos.numpy(), x.rope_sin.numpy()
-    cached = x.cached.numpy()[:B]
-    with threadpool_limits(limits=threads):
-        t0 = time.perf_counter()
-        k2, v2, q2 = O.append_contiguous(kc, vc, cached, kn, vn, cos, sin, dt, q=q)
-        if window:
-            import oracle.kvc_window_oracle as WO
-            WO.decode_attention_window(q2, k2, v2, cached + 1, window, dt)
+    cached = x.cached.numpy()
+    n_new = w.new_tokens
+    q, kn, vn = _np_store(x.q, dt), _np_store(x.k_new, dt), _np_store(x.v_new, dt)
+    tbl = x.block_table.numpy() if w.paged else None
+    if kind == "u8":
+        import oracle.kvc_quant_oracle as QO
+        arrs = [a.numpy() for a in (qc.k_codes, qc.k_sz, qc.v_codes, qc.v_sz)]
+    else:
+        kc, vc = _np_store(x.k_cache, dt), _np_store(x.v_cache, dt)
+
+    def rows(a, b, j, L):
+        """[1, 1, L, ...] rows of group (b, j): a slice, or a gather from a pool."""
+        if w.paged:
+            return O.gather_paged(a, tbl, w.block_size, b, L)[None, j:j + 1]
+        return a[b:b + 1, j:j + 1, :L]
+
+    def task(i):
+        b, j = divmod(i, H_kv)
+        hs = slice(j * G, (j + 1) * G)
+        c = cached[b:b + 1]
+        L = int(cached[b]) + n_new
+        if kind == "u8":
+            g = [rows(a, b, j, L) for a in arrs]
+            g = QO.append_contiguous_u8(*g, c, kn[b:b + 1, j:j + 1], vn[b:b + 1, j:j + 1], cos, sin, dt,
+                                        q=q[b:b + 1, hs])
+            QO.decode_attention_u8(g[4], *g[:4], [L], dt)
+        elif n_new > 1:
+            import oracle.kvc_multi_oracle as MO
+            k2, v2, q2 = MO.append_multi(rows(kc, b, j, L), rows(vc, b, j, L), c, kn[b:b + 1, :, j:j + 1],
+                                         vn[b:b + 1, :, j:j + 1], cos, sin, dt, q=q[b:b + 1, :, hs])
+            MO.decode_attention_multi(q2, k2, v2, [L], dt, window)
         else:
-            O.decode_attention(q2, k2, v2, cached + 1, dt)
-        sec = time.perf_counter() - t0
-    nbytes = kv_read_bytes(attended(cached + 1, window), w.H_kv, w.d, 2 if dt == "bf16" else 4)
-    what = f"append + attention over the last {window} tokens" if window else "append + attention"
-    how = "one thread" if threads == 1 else f"{threads} BLAS threads"
-    return {"value": round(nbytes / sec / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{B} of {w.B} sequences of {w.name} ({what}, float64, numpy, {how}), {sec:.2f} s"}
+            k2, v2, q2 = O.append_contiguous(rows(kc, b, j, L), rows(vc, b, j, L), c, kn[b:b + 1, j:j + 1],
+                                             vn[b:b + 1, j:j + 1], cos, sin, dt, q=q[b:b + 1, hs])
+            if window:
+                import oracle.kvc_window_oracle as WO
+                WO.decode_attention_window(q2, k2, v2, [L], window, dt)
+            else:
+                O.decode_attention(q2, k2, v2, [L], dt)
+
+    lens = (cached + n_new).tolist()
+    if kind == "u8":
+        nbytes = kv_read_bytes_u8(lens, H_kv, w.d)
+        what = "uint8 cache, append + attention"
+    else:
+        span = window + n_new - 1 if window else 0
+        nbytes = kv_read_bytes(attended(lens, span), H_kv, w.d, e)
+        what = (f"append of {n_new} tokens + their attention" if n_new > 1 else "append + attention") + \
+            (f" over the last {window} tokens" if window else "") + (", rows gathered through the block table"
+                                                                     if w.paged else "")
+    return task, w.B * H_kv, nbytes, what
 
 
-def cpu_baseline_multi(x, n_seqs, window=0):
-    """Time the multi-token oracle (as it stands, one thread) on the same step."""
-    import numpy as np
-    import torch
-    from threadpoolctl import threadpool_limits
-
-    import oracle.kvc_multi_oracle as MO
-
-    w = x.workload
-    B = w.B if n_seqs <= 0 else min(n_seqs, w.B)
-    dt = w.dtype
-
-    def np_store(t):
-        t = t.contiguous()
-        return t.view(torch.int16).numpy().view(np.uint16) if dt == "bf16" else t.numpy()
-
-    if w.paged:
-        raise NotImplementedError("CPU baseline is timed on contiguous workloads")
-    kc, vc = np_store(x.k_cache[:B]), np_store(x.v_cache[:B])
-    q, kn, vn = np_store(x.q[:B]), np_store(x.k_new[:B]), np_store(x.v_new[:B])
-    cos, sin = x.rope_cos.numpy(), x.rope_sin.numpy()
-    cached = x.cached.numpy()[:B]
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        k2, v2, q2 = MO.append_multi(kc, vc, cached, kn, vn, cos, sin, dt, q=q)
-        MO.decode_attention_multi(q2, k2, v2, cached + w.new_tokens, dt, window)
-        sec = time.perf_counter() - t0
-    nbytes = kv_read_bytes(attended(cached + w.new_tokens, window + w.new_tokens - 1 if window else 0), w.H_kv, w.d,
-                           2 if dt == "bf16" else 4)
-    return {"value": round(nbytes / sec / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{B} of {w.B} sequences of {w.name} (append of {w.new_tokens} tokens + their attention, "
-                      f"float64, numpy, one thread), {sec:.2f} s"}
-
-
-def cpu_baseline_u8(x, qc, n_seqs):
-    """Time the quantized-cache oracle (as it stands, one thread) on the same step."""
-    import numpy as np
-    from threadpoolctl import threadpool_limits
-
-    import oracle.kvc_quant_oracle as QO
+def oracle_tasks_mla(x):
+    """The latent-cache oracle as one task per sequence (the listing's per-head
+    up-projection of that sequence's latents, then the attention)."""
+    import oracle.kvc_mla_oracle as MO
 
     w = x.workload
-    B = w.B if n_seqs <= 0 else min(n_seqs, w.B)
-    dt = w.dtype
-    import torch
+    cache = _np_store(x.cache, "bf16")
+    n = {k: _np_store(getattr(x, k), "bf16") for k in ("w_uk", "b_uk", "w_uv", "b_uv")}
+    q, ckv, kr = _np_store(x.q, "bf16"), _np_store(x.c_kv_new, "bf16"), _np_store(x.k_rope_new, "bf16")
+    cached = x.cached.numpy()
 
-    def np_store(t):
-        t = t.contiguous()
-        return t.view(torch.int16).numpy().view(np.uint16) if dt == "bf16" else t.numpy()
+    def task(b):
+        c2 = MO.append_mla(cache[b:b + 1], cached[b:b + 1], ckv[b:b + 1], kr[b:b + 1])
+        MO.decode_attention_mla(q[b:b + 1], c2, cached[b:b + 1] + 1, n["w_uk"], n["b_uk"], n["w_uv"], n["b_uv"],
+                                w.d_latent, w.dtype)
 
-    if w.paged:
-        raise NotImplementedError("CPU baseline is timed on contiguous workloads")
-    arrs = [a[:B].numpy() for a in (qc.k_codes, qc.k_sz, qc.v_codes, qc.v_sz)]
-    q, kn, vn = np_store(x.q[:B]), np_store(x.k_new[:B]), np_store(x.v_new[:B])
-    cos, sin = x.rope_cos.numpy(), x.rope_sin.numpy()
-    cached = x.cached.numpy()[:B]
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        kc, ks, vc, vs, q2 = QO.append_contiguous_u8(*arrs, cached, kn, vn, cos, sin, dt, q=q)
-        QO.decode_attention_u8(q2, kc, ks, vc, vs, cached + 1, dt)
-        sec = time.perf_counter() - t0
-    nbytes = kv_read_bytes_u8(cached + 1, w.H_kv, w.d)
-    return {"value": round(nbytes / sec / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{B} of {w.B} sequences of {w.name}, uint8 cache (append + attention, float64, numpy, "
-                      f"one thread), {sec:.2f} s"}
+    nbytes = latent_read_bytes(cached + 1, w.d_latent, 2)
+    return task, w.B, nbytes, "append + per-head up-projection of the latents + attention"
+
+
+def cpu_baselines(tasks, name: str, B: int) -> dict:
+    """The oracle (as it stands, float64 numpy) timed on the host on the whole
+    step: over all cores this process may use (one worker process per core,
+    tasks handed out one at a time), and on one core."""
+    task, n, nbytes, what = tasks
+    procs = cpu_threads()
+    out = {}
+    for key, p in (("cpu_baseline", procs), ("cpu_baseline_one_core", 1)):
+        sec = time_cpu_tasks(task, n, p)
+        how = "one process" if p == 1 else f"{p} worker processes, one per core"
+        out[key] = {"value": round(nbytes / sec / 1e9, 4), "unit": "GB/s", "cores": p, "kind": "oracle",
+                    "sample": f"all {B} sequences of {name} as {n} independent tasks ({what}; float64, numpy, "
+                              f"one BLAS thread each; {how}), {sec:.2f} s"}
+    return out
 
 
 def latent_read_bytes(seq_lens, d_latent, elem_bytes):
     """Bytes of the latent cache a step must read: sum_b L_b * d_latent * e (the
     rope part of each row is stored but not attended)."""
     return int(sum(int(L) for L in seq_lens)) * d_latent * elem_bytes
-
-
-def cpu_baseline_mla(x, n_seqs):
-    """Time the latent-cache oracle (as it stands, one thread: the listing's
-    per-head up-projection of every cached latent, then the attention) on the
-    first n_seqs sequences of the same step."""
-    import numpy as np
-    import torch
-    from threadpoolctl import threadpool_limits
-
-    import oracle.kvc_mla_oracle as MO
-
-    w = x.workload
-    B = min(max(n_seqs, 1), w.B)
-
-    def np_store(t):
-        return t.contiguous().view(torch.int16).numpy().view(np.uint16)
-
-    cache = np_store(x.cache[:B])
-    n = {k: np_store(getattr(x, k)) for k in ("w_uk", "b_uk", "w_uv", "b_uv")}
-    q, ckv, kr = np_store(x.q[:B]), np_store(x.c_kv_new[:B]), np_store(x.k_rope_new[:B])
-    cached = x.cached.numpy()[:B]
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        c2 = MO.append_mla(cache, cached, ckv, kr)
-        MO.decode_attention_mla(q, c2, cached + 1, n["w_uk"], n["b_uk"], n["w_uv"], n["b_uv"], w.d_latent, w.dtype)
-        sec = time.perf_counter() - t0
-    nbytes = latent_read_bytes(cached + 1, w.d_latent, 2)
-    return {"value": round(nbytes / sec / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{B} of {w.B} sequences of {w.name} (append + per-head up-projection of the latents + "
-                      f"attention, float64, numpy, one thread), {sec:.2f} s"}
 
 
 def bench_mla(args, W) -> dict:
@@ -283,8 +290,13 @@ def bench_mla(args, W) -> dict:
 
     w = W.MLA_WORKLOADS[args.workload]
     x = W.draw_mla(w)
+    # the host oracle first: its worker processes are forked before this
+    # process touches the GPU
+    cpu = None if args.no_cpu_baseline else cpu_baselines(oracle_tasks_mla(x), w.name, w.B)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    kvc.load()
+    probe = read_probe(reps=5)      # also brings the part to its working clocks before the timed steps
     e = 2
     kv_bytes = latent_read_bytes(x.seq_lens.tolist(), w.d_latent, e)
     weight_bytes = 2 * w.H * w.d_k * w.d_latent * e
@@ -350,15 +362,12 @@ def bench_mla(args, W) -> dict:
                      "bytes_per_launch": kv_bytes},
         "wall_s_timed": round(wall, 4),
     }
-    del caches
-    torch.cuda.empty_cache()
-    probe = read_probe(reps=5)
     ceil_nt = probe["nontemporal"]["best_gbs"]
     res["read_ceiling"] = {"probe": "kvc_hbm_read_probe, 4 GiB, best grid",
                            "default_policy_gbs": probe["default"]["best_gbs"], "nontemporal_gbs": ceil_nt,
                            "kernel_frac_of_ceiling": round(achieved / ceil_nt, 4)}
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline_mla(x, args.cpu_sample_seqs or 4)
+    if cpu:
+        res.update(cpu)
     return res
 
 
@@ -447,13 +456,13 @@ def main():
 
     import torch
 
-    import mqa_decode_attention_amd as kvc
     import workloads as W
 
-    if not torch.cuda.is_available():
+    # (device_count does not create a GPU context: the host oracle's worker
+    # processes are forked before anything does)
+    if torch.cuda.device_count() < 1:
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    kvc.load()   # fails loudly if libkvc.so is missing
 
     if args.workload in W.MLA_WORKLOADS:
         if args.window or args.ring or args.kv_cache != "native":
@@ -463,8 +472,6 @@ def main():
         return
     w = W.WORKLOADS[args.workload]
     x = W.draw(w)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     u8 = args.kv_cache == "u8"
     win = args.window
     multi = w.new_tokens > 1          # several new tokens per sequence: append_multi + decode_attn_multi
@@ -476,8 +483,19 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     e = 2 if w.dtype == "bf16" else 4
+    qc = W.draw_quantized(x) if u8 else None
+    # the host oracle first: its worker processes are forked before this
+    # process touches the GPU
+    cpu = None if args.no_cpu_baseline else \
+        cpu_baselines(oracle_tasks(x, "u8" if u8 else "native", win, qc), w.name, w.B)
+
+    import mqa_decode_attention_amd as kvc
+
+    kvc.load()   # fails loudly if libkvc.so is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    probe = read_probe(reps=5)      # also brings the part to its working clocks before the timed steps
     if u8:
-        qc = W.draw_quantized(x)
         kv_bytes = kv_read_bytes_u8(x.seq_lens.tolist(), w.H_kv, w.d)
         cache_bytes = (qc.k_codes.numel() + qc.k_sz.numel() * 4) * 2
     else:
@@ -622,19 +640,12 @@ def main():
                      "bytes_per_launch": kv_bytes},
         "wall_s_timed": round(wall, 4),
     }
-    del ks, vs
-    torch.cuda.empty_cache()
-    probe = read_probe(reps=5)
     ceil_nt = probe["nontemporal"]["best_gbs"]
     res["read_ceiling"] = {"probe": "kvc_hbm_read_probe, 4 GiB, best grid",
                            "default_policy_gbs": probe["default"]["best_gbs"], "nontemporal_gbs": ceil_nt,
                            "kernel_frac_of_ceiling": round(achieved / ceil_nt, 4)}
-    if not args.no_cpu_baseline and not w.paged:
-        res["cpu_baseline"] = cpu_baseline_u8(x, qc, args.cpu_sample_seqs) if u8 else \
-            cpu_baseline_multi(x, args.cpu_sample_seqs, win) if multi else cpu_baseline(x, args.cpu_sample_seqs, win)
-        if not u8 and not multi and cpu_threads() > 1:
-            # the same oracle with the host's cores for its BLAS calls (information)
-            res["cpu_baseline_threads"] = cpu_baseline(x, args.cpu_sample_seqs, win, threads=cpu_threads())
+    if cpu:
+        res.update(cpu)
     print(json.dumps(res), flush=True)
 
 

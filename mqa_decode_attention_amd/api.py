@@ -7,7 +7,6 @@ kernels; nothing here touches tensor values.
 """
 from __future__ import annotations
 
-import math
 from typing import Dict, Optional, Tuple
 
 import torch
@@ -128,7 +127,10 @@ def split_tokens(dtype: torch.dtype, B: int, H_q: int, H_kv: int, d: int, max_se
 
 
 # Workspaces kept per (device, stream); calls on one stream run one at a time,
-# so they can share one buffer.
+# so they can share one buffer.  Each is allocated with its stream current, so
+# the caching allocator ties its memory to that stream: when a larger one
+# replaces it, the old block is handed out again only in that stream's order,
+# never while a kernel still queued there uses it.
 _WORKSPACES: Dict[Tuple[int, int], torch.Tensor] = {}
 
 
@@ -138,7 +140,8 @@ def _workspace(device: torch.device, stream_handle: int, nbytes: int) -> Tuple[O
     key = (device.index if device.index is not None else torch.cuda.current_device(), stream_handle)
     ws = _WORKSPACES.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        with torch.cuda.stream(torch.cuda.ExternalStream(stream_handle, device=device)):
+            ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
         _WORKSPACES[key] = ws
     return ws.data_ptr(), ws.numel()
 

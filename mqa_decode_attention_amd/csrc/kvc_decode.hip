@@ -58,6 +58,9 @@ struct Layout {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Start of the running max: the largest finite float, negated.
+constexpr float kNoMaxF = 3.402823466e38f;
+
 template <typename T>
 __device__ __forceinline__ void store_out(void* out, size_t i, float x);
 template <>
@@ -179,7 +182,11 @@ decode_split_kernel(const DecodeParams p) {
         constexpr int HALF = D / 2;
         pos = p.positions[b];
         const bool pos_ok = pos >= 0 && pos < p.capacity && pos < p.rope_rows;
-        holds = pos_ok && pos >= t_begin && pos < t_end;
+        // the last split stores the new row whenever its slot is valid; it
+        // also reads it from LDS when the row is attended (L = pos + 1 is
+        // within max_seq_len, so pos lies in this split)
+        const bool own = pos_ok && split == nsp - 1;
+        holds = own && pos >= t_begin && pos < t_end;
         auto ld = [](const T* a, int i) { return Store<T>::load(a, i); };
         auto pair_at = [&](int i, int& e0, int& e1) {
             if (p.rope_style == KVC_ROPE_HALF) { e0 = i; e1 = i + HALF; }
@@ -198,7 +205,7 @@ decode_split_kernel(const DecodeParams p) {
             Store<T>::store(sm_q + g * D, e0, r0);
             Store<T>::store(sm_q + g * D, e1, r1);
         }
-        if (holds) {
+        if (own) {
             const T* ksrc = static_cast<const T*>(p.k_new) + (static_cast<size_t>(b) * p.H_kv + j) * D;
             const T* vsrc = static_cast<const T*>(p.v_new) + (static_cast<size_t>(b) * p.H_kv + j) * D;
             for (int i = tid; i < HALF; i += NT) {
@@ -217,7 +224,7 @@ decode_split_kernel(const DecodeParams p) {
             T* qdst = static_cast<T*>(p.q_rot_out) + (static_cast<size_t>(b) * p.H_q + h0) * D;
             for (int idx = tid; idx < GC * D; idx += NT) qdst[idx] = sm_q[idx];
         }
-        if (holds && chunk == 0) {
+        if (own && chunk == 0) {
             const size_t slot = ((static_cast<size_t>(b) * p.H_kv + j) * p.T_max + pos) * D;
             for (int e = tid; e < D; e += NT) {
                 static_cast<T*>(const_cast<void*>(p.k))[slot + e] = sm_kn[e];
@@ -238,10 +245,14 @@ decode_split_kernel(const DecodeParams p) {
         v_new_row = *reinterpret_cast<const uint4*>(sm_vn + el0);
     }
 
+    // The running max starts at the lowest finite float, not at -inf: a tile
+    // whose rows are all masked (a window's first rows, rounded down to the
+    // split origin) then gives alpha = 2^0 and weights 2^-inf = 0, where a
+    // start at -inf would give 2^(-inf + inf) = NaN.
     float m[GC], l[GC], acc[GC][EPL];
 #pragma unroll
     for (int g = 0; g < GC; ++g) {
-        m[g] = -INFINITY;
+        m[g] = -kNoMaxF;
         l[g] = 0.0f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[g][e] = 0.0f;
@@ -348,7 +359,7 @@ decode_split_kernel(const DecodeParams p) {
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
             const float mw = sm_m[w][g];
-            const float f = (mw == -INFINITY) ? 0.0f : fast_exp2(mw - M);
+            const float f = (mw == -kNoMaxF) ? 0.0f : fast_exp2(mw - M);   // a wave that saw no row
             A = fmaf(sm_acc[w][g][e], f, A);
             Ls = fmaf(sm_l[w][g], f, Ls);
         }

@@ -91,15 +91,35 @@ def oracle_decode(x: W.DecodeInputs, k2, v2, q2, seq_lens=None):
     return o
 
 
+def ulp_distance(a: np.ndarray, b: np.ndarray, dtype: str) -> int:
+    """Largest distance, in units in the last place of the storage dtype,
+    between two arrays of stored values (bit patterns mapped onto a signed
+    integer line, so neighbouring representable values are 1 apart)."""
+    if a.size == 0:
+        return 0
+    ut, st, top = (np.uint16, np.int64, 0x8000) if dtype == "bf16" else (np.uint32, np.int64, 0x80000000)
+
+    def line(x):
+        u = np.ascontiguousarray(x).view(ut).astype(st)
+        return np.where(u & top, -(u & (top - 1)), u)
+
+    return int(np.max(np.abs(line(a) - line(b))))
+
+
 def compare_out(got: torch.Tensor, ref64: np.ndarray, dtype: str, what: str = ""):
-    """Max-abs error of the GPU output against the oracle rounded to the storage dtype."""
-    g = O.to_f64(store_np(got, dtype), dtype)
-    r = O.to_f64(O.round_store(ref64, dtype), dtype)
+    """Max-abs error of the GPU output against the oracle rounded to the storage
+    dtype, over every output; also reports max|out| and the largest distance in
+    storage-dtype ulps, so the headroom under the bar is visible."""
+    gs = store_np(got, dtype)
+    rs = O.round_store(ref64, dtype)
+    g = O.to_f64(gs, dtype)
+    r = O.to_f64(rs, dtype)
     assert g.shape == r.shape, (g.shape, r.shape)
     assert np.all(np.isfinite(g)), f"{what}: non-finite GPU output"
     err = float(np.max(np.abs(g - r))) if g.size else 0.0
     tol = BF16_TOL if dtype == "bf16" else F32_TOL
-    say(f"  {what}: max|err| = {err:.3g} (tol {tol}), max|out| = {float(np.max(np.abs(r))) if r.size else 0:.3g}")
+    say(f"  {what}: {g.size} outputs, max|err| = {err:.3g} (tol {tol}), "
+        f"max|out| = {float(np.max(np.abs(r))) if r.size else 0:.3g}, max ulp distance = {ulp_distance(gs, rs, dtype)}")
     assert err <= tol, f"{what}: max abs error {err} > {tol}"
     return err
 

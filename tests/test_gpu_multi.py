@@ -9,8 +9,8 @@ through the C ABI.
   chunks of 32 rows), head_dim 64 / 128 / 256, every paged mode, with and
   without a window, for several splits; with n = 1 it must equal the
   single-token kvc_decode_attn bit for bit.
-* spec_gqa at full size (16 sequences x 8192 cached + 6 new tokens) on sampled
-  groups in the library's launch plan.
+* spec_gqa at full size (16 sequences x 8192 cached + 6 new tokens), every
+  output, in the library's launch plan.
 """
 import numpy as np
 import pytest
@@ -128,29 +128,14 @@ def test_multi_single_token_equals_decode():
         assert torch.equal(one.view(torch.int16), multi[:, 0].view(torch.int16)), f"split {split}"
 
 
-def test_multi_full_size_sampled():
-    """spec_gqa: 16 sequences x (8192 cached + 6 new), the library's plan."""
+def test_multi_full_size():
+    """spec_gqa: 16 sequences x (8192 cached + 6 new), the library's plan, the
+    append bit for bit and every output compared."""
     w = W.WORKLOADS["spec_gqa"]
     x = W.draw(w)
     say(f"[multi full spec_gqa] n={w.new_tokens}")
     step = MultiStep(x)
-    step.append()
+    k2, v2, q2 = _append_and_check(step, x)
     out = step.decode()
     torch.cuda.synchronize()
-    dt = w.dtype
-    q2 = store_np(step.q, dt)
-    got = store_np(out, dt)
-    lens = x.seq_lens.numpy()
-    rng = np.random.default_rng(6)
-    pairs = {(0, 0), (w.B - 1, w.H_kv - 1)} | {(int(rng.integers(w.B)), int(rng.integers(w.H_kv))) for _ in range(4)}
-    for b, j in sorted(pairs):
-        L = int(lens[b])
-        kb = store_np(step.k[b:b + 1, j:j + 1, :L], dt)
-        vb = store_np(step.v[b:b + 1, j:j + 1, :L], dt)
-        hs = slice(j * w.G, (j + 1) * w.G)
-        ref = MO.decode_attention_multi(q2[b:b + 1, :, hs], kb, vb, [L], dt)
-        g = O.to_f64(got[b:b + 1, :, hs], dt)
-        r = O.to_f64(O.round_store(ref, dt), dt)
-        err = float(np.max(np.abs(g - r)))
-        say(f"  (b={b}, j={j}) max|err| = {err:.3g}")
-        assert err <= 2e-3
+    compare_out(out, oracle_decode_multi(x, k2, v2, q2, 0), w.dtype, "spec_gqa full size")

@@ -3,8 +3,8 @@
 Append: bit-exact over the whole cache buffers and the rotated query.
 Attention: max-abs error <= 2e-3 (bf16; the oracle rounded to bf16) and
 <= 1e-5 (float32), at oracle-sized shapes that span many tiles and splits with
-ragged tails, and at the workloads' full sizes on sampled (sequence, KV head)
-groups in the launch configuration the benchmark times.
+ragged tails, and at the workloads' full sizes on every output, in the launch
+configuration the benchmark times.
 """
 import numpy as np
 import pytest
@@ -121,6 +121,23 @@ def test_nondefault_stream():
     compare_out(out, oracle_decode(x, k2, v2, q2), "bf16", "side stream")
 
 
+def test_stream_argument_outside_its_context():
+    """stream= given without making that stream current: the calls run there,
+    and the workspace the binding grows for the second (longer) call belongs
+    to that stream, so both results are right."""
+    s = torch.cuda.Stream()
+    for i, (w, split) in enumerate(((SMALL["gqa_8b"], 64), (SMALL["long_gqa"], 16))):
+        x = W.draw(w)
+        say(f"[side stream, not current] {w.name} split={split}")
+        step = GpuStep(x)
+        s.wait_stream(torch.cuda.current_stream())
+        step.append(stream=s)
+        out = step.decode(split_tokens=split, stream=s)
+        s.synchronize()
+        k2, v2, q2 = _check_append(step, x)
+        compare_out(out, oracle_decode(x, k2, v2, q2), w.dtype, f"side stream call {i}")
+
+
 def test_paged_equals_contiguous():
     """The same logical cache as a contiguous buffer and as a shuffled block pool.
 
@@ -173,16 +190,9 @@ def test_paged_equals_contiguous():
 # ---------------------------------------------------------------------------
 
 
-def _sample_groups(w, n, seed):
-    rng = np.random.default_rng(seed)
-    pairs = {(0, 0), (w.B - 1, w.H_kv - 1)}
-    while len(pairs) < min(n, w.B * w.H_kv):
-        pairs.add((int(rng.integers(w.B)), int(rng.integers(w.H_kv))))
-    return sorted(pairs)
-
-
 @pytest.mark.parametrize("name", ["gqa_8b", "mqa_ragged", "long_gqa", "paged_gqa"])
-def test_full_size_sampled(name):
+def test_full_size(name):
+    """Every output at the workload's full size, in the default launch plan."""
     w = W.WORKLOADS[name]
     x = W.draw(w)
     say(f"[{name} full] B={w.B} max_len={int(x.seq_lens.max())}")
@@ -192,28 +202,8 @@ def test_full_size_sampled(name):
     torch.cuda.synchronize()
     # the append, over the whole buffers
     k2, v2, q2 = _check_append(step, x)
-    # attention, on sampled (sequence, KV head) groups computed one by one
-    dt, G = w.dtype, w.G
-    got = store_np(out, dt)
-    lens = x.seq_lens.numpy()
-    worst = 0.0
-    for b, j in _sample_groups(w, 6, seed=w.seed):
-        hs = slice(j * G, (j + 1) * G)
-        qg = q2[b:b + 1, hs]
-        if w.paged:
-            Lb = int(lens[b])
-            kg = O.gather_paged(k2, x.block_table.numpy(), w.block_size, b, Lb)[None, j:j + 1]
-            vg = O.gather_paged(v2, x.block_table.numpy(), w.block_size, b, Lb)[None, j:j + 1]
-        else:
-            kg, vg = k2[b:b + 1, j:j + 1], v2[b:b + 1, j:j + 1]
-        ref = O.decode_attention(qg, kg, vg, lens[b:b + 1], dt)
-        g = O.to_f64(got[b:b + 1, hs], dt)
-        r = O.to_f64(O.round_store(ref, dt), dt)
-        err = float(np.max(np.abs(g - r)))
-        worst = max(worst, err)
-        assert err <= 2e-3, f"{name} (b={b}, j={j}): max abs error {err}"
-    assert np.all(np.isfinite(O.to_f64(got, dt)))
-    say(f"  {name}: sampled max|err| = {worst:.3g}")
+    # attention: every (sequence, query head) row
+    compare_out(out, oracle_decode(x, k2, v2, q2), w.dtype, f"{name} full size")
 
 
 def test_workspace_reuse_across_shapes():
@@ -240,6 +230,8 @@ GROUP_CASES = [
     (8, 8, 128, "bf16"), (12, 4, 128, "bf16"), (16, 1, 128, "bf16"), (24, 1, 128, "bf16"),
     (48, 2, 128, "bf16"), (8, 2, 64, "bf16"), (8, 2, 256, "bf16"), (64, 2, 256, "bf16"),
     (8, 2, 32, "bf16"), (4, 4, 16, "bf16"), (16, 4, 128, "f32"), (6, 2, 16, "f32"), (64, 2, 64, "f32"),
+    # groups beyond 32 heads in bf16 (vector kernel, several head chunks)
+    (64, 1, 128, "bf16"), (96, 2, 64, "bf16"),
 ]
 
 

@@ -12,8 +12,8 @@
   decode must match the oracle's decode over the ring's slots.
 * kvc_decode_step_window must equal the oracle's append + windowed decode, and
   equal kvc_append + kvc_decode_attn_window bit for bit (full cache and ring).
-* At the gqa_8b workload's full size with Mistral's 4096-token window, sampled
-  (sequence, KV head) groups in the launch configuration of the library's plan.
+* At the gqa_8b workload's full size with Mistral's 4096-token window, every
+  output, in the launch configuration of the library's plan.
 """
 import numpy as np
 import pytest
@@ -132,6 +132,45 @@ def test_window_edge_lengths():
             assert torch.count_nonzero(out).item() == 0, "L = 0 must give zeros"
 
 
+VECTOR_PAGED = {
+    # the vector kernel: float32, and bf16 groups of more than 32 heads; its
+    # tiles (4 or 8 rows) are shorter than the 16-row split alignment
+    "f32_d128": W.WORKLOADS["paged_gqa"].replace(B=4, H_q=16, H_kv=4, d=128, dtype="f32", cached_lo=304,
+                                                 cached_hi=304),
+    "f32_d256": W.WORKLOADS["paged_gqa"].replace(B=4, H_q=8, H_kv=2, d=256, dtype="f32", cached_lo=304,
+                                                 cached_hi=304),
+    "bf16_d256_g64": W.WORKLOADS["paged_gqa"].replace(B=4, H_q=64, H_kv=1, d=256, dtype="bf16", cached_lo=304,
+                                                      cached_hi=304),
+}
+
+
+@pytest.mark.parametrize("name", sorted(VECTOR_PAGED))
+def test_window_vector_kernel_masked_first_tiles(name):
+    """Windows whose first token lies 8 to 15 rows past its split's origin (the
+    window start rounded down to 16): the first tile of some waves then lies
+    wholly before the window, and its rows are all masked."""
+    window = 37
+    xs = W.draw(VECTOR_PAGED[name])
+    w = xs.workload
+    xs.cached[:] = torch.tensor([lo + window - 1 for lo in (268, 264, 31, 9)], dtype=torch.int32)
+    bs = w.block_size
+    for b, c in enumerate(xs.cached.tolist()):        # NaN past each new length
+        for t in range(c, xs.block_table.shape[1] * bs):
+            blk = int(xs.block_table[b, t // bs])
+            if blk >= 0:
+                xs.k_cache[blk, :, t % bs] = float("nan")
+                xs.v_cache[blk, :, t % bs] = float("nan")
+    poison_before_window(xs, window)
+    lens = xs.seq_lens.tolist()
+    say(f"[window vector kernel {name} W={window}] lens={lens} window starts mod 16="
+        f"{[WO.window_start(L, window) % 16 for L in lens]}")
+    step = GpuStep(xs)
+    k2, v2, q2 = _append_and_check(step, xs)
+    ref = oracle_window(xs, k2, v2, q2, window)
+    for split in (0, 16, 48, 1 << 20):
+        compare_out(_decode_window(step, window, split), ref, w.dtype, f"{name} W={window} split={split}")
+
+
 def _ring_inputs(B=4, H_q=32, H_kv=8, d=128, T=64, positions=(5, 63, 64, 200), dtype="bf16", seed=31):
     """A ring [B, H_kv, T, d] holding each sequence's window before the step
     (slots of tokens never written are NaN), and the step's raw q / k / v."""
@@ -213,9 +252,9 @@ def test_step_ring():
     compare_out(out, WO.decode_attention_ring(q2, k2, v2, (pos + 1).numpy(), "bf16"), "bf16", "ring step")
 
 
-def test_window_full_size_sampled():
+def test_window_full_size():
     """gqa_8b at full size (16 x 8193 tokens) with a 4096-token window, through
-    the fused step in the library's launch plan, on sampled groups."""
+    the fused step in the library's launch plan, every output compared."""
     w = W.WORKLOADS["gqa_8b"]
     window = 4096
     x = W.draw(w)
@@ -226,21 +265,7 @@ def test_window_full_size_sampled():
     out, q_rot = kvc.decode_step_window(x.q.to("cuda"), k, v, step.pos, step.kn, step.vn, step.cos, step.sin,
                                         step.max_len, window)
     torch.cuda.synchronize()
-    dt = w.dtype
-    q2 = store_np(q_rot, dt)
-    got = store_np(out, dt)
-    lens = x.seq_lens.numpy()
-    rng = np.random.default_rng(5)
-    pairs = {(0, 0), (w.B - 1, w.H_kv - 1)} | {(int(rng.integers(w.B)), int(rng.integers(w.H_kv))) for _ in range(4)}
-    for b, j in sorted(pairs):
-        L = int(lens[b])
-        lo = WO.window_start(L, window)
-        kb = store_np(k[b:b + 1, j:j + 1, lo:L], dt)
-        vb = store_np(v[b:b + 1, j:j + 1, lo:L], dt)
-        hs = slice(j * w.G, (j + 1) * w.G)
-        ref = O.decode_attention(q2[b:b + 1, hs], kb, vb, [L - lo], dt)
-        g = O.to_f64(got[b:b + 1, hs], dt)
-        r = O.to_f64(O.round_store(ref, dt), dt)
-        err = float(np.max(np.abs(g - r)))
-        say(f"  (b={b}, j={j}) max|err| = {err:.3g}")
-        assert err <= 2e-3
+    k2, v2, q2 = oracle_append(x)
+    assert np.array_equal(bits(k), np.ascontiguousarray(k2).view(np.uint8)), "K cache differs from the oracle"
+    assert np.array_equal(bits(q_rot), np.ascontiguousarray(q2).view(np.uint8)), "rotated q differs"
+    compare_out(out, oracle_window(x, k2, v2, q2, window), w.dtype, f"gqa_8b W={window} full size")
