@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 7
+#define KVC_ABI_VERSION 8
 
 typedef enum kvc_status {
     KVC_OK = 0,
@@ -252,6 +252,41 @@ kvc_status kvc_decode_step(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
                            const void* v_new, const float* rope_cos, const float* rope_sin,
                            int rope_rows, int rope_style, int max_seq_len, float scale, void* out,
                            int split_tokens, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kvc_decode_step_noalloc - kvc_decode_step for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.
+ *
+ * Arguments, results and errors as kvc_decode_step, without the workspace:
+ * the split partials go to a fixed array of device memory inside the library
+ * (kvc_decode_step_noalloc_max_bytes() bytes, 32 MiB; one copy per device,
+ * held until the process ends).  The call allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine); the caller passes every input and
+ * output.  The first call on a device looks up that device's copy of the
+ * array (hipGetSymbolAddress, the device current).
+ *
+ * Limit: a call whose partials would need more than the array holds (as
+ * kvc_decode_workspace_bytes reports for the same sizes) returns
+ * KVC_ERR_WORKSPACE before anything is launched; a longer split_tokens, or
+ * kvc_decode_step with a workspace of the caller's, serves such sizes.
+ *
+ * Every call on one device shares that device's array, which keeps whatever
+ * the last call left in it (nothing needs clearing: every call writes the
+ * partials it reads).  Calls that overlap in time on one device - on
+ * different streams, or from different threads - race on it and give
+ * unspecified results; serialise them (one stream, or events).
+ */
+kvc_status kvc_decode_step_noalloc(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
+                                   const void* q, void* q_rot_out, void* k_cache, void* v_cache, int T_max,
+                                   const int32_t* block_table, int block_size, int max_blocks_per_seq,
+                                   int num_blocks, const int32_t* positions, const void* k_new,
+                                   const void* v_new, const float* rope_cos, const float* rope_sin,
+                                   int rope_rows, int rope_style, int max_seq_len, float scale, void* out,
+                                   int split_tokens, void* stream);
+
+/* Bytes of split partials kvc_decode_step_noalloc can hold (its fixed array). */
+size_t kvc_decode_step_noalloc_max_bytes(void);
 
 /*
  * Sliding window: the new token attends only the last `window` tokens of its

@@ -33,8 +33,9 @@ and for a latent cache (multi-head latent attention, one [c_kv | k_rope] row per
 """
 from .api import (KVC_BF16, KVC_F32, KVC_U8, KvcError, append, append_multi, append_ring, append_u8,  # noqa: F401
                   decode_attn, decode_attn_multi, decode_attn_paged, decode_attn_paged_u8, decode_attn_u8,
-                  decode_attn_window, decode_step, decode_step_window, multi_split_tokens, multi_workspace_bytes,
-                  profile_next_decode, split_tokens, window_span, workspace_bytes)
+                  decode_attn_window, decode_step, decode_step_noalloc, decode_step_window, multi_split_tokens,
+                  multi_workspace_bytes, noalloc_max_bytes, profile_next_decode, split_tokens, window_span,
+                  workspace_bytes)
 from .api import (append_mla, decode_attn_mla, decode_step_mla, mla_split_tokens,  # noqa: F401
                   mla_workspace_bytes)
 from ._lib import LIB_PATH, load  # noqa: F401

@@ -42,6 +42,13 @@ SIGNATURES = {
                                 c_void_p, c_void_p, c_void_p, c_void_p,
                                 c_int, c_int, c_int, c_float, c_void_p,
                                 c_int, c_void_p, c_size_t, c_void_p]),
+    "kvc_decode_step_noalloc": (c_int, [c_int, c_int, c_int, c_int, c_int,
+                                        c_void_p, c_void_p, c_void_p, c_void_p, c_int,
+                                        c_void_p, c_int, c_int, c_int, c_void_p,
+                                        c_void_p, c_void_p, c_void_p, c_void_p,
+                                        c_int, c_int, c_int, c_float, c_void_p,
+                                        c_int, c_void_p]),
+    "kvc_decode_step_noalloc_max_bytes": (c_size_t, []),
     "kvc_append_ring": (c_int, [c_int, c_int, c_int, c_int, c_int,
                                 c_void_p, c_void_p, c_int, c_void_p,
                                 c_void_p, c_void_p, c_void_p,
@@ -100,7 +107,7 @@ SIGNATURES = {
                                     c_size_t, c_void_p]),
 }
 
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 _lib = None
 

@@ -258,6 +258,47 @@ def decode_step(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     return out, q_rot_out
 
 
+def decode_step_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                        positions: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                        rope_cos: torch.Tensor, rope_sin: torch.Tensor, max_seq_len: int,
+                        q_rot_out: torch.Tensor, out: torch.Tensor,
+                        block_table: Optional[torch.Tensor] = None, rope_style: str = "interleaved",
+                        scale: Optional[float] = None, split_tokens: int = 0, stream=None) -> None:
+    """kvc_decode_step_noalloc: kvc_decode_step with the split partials in the
+    library's fixed device array; allocates nothing (out and q_rot_out are the
+    caller's).  Calls that overlap on one device race on that array."""
+    lib = _lib.load()
+    if out is None or q_rot_out is None:
+        raise ValueError("decode_step_noalloc allocates nothing: pass out and q_rot_out")
+    dt, B, H_q, d, out = _decode_args(q, out)
+    H_kv = k_new.shape[1]
+    if rope_cos.dim() != 2 or rope_cos.shape[1] != d // 2:
+        raise ValueError(f"rope_cos must be [rows, {d // 2}], got {tuple(rope_cos.shape)}")
+    if block_table is not None:
+        num_blocks, _, block_size, _ = k_cache.shape
+        T_max, mb = 0, block_table.shape[1]
+        tbl = _dev(block_table, "block_table", torch.int32, (B, mb))
+        shape = (num_blocks, H_kv, block_size, d)
+    else:
+        T_max = k_cache.shape[2]
+        tbl, block_size, mb, num_blocks = None, 0, 0, 0
+        shape = (B, H_kv, T_max, d)
+    _check(lib.kvc_decode_step_noalloc(
+        dt, B, H_q, H_kv, d, _dev(q, "q", q.dtype, (B, H_q, d)),
+        _dev(q_rot_out, "q_rot_out", q.dtype, (B, H_q, d)),
+        _dev(k_cache, "k_cache", q.dtype, shape), _dev(v_cache, "v_cache", q.dtype, shape), T_max,
+        tbl, block_size, mb, num_blocks, _dev(positions, "positions", torch.int32, (B,)),
+        _dev(k_new, "k_new", q.dtype, (B, H_kv, d)), _dev(v_new, "v_new", q.dtype, (B, H_kv, d)),
+        _dev(rope_cos, "rope_cos", torch.float32), _dev(rope_sin, "rope_sin", torch.float32, rope_cos.shape),
+        rope_cos.shape[0], ROPE_STYLES[rope_style], int(max_seq_len), float(scale) if scale else 0.0,
+        _dev(out, "out", q.dtype, (B, H_q, d)), int(split_tokens), _stream(q.device, stream)))
+
+
+def noalloc_max_bytes() -> int:
+    """kvc_decode_step_noalloc_max_bytes: size of the library's fixed partials array."""
+    return int(_lib.load().kvc_decode_step_noalloc_max_bytes())
+
+
 # ---------------------------------------------------------------------------
 # sliding window: attend the last `window` tokens (full cache or a ring)
 # ---------------------------------------------------------------------------

@@ -11,6 +11,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "kvc_internal.h"
 
@@ -656,6 +657,87 @@ kvc_status kvc_decode_step(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
                              workspace, workspace_bytes, stream, &st);
     return decode_common(dtype, B, H_q, H_kv, d, q, k_cache, v_cache, T_max, 0, 0, nullptr, 0, nullptr,
                          max_seq_len, scale, out, split_tokens, workspace, workspace_bytes, stream, &st);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// kvc_decode_step_noalloc: kvc_decode_step with its workspace in a fixed
+// array of device memory that the library owns, for callers that cannot
+// allocate.  Each device the library runs on holds its own copy of `scratch`
+// until the process ends; its device address is looked up once per device
+// (hipGetSymbolAddress, with that device current) and only that address is
+// handed to kernels - the array's name in host code is not a device address.
+// The split partials it holds are written before they are read in every
+// call, so nothing needs clearing; every call on a device shares the array,
+// so calls that overlap on one device race.
+// ---------------------------------------------------------------------------
+
+namespace {
+
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices];   // device address of `scratch` per device (nullptr: not looked up)
+
+kvc_status scratch_address(void** addr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "kvc_decode_step_noalloc: hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(KVC_ERR_UNSUPPORTED, "kvc_decode_step_noalloc: device index %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_addr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e, "kvc_decode_step_noalloc: hipGetSymbolAddress(scratch)");
+        if (p == nullptr || reinterpret_cast<uintptr_t>(p) % 256 != 0)
+            return fail(KVC_ERR_HIP, "kvc_decode_step_noalloc: scratch address %p unusable", p);
+        g_scratch_addr[dev] = p;
+    }
+    *addr = g_scratch_addr[dev];
+    return KVC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kvc_decode_step_noalloc_max_bytes(void) { return kScratchBytes; }
+
+kvc_status kvc_decode_step_noalloc(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
+                                   const void* q, void* q_rot_out, void* k_cache, void* v_cache, int T_max,
+                                   const int32_t* block_table, int block_size, int max_blocks_per_seq,
+                                   int num_blocks, const int32_t* positions, const void* k_new,
+                                   const void* v_new, const float* rope_cos, const float* rope_sin,
+                                   int rope_rows, int rope_style, int max_seq_len, float scale, void* out,
+                                   int split_tokens, void* stream) {
+    // the plan's workspace, checked against the fixed array before any HIP
+    // call (invalid sizes fall through to kvc_decode_step, which names them)
+    const long long pool_tokens =
+        block_table ? static_cast<long long>(num_blocks) * std::max(block_size, 0) : 0;
+    const size_t need = (B > 0 && max_seq_len >= 0 && pool_tokens >= 0)
+                            ? kvc_decode_workspace_bytes(dtype, B, H_q, H_kv, d, max_seq_len, pool_tokens,
+                                                         split_tokens)
+                            : 0;
+    if (need != static_cast<size_t>(-1) && need > kScratchBytes)
+        return fail(KVC_ERR_WORKSPACE,
+                    "kvc_decode_step_noalloc: this call needs %zu bytes of split partials, more than the %zu bytes "
+                    "of the library's fixed scratch (use kvc_decode_step with a workspace, or longer splits)",
+                    need, kScratchBytes);
+    if (B > 0 && (!q || !q_rot_out || !k_cache || !v_cache || !out || !positions || !k_new || !v_new || !rope_cos ||
+                  !rope_sin))
+        return fail(KVC_ERR_NULL, "kvc_decode_step_noalloc: a required pointer is NULL");
+    void* ws = nullptr;
+    if (B > 0 && need != static_cast<size_t>(-1)) {   // (invalid sizes: kvc_decode_step reports them)
+        const kvc_status st = scratch_address(&ws);
+        if (st != KVC_OK) return st;
+    }
+    return kvc_decode_step(dtype, B, H_q, H_kv, d, q, q_rot_out, k_cache, v_cache, T_max, block_table, block_size,
+                           max_blocks_per_seq, num_blocks, positions, k_new, v_new, rope_cos, rope_sin, rope_rows,
+                           rope_style, max_seq_len, scale, out, split_tokens, ws, kScratchBytes, stream);
 }
 
 kvc_status kvc_decode_attn_window(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const void* q,

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kvc_abi_version() == _lib.ABI_VERSION == 7
+    assert lib.kvc_abi_version() == _lib.ABI_VERSION == 8
     for s in range(6):
         assert lib.kvc_status_string(s)
     assert lib.kvc_status_string(99) == b"unknown status"
@@ -316,3 +316,29 @@ def test_latent_cache_plan(lib):
     one = ws(16, 32, 512, 200, 0)                                  # one split: one partial per head
     assert 2 * rows * 512 * 4 + rows * (512 + 2) * 4 <= one < 2 * rows * 512 * 4 + rows * (512 + 2) * 4 + 1024
     assert ws(16, 32, 384, 8193, 0) == (1 << 64) - 1
+
+
+def _noalloc(lib, **kw):
+    a = dict(dt=BF16, B=2, H_q=8, H_kv=2, d=128, q=FAKE, qr=FAKE, k=FAKE, v=FAKE, T_max=4096, tbl=None, bs=0,
+             mb=0, nb=0, pos=FAKE, kn=FAKE, vn=FAKE, cos=FAKE, sin=FAKE, rows=4096, style=0, max_len=4096,
+             scale=0.0, out=FAKE, split=0, stream=None)
+    a.update(kw)
+    return lib.kvc_decode_step_noalloc(a["dt"], a["B"], a["H_q"], a["H_kv"], a["d"], a["q"], a["qr"], a["k"],
+                                       a["v"], a["T_max"], a["tbl"], a["bs"], a["mb"], a["nb"], a["pos"], a["kn"],
+                                       a["vn"], a["cos"], a["sin"], a["rows"], a["style"], a["max_len"],
+                                       a["scale"], a["out"], a["split"], a["stream"])
+
+
+def test_noalloc_step_host_checks(lib):
+    """The entry point that allocates nothing refuses, on the host, a call whose
+    split partials would not fit its fixed array, and names invalid sizes as
+    kvc_decode_step does."""
+    cap = lib.kvc_decode_step_noalloc_max_bytes()
+    assert cap == 32 << 20
+    need = lib.kvc_decode_workspace_bytes(BF16, 64, 64, 8, 128, 4096, 0, 16)
+    assert need > cap
+    assert _noalloc(lib, B=64, H_q=64, H_kv=8, split=16) == KVC_ERR_WORKSPACE
+    assert b"scratch" in lib.kvc_last_error()
+    assert _noalloc(lib, H_q=6, H_kv=4) == KVC_ERR_SHAPE
+    assert _noalloc(lib, q=None) == KVC_ERR_NULL
+    assert _noalloc(lib, B=0) == KVC_OK
