@@ -532,6 +532,14 @@ def main():
 
     q_rot = torch.empty_like(q)
     q_work = q.clone()    # u8 step: the append rotates the query in place (rotation keeps its norm)
+    # the plain step (contiguous or paged cache): each replica's call checked
+    # once, as a serving loop that reuses its buffers would; launching it is
+    # then one foreign call
+    prepared = None
+    if not (u8 or multi or win):
+        prepared = [kvc.prepare_decode_step(q, ks[r], vs[r], pos, kn, vn, cos, sin, max_len, block_table=tbl,
+                                            q_rot_out=q_rot, out=out, split_tokens=args.split_tokens)
+                    for r in range(R)]
 
     def step(i, ev=None):
         r = i % R
@@ -559,8 +567,7 @@ def main():
             kvc.decode_step_window(q, ks[r], vs[r], pos, kn, vn, cos, sin, max_len, win, ring=args.ring,
                                    block_table=tbl, q_rot_out=q_rot, out=out, split_tokens=args.split_tokens)
             return
-        kvc.decode_step(q, ks[r], vs[r], pos, kn, vn, cos, sin, max_len, block_table=tbl, q_rot_out=q_rot,
-                        out=out, split_tokens=args.split_tokens)
+        prepared[r]()
 
     for i in range(args.warmup):
         step(i)

@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 8
+#define KVC_ABI_VERSION 9
 
 typedef enum kvc_status {
     KVC_OK = 0,
@@ -158,13 +158,26 @@ kvc_status kvc_append(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
  * contiguous cache; pass the same sizes as the decode call.
  *
  * The workspace holds the per-split partial results (running max and sum
- * per query head, weighted value sums) that the split kernel writes and the
- * merge kernel of the same call reads.  Its contents need no initialisation
- * and mean nothing between calls; calls that overlap in time must not share
- * a workspace.
+ * per query head, weighted value sums) and, in its first
+ * kvc_workspace_zeroed_bytes() bytes, one arrival counter per (sequence, KV
+ * head) that the splits of the bf16 matrix-core kernel count themselves in
+ * with: the last split of each to finish merges the partials, in the same
+ * launch.  Those first bytes must be zero before a workspace is first used
+ * (e.g. hipMemset once after allocating it); every call that runs to
+ * completion leaves them zero again, so a workspace needs no clearing between
+ * calls.  The rest needs no initialisation and means nothing between calls.
+ * Calls that overlap in time must not share a workspace.
  */
 size_t kvc_decode_workspace_bytes(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
                                   int max_seq_len, long long pool_tokens, int split_tokens);
+
+/*
+ * Length of the prefix of every decode and latent-cache workspace that holds
+ * the split kernels' arrival counters (64 KiB): zero before the workspace's
+ * first use, and left zero by every completed call.  A workspace of 0 bytes
+ * (kvc_decode_workspace_bytes returned 0) has none.
+ */
+size_t kvc_workspace_zeroed_bytes(void);
 
 /*
  * The split length (tokens per workgroup) a decode call with these sizes
@@ -176,7 +189,11 @@ size_t kvc_decode_workspace_bytes(kvc_dtype dtype, int B, int H_q, int H_kv, int
  * kernel, spread over B * H_kv sequence-head pairs); for a paged pool much
  * smaller than B * max_seq_len (ragged lengths), about four rounds of
  * shorter splits; never fewer than 32 * (H_q / H_kv) tokens, so that the
- * partial results stay a few percent of the bytes read.
+ * partial results stay a few percent of the bytes read.  With the library's
+ * choice over a contiguous bf16 cache, the last split of a sequence also
+ * takes a remainder shorter than one loop step of the kernel (64 tokens up
+ * to head_dim 128, else 128): 8193 tokens in splits of 4096 are two splits,
+ * of 4096 and 4097 tokens.
  */
 int kvc_decode_split_tokens(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_len,
                             long long pool_tokens, int split_tokens);
@@ -272,8 +289,10 @@ kvc_status kvc_decode_step(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
  * kvc_decode_step with a workspace of the caller's, serves such sizes.
  *
  * Every call on one device shares that device's array, which keeps whatever
- * the last call left in it (nothing needs clearing: every call writes the
- * partials it reads).  Calls that overlap in time on one device - on
+ * the last call left in it.  Its first kvc_workspace_zeroed_bytes() bytes are
+ * the arrival counters of a workspace (zero when the library is loaded, and
+ * left zero by every completed call); the rest needs no clearing, since every
+ * call writes the partials it reads.  Calls that overlap in time on one device - on
  * different streams, or from different threads - race on it and give
  * unspecified results; serialise them (one stream, or events).
  */
@@ -493,13 +512,15 @@ kvc_status kvc_append_mla(kvc_dtype dtype, int B, int d_latent, int rope_dim, vo
                           const int32_t* positions, const void* c_kv_new, const void* k_rope_new, void* stream);
 
 /*
- * Workspace bytes (256-byte aligned, no initialisation needed) and split
- * length of kvc_decode_attn_mla with these sizes (max_seq_len bounds the
- * attended lengths; split_tokens 0 = the library's choice, else a multiple of
- * 32).  (size_t)-1 / -1 for invalid or unsupported sizes.  The workspace holds
- * the absorbed queries and the merged latent context, [B, H, d_latent]
- * float32 each, and the split partials, [B, H, splits] (max, sum) pairs and
- * [B, H, splits, d_latent] float32.
+ * Workspace bytes (256-byte aligned) and split length of kvc_decode_attn_mla
+ * with these sizes (max_seq_len bounds the attended lengths; split_tokens 0 =
+ * the library's choice, else a multiple of 32).  (size_t)-1 / -1 for invalid
+ * or unsupported sizes.  Past the first kvc_workspace_zeroed_bytes() bytes,
+ * which these calls neither read nor write (so one buffer can serve them and
+ * the other decode calls), the workspace holds the absorbed queries and the
+ * merged latent context, [B, H, d_latent] float32 each, and the split
+ * partials, [B, H, splits] (max, sum) pairs and [B, H, splits, d_latent]
+ * float32; none of it needs initialisation.
  */
 size_t kvc_decode_mla_workspace_bytes(int B, int H, int d_latent, int max_seq_len, int split_tokens);
 int kvc_decode_mla_split_tokens(int B, int H, int d_latent, int max_seq_len, int split_tokens);

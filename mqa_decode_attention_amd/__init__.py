@@ -7,6 +7,7 @@ include/kvc.h); this package only marshals torch tensors into it:
     decode_attn(q, k_cache, v_cache, seq_lens, max_seq_len)
     decode_attn_paged(q, k_pool, v_pool, block_table, seq_lens, max_seq_len)
     decode_step(q, k_cache, v_cache, positions, k_new, v_new, rope_cos, rope_sin, max_seq_len, ...)
+    step = prepare_decode_step(...same arguments...); step()   # checked once, launched per call
 
 with a sliding window (the last `window` tokens of a full cache, or a ring of slots):
 
@@ -34,8 +35,9 @@ and for a latent cache (multi-head latent attention, one [c_kv | k_rope] row per
 from .api import (KVC_BF16, KVC_F32, KVC_U8, KvcError, append, append_multi, append_ring, append_u8,  # noqa: F401
                   decode_attn, decode_attn_multi, decode_attn_paged, decode_attn_paged_u8, decode_attn_u8,
                   decode_attn_window, decode_step, decode_step_noalloc, decode_step_window, multi_split_tokens,
-                  multi_workspace_bytes, noalloc_max_bytes, profile_next_decode, split_tokens, window_span,
-                  workspace_bytes)
+                  multi_workspace_bytes, noalloc_max_bytes, prepare_decode_step, PreparedCall, profile_next_decode,
+                  split_tokens, window_span,
+                  workspace_bytes, workspace_zeroed_bytes)
 from .api import (append_mla, decode_attn_mla, decode_step_mla, mla_split_tokens,  # noqa: F401
                   mla_workspace_bytes)
 from ._lib import LIB_PATH, load  # noqa: F401

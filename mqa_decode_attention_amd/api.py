@@ -115,6 +115,12 @@ def workspace_bytes(dtype: torch.dtype, B: int, H_q: int, H_kv: int, d: int, max
     return n
 
 
+def workspace_zeroed_bytes() -> int:
+    """kvc_workspace_zeroed_bytes: the prefix of a caller's `workspace` tensor
+    that must be zero before its first use (every completed call leaves it so)."""
+    return _lib.load().kvc_workspace_zeroed_bytes()
+
+
 def split_tokens(dtype: torch.dtype, B: int, H_q: int, H_kv: int, d: int, max_seq_len: int,
                  split_tokens: int = 0, pool_tokens: int = 0) -> int:
     """kvc_decode_split_tokens: the split length a decode call with these sizes uses."""
@@ -140,8 +146,10 @@ def _workspace(device: torch.device, stream_handle: int, nbytes: int) -> Tuple[O
     key = (device.index if device.index is not None else torch.cuda.current_device(), stream_handle)
     ws = _WORKSPACES.get(key)
     if ws is None or ws.numel() < nbytes:
+        # (zeroed once: its first bytes hold the split kernels' arrival
+        # counters, which every completed call leaves at zero)
         with torch.cuda.stream(torch.cuda.ExternalStream(stream_handle, device=device)):
-            ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+            ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
         _WORKSPACES[key] = ws
     return ws.data_ptr(), ws.numel()
 
@@ -223,6 +231,59 @@ def decode_step(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
 
     q is the raw query (left unchanged); returns (out, q_rot_out).
     """
+    fn, args, out, q_rot_out = _step_call(q, k_cache, v_cache, positions, k_new, v_new, rope_cos, rope_sin,
+                                          max_seq_len, block_table, rope_style, q_rot_out, out, scale, split_tokens,
+                                          workspace, stream)
+    _check(fn(*args))
+    return out, q_rot_out
+
+
+class PreparedCall:
+    """A library call whose arguments were checked and converted once: each
+    call of this object makes that one foreign call again, on the same
+    buffers and stream, with no other host work (the form a serving loop that
+    reuses its buffers every step wants).  Returns what the call returns."""
+
+    __slots__ = ("_fn", "_args", "_result", "_keep")
+
+    def __init__(self, fn, args, result, keep=()):
+        self._fn = fn
+        # (values already of the declared ctypes types pass through the
+        # foreign call without conversion)
+        self._args = tuple(a if a is None else t(a) for t, a in zip(fn.argtypes, args))
+        self._result = result
+        self._keep = keep          # the tensors whose addresses the arguments hold
+
+    def __call__(self):
+        status = self._fn(*self._args)
+        if status:
+            _check(status)
+        return self._result
+
+
+def prepare_decode_step(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                        positions: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                        rope_cos: torch.Tensor, rope_sin: torch.Tensor, max_seq_len: int,
+                        block_table: Optional[torch.Tensor] = None, rope_style: str = "interleaved",
+                        q_rot_out: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                        scale: Optional[float] = None, split_tokens: int = 0,
+                        workspace: Optional[torch.Tensor] = None, stream=None) -> PreparedCall:
+    """decode_step's checks and argument conversion done once, the launch left
+    for later: returns a PreparedCall that runs kvc_decode_step on these
+    buffers (their contents at that time) and returns (out, q_rot_out).  The
+    tensors must stay alive and in place while it is used."""
+    fn, args, out, q_rot_out = _step_call(q, k_cache, v_cache, positions, k_new, v_new, rope_cos, rope_sin,
+                                          max_seq_len, block_table, rope_style, q_rot_out, out, scale, split_tokens,
+                                          workspace, stream)
+    if workspace is None:       # the library's own workspace for this stream, held for the call object's life
+        workspace = _WORKSPACES.get((q.device.index if q.device.index is not None else torch.cuda.current_device(),
+                                     args[-1]))
+    return PreparedCall(fn, args, (out, q_rot_out),
+                        (q, k_cache, v_cache, positions, k_new, v_new, rope_cos, rope_sin, block_table, workspace))
+
+
+def _step_call(q, k_cache, v_cache, positions, k_new, v_new, rope_cos, rope_sin, max_seq_len, block_table,
+               rope_style, q_rot_out, out, scale, split_tokens, workspace, stream):
     lib = _lib.load()
     dt, B, H_q, d, out = _decode_args(q, out)
     H_kv = k_new.shape[1]
@@ -246,16 +307,15 @@ def decode_step(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         ws, wsn = _dev(workspace, "workspace", torch.uint8), workspace.numel()
     else:
         ws, wsn = _workspace(q.device, st, need)
-    _check(lib.kvc_decode_step(
-        dt, B, H_q, H_kv, d, _dev(q, "q", q.dtype, (B, H_q, d)),
-        _dev(q_rot_out, "q_rot_out", q.dtype, (B, H_q, d)),
-        _dev(k_cache, "k_cache", q.dtype, shape), _dev(v_cache, "v_cache", q.dtype, shape), T_max,
-        tbl, block_size, mb, num_blocks, _dev(positions, "positions", torch.int32, (B,)),
-        _dev(k_new, "k_new", q.dtype, (B, H_kv, d)), _dev(v_new, "v_new", q.dtype, (B, H_kv, d)),
-        _dev(rope_cos, "rope_cos", torch.float32), _dev(rope_sin, "rope_sin", torch.float32, rope_cos.shape),
-        rope_cos.shape[0], ROPE_STYLES[rope_style], int(max_seq_len), float(scale) if scale else 0.0,
-        _dev(out, "out", q.dtype, (B, H_q, d)), int(split_tokens), ws, wsn, st))
-    return out, q_rot_out
+    args = (dt, B, H_q, H_kv, d, _dev(q, "q", q.dtype, (B, H_q, d)),
+            _dev(q_rot_out, "q_rot_out", q.dtype, (B, H_q, d)),
+            _dev(k_cache, "k_cache", q.dtype, shape), _dev(v_cache, "v_cache", q.dtype, shape), T_max,
+            tbl, block_size, mb, num_blocks, _dev(positions, "positions", torch.int32, (B,)),
+            _dev(k_new, "k_new", q.dtype, (B, H_kv, d)), _dev(v_new, "v_new", q.dtype, (B, H_kv, d)),
+            _dev(rope_cos, "rope_cos", torch.float32), _dev(rope_sin, "rope_sin", torch.float32, rope_cos.shape),
+            rope_cos.shape[0], ROPE_STYLES[rope_style], int(max_seq_len), float(scale) if scale else 0.0,
+            _dev(out, "out", q.dtype, (B, H_q, d)), int(split_tokens), ws, wsn, st)
+    return lib.kvc_decode_step, args, out, q_rot_out
 
 
 def decode_step_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

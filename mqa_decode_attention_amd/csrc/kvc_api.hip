@@ -123,10 +123,16 @@ bool plan_decode(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_l
         return false;
     }
     const long long units = static_cast<long long>(B) * H_kv * pl.n_chunks;
+    // workgroups of the streaming kernel the device holds at once
+    const long long slots = static_cast<long long>(cu_count()) *
+                            (u8 ? decode_u8_wgs_per_cu(d, G)
+                                : (pl.mfma ? decode_mfma_wgs_per_cu(d, pl.heads_per_wg, pool_tokens > 0) : 1));
     const int tile = u8 ? decode_u8_step_tokens()
                         : (pl.mfma ? decode_mfma_step_tokens(d, pool_tokens > 0) : decode_tile_tokens(dtype, d));
     const int L = std::max(max_seq_len, 1);
     long long ts;
+    int tail = 0;       // tokens the last split may take beyond split_tokens
+    auto n_of = [&](long long t) { return std::max(1LL, (L - tail + t - 1) / t); };
     if (split_tokens > 0) {
         ts = split_tokens;
         if ((L + ts - 1) / ts > kMaxSplits) {
@@ -146,9 +152,6 @@ bool plan_decode(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_l
         // partial rows, about G / split_tokens of the bytes it reads: at
         // least 32 * G tokens per split keeps that near 3 %, 12 * G (for
         // the large groups) near 8 %.
-        const long long slots = static_cast<long long>(cu_count()) *
-                                (u8 ? decode_u8_wgs_per_cu(d, G)
-                                    : decode_mfma_wgs_per_cu(d, pl.heads_per_wg, pool_tokens > 0));
         const long long full = units * L;
         const int rpw = pl.heads_per_wg;      // query rows per workgroup
         const bool large_group = rpw > 16;
@@ -158,12 +161,25 @@ bool plan_decode(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_l
             const long long S = std::max(1LL, (large_group ? 3 : 1) * slots / std::max(1LL, units));
             ts = (L + S - 1) / S;
         }
-        ts = std::max<long long>(ts, (large_group ? 12LL : 32LL) * rpw);
+        const long long least = (large_group ? 12LL : 32LL) * rpw;
+        ts = std::max<long long>(ts, least);
         // Whole loop steps of the kernel (64 or 128 tokens): splits that
         // start off a step boundary (e.g. balanced 4112 + 4081 for 8193
         // tokens with 128-token steps) streamed 2-13 % slower.
-        ts = (ts + tile - 1) / tile * tile;
-        while ((L + ts - 1) / ts > kMaxSplits) ts += tile;
+        const long long up = (ts + tile - 1) / tile * tile;
+        const long long dn = ts / tile * tile;
+        ts = up;
+        if (!u8 && pool_tokens == 0 && qlen <= 1) {
+            // Over a contiguous cache the last split also takes a remainder
+            // of less than one step: 8193 tokens are two splits of 4096 and
+            // 4097 rather than 4160 and 4033 (the longest split one step
+            // shorter; its extra token is the step's new one, patched in
+            // from registers with no memory read), and no split of a few
+            // tokens pays a whole prologue.
+            tail = tile - 1;
+            if (dn >= least && n_of(dn) <= n_of(up)) ts = dn;
+        }
+        while (n_of(ts) > kMaxSplits) ts += tile;
     } else {
         long long want = units > 0 ? (kTargetWorkgroups + units - 1) / units : 1;
         want = std::max(1LL, std::min<long long>(want, kMaxSplits));
@@ -172,12 +188,21 @@ bool plan_decode(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_l
         while ((L + ts - 1) / ts > kMaxSplits) ts += tile;
     }
     pl.split_tokens = static_cast<int>(std::min<long long>(ts, 0x7FFFFFFF));
-    pl.n_splits = static_cast<int>((L + ts - 1) / ts);
+    pl.split_tail = tail;
+    pl.n_splits = static_cast<int>(n_of(ts));
     if (pl.n_splits > 1) {
         const size_t bh = static_cast<size_t>(B) * H_q * std::max(qlen, 1);   // output rows
-        pl.ws_ml = 0;
-        pl.ws_part = align_up(bh * pl.n_splits * sizeof(float2), 256);
+        pl.ws_ml = kWsCounterBytes;
+        pl.ws_part = align_up(pl.ws_ml + bh * pl.n_splits * sizeof(float2), 256);
         pl.ws_bytes = align_up(pl.ws_part + bh * pl.n_splits * d * sizeof(float), 256);
+        // The bf16 matrix-core kernel merges the splits of a unit in its last
+        // split to finish when all its workgroups fit in one round: each
+        // split then waits for its partial rows to be written and for its
+        // count (a few microseconds), once, in place of a merge launch.  With
+        // several rounds that wait would hold a workgroup slot every round.
+        // (Partial offsets stay below 2^31 for its 32-bit buffer offsets.)
+        pl.merge_in_kernel = pl.mfma && !u8 && units <= kMergeCounters && units * pl.n_splits <= slots &&
+                             pl.ws_bytes - pl.ws_part < (size_t{1} << 31);
     }
     *plan = pl;
     return true;
@@ -189,6 +214,8 @@ bool plan_mla(int B, int H, int d_latent, int max_seq_len, int split_tokens, Mla
     const long long units = static_cast<long long>(B) * pl.n_chunks;
     const int L = std::max(max_seq_len, 1);
     long long ts;
+    int tail = 0;       // tokens the last split may take beyond split_tokens
+    auto n_of = [&](long long t) { return std::max(1LL, (L - tail + t - 1) / t); };
     if (split_tokens > 0) {
         if (split_tokens % kMlaTile != 0) {
             *why = "split_tokens must be a multiple of 32 for the latent-cache kernel";
@@ -215,8 +242,10 @@ bool plan_mla(int B, int H, int d_latent, int max_seq_len, int split_tokens, Mla
     pl.split_tokens = static_cast<int>(ts);
     pl.n_splits = static_cast<int>((L + ts - 1) / ts);
     const size_t rows = static_cast<size_t>(B) * H;
-    pl.qt = 0;
-    pl.ctx = align_up(rows * d_latent * sizeof(float), 256);
+    // (after the merge counters every workspace starts with, which this
+    // kernel leaves alone, so one buffer can serve both kinds of call)
+    pl.qt = kWsCounterBytes;
+    pl.ctx = pl.qt + align_up(rows * d_latent * sizeof(float), 256);
     pl.ws_ml = pl.ctx + align_up(rows * d_latent * sizeof(float), 256);
     pl.ws_part = pl.ws_ml + align_up(rows * pl.n_splits * sizeof(float2), 256);
     pl.ws_bytes = pl.ws_part + align_up(rows * pl.n_splits * d_latent * sizeof(float), 256);
@@ -382,6 +411,8 @@ kvc_status kvc_append_u8(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
     p.rope_style = rope_style;
     return hip_status(kvc::launch_append_u8(p, static_cast<hipStream_t>(stream)), "kvc_append_u8 launch");
 }
+
+size_t kvc_workspace_zeroed_bytes(void) { return kvc::kWsCounterBytes; }
 
 size_t kvc_decode_workspace_bytes(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
                                   int max_seq_len, long long pool_tokens, int split_tokens) {
@@ -552,10 +583,16 @@ kvc_status decode_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const
     char* ws = static_cast<char*>(workspace);
     p.ws_part = pl.ws_bytes ? reinterpret_cast<float*>(ws + pl.ws_part) : nullptr;
     p.ws_ml = pl.ws_bytes ? reinterpret_cast<float2*>(ws + pl.ws_ml) : nullptr;
+    // the bf16 matrix-core kernel merges the splits itself when the plan says
+    // so: the last split of each unit to finish (counted in the workspace's
+    // first bytes) does it
+    const bool merge_in_kernel = pl.merge_in_kernel;
+    p.merge_cnt = merge_in_kernel ? reinterpret_cast<unsigned*>(ws) : nullptr;
     p.B = B; p.H_q = H_q; p.H_kv = H_kv; p.G = H_q / H_kv; p.n_chunks = pl.n_chunks;
     p.T_max = T_max; p.block_size = block_size; p.max_blocks_per_seq = max_blocks_per_seq;
     p.num_blocks = num_blocks;
     p.max_seq_len = max_seq_len; p.split_tokens = pl.split_tokens; p.n_splits = pl.n_splits;
+    p.split_tail = pl.split_tail;
     p.window = ring ? 0 : window;
     p.ring = ring ? 1 : 0;
     p.align = paged ? 16 : 1;
@@ -611,7 +648,7 @@ kvc_status decode_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const
     else e = pl.mfma ? kvc::launch_decode_mfma(d, qlen > 1 ? pl.heads_per_wg : p.G, paged, fused, multi, p, hs, tm)
                      : kvc::launch_decode_split(dtype, d, pl.heads_per_wg, paged, p, hs, tm);
     if (e != hipSuccess) return hip_status(e, "decode split launch");
-    if (pl.n_splits > 1) {
+    if (pl.n_splits > 1 && !merge_in_kernel) {
         e = kvc::launch_decode_merge(u8 ? KVC_BF16 : dtype, d, p, hs);
         if (e != hipSuccess) return hip_status(e, "decode merge launch");
     }

@@ -159,7 +159,7 @@ decode_split_kernel(const DecodeParams p) {
     const int nsp = split_count(p, tr);
     if (split >= nsp) return;
     const int t_begin = tr.org + split * p.split_tokens;
-    const int t_end = min(tr.hi, t_begin + p.split_tokens);
+    const int t_end = split_end(p, tr, split, nsp);
     const int t_lo = tr.lo;                     // rows before it (window) are masked, never read
 
     const int tid = threadIdx.x;

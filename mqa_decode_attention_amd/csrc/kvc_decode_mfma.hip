@@ -49,6 +49,11 @@ namespace {
 
 using namespace mfma;
 
+// Cache policy of device-scope buffer accesses (sc1): coherent across the
+// XCDs without any cache flush - the split partials one workgroup writes and
+// another merges in the same launch.
+constexpr int kDevScope = 16;
+
 // MODE 0: contiguous cache.  MODE 1: paged, any block size (each row's block
 // looked up per lane).  MODE 2: paged with block_size % 16 == 0 and splits
 // starting on 32-token boundaries, so every 16-row group of a tile lies in one
@@ -128,7 +133,7 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     const int nsp = split_count(p, tr);
     if (split >= nsp) return;
     const int t_begin = tr.org + split * p.split_tokens;
-    const int t_end = min(tr.hi, t_begin + p.split_tokens);
+    const int t_end = split_end(p, tr, split, nsp);
     const int t_lo = tr.lo;
 
     const int tid = threadIdx.x;
@@ -193,7 +198,13 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     // row t_end of this (sequence, KV head): rows past the split read as zeros
     // without touching memory, so no clamping is needed.  Paged caches clamp
     // the row to t_end - 1 (always a valid, finite row of this sequence).
-    const size_t rows_bytes = static_cast<size_t>(t_end) * D * 2;
+    // In the fused step the new token's row is patched into its tile from
+    // registers (below), so the range of the split holding it stops before
+    // that row: it is never read, and a last step holding only it reads
+    // nothing from memory.
+    const bool patch_new = FUSED && MODE == 0 && split == nsp - 1 && pos >= 0 && pos < p.capacity &&
+                           pos < p.rope_rows && pos < t_end;
+    const size_t rows_bytes = static_cast<size_t>(patch_new ? pos : t_end) * D * 2;
     const __amdgpu_buffer_rsrc_t krs = make_uniform_rsrc(kbase + seq_off, static_cast<int>(rows_bytes));
     const __amdgpu_buffer_rsrc_t vrs = make_uniform_rsrc(vbase + seq_off, static_cast<int>(rows_bytes));
 
@@ -746,6 +757,9 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     constexpr int NCH = D / 4;            // 16-byte chunks per row
     static_assert(NW * RB * D * 4 <= NW * STAGE && RB >= 4, "merge area");
     auto chunk_at = [](int row, int ch) { return ch ^ ((4 * row) & (NCH - 1)); };
+    // (the in-kernel merge's partials: offsets below 2^31, as planned)
+    const __amdgpu_buffer_rsrc_t part_rs = make_uniform_rsrc(p.ws_part, 0x7FFFFFFF);
+    const __amdgpu_buffer_rsrc_t ml_rs = make_uniform_rsrc(p.ws_ml, 0x7FFFFFFF);
     float* sm_o = reinterpret_cast<float*>(vbuf0);                // [NW][RB][D]
     float* sm_m = reinterpret_cast<float*>(KLDS ? kbuf : vbuf1);  // [NW][16]
     float* sm_l = sm_m + NW * 16;                                   // [NW][16]
@@ -808,12 +822,105 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
                     packed.y = static_cast<uint32_t>(f32_to_bf16_rne(Ls > 0.0f ? A.z / Ls : 0.0f)) |
                                (static_cast<uint32_t>(f32_to_bf16_rne(Ls > 0.0f ? A.w / Ls : 0.0f)) << 16);
                     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + bh * D + c) = packed;
+                } else if (p.merge_cnt != nullptr) {
+                    // device-scope stores (written through to memory that
+                    // every XCD sees), for the merge below
+                    const int o = static_cast<int>(((bh * p.n_splits + split) * D + c) * 4);
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, A), part_rs, o, 0, kDevScope);
+                    if (ch == 0)
+                        __builtin_amdgcn_raw_buffer_store_b64(
+                            __builtin_bit_cast(u32x2_t, make_float2(M, Ls)), ml_rs,
+                            static_cast<int>((bh * p.n_splits + split) * 8), 0, kDevScope);
                 } else {
                     *reinterpret_cast<float4*>(p.ws_part + (bh * p.n_splits + split) * D + c) = A;
                     if (ch == 0) p.ws_ml[bh * p.n_splits + split] = make_float2(M, Ls);
                 }
             }
             __syncthreads();
+        }
+    }
+
+    // ---- merge of the unit's splits by the last of them to finish.  The
+    // partial rows above went out as device-scope stores; once they have
+    // completed, each split counts itself in.  The increment wraps at
+    // nsp - 1, so the split that reads nsp - 1 is the last (it leaves the
+    // counter at zero for the next call) and reads every split's rows back
+    // with device-scope loads.  No workgroup ever waits for another, and no
+    // cache is flushed.  The merge: M = max_s m_s, w_s = 2^(m_s - M),
+    // out = sum_s w_s acc_s / sum_s w_s l_s, the splits in order, MB of them
+    // requested at a time (their max folded into the running one).
+    if (nsp > 1 && p.merge_cnt != nullptr) {
+        __shared__ int s_last;
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __syncthreads();
+        if (tid == 0)
+            s_last = __builtin_amdgcn_atomic_inc32(p.merge_cnt + unit, static_cast<unsigned>(nsp - 1),
+                                                   __ATOMIC_RELAXED, "agent") == static_cast<unsigned>(nsp - 1);
+        __syncthreads();
+        if (!s_last) return;
+        constexpr int MB = 8;
+        const int rows = MQ ? min(16 * HB, G * p.qlen - chunk * 16 * HB) : G;
+        for (int idx = tid; idx < rows * NCH; idx += NT) {
+            const int gr = idx / NCH;
+            const int c = 4 * (idx % NCH);
+            size_t bh;
+            if constexpr (MQ) {
+                const int rho = chunk * 16 * HB + gr;
+                const int qi = rho / G;
+                bh = (static_cast<size_t>(b) * p.qlen + qi) * p.H_q + j * G + (rho - qi * G);
+            } else {
+                bh = static_cast<size_t>(b) * p.H_q + j * G + gr;
+            }
+            const int ml0 = static_cast<int>(bh * p.n_splits * 8);
+            const int part0 = static_cast<int>((bh * p.n_splits * D + c) * 4);
+            float M = -INFINITY, Ls = 0.0f;
+            float4 A = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            for (int s0 = 0; s0 < nsp; s0 += MB) {
+                float mv[MB], lv[MB];
+                float4 pv[MB];
+#pragma unroll
+                for (int u = 0; u < MB; ++u) {
+                    if (s0 + u < nsp) {
+                        const int sp = s0 + u;
+                        const float2 m2 = __builtin_bit_cast(
+                            float2, __builtin_amdgcn_raw_buffer_load_b64(ml_rs, ml0 + 8 * sp, 0, kDevScope));
+                        mv[u] = m2.x;
+                        lv[u] = m2.y;
+                        pv[u] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                               part_rs, part0 + 4 * D * sp, 0, kDevScope));
+                    }
+                }
+                float Mb = M;
+#pragma unroll
+                for (int u = 0; u < MB; ++u)
+                    if (s0 + u < nsp) Mb = fmaxf(Mb, mv[u]);
+                // (split maxima are finite, so after the first batch M is too)
+                const float r = s0 == 0 ? 0.0f : fast_exp2(M - Mb);
+                A.x *= r;
+                A.y *= r;
+                A.z *= r;
+                A.w *= r;
+                Ls *= r;
+                M = Mb;
+#pragma unroll
+                for (int u = 0; u < MB; ++u) {
+                    if (s0 + u < nsp) {
+                        const float w = fast_exp2(mv[u] - M);
+                        A.x = fmaf(w, pv[u].x, A.x);
+                        A.y = fmaf(w, pv[u].y, A.y);
+                        A.z = fmaf(w, pv[u].z, A.z);
+                        A.w = fmaf(w, pv[u].w, A.w);
+                        Ls = fmaf(w, lv[u], Ls);
+                    }
+                }
+            }
+            const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
+            uint2 packed;
+            packed.x = static_cast<uint32_t>(f32_to_bf16_rne(A.x * inv)) |
+                       (static_cast<uint32_t>(f32_to_bf16_rne(A.y * inv)) << 16);
+            packed.y = static_cast<uint32_t>(f32_to_bf16_rne(A.z * inv)) |
+                       (static_cast<uint32_t>(f32_to_bf16_rne(A.w * inv)) << 16);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + bh * D + c) = packed;
         }
     }
 }

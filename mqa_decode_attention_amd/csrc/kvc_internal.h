@@ -47,14 +47,27 @@ struct DecodePlan {
     int heads_per_wg;   // query heads one workgroup serves (a divisor of G)
     int n_chunks;       // G / heads_per_wg
     int split_tokens;   // tokens per split
+    int split_tail;     // the last split of a sequence takes up to this many tokens more
     int n_splits;       // splits of the longest sequence (>= 1)
     size_t ws_ml;       // byte offsets inside the workspace
     size_t ws_part;
     size_t ws_bytes;    // 0 when n_splits == 1
+    bool merge_in_kernel;   // the streaming kernel merges the splits (no merge launch)
 };
 
 // Largest split count the merge step supports (partials live in LDS).
 constexpr int kMaxSplits = 256;
+
+// Every decode and latent-cache workspace starts with kMergeCounters 32-bit
+// arrival counters, one per (sequence, KV head, chunk) unit: the matrix-core
+// kernel's splits count themselves in, and the last one to arrive merges the
+// unit's partial results (no separate merge launch).  The counters must be
+// zero before a workspace is first used; the last arrival's increment wraps
+// its counter back to zero, so every completed call leaves them zero.  Only
+// plans of one round of workgroups merge so (see plan_decode); the others,
+// and plans with more units, merge in a separate launch.
+constexpr int kMergeCounters = 16384;
+constexpr size_t kWsCounterBytes = kMergeCounters * sizeof(unsigned);
 
 // Block-table entries of one split that the paged kernels with staged tiles
 // keep in LDS (4 KiB).  The bf16 kernel falls back to per-group table reads
@@ -71,9 +84,11 @@ struct DecodeParams {
     const int32_t* block_table;  // NULL => contiguous
     float* ws_part;              // [B*H_q, n_splits, d]   weighted-value partials
     float2* ws_ml;               // [B*H_q, n_splits]      (running max (log2), sum)
+    unsigned* merge_cnt;         // [units] arrival counters (in-kernel merge), or NULL
     int B, H_q, H_kv, G, n_chunks;
     int T_max, block_size, max_blocks_per_seq, num_blocks;
     int max_seq_len, split_tokens, n_splits;
+    int split_tail;              // the last split also takes up to this many tokens (a short remainder)
     int n_wg, n_wg_pad;          // logical workgroups, padded to a multiple of 8
     float scale_log2;            // softmax scale * log2(e)
 
@@ -119,7 +134,7 @@ __device__ __forceinline__ int attended_len(const DecodeParams& p, int b) {
 
 // Tokens a decode of a sequence holding L tokens attends, [lo, hi), and the
 // origin org of its splits: split s covers [org + s * split_tokens, ...) up to
-// hi.  org is lo rounded down to p.align (16 for the paged kernels, whose tiles
+// hi, the last one to hi (a remainder of up to split_tail tokens joins it).  org is lo rounded down to p.align (16 for the paged kernels, whose tiles
 // are 16-row groups of one block); those kernels mask the rows in [org, lo)
 // and do not read them.
 struct TokenRange {
@@ -141,8 +156,13 @@ __device__ __forceinline__ TokenRange token_range(const DecodeParams& p, int L) 
 }
 // Splits of that range (at least 1).
 __device__ __forceinline__ int split_count(const DecodeParams& p, const TokenRange& r) {
-    const int n = (r.hi - r.org + p.split_tokens - 1) / p.split_tokens;
+    const int n = (r.hi - r.org - p.split_tail + p.split_tokens - 1) / p.split_tokens;
     return n < 1 ? 1 : n;
+}
+// End of split s of nsp (exclusive).
+__device__ __forceinline__ int split_end(const DecodeParams& p, const TokenRange& r, int s, int nsp) {
+    const int e = r.org + (s + 1) * p.split_tokens;
+    return (s == nsp - 1 || e > r.hi) ? r.hi : e;
 }
 
 // Returns false (and leaves *plan untouched) when the sizes cannot be planned.

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kvc_abi_version() == _lib.ABI_VERSION == 8
+    assert lib.kvc_abi_version() == _lib.ABI_VERSION == 9
     for s in range(6):
         assert lib.kvc_status_string(s)
     assert lib.kvc_status_string(99) == b"unknown status"
@@ -163,10 +163,15 @@ def test_workspace_sizes(lib):
     ws = lib.kvc_decode_workspace_bytes
     assert ws(F32, 1, 4, 4, 16, 6, 0, 0) == 0                     # one split, no workspace
     assert ws(BF16, 16, 32, 8, 128, 8193, 0, 0) > 0
-    # explicit split: partials for B*H_q heads, n_splits each, d + 2 floats, 256-aligned regions
+    # explicit split: the arrival counters (one per sequence and KV head, in a
+    # fixed 64 KiB prefix), then partials for B*H_q heads, n_splits each,
+    # d + 2 floats, 256-aligned regions
+    zb = lib.kvc_workspace_zeroed_bytes()
+    assert zb == 16384 * 4
     n = ws(BF16, 16, 32, 8, 128, 8193, 0, 1024)
     splits = -(-8193 // 1024)
-    assert n >= 16 * 32 * splits * (128 + 2) * 4 and n % 256 == 0
+    assert n >= zb + 16 * 32 * splits * (128 + 2) * 4 and n % 256 == 0
+    assert n < zb + 16 * 32 * splits * (128 + 2) * 4 + 1024
     assert ws(BF16, 16, 32, 8, 128, 8193, 0, 8193) == 0
     assert ws(BF16, 16, 30, 8, 128, 8193, 0, 0) == (1 << 64) - 1  # invalid sizes
     assert ws(BF16, 16, 32, 8, 128, 8193, -1, 0) == (1 << 64) - 1
@@ -182,10 +187,22 @@ def test_split_choice(lib):
     st = lib.kvc_decode_split_tokens
     # contiguous d = 128: one workgroup per CU, 256 slots
     # (splits are whole 64-token steps)
-    assert st(BF16, 16, 32, 8, 128, 8193, 0, 0) == 4160         # 128 units: 2 splits
-    assert st(BF16, 1, 64, 8, 128, 131073, 0, 0) == 4160        # 8 units: 32 splits
+    # (the last split of a contiguous cache also takes a remainder shorter
+    # than one step, so 8193 tokens are 4096 + 4097, not 4160 + 4033)
+    wsb = lib.kvc_decode_workspace_bytes
+    zb = lib.kvc_workspace_zeroed_bytes()
+    assert st(BF16, 16, 32, 8, 128, 8193, 0, 0) == 4096         # 128 units: 2 splits
+    assert wsb(BF16, 16, 32, 8, 128, 8193, 0, 0) == zb + 16 * 32 * 2 * (8 + 128 * 4)
+    assert st(BF16, 1, 64, 8, 128, 131073, 0, 0) == 4096        # 8 units: 32 splits
+    assert wsb(BF16, 1, 64, 8, 128, 131073, 0, 0) == zb + 64 * 32 * (8 + 128 * 4)
     assert st(BF16, 64, 32, 1, 128, 4097, 0, 0) == 384          # G = 32: ~3 per slot, >= 12 * G tokens
-    assert st(BF16, 16, 32, 8, 64, 8193, 0, 0) == 2112          # d = 64: two per CU, 512 slots
+    assert st(BF16, 16, 32, 8, 64, 8193, 0, 0) == 2048          # d = 64: two per CU, 512 slots
+    assert st(BF16, 16, 32, 8, 256, 8193, 0, 0) == 4096         # d = 256: 128-token steps, 4096 + 4097
+    # a remainder of a whole step or more is a split of its own
+    assert wsb(BF16, 16, 32, 8, 128, 8193 + 63, 0, 0) == wsb(BF16, 16, 32, 8, 128, 8193, 0, 0)
+    assert st(BF16, 16, 32, 8, 128, 8193 + 64, 0, 0) == 4160
+    # explicit splits and paged pools keep whole splits: no remainder joins
+    assert wsb(BF16, 16, 32, 8, 128, 8193, 0, 4096) == zb + 16 * 32 * 3 * (8 + 128 * 4)
     assert st(BF16, 16, 32, 8, 128, 8193, 0, 1000) == 1000      # explicit split kept
     # paged pool holding about half of B * max_seq_len tokens: ~4 rounds of
     # splits over 768 slots (three per CU): 17408 * 16 * 8 / (4 * 768) = 725.3 -> 768
@@ -311,10 +328,11 @@ def test_latent_cache_plan(lib):
     assert st(16, 32, 512, 8193, 96) == 96
     rows = 16 * 32
     splits = -(-8193 // 544)
+    zb = lib.kvc_workspace_zeroed_bytes()                         # (left to the other decode calls)
     n = ws(16, 32, 512, 8193, 0)
-    assert n >= 2 * rows * 512 * 4 + rows * splits * (512 + 2) * 4 and n % 256 == 0
+    assert n >= zb + 2 * rows * 512 * 4 + rows * splits * (512 + 2) * 4 and n % 256 == 0
     one = ws(16, 32, 512, 200, 0)                                  # one split: one partial per head
-    assert 2 * rows * 512 * 4 + rows * (512 + 2) * 4 <= one < 2 * rows * 512 * 4 + rows * (512 + 2) * 4 + 1024
+    assert zb + 2 * rows * 512 * 4 + rows * (512 + 2) * 4 <= one < zb + 2 * rows * 512 * 4 + rows * (512 + 2) * 4 + 1024
     assert ws(16, 32, 384, 8193, 0) == (1 << 64) - 1
 
 

@@ -208,9 +208,14 @@ def test_full_size(name):
 
 def test_workspace_reuse_across_shapes():
     """One workspace buffer shared by calls of different shapes, filled with
-    garbage first: no call may depend on what an earlier call left in it."""
+    garbage first past its zeroed prefix (the arrival counters): no call may
+    depend on what an earlier call left in it, and every call leaves the
+    counters at zero."""
     import mqa_decode_attention_amd as kvc
     ws = torch.full((64 << 20,), 0x7F, dtype=torch.uint8, device="cuda")
+    zb = kvc.workspace_zeroed_bytes()
+    assert zb > 0 and zb % 256 == 0
+    ws[:zb].zero_()
     cases = [SMALL["long_gqa"], SMALL["mqa_ragged"], SMALL["gqa_8b"], SMALL["long_gqa"]]
     for i, w in enumerate(cases):
         x = W.draw(w)
@@ -223,6 +228,7 @@ def test_workspace_reuse_across_shapes():
             torch.cuda.synchronize()
             k2, v2, q2 = oracle_append(x)
             compare_out(out, oracle_decode(x, k2, v2, q2), w.dtype, f"reuse {w.name} split={split}")
+            assert int(torch.count_nonzero(ws[:zb])) == 0, "arrival counters left nonzero"
 
 
 GROUP_CASES = [

@@ -132,3 +132,71 @@ def test_step_full_size(name):
     assert np.array_equal(bits(v), np.ascontiguousarray(v2).view(np.uint8)), "V cache differs from the oracle"
     assert np.array_equal(bits(q_rot), np.ascontiguousarray(q2).view(np.uint8)), "rotated q differs"
     compare_out(out, oracle_decode(x, k2, v2, q2), w.dtype, f"step {name} full size")
+
+
+@pytest.mark.parametrize("name", ["gqa_8b", "paged_gqa", "mqa_ragged"])
+def test_prepared_step_equals_decode_step(name):
+    """prepare_decode_step checks once and launches per call: each call gives
+    bit for bit what decode_step gives on the buffers' contents at that time
+    (a second call after the positions and the new token moved on)."""
+    import mqa_decode_attention_amd as kvc
+    x = W.draw(CASES[name])
+    say(f"[prepared step {name}]")
+    s = GpuStep(x)
+    k, v = s.k.clone(), s.v.clone()
+    q = x.q.to("cuda")
+    pos = s.pos.clone()
+    kn, vn = s.kn.clone(), s.vn.clone()
+    out, q_rot = torch.empty_like(q), torch.empty_like(q)
+    call = kvc.prepare_decode_step(q, k, v, pos, kn, vn, s.cos, s.sin, s.max_len + 1, block_table=s.tbl,
+                                   q_rot_out=q_rot, out=out)
+    k2, v2 = s.k.clone(), s.v.clone()
+    for rnd in range(2):
+        got = call()
+        assert got[0] is out and got[1] is q_rot
+        ref_out, ref_q = kvc.decode_step(q, k2, v2, pos, kn, vn, s.cos, s.sin, s.max_len + 1, block_table=s.tbl)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(k), bits(k2)) and np.array_equal(bits(v), bits(v2)), f"caches differ ({rnd})"
+        assert np.array_equal(bits(q_rot), bits(ref_q)), f"rotated q differs ({rnd})"
+        assert np.array_equal(bits(out), bits(ref_out)), f"output differs ({rnd})"
+        # the next step: one position on, a new token
+        pos += 1
+        kn.copy_(torch.randn(kn.shape, generator=torch.Generator().manual_seed(rnd)).to(kn.dtype))
+        vn.copy_(torch.randn(vn.shape, generator=torch.Generator().manual_seed(rnd + 9)).to(vn.dtype))
+
+
+def test_last_split_takes_short_remainder():
+    """With the library's split length over a contiguous cache, a sequence
+    whose length exceeds a multiple of it by less than one kernel step (64
+    tokens) has that remainder in its last split (4096 + 4097 for 8193
+    tokens); by 64 or more, a split of its own.  Lengths on both sides of
+    that edge, through the fused step and append + decode, against the
+    oracle."""
+    import mqa_decode_attention_amd as kvc
+    # (drawn with every sequence full, then cut to the lengths wanted: slots
+    # at and past each new length hold NaN again)
+    w = W.WORKLOADS["gqa_8b"].replace(B=4, cached_lo=1099, cached_hi=1099, T_max=1104)
+    x = W.draw(w)
+    M = 1100
+    ts = kvc.split_tokens(torch.bfloat16, w.B, w.H_q, w.H_kv, w.d, M)
+    q = (M - 64) // ts
+    lens = [q * ts + 1, q * ts + 63, q * ts + 64, M]
+    assert len(set(lens)) == 4 and max(lens) == M and all(L % ts for L in lens[:3])
+    x.cached[:] = torch.tensor([L - 1 for L in lens], dtype=torch.int32)
+    x.seq_lens[:] = torch.tensor(lens, dtype=torch.int32)
+    for b, c in enumerate(x.cached.tolist()):
+        x.k_cache[b, :, c:] = float("nan")
+        x.v_cache[b, :, c:] = float("nan")
+    say(f"[remainder] split {ts}, lengths {lens}")
+    s = GpuStep(x)
+    assert s.max_len == M
+    k, v, q_rot, out = run_step(s)
+    a = GpuStep(x)
+    a.append()
+    out_a = a.decode()
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(k), bits(a.k)) and np.array_equal(bits(v), bits(a.v))
+    assert np.array_equal(bits(out), bits(out_a)), "step differs from append + decode"
+    k2, v2, q2 = oracle_append(x)
+    assert np.array_equal(bits(k), np.ascontiguousarray(k2).view(np.uint8))
+    compare_out(out, oracle_decode(x, k2, v2, q2), w.dtype, "remainder in the last split")
