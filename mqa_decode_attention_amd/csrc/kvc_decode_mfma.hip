@@ -105,7 +105,7 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     __shared__ __attribute__((aligned(16))) char kbuf[KLDS ? NW * STAGE : 16];
     __shared__ __attribute__((aligned(16))) char kbuf1[NSTG == 2 ? NW * STAGE : 16];
     __shared__ int tbl_lds[MODE == 3 ? kTblMax : 1];
-    static_assert(NW * STAGE >= 2 * NW * 16 * 4, "merge area (m, l)");
+    __shared__ float sm_ml[2 * NW * 16];   // the waves' (m, l) per head row, for their merge
 
     // Workgroups in launch order: the splits of one (sequence, KV head) are
     // neighbours, and the hardware deals consecutive workgroups to the XCDs
@@ -748,21 +748,27 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, vn), vsrs, (lane % LPR) * 16, 0, 0);
     }
     // The waves' partial results go through LDS, RB head rows at a time:
-    // [NW][RB][D] floats of O fit in one V buffer (RB = 8 for 16-row tiles,
-    // 16 for 32-row tiles), so up to 8 heads take one pass.  Rows are D
-    // floats apart, a multiple of the bank count: the 16-byte chunks of row
-    // r are XOR-swizzled by 4r, so the lanes writing one column block of
-    // several rows hit distinct banks.
-    constexpr int RB = (STAGE / (4 * D)) < 16 ? (STAGE / (4 * D)) : 16;
+    // [NW][RB1][D] floats of O fit in one stage buffer (RB1 = 8 for 16-row
+    // tiles, 16 for 32-row tiles); with K staged too, rows RB1.. go to the K
+    // buffer, so a whole 16-head block takes one pass (two barriers) at
+    // every tile height.  Rows are D floats apart, a multiple of the bank
+    // count: the 16-byte chunks of row r are XOR-swizzled by 4r, so the
+    // lanes writing one column block of several rows hit distinct banks.
+    constexpr int RB1 = (STAGE / (4 * D)) < 16 ? (STAGE / (4 * D)) : 16;
+    constexpr bool TWO = KLDS && RB1 < 16 && !MQ;   // (the multi-token kernel has no registers to spare)
+    constexpr int RB = TWO ? 2 * RB1 : RB1;
     constexpr int NCH = D / 4;            // 16-byte chunks per row
-    static_assert(NW * RB * D * 4 <= NW * STAGE && RB >= 4, "merge area");
+    static_assert(NW * RB1 * D * 4 <= NW * STAGE && RB >= 4, "merge area");
     auto chunk_at = [](int row, int ch) { return ch ^ ((4 * row) & (NCH - 1)); };
+    auto o_row = [&](int w, int row) __attribute__((always_inline)) {
+        char* region = (TWO && row >= RB1) ? kbuf : vbuf0;
+        return reinterpret_cast<float*>(region) + (w * RB1 + (TWO && row >= RB1 ? row - RB1 : row)) * D;
+    };
     // (the in-kernel merge's partials: offsets below 2^31, as planned)
     const __amdgpu_buffer_rsrc_t part_rs = make_uniform_rsrc(p.ws_part, 0x7FFFFFFF);
     const __amdgpu_buffer_rsrc_t ml_rs = make_uniform_rsrc(p.ws_ml, 0x7FFFFFFF);
-    float* sm_o = reinterpret_cast<float*>(vbuf0);                // [NW][RB][D]
-    float* sm_m = reinterpret_cast<float*>(KLDS ? kbuf : vbuf1);  // [NW][16]
-    float* sm_l = sm_m + NW * 16;                                   // [NW][16]
+    float* sm_m = sm_ml;                  // [NW][16]
+    float* sm_l = sm_ml + NW * 16;        // [NW][16]
     const int NT = NW * 64;
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
@@ -776,7 +782,7 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
             // lane holds O^T[c][g] for c = 16*nb + 4*q4 + e, g = 16*hb + r16
             const int row = r16 - r0;
             if (row >= 0 && row < RB && r16 < heads) {
-                float* dst = sm_o + (wave * RB + row) * D;
+                float* dst = o_row(wave, row);
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
                     *reinterpret_cast<float4*>(dst + 4 * chunk_at(row, 4 * nb + q4)) =
@@ -799,7 +805,7 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
                 for (int w = 0; w < NW; ++w) {
                     const float mw = sm_m[w * 16 + gh];
                     const float f = (mw == -kNoMax) ? 0.0f : fast_exp2(mw - M);
-                    const float4 ow = *reinterpret_cast<const float4*>(sm_o + (w * RB + gr) * D + at);
+                    const float4 ow = *reinterpret_cast<const float4*>(o_row(w, gr) + at);
                     A.x = fmaf(ow.x, f, A.x);
                     A.y = fmaf(ow.y, f, A.y);
                     A.z = fmaf(ow.z, f, A.z);
@@ -816,11 +822,12 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
                 }
                 const int c = 4 * ch;
                 if (nsp == 1) {
+                    const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
                     uint2 packed;
-                    packed.x = static_cast<uint32_t>(f32_to_bf16_rne(Ls > 0.0f ? A.x / Ls : 0.0f)) |
-                               (static_cast<uint32_t>(f32_to_bf16_rne(Ls > 0.0f ? A.y / Ls : 0.0f)) << 16);
-                    packed.y = static_cast<uint32_t>(f32_to_bf16_rne(Ls > 0.0f ? A.z / Ls : 0.0f)) |
-                               (static_cast<uint32_t>(f32_to_bf16_rne(Ls > 0.0f ? A.w / Ls : 0.0f)) << 16);
+                    packed.x = static_cast<uint32_t>(f32_to_bf16_rne(A.x * inv)) |
+                               (static_cast<uint32_t>(f32_to_bf16_rne(A.y * inv)) << 16);
+                    packed.y = static_cast<uint32_t>(f32_to_bf16_rne(A.z * inv)) |
+                               (static_cast<uint32_t>(f32_to_bf16_rne(A.w * inv)) << 16);
                     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + bh * D + c) = packed;
                 } else if (p.merge_cnt != nullptr) {
                     // device-scope stores (written through to memory that
