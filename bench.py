@@ -531,12 +531,17 @@ def main():
     torch.cuda.synchronize()
 
     q_rot = torch.empty_like(q)
-    q_work = q.clone()    # u8 step: the append rotates the query in place (rotation keeps its norm)
+    q_work = q.clone()    # multi-token step: the append rotates the query in place (rotation keeps its norm)
     # the plain step (contiguous or paged cache): each replica's call checked
     # once, as a serving loop that reuses its buffers would; launching it is
     # then one foreign call
     prepared = None
-    if not (u8 or multi or win):
+    if u8:
+        prepared = [kvc.prepare_decode_step_u8(q, ks[r][0], ks[r][1], vs[r][0], vs[r][1], pos, kn, vn, cos, sin,
+                                               max_len, block_table=tbl, q_rot_out=q_rot, out=out,
+                                               split_tokens=args.split_tokens)
+                    for r in range(R)]
+    elif not (multi or win):
         prepared = [kvc.prepare_decode_step(q, ks[r], vs[r], pos, kn, vn, cos, sin, max_len, block_table=tbl,
                                             q_rot_out=q_rot, out=out, split_tokens=args.split_tokens)
                     for r in range(R)]
@@ -544,15 +549,9 @@ def main():
     def step(i, ev=None):
         r = i % R
         if u8:
-            (kc, ksz), (vc, vsz) = ks[r], vs[r]
-            kvc.append_u8(kc, ksz, vc, vsz, pos, kn, vn, cos, sin, q=q_work, block_table=tbl)
             if ev is not None:
                 kvc.profile_next_decode(ev[0], ev[1])
-            if tbl is not None:
-                kvc.decode_attn_paged_u8(q_work, kc, ksz, vc, vsz, tbl, lens, max_len, out=out,
-                                         split_tokens=args.split_tokens)
-            else:
-                kvc.decode_attn_u8(q_work, kc, ksz, vc, vsz, lens, max_len, out=out, split_tokens=args.split_tokens)
+            prepared[r]()
             return
         if multi:
             kvc.append_multi(ks[r], vs[r], pos, kn, vn, cos, sin, q=q_work, block_table=tbl)
@@ -639,11 +638,12 @@ def main():
         "hbm_pct_step": round(100 * value / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": ("decode_u8_kernel (streaming pass over the codes; the append and the split merge "
-                                "are separate small kernels)") if u8 else
+                     "kernel": ("decode_u8_kernel (streaming pass over the codes with the fused append; a one-round "
+                                "plan merges its splits in the same launch, else a small merge kernel follows)") if u8 else
                                ("decode_mfma_kernel, multi-token rows (one pass over the cache for all new tokens' "
                                 "queries; the append and the split merge are separate small kernels)") if multi else
-                               "decode_mfma_kernel (streaming pass with the fused append; the split merge is a separate small kernel)",
+                               ("decode_mfma_kernel (streaming pass with the fused append; a one-round plan merges "
+                                "its splits in the same launch, else a small merge kernel follows)"),
                      "bytes_per_launch": kv_bytes},
         "wall_s_timed": round(wall, 4),
     }

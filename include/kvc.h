@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 9
+#define KVC_ABI_VERSION 10
 
 typedef enum kvc_status {
     KVC_OK = 0,
@@ -477,6 +477,27 @@ kvc_status kvc_decode_attn_paged_u8(int B, int H_q, int H_kv, int d, const void*
                                     int block_size, const int32_t* block_table, int max_blocks_per_seq,
                                     const int32_t* seq_lens, int max_seq_len, float scale, void* out,
                                     int split_tokens, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kvc_decode_step_u8 - kvc_append_u8 then kvc_decode_attn_u8 (block_table
+ * NULL) or kvc_decode_attn_paged_u8 in one launch over a quantized cache: the
+ * decode step of kvc_decode_step with the new key and value stored as codes
+ * and pairs (quantized exactly as kvc_append_u8 does) and attended from those.
+ * q is the raw bf16 query (left unchanged); its rotation (kvc_append's, bf16)
+ * goes to q_rot_out.  Sequence b attends positions[b] + 1 tokens (0 when the
+ * position is outside the cache or the rotation table, and nothing is then
+ * stored).  Sizes, layouts, workspace and split rules as for kvc_decode_step
+ * and kvc_decode_attn[_paged]_u8 (kvc_decode_workspace_bytes /
+ * kvc_decode_split_tokens with dtype KVC_U8); T_max is ignored when
+ * block_table is given.  The results, codes and pairs are bit for bit those of
+ * the two calls with the same split length.
+ */
+kvc_status kvc_decode_step_u8(int B, int H_q, int H_kv, int d, const void* q, void* q_rot_out, void* k_codes,
+                              float* k_sz, void* v_codes, float* v_sz, int T_max, const int32_t* block_table,
+                              int block_size, int max_blocks_per_seq, int num_blocks, const int32_t* positions,
+                              const void* k_new, const void* v_new, const float* rope_cos, const float* rope_sin,
+                              int rope_rows, int rope_style, int max_seq_len, float scale, void* out,
+                              int split_tokens, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Latent cache (multi-head latent attention), following the

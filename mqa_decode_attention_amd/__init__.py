@@ -25,6 +25,7 @@ and, for a uint8 quantized cache (codes plus a (step, zero point) pair per vecto
     append_u8(k_codes, k_sz, v_codes, v_sz, positions, k_new, v_new, rope_cos, rope_sin, ...)
     decode_attn_u8(q, k_codes, k_sz, v_codes, v_sz, seq_lens, max_seq_len)
     decode_attn_paged_u8(q, k_codes, k_sz, v_codes, v_sz, block_table, seq_lens, max_seq_len)
+    decode_step_u8(q, k_codes, k_sz, v_codes, v_sz, positions, k_new, v_new, rope_cos, rope_sin, max_seq_len, ...)
 
 and for a latent cache (multi-head latent attention, one [c_kv | k_rope] row per token):
 
@@ -34,7 +35,8 @@ and for a latent cache (multi-head latent attention, one [c_kv | k_rope] row per
 """
 from .api import (KVC_BF16, KVC_F32, KVC_U8, KvcError, append, append_multi, append_ring, append_u8,  # noqa: F401
                   decode_attn, decode_attn_multi, decode_attn_paged, decode_attn_paged_u8, decode_attn_u8,
-                  decode_attn_window, decode_step, decode_step_noalloc, decode_step_window, multi_split_tokens,
+                  decode_attn_window, decode_step, decode_step_noalloc, decode_step_u8, decode_step_window,
+                  multi_split_tokens, prepare_decode_step_u8,
                   multi_workspace_bytes, noalloc_max_bytes, prepare_decode_step, PreparedCall, profile_next_decode,
                   split_tokens, window_span,
                   workspace_bytes, workspace_zeroed_bytes)

@@ -94,6 +94,10 @@ SIGNATURES = {
                                          c_int, c_void_p, c_int,
                                          c_void_p, c_int, c_float, c_void_p,
                                          c_int, c_void_p, c_size_t, c_void_p]),
+    "kvc_decode_step_u8": (c_int, [c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
+                                   c_void_p, c_void_p, c_int, c_void_p, c_int, c_int, c_int, c_void_p,
+                                   c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_float,
+                                   c_void_p, c_int, c_void_p, c_size_t, c_void_p]),
     "kvc_append_mla": (c_int, [c_int, c_int, c_int, c_int, c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p]),
     "kvc_decode_mla_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int]),
     "kvc_decode_mla_split_tokens": (c_int, [c_int, c_int, c_int, c_int, c_int]),
@@ -108,7 +112,7 @@ SIGNATURES = {
                                     c_size_t, c_void_p]),
 }
 
-ABI_VERSION = 9
+ABI_VERSION = 10
 
 _lib = None
 

@@ -639,6 +639,80 @@ def decode_attn_paged_u8(q: torch.Tensor, k_codes: torch.Tensor, k_sz: torch.Ten
     return out
 
 
+def decode_step_u8(q: torch.Tensor, k_codes: torch.Tensor, k_sz: torch.Tensor, v_codes: torch.Tensor,
+                   v_sz: torch.Tensor, positions: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                   rope_cos: torch.Tensor, rope_sin: torch.Tensor, max_seq_len: int,
+                   block_table: Optional[torch.Tensor] = None, rope_style: str = "interleaved",
+                   q_rot_out: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                   scale: Optional[float] = None, split_tokens: int = 0,
+                   workspace: Optional[torch.Tensor] = None, stream=None):
+    """kvc_decode_step_u8: the decode step over a quantized cache (contiguous
+    codes [B, H_kv, T_max, d] or pools [num_blocks, H_kv, block_size, d] with a
+    block table), append and attention in one launch; returns (out, q_rot_out)."""
+    fn, args, out, q_rot_out = _step_u8_call(q, k_codes, k_sz, v_codes, v_sz, positions, k_new, v_new, rope_cos,
+                                             rope_sin, max_seq_len, block_table, rope_style, q_rot_out, out, scale,
+                                             split_tokens, workspace, stream)
+    _check(fn(*args))
+    return out, q_rot_out
+
+
+def prepare_decode_step_u8(q: torch.Tensor, k_codes: torch.Tensor, k_sz: torch.Tensor, v_codes: torch.Tensor,
+                           v_sz: torch.Tensor, positions: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                           rope_cos: torch.Tensor, rope_sin: torch.Tensor, max_seq_len: int,
+                           block_table: Optional[torch.Tensor] = None, rope_style: str = "interleaved",
+                           q_rot_out: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                           scale: Optional[float] = None, split_tokens: int = 0,
+                           workspace: Optional[torch.Tensor] = None, stream=None) -> PreparedCall:
+    """decode_step_u8 checked once, launched per call (as prepare_decode_step)."""
+    fn, args, out, q_rot_out = _step_u8_call(q, k_codes, k_sz, v_codes, v_sz, positions, k_new, v_new, rope_cos,
+                                             rope_sin, max_seq_len, block_table, rope_style, q_rot_out, out, scale,
+                                             split_tokens, workspace, stream)
+    if workspace is None:
+        workspace = _WORKSPACES.get((q.device.index if q.device.index is not None else torch.cuda.current_device(),
+                                     args[-1]))
+    return PreparedCall(fn, args, (out, q_rot_out),
+                        (q, k_codes, k_sz, v_codes, v_sz, positions, k_new, v_new, rope_cos, rope_sin, block_table,
+                         workspace))
+
+
+def _step_u8_call(q, k_codes, k_sz, v_codes, v_sz, positions, k_new, v_new, rope_cos, rope_sin, max_seq_len,
+                  block_table, rope_style, q_rot_out, out, scale, split_tokens, workspace, stream):
+    lib = _lib.load()
+    B, H_q, d = q.shape
+    H_kv = k_new.shape[1]
+    out = torch.empty_like(q) if out is None else out
+    q_rot_out = torch.empty_like(q) if q_rot_out is None else q_rot_out
+    if rope_cos.dim() != 2 or rope_cos.shape[1] != d // 2:
+        raise ValueError(f"rope_cos must be [rows, {d // 2}], got {tuple(rope_cos.shape)}")
+    if block_table is not None:
+        num_blocks, _, block_size, _ = k_codes.shape
+        T_max, mb = 0, block_table.shape[1]
+        tbl = _dev(block_table, "block_table", torch.int32, (B, mb))
+        lead = (num_blocks, H_kv, block_size)
+        pool_tokens = num_blocks * block_size
+    else:
+        T_max = k_codes.shape[2]
+        tbl, block_size, mb, num_blocks = None, 0, 0, 0
+        lead = (B, H_kv, T_max)
+        pool_tokens = 0
+    st = _stream(q.device, stream)
+    need = workspace_bytes(torch.uint8, B, H_q, H_kv, d, max_seq_len, split_tokens, pool_tokens=pool_tokens)
+    if workspace is not None:
+        ws, wsn = _dev(workspace, "workspace", torch.uint8), workspace.numel()
+    else:
+        ws, wsn = _workspace(q.device, st, need)
+    args = (B, H_q, H_kv, d, _dev(q, "q", torch.bfloat16, (B, H_q, d)),
+            _dev(q_rot_out, "q_rot_out", torch.bfloat16, (B, H_q, d)),
+            _dev(k_codes, "k_codes", torch.uint8, lead + (d,)), _dev(k_sz, "k_sz", torch.float32, lead + (2,)),
+            _dev(v_codes, "v_codes", torch.uint8, lead + (d,)), _dev(v_sz, "v_sz", torch.float32, lead + (2,)),
+            T_max, tbl, block_size, mb, num_blocks, _dev(positions, "positions", torch.int32, (B,)),
+            _dev(k_new, "k_new", torch.bfloat16, (B, H_kv, d)), _dev(v_new, "v_new", torch.bfloat16, (B, H_kv, d)),
+            _dev(rope_cos, "rope_cos", torch.float32), _dev(rope_sin, "rope_sin", torch.float32, rope_cos.shape),
+            rope_cos.shape[0], ROPE_STYLES[rope_style], int(max_seq_len), float(scale) if scale else 0.0,
+            _dev(out, "out", torch.bfloat16, (B, H_q, d)), int(split_tokens), ws, wsn, st)
+    return lib.kvc_decode_step_u8, args, out, q_rot_out
+
+
 # ---------------------------------------------------------------------------
 # Latent cache (multi-head latent attention): cache [B, T_max, d_latent + rope_dim]
 # ---------------------------------------------------------------------------

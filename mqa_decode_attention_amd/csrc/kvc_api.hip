@@ -201,7 +201,7 @@ bool plan_decode(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_l
         // count (a few microseconds), once, in place of a merge launch.  With
         // several rounds that wait would hold a workgroup slot every round.
         // (Partial offsets stay below 2^31 for its 32-bit buffer offsets.)
-        pl.merge_in_kernel = pl.mfma && !u8 && units <= kMergeCounters && units * pl.n_splits <= slots &&
+        pl.merge_in_kernel = pl.mfma && units <= kMergeCounters && units * pl.n_splits <= slots &&
                              pl.ws_bytes - pl.ws_part < (size_t{1} << 31);
     }
     *plan = pl;
@@ -583,7 +583,7 @@ kvc_status decode_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const
     char* ws = static_cast<char*>(workspace);
     p.ws_part = pl.ws_bytes ? reinterpret_cast<float*>(ws + pl.ws_part) : nullptr;
     p.ws_ml = pl.ws_bytes ? reinterpret_cast<float2*>(ws + pl.ws_ml) : nullptr;
-    // the bf16 matrix-core kernel merges the splits itself when the plan says
+    // the matrix-core kernels merge the splits themselves when the plan says
     // so: the last split of each unit to finish (counted in the workspace's
     // first bytes) does it
     const bool merge_in_kernel = pl.merge_in_kernel;
@@ -644,7 +644,8 @@ kvc_status decode_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const
             p.q = step->q_rot_out;
         }
     }
-    if (u8) e = kvc::launch_decode_u8(d, p.G, paged, p, k_sz, v_sz, hs, tm);
+    if (u8)
+        e = kvc::launch_decode_u8(d, p.G, paged, fused, p, const_cast<float*>(k_sz), const_cast<float*>(v_sz), hs, tm);
     else e = pl.mfma ? kvc::launch_decode_mfma(d, qlen > 1 ? pl.heads_per_wg : p.G, paged, fused, multi, p, hs, tm)
                      : kvc::launch_decode_split(dtype, d, pl.heads_per_wg, paged, p, hs, tm);
     if (e != hipSuccess) return hip_status(e, "decode split launch");
@@ -843,6 +844,24 @@ kvc_status kvc_decode_attn_paged_u8(int B, int H_q, int H_kv, int d, const void*
     return decode_common(KVC_U8, B, H_q, H_kv, d, q, k_codes, v_codes, 0, num_blocks, block_size, block_table,
                          max_blocks_per_seq, seq_lens, max_seq_len, scale, out, split_tokens, workspace,
                          workspace_bytes, stream, nullptr, k_sz, v_sz);
+}
+
+kvc_status kvc_decode_step_u8(int B, int H_q, int H_kv, int d, const void* q, void* q_rot_out, void* k_codes,
+                              float* k_sz, void* v_codes, float* v_sz, int T_max, const int32_t* block_table,
+                              int block_size, int max_blocks_per_seq, int num_blocks, const int32_t* positions,
+                              const void* k_new, const void* v_new, const float* rope_cos, const float* rope_sin,
+                              int rope_rows, int rope_style, int max_seq_len, float scale, void* out,
+                              int split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+    StepArgs st{positions, k_new, v_new, q_rot_out, rope_cos, rope_sin, rope_rows, rope_style};
+    if (block_table) {
+        if (block_size % 16 != 0)
+            return fail(KVC_ERR_UNSUPPORTED, "the quantized paged kernel needs block_size a multiple of 16");
+        return decode_common(KVC_U8, B, H_q, H_kv, d, q, k_codes, v_codes, 0, num_blocks, block_size, block_table,
+                             max_blocks_per_seq, nullptr, max_seq_len, scale, out, split_tokens, workspace,
+                             workspace_bytes, stream, &st, k_sz, v_sz);
+    }
+    return decode_common(KVC_U8, B, H_q, H_kv, d, q, k_codes, v_codes, T_max, 0, 0, nullptr, 0, nullptr,
+                         max_seq_len, scale, out, split_tokens, workspace, workspace_bytes, stream, &st, k_sz, v_sz);
 }
 
 }  // extern "C"

@@ -49,10 +49,6 @@ namespace {
 
 using namespace mfma;
 
-// Cache policy of device-scope buffer accesses (sc1): coherent across the
-// XCDs without any cache flush - the split partials one workgroup writes and
-// another merges in the same launch.
-constexpr int kDevScope = 16;
 
 // MODE 0: contiguous cache.  MODE 1: paged, any block size (each row's block
 // looked up per lane).  MODE 2: paged with block_size % 16 == 0 and splits
@@ -865,70 +861,16 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
                                                    __ATOMIC_RELAXED, "agent") == static_cast<unsigned>(nsp - 1);
         __syncthreads();
         if (!s_last) return;
-        constexpr int MB = 8;
         const int rows = MQ ? min(16 * HB, G * p.qlen - chunk * 16 * HB) : G;
-        for (int idx = tid; idx < rows * NCH; idx += NT) {
-            const int gr = idx / NCH;
-            const int c = 4 * (idx % NCH);
-            size_t bh;
+        merge_split_rows<D>(p, part_rs, ml_rs, rows, nsp, [&](int gr) -> size_t {
             if constexpr (MQ) {
                 const int rho = chunk * 16 * HB + gr;
                 const int qi = rho / G;
-                bh = (static_cast<size_t>(b) * p.qlen + qi) * p.H_q + j * G + (rho - qi * G);
+                return (static_cast<size_t>(b) * p.qlen + qi) * p.H_q + j * G + (rho - qi * G);
             } else {
-                bh = static_cast<size_t>(b) * p.H_q + j * G + gr;
+                return static_cast<size_t>(b) * p.H_q + j * G + gr;
             }
-            const int ml0 = static_cast<int>(bh * p.n_splits * 8);
-            const int part0 = static_cast<int>((bh * p.n_splits * D + c) * 4);
-            float M = -INFINITY, Ls = 0.0f;
-            float4 A = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            for (int s0 = 0; s0 < nsp; s0 += MB) {
-                float mv[MB], lv[MB];
-                float4 pv[MB];
-#pragma unroll
-                for (int u = 0; u < MB; ++u) {
-                    if (s0 + u < nsp) {
-                        const int sp = s0 + u;
-                        const float2 m2 = __builtin_bit_cast(
-                            float2, __builtin_amdgcn_raw_buffer_load_b64(ml_rs, ml0 + 8 * sp, 0, kDevScope));
-                        mv[u] = m2.x;
-                        lv[u] = m2.y;
-                        pv[u] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                               part_rs, part0 + 4 * D * sp, 0, kDevScope));
-                    }
-                }
-                float Mb = M;
-#pragma unroll
-                for (int u = 0; u < MB; ++u)
-                    if (s0 + u < nsp) Mb = fmaxf(Mb, mv[u]);
-                // (split maxima are finite, so after the first batch M is too)
-                const float r = s0 == 0 ? 0.0f : fast_exp2(M - Mb);
-                A.x *= r;
-                A.y *= r;
-                A.z *= r;
-                A.w *= r;
-                Ls *= r;
-                M = Mb;
-#pragma unroll
-                for (int u = 0; u < MB; ++u) {
-                    if (s0 + u < nsp) {
-                        const float w = fast_exp2(mv[u] - M);
-                        A.x = fmaf(w, pv[u].x, A.x);
-                        A.y = fmaf(w, pv[u].y, A.y);
-                        A.z = fmaf(w, pv[u].z, A.z);
-                        A.w = fmaf(w, pv[u].w, A.w);
-                        Ls = fmaf(w, lv[u], Ls);
-                    }
-                }
-            }
-            const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
-            uint2 packed;
-            packed.x = static_cast<uint32_t>(f32_to_bf16_rne(A.x * inv)) |
-                       (static_cast<uint32_t>(f32_to_bf16_rne(A.y * inv)) << 16);
-            packed.y = static_cast<uint32_t>(f32_to_bf16_rne(A.z * inv)) |
-                       (static_cast<uint32_t>(f32_to_bf16_rne(A.w * inv)) << 16);
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + bh * D + c) = packed;
-        }
+        });
     }
 }
 

@@ -27,6 +27,15 @@
 // completed.  MODE 0: contiguous codes [B, H_kv, T_max, d], pairs
 // [B, H_kv, T_max, 2].  MODE 3: pools [N_blk, H_kv, bs, d] / [.., bs, 2] with
 // bs % 16 == 0; the split's slice of the block table is staged in LDS.
+//
+// Fused step (FUSED): the append runs inside the streaming pass, as in the
+// bf16 kernel.  Every workgroup rotates its queries in registers; the last
+// split of a (sequence, KV head) also rotates the new key (float32, not
+// rounded), quantizes it and the raw new value exactly as the append kernel
+// does (min and max over the vector, step = (max - min) / 255, zero point and
+// codes rounded to nearest even and clamped to [0, 255]), patches the codes
+// and pairs into the tile it loaded (the stored row may not have landed yet)
+// and stores them once all its loads are done.
 
 #include <type_traits>
 
@@ -58,10 +67,9 @@ __device__ __forceinline__ uint4 codes8_to_bf16(uint2 c) {
     return r;
 }
 
-template <int D, int HB, int MODE>
+template <int D, int HB, int MODE, bool FUSED>
 __global__ void __launch_bounds__(kNWq * 64)
-decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, const float* __restrict__ k_sz,
-                 const float* __restrict__ v_sz) {
+decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, float* k_sz, float* v_sz) {
     constexpr bool PAGED = MODE == 3;
     constexpr int NW = kNWq;
     constexpr int TT = kTTq;
@@ -98,7 +106,8 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
     const int j = unit % p.H_kv;
     const int G = p.G;
     // (the quantized entry points have no window: the range is [0, L))
-    const int L = attended_len(p, b);
+    const int pos = FUSED ? p.positions[b] : 0;
+    const int L = FUSED ? len_from_position(p, pos) : attended_len(p, b);
     int nsp = (L + p.split_tokens - 1) / p.split_tokens;
     nsp = nsp < 1 ? 1 : nsp;
     if (split >= nsp) return;
@@ -204,7 +213,8 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
         }
     }
     const size_t qgrp = (static_cast<size_t>(b) * p.H_q + static_cast<size_t>(j) * G) * D;
-    const __amdgpu_buffer_rsrc_t qrs = make_uniform_rsrc(static_cast<const uint16_t*>(p.q) + qgrp, G * D * 2);
+    const __amdgpu_buffer_rsrc_t qrs =
+        make_uniform_rsrc(static_cast<const uint16_t*>(FUSED ? p.q_raw : p.q) + qgrp, G * D * 2);
     uint4 qb[HB][KK];
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb)
@@ -212,6 +222,40 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
         for (int kk = 0; kk < KK; ++kk)
             qb[hb][kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                 qrs, ((16 * hb + r16) * D + 32 * kk + 8 * q4) * 2, 0, 0));
+
+    // Fused step: the new key and value in the operand layout (lane (r16, q4)
+    // holds elements 32 kk + 8 q4 .. +7 of chunk kk; the last split only -
+    // other workgroups get a zero range) and the rotation row of the slot.
+    const bool pos_ok = FUSED && pos >= 0 && pos < p.capacity && pos < p.rope_rows;
+    const bool own = pos_ok && split == nsp - 1;
+    const bool half = FUSED && p.rope_style == KVC_ROPE_HALF;
+    uint4 kraw[FUSED ? KK : 1], vraw[FUSED ? KK : 1];
+    float4 cw[FUSED ? KK : 1], sw[FUSED ? KK : 1];
+    if constexpr (FUSED) {
+        const size_t kv_in = (static_cast<size_t>(b) * p.H_kv + j) * D;
+        const __amdgpu_buffer_rsrc_t knrs =
+            make_uniform_rsrc(static_cast<const uint16_t*>(p.k_new) + kv_in, own ? D * 2 : 0);
+        const __amdgpu_buffer_rsrc_t vnrs =
+            make_uniform_rsrc(static_cast<const uint16_t*>(p.v_new) + kv_in, own ? D * 2 : 0);
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            kraw[kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(knrs, (32 * kk + 8 * q4) * 2, 0, 0));
+            vraw[kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vnrs, (32 * kk + 8 * q4) * 2, 0, 0));
+        }
+        // interleaved pairs: chunk kk holds pairs 16 kk + 4 q4 .. +3; split
+        // halves: chunks m and m + KK/2 pair element by element, pairs
+        // 32 m + 8 q4 .. +7, as cw[2m], cw[2m + 1]  (row 0 stands in for an
+        // invalid position: nothing is then rotated or stored)
+        const size_t trow = static_cast<size_t>(pos_ok ? pos : 0) * (D / 2);
+        const __amdgpu_buffer_rsrc_t crs = make_uniform_rsrc(p.rope_cos + trow, D * 2);
+        const __amdgpu_buffer_rsrc_t srs = make_uniform_rsrc(p.rope_sin + trow, D * 2);
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            const int i0 = half ? 32 * (kk >> 1) + 8 * q4 + 4 * (kk & 1) : 16 * kk + 4 * q4;
+            cw[kk] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(crs, i0 * 4, 0, 0));
+            sw[kk] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(srs, i0 * 4, 0, 0));
+        }
+    }
     if constexpr (PAGED) {
 #pragma unroll
         for (int k = 0; k < kTblPer; ++k) {
@@ -223,6 +267,116 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
     }
     load_tensor(std::true_type{}, base);
     load_tensor(std::false_type{}, base);
+
+    // Fused step: rotate the queries (bf16, as stored by the append) and the
+    // new key (float32), quantize the key and the value.
+    uint2 kcode[FUSED ? KK : 1] = {}, vcode[FUSED ? KK : 1] = {};   // 8 codes per chunk
+    float2 kpair = make_float2(0.0f, 0.0f), vpair = make_float2(0.0f, 0.0f);
+    int patch_row = -1;                   // token index of the patched row, or -1
+    size_t slot_row = 0;                  // vector index of the new token's slot
+    bool slot_ok = false;
+    if constexpr (FUSED) {
+        auto fget = [](const float4& v, int i) __attribute__((always_inline)) {
+            return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+        };
+        // one vector in the operand layout -> rotated float32 values
+        auto rotate = [&](const uint4 (&x)[KK], float (&r)[KK][8]) __attribute__((always_inline)) {
+            if (half) {
+#pragma unroll
+                for (int m = 0; m < KK / 2; ++m) {
+                    const uint32_t* xa = reinterpret_cast<const uint32_t*>(&x[m]);
+                    const uint32_t* ya = reinterpret_cast<const uint32_t*>(&x[m + KK / 2]);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float a = (e & 1) ? bf16_hi(xa[e / 2]) : bf16_lo(xa[e / 2]);
+                        const float c = (e & 1) ? bf16_hi(ya[e / 2]) : bf16_lo(ya[e / 2]);
+                        rope_pair(a, c, fget(cw[2 * m + e / 4], e % 4), fget(sw[2 * m + e / 4], e % 4), r[m][e],
+                                  r[m + KK / 2][e]);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) {
+                    const uint32_t* xa = reinterpret_cast<const uint32_t*>(&x[kk]);
+#pragma unroll
+                    for (int w = 0; w < 4; ++w)
+                        rope_pair(bf16_lo(xa[w]), bf16_hi(xa[w]), fget(cw[kk], w), fget(sw[kk], w), r[kk][2 * w],
+                                  r[kk][2 * w + 1]);
+                }
+            }
+        };
+        if (pos_ok) {
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb) {
+                float r[KK][8];
+                rotate(qb[hb], r);
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk)
+                    qb[hb][kk] = make_uint4(pack_bf16x2(r[kk][0], r[kk][1]), pack_bf16x2(r[kk][2], r[kk][3]),
+                                            pack_bf16x2(r[kk][4], r[kk][5]), pack_bf16x2(r[kk][6], r[kk][7]));
+            }
+        }
+        // quantize one vector (the four lanes q4 = 0..3 of a row hold all of
+        // it): the affine grid of its min and max, codes rounded and clamped
+        auto quantize = [&](const float (&x)[KK][8], uint2 (&code)[KK], float2& pair) __attribute__((always_inline)) {
+            float mn = x[0][0], mx = x[0][0];
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    mn = fminf(mn, x[kk][e]);
+                    mx = fmaxf(mx, x[kk][e]);
+                }
+            mn = fminf(mn, __shfl_xor(mn, 16, 64));
+            mn = fminf(mn, __shfl_xor(mn, 32, 64));
+            mx = max_same_head(mx);
+            float step = (mx - mn) / 255.0f;
+            step = step == 0.0f ? 1.0f : step;
+            const float zp = fminf(fmaxf(rintf(-mn / step), 0.0f), 255.0f);
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                uint32_t w[2] = {0u, 0u};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t c = static_cast<uint32_t>(fminf(fmaxf(rintf(x[kk][e] / step + zp), 0.0f), 255.0f));
+                    w[e / 4] |= c << (8 * (e % 4));
+                }
+                code[kk] = make_uint2(w[0], w[1]);
+            }
+            pair = make_float2(step, zp);
+        };
+        // (only the split that stores the token: the divisions of the
+        // quantizer would delay every other workgroup's first tile)
+        if (own) {
+            float kf[KK][8], vf[KK][8];
+            rotate(kraw, kf);
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                const uint32_t* xa = reinterpret_cast<const uint32_t*>(&vraw[kk]);
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    vf[kk][2 * w] = bf16_lo(xa[w]);
+                    vf[kk][2 * w + 1] = bf16_hi(xa[w]);
+                }
+            }
+            quantize(kf, kcode, kpair);
+            quantize(vf, vcode, vpair);
+        }
+
+        // the new token's slot (a clamped table entry would be another
+        // sequence's block: then nothing is stored)
+        if constexpr (PAGED) {
+            if (own) {
+                const int blk = table[pos / p.block_size];
+                slot_ok = blk >= 0 && blk < p.num_blocks;
+                slot_row = (static_cast<size_t>(slot_ok ? blk : 0) * p.H_kv + j) * p.block_size + pos % p.block_size;
+            }
+        } else {
+            slot_ok = own;
+            slot_row = seq_rows + static_cast<size_t>(own ? pos : 0);
+        }
+        patch_row = __builtin_amdgcn_readfirstlane(slot_ok && pos < t_end ? pos : -1);
+    }
 
     // sum over d of each query head (the zero-point term of the scores): this
     // lane's 8*KK elements, then the four lanes of the head
@@ -253,6 +407,24 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
         // K codes and pairs were issued before this tile's V loads and nothing
         // after them: at most kTensorLoads outstanding
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(kTensorLoads));
+        // fused step: the tile holding the new token gets its codes and pair
+        // over what was loaded for that row (every read below comes after)
+        const int dp = patch_row - base;
+        const bool patch = FUSED && static_cast<unsigned>(dp) < static_cast<unsigned>(TT);
+        if constexpr (FUSED) {
+            if (patch) {
+                char* kcw = kc_lds + wave * CSTAGE;
+                if (r16 == 0) {
+#pragma unroll
+                    for (int kk = 0; kk < KK; ++kk) {
+                        const int c8 = 4 * kk + q4;
+                        *reinterpret_cast<uint2*>(kcw + dp * CROW + 16 * ((c8 / 2) ^ (dp % CLPR)) + 8 * (c8 % 2)) =
+                            kcode[kk];
+                    }
+                }
+                if (lane == 0) *reinterpret_cast<float2*>(ksz_lds + wave * TT * 8 + 8 * dp) = kpair;
+            }
+        }
         uint4 ka[KB][KK];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
@@ -293,6 +465,17 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
 
         // V codes and pairs: issued before the K loads just above
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(kTensorLoads));
+        if constexpr (FUSED) {
+            if (patch) {
+                char* vcw = vc_lds + wave * CSTAGE;
+                if (r16 == 0) {
+#pragma unroll
+                    for (int kk = 0; kk < KK; ++kk)
+                        *reinterpret_cast<uint2*>(vcw + dp * CROW + 32 * kk + 8 * q4) = vcode[kk];
+                }
+                if (lane == 0) *reinterpret_cast<float2*>(vsz_lds + wave * TT * 8 + 8 * dp) = vpair;
+            }
+        }
         float vstep[NS], vzp[NS];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -403,12 +586,46 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
 
+    if constexpr (FUSED) {
+        // Results of the append, stored once every load of this workgroup has
+        // completed: the rotated query (split 0) and the new token's codes and
+        // pairs (the split that holds it; it patched them into its tile).
+        const bool qout = split == 0 && wave == 0 && p.q_rot_out != nullptr;
+        const __amdgpu_buffer_rsrc_t qors =
+            make_uniform_rsrc(qout ? static_cast<uint16_t*>(p.q_rot_out) + qgrp : p.q_rot_out, qout ? G * D * 2 : 0);
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, qb[hb][kk]), qors,
+                                                       ((16 * hb + r16) * D + 32 * kk + 8 * q4) * 2, 0, 0);
+        const bool st = slot_ok && wave == 0 && r16 == 0;
+        const __amdgpu_buffer_rsrc_t kcs = make_uniform_rsrc(static_cast<uint8_t*>(const_cast<void*>(p.k)) + slot_row * D,
+                                                             slot_ok ? D : 0);
+        const __amdgpu_buffer_rsrc_t vcs = make_uniform_rsrc(static_cast<uint8_t*>(const_cast<void*>(p.v)) + slot_row * D,
+                                                             slot_ok ? D : 0);
+        if (st) {
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, kcode[kk]), kcs, 32 * kk + 8 * q4, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, vcode[kk]), vcs, 32 * kk + 8 * q4, 0, 0);
+            }
+        }
+        if (slot_ok && tid == 0) {
+            *reinterpret_cast<float2*>(k_sz + slot_row * 2) = kpair;
+            *reinterpret_cast<float2*>(v_sz + slot_row * 2) = vpair;
+        }
+    }
+
     // O rows of the group's heads through LDS, RB rows per pass (chunks of row
     // r XOR-swizzled by 4r); one thread per 16-byte column chunk of a row
     constexpr int RB = (NW * STAGE / (NW * 4 * D)) < 16 ? (NW * STAGE / (NW * 4 * D)) : 16;
     constexpr int NCH = D / 4;
     static_assert(RB >= 4, "merge area");
     auto chunk_at = [](int row, int ch) { return ch ^ ((4 * row) & (NCH - 1)); };
+    // (the in-kernel merge's partials: offsets below 2^31, as planned)
+    const __amdgpu_buffer_rsrc_t part_rs = make_uniform_rsrc(p.ws_part, 0x7FFFFFFF);
+    const __amdgpu_buffer_rsrc_t ml_rs = make_uniform_rsrc(p.ws_ml, 0x7FFFFFFF);
     float* sm_o = reinterpret_cast<float*>(vb_lds);               // [NW][RB][D]
     float* sm_m = reinterpret_cast<float*>(kc_lds);               // [NW][16]
     float* sm_l = sm_m + NW * 16;                                   // [NW][16]
@@ -461,6 +678,15 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
                     packed.y = static_cast<uint32_t>(f32_to_bf16_rne(Ls > 0.0f ? A.z / Ls : 0.0f)) |
                                (static_cast<uint32_t>(f32_to_bf16_rne(Ls > 0.0f ? A.w / Ls : 0.0f)) << 16);
                     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + bh * D + c) = packed;
+                } else if (p.merge_cnt != nullptr) {
+                    // device-scope stores (written through to memory that
+                    // every XCD sees), for the merge below
+                    const int o = static_cast<int>(((bh * p.n_splits + split) * D + c) * 4);
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, A), part_rs, o, 0, kDevScope);
+                    if (ch == 0)
+                        __builtin_amdgcn_raw_buffer_store_b64(
+                            __builtin_bit_cast(u32x2_t, make_float2(M, Ls)), ml_rs,
+                            static_cast<int>((bh * p.n_splits + split) * 8), 0, kDevScope);
                 } else {
                     *reinterpret_cast<float4*>(p.ws_part + (bh * p.n_splits + split) * D + c) = A;
                     if (ch == 0) p.ws_ml[bh * p.n_splits + split] = make_float2(M, Ls);
@@ -469,14 +695,38 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
             __syncthreads();
         }
     }
+
+    // ---- merge of the unit's splits by the last of them to finish (as in
+    // the bf16 kernel: device-scope partial rows, a wrapping arrival count,
+    // no workgroup waiting for another)
+    if (nsp > 1 && p.merge_cnt != nullptr) {
+        __shared__ int s_last;
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __syncthreads();
+        if (tid == 0)
+            s_last = __builtin_amdgcn_atomic_inc32(p.merge_cnt + unit, static_cast<unsigned>(nsp - 1),
+                                                   __ATOMIC_RELAXED, "agent") == static_cast<unsigned>(nsp - 1);
+        __syncthreads();
+        if (!s_last) return;
+        const size_t row0 = static_cast<size_t>(b) * p.H_q + static_cast<size_t>(j) * G;
+        merge_split_rows<D>(p, part_rs, ml_rs, G, nsp, [&](int gr) -> size_t { return row0 + gr; });
+    }
+}
+
+template <int D, int HB, bool FUSED>
+hipError_t launch_dhf(bool paged, const DecodeParams& p, float* k_sz, float* v_sz, hipStream_t stream,
+                      const KernelTiming& tm) {
+    const dim3 grid(p.n_wg_pad), block(kNWq * 64);
+    if (paged)
+        return launch_timed(decode_u8_kernel<D, HB, 3, FUSED>, grid, block, stream, tm, p, p.block_table, k_sz, v_sz);
+    return launch_timed(decode_u8_kernel<D, HB, 0, FUSED>, grid, block, stream, tm, p, p.block_table, k_sz, v_sz);
 }
 
 template <int D, int HB>
-hipError_t launch_dh(bool paged, const DecodeParams& p, const float* k_sz, const float* v_sz, hipStream_t stream,
+hipError_t launch_dh(bool paged, bool fused, const DecodeParams& p, float* k_sz, float* v_sz, hipStream_t stream,
                      const KernelTiming& tm) {
-    const dim3 grid(p.n_wg_pad), block(kNWq * 64);
-    if (paged) return launch_timed(decode_u8_kernel<D, HB, 3>, grid, block, stream, tm, p, p.block_table, k_sz, v_sz);
-    return launch_timed(decode_u8_kernel<D, HB, 0>, grid, block, stream, tm, p, p.block_table, k_sz, v_sz);
+    return fused ? launch_dhf<D, HB, true>(paged, p, k_sz, v_sz, stream, tm)
+                 : launch_dhf<D, HB, false>(paged, p, k_sz, v_sz, stream, tm);
 }
 
 }  // namespace
@@ -494,12 +744,16 @@ int decode_u8_wgs_per_cu(int d, int G) {
     return G > 16 ? 1 : 2;
 }
 
-hipError_t launch_decode_u8(int d, int G, bool paged, const DecodeParams& p, const float* k_sz, const float* v_sz,
+hipError_t launch_decode_u8(int d, int G, bool paged, bool fused, const DecodeParams& p, float* k_sz, float* v_sz,
                             hipStream_t stream, const KernelTiming& tm) {
     const bool two = G > 16;
     switch (d) {
-        case 64: return two ? launch_dh<64, 2>(paged, p, k_sz, v_sz, stream, tm) : launch_dh<64, 1>(paged, p, k_sz, v_sz, stream, tm);
-        case 128: return two ? launch_dh<128, 2>(paged, p, k_sz, v_sz, stream, tm) : launch_dh<128, 1>(paged, p, k_sz, v_sz, stream, tm);
+        case 64:
+            return two ? launch_dh<64, 2>(paged, fused, p, k_sz, v_sz, stream, tm)
+                       : launch_dh<64, 1>(paged, fused, p, k_sz, v_sz, stream, tm);
+        case 128:
+            return two ? launch_dh<128, 2>(paged, fused, p, k_sz, v_sz, stream, tm)
+                       : launch_dh<128, 1>(paged, fused, p, k_sz, v_sz, stream, tm);
         default: return hipErrorInvalidValue;
     }
 }

@@ -219,8 +219,10 @@ hipError_t launch_decode_mfma(int d, int rows, bool paged, bool fused, bool mult
 bool decode_u8_supported(int d, int G);
 int decode_u8_step_tokens();
 int decode_u8_wgs_per_cu(int d, int G);
-hipError_t launch_decode_u8(int d, int G, bool paged, const DecodeParams& p, const float* k_sz,
-                            const float* v_sz, hipStream_t stream, const KernelTiming& tm);
+// fused: the step's append runs inside (p.positions etc. set; the new token's
+// codes and pairs are written to the cache and k_sz / v_sz).
+hipError_t launch_decode_u8(int d, int G, bool paged, bool fused, const DecodeParams& p, float* k_sz, float* v_sz,
+                            hipStream_t stream, const KernelTiming& tm);
 
 // The log-sum-exp merge of the splits (only when n_splits > 1).
 hipError_t launch_decode_merge(kvc_dtype dtype, int d, const DecodeParams& p, hipStream_t stream);

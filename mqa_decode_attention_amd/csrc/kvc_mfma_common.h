@@ -86,5 +86,78 @@ __device__ __forceinline__ float sum_same_head(float x) {
     return x + __shfl_xor(x, 32, 64);
 }
 
+// Cache policy of device-scope buffer accesses (sc1): coherent across the
+// XCDs without any cache flush - the split partials one workgroup writes and
+// another merges in the same launch.
+constexpr int kDevScope = 16;
+
+// Merge of one unit's splits, run by the split that arrived last once every
+// split's partial rows went out as device-scope stores: M = max_s m_s,
+// w_s = 2^(m_s - M), out = sum_s w_s acc_s / sum_s w_s l_s, the splits in
+// order, MB of them requested at a time (their max folded into the running
+// one).  rows: output rows of the unit; row_of(r): the output row index of its
+// row r (the partials of output row i are at i * n_splits + s).  One thread
+// per 16-byte column chunk of a row, bf16 output.
+template <int D, typename RowOf>
+__device__ __forceinline__ void merge_split_rows(const DecodeParams& p, __amdgpu_buffer_rsrc_t part_rs,
+                                                 __amdgpu_buffer_rsrc_t ml_rs, int rows, int nsp, RowOf row_of) {
+    constexpr int NCH = D / 4;
+    constexpr int MB = 8;
+    for (int idx = threadIdx.x; idx < rows * NCH; idx += blockDim.x) {
+        const int c = 4 * (idx % NCH);
+        const size_t bh = row_of(idx / NCH);
+        const int ml0 = static_cast<int>(bh * p.n_splits * 8);
+        const int part0 = static_cast<int>((bh * p.n_splits * D + c) * 4);
+        float M = -INFINITY, Ls = 0.0f;
+        float4 A = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        for (int s0 = 0; s0 < nsp; s0 += MB) {
+            float mv[MB], lv[MB];
+            float4 pv[MB];
+#pragma unroll
+            for (int u = 0; u < MB; ++u) {
+                if (s0 + u < nsp) {
+                    const int sp = s0 + u;
+                    const float2 m2 = __builtin_bit_cast(
+                        float2, __builtin_amdgcn_raw_buffer_load_b64(ml_rs, ml0 + 8 * sp, 0, kDevScope));
+                    mv[u] = m2.x;
+                    lv[u] = m2.y;
+                    pv[u] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                           part_rs, part0 + 4 * D * sp, 0, kDevScope));
+                }
+            }
+            float Mb = M;
+#pragma unroll
+            for (int u = 0; u < MB; ++u)
+                if (s0 + u < nsp) Mb = fmaxf(Mb, mv[u]);
+            // (split maxima are finite, so after the first batch M is too)
+            const float r = s0 == 0 ? 0.0f : fast_exp2(M - Mb);
+            A.x *= r;
+            A.y *= r;
+            A.z *= r;
+            A.w *= r;
+            Ls *= r;
+            M = Mb;
+#pragma unroll
+            for (int u = 0; u < MB; ++u) {
+                if (s0 + u < nsp) {
+                    const float w = fast_exp2(mv[u] - M);
+                    A.x = fmaf(w, pv[u].x, A.x);
+                    A.y = fmaf(w, pv[u].y, A.y);
+                    A.z = fmaf(w, pv[u].z, A.z);
+                    A.w = fmaf(w, pv[u].w, A.w);
+                    Ls = fmaf(w, lv[u], Ls);
+                }
+            }
+        }
+        const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
+        uint2 packed;
+        packed.x = static_cast<uint32_t>(f32_to_bf16_rne(A.x * inv)) |
+                   (static_cast<uint32_t>(f32_to_bf16_rne(A.y * inv)) << 16);
+        packed.y = static_cast<uint32_t>(f32_to_bf16_rne(A.z * inv)) |
+                   (static_cast<uint32_t>(f32_to_bf16_rne(A.w * inv)) << 16);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + bh * D + c) = packed;
+    }
+}
+
 }  // namespace mfma
 }  // namespace kvc

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kvc_abi_version() == _lib.ABI_VERSION == 9
+    assert lib.kvc_abi_version() == _lib.ABI_VERSION == 10
     for s in range(6):
         assert lib.kvc_status_string(s)
     assert lib.kvc_status_string(99) == b"unknown status"
@@ -360,3 +360,32 @@ def test_noalloc_step_host_checks(lib):
     assert _noalloc(lib, H_q=6, H_kv=4) == KVC_ERR_SHAPE
     assert _noalloc(lib, q=None) == KVC_ERR_NULL
     assert _noalloc(lib, B=0) == KVC_OK
+
+
+def _step_u8(lib, **kw):
+    a = dict(B=2, H_q=8, H_kv=2, d=128, q=FAKE, qr=FAKE, kc=FAKE, ks=FAKE, vc=FAKE, vs=FAKE, T_max=4096, tbl=None,
+             bs=0, mb=0, nb=0, pos=FAKE, kn=FAKE, vn=FAKE, cos=FAKE, sin=FAKE, rows=4096, style=0, max_len=4096,
+             scale=0.0, out=FAKE, split=0, ws=None, wsn=0, stream=None)
+    a.update(kw)
+    return lib.kvc_decode_step_u8(a["B"], a["H_q"], a["H_kv"], a["d"], a["q"], a["qr"], a["kc"], a["ks"], a["vc"],
+                                  a["vs"], a["T_max"], a["tbl"], a["bs"], a["mb"], a["nb"], a["pos"], a["kn"],
+                                  a["vn"], a["cos"], a["sin"], a["rows"], a["style"], a["max_len"], a["scale"],
+                                  a["out"], a["split"], a["ws"], a["wsn"], a["stream"])
+
+
+def test_step_u8_host_checks(lib):
+    """The quantized decode step checks its sizes and pointers on the host as
+    the quantized decode and the bf16 step do, before anything is launched."""
+    assert _step_u8(lib, B=0) == KVC_OK
+    assert _step_u8(lib, pos=None) == KVC_ERR_NULL
+    assert _step_u8(lib, ks=None) == KVC_ERR_NULL
+    assert _step_u8(lib, kn=None) == KVC_ERR_NULL
+    assert _step_u8(lib, style=7) == KVC_ERR_UNSUPPORTED
+    assert _step_u8(lib, d=96) == KVC_ERR_UNSUPPORTED                 # the kernel's head dims: 64 and 128
+    assert _step_u8(lib, H_q=8 * 33, H_kv=8) == KVC_ERR_UNSUPPORTED   # groups of up to 32
+    assert _step_u8(lib, max_len=5000) == KVC_ERR_SHAPE               # beyond T_max
+    assert _step_u8(lib, tbl=FAKE, bs=8, mb=512, nb=64) == KVC_ERR_UNSUPPORTED   # block size not a multiple of 16
+    # a long sequence needs splits: a workspace is required
+    need = lib.kvc_decode_workspace_bytes(U8, 2, 8, 2, 128, 100000, 0, 0)
+    assert need > 0
+    assert _step_u8(lib, T_max=100000, max_len=100000) == KVC_ERR_WORKSPACE

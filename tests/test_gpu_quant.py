@@ -171,3 +171,68 @@ def test_decode_u8_full_size(name):
     else:
         ref = QO.decode_attention_u8(q2, kc, ks, vc, vs, lens, "bf16")
     compare_out(out, ref, "bf16", f"u8 {name} full size")
+
+
+def _run_step_u8(step: QStep, style="interleaved", split=0):
+    """kvc_decode_step_u8 on copies of the step's cache: (codes, pairs, q_rot, out)."""
+    kc, ks, vc, vs = step.kc.clone(), step.ks.clone(), step.vc.clone(), step.vs.clone()
+    q_raw = step.x.q.to("cuda")
+    out, q_rot = kvc.decode_step_u8(q_raw, kc, ks, vc, vs, step.pos, step.kn, step.vn, step.cos, step.sin,
+                                    step.max_len, block_table=step.tbl, rope_style=style, split_tokens=split)
+    return kc, ks, vc, vs, q_rot, out
+
+
+@pytest.mark.parametrize("style", ["interleaved", "half"])
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_step_u8_equals_append_then_decode(name, style):
+    """The fused step over a quantized cache gives bit for bit what
+    kvc_append_u8 then kvc_decode_attn[_paged]_u8 give with the same split
+    length (codes, pairs, rotated query and output), and the oracle's results
+    (bit-exact append, attention within tolerance)."""
+    x = W.draw(SMALL[name])
+    w = x.workload
+    qc = W.draw_quantized(x)
+    say(f"[step_u8 {name} {style}] G={w.G} d={w.d} lens={x.seq_lens.tolist()[:6]}")
+    ref = QStep(x, qc)
+    ref.append(style)
+    torch.cuda.synchronize()
+    kc2, ks2, vc2, vs2, q2 = check_append(ref, x, qc, style)
+    for split in (0, 64, 1 << 20):
+        fresh = QStep(x, qc)
+        kc, ks, vc, vs, q_rot, out = _run_step_u8(fresh, style, split)
+        out_a = ref.decode(split)
+        torch.cuda.synchronize()
+        for what, got, exp in (("K codes", kc, ref.kc), ("K pairs", ks, ref.ks), ("V codes", vc, ref.vc),
+                               ("V pairs", vs, ref.vs), ("rotated q", q_rot, ref.q)):
+            assert np.array_equal(bits(got), bits(exp)), f"{what} differ from the append (split {split})"
+        assert np.array_equal(bits(out), bits(out_a)), f"output differs from append + decode (split {split})"
+    lens = x.seq_lens.numpy()
+    if w.paged:
+        oref = QO.decode_attention_paged_u8(q2, kc2, ks2, vc2, vs2, x.block_table.numpy(), w.block_size, lens, "bf16")
+    else:
+        oref = QO.decode_attention_u8(q2, kc2, ks2, vc2, vs2, lens, "bf16")
+    compare(out, oref, f"step_u8 {name} {style}")
+
+
+@pytest.mark.parametrize("name", ["gqa_8b", "paged_gqa"])
+def test_step_u8_full_size(name):
+    """The benchmarked quantized step (default plan) at full size: the new
+    codes and pairs, the rotated query bit for bit, every output row within
+    tolerance of the oracle."""
+    w = W.WORKLOADS[name]
+    x = W.draw(w)
+    qc = W.draw_quantized(x)
+    say(f"[step_u8 {name} full] B={w.B} max_len={int(x.seq_lens.max())}")
+    step = QStep(x, qc)
+    kc, ks, vc, vs, q_rot, out = _run_step_u8(step)
+    torch.cuda.synchronize()
+    kc2, ks2, vc2, vs2, q2 = oracle_append_u8(x, qc)
+    for what, got, ref in (("K codes", kc, kc2), ("K pairs", ks, ks2), ("V codes", vc, vc2), ("V pairs", vs, vs2),
+                           ("rotated q", q_rot, q2)):
+        assert np.array_equal(bits(got), np.ascontiguousarray(ref).view(np.uint8)), f"{what} differ from the oracle"
+    lens = x.seq_lens.numpy()
+    if w.paged:
+        ref = QO.decode_attention_paged_u8(q2, kc2, ks2, vc2, vs2, x.block_table.numpy(), w.block_size, lens, "bf16")
+    else:
+        ref = QO.decode_attention_u8(q2, kc2, ks2, vc2, vs2, lens, "bf16")
+    compare_out(out, ref, "bf16", f"step_u8 {name} full size")
