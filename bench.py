@@ -34,13 +34,20 @@ MALL_DEFEAT_BYTES = 2 << 30
 # the streaming kernel is built from: counters taken on other versions of them
 # do not describe the current kernel
 _CSRC = os.path.join(ROOT, "mqa_decode_attention_amd", "csrc")
+_COMMON = ("kvc_mfma_common.h", "kvc_device.h", "kvc_internal.h")
+# rocprofv3 FETCH_SIZE / WRITE_SIZE summaries of the streaming kernel per
+# configuration (profiles/), and the sources of that kernel they were taken on
 TRAFFIC = {
-    ("native", "gqa_8b"): ("decode_gqa_8b_traffic.json",
-                           ("kvc_decode_mfma.hip", "kvc_mfma_common.h", "kvc_device.h", "kvc_internal.h")),
-    ("u8", "gqa_8b"): ("decode_u8_gqa_8b_traffic.json",
-                       ("kvc_decode_u8.hip", "kvc_mfma_common.h", "kvc_device.h", "kvc_internal.h")),
-    ("native", "mla_latent"): ("decode_mla_latent_traffic.json",
-                               ("kvc_mla.hip", "kvc_mfma_common.h", "kvc_device.h", "kvc_internal.h")),
+    ("native", "gqa_8b"): ("decode_gqa_8b_traffic.json", ("kvc_decode_mfma.hip",) + _COMMON),
+    ("u8", "gqa_8b"): ("decode_u8_gqa_8b_traffic.json", ("kvc_decode_u8.hip",) + _COMMON),
+    ("native", "mqa_ragged"): ("decode_mqa_ragged_traffic.json", ("kvc_decode_mfma.hip", "kvc_decode.hip") + _COMMON),
+    ("native", "long_gqa"): ("decode_long_gqa_traffic.json", ("kvc_decode_mfma.hip",) + _COMMON),
+    ("native", "paged_gqa"): ("decode_paged_gqa_traffic.json", ("kvc_decode_mfma.hip", "kvc_decode.hip") + _COMMON),
+    ("u8", "paged_gqa"): ("decode_u8_paged_gqa_traffic.json", ("kvc_decode_u8.hip",) + _COMMON),
+    ("native", "tiny_mha"): ("decode_tiny_mha_traffic.json", ("kvc_decode.hip",) + _COMMON),
+    ("native", "spec_gqa"): ("decode_spec_gqa_traffic.json",
+                             ("kvc_decode_mfma.hip", "kvc_append.hip", "kvc_decode.hip") + _COMMON),
+    ("native", "mla_latent"): ("decode_mla_latent_traffic.json", ("kvc_mla.hip",) + _COMMON),
 }
 
 
@@ -330,6 +337,7 @@ def bench_mla(args, W) -> dict:
     torch.cuda.synchronize()
     dec_ms = [a.elapsed_time(b) for a, b in evs]
     dec_avg_ms = sum(dec_ms) / len(dec_ms)
+    timing = "start and stop events attached to each launch"
     achieved = kv_bytes / (dec_avg_ms * 1e-3) / 1e9
     check_kernel_timing(achieved, w.name)
     value = kv_bytes / (step_ms * 1e-3) / 1e9
@@ -359,7 +367,7 @@ def bench_mla(args, W) -> dict:
                      "traffic": traffic_for_current_kernel("native", w.name),
                      "kernel": "mla_decode_kernel (streaming pass over the latent rows; the absorbed queries with "
                                "the append, the split merge and the value up-projection are separate small kernels)",
-                     "bytes_per_launch": kv_bytes},
+                     "bytes_per_launch": kv_bytes, "launch_timing": timing},
         "wall_s_timed": round(wall, 4),
     }
     ceil_nt = probe["nontemporal"]["best_gbs"]
@@ -576,8 +584,12 @@ def main():
     # boundaries marked inside), nothing else in between
     step_ms, batch_stats, wall = timed_steps(step, args.steps)
 
-    # per-launch duration of the streaming decode kernel: events the library
-    # records on its stream right before and after that kernel
+    # Per-launch duration of the streaming decode kernel: start and stop
+    # events the library attaches to that kernel's launch on its stream
+    # (hipExtLaunchKernel).  (The runtime's processing of those events adds a
+    # few microseconds to each timed launch - about 4 us on the 83 us gqa_8b
+    # kernel, more on short kernels - so this figure is an upper bound; the
+    # rocprofv3 kernel traces give the kernel alone.)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     for a, b in evs:        # create the underlying HIP events
@@ -588,13 +600,14 @@ def main():
         step(i, evs[i])
     torch.cuda.synchronize()
     dec_ms = [a.elapsed_time(b) for a, b in evs]
+    timing = "start and stop events attached to each launch"
     dec_avg_ms = sum(dec_ms) / len(dec_ms)
     dec_med_ms = sorted(dec_ms)[len(dec_ms) // 2]
 
     achieved = kv_bytes / (dec_avg_ms * 1e-3) / 1e9
     check_kernel_timing(achieved, w.name)
     value = kv_bytes / (step_ms * 1e-3) / 1e9
-    traffic = None if (win or multi) else traffic_for_current_kernel(args.kv_cache, w.name)
+    traffic = None if (win or args.ring) else traffic_for_current_kernel(args.kv_cache, w.name)
     # algorithmic flops: score and PV multiply-adds, 4 * d per (query head,
     # attended token), for every new token's query
     att = attended(x.seq_lens.tolist(), win + w.new_tokens - 1 if win else 0)
@@ -644,7 +657,7 @@ def main():
                                 "queries; the append and the split merge are separate small kernels)") if multi else
                                ("decode_mfma_kernel (streaming pass with the fused append; a one-round plan merges "
                                 "its splits in the same launch, else a small merge kernel follows)"),
-                     "bytes_per_launch": kv_bytes},
+                     "bytes_per_launch": kv_bytes, "launch_timing": timing},
         "wall_s_timed": round(wall, 4),
     }
     ceil_nt = probe["nontemporal"]["best_gbs"]

@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 10
+#define KVC_ABI_VERSION 11
 
 typedef enum kvc_status {
     KVC_OK = 0,
@@ -196,6 +196,17 @@ size_t kvc_workspace_zeroed_bytes(void);
  * of 4096 and 4097 tokens.
  */
 int kvc_decode_split_tokens(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_len,
+                            long long pool_tokens, int split_tokens);
+
+/*
+ * Whether a decode call with these sizes (arguments as for
+ * kvc_decode_workspace_bytes) launches a separate merge kernel after the
+ * streaming kernel: 1 if it does, 0 if not (one split per sequence, or a plan
+ * whose workgroups all fit in one round, where the last split of each
+ * (sequence, KV head) merges in the streaming kernel itself; the bf16 and
+ * uint8 matrix-core kernels only); -1 for invalid sizes.
+ */
+int kvc_decode_merge_launch(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_len,
                             long long pool_tokens, int split_tokens);
 
 /*

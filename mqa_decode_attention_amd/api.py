@@ -115,6 +115,17 @@ def workspace_bytes(dtype: torch.dtype, B: int, H_q: int, H_kv: int, d: int, max
     return n
 
 
+def merge_launch(dtype: torch.dtype, B: int, H_q: int, H_kv: int, d: int, max_seq_len: int,
+                 split_tokens: int = 0, pool_tokens: int = 0) -> bool:
+    """kvc_decode_merge_launch: True when a decode with these sizes launches a
+    separate merge kernel after the streaming kernel."""
+    lib = _lib.load()
+    n = lib.kvc_decode_merge_launch(_cache_code(dtype), B, H_q, H_kv, d, max_seq_len, pool_tokens, split_tokens)
+    if n < 0:
+        raise KvcError(2, lib.kvc_last_error().decode() or "invalid sizes")
+    return bool(n)
+
+
 def workspace_zeroed_bytes() -> int:
     """kvc_workspace_zeroed_bytes: the prefix of a caller's `workspace` tensor
     that must be zero before its first use (every completed call leaves it so)."""
@@ -154,11 +165,12 @@ def _workspace(device: torch.device, stream_handle: int, nbytes: int) -> Tuple[O
     return ws.data_ptr(), ws.numel()
 
 
-def profile_next_decode(start: "torch.cuda.Event", stop: "torch.cuda.Event") -> None:
+def profile_next_decode(start: Optional["torch.cuda.Event"], stop: Optional["torch.cuda.Event"]) -> None:
     """Have the next decode call on this thread record `start`/`stop` around its
-    streaming kernel (kvc_profile_next_decode).  The events must exist already
-    (record them once before the first use)."""
-    _lib.load().kvc_profile_next_decode(start.cuda_event, stop.cuda_event)
+    streaming kernel (kvc_profile_next_decode; either may be None).  The events
+    must exist already (record them once before the first use)."""
+    _lib.load().kvc_profile_next_decode(start.cuda_event if start is not None else None,
+                                        stop.cuda_event if stop is not None else None)
 
 
 def _decode_args(q, out):

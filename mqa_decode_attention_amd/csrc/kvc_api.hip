@@ -445,6 +445,20 @@ int kvc_decode_split_tokens(kvc_dtype dtype, int B, int H_q, int H_kv, int d, in
     return pl.split_tokens;
 }
 
+int kvc_decode_merge_launch(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_len,
+                            long long pool_tokens, int split_tokens) {
+    if (check_heads(dtype == KVC_U8 ? KVC_BF16 : dtype, B, H_q, H_kv, d) != KVC_OK || max_seq_len < 0 || split_tokens < 0 ||
+        pool_tokens < 0)
+        return -1;
+    kvc::DecodePlan pl;
+    const char* why = nullptr;
+    if (!kvc::plan_decode(dtype, B, H_q, H_kv, d, max_seq_len, pool_tokens, split_tokens, &pl, &why)) {
+        fail(KVC_ERR_UNSUPPORTED, "%s", why);
+        return -1;
+    }
+    return pl.n_splits > 1 && !pl.merge_in_kernel ? 1 : 0;
+}
+
 namespace {
 // plan of a multi-token call (sizes as kvc_decode_attn_multi's); false if invalid
 bool plan_multi(kvc_dtype dtype, int B, int n, int H_q, int H_kv, int d, int max_seq_len, int window,

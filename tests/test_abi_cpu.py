@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kvc_abi_version() == _lib.ABI_VERSION == 10
+    assert lib.kvc_abi_version() == _lib.ABI_VERSION == 11
     for s in range(6):
         assert lib.kvc_status_string(s)
     assert lib.kvc_status_string(99) == b"unknown status"
@@ -203,6 +203,17 @@ def test_split_choice(lib):
     assert st(BF16, 16, 32, 8, 128, 8193 + 64, 0, 0) == 4160
     # explicit splits and paged pools keep whole splits: no remainder joins
     assert wsb(BF16, 16, 32, 8, 128, 8193, 0, 4096) == zb + 16 * 32 * 3 * (8 + 128 * 4)
+    # one round of workgroups merges in the streaming kernel; more rounds, or
+    # the vector kernel, launch a merge kernel; one split needs none
+    ml = lib.kvc_decode_merge_launch
+    assert ml(BF16, 16, 32, 8, 128, 8193, 0, 0) == 0            # 256 workgroups on 256 slots
+    assert ml(BF16, 1, 64, 8, 128, 131073, 0, 0) == 0
+    assert ml(U8, 16, 32, 8, 128, 8193, 0, 0) == 0              # 512 on 512
+    assert ml(BF16, 64, 32, 1, 128, 4097, 0, 0) == 1            # ~3 rounds
+    assert ml(BF16, 16, 32, 8, 128, 8193, 0, 1024) == 1         # 1152 workgroups
+    assert ml(F32, 16, 32, 8, 128, 8193, 0, 0) == 1             # the vector kernel
+    assert ml(BF16, 16, 32, 8, 128, 100, 0, 0) == 0             # one split
+    assert ml(BF16, 16, 30, 8, 128, 100, 0, 0) == -1
     assert st(BF16, 16, 32, 8, 128, 8193, 0, 1000) == 1000      # explicit split kept
     # paged pool holding about half of B * max_seq_len tokens: ~4 rounds of
     # splits over 768 slots (three per CU): 17408 * 16 * 8 / (4 * 768) = 725.3 -> 768
