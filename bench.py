@@ -586,10 +586,10 @@ def main():
 
     # Per-launch duration of the streaming decode kernel: start and stop
     # events the library attaches to that kernel's launch on its stream
-    # (hipExtLaunchKernel).  (The runtime's processing of those events adds a
-    # few microseconds to each timed launch - about 4 us on the 83 us gqa_8b
-    # kernel, more on short kernels - so this figure is an upper bound; the
-    # rocprofv3 kernel traces give the kernel alone.)
+    # (hipExtLaunchKernel).  (In a plain run these agree with rocprofv3's
+    # kernel durations within a few per cent; the attached events can
+    # lengthen the launches they time - the quantized kernel's by about 10 % -
+    # so the figure is an upper bound on the kernel's own time.)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     for a, b in evs:        # create the underlying HIP events
