@@ -119,6 +119,28 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     const int G = p.G;
     static_assert(!(MQ && FUSED), "several new tokens: the append runs first");
 
+    // MODE 3 without a window: the split's first block is known before its
+    // sequence's length (the split starts at split * split_tokens), so the
+    // table entries it may span are requested together with the length, and
+    // the first tile waits for one round trip less.  (Entries past the row
+    // are clamped into it; those past the split are not used.)
+    constexpr int kTblPer = kTblMax / (NW * 64);
+    int tv[kTblPer];
+    const bool tbl_early = MODE == 3 && p.window == 0;
+    if constexpr (MODE == 3) {
+        if (tbl_early) {
+            const int fb0 = (split * p.split_tokens) / p.block_size;
+            const int span = min(p.split_tokens / p.block_size + 1, p.max_blocks_per_seq - fb0);
+            const int32_t* trow = block_table + static_cast<size_t>(b) * p.max_blocks_per_seq;
+            const int first = min(fb0, p.max_blocks_per_seq - 1);
+#pragma unroll
+            for (int k = 0; k < kTblPer; ++k) {
+                const int i = static_cast<int>(threadIdx.x) + k * NW * 64;
+                tv[k] = trow[i < span ? fb0 + i : first];
+            }
+        }
+    }
+
     // fused step: slot of the new token (read once; it also gives L)
     const int pos = FUSED ? p.positions[b] : 0;
     const int L = FUSED ? len_from_position(p, pos) : attended_len(p, b);
@@ -328,17 +350,18 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     int base = t_begin + (ILV ? 0 : wave * TT);   // step base: the workgroup's, or this wave's
     uint4 ka0[KB][KK], ka1[KB][KK];
 
-    // MODE 3: the table entries of the blocks this split spans (read first:
-    // the first tile's addresses depend on them).  Indices past the split are
-    // clamped to its first entry, so every read stays in this sequence's row.
-    constexpr int kTblPer = kTblMax / (NW * 64);
-    int tv[kTblPer];
+    // MODE 3 with a window: the table entries of the blocks this split spans
+    // (read first: the first tile's addresses depend on them).  Indices past
+    // the split are clamped to its first entry, so every read stays in this
+    // sequence's row.
     const int nblk = PAGED ? (t_end - 1) / p.block_size - fb + 1 : 0;
     if constexpr (MODE == 3) {
+        if (!tbl_early) {
 #pragma unroll
-        for (int k = 0; k < kTblPer; ++k) {
-            const int i = tid + k * NW * 64;
-            tv[k] = table[fb + (i < nblk ? i : 0)];
+            for (int k = 0; k < kTblPer; ++k) {
+                const int i = tid + k * NW * 64;
+                tv[k] = table[fb + (i < nblk ? i : 0)];
+            }
         }
     }
 

@@ -534,8 +534,14 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
             const uint4 c = *reinterpret_cast<const uint4*>(vc + 16 * ci);
             const uint4 lo = codes8_to_bf16(make_uint2(c.x, c.y));
             const uint4 hi = codes8_to_bf16(make_uint2(c.z, c.w));
-            *reinterpret_cast<uint4*>(vb + r * ROWB + 16 * ((2 * u) ^ swz(r))) = lo;
-            *reinterpret_cast<uint4*>(vb + r * ROWB + 16 * ((2 * u + 1) ^ swz(r))) = hi;
+            // (d = 128: the eight lanes of one row write the low halves of
+            // chunks 0-3 and the high halves of chunks 4-7 first, so every
+            // 128-byte bank sweep gets eight distinct 16-byte slots per store)
+            const bool hi_first = D == 128 && u >= CLPR / 2;
+            *reinterpret_cast<uint4*>(vb + r * ROWB + 16 * ((2 * u + (hi_first ? 1 : 0)) ^ swz(r))) =
+                select4(hi_first, hi, lo);
+            *reinterpret_cast<uint4*>(vb + r * ROWB + 16 * ((2 * u + (hi_first ? 0 : 1)) ^ swz(r))) =
+                select4(hi_first, lo, hi);
         }
         // the V stage is free once its reads are done: the next tile's V
         __builtin_amdgcn_s_waitcnt(kLgkmZero);
