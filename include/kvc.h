@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 11
+#define KVC_ABI_VERSION 12
 
 typedef enum kvc_status {
     KVC_OK = 0,
@@ -158,7 +158,9 @@ kvc_status kvc_append(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
  * contiguous cache; pass the same sizes as the decode call.
  *
  * The workspace holds the per-split partial results (running max and sum
- * per query head, weighted value sums) and, in its first
+ * per query head, weighted value sums; under the balanced schedule, two
+ * partial rows per query head of a group for each of its workgroups) and, in
+ * its first
  * kvc_workspace_zeroed_bytes() bytes, one arrival counter per (sequence, KV
  * head) that the splits of the bf16 matrix-core kernel count themselves in
  * with: the last split of each to finish merges the partials, in the same
@@ -204,10 +206,32 @@ int kvc_decode_split_tokens(kvc_dtype dtype, int B, int H_q, int H_kv, int d, in
  * streaming kernel: 1 if it does, 0 if not (one split per sequence, or a plan
  * whose workgroups all fit in one round, where the last split of each
  * (sequence, KV head) merges in the streaming kernel itself; the bf16 and
- * uint8 matrix-core kernels only); -1 for invalid sizes.
+ * uint8 matrix-core kernels only, and always under the balanced schedule);
+ * -1 for invalid sizes.
  */
 int kvc_decode_merge_launch(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_len,
                             long long pool_tokens, int split_tokens);
+
+/*
+ * Whether a single-token decode with these sizes (arguments as for
+ * kvc_decode_workspace_bytes; a call without a window) runs the balanced
+ * schedule: 1 if it does, 0 if it uses splits of the planned length, -1 for
+ * invalid sizes.
+ *
+ * The balanced schedule (bf16, head_dim 64 or 128, at most 512 sequences,
+ * the library's split choice, paged pools of blocks of a multiple of 16
+ * tokens): every workgroup reads the B lengths, lays the loop steps of all
+ * (sequence, KV head) units out in one list and streams an equal share of it,
+ * so ragged lengths cost no idle or short workgroups (the units are the
+ * partition of "Grouped-query attention: berbagi KV head di antara grup
+ * query", nalar.dev, section "Jumlah head menentukan batas grup"; their
+ * partial results merge by log-sum-exp as the splits' do).  The library uses
+ * it for paged pools much smaller than B * max_seq_len (ragged lengths); a
+ * call with a sliding window, several new tokens or another block size takes
+ * the split plan, whose workspace the returned size also covers.
+ */
+int kvc_decode_balanced(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_len,
+                        long long pool_tokens, int split_tokens);
 
 /*
  * kvc_decode_attn - attention of the new token over a contiguous cache.

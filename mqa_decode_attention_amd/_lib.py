@@ -28,6 +28,7 @@ SIGNATURES = {
     "kvc_decode_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int, c_int, c_longlong, c_int]),
     "kvc_workspace_zeroed_bytes": (c_size_t, []),
     "kvc_decode_merge_launch": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_longlong, c_int]),
+    "kvc_decode_balanced": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_longlong, c_int]),
     "kvc_decode_split_tokens": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_longlong, c_int]),
     "kvc_decode_attn": (c_int, [c_int, c_int, c_int, c_int, c_int,
                                 c_void_p, c_void_p, c_void_p, c_int,
@@ -113,7 +114,7 @@ SIGNATURES = {
                                     c_size_t, c_void_p]),
 }
 
-ABI_VERSION = 11
+ABI_VERSION = 12
 
 _lib = None
 

@@ -94,7 +94,8 @@ kvc_status check_heads(kvc_dtype dt, int B, int H_q, int H_kv, int d) {
 namespace kvc {
 
 bool plan_decode(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_len,
-                 long long pool_tokens, int split_tokens, DecodePlan* plan, const char** why, int qlen) {
+                 long long pool_tokens, int split_tokens, DecodePlan* plan, const char** why, int qlen,
+                 bool allow_bal) {
     DecodePlan pl{};
     const int G = H_q / H_kv;
     if (qlen > 1 && (dtype != KVC_BF16 || !decode_mfma_supported(dtype, d, 1))) {
@@ -203,6 +204,35 @@ bool plan_decode(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_l
         // (Partial offsets stay below 2^31 for its 32-bit buffer offsets.)
         pl.merge_in_kernel = pl.mfma && units <= kMergeCounters && units * pl.n_splits <= slots &&
                              pl.ws_bytes - pl.ws_part < (size_t{1} << 31);
+    }
+    // Balanced schedule (bf16 matrix-core kernel, one new token, library
+    // splits) for ragged paged pools, whose split plan above is sized from
+    // the longest sequence and leaves many short or empty splits, each paying
+    // a prologue.  One round of workgroups (more only if a workgroup would
+    // take more than kBalMaxSteps steps); the step count must fit in 31 bits.
+    // (Measured on the ragged paged workload: 202 -> 198 us.  Over a
+    // contiguous cache with groups of 32 heads it was slower than the split
+    // plan - 25 -> 39 us on the ragged MQA workload, whose per-segment
+    // prologue and epilogue cost as much as a share of the stream - so
+    // contiguous caches keep the split plan.)
+    if (allow_bal && split_tokens == 0 && pl.mfma && !u8 && qlen <= 1 && d <= 128 && B <= kBalMaxB &&
+        units <= kMergeCounters) {
+        const bool ragged_pool = pool_tokens > 0 && pool_tokens * H_kv * 10 < units * L * 9;
+        const long long steps = units * ((L + tile - 1) / tile);      // >= the steps of any call
+        if (ragged_pool && steps < (1LL << 31) - units) {
+            const long long nwg = std::max(slots, (steps + kBalMaxSteps - 1) / kBalMaxSteps);
+            const size_t rows = static_cast<size_t>(nwg) * 2 * G;    // two partial slots per workgroup
+            const size_t ml = kWsCounterBytes;
+            const size_t part = align_up(ml + rows * sizeof(float2), 256);
+            const size_t bytes = align_up(part + rows * d * sizeof(float), 256);
+            if (bytes - part < (size_t{1} << 31) && nwg < (1LL << 24)) {
+                pl.bal = true;
+                pl.bal_wg = static_cast<int>(nwg);
+                pl.ws_ml = ml;
+                pl.ws_part = part;
+                pl.ws_bytes = std::max(pl.ws_bytes, bytes);
+            }
+        }
     }
     *plan = pl;
     return true;
@@ -456,7 +486,21 @@ int kvc_decode_merge_launch(kvc_dtype dtype, int B, int H_q, int H_kv, int d, in
         fail(KVC_ERR_UNSUPPORTED, "%s", why);
         return -1;
     }
-    return pl.n_splits > 1 && !pl.merge_in_kernel ? 1 : 0;
+    return pl.n_splits > 1 && !pl.merge_in_kernel && !pl.bal ? 1 : 0;
+}
+
+int kvc_decode_balanced(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_len,
+                        long long pool_tokens, int split_tokens) {
+    if (check_heads(dtype == KVC_U8 ? KVC_BF16 : dtype, B, H_q, H_kv, d) != KVC_OK || max_seq_len < 0 ||
+        split_tokens < 0 || pool_tokens < 0)
+        return -1;
+    kvc::DecodePlan pl;
+    const char* why = nullptr;
+    if (!kvc::plan_decode(dtype, B, H_q, H_kv, d, max_seq_len, pool_tokens, split_tokens, &pl, &why)) {
+        fail(KVC_ERR_UNSUPPORTED, "%s", why);
+        return -1;
+    }
+    return pl.bal ? 1 : 0;
 }
 
 namespace {
@@ -571,6 +615,12 @@ kvc_status decode_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const
     const int span = kvc_window_span(max_seq_len, window > 0 ? window + qlen - 1 : 0, ring, T_max);
     if (!kvc::plan_decode(dtype, B, H_q, H_kv, d, span, pool_tokens, split_tokens, &pl, &why, qlen))
         return fail(KVC_ERR_UNSUPPORTED, "%s", why);
+    // the balanced schedule serves one new token over a full paged cache of
+    // blocks of a multiple of 16 tokens; other calls take the split plan,
+    // whose workspace the balanced plan's size covers
+    if (pl.bal && (multi || window != 0 || ring || !paged || block_size % 16 != 0) &&
+        !kvc::plan_decode(dtype, B, H_q, H_kv, d, span, pool_tokens, split_tokens, &pl, &why, qlen, false))
+        return fail(KVC_ERR_UNSUPPORTED, "%s", why);
     if (u8 && paged) {
         // 32-token tiles of 16-row groups, each inside one block, found in a
         // staged slice of at most kTblMax table entries
@@ -587,7 +637,7 @@ kvc_status decode_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const
         if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
             return fail(KVC_ERR_WORKSPACE, "workspace must be 256-byte aligned");
     }
-    const long long n_wg = static_cast<long long>(B) * H_kv * pl.n_chunks * pl.n_splits;
+    const long long n_wg = pl.bal ? pl.bal_wg : static_cast<long long>(B) * H_kv * pl.n_chunks * pl.n_splits;
     if (n_wg > 0x7FFFFFF0LL) return fail(KVC_ERR_SHAPE, "too many workgroups");
 
     kvc::DecodeParams p{};
@@ -600,8 +650,9 @@ kvc_status decode_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const
     // the matrix-core kernels merge the splits themselves when the plan says
     // so: the last split of each unit to finish (counted in the workspace's
     // first bytes) does it
-    const bool merge_in_kernel = pl.merge_in_kernel;
+    const bool merge_in_kernel = pl.merge_in_kernel || pl.bal;
     p.merge_cnt = merge_in_kernel ? reinterpret_cast<unsigned*>(ws) : nullptr;
+    p.bal = pl.bal ? 1 : 0;
     p.B = B; p.H_q = H_q; p.H_kv = H_kv; p.G = H_q / H_kv; p.n_chunks = pl.n_chunks;
     p.T_max = T_max; p.block_size = block_size; p.max_blocks_per_seq = max_blocks_per_seq;
     p.num_blocks = num_blocks;

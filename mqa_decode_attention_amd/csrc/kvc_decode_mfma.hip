@@ -32,10 +32,14 @@
 //   tokens of one V column - the A operand V^T - with one instruction.
 // * Query heads beyond G are zero rows of the B operand; more than 16 heads use
 //   several 16-head blocks over the same K/V registers.
-// * The probabilities enter the second product as a pair of bf16 operands
-//   (hi = bf16(p), lo = bf16(p - hi)), two MFMAs, so p carries about 16
-//   significant bits: rounding p once to bf16 alone would leave errors of a
-//   few 1e-4 in the output, enough to move it across a bf16 rounding boundary.
+// * The probabilities enter the second product as three bf16 operands
+//   (hi = bf16(p), mid = bf16(p - hi), lo = bf16(p - hi - mid)), three MFMAs,
+//   so p carries about 24 significant bits, as a float32 weight would (the
+//   32-row multi-token kernel: hi and mid only, for want of registers).  One
+//   bf16 operand alone leaves errors of a few 1e-4 in the output; two (about
+//   16 bits, relative error up to ~4e-6 per weight) still moved outputs of
+//   short sequences with |O| >= 0.5 across a bf16 rounding boundary now and
+//   then (one bf16 step there is 3.9e-3).
 
 #include <type_traits>
 
@@ -59,8 +63,8 @@ using namespace mfma;
 // once, and K and V tiles are staged like those of a contiguous cache.
 // (The paged kernel with staged tiles and one head block is planned at three
 // workgroups per CU: its registers are held to three waves per SIMD.)
-template <int D, int HB, int NW, int MODE, bool FUSED, bool MQ>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((MODE == 3 && HB == 1) ? 3 : ((MQ && HB == 2 && MODE == 0 && D <= 128) ? 2 : 1), 8)))
+template <int D, int HB, int NW, int MODE, bool FUSED, bool MQ, bool BAL>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((MODE == 3 && HB == 1) ? 3 : ((HB == 2 && MODE == 0 && D <= 128) ? 2 : 1), 8)))
 decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table) {
     // (the block table as its own restrict argument: nothing this kernel stores
     // can alias it, so its wave-uniform reads may use scalar loads)
@@ -103,60 +107,206 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     __shared__ int tbl_lds[MODE == 3 ? kTblMax : 1];
     __shared__ float sm_ml[2 * NW * 16];   // the waves' (m, l) per head row, for their merge
 
-    // Workgroups in launch order: the splits of one (sequence, KV head) are
-    // neighbours, and the hardware deals consecutive workgroups to the XCDs
-    // in turn.  (Grouping each unit's splits on one XCD gains nothing for a
-    // stream without reuse, and with ragged lengths it left some XCDs with
-    // far more work than others: the paged workload ran 2.4 % slower.)
+    __shared__ int s_last;                 // the in-kernel merge: this workgroup arrived last
+    // balanced schedule: per-sequence step prefix, lengths, positions
+    __shared__ int bal_pre[BAL ? kBalMaxB + 1 : 1];
+    __shared__ int bal_len[BAL ? kBalMaxB : 1];
+    __shared__ int bal_pos[(BAL && FUSED) ? kBalMaxB : 1];
+    __shared__ int bal_misc[NW + 1];
+
     const int wid = blockIdx.x < static_cast<unsigned>(p.n_wg) ? static_cast<int>(blockIdx.x) : -1;
     if (wid < 0) return;
-    const int split = wid % p.n_splits;
-    const int unit = wid / p.n_splits;    // b * H_kv + j (MQ: (b * H_kv + j) * n_chunks + chunk)
+    const int G = p.G;
+    static_assert(!(MQ && FUSED), "several new tokens: the append runs first");
+    static_assert(!(BAL && MQ), "the balanced schedule serves single-token steps");
+    constexpr int kStep = NW * TT;        // tokens per loop step of the workgroup
+
+    const int tid0 = threadIdx.x;
+
+    // Balanced schedule.  Sequence b holds n_b = ceil(L_b / kStep) loop steps
+    // (at least one, so that an empty sequence still writes its zero rows) for
+    // each of its H_kv units; the units' steps, in unit order, form one list of
+    // T steps, and workgroup w of N takes steps [w T / N, (w + 1) T / N): every
+    // workgroup streams the same number of steps (within one), whatever the
+    // lengths, and all of them start at once (N is the planned count, or T
+    // when there are fewer steps).  A workgroup's range crosses
+    // units, so it runs the split body once per segment (a unit's steps inside
+    // the range); a unit that several workgroups share is merged by the last
+    // of them to finish, from partial rows each writes to one of two slots of
+    // its own (its first segment, its last one).  Every workgroup reads all B
+    // lengths once and derives its segments from them.
+    if constexpr (BAL) {
+        constexpr int PER = kBalMaxB / (NW * 64);
+        int nst[PER];
+        int sum = 0;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int bb = tid0 * PER + k;
+            int n = 0;
+            if (bb < p.B) {
+                const int ps = FUSED ? p.positions[bb] : 0;
+                const int Lb = FUSED ? len_from_position(p, ps) : attended_len(p, bb);
+                bal_len[bb] = Lb;
+                if constexpr (FUSED) bal_pos[bb] = ps;
+                n = Lb > 0 ? (Lb + kStep - 1) / kStep : 1;
+            }
+            nst[k] = n;
+            sum += n;
+        }
+        // exclusive prefix over the threads (each holds PER consecutive
+        // sequences): inside each wave, then over the waves' totals
+        int inc = sum;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int v = __shfl_up(inc, o, 64);
+            if ((tid0 & 63) >= o) inc += v;
+        }
+        if ((tid0 & 63) == 63) bal_misc[tid0 >> 6] = inc;
+        __syncthreads();
+        int ex = inc - sum, tot = 0;
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2) {
+            const int v = bal_misc[w2];
+            ex += w2 < (tid0 >> 6) ? v : 0;
+            tot += v;
+        }
+        // (the schedule's values are the same in every lane: scalar registers)
+        tot = __builtin_amdgcn_readfirstlane(tot);
+        // (with fewer steps than workgroups only the first T take part, so
+        // that every range holds a step: a unit's partials then come from
+        // exactly the workgroups its steps fall into)
+        const long long T = static_cast<long long>(tot) * p.H_kv;
+        const int nwg = T < p.n_wg ? static_cast<int>(T) : p.n_wg;
+        const long long s0 = static_cast<long long>(wid) * T / nwg;
+        const long long s1 = static_cast<long long>(wid + 1) * T / nwg;
+        __syncthreads();                  // (bal_misc is reused below)
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int bb = tid0 * PER + k;
+            if (bb < p.B) {
+                bal_pre[bb] = ex;
+                // the sequence holding this workgroup's first step
+                if (static_cast<long long>(ex) * p.H_kv <= s0 && s0 < static_cast<long long>(ex + nst[k]) * p.H_kv)
+                    bal_misc[NW] = bb;
+            }
+            ex += nst[k];
+        }
+        if (tid0 == 0) bal_pre[p.B] = tot;
+        __syncthreads();
+        if (wid >= nwg) return;
+    }
+
+    // MODE 3 without a window (split schedule): the split's first block is
+    // known before its sequence's length (the split starts at split *
+    // split_tokens), so the table entries it may span are requested together
+    // with the length, and the first tile waits for one round trip less.
+    // (Entries past the row are clamped into it; those past the split are not
+    // used.)
+    constexpr int kTblPer = kTblMax / (NW * 64);
+    int tv[kTblPer];
+    const bool tbl_early = MODE == 3 && p.window == 0 && !BAL;
+
+    // (one pass under the split schedule: a trip count the compiler can see
+    // keeps its register allocation that of straight-line code)
+    for (int it = 0; BAL || it < 1; ++it) {
+    // ---- one split (balanced schedule: one segment) of one unit
+    int unit, split, nsp, t_begin, t_end, t_lo, L, pos;
+    int bal_wf = 0, bal_slot0 = 0;        // the unit's first workgroup; slot of its partial
+    size_t bal_row = 0;                   // this segment's partial rows
+    if constexpr (BAL) {
+        // Segment it is the workgroup's it-th unit: everything is derived
+        // again from LDS and the iteration count, so no state of the schedule
+        // stays live through the split body (its scalar registers are full).
+        const int tot = __builtin_amdgcn_readfirstlane(bal_pre[p.B]);
+        const long long T = static_cast<long long>(tot) * p.H_kv;
+        const int nwg = T < p.n_wg ? static_cast<int>(T) : p.n_wg;
+        const long long s0 = static_cast<long long>(wid) * T / nwg;
+        const long long s1 = static_cast<long long>(wid + 1) * T / nwg;
+        auto unit_start = [&](int b_, int j_, int& n_) -> long long {   // first step of unit (b_, j_); n_: its steps
+            const int pre = __builtin_amdgcn_readfirstlane(bal_pre[b_]);
+            n_ = __builtin_amdgcn_readfirstlane(bal_pre[b_ + 1]) - pre;
+            return static_cast<long long>(p.H_kv) * pre + static_cast<long long>(j_) * n_;
+        };
+        int n0;
+        const int b0 = __builtin_amdgcn_readfirstlane(bal_misc[NW]);   // the sequence holding step s0
+        const long long sb0 = unit_start(b0, 0, n0);
+        const int u = b0 * p.H_kv + static_cast<int>((s0 - sb0) / n0) + it;
+        if (u >= p.B * p.H_kv) break;
+        const int bq = u / p.H_kv, jj = u - bq * p.H_kv;
+        int nb_;
+        const long long ub = unit_start(bq, jj, nb_);                  // the unit's steps [ub, ue)
+        if (ub >= s1) break;
+        const long long ue = ub + nb_;
+        const long long sa = ub > s0 ? ub : s0;                        // this segment: [sa, se)
+        const long long se = ue < s1 ? ue : s1;
+        // workgroup holding step x: the last w with w T / N <= x
+        auto w_of = [&](long long x) { return static_cast<int>(((x + 1) * nwg - 1) / T); };
+        bal_wf = w_of(ub);
+        unit = u;
+        nsp = w_of(ue - 1) - bal_wf + 1;
+        split = wid - bal_wf;
+        L = __builtin_amdgcn_readfirstlane(bal_len[bq]);
+        pos = FUSED ? __builtin_amdgcn_readfirstlane(bal_pos[bq]) : 0;
+        t_begin = static_cast<int>(sa - ub) * kStep;
+        t_end = min(static_cast<int>(se - ub) * kStep, L);
+        t_lo = 0;
+        // the unit's first partial is its first workgroup's second segment when
+        // that workgroup's range starts before the unit
+        bal_slot0 = static_cast<long long>(bal_wf) * T / nwg < ub ? 1 : 0;
+        bal_row = static_cast<size_t>(2 * wid + (it == 0 ? 0 : 1)) * G;
+        // (the previous segment's output stores, before this one's loads)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    } else {
+        // Workgroups in launch order: the splits of one (sequence, KV head)
+        // are neighbours, and the hardware deals consecutive workgroups to the
+        // XCDs in turn.  (Grouping each unit's splits on one XCD gains nothing
+        // for a stream without reuse, and with ragged lengths it left some
+        // XCDs with far more work than others: the paged workload ran 2.4 %
+        // slower.)
+        split = wid % p.n_splits;
+        unit = wid / p.n_splits;          // b * H_kv + j (MQ: (b * H_kv + j) * n_chunks + chunk)
+        if constexpr (MODE == 3) {
+            if (tbl_early) {
+                const int b0 = (MQ ? unit / p.n_chunks : unit) / p.H_kv;
+                const int fb0 = (split * p.split_tokens) / p.block_size;
+                const int span = min(p.split_tokens / p.block_size + 1, p.max_blocks_per_seq - fb0);
+                const int32_t* trow = block_table + static_cast<size_t>(b0) * p.max_blocks_per_seq;
+                const int first = min(fb0, p.max_blocks_per_seq - 1);
+#pragma unroll
+                for (int k = 0; k < kTblPer; ++k) {
+                    const int i = tid0 + k * NW * 64;
+                    tv[k] = trow[i < span ? fb0 + i : first];
+                }
+            }
+        }
+        const int b0 = (MQ ? unit / p.n_chunks : unit) / p.H_kv;
+        // fused step: slot of the new token (read once; it also gives L)
+        pos = FUSED ? p.positions[b0] : 0;
+        L = FUSED ? len_from_position(p, pos) : attended_len(p, b0);
+        // attended tokens [t_lo, hi) (a sliding window starts past 0); the
+        // paged modes start their splits at t_lo rounded down to 16 and read
+        // the rows before t_lo as zeros (out-of-range offsets) or as row
+        // t_lo, masked
+        const TokenRange tr = token_range(p, L);
+        nsp = split_count(p, tr);
+        if (split >= nsp) return;
+        t_begin = tr.org + split * p.split_tokens;
+        t_end = split_end(p, tr, split, nsp);
+        t_lo = tr.lo;
+    }
+    // The lane index, opaque to the compiler inside each segment of the
+    // balanced schedule: the per-lane offsets derived from it are then
+    // computed per segment rather than hoisted above the segment loop, where
+    // they would stay live through every epilogue (about 50 registers more).
+    int tid = tid0;
+    if constexpr (BAL) asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int chunk = MQ ? unit % p.n_chunks : 0;
     const int bj = MQ ? unit / p.n_chunks : unit;
     const int b = bj / p.H_kv;
     const int j = bj % p.H_kv;
-    const int G = p.G;
-    static_assert(!(MQ && FUSED), "several new tokens: the append runs first");
 
-    // MODE 3 without a window: the split's first block is known before its
-    // sequence's length (the split starts at split * split_tokens), so the
-    // table entries it may span are requested together with the length, and
-    // the first tile waits for one round trip less.  (Entries past the row
-    // are clamped into it; those past the split are not used.)
-    constexpr int kTblPer = kTblMax / (NW * 64);
-    int tv[kTblPer];
-    const bool tbl_early = MODE == 3 && p.window == 0;
-    if constexpr (MODE == 3) {
-        if (tbl_early) {
-            const int fb0 = (split * p.split_tokens) / p.block_size;
-            const int span = min(p.split_tokens / p.block_size + 1, p.max_blocks_per_seq - fb0);
-            const int32_t* trow = block_table + static_cast<size_t>(b) * p.max_blocks_per_seq;
-            const int first = min(fb0, p.max_blocks_per_seq - 1);
-#pragma unroll
-            for (int k = 0; k < kTblPer; ++k) {
-                const int i = static_cast<int>(threadIdx.x) + k * NW * 64;
-                tv[k] = trow[i < span ? fb0 + i : first];
-            }
-        }
-    }
-
-    // fused step: slot of the new token (read once; it also gives L)
-    const int pos = FUSED ? p.positions[b] : 0;
-    const int L = FUSED ? len_from_position(p, pos) : attended_len(p, b);
-    // attended tokens [t_lo, hi) (a sliding window starts past 0); the paged
-    // modes start their splits at t_lo rounded down to 16 and read the rows
-    // before t_lo as zeros (out-of-range offsets) or as row t_lo, masked
-    const TokenRange tr = token_range(p, L);
-    const int nsp = split_count(p, tr);
-    if (split >= nsp) return;
-    const int t_begin = tr.org + split * p.split_tokens;
-    const int t_end = split_end(p, tr, split, nsp);
-    const int t_lo = tr.lo;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15;            // row/column index inside the operand
     const int q4 = lane >> 4;             // 16-lane group: reduction slots 8*q4 .. +7
 
@@ -252,14 +402,21 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     // the staged table slice; its range ends at the last row < t_end, so rows
     // past the split read as zeros without a memory access.
     const int fb = PAGED ? t_begin / p.block_size : 0;   // first block index of the split
-    auto tile_rsrc = [&](const uint16_t* pool, int row0_) -> __amdgpu_buffer_rsrc_t {
+    // (the block id of the tile at row0, read from the staged slice; a tile's
+    // K and V rows share it, so the tile computation reads it once, early,
+    // for the tile it refills)
+    auto tile_block = [&](int row0_) -> int {
+        const int row0 = __builtin_amdgcn_readfirstlane(row0_);
+        int ti = row0 / p.block_size - fb;
+        ti = ti < 0 ? 0 : (ti >= kTblMax ? kTblMax - 1 : ti);
+        return tbl_lds[ti];
+    };
+    auto tile_rsrc = [&](const uint16_t* pool, int row0_, int blk_) -> __amdgpu_buffer_rsrc_t {
         const int row0 = __builtin_amdgcn_readfirstlane(row0_);
         int nvalid = __builtin_amdgcn_readfirstlane(t_end) - row0;
         nvalid = nvalid < 0 ? 0 : (nvalid > 16 ? 16 : nvalid);
         const int lb = row0 / p.block_size;
-        int ti = lb - fb;
-        ti = ti < 0 ? 0 : (ti >= kTblMax ? kTblMax - 1 : ti);
-        const int blk = __builtin_amdgcn_readfirstlane(nvalid > 0 ? tbl_lds[ti] : 0);
+        const int blk = __builtin_amdgcn_readfirstlane(nvalid > 0 ? blk_ : 0);
         const int in_blk = row0 - lb * p.block_size;
         const uint16_t* g0 = pool + ((static_cast<size_t>(blk) * p.H_kv + j) * p.block_size + in_blk) * D;
         return make_uniform_rsrc(g0, nvalid * D * 2);
@@ -294,7 +451,7 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     // registers: lane l of load i fills LDS bytes [16 l, 16 l + 16) of that
     // load's 1 KiB, i.e. row VROWS*i + l / LPR, slot l % LPR, so it fetches
     // chunk (slot ^ swizzle(row)).
-    auto load_rows = [&](auto is_k, int base, char* buf) __attribute__((always_inline)) {
+    auto load_rows = [&](auto is_k, int base, char* buf, int blk_) __attribute__((always_inline)) {
         constexpr bool ISK = decltype(is_k)::value;
         const uint16_t* pool = ISK ? kbase : vbase;
         char* wbuf = buf + wave * STAGE;
@@ -307,7 +464,7 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
             // (rows before the window's first token get an offset past the
             // 16-row range, so they read as zeros without a memory access)
             if constexpr (MODE == 3) {
-                const __amdgpu_buffer_rsrc_t rs = tile_rsrc(pool, base);
+                const __amdgpu_buffer_rsrc_t rs = tile_rsrc(pool, base, blk_);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, ((t < t_lo ? 16 : r) * D + 8 * u) * 2, 0, 0,
                                                          kNT);
             } else if constexpr (MODE == 2) {
@@ -325,9 +482,10 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     };
     // one tile: K (LDS or registers), then V
     auto load_tile = [&](int base, uint4 (&ka)[KB][KK], char* kb, char* vb) __attribute__((always_inline)) {
-        if constexpr (KLDS) load_rows(std::true_type{}, base, kb);
+        const int blk = MODE == 3 ? tile_block(base) : 0;
+        if constexpr (KLDS) load_rows(std::true_type{}, base, kb, blk);
         else load_k(base, ka);
-        load_rows(std::false_type{}, base, vb);
+        load_rows(std::false_type{}, base, vb, blk);
     };
     // K operand of a tile staged in LDS: lane (r16, q4) takes 16-byte chunk
     // 4*kk + q4 of rows r16 and 16 + r16 (the layout load_k produces)
@@ -346,7 +504,6 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     // step, the new token and its rotation table row), then the first tile:
     // loads complete in order, so the rotation waits for the small loads
     // only and runs while the tile is in flight.
-    constexpr int kStep = NW * TT;
     int base = t_begin + (ILV ? 0 : wave * TT);   // step base: the workgroup's, or this wave's
     uint4 ka0[KB][KK], ka1[KB][KK];
 
@@ -558,6 +715,9 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     // keeps the compiler from moving the refill in among those reads.
     auto compute_tile = [&](uint4 (&ka)[KB][KK], char* kb, char* buf, int base) __attribute__((always_inline)) {
         char* wbuf = buf + wave * STAGE;
+        // block id of the tile NSTG steps ahead (paged, staged table): read
+        // first, so the wait before the K refill covers it
+        const int blk_next = MODE == 3 ? tile_block(base + NSTG * kStep) : 0;
         if constexpr (KLDS) {
             // this tile's K rows were issued before its V rows and nothing
             // after those (two stages: and the next tile's K and V): at most
@@ -568,7 +728,7 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
             // the tile NSTG steps ahead go out now (past the split: zeros,
             // no traffic)
             __builtin_amdgcn_s_waitcnt(kLgkmZero);
-            load_rows(std::true_type{}, base + NSTG * kStep, kb);
+            load_rows(std::true_type{}, base + NSTG * kStep, kb, blk_next);
         }
         // the tile holding the new token (fused step): its key row goes into
         // the K operand here, its value row over the staged one below
@@ -613,8 +773,11 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
         // online softmax per head.  The reference max m is only moved when the
         // tile max exceeds it by more than 2^kLazy (then O and l are rescaled);
         // otherwise p = 2^(s - m) <= 2^kLazy, exact after the final division.
-        // P^T goes in as two bf16 B operands, hi + lo = p to ~16 significant bits.
-        uint32_t ph[HB][NS / 2], pl[HB][NS / 2];
+        // P^T goes in as three bf16 B operands, hi + mid + lo = p to ~24
+        // significant bits (the 32-row multi-token kernel, whose registers
+        // have no room for a third, as two: ~16 bits).
+        constexpr bool P3 = !(MQ && HB == 2);
+        uint32_t ph[HB][NS / 2], pm[HB][NS / 2], pl[HB][NS / 2];
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb) {
             float mt = s[hb][0];
@@ -639,7 +802,9 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
 #pragma unroll
             for (int i = 0; i < NS / 2; ++i) {
                 ph[hb][i] = pack2_bf16(pr[2 * i], pr[2 * i + 1]);
-                pl[hb][i] = pack2_bf16(pr[2 * i] - bf16_lo(ph[hb][i]), pr[2 * i + 1] - bf16_hi(ph[hb][i]));
+                const float r0 = pr[2 * i] - bf16_lo(ph[hb][i]), r1 = pr[2 * i + 1] - bf16_hi(ph[hb][i]);
+                pm[hb][i] = pack2_bf16(r0, r1);
+                if constexpr (P3) pl[hb][i] = pack2_bf16(r0 - bf16_lo(pm[hb][i]), r1 - bf16_hi(pm[hb][i]));
             }
             l[hb] += ps;
         }
@@ -678,20 +843,27 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
 #pragma unroll
                 for (int hb = 0; hb < HB; ++hb) {
                     o[hb][nb] = mfma16(va, make_uint4(ph[hb][0], ph[hb][1], ph[hb][2], ph[hb][3]), o[hb][nb]);
-                    o[hb][nb] = mfma16(va, make_uint4(pl[hb][0], pl[hb][1], pl[hb][2], pl[hb][3]), o[hb][nb]);
+                    o[hb][nb] = mfma16(va, make_uint4(pm[hb][0], pm[hb][1], pm[hb][2], pm[hb][3]), o[hb][nb]);
+                    if constexpr (P3)
+                        o[hb][nb] = mfma16(va, make_uint4(pl[hb][0], pl[hb][1], pl[hb][2], pl[hb][3]), o[hb][nb]);
                 }
             } else {
 #pragma unroll
                 for (int hb = 0; hb < HB; ++hb) {
                     o[hb][nb] = mfma16k16(lo, make_uint2(ph[hb][0], ph[hb][1]), o[hb][nb]);
-                    o[hb][nb] = mfma16k16(lo, make_uint2(pl[hb][0], pl[hb][1]), o[hb][nb]);
+                    o[hb][nb] = mfma16k16(lo, make_uint2(pm[hb][0], pm[hb][1]), o[hb][nb]);
+                    if constexpr (P3) o[hb][nb] = mfma16k16(lo, make_uint2(pl[hb][0], pl[hb][1]), o[hb][nb]);
                 }
             }
         }
         if constexpr (KLDS) {
-            // the V stage is free: the V rows of the tile NSTG steps ahead go out
+            // the V stage is free: the V rows of the tile NSTG steps ahead go
+            // out.  (Issued before the products instead - the operand reads
+            // first, then the refill, then the products behind a scheduling
+            // barrier - the stream ran ~1 % slower: the products then no
+            // longer overlap the transposed reads.)
             __builtin_amdgcn_s_waitcnt(kLgkmZero);
-            load_rows(std::false_type{}, base + NSTG * kStep, buf);
+            load_rows(std::false_type{}, base + NSTG * kStep, buf, blk_next);
         }
     };
 
@@ -851,12 +1023,12 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
                 } else if (p.merge_cnt != nullptr) {
                     // device-scope stores (written through to memory that
                     // every XCD sees), for the merge below
-                    const int o = static_cast<int>(((bh * p.n_splits + split) * D + c) * 4);
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, A), part_rs, o, 0, kDevScope);
+                    const size_t pr = BAL ? bal_row + 16 * hb + gh : bh * p.n_splits + split;
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, A), part_rs,
+                                                           static_cast<int>((pr * D + c) * 4), 0, kDevScope);
                     if (ch == 0)
-                        __builtin_amdgcn_raw_buffer_store_b64(
-                            __builtin_bit_cast(u32x2_t, make_float2(M, Ls)), ml_rs,
-                            static_cast<int>((bh * p.n_splits + split) * 8), 0, kDevScope);
+                        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, make_float2(M, Ls)),
+                                                              ml_rs, static_cast<int>(pr * 8), 0, kDevScope);
                 } else {
                     *reinterpret_cast<float4*>(p.ws_part + (bh * p.n_splits + split) * D + c) = A;
                     if (ch == 0) p.ws_ml[bh * p.n_splits + split] = make_float2(M, Ls);
@@ -875,17 +1047,18 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     // cache is flushed.  The merge: M = max_s m_s, w_s = 2^(m_s - M),
     // out = sum_s w_s acc_s / sum_s w_s l_s, the splits in order, MB of them
     // requested at a time (their max folded into the running one).
+    // (Balanced schedule: the unit's partials are those of workgroups wf ..
+    // wf + nsp - 1, each in its first-segment slot except the first one's.)
     if (nsp > 1 && p.merge_cnt != nullptr) {
-        __shared__ int s_last;
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __syncthreads();
         if (tid == 0)
             s_last = __builtin_amdgcn_atomic_inc32(p.merge_cnt + unit, static_cast<unsigned>(nsp - 1),
                                                    __ATOMIC_RELAXED, "agent") == static_cast<unsigned>(nsp - 1);
         __syncthreads();
-        if (!s_last) return;
+        if (!s_last) continue;
         const int rows = MQ ? min(16 * HB, G * p.qlen - chunk * 16 * HB) : G;
-        merge_split_rows<D>(p, part_rs, ml_rs, rows, nsp, [&](int gr) -> size_t {
+        auto row_of = [&](int gr) -> size_t {
             if constexpr (MQ) {
                 const int rho = chunk * 16 * HB + gr;
                 const int qi = rho / G;
@@ -893,8 +1066,15 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
             } else {
                 return static_cast<size_t>(b) * p.H_q + j * G + gr;
             }
+        };
+        merge_split_rows<D>(p, part_rs, ml_rs, rows, nsp, row_of, [&](int gr, int sp) -> size_t {
+            if constexpr (BAL)
+                return static_cast<size_t>(2 * (bal_wf + sp) + (sp == 0 ? bal_slot0 : 0)) * G + gr;
+            else
+                return row_of(gr) * p.n_splits + sp;
         });
     }
+    }   // segments
 }
 
 constexpr int kNWm = 4;
@@ -903,14 +1083,26 @@ template <int D, int HB, bool FUSED, bool MQ>
 hipError_t launch_dhf(bool paged, const DecodeParams& p, hipStream_t stream, const KernelTiming& tm) {
     const dim3 grid(p.n_wg_pad), block(kNWm * 64);
     const int32_t* tbl = p.block_table;
-    if (!paged) return launch_timed(decode_mfma_kernel<D, HB, kNWm, 0, FUSED, MQ>, grid, block, stream, tm, p, tbl);
+    if constexpr (D <= 128 && !MQ) {
+        // balanced schedule (planned for paged pools, d <= 128, one new token,
+        // no window, block sizes that are multiples of 16, at most kBalMaxB
+        // sequences)
+        if (p.bal) {
+            if (!paged || p.B > kBalMaxB || p.block_size % 16 != 0) return hipErrorInvalidValue;
+            return launch_timed(decode_mfma_kernel<D, HB, kNWm, 3, FUSED, MQ, true>, grid, block, stream, tm, p, tbl);
+        }
+    }
+    if (p.bal) return hipErrorInvalidValue;
+    if (!paged)
+        return launch_timed(decode_mfma_kernel<D, HB, kNWm, 0, FUSED, MQ, false>, grid, block, stream, tm, p, tbl);
     if constexpr (D <= 128) {
         if (p.block_size % 16 == 0 && p.split_tokens % 16 == 0 && p.split_tokens / p.block_size + 2 <= kTblMax)
-            return launch_timed(decode_mfma_kernel<D, HB, kNWm, 3, FUSED, MQ>, grid, block, stream, tm, p, tbl);
+            return launch_timed(decode_mfma_kernel<D, HB, kNWm, 3, FUSED, MQ, false>, grid, block, stream, tm, p,
+                                tbl);
     }
     if (p.block_size % 16 == 0 && p.split_tokens % 32 == 0)
-        return launch_timed(decode_mfma_kernel<D, HB, kNWm, 2, FUSED, MQ>, grid, block, stream, tm, p, tbl);
-    return launch_timed(decode_mfma_kernel<D, HB, kNWm, 1, FUSED, MQ>, grid, block, stream, tm, p, tbl);
+        return launch_timed(decode_mfma_kernel<D, HB, kNWm, 2, FUSED, MQ, false>, grid, block, stream, tm, p, tbl);
+    return launch_timed(decode_mfma_kernel<D, HB, kNWm, 1, FUSED, MQ, false>, grid, block, stream, tm, p, tbl);
 }
 
 // rows: query rows one workgroup serves (G, or a chunk of the G * qlen rows
@@ -943,9 +1135,13 @@ int decode_mfma_wgs_per_cu(int d, int G, bool paged) {
     // cache at d = 128 still streamed best with one workgroup per CU (its
     // 32 KiB in flight is what a plain streaming read needs; two measured
     // about 1.5 % slower); a ragged paged pool, whose many short splits each
-    // pay a prologue, with three (registers: about 168 per lane with one
-    // 16-head block, three waves per SIMD; about 260 with two, one).  At
-    // d = 256 (TT = 32, K in registers): two V tiles per wave, 128 KiB.
+    // pay a prologue, with three (registers: at most 168 per lane with one
+    // 16-head block, three waves per SIMD).  Two 16-head blocks: planned as
+    // one, though over a contiguous cache the kernel's registers are held to
+    // two waves per SIMD and a CU runs two of them (the split plans for those
+    // groups, about three workgroups per slot, were measured with this count:
+    // doubling it doubled the multi-token workload's splits, 96 -> 106 us).
+    // At d = 256 (TT = 32, K in registers): two V tiles per wave, 128 KiB.
     const bool two_blocks = G > 16;
     if (d <= 64) return two_blocks ? 2 : (paged ? 3 : 2);
     if (d <= 128) return two_blocks ? 1 : (paged ? 3 : 1);

@@ -715,7 +715,8 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
         __syncthreads();
         if (!s_last) return;
         const size_t row0 = static_cast<size_t>(b) * p.H_q + static_cast<size_t>(j) * G;
-        merge_split_rows<D>(p, part_rs, ml_rs, G, nsp, [&](int gr) -> size_t { return row0 + gr; });
+        merge_split_rows<D>(p, part_rs, ml_rs, G, nsp, [&](int gr) -> size_t { return row0 + gr; },
+                            [&](int gr, int s) -> size_t { return (row0 + gr) * p.n_splits + s; });
     }
 }
 

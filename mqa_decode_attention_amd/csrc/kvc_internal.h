@@ -53,7 +53,19 @@ struct DecodePlan {
     size_t ws_part;
     size_t ws_bytes;    // 0 when n_splits == 1
     bool merge_in_kernel;   // the streaming kernel merges the splits (no merge launch)
+    // Balanced schedule of the bf16 matrix-core kernel: bal_wg workgroups share
+    // the steps of all units equally, whatever the lengths (ws_ml / ws_part
+    // then hold 2 * G partial rows per workgroup; ws_bytes also covers the
+    // split layout, which calls the balanced kernel does not serve use).
+    bool bal;
+    int bal_wg;
 };
+
+// Sequences the balanced schedule handles (their lengths are staged in LDS).
+constexpr int kBalMaxB = 512;
+// Longest range of loop steps one workgroup of the balanced schedule takes
+// (its paged segments then span at most kTblMax - 2 blocks of 16 tokens).
+constexpr int kBalMaxSteps = 240;
 
 // Largest split count the merge step supports (partials live in LDS).
 constexpr int kMaxSplits = 256;
@@ -90,6 +102,7 @@ struct DecodeParams {
     int max_seq_len, split_tokens, n_splits;
     int split_tail;              // the last split also takes up to this many tokens (a short remainder)
     int n_wg, n_wg_pad;          // logical workgroups, padded to a multiple of 8
+    int bal;                     // balanced schedule (n_wg workgroups share all units' steps)
     float scale_log2;            // softmax scale * log2(e)
 
     // Set for kvc_decode_step: lengths come from positions (L_b = positions[b] + 1)
@@ -169,8 +182,11 @@ __device__ __forceinline__ int split_end(const DecodeParams& p, const TokenRange
 // pool_tokens: token capacity of a paged pool (num_blocks * block_size), which
 // bounds the tokens all sequences attend over together; 0 for a contiguous cache.
 // qlen: new tokens per sequence (query rows G * qlen per KV group).
+// allow_bal: the call may use the balanced schedule (a single-token decode
+// over a full cache); the workspace size is the same either way.
 bool plan_decode(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_len,
-                 long long pool_tokens, int split_tokens, DecodePlan* plan, const char** why, int qlen = 1);
+                 long long pool_tokens, int split_tokens, DecodePlan* plan, const char** why, int qlen = 1,
+                 bool allow_bal = true);
 
 // Is there a kernel for this (dtype, head dim, heads per workgroup)?
 bool decode_supported(kvc_dtype dtype, int d, int heads_per_wg);

@@ -96,18 +96,19 @@ constexpr int kDevScope = 16;
 // w_s = 2^(m_s - M), out = sum_s w_s acc_s / sum_s w_s l_s, the splits in
 // order, MB of them requested at a time (their max folded into the running
 // one).  rows: output rows of the unit; row_of(r): the output row index of its
-// row r (the partials of output row i are at i * n_splits + s).  One thread
-// per 16-byte column chunk of a row, bf16 output.
-template <int D, typename RowOf>
+// row r; part_of(r, s): the index of split s's partial row for it (the
+// partial rows are D floats each in ws_part, their (m, l) pairs in ws_ml).
+// One thread per 16-byte column chunk of a row, bf16 output.
+template <int D, typename RowOf, typename PartOf>
 __device__ __forceinline__ void merge_split_rows(const DecodeParams& p, __amdgpu_buffer_rsrc_t part_rs,
-                                                 __amdgpu_buffer_rsrc_t ml_rs, int rows, int nsp, RowOf row_of) {
+                                                 __amdgpu_buffer_rsrc_t ml_rs, int rows, int nsp, RowOf row_of,
+                                                 PartOf part_of) {
     constexpr int NCH = D / 4;
     constexpr int MB = 8;
     for (int idx = threadIdx.x; idx < rows * NCH; idx += blockDim.x) {
         const int c = 4 * (idx % NCH);
-        const size_t bh = row_of(idx / NCH);
-        const int ml0 = static_cast<int>(bh * p.n_splits * 8);
-        const int part0 = static_cast<int>((bh * p.n_splits * D + c) * 4);
+        const int gr = idx / NCH;
+        const size_t bh = row_of(gr);
         float M = -INFINITY, Ls = 0.0f;
         float4 A = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         for (int s0 = 0; s0 < nsp; s0 += MB) {
@@ -116,13 +117,13 @@ __device__ __forceinline__ void merge_split_rows(const DecodeParams& p, __amdgpu
 #pragma unroll
             for (int u = 0; u < MB; ++u) {
                 if (s0 + u < nsp) {
-                    const int sp = s0 + u;
+                    const size_t pr = part_of(gr, s0 + u);
                     const float2 m2 = __builtin_bit_cast(
-                        float2, __builtin_amdgcn_raw_buffer_load_b64(ml_rs, ml0 + 8 * sp, 0, kDevScope));
+                        float2, __builtin_amdgcn_raw_buffer_load_b64(ml_rs, static_cast<int>(pr * 8), 0, kDevScope));
                     mv[u] = m2.x;
                     lv[u] = m2.y;
                     pv[u] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                           part_rs, part0 + 4 * D * sp, 0, kDevScope));
+                                                           part_rs, static_cast<int>((pr * D + c) * 4), 0, kDevScope));
                 }
             }
             float Mb = M;

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kvc_abi_version() == _lib.ABI_VERSION == 11
+    assert lib.kvc_abi_version() == _lib.ABI_VERSION == 12
     for s in range(6):
         assert lib.kvc_status_string(s)
     assert lib.kvc_status_string(99) == b"unknown status"
@@ -209,7 +209,7 @@ def test_split_choice(lib):
     assert ml(BF16, 16, 32, 8, 128, 8193, 0, 0) == 0            # 256 workgroups on 256 slots
     assert ml(BF16, 1, 64, 8, 128, 131073, 0, 0) == 0
     assert ml(U8, 16, 32, 8, 128, 8193, 0, 0) == 0              # 512 on 512
-    assert ml(BF16, 64, 32, 1, 128, 4097, 0, 0) == 1            # ~3 rounds
+    assert ml(BF16, 64, 32, 1, 128, 4097, 0, 0) == 1            # G = 32: ~3 per slot
     assert ml(BF16, 16, 32, 8, 128, 8193, 0, 1024) == 1         # 1152 workgroups
     assert ml(F32, 16, 32, 8, 128, 8193, 0, 0) == 1             # the vector kernel
     assert ml(BF16, 16, 32, 8, 128, 100, 0, 0) == 0             # one split
@@ -400,3 +400,34 @@ def test_step_u8_host_checks(lib):
     need = lib.kvc_decode_workspace_bytes(U8, 2, 8, 2, 128, 100000, 0, 0)
     assert need > 0
     assert _step_u8(lib, T_max=100000, max_len=100000) == KVC_ERR_WORKSPACE
+
+
+def test_balanced_schedule_choice(lib):
+    """The balanced schedule serves ragged paged pools (bf16, head_dim <= 128,
+    the library's split choice, at most 512 sequences); its workspace: the
+    64 KiB of counters, then two partial rows per query head of a group for
+    each of its workgroups (one round: 768 for the paged kernel's three per
+    CU at one 16-head block, 256 at two), or the split plan's size when that
+    is larger."""
+    bal = lib.kvc_decode_balanced
+    wsb = lib.kvc_decode_workspace_bytes
+    zb = lib.kvc_workspace_zeroed_bytes()
+    pool = 32 * 8700                                            # ragged paged pool
+    assert bal(BF16, 32, 32, 8, 128, 16385, pool, 0) == 1
+    assert bal(BF16, 32, 32, 8, 64, 16385, pool, 0) == 1
+    assert bal(BF16, 32, 32, 8, 128, 16385, 32 * 16400, 0) == 0  # a pool as large as B * L
+    assert bal(BF16, 32, 32, 8, 256, 16385, pool, 0) == 0       # head_dim 256
+    assert bal(BF16, 32, 32, 8, 128, 16385, pool, 768) == 0     # explicit splits
+    assert bal(F32, 32, 32, 8, 128, 16385, pool, 0) == 0        # the vector kernel
+    assert bal(U8, 32, 32, 8, 128, 16385, pool, 0) == 0         # the quantized kernel
+    assert bal(BF16, 513, 32, 8, 128, 16385, pool, 0) == 0      # more sequences than staged
+    assert bal(BF16, 16, 32, 8, 128, 8193, 0, 0) == 0           # contiguous caches: splits
+    assert bal(BF16, 64, 32, 1, 128, 4097, 0, 0) == 0
+    assert bal(BF16, 16, 30, 8, 128, 100, pool, 0) == -1
+    # workspace: the larger of the two layouts
+    n = wsb(BF16, 32, 32, 8, 128, 16385, pool, 0)
+    assert n >= zb + 768 * 2 * 4 * (8 + 128 * 4) and n % 256 == 0
+    # groups of 32 heads: 256 workgroups (one per CU), 32 rows each
+    assert wsb(BF16, 32, 64, 2, 128, 16385, 32 * 8700, 0) >= zb + 256 * 2 * 32 * (8 + 128 * 4)
+    # a short call still needs its partial rows (units shared by workgroups)
+    assert wsb(BF16, 3, 32, 8, 128, 200, 3 * 16 * 5, 0) == zb + 768 * 2 * 4 * (8 + 128 * 4)
