@@ -205,22 +205,24 @@ bool plan_decode(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_l
         pl.merge_in_kernel = pl.mfma && units <= kMergeCounters && units * pl.n_splits <= slots &&
                              pl.ws_bytes - pl.ws_part < (size_t{1} << 31);
     }
-    // Balanced schedule (bf16 matrix-core kernel, one new token, library
-    // splits) for ragged paged pools, whose split plan above is sized from
-    // the longest sequence and leaves many short or empty splits, each paying
-    // a prologue.  One round of workgroups (more only if a workgroup would
-    // take more than kBalMaxSteps steps); the step count must fit in 31 bits.
+    // Balanced schedule (the matrix-core kernels, bf16 or uint8 cache, one
+    // new token, library splits) for ragged paged pools, whose split plan
+    // above is sized from the longest sequence and leaves many short or empty
+    // splits, each paying a prologue.  One round of workgroups (more only if
+    // a workgroup would take more than kBalMaxTokens tokens); the step count
+    // must fit in 31 bits.
     // (Measured on the ragged paged workload: 202 -> 198 us.  Over a
     // contiguous cache with groups of 32 heads it was slower than the split
     // plan - 25 -> 39 us on the ragged MQA workload, whose per-segment
     // prologue and epilogue cost as much as a share of the stream - so
     // contiguous caches keep the split plan.)
-    if (allow_bal && split_tokens == 0 && pl.mfma && !u8 && qlen <= 1 && d <= 128 && B <= kBalMaxB &&
+    if (allow_bal && split_tokens == 0 && pl.mfma && qlen <= 1 && d <= 128 && B <= kBalMaxB &&
         units <= kMergeCounters) {
         const bool ragged_pool = pool_tokens > 0 && pool_tokens * H_kv * 10 < units * L * 9;
         const long long steps = units * ((L + tile - 1) / tile);      // >= the steps of any call
         if (ragged_pool && steps < (1LL << 31) - units) {
-            const long long nwg = std::max(slots, (steps + kBalMaxSteps - 1) / kBalMaxSteps);
+            const long long max_steps = kBalMaxTokens / tile;
+            const long long nwg = std::max(slots, (steps + max_steps - 1) / max_steps);
             const size_t rows = static_cast<size_t>(nwg) * 2 * G;    // two partial slots per workgroup
             const size_t ml = kWsCounterBytes;
             const size_t part = align_up(ml + rows * sizeof(float2), 256);

@@ -108,11 +108,7 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     __shared__ float sm_ml[2 * NW * 16];   // the waves' (m, l) per head row, for their merge
 
     __shared__ int s_last;                 // the in-kernel merge: this workgroup arrived last
-    // balanced schedule: per-sequence step prefix, lengths, positions
-    __shared__ int bal_pre[BAL ? kBalMaxB + 1 : 1];
-    __shared__ int bal_len[BAL ? kBalMaxB : 1];
-    __shared__ int bal_pos[(BAL && FUSED) ? kBalMaxB : 1];
-    __shared__ int bal_misc[NW + 1];
+    __shared__ std::conditional_t<BAL, BalLds, char> bal;   // the balanced schedule's lengths and prefix
 
     const int wid = blockIdx.x < static_cast<unsigned>(p.n_wg) ? static_cast<int>(blockIdx.x) : -1;
     if (wid < 0) return;
@@ -123,77 +119,11 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
 
     const int tid0 = threadIdx.x;
 
-    // Balanced schedule.  Sequence b holds n_b = ceil(L_b / kStep) loop steps
-    // (at least one, so that an empty sequence still writes its zero rows) for
-    // each of its H_kv units; the units' steps, in unit order, form one list of
-    // T steps, and workgroup w of N takes steps [w T / N, (w + 1) T / N): every
-    // workgroup streams the same number of steps (within one), whatever the
-    // lengths, and all of them start at once (N is the planned count, or T
-    // when there are fewer steps).  A workgroup's range crosses
-    // units, so it runs the split body once per segment (a unit's steps inside
-    // the range); a unit that several workgroups share is merged by the last
-    // of them to finish, from partial rows each writes to one of two slots of
-    // its own (its first segment, its last one).  Every workgroup reads all B
-    // lengths once and derives its segments from them.
+    // Balanced schedule (paged pools with ragged lengths; the helpers in
+    // kvc_mfma_common.h): every workgroup reads all lengths, then runs its
+    // split body once per segment of its equal share of all units' steps.
     if constexpr (BAL) {
-        constexpr int PER = kBalMaxB / (NW * 64);
-        int nst[PER];
-        int sum = 0;
-#pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int bb = tid0 * PER + k;
-            int n = 0;
-            if (bb < p.B) {
-                const int ps = FUSED ? p.positions[bb] : 0;
-                const int Lb = FUSED ? len_from_position(p, ps) : attended_len(p, bb);
-                bal_len[bb] = Lb;
-                if constexpr (FUSED) bal_pos[bb] = ps;
-                n = Lb > 0 ? (Lb + kStep - 1) / kStep : 1;
-            }
-            nst[k] = n;
-            sum += n;
-        }
-        // exclusive prefix over the threads (each holds PER consecutive
-        // sequences): inside each wave, then over the waves' totals
-        int inc = sum;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int v = __shfl_up(inc, o, 64);
-            if ((tid0 & 63) >= o) inc += v;
-        }
-        if ((tid0 & 63) == 63) bal_misc[tid0 >> 6] = inc;
-        __syncthreads();
-        int ex = inc - sum, tot = 0;
-#pragma unroll
-        for (int w2 = 0; w2 < NW; ++w2) {
-            const int v = bal_misc[w2];
-            ex += w2 < (tid0 >> 6) ? v : 0;
-            tot += v;
-        }
-        // (the schedule's values are the same in every lane: scalar registers)
-        tot = __builtin_amdgcn_readfirstlane(tot);
-        // (with fewer steps than workgroups only the first T take part, so
-        // that every range holds a step: a unit's partials then come from
-        // exactly the workgroups its steps fall into)
-        const long long T = static_cast<long long>(tot) * p.H_kv;
-        const int nwg = T < p.n_wg ? static_cast<int>(T) : p.n_wg;
-        const long long s0 = static_cast<long long>(wid) * T / nwg;
-        const long long s1 = static_cast<long long>(wid + 1) * T / nwg;
-        __syncthreads();                  // (bal_misc is reused below)
-#pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int bb = tid0 * PER + k;
-            if (bb < p.B) {
-                bal_pre[bb] = ex;
-                // the sequence holding this workgroup's first step
-                if (static_cast<long long>(ex) * p.H_kv <= s0 && s0 < static_cast<long long>(ex + nst[k]) * p.H_kv)
-                    bal_misc[NW] = bb;
-            }
-            ex += nst[k];
-        }
-        if (tid0 == 0) bal_pre[p.B] = tot;
-        __syncthreads();
-        if (wid >= nwg) return;
+        if (!bal_setup<NW * 64, kStep, FUSED>(p, wid, bal)) return;
     }
 
     // MODE 3 without a window (split schedule): the split's first block is
@@ -211,49 +141,17 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     for (int it = 0; BAL || it < 1; ++it) {
     // ---- one split (balanced schedule: one segment) of one unit
     int unit, split, nsp, t_begin, t_end, t_lo, L, pos;
-    int bal_wf = 0, bal_slot0 = 0;        // the unit's first workgroup; slot of its partial
-    size_t bal_row = 0;                   // this segment's partial rows
+    BalSeg sg{};                          // balanced schedule: this segment
     if constexpr (BAL) {
-        // Segment it is the workgroup's it-th unit: everything is derived
-        // again from LDS and the iteration count, so no state of the schedule
-        // stays live through the split body (its scalar registers are full).
-        const int tot = __builtin_amdgcn_readfirstlane(bal_pre[p.B]);
-        const long long T = static_cast<long long>(tot) * p.H_kv;
-        const int nwg = T < p.n_wg ? static_cast<int>(T) : p.n_wg;
-        const long long s0 = static_cast<long long>(wid) * T / nwg;
-        const long long s1 = static_cast<long long>(wid + 1) * T / nwg;
-        auto unit_start = [&](int b_, int j_, int& n_) -> long long {   // first step of unit (b_, j_); n_: its steps
-            const int pre = __builtin_amdgcn_readfirstlane(bal_pre[b_]);
-            n_ = __builtin_amdgcn_readfirstlane(bal_pre[b_ + 1]) - pre;
-            return static_cast<long long>(p.H_kv) * pre + static_cast<long long>(j_) * n_;
-        };
-        int n0;
-        const int b0 = __builtin_amdgcn_readfirstlane(bal_misc[NW]);   // the sequence holding step s0
-        const long long sb0 = unit_start(b0, 0, n0);
-        const int u = b0 * p.H_kv + static_cast<int>((s0 - sb0) / n0) + it;
-        if (u >= p.B * p.H_kv) break;
-        const int bq = u / p.H_kv, jj = u - bq * p.H_kv;
-        int nb_;
-        const long long ub = unit_start(bq, jj, nb_);                  // the unit's steps [ub, ue)
-        if (ub >= s1) break;
-        const long long ue = ub + nb_;
-        const long long sa = ub > s0 ? ub : s0;                        // this segment: [sa, se)
-        const long long se = ue < s1 ? ue : s1;
-        // workgroup holding step x: the last w with w T / N <= x
-        auto w_of = [&](long long x) { return static_cast<int>(((x + 1) * nwg - 1) / T); };
-        bal_wf = w_of(ub);
-        unit = u;
-        nsp = w_of(ue - 1) - bal_wf + 1;
-        split = wid - bal_wf;
-        L = __builtin_amdgcn_readfirstlane(bal_len[bq]);
-        pos = FUSED ? __builtin_amdgcn_readfirstlane(bal_pos[bq]) : 0;
-        t_begin = static_cast<int>(sa - ub) * kStep;
-        t_end = min(static_cast<int>(se - ub) * kStep, L);
+        if (!bal_segment<kStep, FUSED>(p, wid, it, bal, sg)) break;
+        unit = sg.unit;
+        nsp = sg.nsp;
+        split = sg.split;
+        L = sg.L;
+        pos = sg.pos;
+        t_begin = sg.t_begin;
+        t_end = sg.t_end;
         t_lo = 0;
-        // the unit's first partial is its first workgroup's second segment when
-        // that workgroup's range starts before the unit
-        bal_slot0 = static_cast<long long>(bal_wf) * T / nwg < ub ? 1 : 0;
-        bal_row = static_cast<size_t>(2 * wid + (it == 0 ? 0 : 1)) * G;
         // (the previous segment's output stores, before this one's loads)
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     } else {
@@ -1023,7 +921,7 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
                 } else if (p.merge_cnt != nullptr) {
                     // device-scope stores (written through to memory that
                     // every XCD sees), for the merge below
-                    const size_t pr = BAL ? bal_row + 16 * hb + gh : bh * p.n_splits + split;
+                    const size_t pr = BAL ? sg.row + 16 * hb + gh : bh * p.n_splits + split;
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, A), part_rs,
                                                            static_cast<int>((pr * D + c) * 4), 0, kDevScope);
                     if (ch == 0)
@@ -1048,7 +946,7 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     // out = sum_s w_s acc_s / sum_s w_s l_s, the splits in order, MB of them
     // requested at a time (their max folded into the running one).
     // (Balanced schedule: the unit's partials are those of workgroups wf ..
-    // wf + nsp - 1, each in its first-segment slot except the first one's.)
+    // wf + nsp - 1, each in its first-segment slot except maybe the first's.)
     if (nsp > 1 && p.merge_cnt != nullptr) {
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __syncthreads();
@@ -1069,7 +967,7 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
         };
         merge_split_rows<D>(p, part_rs, ml_rs, rows, nsp, row_of, [&](int gr, int sp) -> size_t {
             if constexpr (BAL)
-                return static_cast<size_t>(2 * (bal_wf + sp) + (sp == 0 ? bal_slot0 : 0)) * G + gr;
+                return bal_part_row(p, sg, gr, sp);
             else
                 return row_of(gr) * p.n_splits + sp;
         });

@@ -67,8 +67,10 @@ __device__ __forceinline__ uint4 codes8_to_bf16(uint2 c) {
     return r;
 }
 
-template <int D, int HB, int MODE, bool FUSED>
-__global__ void __launch_bounds__(kNWq * 64)
+// (one 16-head block: registers held to two waves per SIMD, so that two
+// workgroups share a CU as planned)
+template <int D, int HB, int MODE, bool FUSED, bool BAL>
+__global__ void __launch_bounds__(kNWq * 64) __attribute__((amdgpu_waves_per_eu(HB == 1 ? 2 : 1, 8)))
 decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, float* k_sz, float* v_sz) {
     constexpr bool PAGED = MODE == 3;
     constexpr int NW = kNWq;
@@ -96,25 +98,60 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
     __shared__ __attribute__((aligned(16))) char ksz_lds[NW * TT * 8];
     __shared__ __attribute__((aligned(16))) char vsz_lds[NW * TT * 8];
     __shared__ int tbl_lds[PAGED ? kTblMax : 1];
+    __shared__ int s_last;                 // the in-kernel merge: this workgroup arrived last
+    __shared__ std::conditional_t<BAL, BalLds, char> bal;   // the balanced schedule's lengths and prefix
     static_assert(NW * STAGE >= 2 * NW * 16 * 4 && NW * CSTAGE >= 2 * NW * 16 * 4, "merge area");
+    static_assert(!BAL || PAGED, "the balanced schedule serves paged pools");
+    constexpr int kStep = NW * TT;        // tokens per loop step of the workgroup
 
     const int wid = blockIdx.x < static_cast<unsigned>(p.n_wg) ? static_cast<int>(blockIdx.x) : -1;
     if (wid < 0) return;
-    const int split = wid % p.n_splits;
-    const int unit = wid / p.n_splits;    // b * H_kv + j
+
+    // Balanced schedule (paged pools with ragged lengths; the helpers in
+    // kvc_mfma_common.h): every workgroup reads all lengths, then runs its
+    // split body once per segment of its equal share of all units' steps.
+    if constexpr (BAL) {
+        if (!bal_setup<NW * 64, kStep, FUSED>(p, wid, bal)) return;
+    }
+
+    // (one pass under the split schedule: a trip count the compiler can see
+    // keeps its register allocation that of straight-line code)
+    for (int it = 0; BAL || it < 1; ++it) {
+    // ---- one split (balanced schedule: one segment) of one unit
+    int unit, split, nsp, t_begin, t_end, L, pos;
+    BalSeg sg{};
+    if constexpr (BAL) {
+        if (!bal_segment<kStep, FUSED>(p, wid, it, bal, sg)) break;
+        unit = sg.unit;
+        nsp = sg.nsp;
+        split = sg.split;
+        L = sg.L;
+        pos = sg.pos;
+        t_begin = sg.t_begin;
+        t_end = sg.t_end;
+        // (the previous segment's output stores, before this one's loads)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    } else {
+        split = wid % p.n_splits;
+        unit = wid / p.n_splits;          // b * H_kv + j
+        // (the quantized entry points have no window: the range is [0, L))
+        pos = FUSED ? p.positions[unit / p.H_kv] : 0;
+        L = FUSED ? len_from_position(p, pos) : attended_len(p, unit / p.H_kv);
+        nsp = (L + p.split_tokens - 1) / p.split_tokens;
+        nsp = nsp < 1 ? 1 : nsp;
+        if (split >= nsp) return;
+        t_begin = split * p.split_tokens;
+        t_end = min(L, t_begin + p.split_tokens);
+    }
     const int b = unit / p.H_kv;
     const int j = unit % p.H_kv;
     const int G = p.G;
-    // (the quantized entry points have no window: the range is [0, L))
-    const int pos = FUSED ? p.positions[b] : 0;
-    const int L = FUSED ? len_from_position(p, pos) : attended_len(p, b);
-    int nsp = (L + p.split_tokens - 1) / p.split_tokens;
-    nsp = nsp < 1 ? 1 : nsp;
-    if (split >= nsp) return;
-    const int t_begin = split * p.split_tokens;
-    const int t_end = min(L, t_begin + p.split_tokens);
 
-    const int tid = threadIdx.x;
+    // (the lane index opaque to the compiler inside each segment of the
+    // balanced schedule, so the per-lane offsets derived from it are not
+    // hoisted above the segment loop and kept live through every epilogue)
+    int tid = threadIdx.x;
+    if constexpr (BAL) asm volatile("" : "+v"(tid));
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15;
@@ -142,16 +179,15 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
     // the split read as zeros without a memory access.  Contiguous: rows of
     // this (sequence, KV head); paged: the 16-row group at row0 (a multiple
     // of 16) lies in one block, found in the staged table.
-    auto rows_rsrc = [&](const void* base_ptr, int width, int row0_, int n) -> __amdgpu_buffer_rsrc_t {
+    // (blk_: the group's block id from the staged table, read by the caller)
+    auto rows_rsrc = [&](const void* base_ptr, int width, int row0_, int n, int blk_) -> __amdgpu_buffer_rsrc_t {
         const int row0 = __builtin_amdgcn_readfirstlane(row0_);
         int nvalid = __builtin_amdgcn_readfirstlane(t_end) - row0;
         nvalid = nvalid < 0 ? 0 : (nvalid > n ? n : nvalid);
         size_t first;
         if constexpr (PAGED) {
             const int lb = row0 / p.block_size;
-            int ti = lb - fb;
-            ti = ti < 0 ? 0 : (ti >= kTblMax ? kTblMax - 1 : ti);
-            const int blk = __builtin_amdgcn_readfirstlane(nvalid > 0 ? tbl_lds[ti] : 0);
+            const int blk = __builtin_amdgcn_readfirstlane(nvalid > 0 ? blk_ : 0);
             first = (static_cast<size_t>(blk) * p.H_kv + j) * p.block_size + (row0 - lb * p.block_size);
         } else {
             first = seq_rows + static_cast<size_t>(row0);
@@ -165,7 +201,27 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
     // slot l % CLPR; K rows hold chunk (slot ^ (row % CLPR)) there (so the
     // 16 lanes reading one chunk of 16 rows for the operand spread over the
     // banks), V rows are stored as they come.
-    auto load_tensor = [&](auto is_k, int base) __attribute__((always_inline)) {
+    // Block ids of the two 16-row groups of the tile at row base (paged):
+    // read once per tile, unconditionally (index clamped into the slice;
+    // groups past the split get a zero range whatever they read), and shared
+    // by its code and pair loads.  Read per load instead, each load waited
+    // for its own table read.
+    struct TileBlocks {
+        int g[2];
+    };
+    auto tile_blocks = [&](int base) __attribute__((always_inline)) {
+        TileBlocks tb{};
+        if constexpr (PAGED) {
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                int ti = __builtin_amdgcn_readfirstlane(base + 16 * g) / p.block_size - fb;
+                ti = ti < 0 ? 0 : (ti >= kTblMax ? kTblMax - 1 : ti);
+                tb.g[g] = tbl_lds[ti];
+            }
+        }
+        return tb;
+    };
+    auto load_tensor = [&](auto is_k, int base, const TileBlocks& tb) __attribute__((always_inline)) {
         constexpr bool ISK = decltype(is_k)::value;
         const uint8_t* codes = ISK ? kcodes : vcodes;
         const float* sz = ISK ? k_sz : v_sz;
@@ -176,7 +232,8 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
             const int r = CROWS * i + lane / CLPR;
             const int u = ISK ? ((lane % CLPR) ^ (r % CLPR)) : (lane % CLPR);
             const int g0 = (CROWS * i / 16) * 16;                 // this load's 16-row group
-            const __amdgpu_buffer_rsrc_t rs = rows_rsrc(codes, CROW, base + (PAGED ? g0 : 0), PAGED ? 16 : TT);
+            const __amdgpu_buffer_rsrc_t rs =
+                rows_rsrc(codes, CROW, base + (PAGED ? g0 : 0), PAGED ? 16 : TT, tb.g[g0 / 16]);
             const int row_in = PAGED ? r - g0 : r;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(cbuf + 1024 * i), 16,
                                                      row_in * CROW + 16 * u, 0, 0, kNT);
@@ -186,7 +243,7 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
             // SZROWS rows of 8 bytes are SZROWS / 2 lanes of 16 bytes; the other
             // lanes stay idle, so the load writes only those bytes of LDS (the
             // instruction is still issued once per wave: the wait counts hold)
-            const __amdgpu_buffer_rsrc_t rs = rows_rsrc(sz, 8, base + SZROWS * i, SZROWS);
+            const __amdgpu_buffer_rsrc_t rs = rows_rsrc(sz, 8, base + SZROWS * i, SZROWS, tb.g[PAGED ? i : 0]);
             if (lane < SZROWS / 2)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(sbuf + 8 * SZROWS * i), 16, 16 * lane, 0,
                                                          0, kNT);
@@ -194,13 +251,8 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
     };
     constexpr int kTensorLoads = CLOADS + SZLOADS;
 
-    // pair (step, zero point) of tile row r from a staged pair slice
-    auto pair_at = [&](const char* sbuf, int r) __attribute__((always_inline)) {
-        return *reinterpret_cast<const float2*>(sbuf + 8 * r);
-    };
 
     // Prologue: the table slice (paged), then the query, then the first tile.
-    constexpr int kStep = NW * TT;
     int base = t_begin + wave * TT;
     constexpr int kTblPer = kTblMax / (NW * 64);
     int tv[kTblPer];
@@ -265,8 +317,11 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
         }
         __syncthreads();
     }
-    load_tensor(std::true_type{}, base);
-    load_tensor(std::false_type{}, base);
+    {
+        const TileBlocks tb0 = tile_blocks(base);
+        load_tensor(std::true_type{}, base, tb0);
+        load_tensor(std::false_type{}, base, tb0);
+    }
 
     // Fused step: rotate the queries (bf16, as stored by the append) and the
     // new key (float32), quantize the key and the value.
@@ -403,6 +458,8 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
         char* vb = vb_lds + wave * STAGE;
         const char* ks = ksz_lds + wave * TT * 8;
         const char* vs = vsz_lds + wave * TT * 8;
+        // block ids of the next tile (paged), before the waits below cover them
+        const TileBlocks tb_next = tile_blocks(base + kStep);
 
         // K codes and pairs were issued before this tile's V loads and nothing
         // after them: at most kTensorLoads outstanding
@@ -425,25 +482,57 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
                 if (lane == 0) *reinterpret_cast<float2*>(ksz_lds + wave * TT * 8 + 8 * dp) = kpair;
             }
         }
-        uint4 ka[KB][KK];
+        // The K operand's codes and the K pairs, read as inline assembly for
+        // the reason given at the V^T reads below (through plain loads they
+        // drew a wait for every load in flight, this tile's V included); the
+        // wait above is the one they need, and the one below, tied to every
+        // result, keeps their uses after the data.
+        static_assert(KB == 2 && KB * KK + 4 * KB <= 16, "the wait below names every result");
+        u32x2_t kw[KB * KK], pw2[4 * KB];
+        const unsigned kcb = static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_void_t*)kc));
+        const unsigned ksb = static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_void_t*)ks));
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             const int r = 16 * kb + r16;
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
                 const int c8 = 4 * kk + q4;                         // 8-byte piece of the row
-                const char* a = kc + r * CROW + 16 * ((c8 / 2) ^ (r % CLPR)) + 8 * (c8 % 2);
-                ka[kb][kk] = codes8_to_bf16(*reinterpret_cast<const uint2*>(a));
+                const unsigned a = kcb + r * CROW + 16 * ((c8 / 2) ^ (r % CLPR)) + 8 * (c8 % 2);
+                asm volatile("ds_read_b64 %0, %1" : "=v"(kw[kb * KK + kk]) : "v"(a) : "memory");
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const unsigned a = ksb + 8 * (16 * kb + 4 * q4 + e);
+                asm volatile("ds_read_b64 %0, %1" : "=v"(pw2[4 * kb + e]) : "v"(a) : "memory");
             }
         }
+        if constexpr (KK == 4) {
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(kw[0]), "+v"(kw[1]), "+v"(kw[2]), "+v"(kw[3]), "+v"(kw[4]), "+v"(kw[5]),
+                           "+v"(kw[6]), "+v"(kw[7]), "+v"(pw2[0]), "+v"(pw2[1]), "+v"(pw2[2]), "+v"(pw2[3]),
+                           "+v"(pw2[4]), "+v"(pw2[5]), "+v"(pw2[6]), "+v"(pw2[7])
+                         :
+                         : "memory");
+        } else {
+            static_assert(KK == 2, "head_dim 64 or 128");
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(kw[0]), "+v"(kw[1]), "+v"(kw[2]), "+v"(kw[3]), "+v"(pw2[0]), "+v"(pw2[1]),
+                           "+v"(pw2[2]), "+v"(pw2[3]), "+v"(pw2[4]), "+v"(pw2[5]), "+v"(pw2[6]), "+v"(pw2[7])
+                         :
+                         : "memory");
+        }
+        uint4 ka[KB][KK];
         float2 kp[KB][4];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) kp[kb][e] = pair_at(ks, 16 * kb + 4 * q4 + e);
+            for (int kk = 0; kk < KK; ++kk) ka[kb][kk] = codes8_to_bf16(__builtin_bit_cast(uint2, kw[kb * KK + kk]));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) kp[kb][e] = __builtin_bit_cast(float2, pw2[4 * kb + e]);
+        }
         // the K stage is free once those reads are done: the next tile's K
         __builtin_amdgcn_s_waitcnt(kLgkmZero);
-        load_tensor(std::true_type{}, base + kStep);
+        load_tensor(std::true_type{}, base + kStep, tb_next);
 
         // scores: step * (q . c - zp * sum(q)), in log2 units; past t_end masked
         constexpr int NS = 4 * KB;
@@ -476,12 +565,48 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
                 if (lane == 0) *reinterpret_cast<float2*>(vsz_lds + wave * TT * 8 + 8 * dp) = vpair;
             }
         }
+        // the V pairs and this lane's V code pieces (inline assembly, as the
+        // K reads above; the wait above is the one they need)
+        constexpr int VCR = CSTAGE / 1024;    // 16-byte code pieces per lane
+        static_assert(4 * KB + VCR <= 16, "the wait below names every result");
+        u32x2_t vpw[4 * KB];
+        u32x4_t vcw4[VCR];
+        {
+            const unsigned vsb = static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_void_t*)vs));
+            const unsigned vcb = static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_void_t*)vc));
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const unsigned a = vsb + 8 * (16 * kb + 4 * q4 + e);
+                    asm volatile("ds_read_b64 %0, %1" : "=v"(vpw[4 * kb + e]) : "v"(a) : "memory");
+                }
+#pragma unroll
+            for (int m8 = 0; m8 < VCR; ++m8) {
+                const unsigned a = vcb + 16 * (64 * m8 + lane);
+                asm volatile("ds_read_b128 %0, %1" : "=v"(vcw4[m8]) : "v"(a) : "memory");
+            }
+            if constexpr (VCR == 4) {
+                asm volatile("s_waitcnt lgkmcnt(0)"
+                             : "+v"(vpw[0]), "+v"(vpw[1]), "+v"(vpw[2]), "+v"(vpw[3]), "+v"(vpw[4]), "+v"(vpw[5]),
+                               "+v"(vpw[6]), "+v"(vpw[7]), "+v"(vcw4[0]), "+v"(vcw4[1]), "+v"(vcw4[2]), "+v"(vcw4[3])
+                             :
+                             : "memory");
+            } else {
+                static_assert(VCR == 2, "head_dim 64 or 128");
+                asm volatile("s_waitcnt lgkmcnt(0)"
+                             : "+v"(vpw[0]), "+v"(vpw[1]), "+v"(vpw[2]), "+v"(vpw[3]), "+v"(vpw[4]), "+v"(vpw[5]),
+                               "+v"(vpw[6]), "+v"(vpw[7]), "+v"(vcw4[0]), "+v"(vcw4[1])
+                             :
+                             : "memory");
+            }
+        }
         float vstep[NS], vzp[NS];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float2 sz = pair_at(vs, 16 * kb + 4 * q4 + e);
+                const float2 sz = __builtin_bit_cast(float2, vpw[4 * kb + e]);
                 vstep[4 * kb + e] = sz.x;
                 vzp[4 * kb + e] = sz.y;
             }
@@ -527,41 +652,70 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
         // (chunk u of row r at slot u ^ swz(r)): each lane converts 16-byte
         // pieces of the code tile
 #pragma unroll
-        for (int m8 = 0; m8 < CSTAGE / 1024; ++m8) {
+        for (int m8 = 0; m8 < VCR; ++m8) {
             const int ci = 64 * m8 + lane;
             const int r = ci / CLPR;
             const int u = ci % CLPR;
-            const uint4 c = *reinterpret_cast<const uint4*>(vc + 16 * ci);
+            const uint4 c = __builtin_bit_cast(uint4, vcw4[m8]);
             const uint4 lo = codes8_to_bf16(make_uint2(c.x, c.y));
             const uint4 hi = codes8_to_bf16(make_uint2(c.z, c.w));
             // (d = 128: the eight lanes of one row write the low halves of
             // chunks 0-3 and the high halves of chunks 4-7 first, so every
             // 128-byte bank sweep gets eight distinct 16-byte slots per store)
+            // (inline-assembly stores, for the reason given at the V^T reads
+            // below; those reads' wait also covers these stores)
             const bool hi_first = D == 128 && u >= CLPR / 2;
-            *reinterpret_cast<uint4*>(vb + r * ROWB + 16 * ((2 * u + (hi_first ? 1 : 0)) ^ swz(r))) =
-                select4(hi_first, hi, lo);
-            *reinterpret_cast<uint4*>(vb + r * ROWB + 16 * ((2 * u + (hi_first ? 0 : 1)) ^ swz(r))) =
-                select4(hi_first, lo, hi);
+            const unsigned vbb = static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_void_t*)vb));
+            const unsigned s0 = vbb + r * ROWB + 16 * ((2 * u + (hi_first ? 1 : 0)) ^ swz(r));
+            const unsigned s1 = vbb + r * ROWB + 16 * ((2 * u + (hi_first ? 0 : 1)) ^ swz(r));
+            const u32x4_t w0 = __builtin_bit_cast(u32x4_t, select4(hi_first, hi, lo));
+            const u32x4_t w1 = __builtin_bit_cast(u32x4_t, select4(hi_first, lo, hi));
+            asm volatile("ds_write_b128 %0, %1" : : "v"(s0), "v"(w0) : "memory");
+            asm volatile("ds_write_b128 %0, %1" : : "v"(s1), "v"(w1) : "memory");
         }
         // the V stage is free once its reads are done: the next tile's V
         __builtin_amdgcn_s_waitcnt(kLgkmZero);
-        load_tensor(std::false_type{}, base + kStep);
+        load_tensor(std::false_type{}, base + kStep, tb_next);
 
         // O^T += V^T P^T, V^T read transposed from the bf16 copy (two 16-row
-        // halves per column block, one 16x16x32 product)
+        // halves per column block, one 16x16x32 product).  The reads are
+        // written as inline assembly: issued through the builtin, they drew
+        // compiler waits for every direct-to-LDS load in flight (the next
+        // tiles' codes and pairs, which never touch the bf16 copy), so each
+        // tile's products waited for the next tile's data.  The "memory"
+        // clobbers keep the copy's stores above before the reads; the
+        // explicit wait, tied to every result, keeps the products after the
+        // data has arrived.
+        const unsigned vbw = static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_void_t*)(vb_lds + wave * STAGE)));
+        u32x2_t vt[2 * NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             const int u = 2 * nb + (s16 % 4) / 2;
             const int r0 = tr_row, r1 = tr_row + 16;
-            const char* a0 = vb + r0 * ROWB + 16 * (u ^ swz(r0)) + 8 * (s16 & 1);
-            const char* a1 = vb + r1 * ROWB + 16 * (u ^ swz(r1)) + 8 * (s16 & 1);
-            const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)a0);
-            const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)a1);
-            uint4 va;
-            va.x = __builtin_bit_cast(uint2, lo).x;
-            va.y = __builtin_bit_cast(uint2, lo).y;
-            va.z = __builtin_bit_cast(uint2, hi).x;
-            va.w = __builtin_bit_cast(uint2, hi).y;
+            const unsigned a0 = vbw + r0 * ROWB + 16 * (u ^ swz(r0)) + 8 * (s16 & 1);
+            const unsigned a1 = vbw + r1 * ROWB + 16 * (u ^ swz(r1)) + 8 * (s16 & 1);
+            asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(vt[2 * nb]) : "v"(a0) : "memory");
+            asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(vt[2 * nb + 1]) : "v"(a1) : "memory");
+        }
+        static_assert(2 * NB <= 16, "the wait below names every result");
+        if constexpr (NB == 8) {
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(vt[0]), "+v"(vt[1]), "+v"(vt[2]), "+v"(vt[3]), "+v"(vt[4]), "+v"(vt[5]),
+                           "+v"(vt[6]), "+v"(vt[7]), "+v"(vt[8]), "+v"(vt[9]), "+v"(vt[10]), "+v"(vt[11]),
+                           "+v"(vt[12]), "+v"(vt[13]), "+v"(vt[14]), "+v"(vt[15])
+                         :
+                         : "memory");
+        } else {
+            static_assert(NB == 4, "head_dim 64 or 128");
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(vt[0]), "+v"(vt[1]), "+v"(vt[2]), "+v"(vt[3]), "+v"(vt[4]), "+v"(vt[5]),
+                           "+v"(vt[6]), "+v"(vt[7])
+                         :
+                         : "memory");
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const uint4 va = make_uint4(vt[2 * nb].x, vt[2 * nb].y, vt[2 * nb + 1].x, vt[2 * nb + 1].y);
 #pragma unroll
             for (int hb = 0; hb < HB; ++hb) {
                 o[hb][nb] = mfma16(va, make_uint4(ph[hb][0], ph[hb][1], ph[hb][2], ph[hb][3]), o[hb][nb]);
@@ -687,12 +841,12 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
                 } else if (p.merge_cnt != nullptr) {
                     // device-scope stores (written through to memory that
                     // every XCD sees), for the merge below
-                    const int o = static_cast<int>(((bh * p.n_splits + split) * D + c) * 4);
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, A), part_rs, o, 0, kDevScope);
+                    const size_t pr = BAL ? sg.row + 16 * hb + gh : bh * p.n_splits + split;
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, A), part_rs,
+                                                           static_cast<int>((pr * D + c) * 4), 0, kDevScope);
                     if (ch == 0)
-                        __builtin_amdgcn_raw_buffer_store_b64(
-                            __builtin_bit_cast(u32x2_t, make_float2(M, Ls)), ml_rs,
-                            static_cast<int>((bh * p.n_splits + split) * 8), 0, kDevScope);
+                        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, make_float2(M, Ls)),
+                                                              ml_rs, static_cast<int>(pr * 8), 0, kDevScope);
                 } else {
                     *reinterpret_cast<float4*>(p.ws_part + (bh * p.n_splits + split) * D + c) = A;
                     if (ch == 0) p.ws_ml[bh * p.n_splits + split] = make_float2(M, Ls);
@@ -706,27 +860,38 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
     // the bf16 kernel: device-scope partial rows, a wrapping arrival count,
     // no workgroup waiting for another)
     if (nsp > 1 && p.merge_cnt != nullptr) {
-        __shared__ int s_last;
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __syncthreads();
         if (tid == 0)
             s_last = __builtin_amdgcn_atomic_inc32(p.merge_cnt + unit, static_cast<unsigned>(nsp - 1),
                                                    __ATOMIC_RELAXED, "agent") == static_cast<unsigned>(nsp - 1);
         __syncthreads();
-        if (!s_last) return;
+        if (!s_last) continue;
         const size_t row0 = static_cast<size_t>(b) * p.H_q + static_cast<size_t>(j) * G;
         merge_split_rows<D>(p, part_rs, ml_rs, G, nsp, [&](int gr) -> size_t { return row0 + gr; },
-                            [&](int gr, int s) -> size_t { return (row0 + gr) * p.n_splits + s; });
+                            [&](int gr, int s) -> size_t {
+                                if constexpr (BAL) return bal_part_row(p, sg, gr, s);
+                                else return (row0 + gr) * p.n_splits + s;
+                            });
     }
+    }   // segments
 }
 
 template <int D, int HB, bool FUSED>
 hipError_t launch_dhf(bool paged, const DecodeParams& p, float* k_sz, float* v_sz, hipStream_t stream,
                       const KernelTiming& tm) {
     const dim3 grid(p.n_wg_pad), block(kNWq * 64);
+    if (p.bal) {
+        // balanced schedule: planned for paged pools of at most kBalMaxB sequences
+        if (!paged || p.B > kBalMaxB) return hipErrorInvalidValue;
+        return launch_timed(decode_u8_kernel<D, HB, 3, FUSED, true>, grid, block, stream, tm, p, p.block_table, k_sz,
+                            v_sz);
+    }
     if (paged)
-        return launch_timed(decode_u8_kernel<D, HB, 3, FUSED>, grid, block, stream, tm, p, p.block_table, k_sz, v_sz);
-    return launch_timed(decode_u8_kernel<D, HB, 0, FUSED>, grid, block, stream, tm, p, p.block_table, k_sz, v_sz);
+        return launch_timed(decode_u8_kernel<D, HB, 3, FUSED, false>, grid, block, stream, tm, p, p.block_table, k_sz,
+                            v_sz);
+    return launch_timed(decode_u8_kernel<D, HB, 0, FUSED, false>, grid, block, stream, tm, p, p.block_table, k_sz,
+                        v_sz);
 }
 
 template <int D, int HB>

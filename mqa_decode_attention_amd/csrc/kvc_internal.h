@@ -63,9 +63,11 @@ struct DecodePlan {
 
 // Sequences the balanced schedule handles (their lengths are staged in LDS).
 constexpr int kBalMaxB = 512;
-// Longest range of loop steps one workgroup of the balanced schedule takes
-// (its paged segments then span at most kTblMax - 2 blocks of 16 tokens).
-constexpr int kBalMaxSteps = 240;
+// Most tokens one workgroup of the balanced schedule takes (its paged
+// segments then span at most 960 + 2 blocks of 16 tokens, inside the kTblMax
+// entries of the staged table): 240 loop steps of the bf16 kernel, 120 of the
+// quantized one.
+constexpr int kBalMaxTokens = 15360;
 
 // Largest split count the merge step supports (partials live in LDS).
 constexpr int kMaxSplits = 256;

@@ -160,5 +160,149 @@ __device__ __forceinline__ void merge_split_rows(const DecodeParams& p, __amdgpu
     }
 }
 
+// ---------------------------------------------------------------------------
+// Balanced schedule of the streaming kernels (paged pools with ragged
+// lengths).  Sequence b holds n_b = ceil(L_b / STEP) loop steps (at least
+// one, so that an empty sequence still writes its zero rows) for each of its
+// H_kv units (b, j); the units' steps, in unit order, form one list of T
+// steps, and workgroup w of N takes steps [w T / N, (w + 1) T / N): every
+// workgroup streams the same number of steps (within one) whatever the
+// lengths, and all of them start at once.  N is the planned count, or T when
+// there are fewer steps, so that every range holds a step.  A range crosses
+// units, so a workgroup runs its split body once per segment (a unit's steps
+// inside its range); a unit several workgroups share is merged by the last of
+// them to finish, from partial rows each writes to one of two slots of its
+// own: slot 0 for its first segment, slot 1 for its last.
+// ---------------------------------------------------------------------------
+
+// LDS of the schedule: per-sequence step prefix, lengths, new-token slots.
+struct BalLds {
+    int pre[kBalMaxB + 1];
+    int len[kBalMaxB];
+    int pos[kBalMaxB];
+    int misc[8];          // per-wave totals; [7]: the sequence holding the first step
+};
+
+// Every thread of the workgroup (NT of them, NT * PER >= kBalMaxB) reads PER
+// lengths, then the workgroup scans them.  Returns false when this workgroup
+// takes no steps (it may return at once).  FUSED: lengths from the new
+// tokens' positions (their slots kept for the append).
+template <int NT, int STEP, bool FUSED>
+__device__ __forceinline__ bool bal_setup(const DecodeParams& p, int wid, BalLds& s) {
+    constexpr int PER = kBalMaxB / NT;
+    static_assert(PER * NT == kBalMaxB && NT / 64 <= 7, "schedule layout");
+    const int tid = threadIdx.x;
+    int nst[PER];
+    int sum = 0;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int bb = tid * PER + k;
+        int n = 0;
+        if (bb < p.B) {
+            const int ps = FUSED ? p.positions[bb] : 0;
+            const int Lb = FUSED ? len_from_position(p, ps) : attended_len(p, bb);
+            s.len[bb] = Lb;
+            if constexpr (FUSED) s.pos[bb] = ps;
+            n = Lb > 0 ? (Lb + STEP - 1) / STEP : 1;
+        }
+        nst[k] = n;
+        sum += n;
+    }
+    // exclusive prefix over the threads: inside each wave, then over the
+    // waves' totals
+    int inc = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(inc, o, 64);
+        if ((tid & 63) >= o) inc += v;
+    }
+    if ((tid & 63) == 63) s.misc[tid >> 6] = inc;
+    __syncthreads();
+    int ex = inc - sum, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+        const int v = s.misc[w];
+        ex += w < (tid >> 6) ? v : 0;
+        tot += v;
+    }
+    tot = __builtin_amdgcn_readfirstlane(tot);
+    const long long T = static_cast<long long>(tot) * p.H_kv;
+    const int nwg = T < p.n_wg ? static_cast<int>(T) : p.n_wg;
+    const long long s0 = static_cast<long long>(wid) * T / nwg;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int bb = tid * PER + k;
+        if (bb < p.B) {
+            s.pre[bb] = ex;
+            if (static_cast<long long>(ex) * p.H_kv <= s0 && s0 < static_cast<long long>(ex + nst[k]) * p.H_kv)
+                s.misc[7] = bb;
+        }
+        ex += nst[k];
+    }
+    if (tid == 0) s.pre[p.B] = tot;
+    __syncthreads();
+    return wid < nwg;
+}
+
+// One segment of the schedule.
+struct BalSeg {
+    int unit;             // b * H_kv + j
+    int b, nsp, split;    // the unit's workgroups, this one's index among them
+    int L, pos;           // the sequence's attended length, new-token slot (FUSED)
+    int t_begin, t_end;   // tokens of the segment
+    int wf, slot0;        // the unit's first workgroup, the slot of its partial
+    size_t row;           // first partial row of this segment (rows of G)
+};
+
+// Segment it of workgroup wid (false past its range).  Everything is derived
+// again from LDS and the iteration count, so no state of the schedule stays
+// live through the split body between segments.
+template <int STEP, bool FUSED>
+__device__ __forceinline__ bool bal_segment(const DecodeParams& p, int wid, int it, const BalLds& s, BalSeg& sg) {
+    const int tot = __builtin_amdgcn_readfirstlane(s.pre[p.B]);
+    const long long T = static_cast<long long>(tot) * p.H_kv;
+    const int nwg = T < p.n_wg ? static_cast<int>(T) : p.n_wg;
+    const long long s0 = static_cast<long long>(wid) * T / nwg;
+    const long long s1 = static_cast<long long>(wid + 1) * T / nwg;
+    auto unit_start = [&](int b_, int j_, int& n_) -> long long {   // first step of unit (b_, j_); n_: its steps
+        const int pre = __builtin_amdgcn_readfirstlane(s.pre[b_]);
+        n_ = __builtin_amdgcn_readfirstlane(s.pre[b_ + 1]) - pre;
+        return static_cast<long long>(p.H_kv) * pre + static_cast<long long>(j_) * n_;
+    };
+    int n0;
+    const int b0 = __builtin_amdgcn_readfirstlane(s.misc[7]);
+    const long long sb0 = unit_start(b0, 0, n0);
+    const int u = b0 * p.H_kv + static_cast<int>((s0 - sb0) / n0) + it;
+    if (u >= p.B * p.H_kv) return false;
+    const int bq = u / p.H_kv, jj = u - bq * p.H_kv;
+    int nb;
+    const long long ub = unit_start(bq, jj, nb);                   // the unit's steps [ub, ue)
+    if (ub >= s1) return false;
+    const long long ue = ub + nb;
+    const long long sa = ub > s0 ? ub : s0;                        // this segment: [sa, se)
+    const long long se = ue < s1 ? ue : s1;
+    // workgroup holding step x: the last w with w T / N <= x
+    auto w_of = [&](long long x) { return static_cast<int>(((x + 1) * nwg - 1) / T); };
+    sg.wf = w_of(ub);
+    sg.unit = u;
+    sg.b = bq;
+    sg.nsp = w_of(ue - 1) - sg.wf + 1;
+    sg.split = wid - sg.wf;
+    sg.L = __builtin_amdgcn_readfirstlane(s.len[bq]);
+    sg.pos = FUSED ? __builtin_amdgcn_readfirstlane(s.pos[bq]) : 0;
+    sg.t_begin = static_cast<int>(sa - ub) * STEP;
+    sg.t_end = min(static_cast<int>(se - ub) * STEP, sg.L);
+    // the unit's first partial is its first workgroup's second segment when
+    // that workgroup's range starts before the unit
+    sg.slot0 = static_cast<long long>(sg.wf) * T / nwg < ub ? 1 : 0;
+    sg.row = static_cast<size_t>(2 * wid + (it == 0 ? 0 : 1)) * p.G;
+    return true;
+}
+
+// Partial row of output row gr of split sp of the segment's unit.
+__device__ __forceinline__ size_t bal_part_row(const DecodeParams& p, const BalSeg& sg, int gr, int sp) {
+    return static_cast<size_t>(2 * (sg.wf + sp) + (sp == 0 ? sg.slot0 : 0)) * p.G + gr;
+}
+
 }  // namespace mfma
 }  // namespace kvc

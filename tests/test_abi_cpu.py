@@ -403,12 +403,12 @@ def test_step_u8_host_checks(lib):
 
 
 def test_balanced_schedule_choice(lib):
-    """The balanced schedule serves ragged paged pools (bf16, head_dim <= 128,
-    the library's split choice, at most 512 sequences); its workspace: the
-    64 KiB of counters, then two partial rows per query head of a group for
-    each of its workgroups (one round: 768 for the paged kernel's three per
-    CU at one 16-head block, 256 at two), or the split plan's size when that
-    is larger."""
+    """The balanced schedule serves ragged paged pools (bf16 or uint8 cache,
+    head_dim <= 128, the library's split choice, at most 512 sequences); its
+    workspace: the 64 KiB of counters, then two partial rows per query head of
+    a group for each of its workgroups (one round: 768 for the bf16 paged
+    kernel's three per CU at one 16-head block, 256 at two; 512 for the
+    quantized kernel's two), or the split plan's size when that is larger."""
     bal = lib.kvc_decode_balanced
     wsb = lib.kvc_decode_workspace_bytes
     zb = lib.kvc_workspace_zeroed_bytes()
@@ -419,7 +419,8 @@ def test_balanced_schedule_choice(lib):
     assert bal(BF16, 32, 32, 8, 256, 16385, pool, 0) == 0       # head_dim 256
     assert bal(BF16, 32, 32, 8, 128, 16385, pool, 768) == 0     # explicit splits
     assert bal(F32, 32, 32, 8, 128, 16385, pool, 0) == 0        # the vector kernel
-    assert bal(U8, 32, 32, 8, 128, 16385, pool, 0) == 0         # the quantized kernel
+    assert bal(U8, 32, 32, 8, 128, 16385, pool, 0) == 1         # the quantized kernel too
+    assert bal(U8, 16, 32, 8, 128, 8193, 0, 0) == 0             # (contiguous: splits)
     assert bal(BF16, 513, 32, 8, 128, 16385, pool, 0) == 0      # more sequences than staged
     assert bal(BF16, 16, 32, 8, 128, 8193, 0, 0) == 0           # contiguous caches: splits
     assert bal(BF16, 64, 32, 1, 128, 4097, 0, 0) == 0
@@ -431,3 +432,4 @@ def test_balanced_schedule_choice(lib):
     assert wsb(BF16, 32, 64, 2, 128, 16385, 32 * 8700, 0) >= zb + 256 * 2 * 32 * (8 + 128 * 4)
     # a short call still needs its partial rows (units shared by workgroups)
     assert wsb(BF16, 3, 32, 8, 128, 200, 3 * 16 * 5, 0) == zb + 768 * 2 * 4 * (8 + 128 * 4)
+    assert wsb(U8, 3, 32, 8, 128, 200, 3 * 16 * 5, 0) == zb + 512 * 2 * 4 * (8 + 128 * 4)

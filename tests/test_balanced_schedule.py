@@ -23,7 +23,7 @@ import random
 
 import pytest
 
-K_BAL_MAX_STEPS = 240      # kvc_internal.h: kBalMaxSteps
+K_BAL_MAX_TOKENS = 15360   # kvc_internal.h: kBalMaxTokens
 
 
 def steps_of(L, step):
@@ -32,9 +32,10 @@ def steps_of(L, step):
 
 def plan_workgroups(units, max_len, step, slots):
     """The plan's workgroup count: one round, more if a range would exceed
-    kBalMaxSteps steps (bound from the longest possible sequence)."""
+    kBalMaxTokens tokens (bound from the longest possible sequence)."""
     bound = units * ((max(max_len, 1) + step - 1) // step)
-    return max(slots, (bound + K_BAL_MAX_STEPS - 1) // K_BAL_MAX_STEPS)
+    max_steps = K_BAL_MAX_TOKENS // step
+    return max(slots, (bound + max_steps - 1) // max_steps)
 
 
 def schedule(lens, H_kv, N, step):
@@ -99,7 +100,7 @@ def check(lens, H_kv, N, step):
     for w, segs in enumerate(sched):
         assert len(segs) == 0 or segs[0]["sa"] == w * T // N
         for k, sg in enumerate(segs):
-            assert sg["se"] - sg["sa"] <= K_BAL_MAX_STEPS or N * K_BAL_MAX_STEPS < T
+            assert (sg["se"] - sg["sa"]) * step <= K_BAL_MAX_TOKENS or N * (K_BAL_MAX_TOKENS // step) < T
             for x in range(sg["sa"], sg["se"]):
                 assert x not in covered
                 covered[x] = sg["unit"]
@@ -138,7 +139,7 @@ def test_random_ragged_shapes(seed):
     rng = random.Random(seed)
     B = rng.choice([1, 2, 3, 7, 16, 32, 64, 100])
     H_kv = rng.choice([1, 2, 8])
-    step = 64
+    step = rng.choice([64, 128])          # the bf16 and the quantized kernels' loop steps
     max_len = rng.choice([1, 63, 64, 65, 500, 4096, 16384])
     lens = [rng.choice([0, 1, rng.randint(0, max_len), max_len, (rng.randint(0, max_len) // 64) * 64])
             for _ in range(B)]
@@ -160,18 +161,23 @@ def test_edge_shapes(lens, H_kv, N):
 
 
 def test_workload_shapes():
-    """The ragged workloads the schedule serves: 64 sequences of 512..4096
-    tokens under one KV head on 256 workgroups, and 32 sequences of
-    1024..16384 tokens under 8 KV heads on 768."""
+    """The ragged paged workload the schedule serves: 32 sequences of
+    1024..16384 tokens under 8 KV heads, on 768 workgroups of 64-token steps
+    (bf16) and 512 of 128-token steps (uint8); and a 64-sequence MQA batch."""
     rng = random.Random(7)
+    lens = [rng.randint(1024, 16384) + 1 for _ in range(32)]
+    check(lens, 8, 768, 64)
+    check(lens, 8, 512, 128)
     check([rng.randint(512, 4096) + 1 for _ in range(64)], 1, 256, 64)
-    check([rng.randint(1024, 16384) + 1 for _ in range(32)], 8, 768, 64)
 
 
 def test_plan_bounds_range_length():
-    """The planned workgroup count keeps every range within kBalMaxSteps
-    steps whatever the lengths (at most max_len each)."""
-    for units, max_len in ((256, 16384), (8, 131072), (512, 1 << 20), (1, 64)):
-        N = plan_workgroups(units, max_len, 64, 256)
-        T = units * steps_of(max_len, 64)
-        assert -(-T // N) <= K_BAL_MAX_STEPS
+    """The planned workgroup count keeps every range within kBalMaxTokens
+    tokens (960 blocks of 16, inside the staged table of 1024 entries)
+    whatever the lengths (at most max_len each), for both kernels' steps."""
+    for step in (64, 128):
+        for units, max_len in ((256, 16384), (8, 131072), (512, 1 << 20), (1, 64)):
+            N = plan_workgroups(units, max_len, step, 256)
+            T = units * steps_of(max_len, step)
+            assert -(-T // N) * step <= K_BAL_MAX_TOKENS
+            assert K_BAL_MAX_TOKENS // 16 + 2 <= 1024

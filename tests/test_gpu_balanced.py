@@ -135,3 +135,68 @@ def test_fused_step(name, style):
     assert np.array_equal(bits(q_rot), np.ascontiguousarray(q2).view(np.uint8)), "rotated q differs"
     compare_out(out, oracle_decode(x, k2, v2, q2), "bf16", f"step {name} {style}")
     assert np.array_equal(bits(out), bits(out_a)), "step output differs from append + decode"
+
+
+# ---- the quantized (uint8) cache under the same schedule (128-token steps)
+
+U8_CASES = {
+    "g4": W.Workload("bal_u8_g4", 51, B=12, H_q=32, H_kv=8, d=128, dtype="bf16", cached_lo=1, cached_hi=3000,
+                     layout="paged", block_size=16),
+    "g32_d64": W.Workload("bal_u8_g32", 52, B=7, H_q=32, H_kv=1, d=64, dtype="bf16", cached_lo=0, cached_hi=2500,
+                          layout="paged", block_size=32),
+}
+
+
+@pytest.mark.parametrize("name", sorted(U8_CASES))
+def test_u8_ragged_pool(name):
+    from test_gpu_quant import QStep, check_append
+    import oracle.kvc_quant_oracle as QO
+    w = U8_CASES[name]
+    x = W.draw(w)
+    qc = W.draw_quantized(x)
+    s = QStep(x, qc)
+    pool = int(s.kc.shape[0]) * w.block_size
+    assert kvc.balanced(torch.uint8, w.B, w.H_q, w.H_kv, w.d, s.max_len, pool_tokens=pool), \
+        "expected the balanced schedule for these sizes"
+    say(f"[balanced u8 {name}] B={w.B} G={w.H_q // w.H_kv} d={w.d} lens={x.seq_lens.tolist()[:12]}")
+    s.append()
+    torch.cuda.synchronize()
+    kc, ks, vc, vs, q2 = check_append(s, x, qc)
+    tbl = x.block_table.numpy()
+    full = x.seq_lens.numpy()
+    short = np.minimum(np.array([0, 1, 127, 128, 129, 2000, 16, 17, 3, 1000, 256, 257][:w.B], np.int32), full)
+    for lens in (full, short):
+        t = torch.from_numpy(np.ascontiguousarray(lens)).cuda()
+        out = kvc.decode_attn_paged_u8(s.q, s.kc, s.ks, s.vc, s.vs, s.tbl, t, s.max_len)
+        again = kvc.decode_attn_paged_u8(s.q, s.kc, s.ks, s.vc, s.vs, s.tbl, t, s.max_len)
+        torch.cuda.synchronize()
+        ref = QO.decode_attention_paged_u8(q2, kc, ks, vc, vs, tbl, w.block_size, lens, "bf16")
+        compare_out(out, ref, "bf16", f"u8 {name} lens={lens.tolist()[:6]}")
+        assert torch.equal(out.view(torch.int16), again.view(torch.int16)), "run-to-run difference"
+
+
+@pytest.mark.parametrize("name", sorted(U8_CASES))
+def test_u8_fused_step(name):
+    """kvc_decode_step_u8 under the balanced schedule: bitwise equal to
+    kvc_append_u8 then kvc_decode_attn_paged_u8 (same schedule), the append
+    bit-exact against the oracle, attention within tolerance."""
+    from test_gpu_quant import QStep, check_append, _run_step_u8
+    import oracle.kvc_quant_oracle as QO
+    w = U8_CASES[name]
+    x = W.draw(w)
+    qc = W.draw_quantized(x)
+    say(f"[balanced u8 step {name}] lens={x.seq_lens.tolist()[:12]}")
+    ref = QStep(x, qc)
+    ref.append()
+    torch.cuda.synchronize()
+    kc2, ks2, vc2, vs2, q2 = check_append(ref, x, qc)
+    kc, ks, vc, vs, q_rot, out = _run_step_u8(QStep(x, qc))
+    out_a = ref.decode()
+    torch.cuda.synchronize()
+    for what, got, exp in (("K codes", kc, ref.kc), ("K pairs", ks, ref.ks), ("V codes", vc, ref.vc),
+                           ("V pairs", vs, ref.vs), ("rotated q", q_rot, ref.q)):
+        assert np.array_equal(bits(got), bits(exp)), f"{what} differ from the append"
+    assert np.array_equal(bits(out), bits(out_a)), "output differs from append + decode"
+    oref = QO.decode_attention_paged_u8(q2, kc2, ks2, vc2, vs2, x.block_table.numpy(), w.block_size,
+                                        x.seq_lens.numpy(), "bf16")
+    compare_out(out, oref, "bf16", f"u8 step {name}")
