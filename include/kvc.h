@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 12
+#define KVC_ABI_VERSION 13
 
 typedef enum kvc_status {
     KVC_OK = 0,
@@ -195,7 +195,8 @@ size_t kvc_workspace_zeroed_bytes(void);
  * choice over a contiguous bf16 cache, the last split of a sequence also
  * takes a remainder shorter than one loop step of the kernel (64 tokens up
  * to head_dim 128, else 128): 8193 tokens in splits of 4096 are two splits,
- * of 4096 and 4097 tokens.
+ * of 4096 and 4097 tokens.  Under the compacted schedule (kvc_decode_compact)
+ * this is the shortest split length the kernel may pick.
  */
 int kvc_decode_split_tokens(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_len,
                             long long pool_tokens, int split_tokens);
@@ -232,6 +233,30 @@ int kvc_decode_merge_launch(kvc_dtype dtype, int B, int H_q, int H_kv, int d, in
  */
 int kvc_decode_balanced(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_len,
                         long long pool_tokens, int split_tokens);
+
+/*
+ * Whether a single-token decode with these sizes (arguments as for
+ * kvc_decode_workspace_bytes) runs the compacted schedule: 1 if it does, 0 if
+ * not, -1 for invalid sizes.
+ *
+ * The compacted schedule (bf16 matrix-core kernel, contiguous cache, at most
+ * 256 sequences, B * H_kv at most half the workgroups the device holds at
+ * once, the library's split choice) replaces split plans that would take
+ * several rounds of workgroups.  The host knows only max_seq_len, so such a
+ * plan, sized for the longest sequence, leaves many splits past the end of
+ * shorter ones.  Instead every workgroup reads the B lengths and picks the
+ * split length itself: the shortest multiple of the kernel's loop step, at
+ * least kvc_decode_split_tokens, whose splits of all (sequence, KV head)
+ * units fit in one round of workgroups; the splits that exist take the first
+ * workgroup indices, and the merge kernel, which derives the same length from
+ * the same lengths, combines them (the split and merge of "Arsitektur
+ * Inferensi LLM", tveniu.com, section 5, with the units of "Grouped-query
+ * attention: berbagi KV head di antara grup query", nalar.dev, section
+ * "Jumlah head menentukan batas grup").  The workspace is that of the
+ * shortest split length.
+ */
+int kvc_decode_compact(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_len,
+                       long long pool_tokens, int split_tokens);
 
 /*
  * kvc_decode_attn - attention of the new token over a contiguous cache.

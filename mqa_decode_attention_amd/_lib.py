@@ -29,6 +29,7 @@ SIGNATURES = {
     "kvc_workspace_zeroed_bytes": (c_size_t, []),
     "kvc_decode_merge_launch": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_longlong, c_int]),
     "kvc_decode_balanced": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_longlong, c_int]),
+    "kvc_decode_compact": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_longlong, c_int]),
     "kvc_decode_split_tokens": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_longlong, c_int]),
     "kvc_decode_attn": (c_int, [c_int, c_int, c_int, c_int, c_int,
                                 c_void_p, c_void_p, c_void_p, c_int,
@@ -114,7 +115,7 @@ SIGNATURES = {
                                     c_size_t, c_void_p]),
 }
 
-ABI_VERSION = 12
+ABI_VERSION = 13
 
 _lib = None
 

@@ -138,6 +138,18 @@ def balanced(dtype: torch.dtype, B: int, H_q: int, H_kv: int, d: int, max_seq_le
     return bool(n)
 
 
+def compact(dtype: torch.dtype, B: int, H_q: int, H_kv: int, d: int, max_seq_len: int,
+            split_tokens: int = 0, pool_tokens: int = 0) -> bool:
+    """kvc_decode_compact: True when a single-token decode with these sizes
+    runs the compacted schedule (split length picked on the device from the
+    lengths, the existing splits numbered first, merged in the same launch)."""
+    lib = _lib.load()
+    n = lib.kvc_decode_compact(_cache_code(dtype), B, H_q, H_kv, d, max_seq_len, pool_tokens, split_tokens)
+    if n < 0:
+        raise KvcError(2, lib.kvc_last_error().decode() or "invalid sizes")
+    return bool(n)
+
+
 def workspace_zeroed_bytes() -> int:
     """kvc_workspace_zeroed_bytes: the prefix of a caller's `workspace` tensor
     that must be zero before its first use (every completed call leaves it so)."""

@@ -191,11 +191,44 @@ bool plan_decode(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_l
     pl.split_tokens = static_cast<int>(std::min<long long>(ts, 0x7FFFFFFF));
     pl.split_tail = tail;
     pl.n_splits = static_cast<int>(n_of(ts));
+    pl.one_round = units * pl.n_splits <= slots;
+    // Compacted schedule for contiguous caches whose split plan takes several
+    // rounds: the kernel picks the split length from the lengths (the
+    // shortest that fits every split in one round of `slots` workgroups);
+    // the host plans the shortest length it may pick, which sizes the
+    // workspace, and the merge kernel derives the kernel's length again.
+    // (Ragged 64-sequence MQA: the split plan's 384-token splits 25.7 us +
+    // a 4 us merge launch, step 29.6 us; 640-token splits with the existing
+    // splits numbered first 24.0 us, step 27.0.  Merged in the streaming
+    // kernel instead, as one-round plans are, its 32-row groups took 28.4 us,
+    // step 29.1: the last split of a unit merges up to 32 rows x 11 splits
+    // alone, where the merge kernel spreads them over a wave per row.)
+    if (allow_bal && split_tokens == 0 && pl.mfma && !u8 && pool_tokens == 0 && qlen <= 1 && !pl.one_round &&
+        B <= kCmpMaxB && units * 2 <= slots) {
+        // (no remainder joins a sequence's last split here: in one round the
+        // longest split sets the time, and a remainder of up to a step made
+        // some splits 703 tokens long instead of 640 - 25.3 against 24.0 us)
+        const long long least = (pl.heads_per_wg > 16 ? 12LL : 32LL) * pl.heads_per_wg;
+        tail = 0;
+        ts = std::max<long long>(tile, (least + tile - 1) / tile * tile);
+        while (n_of(ts) > kMaxSplits) ts += tile;
+        pl.split_tokens = static_cast<int>(ts);
+        pl.split_tail = 0;
+        pl.n_splits = static_cast<int>(n_of(ts));
+        pl.compact = true;
+        pl.cmp_slots = static_cast<int>(std::min<long long>(slots, 0x7FFFFFFF));
+        pl.cmp_step = tile;
+        pl.cmp_tmax = static_cast<int>(std::min<long long>((L + tile - 1LL) / tile * tile, 0x7FFFFFC0));
+    }
     if (pl.n_splits > 1) {
         const size_t bh = static_cast<size_t>(B) * H_q * std::max(qlen, 1);   // output rows
         pl.ws_ml = kWsCounterBytes;
         pl.ws_part = align_up(pl.ws_ml + bh * pl.n_splits * sizeof(float2), 256);
         pl.ws_bytes = align_up(pl.ws_part + bh * pl.n_splits * d * sizeof(float), 256);
+        if (pl.compact) {
+            pl.ws_nsp = pl.ws_bytes;
+            pl.ws_bytes = align_up(pl.ws_nsp + units * sizeof(int), 256);
+        }
         // The bf16 matrix-core kernel merges the splits of a unit in its last
         // split to finish when all its workgroups fit in one round: each
         // split then waits for its partial rows to be written and for its
@@ -505,6 +538,20 @@ int kvc_decode_balanced(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int ma
     return pl.bal ? 1 : 0;
 }
 
+int kvc_decode_compact(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_len,
+                       long long pool_tokens, int split_tokens) {
+    if (check_heads(dtype == KVC_U8 ? KVC_BF16 : dtype, B, H_q, H_kv, d) != KVC_OK || max_seq_len < 0 ||
+        split_tokens < 0 || pool_tokens < 0)
+        return -1;
+    kvc::DecodePlan pl;
+    const char* why = nullptr;
+    if (!kvc::plan_decode(dtype, B, H_q, H_kv, d, max_seq_len, pool_tokens, split_tokens, &pl, &why)) {
+        fail(KVC_ERR_UNSUPPORTED, "%s", why);
+        return -1;
+    }
+    return pl.compact ? 1 : 0;
+}
+
 namespace {
 // plan of a multi-token call (sizes as kvc_decode_attn_multi's); false if invalid
 bool plan_multi(kvc_dtype dtype, int B, int n, int H_q, int H_kv, int d, int max_seq_len, int window,
@@ -516,7 +563,7 @@ bool plan_multi(kvc_dtype dtype, int B, int n, int H_q, int H_kv, int d, int max
     }
     const char* why = nullptr;
     const int span = kvc_window_span(max_seq_len, window > 0 ? window + n - 1 : 0, 0, 0);
-    if (!kvc::plan_decode(dtype, B, H_q, H_kv, d, span, pool_tokens, split_tokens, pl, &why, n)) {
+    if (!kvc::plan_decode(dtype, B, H_q, H_kv, d, span, pool_tokens, split_tokens, pl, &why, n, false)) {
         fail(KVC_ERR_UNSUPPORTED, "%s", why);
         return false;
     }
@@ -620,7 +667,7 @@ kvc_status decode_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const
     // the balanced schedule serves one new token over a full paged cache of
     // blocks of a multiple of 16 tokens; other calls take the split plan,
     // whose workspace the balanced plan's size covers
-    if (pl.bal && (multi || window != 0 || ring || !paged || block_size % 16 != 0) &&
+    if (((pl.bal && (multi || window != 0 || ring || !paged || block_size % 16 != 0)) || (pl.compact && multi)) &&
         !kvc::plan_decode(dtype, B, H_q, H_kv, d, span, pool_tokens, split_tokens, &pl, &why, qlen, false))
         return fail(KVC_ERR_UNSUPPORTED, "%s", why);
     if (u8 && paged) {
@@ -655,6 +702,11 @@ kvc_status decode_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const
     const bool merge_in_kernel = pl.merge_in_kernel || pl.bal;
     p.merge_cnt = merge_in_kernel ? reinterpret_cast<unsigned*>(ws) : nullptr;
     p.bal = pl.bal ? 1 : 0;
+    p.compact = pl.compact ? 1 : 0;
+    p.ws_nsp = pl.compact && pl.ws_bytes ? reinterpret_cast<int*>(ws + pl.ws_nsp) : nullptr;
+    p.cmp_slots = pl.cmp_slots;
+    p.cmp_step = pl.cmp_step;
+    p.cmp_tmax = pl.cmp_tmax;
     p.B = B; p.H_q = H_q; p.H_kv = H_kv; p.G = H_q / H_kv; p.n_chunks = pl.n_chunks;
     p.T_max = T_max; p.block_size = block_size; p.max_blocks_per_seq = max_blocks_per_seq;
     p.num_blocks = num_blocks;

@@ -416,7 +416,10 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(const DecodeParams p)
     // (over all n_splits slots of the workspace; those past the sequence's
     // splits are masked once it is), so the two round trips overlap.
     fetch(0, p.n_splits);
-    const int nsp = split_count(p, token_range(p, attended_len(p, b)));
+    // (under the compacted schedule the streaming kernel picked the split
+    // length on the device and recorded each unit's split count)
+    const int nsp = p.compact ? p.ws_nsp[static_cast<long long>(b) * p.H_kv + (bh % p.H_q) / (p.H_q / p.H_kv)]
+                              : split_count(p, token_range(p, attended_len(p, b)));
     if (nsp <= 1) return;                        // written directly by the split kernel
 #pragma unroll
     for (int u = 0; u < KU; ++u) {

@@ -116,6 +116,7 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     static_assert(!(MQ && FUSED), "several new tokens: the append runs first");
     static_assert(!(BAL && MQ), "the balanced schedule serves single-token steps");
     constexpr int kStep = NW * TT;        // tokens per loop step of the workgroup
+    constexpr bool CMP = MODE == 0 && !MQ && !BAL;   // compacted numbering available (p.compact)
 
     const int tid0 = threadIdx.x;
 
@@ -154,6 +155,24 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
         t_lo = 0;
         // (the previous segment's output stores, before this one's loads)
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    } else if (CMP && p.compact) {
+        // Compacted schedule (contiguous cache, plans of several rounds; the
+        // helper in kvc_mfma_common.h): the split length comes from the
+        // lengths themselves, and the splits that exist take the first
+        // workgroup indices.
+        CmpSeg c;
+        if (!cmp_locate<FUSED>(p, wid, c)) return;
+        unit = c.unit;
+        split = c.split;
+        nsp = c.nsp;
+        L = c.L;
+        pos = c.pos;
+        if (split == 0 && tid0 == 0 && p.ws_nsp != nullptr) p.ws_nsp[unit] = nsp;   // for the merge kernel
+        const TokenRange tr = token_range(p, L);
+        t_begin = tr.org + split * c.T;
+        const int e = tr.org + (split + 1) * c.T;
+        t_end = (split == nsp - 1 || e > tr.hi) ? tr.hi : e;
+        t_lo = tr.lo;
     } else {
         // Workgroups in launch order: the splits of one (sequence, KV head)
         // are neighbours, and the hardware deals consecutive workgroups to the

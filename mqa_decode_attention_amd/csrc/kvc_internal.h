@@ -53,6 +53,14 @@ struct DecodePlan {
     size_t ws_part;
     size_t ws_bytes;    // 0 when n_splits == 1
     bool merge_in_kernel;   // the streaming kernel merges the splits (no merge launch)
+    bool one_round;     // every workgroup of the split plan fits on the device at once
+    // Compacted schedule (bf16 matrix-core kernel, contiguous cache, one new
+    // token, library splits, plans of several rounds): the kernel picks the
+    // split length, at least split_tokens, from the lengths so that the
+    // splits fit in cmp_slots workgroups, and merges them itself.
+    bool compact;
+    int cmp_slots, cmp_step, cmp_tmax;
+    size_t ws_nsp;      // byte offset of its per-unit split counts in the workspace
     // Balanced schedule of the bf16 matrix-core kernel: bal_wg workgroups share
     // the steps of all units equally, whatever the lengths (ws_ml / ws_part
     // then hold 2 * G partial rows per workgroup; ws_bytes also covers the
@@ -60,6 +68,10 @@ struct DecodePlan {
     bool bal;
     int bal_wg;
 };
+
+// Sequences the compacted numbering handles (64 lengths per lane load).
+constexpr int kCmpChunks = 4;
+constexpr int kCmpMaxB = 64 * kCmpChunks;
 
 // Sequences the balanced schedule handles (their lengths are staged in LDS).
 constexpr int kBalMaxB = 512;
@@ -105,6 +117,9 @@ struct DecodeParams {
     int split_tail;              // the last split also takes up to this many tokens (a short remainder)
     int n_wg, n_wg_pad;          // logical workgroups, padded to a multiple of 8
     int bal;                     // balanced schedule (n_wg workgroups share all units' steps)
+    int compact;                 // compacted schedule: split length from the lengths, existing splits first
+    int* ws_nsp;                 // [B * H_kv] its split count per unit, for the merge kernel
+    int cmp_slots, cmp_step, cmp_tmax;   // its workgroup budget, loop step, longest split
     float scale_log2;            // softmax scale * log2(e)
 
     // Set for kvc_decode_step: lengths come from positions (L_b = positions[b] + 1)
@@ -178,6 +193,150 @@ __device__ __forceinline__ int split_count(const DecodeParams& p, const TokenRan
 __device__ __forceinline__ int split_end(const DecodeParams& p, const TokenRange& r, int s, int nsp) {
     const int e = r.org + (s + 1) * p.split_tokens;
     return (s == nsp - 1 || e > r.hi) ? r.hi : e;
+}
+
+// ---------------------------------------------------------------------------
+// Compacted schedule of the bf16 streaming kernel over a contiguous cache
+// (plans that would take several rounds of workgroups).  The host knows only
+// the longest sequence, so its split plan leaves many splits past the end of
+// shorter ones, and a split that exists competes for a slot with those that
+// do not.  Here every workgroup reads all lengths (up to kCmpMaxB, 64 per
+// load, requested together) and picks the split length T itself: the
+// shortest multiple of the loop step, at least the host's split_tokens, whose
+// splits of all units (H_kv * nsp_b per sequence) fit in cmp_slots
+// workgroups - one round, so every split starts at once.  The splits that
+// exist, counted in unit order, then take workgroup indices 0, 1, ...; the
+// rest exit at once.  Every workgroup computes the same T and counts from
+// the same lengths; the first split of each unit records the unit's split
+// count in the workspace (ws_nsp) for the merge kernel.
+// ---------------------------------------------------------------------------
+
+struct CmpSeg {
+    int unit, split, nsp;   // b * H_kv + j, this split, the unit's splits
+    int L, pos;             // attended length, new-token slot (FUSED)
+    int T;                  // split length
+};
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// Splits of a sequence of L tokens at split length T (split_count's rule).
+__device__ __forceinline__ int cmp_splits(const DecodeParams& p, int L, int T) {
+    const TokenRange r = token_range(p, L);
+    const int n = (r.hi - r.org - p.split_tail + T - 1) / T;
+    return n < 1 ? 1 : n;
+}
+
+// Lengths (and, FUSED, new-token slots) of sequences 64 k + lane.
+template <bool FUSED>
+__device__ __forceinline__ void cmp_lengths(const DecodeParams& p, int (&lens)[kCmpChunks],
+                                            int (&poss)[kCmpChunks]) {
+    const int ln = threadIdx.x & 63;
+#pragma unroll
+    for (int k = 0; k < kCmpChunks; ++k) {
+        const int bb = 64 * k + ln;
+        poss[k] = 0;
+        lens[k] = 0;
+        if (bb < p.B) {
+            if constexpr (FUSED) {
+                poss[k] = p.positions[bb];
+                lens[k] = len_from_position(p, poss[k]);
+            } else {
+                lens[k] = attended_len(p, bb);
+            }
+        }
+    }
+}
+
+// The unit and split of workgroup wid (false: it takes none).  The split
+// length T: a first estimate from the tokens the splits cover, over the slots
+// less half a split per unit (a sequence's last split is on average half
+// full); then, while the units' splits (counted by the same prefix sum over
+// the lanes that locates wid) exceed the slots, longer: twice in proportion
+// to the count's excess, then in proportion to the splits beyond each unit's
+// first (those that shrink with T), which always ends within the passes
+// (modelled on the host over random ragged shapes: never over the slots, at
+// most ~8 % longer than the shortest length that fits; mostly one pass).  T
+// never passes cmp_tmax, one split per sequence.
+template <bool FUSED>
+__device__ __forceinline__ bool cmp_locate(const DecodeParams& p, int wid, CmpSeg& c) {
+    const int ln = threadIdx.x & 63;
+    int lens[kCmpChunks], poss[kCmpChunks];
+    cmp_lengths<FUSED>(p, lens, poss);
+    // (the estimate in float32: only a starting point, which the count below
+    // checks; the butterfly sum has a fixed order, so every workgroup gets
+    // the same value)
+    float span = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kCmpChunks; ++k) {
+        if (64 * k + ln < p.B) {
+            const TokenRange r = token_range(p, lens[k]);
+            span += static_cast<float>(r.hi - r.org);
+        }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) span += __shfl_xor(span, o, 64);
+    const int step = p.cmp_step;
+    const int units = p.B * p.H_kv;
+    const float room = static_cast<float>(max(1, p.cmp_slots - units / 2));
+    const float steps = ceilf(span * static_cast<float>(p.H_kv) / (room * static_cast<float>(step)));
+    int T = steps >= static_cast<float>(p.cmp_tmax / step) ? p.cmp_tmax : static_cast<int>(steps) * step;
+    T = __builtin_amdgcn_readfirstlane(max(T, p.split_tokens));
+    // per chunk: the lane's splits (H_kv * nsp_b), their inclusive prefix over
+    // the lanes, and the chunk's total
+    int n[kCmpChunks], inc[kCmpChunks], tot[kCmpChunks];
+    for (int pass = 0;; ++pass) {
+        int cnt = 0;
+#pragma unroll
+        for (int k = 0; k < kCmpChunks; ++k) {
+            n[k] = inc[k] = tot[k] = 0;
+            if (64 * k >= p.B) continue;
+            n[k] = 64 * k + ln < p.B ? cmp_splits(p, lens[k], T) * p.H_kv : 0;
+            inc[k] = n[k];
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int v = __shfl_up(inc[k], o, 64);
+                if (ln >= o) inc[k] += v;
+            }
+            tot[k] = __shfl(inc[k], 63, 64);
+            cnt += tot[k];
+        }
+        if (cnt <= p.cmp_slots || T >= p.cmp_tmax || pass == 5) break;
+        const long long free_slots = max(1, p.cmp_slots - units);
+        const long long grown = pass < 2 ? static_cast<long long>(T) * cnt / p.cmp_slots
+                                         : (static_cast<long long>(T) * (cnt - units) + free_slots - 1) / free_slots;
+        T = static_cast<int>(min<long long>(max<long long>(T + step, (grown + step - 1) / step * step), p.cmp_tmax));
+        T = __builtin_amdgcn_readfirstlane(T);
+    }
+    int before = 0;                       // splits of the sequences of earlier chunks
+    bool found = false;
+    c = CmpSeg{};
+    c.T = T;
+#pragma unroll
+    for (int k = 0; k < kCmpChunks; ++k) {
+        if (!found && wid < before + tot[k]) {
+            // the first lane whose prefix passes wid
+            const int lk = __builtin_ctzll(__ballot(before + inc[k] > wid));
+            const int nk = __shfl(n[k], lk, 64);
+            const int r = wid - before - (__shfl(inc[k], lk, 64) - nk);   // index among the sequence's splits
+            c.L = __shfl(lens[k], lk, 64);
+            c.pos = __shfl(poss[k], lk, 64);
+            c.nsp = nk / p.H_kv;
+            c.unit = (64 * k + lk) * p.H_kv + r / c.nsp;
+            c.split = r % c.nsp;
+            found = true;
+        }
+        before += tot[k];
+    }
+    c.unit = __builtin_amdgcn_readfirstlane(c.unit);
+    c.split = __builtin_amdgcn_readfirstlane(c.split);
+    c.nsp = __builtin_amdgcn_readfirstlane(c.nsp);
+    c.L = __builtin_amdgcn_readfirstlane(c.L);
+    c.pos = __builtin_amdgcn_readfirstlane(c.pos);
+    return found;
 }
 
 // Returns false (and leaves *plan untouched) when the sizes cannot be planned.
