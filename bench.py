@@ -61,6 +61,12 @@ def attended(seq_lens, window):
     return [min(int(L), window) if window > 0 else int(L) for L in seq_lens]
 
 
+def kvc_q8_dtype(kind):
+    """The torch dtype naming an 8-bit cache kind in the library's plan queries."""
+    import torch
+    return {"u8": torch.uint8, "fp8_e4m3": torch.float8_e4m3fn, "fp8_e5m2": torch.float8_e5m2}[kind]
+
+
 def kv_read_bytes_u8(seq_lens, H_kv, d):
     """The same for the quantized cache: d codes plus an 8-byte (step, zero
     point) pair per token, KV head and tensor."""
@@ -80,9 +86,10 @@ def parse():
                     help="sliding window of W tokens (kvc_decode_step_window over the full cache; 0 = none)")
     ap.add_argument("--ring", action="store_true",
                     help="with --window: the cache is a ring of W slots holding each sequence's window")
-    ap.add_argument("--kv-cache", choices=("native", "u8"), default="native",
-                    help="native: the workload's dtype (kvc_decode_step); u8: the quantized cache "
-                         "(kvc_append_u8 + kvc_decode_attn[_paged]_u8 on codes drawn by workloads.draw_quantized)")
+    ap.add_argument("--kv-cache", choices=("native", "u8", "fp8_e4m3", "fp8_e5m2"), default="native",
+                    help="native: the workload's dtype (kvc_decode_step); u8: the uint8 cache (kvc_decode_step_u8 "
+                         "on codes drawn by workloads.draw_quantized); fp8_e4m3 / fp8_e5m2: the FP8 cache "
+                         "(kvc_decode_step_fp8 on codes drawn by workloads.draw_fp8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
@@ -197,7 +204,8 @@ def oracle_tasks(x, kind: str, window: int = 0, qc=None):
     n_new = w.new_tokens
     q, kn, vn = _np_store(x.q, dt), _np_store(x.k_new, dt), _np_store(x.v_new, dt)
     tbl = x.block_table.numpy() if w.paged else None
-    if kind == "u8":
+    if kind != "native":
+        import oracle.kvc_fp8_oracle as FO
         import oracle.kvc_quant_oracle as QO
         arrs = [a.numpy() for a in (qc.k_codes, qc.k_sz, qc.v_codes, qc.v_sz)]
     else:
@@ -219,6 +227,12 @@ def oracle_tasks(x, kind: str, window: int = 0, qc=None):
             g = QO.append_contiguous_u8(*g, c, kn[b:b + 1, j:j + 1], vn[b:b + 1, j:j + 1], cos, sin, dt,
                                         q=q[b:b + 1, hs])
             QO.decode_attention_u8(g[4], *g[:4], [L], dt)
+        elif kind != "native":
+            fmt = kind[4:]
+            g = [rows(a, b, j, L) for a in arrs]
+            g = FO.append_contiguous_fp8(*g, c, kn[b:b + 1, j:j + 1], vn[b:b + 1, j:j + 1], cos, sin, dt, fmt,
+                                         q=q[b:b + 1, hs])
+            FO.decode_attention_fp8(g[4], *g[:4], [L], dt, fmt)
         elif n_new > 1:
             import oracle.kvc_multi_oracle as MO
             k2, v2, q2 = MO.append_multi(rows(kc, b, j, L), rows(vc, b, j, L), c, kn[b:b + 1, :, j:j + 1],
@@ -234,9 +248,9 @@ def oracle_tasks(x, kind: str, window: int = 0, qc=None):
                 O.decode_attention(q2, k2, v2, [L], dt)
 
     lens = (cached + n_new).tolist()
-    if kind == "u8":
+    if kind != "native":
         nbytes = kv_read_bytes_u8(lens, H_kv, w.d)
-        what = "uint8 cache, append + attention"
+        what = ("uint8" if kind == "u8" else kind.upper().replace("_", " ")) + " cache, append + attention"
     else:
         span = window + n_new - 1 if window else 0
         nbytes = kv_read_bytes(attended(lens, span), H_kv, w.d, e)
@@ -480,7 +494,8 @@ def main():
         return
     w = W.WORKLOADS[args.workload]
     x = W.draw(w)
-    u8 = args.kv_cache == "u8"
+    u8 = args.kv_cache != "native"         # an 8-bit cache: uint8 or FP8 codes with per-vector pairs
+    fmt = {"u8": None, "fp8_e4m3": "e4m3", "fp8_e5m2": "e5m2"}.get(args.kv_cache)
     win = args.window
     multi = w.new_tokens > 1          # several new tokens per sequence: append_multi + decode_attn_multi
     if multi and (u8 or args.ring):
@@ -491,11 +506,11 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     e = 2 if w.dtype == "bf16" else 4
-    qc = W.draw_quantized(x) if u8 else None
+    qc = (W.draw_quantized(x) if fmt is None else W.draw_fp8(x, fmt)) if u8 else None
     # the host oracle first: its worker processes are forked before this
     # process touches the GPU
     cpu = None if args.no_cpu_baseline else \
-        cpu_baselines(oracle_tasks(x, "u8" if u8 else "native", win, qc), w.name, w.B)
+        cpu_baselines(oracle_tasks(x, args.kv_cache, win, qc), w.name, w.B)
 
     import mqa_decode_attention_amd as kvc
 
@@ -547,7 +562,7 @@ def main():
     if u8:
         prepared = [kvc.prepare_decode_step_u8(q, ks[r][0], ks[r][1], vs[r][0], vs[r][1], pos, kn, vn, cos, sin,
                                                max_len, block_table=tbl, q_rot_out=q_rot, out=out,
-                                               split_tokens=args.split_tokens)
+                                               split_tokens=args.split_tokens, fmt=fmt)
                     for r in range(R)]
     elif not (multi or win):
         prepared = [kvc.prepare_decode_step(q, ks[r], vs[r], pos, kn, vn, cos, sin, max_len, block_table=tbl,
@@ -627,18 +642,22 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": ("synthetic (seeded uint8 codes and per-vector (step, zero point) pairs of N(0,1)-like "
+                 "vectors, NaN pairs past each sequence's length)") if args.kv_cache == "u8" else
+                (f"synthetic (seeded FP8 {fmt.upper()} codes and per-vector (scale, 0) pairs of N(0,1)-like "
                  "vectors, NaN pairs past each sequence's length)") if u8 else
                 "synthetic (seeded N(0,1), NaN past each sequence's length)",
-        "config": {"workload": w.name + ("_u8" if u8 else "") + (f"_window{win}" if win else "") +
+        "config": {"workload": w.name + (f"_{args.kv_cache}" if u8 else "") + (f"_window{win}" if win else "") +
                                ("_ring" if args.ring else ""), "batch": w.B, "H_q": w.H_q, "H_kv": w.H_kv,
                    "head_dim": w.d, "cached_tokens": [w.cached_lo, w.cached_hi], "layout": w.layout,
-                   "kv_cache": "uint8 codes + float32 (step, zero point) per vector" if u8 else w.dtype,
+                   "kv_cache": ("uint8 codes + float32 (step, zero point) per vector" if fmt is None else
+                                f"FP8 {fmt.upper()} codes + float32 (scale, 0) per vector") if u8 else w.dtype,
                    "kv_bytes_per_step": kv_bytes, "cache_replicas": R,
                    "window": win, "ring": bool(args.ring), "new_tokens": w.new_tokens,
                    "split_tokens": (kvc.multi_split_tokens(x.q.dtype, w.B, w.new_tokens, w.H_q, w.H_kv, w.d, max_len,
                                                            win, args.split_tokens, pool_tokens=pool_tokens)
                                     if multi else
-                                    kvc.split_tokens(torch.uint8 if u8 else x.q.dtype, w.B, w.H_q, w.H_kv, w.d,
+                                    kvc.split_tokens(kvc_q8_dtype(args.kv_cache) if u8 else x.q.dtype, w.B, w.H_q,
+                                                     w.H_kv, w.d,
                                                      kvc.window_span(max_len, win, args.ring, win if args.ring else 0),
                                                      args.split_tokens, pool_tokens=pool_tokens)),
                    "split_choice": "explicit" if args.split_tokens else "library"},
@@ -651,8 +670,9 @@ def main():
         "hbm_pct_step": round(100 * value / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": ("decode_u8_kernel (streaming pass over the codes with the fused append; a one-round "
-                                "plan merges its splits in the same launch, else a small merge kernel follows)") if u8 else
+                     "kernel": ("decode_u8_kernel (streaming pass over the 8-bit codes with the fused append; a "
+                                "one-round plan merges its splits in the same launch, else a small merge kernel "
+                                "follows)") if u8 else
                                ("decode_mfma_kernel, multi-token rows (one pass over the cache for all new tokens' "
                                 "queries; the append and the split merge are separate small kernels)") if multi else
                                ("decode_mfma_kernel (streaming pass with the fused append; a one-round plan merges "

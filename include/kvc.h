@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 13
+#define KVC_ABI_VERSION 14
 
 typedef enum kvc_status {
     KVC_OK = 0,
@@ -74,9 +74,17 @@ typedef enum kvc_status {
 } kvc_status;
 
 /* KVC_U8 names the quantized cache of kvc_append_u8 / kvc_decode_attn*_u8
- * (uint8 codes, bf16 queries and outputs); only kvc_decode_workspace_bytes and
- * kvc_decode_split_tokens take it as a dtype. */
-typedef enum kvc_dtype { KVC_F32 = 0, KVC_BF16 = 1, KVC_U8 = 2 } kvc_dtype;
+ * (uint8 codes, bf16 queries and outputs), KVC_FP8_E4M3 / KVC_FP8_E5M2 the FP8
+ * caches of the *_fp8 calls; the sizing and plan queries
+ * (kvc_decode_workspace_bytes, kvc_decode_split_tokens, ...) take them as a
+ * dtype, and the *_fp8 calls as their format argument. */
+typedef enum kvc_dtype {
+    KVC_F32 = 0,
+    KVC_BF16 = 1,
+    KVC_U8 = 2,
+    KVC_FP8_E4M3 = 3,
+    KVC_FP8_E5M2 = 4
+} kvc_dtype;
 
 /* How RoPE pairs the head dimension: (2i, 2i+1), or (i, i + d/2). */
 typedef enum kvc_rope_style { KVC_ROPE_INTERLEAVED = 0, KVC_ROPE_HALF = 1 } kvc_rope_style;
@@ -558,6 +566,58 @@ kvc_status kvc_decode_step_u8(int B, int H_q, int H_kv, int d, const void* q, vo
                               const void* k_new, const void* v_new, const float* rope_cos, const float* rope_sin,
                               int rope_rows, int rope_style, int max_seq_len, float scale, void* out,
                               int split_tokens, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * FP8 KV cache: one byte per cached element, the FP8 / INT8 quantized cache of
+ * "Arsitektur Inferensi LLM" (tveniu.com), section 2 (one byte per element of
+ * a GQA-8 cache), whose section 8 starts an engine with an "fp8" KV-cache
+ * dtype; "KV Cache 최적화 심층 분석" (youngju.dev) turns on fp8_e5m2 in its vLLM
+ * commands.  The pages leave the format open; these calls read it as the OCP
+ * 8-bit floating-point formats:
+ *   KVC_FP8_E4M3  sign, 4 exponent bits (bias 7), 3 mantissa bits, largest
+ *                 finite 448, no infinities; each cached vector gets the
+ *                 float32 scale (largest magnitude of its d elements) / 448
+ *                 (1 when that is 0) and stores the codes of x / scale;
+ *   KVC_FP8_E5M2  sign, 5 exponent bits (bias 15), 2 mantissa bits, largest
+ *                 finite 57344; the direct cast (scale 1).
+ * Codes round to nearest, ties to even, from float32 (one rounding for the
+ * division, one for the code), saturating at the largest finite value.  The
+ * layout is the uint8 cache's: codes uint8 [B, H_kv, T_max, d] (or pools
+ * [num_blocks, H_kv, block_size, d]) and float32 pairs [..., 2] = (scale, 0),
+ * so a cached value reads back as decode(code) * scale.  The key is rotated
+ * as in kvc_append (float32) and quantized from that float32 result, the value
+ * from its dtype converted to float32.  Attention, sizes, rules and errors are
+ * those of the *_u8 calls with the same arguments (format first); the sizing
+ * queries take the format as their dtype.  A format other than the two is
+ * KVC_ERR_UNSUPPORTED.
+ */
+kvc_status kvc_append_fp8(kvc_dtype format, kvc_dtype dtype, int B, int H_q, int H_kv, int d,
+                          void* k_codes, float* k_sz, void* v_codes, float* v_sz, int T_max,
+                          const int32_t* block_table, int block_size, int max_blocks_per_seq,
+                          int num_blocks, const int32_t* positions,
+                          const void* k_new, const void* v_new, void* q_inout,
+                          const float* rope_cos, const float* rope_sin, int rope_rows,
+                          int rope_style, void* stream);
+
+kvc_status kvc_decode_attn_fp8(kvc_dtype format, int B, int H_q, int H_kv, int d, const void* q,
+                               const void* k_codes, const float* k_sz, const void* v_codes, const float* v_sz,
+                               int T_max, const int32_t* seq_lens, int max_seq_len, float scale, void* out,
+                               int split_tokens, void* workspace, size_t workspace_bytes, void* stream);
+
+kvc_status kvc_decode_attn_paged_fp8(kvc_dtype format, int B, int H_q, int H_kv, int d, const void* q,
+                                     const void* k_codes, const float* k_sz, const void* v_codes,
+                                     const float* v_sz, int num_blocks, int block_size, const int32_t* block_table,
+                                     int max_blocks_per_seq, const int32_t* seq_lens, int max_seq_len, float scale,
+                                     void* out, int split_tokens, void* workspace, size_t workspace_bytes,
+                                     void* stream);
+
+kvc_status kvc_decode_step_fp8(kvc_dtype format, int B, int H_q, int H_kv, int d, const void* q, void* q_rot_out,
+                               void* k_codes, float* k_sz, void* v_codes, float* v_sz, int T_max,
+                               const int32_t* block_table, int block_size, int max_blocks_per_seq, int num_blocks,
+                               const int32_t* positions, const void* k_new, const void* v_new,
+                               const float* rope_cos, const float* rope_sin, int rope_rows, int rope_style,
+                               int max_seq_len, float scale, void* out, int split_tokens, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 /*
  * Latent cache (multi-head latent attention), following the

@@ -35,7 +35,8 @@ and for a latent cache (multi-head latent attention, one [c_kv | k_rope] row per
 """
 from .api import (KVC_BF16, KVC_F32, KVC_U8, KvcError, PreparedCall, append, append_multi,  # noqa: F401
                   append_ring, append_u8, balanced, compact, decode_attn, decode_attn_multi, decode_attn_paged,
-                  decode_attn_paged_u8, decode_attn_u8, decode_attn_window, decode_step, decode_step_noalloc, decode_step_u8,
+                  decode_attn_paged_u8, decode_attn_u8, FP8_FORMATS, append_fp8, decode_attn_fp8,
+                  decode_attn_paged_fp8, decode_step_fp8, prepare_decode_step_fp8, decode_attn_window, decode_step, decode_step_noalloc, decode_step_u8,
                   decode_step_window, merge_launch, multi_split_tokens, multi_workspace_bytes, noalloc_max_bytes,
                   prepare_decode_step, prepare_decode_step_u8, profile_next_decode, split_tokens, window_span,
                   workspace_bytes, workspace_zeroed_bytes)

@@ -101,6 +101,24 @@ SIGNATURES = {
                                    c_void_p, c_void_p, c_int, c_void_p, c_int, c_int, c_int, c_void_p,
                                    c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_float,
                                    c_void_p, c_int, c_void_p, c_size_t, c_void_p]),
+    "kvc_append_fp8": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int,
+                               c_void_p, c_void_p, c_void_p, c_void_p, c_int,
+                               c_void_p, c_int, c_int, c_int, c_void_p,
+                               c_void_p, c_void_p, c_void_p,
+                               c_void_p, c_void_p, c_int, c_int, c_void_p]),
+    "kvc_decode_attn_fp8": (c_int, [c_int, c_int, c_int, c_int, c_int, c_void_p,
+                                    c_void_p, c_void_p, c_void_p, c_void_p, c_int,
+                                    c_void_p, c_int, c_float, c_void_p,
+                                    c_int, c_void_p, c_size_t, c_void_p]),
+    "kvc_decode_attn_paged_fp8": (c_int, [c_int, c_int, c_int, c_int, c_int, c_void_p,
+                                          c_void_p, c_void_p, c_void_p, c_void_p, c_int,
+                                          c_int, c_void_p, c_int,
+                                          c_void_p, c_int, c_float, c_void_p,
+                                          c_int, c_void_p, c_size_t, c_void_p]),
+    "kvc_decode_step_fp8": (c_int, [c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
+                                    c_void_p, c_void_p, c_int, c_void_p, c_int, c_int, c_int, c_void_p,
+                                    c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_float,
+                                    c_void_p, c_int, c_void_p, c_size_t, c_void_p]),
     "kvc_append_mla": (c_int, [c_int, c_int, c_int, c_int, c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p]),
     "kvc_decode_mla_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int]),
     "kvc_decode_mla_split_tokens": (c_int, [c_int, c_int, c_int, c_int, c_int]),
@@ -115,7 +133,7 @@ SIGNATURES = {
                                     c_size_t, c_void_p]),
 }
 
-ABI_VERSION = 13
+ABI_VERSION = 14
 
 _lib = None
 

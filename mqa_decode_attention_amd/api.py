@@ -7,13 +7,17 @@ kernels; nothing here touches tensor values.
 """
 from __future__ import annotations
 
+import functools
+
 from typing import Dict, Optional, Tuple
 
 import torch
 
 from . import _lib
 
-KVC_F32, KVC_BF16, KVC_U8 = 0, 1, 2
+KVC_F32, KVC_BF16, KVC_U8, KVC_FP8_E4M3, KVC_FP8_E5M2 = 0, 1, 2, 3, 4
+# FP8 cache formats of the *_fp8 calls
+FP8_FORMATS = {"e4m3": KVC_FP8_E4M3, "e5m2": KVC_FP8_E5M2}
 ROPE_STYLES = {"interleaved": 0, "half": 1}
 
 
@@ -97,10 +101,29 @@ def append(k_cache: torch.Tensor, v_cache: torch.Tensor, positions: torch.Tensor
 
 
 def _cache_code(dtype) -> int:
-    """dtype of the cache: torch.bfloat16, torch.float32, or torch.uint8 (quantized)."""
+    """dtype of the cache: torch.bfloat16, torch.float32, torch.uint8 (uint8
+    codes), or torch.float8_e4m3fn / torch.float8_e5m2 (FP8 codes)."""
     if dtype == torch.uint8:
         return KVC_U8
+    if dtype == torch.float8_e4m3fn:
+        return KVC_FP8_E4M3
+    if dtype == torch.float8_e5m2:
+        return KVC_FP8_E5M2
     return KVC_BF16 if dtype == torch.bfloat16 else KVC_F32
+
+
+def _q8_fn(lib, name: str, fmt: Optional[str]):
+    """The uint8 call kvc_<name>_u8, or (fmt "e4m3" / "e5m2") kvc_<name>_fp8
+    with its format argument bound."""
+    if fmt is None:
+        return getattr(lib, f"kvc_{name}_u8")
+    if fmt not in FP8_FORMATS:
+        raise ValueError(f"FP8 format must be one of {sorted(FP8_FORMATS)}, got {fmt!r}")
+    return functools.partial(getattr(lib, f"kvc_{name}_fp8"), FP8_FORMATS[fmt])
+
+
+def _q8_dtype(fmt: Optional[str]):
+    return torch.uint8 if fmt is None else {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}[fmt]
 
 
 def workspace_bytes(dtype: torch.dtype, B: int, H_q: int, H_kv: int, d: int, max_seq_len: int,
@@ -590,9 +613,10 @@ def append_u8(k_codes: torch.Tensor, k_sz: torch.Tensor, v_codes: torch.Tensor, 
               positions: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, rope_cos: torch.Tensor,
               rope_sin: torch.Tensor, q: Optional[torch.Tensor] = None,
               block_table: Optional[torch.Tensor] = None, rope_style: str = "interleaved",
-              stream=None) -> None:
-    """kvc_append_u8: quantize the rotated new key and the new value into the
-    code / pair arrays; rotate q (bf16 or f32, as k_new) in place if given."""
+              stream=None, fmt: Optional[str] = None) -> None:
+    """kvc_append_u8 (fmt None) or kvc_append_fp8 (fmt "e4m3" / "e5m2"):
+    quantize the rotated new key and the new value into the code / pair
+    arrays; rotate q (bf16 or f32, as k_new) in place if given."""
     lib = _lib.load()
     dt = _dtype_code(k_new)
     B, H_kv, d = k_new.shape
@@ -608,7 +632,7 @@ def append_u8(k_codes: torch.Tensor, k_sz: torch.Tensor, v_codes: torch.Tensor, 
         T_max = k_codes.shape[2]
         tbl, block_size, mb, num_blocks = None, 0, 0, 0
         lead = (B, H_kv, T_max)
-    _check(lib.kvc_append_u8(
+    _check(_q8_fn(lib, "append", fmt)(
         dt, B, H_q, H_kv, d,
         _dev(k_codes, "k_codes", torch.uint8, lead + (d,)), _dev(k_sz, "k_sz", torch.float32, lead + (2,)),
         _dev(v_codes, "v_codes", torch.uint8, lead + (d,)), _dev(v_sz, "v_sz", torch.float32, lead + (2,)), T_max,
@@ -623,21 +647,23 @@ def append_u8(k_codes: torch.Tensor, k_sz: torch.Tensor, v_codes: torch.Tensor, 
 def decode_attn_u8(q: torch.Tensor, k_codes: torch.Tensor, k_sz: torch.Tensor, v_codes: torch.Tensor,
                    v_sz: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
                    out: Optional[torch.Tensor] = None, scale: Optional[float] = None, split_tokens: int = 0,
-                   workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """kvc_decode_attn_u8 over a quantized contiguous cache [B, H_kv, T_max, d];
-    q and out bf16 [B, H_q, d]."""
+                   workspace: Optional[torch.Tensor] = None, stream=None,
+                   fmt: Optional[str] = None) -> torch.Tensor:
+    """kvc_decode_attn_u8 (fmt None) or kvc_decode_attn_fp8 (fmt "e4m3" /
+    "e5m2") over an 8-bit contiguous cache [B, H_kv, T_max, d]; q and out bf16
+    [B, H_q, d]."""
     lib = _lib.load()
     B, H_q, d = q.shape
     out = torch.empty_like(q) if out is None else out
     _, H_kv, T_max, _ = k_codes.shape
     st = _stream(q.device, stream)
-    need = workspace_bytes(torch.uint8, B, H_q, H_kv, d, max_seq_len, split_tokens)
+    need = workspace_bytes(_q8_dtype(fmt), B, H_q, H_kv, d, max_seq_len, split_tokens)
     if workspace is not None:
         ws, wsn = _dev(workspace, "workspace", torch.uint8), workspace.numel()
     else:
         ws, wsn = _workspace(q.device, st, need)
     lead = (B, H_kv, T_max)
-    _check(lib.kvc_decode_attn_u8(
+    _check(_q8_fn(lib, "decode_attn", fmt)(
         B, H_q, H_kv, d, _dev(q, "q", torch.bfloat16),
         _dev(k_codes, "k_codes", torch.uint8, lead + (d,)), _dev(k_sz, "k_sz", torch.float32, lead + (2,)),
         _dev(v_codes, "v_codes", torch.uint8, lead + (d,)), _dev(v_sz, "v_sz", torch.float32, lead + (2,)), T_max,
@@ -650,21 +676,22 @@ def decode_attn_paged_u8(q: torch.Tensor, k_codes: torch.Tensor, k_sz: torch.Ten
                          v_sz: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
                          out: Optional[torch.Tensor] = None, scale: Optional[float] = None,
                          split_tokens: int = 0, workspace: Optional[torch.Tensor] = None,
-                         stream=None) -> torch.Tensor:
-    """kvc_decode_attn_paged_u8 over quantized pools [num_blocks, H_kv, block_size, d]."""
+                         stream=None, fmt: Optional[str] = None) -> torch.Tensor:
+    """kvc_decode_attn_paged_u8 (fmt None) or kvc_decode_attn_paged_fp8 over
+    8-bit pools [num_blocks, H_kv, block_size, d]."""
     lib = _lib.load()
     B, H_q, d = q.shape
     out = torch.empty_like(q) if out is None else out
     num_blocks, H_kv, block_size, _ = k_codes.shape
     st = _stream(q.device, stream)
-    need = workspace_bytes(torch.uint8, B, H_q, H_kv, d, max_seq_len, split_tokens,
+    need = workspace_bytes(_q8_dtype(fmt), B, H_q, H_kv, d, max_seq_len, split_tokens,
                            pool_tokens=num_blocks * block_size)
     if workspace is not None:
         ws, wsn = _dev(workspace, "workspace", torch.uint8), workspace.numel()
     else:
         ws, wsn = _workspace(q.device, st, need)
     lead = (num_blocks, H_kv, block_size)
-    _check(lib.kvc_decode_attn_paged_u8(
+    _check(_q8_fn(lib, "decode_attn_paged", fmt)(
         B, H_q, H_kv, d, _dev(q, "q", torch.bfloat16),
         _dev(k_codes, "k_codes", torch.uint8, lead + (d,)), _dev(k_sz, "k_sz", torch.float32, lead + (2,)),
         _dev(v_codes, "v_codes", torch.uint8, lead + (d,)), _dev(v_sz, "v_sz", torch.float32, lead + (2,)),
@@ -681,13 +708,14 @@ def decode_step_u8(q: torch.Tensor, k_codes: torch.Tensor, k_sz: torch.Tensor, v
                    block_table: Optional[torch.Tensor] = None, rope_style: str = "interleaved",
                    q_rot_out: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                    scale: Optional[float] = None, split_tokens: int = 0,
-                   workspace: Optional[torch.Tensor] = None, stream=None):
-    """kvc_decode_step_u8: the decode step over a quantized cache (contiguous
-    codes [B, H_kv, T_max, d] or pools [num_blocks, H_kv, block_size, d] with a
-    block table), append and attention in one launch; returns (out, q_rot_out)."""
+                   workspace: Optional[torch.Tensor] = None, stream=None, fmt: Optional[str] = None):
+    """kvc_decode_step_u8 (fmt None) or kvc_decode_step_fp8 (fmt "e4m3" /
+    "e5m2"): the decode step over an 8-bit cache (contiguous codes
+    [B, H_kv, T_max, d] or pools [num_blocks, H_kv, block_size, d] with a block
+    table), append and attention in one launch; returns (out, q_rot_out)."""
     fn, args, out, q_rot_out = _step_u8_call(q, k_codes, k_sz, v_codes, v_sz, positions, k_new, v_new, rope_cos,
                                              rope_sin, max_seq_len, block_table, rope_style, q_rot_out, out, scale,
-                                             split_tokens, workspace, stream)
+                                             split_tokens, workspace, stream, fmt)
     _check(fn(*args))
     return out, q_rot_out
 
@@ -698,11 +726,12 @@ def prepare_decode_step_u8(q: torch.Tensor, k_codes: torch.Tensor, k_sz: torch.T
                            block_table: Optional[torch.Tensor] = None, rope_style: str = "interleaved",
                            q_rot_out: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                            scale: Optional[float] = None, split_tokens: int = 0,
-                           workspace: Optional[torch.Tensor] = None, stream=None) -> PreparedCall:
+                           workspace: Optional[torch.Tensor] = None, stream=None,
+                           fmt: Optional[str] = None) -> PreparedCall:
     """decode_step_u8 checked once, launched per call (as prepare_decode_step)."""
     fn, args, out, q_rot_out = _step_u8_call(q, k_codes, k_sz, v_codes, v_sz, positions, k_new, v_new, rope_cos,
                                              rope_sin, max_seq_len, block_table, rope_style, q_rot_out, out, scale,
-                                             split_tokens, workspace, stream)
+                                             split_tokens, workspace, stream, fmt)
     if workspace is None:
         workspace = _WORKSPACES.get((q.device.index if q.device.index is not None else torch.cuda.current_device(),
                                      args[-1]))
@@ -712,7 +741,7 @@ def prepare_decode_step_u8(q: torch.Tensor, k_codes: torch.Tensor, k_sz: torch.T
 
 
 def _step_u8_call(q, k_codes, k_sz, v_codes, v_sz, positions, k_new, v_new, rope_cos, rope_sin, max_seq_len,
-                  block_table, rope_style, q_rot_out, out, scale, split_tokens, workspace, stream):
+                  block_table, rope_style, q_rot_out, out, scale, split_tokens, workspace, stream, fmt=None):
     lib = _lib.load()
     B, H_q, d = q.shape
     H_kv = k_new.shape[1]
@@ -732,7 +761,7 @@ def _step_u8_call(q, k_codes, k_sz, v_codes, v_sz, positions, k_new, v_new, rope
         lead = (B, H_kv, T_max)
         pool_tokens = 0
     st = _stream(q.device, stream)
-    need = workspace_bytes(torch.uint8, B, H_q, H_kv, d, max_seq_len, split_tokens, pool_tokens=pool_tokens)
+    need = workspace_bytes(_q8_dtype(fmt), B, H_q, H_kv, d, max_seq_len, split_tokens, pool_tokens=pool_tokens)
     if workspace is not None:
         ws, wsn = _dev(workspace, "workspace", torch.uint8), workspace.numel()
     else:
@@ -746,7 +775,36 @@ def _step_u8_call(q, k_codes, k_sz, v_codes, v_sz, positions, k_new, v_new, rope
             _dev(rope_cos, "rope_cos", torch.float32), _dev(rope_sin, "rope_sin", torch.float32, rope_cos.shape),
             rope_cos.shape[0], ROPE_STYLES[rope_style], int(max_seq_len), float(scale) if scale else 0.0,
             _dev(out, "out", torch.bfloat16, (B, H_q, d)), int(split_tokens), ws, wsn, st)
+    if fmt is not None:
+        if fmt not in FP8_FORMATS:
+            raise ValueError(f"FP8 format must be one of {sorted(FP8_FORMATS)}, got {fmt!r}")
+        return lib.kvc_decode_step_fp8, (FP8_FORMATS[fmt],) + args, out, q_rot_out
     return lib.kvc_decode_step_u8, args, out, q_rot_out
+
+
+def append_fp8(*args, fmt: str = "e4m3", **kw) -> None:
+    """kvc_append_fp8: append_u8's arguments, FP8 codes of format fmt."""
+    return append_u8(*args, fmt=fmt, **kw)
+
+
+def decode_attn_fp8(*args, fmt: str = "e4m3", **kw) -> torch.Tensor:
+    """kvc_decode_attn_fp8: decode_attn_u8's arguments over FP8 codes of format fmt."""
+    return decode_attn_u8(*args, fmt=fmt, **kw)
+
+
+def decode_attn_paged_fp8(*args, fmt: str = "e4m3", **kw) -> torch.Tensor:
+    """kvc_decode_attn_paged_fp8: decode_attn_paged_u8's arguments over FP8 codes."""
+    return decode_attn_paged_u8(*args, fmt=fmt, **kw)
+
+
+def decode_step_fp8(*args, fmt: str = "e4m3", **kw):
+    """kvc_decode_step_fp8: decode_step_u8's arguments over FP8 codes of format fmt."""
+    return decode_step_u8(*args, fmt=fmt, **kw)
+
+
+def prepare_decode_step_fp8(*args, fmt: str = "e4m3", **kw) -> PreparedCall:
+    """prepare_decode_step_u8 for FP8 codes of format fmt."""
+    return prepare_decode_step_u8(*args, fmt=fmt, **kw)
 
 
 # ---------------------------------------------------------------------------

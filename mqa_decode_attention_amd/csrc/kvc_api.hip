@@ -17,6 +17,12 @@
 
 namespace {
 
+// The 8-bit caches: their dtype codes, and the code format of each.
+bool is_q8(kvc_dtype dt) { return dt == KVC_U8 || dt == KVC_FP8_E4M3 || dt == KVC_FP8_E5M2; }
+int q8_format(kvc_dtype dt) {
+    return dt == KVC_FP8_E4M3 ? kvc::kQ8E4M3 : (dt == KVC_FP8_E5M2 ? kvc::kQ8E5M2 : kvc::kQ8Affine);
+}
+
 thread_local char g_last_error[512] = "";
 thread_local hipEvent_t g_prof_start = nullptr;   // one-shot timing events (kvc_profile_next_decode)
 thread_local hipEvent_t g_prof_stop = nullptr;
@@ -102,7 +108,7 @@ bool plan_decode(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_l
         *why = "several new tokens per sequence need bf16 and head_dim 64, 128 or 256";
         return false;
     }
-    const bool u8 = dtype == KVC_U8;      // quantized cache: its own matrix-core kernel
+    const bool u8 = is_q8(dtype);         // 8-bit cache: its own matrix-core kernel
     if (u8 && !decode_u8_supported(d, G)) {
         *why = "the quantized-cache kernel needs head_dim 64 or 128 and H_q / H_kv <= 32";
         return false;
@@ -438,13 +444,15 @@ int kvc_window_span(int max_seq_len, int window, int ring, int T_max) {
     return max_seq_len;
 }
 
-kvc_status kvc_append_u8(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
-                         void* k_codes, float* k_sz, void* v_codes, float* v_sz, int T_max,
-                         const int32_t* block_table, int block_size, int max_blocks_per_seq,
-                         int num_blocks, const int32_t* positions,
-                         const void* k_new, const void* v_new, void* q_inout,
-                         const float* rope_cos, const float* rope_sin, int rope_rows,
-                         int rope_style, void* stream) {
+}  // extern "C"
+
+namespace {
+// The append into an 8-bit cache of format fmt (KVC_U8, KVC_FP8_E4M3, KVC_FP8_E5M2).
+kvc_status append_q8(kvc_dtype fmt, kvc_dtype dtype, int B, int H_q, int H_kv, int d, void* k_codes, float* k_sz,
+                     void* v_codes, float* v_sz, int T_max, const int32_t* block_table, int block_size,
+                     int max_blocks_per_seq, int num_blocks, const int32_t* positions, const void* k_new,
+                     const void* v_new, void* q_inout, const float* rope_cos, const float* rope_sin, int rope_rows,
+                     int rope_style, void* stream) {
     kvc_status st = check_heads(dtype, B, H_q, H_kv, d);
     if (st != KVC_OK) return st;
     if (d % 2 != 0 || d > 256) return fail(KVC_ERR_SHAPE, "head_dim %d must be even and at most 256", d);
@@ -453,9 +461,10 @@ kvc_status kvc_append_u8(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
     if (rope_rows <= 0) return fail(KVC_ERR_SHAPE, "rope_rows must be positive");
     if (B == 0) return ok();
     if (!k_codes || !k_sz || !v_codes || !v_sz || !positions || !k_new || !v_new || !rope_cos || !rope_sin)
-        return fail(KVC_ERR_NULL, "kvc_append_u8: a required pointer is NULL");
+        return fail(KVC_ERR_NULL, "8-bit cache append: a required pointer is NULL");
     kvc::AppendParams p{};
     p.dtype = dtype;
+    p.qfmt = q8_format(fmt);
     p.B = B; p.H_q = H_q; p.H_kv = H_kv; p.d = d;
     p.k_cache = k_codes; p.v_cache = v_codes; p.k_sz = k_sz; p.v_sz = v_sz; p.T_max = T_max;
     p.block_table = block_table;
@@ -474,14 +483,50 @@ kvc_status kvc_append_u8(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
     p.k_new = k_new; p.v_new = v_new; p.q_inout = q_inout;
     p.rope_cos = rope_cos; p.rope_sin = rope_sin; p.rope_rows = rope_rows;
     p.rope_style = rope_style;
-    return hip_status(kvc::launch_append_u8(p, static_cast<hipStream_t>(stream)), "kvc_append_u8 launch");
+    return hip_status(kvc::launch_append_u8(p, static_cast<hipStream_t>(stream)), "8-bit cache append launch");
+}
+
+kvc_status check_fp8(kvc_dtype format) {
+    if (format != KVC_FP8_E4M3 && format != KVC_FP8_E5M2)
+        return fail(KVC_ERR_UNSUPPORTED, "format %d is not an FP8 cache format (KVC_FP8_E4M3 or KVC_FP8_E5M2)",
+                    static_cast<int>(format));
+    return KVC_OK;
+}
+}  // namespace
+
+extern "C" {
+
+kvc_status kvc_append_u8(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
+                         void* k_codes, float* k_sz, void* v_codes, float* v_sz, int T_max,
+                         const int32_t* block_table, int block_size, int max_blocks_per_seq,
+                         int num_blocks, const int32_t* positions,
+                         const void* k_new, const void* v_new, void* q_inout,
+                         const float* rope_cos, const float* rope_sin, int rope_rows,
+                         int rope_style, void* stream) {
+    return append_q8(KVC_U8, dtype, B, H_q, H_kv, d, k_codes, k_sz, v_codes, v_sz, T_max, block_table, block_size,
+                     max_blocks_per_seq, num_blocks, positions, k_new, v_new, q_inout, rope_cos, rope_sin, rope_rows,
+                     rope_style, stream);
+}
+
+kvc_status kvc_append_fp8(kvc_dtype format, kvc_dtype dtype, int B, int H_q, int H_kv, int d,
+                          void* k_codes, float* k_sz, void* v_codes, float* v_sz, int T_max,
+                          const int32_t* block_table, int block_size, int max_blocks_per_seq,
+                          int num_blocks, const int32_t* positions,
+                          const void* k_new, const void* v_new, void* q_inout,
+                          const float* rope_cos, const float* rope_sin, int rope_rows,
+                          int rope_style, void* stream) {
+    const kvc_status f = check_fp8(format);
+    if (f != KVC_OK) return f;
+    return append_q8(format, dtype, B, H_q, H_kv, d, k_codes, k_sz, v_codes, v_sz, T_max, block_table, block_size,
+                     max_blocks_per_seq, num_blocks, positions, k_new, v_new, q_inout, rope_cos, rope_sin, rope_rows,
+                     rope_style, stream);
 }
 
 size_t kvc_workspace_zeroed_bytes(void) { return kvc::kWsCounterBytes; }
 
 size_t kvc_decode_workspace_bytes(kvc_dtype dtype, int B, int H_q, int H_kv, int d,
                                   int max_seq_len, long long pool_tokens, int split_tokens) {
-    if (check_heads(dtype == KVC_U8 ? KVC_BF16 : dtype, B, H_q, H_kv, d) != KVC_OK || max_seq_len < 0 || split_tokens < 0 ||
+    if (check_heads(is_q8(dtype) ? KVC_BF16 : dtype, B, H_q, H_kv, d) != KVC_OK || max_seq_len < 0 || split_tokens < 0 ||
         pool_tokens < 0) {
         fail(KVC_ERR_SHAPE, "invalid sizes for the decode workspace");
         return static_cast<size_t>(-1);
@@ -498,7 +543,7 @@ size_t kvc_decode_workspace_bytes(kvc_dtype dtype, int B, int H_q, int H_kv, int
 
 int kvc_decode_split_tokens(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_len,
                             long long pool_tokens, int split_tokens) {
-    if (check_heads(dtype == KVC_U8 ? KVC_BF16 : dtype, B, H_q, H_kv, d) != KVC_OK || max_seq_len < 0 || split_tokens < 0 ||
+    if (check_heads(is_q8(dtype) ? KVC_BF16 : dtype, B, H_q, H_kv, d) != KVC_OK || max_seq_len < 0 || split_tokens < 0 ||
         pool_tokens < 0)
         return -1;
     kvc::DecodePlan pl;
@@ -512,7 +557,7 @@ int kvc_decode_split_tokens(kvc_dtype dtype, int B, int H_q, int H_kv, int d, in
 
 int kvc_decode_merge_launch(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_len,
                             long long pool_tokens, int split_tokens) {
-    if (check_heads(dtype == KVC_U8 ? KVC_BF16 : dtype, B, H_q, H_kv, d) != KVC_OK || max_seq_len < 0 || split_tokens < 0 ||
+    if (check_heads(is_q8(dtype) ? KVC_BF16 : dtype, B, H_q, H_kv, d) != KVC_OK || max_seq_len < 0 || split_tokens < 0 ||
         pool_tokens < 0)
         return -1;
     kvc::DecodePlan pl;
@@ -526,7 +571,7 @@ int kvc_decode_merge_launch(kvc_dtype dtype, int B, int H_q, int H_kv, int d, in
 
 int kvc_decode_balanced(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_len,
                         long long pool_tokens, int split_tokens) {
-    if (check_heads(dtype == KVC_U8 ? KVC_BF16 : dtype, B, H_q, H_kv, d) != KVC_OK || max_seq_len < 0 ||
+    if (check_heads(is_q8(dtype) ? KVC_BF16 : dtype, B, H_q, H_kv, d) != KVC_OK || max_seq_len < 0 ||
         split_tokens < 0 || pool_tokens < 0)
         return -1;
     kvc::DecodePlan pl;
@@ -540,7 +585,7 @@ int kvc_decode_balanced(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int ma
 
 int kvc_decode_compact(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_len,
                        long long pool_tokens, int split_tokens) {
-    if (check_heads(dtype == KVC_U8 ? KVC_BF16 : dtype, B, H_q, H_kv, d) != KVC_OK || max_seq_len < 0 ||
+    if (check_heads(is_q8(dtype) ? KVC_BF16 : dtype, B, H_q, H_kv, d) != KVC_OK || max_seq_len < 0 ||
         split_tokens < 0 || pool_tokens < 0)
         return -1;
     kvc::DecodePlan pl;
@@ -617,7 +662,7 @@ kvc_status decode_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const
     qlen = multi ? qlen : 1;
     const hipEvent_t ev0 = g_prof_start, ev1 = g_prof_stop;   // one-shot, cleared by every call
     g_prof_start = g_prof_stop = nullptr;
-    const bool u8 = dtype == KVC_U8;
+    const bool u8 = is_q8(dtype);
     kvc_status st = check_heads(u8 ? KVC_BF16 : dtype, B, H_q, H_kv, d);
     if (st != KVC_OK) return st;
     if (u8 && B > 0 && (!k_sz || !v_sz)) return fail(KVC_ERR_NULL, "quantized decode: k_sz or v_sz is NULL");
@@ -764,7 +809,8 @@ kvc_status decode_common(kvc_dtype dtype, int B, int H_q, int H_kv, int d, const
         }
     }
     if (u8)
-        e = kvc::launch_decode_u8(d, p.G, paged, fused, p, const_cast<float*>(k_sz), const_cast<float*>(v_sz), hs, tm);
+        e = kvc::launch_decode_u8(d, p.G, paged, fused, q8_format(dtype), p, const_cast<float*>(k_sz),
+                                  const_cast<float*>(v_sz), hs, tm);
     else e = pl.mfma ? kvc::launch_decode_mfma(d, qlen > 1 ? pl.heads_per_wg : p.G, paged, fused, multi, p, hs, tm)
                      : kvc::launch_decode_split(dtype, d, pl.heads_per_wg, paged, p, hs, tm);
     if (e != hipSuccess) return hip_status(e, "decode split launch");
@@ -980,6 +1026,54 @@ kvc_status kvc_decode_step_u8(int B, int H_q, int H_kv, int d, const void* q, vo
                              workspace_bytes, stream, &st, k_sz, v_sz);
     }
     return decode_common(KVC_U8, B, H_q, H_kv, d, q, k_codes, v_codes, T_max, 0, 0, nullptr, 0, nullptr,
+                         max_seq_len, scale, out, split_tokens, workspace, workspace_bytes, stream, &st, k_sz, v_sz);
+}
+
+kvc_status kvc_decode_attn_fp8(kvc_dtype format, int B, int H_q, int H_kv, int d, const void* q,
+                               const void* k_codes, const float* k_sz, const void* v_codes, const float* v_sz,
+                               int T_max, const int32_t* seq_lens, int max_seq_len, float scale, void* out,
+                               int split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+    const kvc_status f = check_fp8(format);
+    if (f != KVC_OK) return f;
+    return decode_common(format, B, H_q, H_kv, d, q, k_codes, v_codes, T_max, 0, 0, nullptr, 0, seq_lens,
+                         max_seq_len, scale, out, split_tokens, workspace, workspace_bytes, stream, nullptr,
+                         k_sz, v_sz);
+}
+
+kvc_status kvc_decode_attn_paged_fp8(kvc_dtype format, int B, int H_q, int H_kv, int d, const void* q,
+                                     const void* k_codes, const float* k_sz, const void* v_codes,
+                                     const float* v_sz, int num_blocks, int block_size, const int32_t* block_table,
+                                     int max_blocks_per_seq, const int32_t* seq_lens, int max_seq_len, float scale,
+                                     void* out, int split_tokens, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+    const kvc_status f = check_fp8(format);
+    if (f != KVC_OK) return f;
+    if (!block_table) return fail(KVC_ERR_NULL, "kvc_decode_attn_paged_fp8: block_table is NULL");
+    if (block_size % 16 != 0)
+        return fail(KVC_ERR_UNSUPPORTED, "the 8-bit paged kernel needs block_size a multiple of 16");
+    return decode_common(format, B, H_q, H_kv, d, q, k_codes, v_codes, 0, num_blocks, block_size, block_table,
+                         max_blocks_per_seq, seq_lens, max_seq_len, scale, out, split_tokens, workspace,
+                         workspace_bytes, stream, nullptr, k_sz, v_sz);
+}
+
+kvc_status kvc_decode_step_fp8(kvc_dtype format, int B, int H_q, int H_kv, int d, const void* q, void* q_rot_out,
+                               void* k_codes, float* k_sz, void* v_codes, float* v_sz, int T_max,
+                               const int32_t* block_table, int block_size, int max_blocks_per_seq, int num_blocks,
+                               const int32_t* positions, const void* k_new, const void* v_new,
+                               const float* rope_cos, const float* rope_sin, int rope_rows, int rope_style,
+                               int max_seq_len, float scale, void* out, int split_tokens, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    const kvc_status f = check_fp8(format);
+    if (f != KVC_OK) return f;
+    StepArgs st{positions, k_new, v_new, q_rot_out, rope_cos, rope_sin, rope_rows, rope_style};
+    if (block_table) {
+        if (block_size % 16 != 0)
+            return fail(KVC_ERR_UNSUPPORTED, "the 8-bit paged kernel needs block_size a multiple of 16");
+        return decode_common(format, B, H_q, H_kv, d, q, k_codes, v_codes, 0, num_blocks, block_size, block_table,
+                             max_blocks_per_seq, nullptr, max_seq_len, scale, out, split_tokens, workspace,
+                             workspace_bytes, stream, &st, k_sz, v_sz);
+    }
+    return decode_common(format, B, H_q, H_kv, d, q, k_codes, v_codes, T_max, 0, 0, nullptr, 0, nullptr,
                          max_seq_len, scale, out, split_tokens, workspace, workspace_bytes, stream, &st, k_sz, v_sz);
 }
 

@@ -134,7 +134,15 @@ __global__ void __launch_bounds__(256) append_kernel(const AppendParams p) {
 // code = x / step + zero point rounded and clamped to [0, 255]; float32, one
 // rounding per operation.  One wave per vector: the H_kv keys, the H_kv
 // values, then (q_inout given) the H_q queries, rotated in place as above.
-template <typename T>
+//
+// FP8 cache (FMT kQ8E4M3 / kQ8E5M2: the one-byte FP8 caches of "Arsitektur
+// Inferensi LLM", tveniu.com, sections 2 and 8, and of the vLLM commands of
+// "KV Cache 최적화 심층 분석", youngju.dev): E4M3 codes of x / scale with the
+// float32 scale = (largest magnitude over the vector) / 448 (taken as 1 when
+// it is 0), so that the largest element lands on +-448; E5M2 codes of x
+// itself (scale 1).  Round to nearest even, saturating (fp8_encode); the pair
+// stored is (scale, 0).
+template <typename T, int FMT>
 __global__ void __launch_bounds__(256) append_u8_kernel(const AppendParams p) {
     const int lane = threadIdx.x & 63;
     const int nvec = 2 * p.H_kv + (p.q_inout ? p.H_q : 0);
@@ -205,33 +213,58 @@ __global__ void __launch_bounds__(256) append_u8_kernel(const AppendParams p) {
         return;
     }
 
-    float mn = INFINITY, mx = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        if (!has[k]) continue;
-        mn = fminf(mn, fminf(x[2 * k], x[2 * k + 1]));
-        mx = fmaxf(mx, fmaxf(x[2 * k], x[2 * k + 1]));
-    }
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        mn = fminf(mn, __shfl_xor(mn, off, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-    }
-    float step = (mx - mn) / 255.0f;
-    step = step == 0.0f ? 1.0f : step;
-    const float zp = fminf(fmaxf(rintf(-mn / step), 0.0f), 255.0f);
-
     const size_t row = row0 + static_cast<size_t>(j) * head_rows;
     uint8_t* codes = static_cast<uint8_t*>(is_key ? p.k_cache : p.v_cache) + row * p.d;
+    float first, second;                  // the vector's pair
+    if constexpr (FMT == kQ8Affine) {
+        float mn = INFINITY, mx = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        if (!has[k >> 1]) continue;
-        codes[el[k]] = static_cast<uint8_t>(fminf(fmaxf(rintf(x[k] / step + zp), 0.0f), 255.0f));
+        for (int k = 0; k < 2; ++k) {
+            if (!has[k]) continue;
+            mn = fminf(mn, fminf(x[2 * k], x[2 * k + 1]));
+            mx = fmaxf(mx, fmaxf(x[2 * k], x[2 * k + 1]));
+        }
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            mn = fminf(mn, __shfl_xor(mn, off, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+        }
+        float step = (mx - mn) / 255.0f;
+        step = step == 0.0f ? 1.0f : step;
+        const float zp = fminf(fmaxf(rintf(-mn / step), 0.0f), 255.0f);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (!has[k >> 1]) continue;
+            codes[el[k]] = static_cast<uint8_t>(fminf(fmaxf(rintf(x[k] / step + zp), 0.0f), 255.0f));
+        }
+        first = step;
+        second = zp;
+    } else {
+        float scale = 1.0f;
+        if constexpr (FMT == kQ8E4M3) {
+            float amax = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                if (!has[k]) continue;
+                amax = fmaxf(amax, fmaxf(fabsf(x[2 * k]), fabsf(x[2 * k + 1])));
+            }
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+            scale = amax / 448.0f;
+            scale = scale == 0.0f ? 1.0f : scale;
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (!has[k >> 1]) continue;
+            codes[el[k]] = static_cast<uint8_t>(fp8_encode<FMT>(x[k] / scale));
+        }
+        first = scale;
+        second = 0.0f;
     }
     if (lane == 0) {
         float* sz = (is_key ? p.k_sz : p.v_sz) + row * 2;
-        sz[0] = step;
-        sz[1] = zp;
+        sz[0] = first;
+        sz[1] = second;
     }
 }
 
@@ -241,10 +274,23 @@ hipError_t launch_append_u8(const AppendParams& p, hipStream_t stream) {
     const int nvec = 2 * p.H_kv + (p.q_inout ? p.H_q : 0);
     const long long blocks = (static_cast<long long>(p.B) * nvec + 3) / 4;
     if (blocks <= 0) return hipSuccess;
-    if (p.dtype == KVC_BF16)
-        hipLaunchKernelGGL(append_u8_kernel<uint16_t>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, p);
-    else
-        hipLaunchKernelGGL(append_u8_kernel<float>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, p);
+    const dim3 grid(static_cast<unsigned>(blocks)), block(256);
+    const bool b16 = p.dtype == KVC_BF16;
+    switch (p.qfmt) {
+        case kQ8Affine:
+            if (b16) hipLaunchKernelGGL((append_u8_kernel<uint16_t, kQ8Affine>), grid, block, 0, stream, p);
+            else hipLaunchKernelGGL((append_u8_kernel<float, kQ8Affine>), grid, block, 0, stream, p);
+            break;
+        case kQ8E4M3:
+            if (b16) hipLaunchKernelGGL((append_u8_kernel<uint16_t, kQ8E4M3>), grid, block, 0, stream, p);
+            else hipLaunchKernelGGL((append_u8_kernel<float, kQ8E4M3>), grid, block, 0, stream, p);
+            break;
+        case kQ8E5M2:
+            if (b16) hipLaunchKernelGGL((append_u8_kernel<uint16_t, kQ8E5M2>), grid, block, 0, stream, p);
+            else hipLaunchKernelGGL((append_u8_kernel<float, kQ8E5M2>), grid, block, 0, stream, p);
+            break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

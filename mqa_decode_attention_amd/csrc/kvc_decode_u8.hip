@@ -1,5 +1,12 @@
-// kvc_decode_u8.hip - decode attention over a uint8 quantized KV cache on the
-// gfx950 matrix cores.
+// kvc_decode_u8.hip - decode attention over an 8-bit KV cache (uint8 codes on
+// an affine grid, or FP8 E4M3 / E5M2 codes with a scale) on the gfx950 matrix
+// cores.
+//
+// FP8 caches (FMT kQ8E4M3 / kQ8E5M2; the one-byte FP8 caches of "Arsitektur
+// Inferensi LLM", tveniu.com, sections 2 and 8): each vector's codes with a
+// (scale, 0) pair, reading back as decode(code) * scale.  Every E4M3 or E5M2
+// value is exact in bf16, so they enter the products as the uint8 codes do,
+// and a zero point of 0 makes the corrections below vanish.
 //
 // Cache: each cached key or value vector is d uint8 codes c plus one float
 // (step, zero point) pair, and reads back as (c - zp) * step - the
@@ -52,24 +59,44 @@ using namespace mfma;
 constexpr int kNWq = 4;      // waves per workgroup
 constexpr int kTTq = 32;     // tokens per wave tile
 
-// Eight uint8 codes -> eight bf16 values (exact: integers below 256 need 8
-// significant bits): convert each byte to float32 (v_cvt_f32_ubyteN), keep
-// the upper halves.
+// Eight codes -> eight bf16 values, exact.  uint8 codes: integers below 256
+// need 8 significant bits; each byte converted to float32
+// (v_cvt_f32_ubyteN).  FP8 codes: at most 4 significant bits and exponents
+// well inside bf16's range; two codes per conversion (v_cvt_pk_f32_fp8 for
+// E4M3, v_cvt_pk_f32_bf8 for E5M2, reading the OCP formats on gfx950).  The
+// bf16 values are the float32 results' upper halves.
 __device__ __forceinline__ float byte_f32(uint32_t w, int k) { return static_cast<float>((w >> (8 * k)) & 0xFFu); }
+__device__ __forceinline__ uint32_t hi_halves(float hi, float lo) {
+    return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo), 0x07060302u);
+}
+template <int FMT>
 __device__ __forceinline__ uint4 codes8_to_bf16(uint2 c) {
     uint4 r;
-    const float f0 = byte_f32(c.x, 0), f1 = byte_f32(c.x, 1), f2 = byte_f32(c.x, 2), f3 = byte_f32(c.x, 3);
-    const float f4 = byte_f32(c.y, 0), f5 = byte_f32(c.y, 1), f6 = byte_f32(c.y, 2), f7 = byte_f32(c.y, 3);
-    r.x = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, f1), __builtin_bit_cast(uint32_t, f0), 0x07060302u);
-    r.y = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, f3), __builtin_bit_cast(uint32_t, f2), 0x07060302u);
-    r.z = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, f5), __builtin_bit_cast(uint32_t, f4), 0x07060302u);
-    r.w = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, f7), __builtin_bit_cast(uint32_t, f6), 0x07060302u);
+    if constexpr (FMT == kQ8Affine) {
+        const float f0 = byte_f32(c.x, 0), f1 = byte_f32(c.x, 1), f2 = byte_f32(c.x, 2), f3 = byte_f32(c.x, 3);
+        const float f4 = byte_f32(c.y, 0), f5 = byte_f32(c.y, 1), f6 = byte_f32(c.y, 2), f7 = byte_f32(c.y, 3);
+        r.x = hi_halves(f1, f0);
+        r.y = hi_halves(f3, f2);
+        r.z = hi_halves(f5, f4);
+        r.w = hi_halves(f7, f6);
+    } else {
+        // (the word select is an immediate)
+#define KVC_CVT_PK(w, upper) (FMT == kQ8E4M3 ? __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), upper) \
+                                             : __builtin_amdgcn_cvt_pk_f32_bf8(static_cast<int>(w), upper))
+        const auto a = KVC_CVT_PK(c.x, false), b = KVC_CVT_PK(c.x, true);
+        const auto e = KVC_CVT_PK(c.y, false), f = KVC_CVT_PK(c.y, true);
+#undef KVC_CVT_PK
+        r.x = hi_halves(a[1], a[0]);
+        r.y = hi_halves(b[1], b[0]);
+        r.z = hi_halves(e[1], e[0]);
+        r.w = hi_halves(f[1], f[0]);
+    }
     return r;
 }
 
 // (one 16-head block: registers held to two waves per SIMD, so that two
 // workgroups share a CU as planned)
-template <int D, int HB, int MODE, bool FUSED, bool BAL>
+template <int D, int HB, int MODE, bool FUSED, bool BAL, int FMT>
 __global__ void __launch_bounds__(kNWq * 64) __attribute__((amdgpu_waves_per_eu(HB == 1 ? 2 : 1, 8)))
 decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, float* k_sz, float* v_sz) {
     constexpr bool PAGED = MODE == 3;
@@ -372,8 +399,33 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
             }
         }
         // quantize one vector (the four lanes q4 = 0..3 of a row hold all of
-        // it): the affine grid of its min and max, codes rounded and clamped
+        // it): the affine grid of its min and max, codes rounded and clamped;
+        // FP8: the scale of its largest magnitude (E4M3) or 1 (E5M2), codes
+        // of x / scale rounded to nearest even and saturated, as the append
+        // kernel does
         auto quantize = [&](const float (&x)[KK][8], uint2 (&code)[KK], float2& pair) __attribute__((always_inline)) {
+            if constexpr (FMT != kQ8Affine) {
+                float scale = 1.0f;
+                if constexpr (FMT == kQ8E4M3) {
+                    float amax = 0.0f;
+#pragma unroll
+                    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[kk][e]));
+                    amax = max_same_head(amax);
+                    scale = amax / 448.0f;
+                    scale = scale == 0.0f ? 1.0f : scale;
+                }
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) {
+                    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) w[e / 4] |= fp8_encode<FMT>(x[kk][e] / scale) << (8 * (e % 4));
+                    code[kk] = make_uint2(w[0], w[1]);
+                }
+                pair = make_float2(scale, 0.0f);
+                return;
+            }
             float mn = x[0][0], mx = x[0][0];
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk)
@@ -526,7 +578,7 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) ka[kb][kk] = codes8_to_bf16(__builtin_bit_cast(uint2, kw[kb * KK + kk]));
+            for (int kk = 0; kk < KK; ++kk) ka[kb][kk] = codes8_to_bf16<FMT>(__builtin_bit_cast(uint2, kw[kb * KK + kk]));
 #pragma unroll
             for (int e = 0; e < 4; ++e) kp[kb][e] = __builtin_bit_cast(float2, pw2[4 * kb + e]);
         }
@@ -657,8 +709,8 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
             const int r = ci / CLPR;
             const int u = ci % CLPR;
             const uint4 c = __builtin_bit_cast(uint4, vcw4[m8]);
-            const uint4 lo = codes8_to_bf16(make_uint2(c.x, c.y));
-            const uint4 hi = codes8_to_bf16(make_uint2(c.z, c.w));
+            const uint4 lo = codes8_to_bf16<FMT>(make_uint2(c.x, c.y));
+            const uint4 hi = codes8_to_bf16<FMT>(make_uint2(c.z, c.w));
             // (d = 128: the eight lanes of one row write the low halves of
             // chunks 0-3 and the high halves of chunks 4-7 first, so every
             // 128-byte bank sweep gets eight distinct 16-byte slots per store)
@@ -877,28 +929,39 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
     }   // segments
 }
 
-template <int D, int HB, bool FUSED>
-hipError_t launch_dhf(bool paged, const DecodeParams& p, float* k_sz, float* v_sz, hipStream_t stream,
-                      const KernelTiming& tm) {
+template <int D, int HB, bool FUSED, int FMT>
+hipError_t launch_dhff(bool paged, const DecodeParams& p, float* k_sz, float* v_sz, hipStream_t stream,
+                       const KernelTiming& tm) {
     const dim3 grid(p.n_wg_pad), block(kNWq * 64);
     if (p.bal) {
         // balanced schedule: planned for paged pools of at most kBalMaxB sequences
         if (!paged || p.B > kBalMaxB) return hipErrorInvalidValue;
-        return launch_timed(decode_u8_kernel<D, HB, 3, FUSED, true>, grid, block, stream, tm, p, p.block_table, k_sz,
-                            v_sz);
+        return launch_timed(decode_u8_kernel<D, HB, 3, FUSED, true, FMT>, grid, block, stream, tm, p, p.block_table,
+                            k_sz, v_sz);
     }
     if (paged)
-        return launch_timed(decode_u8_kernel<D, HB, 3, FUSED, false>, grid, block, stream, tm, p, p.block_table, k_sz,
-                            v_sz);
-    return launch_timed(decode_u8_kernel<D, HB, 0, FUSED, false>, grid, block, stream, tm, p, p.block_table, k_sz,
-                        v_sz);
+        return launch_timed(decode_u8_kernel<D, HB, 3, FUSED, false, FMT>, grid, block, stream, tm, p, p.block_table,
+                            k_sz, v_sz);
+    return launch_timed(decode_u8_kernel<D, HB, 0, FUSED, false, FMT>, grid, block, stream, tm, p, p.block_table,
+                        k_sz, v_sz);
+}
+
+template <int D, int HB, bool FUSED>
+hipError_t launch_dhf(bool paged, int qfmt, const DecodeParams& p, float* k_sz, float* v_sz, hipStream_t stream,
+                      const KernelTiming& tm) {
+    switch (qfmt) {
+        case kQ8Affine: return launch_dhff<D, HB, FUSED, kQ8Affine>(paged, p, k_sz, v_sz, stream, tm);
+        case kQ8E4M3: return launch_dhff<D, HB, FUSED, kQ8E4M3>(paged, p, k_sz, v_sz, stream, tm);
+        case kQ8E5M2: return launch_dhff<D, HB, FUSED, kQ8E5M2>(paged, p, k_sz, v_sz, stream, tm);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 template <int D, int HB>
-hipError_t launch_dh(bool paged, bool fused, const DecodeParams& p, float* k_sz, float* v_sz, hipStream_t stream,
-                     const KernelTiming& tm) {
-    return fused ? launch_dhf<D, HB, true>(paged, p, k_sz, v_sz, stream, tm)
-                 : launch_dhf<D, HB, false>(paged, p, k_sz, v_sz, stream, tm);
+hipError_t launch_dh(bool paged, bool fused, int qfmt, const DecodeParams& p, float* k_sz, float* v_sz,
+                     hipStream_t stream, const KernelTiming& tm) {
+    return fused ? launch_dhf<D, HB, true>(paged, qfmt, p, k_sz, v_sz, stream, tm)
+                 : launch_dhf<D, HB, false>(paged, qfmt, p, k_sz, v_sz, stream, tm);
 }
 
 }  // namespace
@@ -916,16 +979,16 @@ int decode_u8_wgs_per_cu(int d, int G) {
     return G > 16 ? 1 : 2;
 }
 
-hipError_t launch_decode_u8(int d, int G, bool paged, bool fused, const DecodeParams& p, float* k_sz, float* v_sz,
-                            hipStream_t stream, const KernelTiming& tm) {
+hipError_t launch_decode_u8(int d, int G, bool paged, bool fused, int qfmt, const DecodeParams& p, float* k_sz,
+                            float* v_sz, hipStream_t stream, const KernelTiming& tm) {
     const bool two = G > 16;
     switch (d) {
         case 64:
-            return two ? launch_dh<64, 2>(paged, fused, p, k_sz, v_sz, stream, tm)
-                       : launch_dh<64, 1>(paged, fused, p, k_sz, v_sz, stream, tm);
+            return two ? launch_dh<64, 2>(paged, fused, qfmt, p, k_sz, v_sz, stream, tm)
+                       : launch_dh<64, 1>(paged, fused, qfmt, p, k_sz, v_sz, stream, tm);
         case 128:
-            return two ? launch_dh<128, 2>(paged, fused, p, k_sz, v_sz, stream, tm)
-                       : launch_dh<128, 1>(paged, fused, p, k_sz, v_sz, stream, tm);
+            return two ? launch_dh<128, 2>(paged, fused, qfmt, p, k_sz, v_sz, stream, tm)
+                       : launch_dh<128, 1>(paged, fused, qfmt, p, k_sz, v_sz, stream, tm);
         default: return hipErrorInvalidValue;
     }
 }

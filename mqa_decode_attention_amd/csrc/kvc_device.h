@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kvc_internal.h"
+
 namespace kvc {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -114,6 +116,42 @@ __device__ __forceinline__ float across_groups_max(float x) {
     if constexpr (W0 <= 16) x = fmaxf(x, __shfl_xor(x, 16, 64));
     if constexpr (W0 <= 32) x = fmaxf(x, __shfl_xor(x, 32, 64));
     return x;
+}
+
+// One float32 value as an 8-bit floating-point code, from the formats'
+// definitions (E4M3: exponent bias 7, 3 mantissa bits, largest finite 448;
+// E5M2: bias 15, 2 mantissa bits, largest finite 57344): round to nearest,
+// ties to even; results past the largest finite value saturate to it; the
+// sign of zero is kept.  (Finite inputs.)
+template <int FMT>
+__device__ __forceinline__ uint32_t fp8_encode(float x) {
+    constexpr int MB = FMT == kQ8E4M3 ? 3 : 2;
+    constexpr int BIAS = FMT == kQ8E4M3 ? 7 : 15;
+    constexpr uint32_t MAXC = FMT == kQ8E4M3 ? 0x7Eu : 0x7Bu;          // codes of 448 and 57344
+    constexpr float VMAX = FMT == kQ8E4M3 ? 448.0f : 57344.0f;
+    constexpr float MIN_NORMAL = FMT == kQ8E4M3 ? 0.015625f : 6.103515625e-05f;   // 2^-6, 2^-14
+    constexpr float SUB_SCALE = static_cast<float>(1 << (BIAS + MB - 1));         // 1 / subnormal step
+    const uint32_t bits = __float_as_uint(x);
+    const uint32_t sign = (bits >> 24) & 0x80u;
+    const float a = fabsf(x);
+    uint32_t mag;
+    if (a >= VMAX) {
+        mag = MAXC;
+    } else if (a < MIN_NORMAL) {
+        // multiples of the subnormal step (the scaling is exact); a count of
+        // 2^MB is the smallest normal's code
+        mag = static_cast<uint32_t>(rintf(a * SUB_SCALE));
+    } else {
+        const int e = static_cast<int>((bits >> 23) & 0xFFu) - 127;
+        uint32_t keep = (bits & 0x7FFFFFu) >> (23 - MB);
+        const uint32_t rest = bits & ((1u << (23 - MB)) - 1u);
+        const uint32_t halfway = 1u << (22 - MB);
+        if (rest > halfway || (rest == halfway && (keep & 1u))) ++keep;
+        // (a carry out of the mantissa moves the code to the next binade)
+        mag = (static_cast<uint32_t>(e + BIAS) << MB) + keep;
+        mag = mag > MAXC ? MAXC : mag;
+    }
+    return sign | mag;
 }
 
 // Workgroup id remap so that consecutive logical ids share one XCD.  The

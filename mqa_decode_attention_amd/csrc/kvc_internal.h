@@ -11,6 +11,12 @@
 
 namespace kvc {
 
+// Codes of the 8-bit caches (the cache's dtype: KVC_U8, KVC_FP8_E4M3,
+// KVC_FP8_E5M2).
+constexpr int kQ8Affine = 0;   // uint8 codes on an affine grid, (step, zero point) per vector
+constexpr int kQ8E4M3 = 1;     // OCP FP8 E4M3 codes, (scale, 0) per vector
+constexpr int kQ8E5M2 = 2;     // OCP FP8 E5M2 codes, (1, 0) per vector
+
 struct AppendParams {
     kvc_dtype dtype;
     int B, H_q, H_kv, d;
@@ -31,10 +37,13 @@ struct AppendParams {
     int rope_style;
     int ring;                    // contiguous ring of T_max slots: position p -> slot p % T_max
     int qlen;                    // new tokens per sequence (token i at position positions[b] + i; 0 means 1)
-    // uint8 quantized cache (launch_append_u8): k_cache / v_cache hold the
-    // codes [.., d] and these the float (step, zero point) pair of each vector
+    // 8-bit cache (launch_append_u8): k_cache / v_cache hold the codes
+    // [.., d] and these the float pair of each vector - (step, zero point) of
+    // the uint8 grid, or (scale, 0) of the FP8 formats (qfmt: kQ8Affine,
+    // kQ8E4M3, kQ8E5M2)
     float* k_sz;
     float* v_sz;
+    int qfmt;
 };
 
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
@@ -390,16 +399,17 @@ int decode_mfma_wgs_per_cu(int d, int G, bool paged);
 hipError_t launch_decode_mfma(int d, int rows, bool paged, bool fused, bool multi, const DecodeParams& p,
                               hipStream_t stream, const KernelTiming& tm);
 
-// The matrix-core streaming kernel over a uint8 quantized cache (bf16 q and
-// out; head_dim 64/128; G <= 32); k_sz / v_sz hold the (step, zero point)
-// pair of each cached vector.
+// The matrix-core streaming kernel over an 8-bit cache (bf16 q and out;
+// head_dim 64/128; G <= 32); k_sz / v_sz hold the pair of each cached vector:
+// (step, zero point) of uint8 codes, (scale, 0) of FP8 codes (qfmt:
+// kQ8Affine, kQ8E4M3, kQ8E5M2).
 bool decode_u8_supported(int d, int G);
 int decode_u8_step_tokens();
 int decode_u8_wgs_per_cu(int d, int G);
 // fused: the step's append runs inside (p.positions etc. set; the new token's
 // codes and pairs are written to the cache and k_sz / v_sz).
-hipError_t launch_decode_u8(int d, int G, bool paged, bool fused, const DecodeParams& p, float* k_sz, float* v_sz,
-                            hipStream_t stream, const KernelTiming& tm);
+hipError_t launch_decode_u8(int d, int G, bool paged, bool fused, int qfmt, const DecodeParams& p, float* k_sz,
+                            float* v_sz, hipStream_t stream, const KernelTiming& tm);
 
 // The log-sum-exp merge of the splits (only when n_splits > 1).
 hipError_t launch_decode_merge(kvc_dtype dtype, int d, const DecodeParams& p, hipStream_t stream);

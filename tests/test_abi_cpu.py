@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kvc_abi_version() == _lib.ABI_VERSION == 13
+    assert lib.kvc_abi_version() == _lib.ABI_VERSION == 14
     for s in range(6):
         assert lib.kvc_status_string(s)
     assert lib.kvc_status_string(99) == b"unknown status"
@@ -280,6 +280,58 @@ def test_quantized_cache_host_checks(lib):
     bad = list(aargs)
     bad[1] = 0
     assert app(*bad) == KVC_OK
+
+
+def test_fp8_cache_host_checks(lib):
+    """The FP8 entry points take the uint8 calls' arguments after a format,
+    which must be KVC_FP8_E4M3 or KVC_FP8_E5M2; the uint8 rules apply."""
+    E4M3, E5M2 = 3, 4
+    dec = lib.kvc_decode_attn_fp8
+    args = [E4M3, 2, 8, 2, 128, FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, 64, 0.0, FAKE, 0, None, 0, None]
+    for fmt in (BF16, U8, 0, 5, -1):
+        bad = list(args)
+        bad[0] = fmt
+        assert dec(*bad) == KVC_ERR_UNSUPPORTED                       # not an FP8 format
+    bad = list(args)
+    bad[7] = None
+    assert dec(*bad) == KVC_ERR_NULL                                  # no K pairs
+    bad = list(args)
+    bad[4] = 256
+    assert dec(*bad) == KVC_ERR_UNSUPPORTED                           # head_dim 256: no 8-bit kernel
+    for fmt in (E4M3, E5M2):
+        ok = list(args)
+        ok[0], ok[1] = fmt, 0
+        assert dec(*ok) == KVC_OK                                     # nothing to do
+    pg = lib.kvc_decode_attn_paged_fp8
+    pargs = [E5M2, 2, 8, 2, 128, FAKE, FAKE, FAKE, FAKE, FAKE, 100, 16, FAKE, 4, FAKE, 64, 0.0, FAKE, 0, None, 0,
+             None]
+    bad = list(pargs)
+    bad[11] = 8
+    assert pg(*bad) == KVC_ERR_UNSUPPORTED                            # block size 8
+    bad = list(pargs)
+    bad[0] = BF16
+    assert pg(*bad) == KVC_ERR_UNSUPPORTED
+    app = lib.kvc_append_fp8
+    aargs = [E4M3, BF16, 2, 8, 2, 128, FAKE, FAKE, FAKE, FAKE, 64, None, 0, 0, 0, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+             64, 0, None]
+    bad = list(aargs)
+    bad[0] = U8
+    assert app(*bad) == KVC_ERR_UNSUPPORTED
+    bad = list(aargs)
+    bad[7] = None
+    assert app(*bad) == KVC_ERR_NULL
+    step = lib.kvc_decode_step_fp8
+    sargs = [E4M3, 2, 8, 2, 128, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, None, 0, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE,
+             64, 0, 64, 0.0, FAKE, 0, None, 0, None]
+    bad = list(sargs)
+    bad[0] = 7
+    assert step(*bad) == KVC_ERR_UNSUPPORTED
+    # the same plan as the uint8 cache (the same kernel)
+    for fmt in (E4M3, E5M2):
+        assert lib.kvc_decode_split_tokens(fmt, 16, 32, 8, 128, 8193, 0, 0) == \
+            lib.kvc_decode_split_tokens(U8, 16, 32, 8, 128, 8193, 0, 0)
+        assert lib.kvc_decode_workspace_bytes(fmt, 64, 32, 1, 128, 4097, 0, 0) == \
+            lib.kvc_decode_workspace_bytes(U8, 64, 32, 1, 128, 4097, 0, 0)
 
 
 def test_quantized_cache_split_choice(lib):

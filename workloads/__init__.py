@@ -51,6 +51,11 @@ second generator seeded with seed + 7919, in the order K pairs -> V pairs ->
 K codes -> V codes, so the unquantized draws stay unchanged.  Slots at or past
 a sequence's cached length hold code 0 and NaN pairs.
 
+FP8 cache (``draw_fp8``): the same layout with one-byte E4M3 or E5M2 codes and
+float32 (scale, 0) pairs, codes drawn as torch's float8 casts of N(0, 1) /
+scale (the casts are torch's, as the bfloat16 casts above), scales uniform in
+[2.5, 3.5) / 448 for E4M3 and 1 for E5M2 (see ``draw_fp8``).
+
 Latent cache (``MLA_WORKLOADS``, ``draw_mla``): the cache layout of the
 MultiHeadLatentAttention listing in "KV Cache 최적화 심층 분석" (youngju.dev),
 one row [c_kv | k_rope] of d_latent + rope_dim values per token, [B, T_max,
@@ -71,8 +76,8 @@ from typing import Optional
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "DecodeInputs", "QuantCache", "draw", "draw_quantized", "rotation_table",
-           "MlaWorkload", "MLA_WORKLOADS", "MlaInputs", "draw_mla"]
+__all__ = ["Workload", "WORKLOADS", "DecodeInputs", "QuantCache", "draw", "draw_quantized", "draw_fp8",
+           "rotation_table", "MlaWorkload", "MLA_WORKLOADS", "MlaInputs", "draw_mla"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -274,6 +279,57 @@ def draw_quantized(x: DecodeInputs) -> QuantCache:
     for sz in (k_sz, v_sz):
         c = torch.randn(shape, generator=g, dtype=torch.float32) / sz[..., :1] + sz[..., 1:]
         codes.append(torch.round(c).clamp(0, 255).to(torch.uint8).contiguous())
+    k_codes, v_codes = codes
+    nan = float("nan")
+    lens = (x.cached + 1).tolist()
+    for b, c in enumerate(x.cached.tolist()):
+        if w.paged:
+            bs = w.block_size
+            for pos in range(c, -(-lens[b] // bs) * bs):
+                blk = int(x.block_table[b, pos // bs])
+                for t in (k_codes, v_codes):
+                    t[blk, :, pos % bs, :] = 0
+                for t in (k_sz, v_sz):
+                    t[blk, :, pos % bs, :] = nan
+        else:
+            for t in (k_codes, v_codes):
+                t[b, :, c:, :] = 0
+            for t in (k_sz, v_sz):
+                t[b, :, c:, :] = nan
+    return QuantCache(k_codes, k_sz, v_codes, v_sz)
+
+
+def draw_fp8(x: DecodeInputs, fmt: str) -> QuantCache:
+    """Draw an FP8 cache (fmt "e4m3" or "e5m2") in the layout of x: uint8 codes
+    and float32 (scale, 0) pairs per cached vector.
+
+    E4M3: scales uniform in [2.5, 3.5) / 448 (the largest magnitude of a few
+    hundred N(0, 1) values over the format's largest value) and codes torch's
+    float8_e4m3fn cast of N(0, 1) / scale, kept within +-448; E5M2: scale 1
+    and torch's float8_e5m2 cast of N(0, 1).  Either reads back as roughly
+    N(0, 1) values.  From a generator seeded with seed + 7919 + 1 (E4M3) or
+    + 2 (E5M2), in the order K scales -> V scales -> K codes -> V codes.  Slots
+    at or past a sequence's cached length hold code 0 and NaN pairs.
+    """
+    w = x.workload
+    g = torch.Generator().manual_seed(w.seed + 7919 + (1 if fmt == "e4m3" else 2))
+    shape = tuple(x.k_cache.shape)
+    lead = shape[:-1]
+    cast = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}[fmt]
+    pairs = []
+    for _ in range(2):
+        if fmt == "e4m3":
+            scale = (2.5 + torch.rand(lead, generator=g, dtype=torch.float32)) / 448.0
+        else:
+            scale = torch.ones(lead, dtype=torch.float32)
+        pairs.append(torch.stack([scale, torch.zeros(lead)], dim=-1).contiguous())
+    k_sz, v_sz = pairs
+    codes = []
+    for sz in (k_sz, v_sz):
+        c = torch.randn(shape, generator=g, dtype=torch.float32) / sz[..., :1]
+        if fmt == "e4m3":
+            c = c.clamp(-448.0, 448.0)
+        codes.append(c.to(cast).view(torch.uint8).contiguous())
     k_codes, v_codes = codes
     nan = float("nan")
     lens = (x.cached + 1).tolist()
