@@ -261,7 +261,13 @@ bool plan_decode(kvc_dtype dtype, int B, int H_q, int H_kv, int d, int max_seq_l
         const long long steps = units * ((L + tile - 1) / tile);      // >= the steps of any call
         if (ragged_pool && steps < (1LL << 31) - units) {
             const long long max_steps = kBalMaxTokens / tile;
-            const long long nwg = std::max(slots, (steps + max_steps - 1) / max_steps);
+            // (the bf16 kernel at head_dim 128 with one 16-head block: two
+            // workgroups per CU, 64 KiB of tiles in flight per CU - 187 us on
+            // the ragged paged workload, against 190 at the three the split
+            // plan counts and 220 at one)
+            const long long bal_slots =
+                (!u8 && d == 128 && G <= 16) ? static_cast<long long>(cu_count()) * 2 : slots;
+            const long long nwg = std::max(bal_slots, (steps + max_steps - 1) / max_steps);
             const size_t rows = static_cast<size_t>(nwg) * 2 * G;    // two partial slots per workgroup
             const size_t ml = kWsCounterBytes;
             const size_t part = align_up(ml + rows * sizeof(float2), 256);

@@ -458,9 +458,10 @@ def test_balanced_schedule_choice(lib):
     """The balanced schedule serves ragged paged pools (bf16 or uint8 cache,
     head_dim <= 128, the library's split choice, at most 512 sequences); its
     workspace: the 64 KiB of counters, then two partial rows per query head of
-    a group for each of its workgroups (one round: 768 for the bf16 paged
-    kernel's three per CU at one 16-head block, 256 at two; 512 for the
-    quantized kernel's two), or the split plan's size when that is larger."""
+    a group for each of its workgroups (one round: 512 for the bf16 paged
+    kernel at head_dim 128 with one 16-head block, two per CU; 768 at head_dim
+    64, three per CU; 256 for two 16-head blocks; 512 for the quantized
+    kernel's two), or the split plan's size when that is larger."""
     bal = lib.kvc_decode_balanced
     wsb = lib.kvc_decode_workspace_bytes
     zb = lib.kvc_workspace_zeroed_bytes()
@@ -479,9 +480,10 @@ def test_balanced_schedule_choice(lib):
     assert bal(BF16, 16, 30, 8, 128, 100, pool, 0) == -1
     # workspace: the larger of the two layouts
     n = wsb(BF16, 32, 32, 8, 128, 16385, pool, 0)
-    assert n >= zb + 768 * 2 * 4 * (8 + 128 * 4) and n % 256 == 0
+    assert n >= zb + 512 * 2 * 4 * (8 + 128 * 4) and n % 256 == 0
+    assert wsb(BF16, 3, 32, 8, 64, 200, 3 * 16 * 5, 0) == zb + 768 * 2 * 4 * (8 + 64 * 4)
     # groups of 32 heads: 256 workgroups (one per CU), 32 rows each
     assert wsb(BF16, 32, 64, 2, 128, 16385, 32 * 8700, 0) >= zb + 256 * 2 * 32 * (8 + 128 * 4)
     # a short call still needs its partial rows (units shared by workgroups)
-    assert wsb(BF16, 3, 32, 8, 128, 200, 3 * 16 * 5, 0) == zb + 768 * 2 * 4 * (8 + 128 * 4)
+    assert wsb(BF16, 3, 32, 8, 128, 200, 3 * 16 * 5, 0) == zb + 512 * 2 * 4 * (8 + 128 * 4)
     assert wsb(U8, 3, 32, 8, 128, 200, 3 * 16 * 5, 0) == zb + 512 * 2 * 4 * (8 + 128 * 4)

@@ -78,7 +78,7 @@ def test_group24_d64():
 
 
 def test_fewer_steps_than_workgroups():
-    """Three sequences shortened to 1, 0 and 2 tokens: 3 steps for 768
+    """Three sequences shortened to 1, 0 and 2 tokens: 3 steps for 512
     planned workgroups."""
     w = W.Workload("bal_tiny", 43, B=3, H_q=8, H_kv=1, d=128, dtype="bf16", cached_lo=0, cached_hi=300,
                    layout="paged", block_size=16)
