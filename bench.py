@@ -48,6 +48,7 @@ TRAFFIC = {
     ("native", "spec_gqa"): ("decode_spec_gqa_traffic.json",
                              ("kvc_decode_mfma.hip", "kvc_append.hip", "kvc_decode.hip") + _COMMON),
     ("native", "mla_latent"): ("decode_mla_latent_traffic.json", ("kvc_mla.hip",) + _COMMON),
+    ("fp8_e4m3", "gqa_8b"): ("decode_fp8_e4m3_gqa_8b_traffic.json", ("kvc_decode_u8.hip",) + _COMMON),
 }
 
 
