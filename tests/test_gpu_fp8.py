@@ -209,3 +209,57 @@ def test_step_fp8_full_size(name, fmt):
                            ("rotated q", q_rot, q2)):
         assert np.array_equal(bits(got), np.ascontiguousarray(ref).view(np.uint8)), f"{what} differ from the oracle"
     compare_out(out, oracle_decode(x, (kc2, ks2, vc2, vs2), q2, fmt), "bf16", f"step_fp8 {fmt} {name} full size")
+
+
+def _edge_vectors(fmt, d, rows):
+    """bf16 vectors whose float32 values sit on the encoder's edge cases: the
+    largest finite value first (an E4M3 vector's scale is then exactly 1, or
+    3 for the second row: every element a tie after the division), then every
+    midpoint between neighbouring values of the format (ties to even),
+    subnormal ones included, alternating in sign; E5M2 rows end with a value
+    past the largest finite one (saturation)."""
+    table = FO.fp8_table(fmt)
+    fin = np.sort(np.unique(np.abs(table[np.isfinite(table)])))
+    mids = (fin[1:] + fin[:-1]) / 2
+    vmax = fin[-1]
+    out = np.zeros((rows, d), np.float64)
+    for r in range(rows):
+        s = 3.0 if (fmt == "e4m3" and r % 2 == 1) else 1.0
+        v = np.concatenate([[vmax], np.roll(mids, 17 * r)])[:d]
+        v = np.concatenate([v, np.zeros(max(0, d - v.size))])
+        v[1::2] *= -1.0
+        if fmt == "e5m2":
+            v[-1] = 61440.0 * (-1.0 if r % 2 else 1.0)
+        out[r] = v * s
+    t = torch.from_numpy(out.astype(np.float32)).to(torch.bfloat16)
+    assert np.array_equal(t.double().numpy(), out), "edge values must be exact in bf16"
+    return t
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_encoder_ties_subnormals_saturation(fmt):
+    """The device encoder (append kernel and the fused step's own) on ties,
+    subnormals and saturation, bit for bit against the oracle: new tokens at
+    position 0, where the rotation is the identity."""
+    B, H_q, H_kv, d = 2, 8, 2, 128
+    w = W.WORKLOADS["gqa_8b"].replace(B=B, H_q=H_q, H_kv=H_kv, cached_lo=0, cached_hi=0, T_max=8)
+    x = W.draw(w)
+    x.k_new[:] = _edge_vectors(fmt, d, B * H_kv).reshape(B, H_kv, d)
+    x.v_new[:] = _edge_vectors(fmt, d, B * H_kv).flip(0).reshape(B, H_kv, d)
+    qc = W.draw_fp8(x, fmt)
+    kc2, ks2, vc2, vs2, q2 = oracle_append(x, qc, fmt)
+    # the append kernel
+    step = FStep(x, qc, fmt)
+    step.append()
+    torch.cuda.synchronize()
+    for what, got, ref in (("K codes", step.kc, kc2), ("K pairs", step.ks, ks2), ("V codes", step.vc, vc2),
+                           ("V pairs", step.vs, vs2)):
+        assert np.array_equal(bits(got), np.ascontiguousarray(ref).view(np.uint8)), f"append: {what} differ"
+    # the fused step's encoder
+    kc, ks, vc, vs, q_rot, out = _run_step(FStep(x, qc, fmt))
+    torch.cuda.synchronize()
+    for what, got, ref in (("K codes", kc, kc2), ("K pairs", ks, ks2), ("V codes", vc, vc2), ("V pairs", vs, vs2)):
+        assert np.array_equal(bits(got), np.ascontiguousarray(ref).view(np.uint8)), f"fused step: {what} differ"
+    # (sanity of the construction: ties and saturation were present)
+    table = FO.fp8_table(fmt)
+    assert np.any(np.abs(table[kc2[:, :, 0]]) == table[0x7E if fmt == "e4m3" else 0x7B])
