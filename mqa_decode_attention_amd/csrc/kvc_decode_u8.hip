@@ -27,11 +27,11 @@
 // tile the K codes, V codes and both pair rows go from HBM to LDS by direct
 // loads (buffer ranges ending at the split, so nothing past it is read); the K
 // operand is read from LDS as 8 codes per lane and converted to bf16; the V
-// tile is converted to a bf16 copy in LDS and read back transposed
-// (ds_read_b64_tr_b16) as the A operand V^T, exactly as for a bf16 cache.
-// Each stage is refilled as soon as the tile is done with it (K after its
-// operand reads, V after its conversion), after every LDS read of it has
-// completed.  MODE 0: contiguous codes [B, H_kv, T_max, d], pairs
+// operand V^T is read from the staged codes transposed (ds_read_b64_tr_b8:
+// each lane gets one column's codes of 8 token rows) and converted the same
+// way.  Each stage is refilled as soon as the tile is done with it (K after
+// its operand reads, V after its transposed reads), after every LDS read of it
+// has completed.  MODE 0: contiguous codes [B, H_kv, T_max, d], pairs
 // [B, H_kv, T_max, 2].  MODE 3: pools [N_blk, H_kv, bs, d] / [.., bs, 2] with
 // bs % 16 == 0; the split's slice of the block table is staged in LDS.
 //
@@ -94,6 +94,16 @@ __device__ __forceinline__ uint4 codes8_to_bf16(uint2 c) {
     return r;
 }
 
+// Slot of the 16-byte chunk u of staged V code row r (an XOR swizzle; also
+// the chunk held by slot u).  One transposed read of 16 lanes takes one chunk
+// of the 8 rows 4 q4 + 0..3 and 16 + 4 q4 + 0..3: the swizzle puts those 128
+// bytes in distinct banks.
+template <int D>
+__device__ __forceinline__ int vslot(int r, int u) {
+    if constexpr (D == 128) return u ^ ((r & 3) | (((r >> 4) & 1) << 2));
+    else return u ^ (((r >> 1) & 1) | (((r >> 4) & 1) << 1));
+}
+
 // (one 16-head block: registers held to two waves per SIMD, so that two
 // workgroups share a CU as planned)
 template <int D, int HB, int MODE, bool FUSED, bool BAL, int FMT>
@@ -110,24 +120,22 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
     constexpr int CROWS = 64 / CLPR;      // code rows per wave-wide 16-byte load
     constexpr int CLOADS = TT / CROWS;    // such loads per tile and tensor
     constexpr int CSTAGE = TT * CROW;     // LDS bytes of one code tile
-    constexpr int ROWB = 2 * D;           // bytes per row of the bf16 V copy
-    constexpr int STAGE = TT * ROWB;      // LDS bytes of the bf16 V copy
-    constexpr int LPR = D / 8;            // 16-byte chunks per bf16 row
     // pair rows: 32 tokens x 8 bytes, one load (contiguous) or one per 16-row
     // block (paged: the halves may lie in different blocks)
     constexpr int SZLOADS = PAGED ? 2 : 1;
     constexpr int SZROWS = TT / SZLOADS;  // rows per pair load
     static_assert(CROWS <= 16 && TT % CROWS == 0, "code rows per load");
 
-    __shared__ __attribute__((aligned(16))) char kc_lds[NW * CSTAGE];
-    __shared__ __attribute__((aligned(16))) char vc_lds[NW * CSTAGE];
-    __shared__ __attribute__((aligned(16))) char vb_lds[NW * STAGE];
+    // the K and V code stages (one array: the epilogue reuses it whole)
+    __shared__ __attribute__((aligned(16))) char code_lds[2 * NW * CSTAGE];
+    char* const kc_lds = code_lds;
+    char* const vc_lds = code_lds + NW * CSTAGE;
     __shared__ __attribute__((aligned(16))) char ksz_lds[NW * TT * 8];
     __shared__ __attribute__((aligned(16))) char vsz_lds[NW * TT * 8];
     __shared__ int tbl_lds[PAGED ? kTblMax : 1];
     __shared__ int s_last;                 // the in-kernel merge: this workgroup arrived last
     __shared__ std::conditional_t<BAL, BalLds, char> bal;   // the balanced schedule's lengths and prefix
-    static_assert(NW * STAGE >= 2 * NW * 16 * 4 && NW * CSTAGE >= 2 * NW * 16 * 4, "merge area");
+    static_assert(NW * TT * 8 >= 2 * NW * 16 * 4, "merge area");
     static_assert(!BAL || PAGED, "the balanced schedule serves paged pools");
     constexpr int kStep = NW * TT;        // tokens per loop step of the workgroup
 
@@ -227,7 +235,8 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
     // [16 l, 16 l + 16) of that load's 1 KiB, i.e. row CROWS*i + l / CLPR,
     // slot l % CLPR; K rows hold chunk (slot ^ (row % CLPR)) there (so the
     // 16 lanes reading one chunk of 16 rows for the operand spread over the
-    // banks), V rows are stored as they come.
+    // banks), V rows chunk vslot(row, slot) (the same for the transposed
+    // reads).
     // Block ids of the two 16-row groups of the tile at row base (paged):
     // read once per tile, unconditionally (index clamped into the slice;
     // groups past the split get a zero range whatever they read), and shared
@@ -257,7 +266,7 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
 #pragma unroll
         for (int i = 0; i < CLOADS; ++i) {
             const int r = CROWS * i + lane / CLPR;
-            const int u = ISK ? ((lane % CLPR) ^ (r % CLPR)) : (lane % CLPR);
+            const int u = ISK ? ((lane % CLPR) ^ (r % CLPR)) : vslot<D>(r, lane % CLPR);
             const int g0 = (CROWS * i / 16) * 16;                 // this load's 16-row group
             const __amdgpu_buffer_rsrc_t rs =
                 rows_rsrc(codes, CROW, base + (PAGED ? g0 : 0), PAGED ? 16 : TT, tb.g[g0 / 16]);
@@ -501,13 +510,10 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
     }
 
     const int s16 = lane & 15;
-    const int tr_row = 4 * q4 + s16 / 4;
-    auto swz = [](int r) { return (2 * r) & (LPR - 1); };
 
     auto compute_tile = [&](int base) __attribute__((always_inline)) {
         const char* kc = kc_lds + wave * CSTAGE;
         const char* vc = vc_lds + wave * CSTAGE;
-        char* vb = vb_lds + wave * STAGE;
         const char* ks = ksz_lds + wave * TT * 8;
         const char* vs = vsz_lds + wave * TT * 8;
         // block ids of the next tile (paged), before the waits below cover them
@@ -611,18 +617,24 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
                 char* vcw = vc_lds + wave * CSTAGE;
                 if (r16 == 0) {
 #pragma unroll
-                    for (int kk = 0; kk < KK; ++kk)
-                        *reinterpret_cast<uint2*>(vcw + dp * CROW + 32 * kk + 8 * q4) = vcode[kk];
+                    for (int kk = 0; kk < KK; ++kk) {
+                        const int c8 = 4 * kk + q4;
+                        *reinterpret_cast<uint2*>(vcw + dp * CROW + 16 * vslot<D>(dp, c8 / 2) + 8 * (c8 % 2)) =
+                            vcode[kk];
+                    }
                 }
                 if (lane == 0) *reinterpret_cast<float2*>(vsz_lds + wave * TT * 8 + 8 * dp) = vpair;
             }
         }
-        // the V pairs and this lane's V code pieces (inline assembly, as the
-        // K reads above; the wait above is the one they need)
-        constexpr int VCR = CSTAGE / 1024;    // 16-byte code pieces per lane
-        static_assert(4 * KB + VCR <= 16, "the wait below names every result");
+        // the V pairs and this lane's part of the V^T operand: for each
+        // 16-column block nb, the codes of column 16 nb + s16 in the 8 token
+        // rows whose weights this lane holds (4 q4 + 0..3, 16 + 4 q4 + 0..3),
+        // by one transposed read in which lanes 2i and 2i + 1 of each 16 name
+        // the two 8-byte halves of row i's chunk nb (inline assembly, as the K
+        // reads above; the wait above is the one they need)
+        static_assert(4 * KB + NB <= 16, "the wait below names every result");
         u32x2_t vpw[4 * KB];
-        u32x4_t vcw4[VCR];
+        u32x2_t vt[NB];
         {
             const unsigned vsb = static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_void_t*)vs));
             const unsigned vcb = static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_void_t*)vc));
@@ -633,26 +645,33 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
                     const unsigned a = vsb + 8 * (16 * kb + 4 * q4 + e);
                     asm volatile("ds_read_b64 %0, %1" : "=v"(vpw[4 * kb + e]) : "v"(a) : "memory");
                 }
+            const int ti = s16 >> 1;
+            const int tr = ti < 4 ? 4 * q4 + ti : 16 + 4 * q4 + (ti - 4);
 #pragma unroll
-            for (int m8 = 0; m8 < VCR; ++m8) {
-                const unsigned a = vcb + 16 * (64 * m8 + lane);
-                asm volatile("ds_read_b128 %0, %1" : "=v"(vcw4[m8]) : "v"(a) : "memory");
+            for (int nb = 0; nb < NB; ++nb) {
+                const unsigned a = vcb + tr * CROW + 16 * vslot<D>(tr, nb) + 8 * (s16 & 1);
+                asm volatile("ds_read_b64_tr_b8 %0, %1" : "=v"(vt[nb]) : "v"(a) : "memory");
             }
-            if constexpr (VCR == 4) {
+            if constexpr (NB == 8) {
                 asm volatile("s_waitcnt lgkmcnt(0)"
                              : "+v"(vpw[0]), "+v"(vpw[1]), "+v"(vpw[2]), "+v"(vpw[3]), "+v"(vpw[4]), "+v"(vpw[5]),
-                               "+v"(vpw[6]), "+v"(vpw[7]), "+v"(vcw4[0]), "+v"(vcw4[1]), "+v"(vcw4[2]), "+v"(vcw4[3])
+                               "+v"(vpw[6]), "+v"(vpw[7]), "+v"(vt[0]), "+v"(vt[1]), "+v"(vt[2]), "+v"(vt[3]),
+                               "+v"(vt[4]), "+v"(vt[5]), "+v"(vt[6]), "+v"(vt[7])
                              :
                              : "memory");
             } else {
-                static_assert(VCR == 2, "head_dim 64 or 128");
+                static_assert(NB == 4, "head_dim 64 or 128");
                 asm volatile("s_waitcnt lgkmcnt(0)"
                              : "+v"(vpw[0]), "+v"(vpw[1]), "+v"(vpw[2]), "+v"(vpw[3]), "+v"(vpw[4]), "+v"(vpw[5]),
-                               "+v"(vpw[6]), "+v"(vpw[7]), "+v"(vcw4[0]), "+v"(vcw4[1])
+                               "+v"(vpw[6]), "+v"(vpw[7]), "+v"(vt[0]), "+v"(vt[1]), "+v"(vt[2]), "+v"(vt[3])
                              :
                              : "memory");
             }
         }
+        // the V stage is free once those reads are done: the next tile's V
+        __builtin_amdgcn_s_waitcnt(kLgkmZero);
+        load_tensor(std::false_type{}, base + kStep, tb_next);
+
         float vstep[NS], vzp[NS];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -700,74 +719,11 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
             l[hb] += ps;
         }
 
-        // the V codes to a bf16 copy laid out as the bf16 kernel stages V rows
-        // (chunk u of row r at slot u ^ swz(r)): each lane converts 16-byte
-        // pieces of the code tile
-#pragma unroll
-        for (int m8 = 0; m8 < VCR; ++m8) {
-            const int ci = 64 * m8 + lane;
-            const int r = ci / CLPR;
-            const int u = ci % CLPR;
-            const uint4 c = __builtin_bit_cast(uint4, vcw4[m8]);
-            const uint4 lo = codes8_to_bf16<FMT>(make_uint2(c.x, c.y));
-            const uint4 hi = codes8_to_bf16<FMT>(make_uint2(c.z, c.w));
-            // (d = 128: the eight lanes of one row write the low halves of
-            // chunks 0-3 and the high halves of chunks 4-7 first, so every
-            // 128-byte bank sweep gets eight distinct 16-byte slots per store)
-            // (inline-assembly stores, for the reason given at the V^T reads
-            // below; those reads' wait also covers these stores)
-            const bool hi_first = D == 128 && u >= CLPR / 2;
-            const unsigned vbb = static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_void_t*)vb));
-            const unsigned s0 = vbb + r * ROWB + 16 * ((2 * u + (hi_first ? 1 : 0)) ^ swz(r));
-            const unsigned s1 = vbb + r * ROWB + 16 * ((2 * u + (hi_first ? 0 : 1)) ^ swz(r));
-            const u32x4_t w0 = __builtin_bit_cast(u32x4_t, select4(hi_first, hi, lo));
-            const u32x4_t w1 = __builtin_bit_cast(u32x4_t, select4(hi_first, lo, hi));
-            asm volatile("ds_write_b128 %0, %1" : : "v"(s0), "v"(w0) : "memory");
-            asm volatile("ds_write_b128 %0, %1" : : "v"(s1), "v"(w1) : "memory");
-        }
-        // the V stage is free once its reads are done: the next tile's V
-        __builtin_amdgcn_s_waitcnt(kLgkmZero);
-        load_tensor(std::false_type{}, base + kStep, tb_next);
-
-        // O^T += V^T P^T, V^T read transposed from the bf16 copy (two 16-row
-        // halves per column block, one 16x16x32 product).  The reads are
-        // written as inline assembly: issued through the builtin, they drew
-        // compiler waits for every direct-to-LDS load in flight (the next
-        // tiles' codes and pairs, which never touch the bf16 copy), so each
-        // tile's products waited for the next tile's data.  The "memory"
-        // clobbers keep the copy's stores above before the reads; the
-        // explicit wait, tied to every result, keeps the products after the
-        // data has arrived.
-        const unsigned vbw = static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_void_t*)(vb_lds + wave * STAGE)));
-        u32x2_t vt[2 * NB];
+        // O^T += V^T P^T: the transposed codes converted to bf16 (exact), one
+        // 16x16x32 product per column block and weight term
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            const int u = 2 * nb + (s16 % 4) / 2;
-            const int r0 = tr_row, r1 = tr_row + 16;
-            const unsigned a0 = vbw + r0 * ROWB + 16 * (u ^ swz(r0)) + 8 * (s16 & 1);
-            const unsigned a1 = vbw + r1 * ROWB + 16 * (u ^ swz(r1)) + 8 * (s16 & 1);
-            asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(vt[2 * nb]) : "v"(a0) : "memory");
-            asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(vt[2 * nb + 1]) : "v"(a1) : "memory");
-        }
-        static_assert(2 * NB <= 16, "the wait below names every result");
-        if constexpr (NB == 8) {
-            asm volatile("s_waitcnt lgkmcnt(0)"
-                         : "+v"(vt[0]), "+v"(vt[1]), "+v"(vt[2]), "+v"(vt[3]), "+v"(vt[4]), "+v"(vt[5]),
-                           "+v"(vt[6]), "+v"(vt[7]), "+v"(vt[8]), "+v"(vt[9]), "+v"(vt[10]), "+v"(vt[11]),
-                           "+v"(vt[12]), "+v"(vt[13]), "+v"(vt[14]), "+v"(vt[15])
-                         :
-                         : "memory");
-        } else {
-            static_assert(NB == 4, "head_dim 64 or 128");
-            asm volatile("s_waitcnt lgkmcnt(0)"
-                         : "+v"(vt[0]), "+v"(vt[1]), "+v"(vt[2]), "+v"(vt[3]), "+v"(vt[4]), "+v"(vt[5]),
-                           "+v"(vt[6]), "+v"(vt[7])
-                         :
-                         : "memory");
-        }
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            const uint4 va = make_uint4(vt[2 * nb].x, vt[2 * nb].y, vt[2 * nb + 1].x, vt[2 * nb + 1].y);
+            const uint4 va = codes8_to_bf16<FMT>(__builtin_bit_cast(uint2, vt[nb]));
 #pragma unroll
             for (int hb = 0; hb < HB; ++hb) {
                 o[hb][nb] = mfma16(va, make_uint4(ph[hb][0], ph[hb][1], ph[hb][2], ph[hb][3]), o[hb][nb]);
@@ -831,15 +787,15 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
 
     // O rows of the group's heads through LDS, RB rows per pass (chunks of row
     // r XOR-swizzled by 4r); one thread per 16-byte column chunk of a row
-    constexpr int RB = (NW * STAGE / (NW * 4 * D)) < 16 ? (NW * STAGE / (NW * 4 * D)) : 16;
+    constexpr int RB = (2 * CSTAGE / (4 * D)) < 16 ? (2 * CSTAGE / (4 * D)) : 16;
     constexpr int NCH = D / 4;
-    static_assert(RB >= 4, "merge area");
+    static_assert(RB >= 4 && NW * RB * D * 4 <= 2 * NW * CSTAGE, "merge area");
     auto chunk_at = [](int row, int ch) { return ch ^ ((4 * row) & (NCH - 1)); };
     // (the in-kernel merge's partials: offsets below 2^31, as planned)
     const __amdgpu_buffer_rsrc_t part_rs = make_uniform_rsrc(p.ws_part, 0x7FFFFFFF);
     const __amdgpu_buffer_rsrc_t ml_rs = make_uniform_rsrc(p.ws_ml, 0x7FFFFFFF);
-    float* sm_o = reinterpret_cast<float*>(vb_lds);               // [NW][RB][D]
-    float* sm_m = reinterpret_cast<float*>(kc_lds);               // [NW][16]
+    float* sm_o = reinterpret_cast<float*>(code_lds);             // [NW][RB][D]
+    float* sm_m = reinterpret_cast<float*>(ksz_lds);              // [NW][16]
     float* sm_l = sm_m + NW * 16;                                   // [NW][16]
     const int NT = NW * 64;
 #pragma unroll
@@ -971,10 +927,10 @@ bool decode_u8_supported(int d, int G) { return (d == 64 || d == 128) && G >= 1 
 int decode_u8_step_tokens() { return kNWq * kTTq; }
 
 int decode_u8_wgs_per_cu(int d, int G) {
-    // LDS per workgroup: code tiles 2 * 4 * 32 * d, the bf16 V copy 4 * 32 * 2d,
-    // pair rows 2 KiB (+ 4 KiB of table when paged): 66-70 KiB at d = 128, so
-    // two per CU; registers (about 180 per lane with one 16-head block, 280
-    // with two) allow two waves per SIMD, or one.
+    // LDS per workgroup: code tiles 2 * 4 * 32 * d, pair rows 2 KiB (+ 4 KiB
+    // of table when paged): 34-40 KiB at d = 128; registers (about 180 per
+    // lane with one 16-head block, 280 with two) allow two waves per SIMD, or
+    // one, so two workgroups per CU, or one.
     (void)d;
     return G > 16 ? 1 : 2;
 }

@@ -231,11 +231,10 @@ def test_u8_no_refill_while_lds_reads_pending(asm_u8):
 def test_u8_staged_reads_wait_for_their_loads(asm_u8):
     """Reads of staged codes and pairs (64/128-bit LDS reads) come after a wait
     that leaves at most one tensor's tile loads outstanding (codes d / 32 loads
-    plus 1 or 2 pair loads).  Excluded: the transposed reads, which read the
-    wave's own bf16 copy (written by its LDS stores), and 32-bit reads (table
-    entries and the merge's scalars)."""
+    plus 1 or 2 pair loads), the transposed reads of the V codes included.
+    Excluded: 32-bit reads (table entries and the merge's scalars)."""
     def staged_read(i):
-        return (i.startswith("ds_read") and "tr_b16" not in i and not re.match(r"ds_read2?(st64)?_b32", i)
+        return (i.startswith("ds_read") and not re.match(r"ds_read2?(st64)?_b32", i)
                 and not i.startswith("ds_read_u") and not i.startswith("ds_read_i"))
     seen = 0
     for name, d, mode, body in kernels_u8(asm_u8):
