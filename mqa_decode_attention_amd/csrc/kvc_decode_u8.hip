@@ -95,13 +95,15 @@ __device__ __forceinline__ uint4 codes8_to_bf16(uint2 c) {
 }
 
 // Slot of the 16-byte chunk u of staged V code row r (an XOR swizzle; also
-// the chunk held by slot u).  One transposed read of 16 lanes takes one chunk
-// of the 8 rows 4 q4 + 0..3 and 16 + 4 q4 + 0..3: the swizzle puts those 128
-// bytes in distinct banks.
+// the chunk held by slot u).  A 64-bit LDS read is served 32 lanes (256
+// bytes, one sweep of the banks) at a time; in a transposed read those lanes
+// take one chunk of the 16 rows 8 h + 0..7 and 16 + 8 h + 0..7 (h = 0, 1),
+// and the swizzle gives the rows that share banks distinct slots (d = 128:
+// rows of equal parity; d = 64: rows equal mod 4).
 template <int D>
 __device__ __forceinline__ int vslot(int r, int u) {
-    if constexpr (D == 128) return u ^ ((r & 3) | (((r >> 4) & 1) << 2));
-    else return u ^ (((r >> 1) & 1) | (((r >> 4) & 1) << 1));
+    if constexpr (D == 128) return u ^ (((r >> 1) & 3) | (((r >> 4) & 1) << 2));
+    else return u ^ (((r >> 2) & 1) | (((r >> 4) & 1) << 1));
 }
 
 // (one 16-head block: registers held to two waves per SIMD, so that two
@@ -233,10 +235,9 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
     // one tensor's tile at row base: codes (CLOADS loads) then pairs (SZLOADS)
     // into this wave's LDS slices.  Codes: lane l of load i fills bytes
     // [16 l, 16 l + 16) of that load's 1 KiB, i.e. row CROWS*i + l / CLPR,
-    // slot l % CLPR; K rows hold chunk (slot ^ (row % CLPR)) there (so the
-    // 16 lanes reading one chunk of 16 rows for the operand spread over the
-    // banks), V rows chunk vslot(row, slot) (the same for the transposed
-    // reads).
+    // slot l % CLPR; K rows hold chunk (slot ^ ((row / (256 / CROW)) % CLPR))
+    // there (the 32 lanes reading one chunk of 16 rows for the operand, 256
+    // bytes, then cover every bank once), V rows chunk vslot(row, slot).
     // Block ids of the two 16-row groups of the tile at row base (paged):
     // read once per tile, unconditionally (index clamped into the slice;
     // groups past the split get a zero range whatever they read), and shared
@@ -266,7 +267,7 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
 #pragma unroll
         for (int i = 0; i < CLOADS; ++i) {
             const int r = CROWS * i + lane / CLPR;
-            const int u = ISK ? ((lane % CLPR) ^ (r % CLPR)) : vslot<D>(r, lane % CLPR);
+            const int u = ISK ? ((lane % CLPR) ^ ((r / (256 / CROW)) % CLPR)) : vslot<D>(r, lane % CLPR);
             const int g0 = (CROWS * i / 16) * 16;                 // this load's 16-row group
             const __amdgpu_buffer_rsrc_t rs =
                 rows_rsrc(codes, CROW, base + (PAGED ? g0 : 0), PAGED ? 16 : TT, tb.g[g0 / 16]);
@@ -533,7 +534,7 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
 #pragma unroll
                     for (int kk = 0; kk < KK; ++kk) {
                         const int c8 = 4 * kk + q4;
-                        *reinterpret_cast<uint2*>(kcw + dp * CROW + 16 * ((c8 / 2) ^ (dp % CLPR)) + 8 * (c8 % 2)) =
+                        *reinterpret_cast<uint2*>(kcw + dp * CROW + 16 * ((c8 / 2) ^ ((dp / (256 / CROW)) % CLPR)) + 8 * (c8 % 2)) =
                             kcode[kk];
                     }
                 }
@@ -555,7 +556,7 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
                 const int c8 = 4 * kk + q4;                         // 8-byte piece of the row
-                const unsigned a = kcb + r * CROW + 16 * ((c8 / 2) ^ (r % CLPR)) + 8 * (c8 % 2);
+                const unsigned a = kcb + r * CROW + 16 * ((c8 / 2) ^ ((r / (256 / CROW)) % CLPR)) + 8 * (c8 % 2);
                 asm volatile("ds_read_b64 %0, %1" : "=v"(kw[kb * KK + kk]) : "v"(a) : "memory");
             }
 #pragma unroll
