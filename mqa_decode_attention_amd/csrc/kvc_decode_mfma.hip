@@ -859,15 +859,18 @@ decode_mfma_kernel(const DecodeParams p, const int32_t* __restrict__ block_table
     // [NW][RB1][D] floats of O fit in one stage buffer (RB1 = 8 for 16-row
     // tiles, 16 for 32-row tiles); with K staged too, rows RB1.. go to the K
     // buffer, so a whole 16-head block takes one pass (two barriers) at
-    // every tile height.  Rows are D floats apart, a multiple of the bank
-    // count: the 16-byte chunks of row r are XOR-swizzled by 4r, so the
-    // lanes writing one column block of several rows hit distinct banks.
+    // every tile height.  Rows are D floats apart, a multiple of the 256
+    // bytes one sweep of the banks serves: the 16-byte chunks of row r are
+    // XOR-swizzled by r mod 16, so the 16 lanes of one 128-bit store (one
+    // column chunk of 16 rows) fill a sweep without conflicts, and 16 threads
+    // reading consecutive chunks of one row do too.
     constexpr int RB1 = (STAGE / (4 * D)) < 16 ? (STAGE / (4 * D)) : 16;
     constexpr bool TWO = KLDS && RB1 < 16 && !MQ;   // (the multi-token kernel has no registers to spare)
     constexpr int RB = TWO ? 2 * RB1 : RB1;
     constexpr int NCH = D / 4;            // 16-byte chunks per row
     static_assert(NW * RB1 * D * 4 <= NW * STAGE && RB >= 4, "merge area");
-    auto chunk_at = [](int row, int ch) { return ch ^ ((4 * row) & (NCH - 1)); };
+    static_assert(NCH >= 16, "16 swizzle slots per row");
+    auto chunk_at = [](int row, int ch) { return ch ^ (row & 15); };
     auto o_row = [&](int w, int row) __attribute__((always_inline)) {
         char* region = (TWO && row >= RB1) ? kbuf : vbuf0;
         return reinterpret_cast<float*>(region) + (w * RB1 + (TWO && row >= RB1 ? row - RB1 : row)) * D;

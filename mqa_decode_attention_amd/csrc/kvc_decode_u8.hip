@@ -787,11 +787,14 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
     }
 
     // O rows of the group's heads through LDS, RB rows per pass (chunks of row
-    // r XOR-swizzled by 4r); one thread per 16-byte column chunk of a row
+    // r XOR-swizzled by r mod 16: the 16 lanes of one 128-bit store, one
+    // column chunk of 16 rows, fill one 256-byte sweep of the banks); one
+    // thread per 16-byte column chunk of a row
     constexpr int RB = (2 * CSTAGE / (4 * D)) < 16 ? (2 * CSTAGE / (4 * D)) : 16;
     constexpr int NCH = D / 4;
     static_assert(RB >= 4 && NW * RB * D * 4 <= 2 * NW * CSTAGE, "merge area");
-    auto chunk_at = [](int row, int ch) { return ch ^ ((4 * row) & (NCH - 1)); };
+    static_assert(NCH >= 16, "16 swizzle slots per row");
+    auto chunk_at = [](int row, int ch) { return ch ^ (row & 15); };
     // (the in-kernel merge's partials: offsets below 2^31, as planned)
     const __amdgpu_buffer_rsrc_t part_rs = make_uniform_rsrc(p.ws_part, 0x7FFFFFFF);
     const __amdgpu_buffer_rsrc_t ml_rs = make_uniform_rsrc(p.ws_ml, 0x7FFFFFFF);
