@@ -58,6 +58,7 @@ using namespace mfma;
 
 constexpr int kNWq = 4;      // waves per workgroup
 constexpr int kTTq = 32;     // tokens per wave tile
+constexpr int kGrpq = 4;     // contiguous caches: tiles whose pair rows come in one load
 
 // Eight codes -> eight bf16 values, exact.  uint8 codes: integers below 256
 // need 8 significant bits; each byte converted to float32
@@ -132,8 +133,13 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
     __shared__ __attribute__((aligned(16))) char code_lds[2 * NW * CSTAGE];
     char* const kc_lds = code_lds;
     char* const vc_lds = code_lds + NW * CSTAGE;
-    __shared__ __attribute__((aligned(16))) char ksz_lds[NW * TT * 8];
-    __shared__ __attribute__((aligned(16))) char vsz_lds[NW * TT * 8];
+    // pair rows per wave and tensor: paged, one tile's; contiguous (GP), two
+    // buffers of kGrp tiles' rows, a group's rows requested in one load
+    constexpr bool GP = !PAGED;
+    constexpr int kGrp = kGrpq;
+    constexpr int PBYTES = GP ? 2 * kGrp * TT * 8 : TT * 8;
+    __shared__ __attribute__((aligned(16))) char ksz_lds[NW * PBYTES];
+    __shared__ __attribute__((aligned(16))) char vsz_lds[NW * PBYTES];
     __shared__ int tbl_lds[PAGED ? kTblMax : 1];
     __shared__ int s_last;                 // the in-kernel merge: this workgroup arrived last
     __shared__ std::conditional_t<BAL, BalLds, char> bal;   // the balanced schedule's lengths and prefix
@@ -263,7 +269,7 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
         const uint8_t* codes = ISK ? kcodes : vcodes;
         const float* sz = ISK ? k_sz : v_sz;
         char* cbuf = (ISK ? kc_lds : vc_lds) + wave * CSTAGE;
-        char* sbuf = (ISK ? ksz_lds : vsz_lds) + wave * TT * 8;
+        char* sbuf = (ISK ? ksz_lds : vsz_lds) + wave * PBYTES;
 #pragma unroll
         for (int i = 0; i < CLOADS; ++i) {
             const int r = CROWS * i + lane / CLPR;
@@ -275,6 +281,7 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(cbuf + 1024 * i), 16,
                                                      row_in * CROW + 16 * u, 0, 0, kNT);
         }
+        if constexpr (GP) return;          // (pair rows by group: load_pair_group)
 #pragma unroll
         for (int i = 0; i < SZLOADS; ++i) {
             // SZROWS rows of 8 bytes are SZROWS / 2 lanes of 16 bytes; the other
@@ -287,6 +294,19 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
         }
     };
     constexpr int kTensorLoads = CLOADS + SZLOADS;
+    // (GP) the pair rows of the wave's kGrp tiles from row gbase on (strided
+    // by kStep) into group buffer gb: lanes 16 k .. 16 k + 15 take tile k's
+    // TT rows, 16 bytes each; the range ends at t_end as for every tile.
+    auto load_pair_group = [&](auto is_k, int gbase, int gb) __attribute__((always_inline)) {
+        constexpr bool ISK = decltype(is_k)::value;
+        static_assert(kGrp * TT * 8 == 64 * 16, "one 16-byte piece per lane");
+        const float* sz = ISK ? k_sz : v_sz;
+        char* sbuf = (ISK ? ksz_lds : vsz_lds) + wave * PBYTES + gb * kGrp * TT * 8;
+        const __amdgpu_buffer_rsrc_t rs = rows_rsrc(sz, 8, gbase, (kGrp - 1) * kStep + TT, 0);
+        const int k = lane / 16;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)sbuf, 16, (k * kStep + 2 * (lane % 16)) * 8, 0, 0,
+                                                 kNT);
+    };
 
 
     // Prologue: the table slice (paged), then the query, then the first tile.
@@ -356,6 +376,10 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
     }
     {
         const TileBlocks tb0 = tile_blocks(base);
+        if constexpr (GP) {
+            load_pair_group(std::true_type{}, base, 0);
+            load_pair_group(std::false_type{}, base, 0);
+        }
         load_tensor(std::true_type{}, base, tb0);
         load_tensor(std::false_type{}, base, tb0);
     }
@@ -512,17 +536,26 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
 
     const int s16 = lane & 15;
 
-    auto compute_tile = [&](int base) __attribute__((always_inline)) {
+    // One tile.  GP: phase = the tile's place in its group, gsel = the
+    // group's pair buffer.  A wave's loads go out in this order: the
+    // prologue's K and V pair groups 0, K codes 0, V codes 0; then in each
+    // tile the next tile's K codes after its K reads and V codes after its V
+    // reads, and at phase 0 after those the next K and V pair groups.  A
+    // tile's pair group is older than its codes, and waiting for its K or V
+    // codes leaves CLOADS later loads outstanding (at phase 1 it could leave
+    // CLOADS + 2: there it also waits for two loads of the previous tile).
+    // Paged: codes and pairs per tile, kTensorLoads per tensor.
+    auto compute_tile = [&](int base, int phase, int gsel) __attribute__((always_inline)) {
         const char* kc = kc_lds + wave * CSTAGE;
         const char* vc = vc_lds + wave * CSTAGE;
-        const char* ks = ksz_lds + wave * TT * 8;
-        const char* vs = vsz_lds + wave * TT * 8;
+        const int poff = GP ? wave * PBYTES + (gsel * kGrp + phase) * TT * 8 : wave * TT * 8;
+        char* ks = ksz_lds + poff;
+        char* vs = vsz_lds + poff;
         // block ids of the next tile (paged), before the waits below cover them
         const TileBlocks tb_next = tile_blocks(base + kStep);
 
-        // K codes and pairs were issued before this tile's V loads and nothing
-        // after them: at most kTensorLoads outstanding
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kTensorLoads));
+        constexpr int kWait = GP ? CLOADS : kTensorLoads;
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kWait));
         // fused step: the tile holding the new token gets its codes and pair
         // over what was loaded for that row (every read below comes after)
         const int dp = patch_row - base;
@@ -538,7 +571,7 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
                             kcode[kk];
                     }
                 }
-                if (lane == 0) *reinterpret_cast<float2*>(ksz_lds + wave * TT * 8 + 8 * dp) = kpair;
+                if (lane == 0) *reinterpret_cast<float2*>(ks + 8 * dp) = kpair;
             }
         }
         // The K operand's codes and the K pairs, read as inline assembly for
@@ -546,8 +579,11 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
         // drew a wait for every load in flight, this tile's V included); the
         // wait above is the one they need, and the one below, tied to every
         // result, keeps their uses after the data.
-        static_assert(KB == 2 && KB * KK + 4 * KB <= 16, "the wait below names every result");
-        u32x2_t kw[KB * KK], pw2[4 * KB];
+        // (a lane's four pair rows of a 16-row block are 32 contiguous bytes:
+        // two 128-bit reads)
+        static_assert(KB == 2 && KB * KK + 2 * KB <= 16, "the wait below names every result");
+        u32x2_t kw[KB * KK];
+        u32x4_t pw4[2 * KB];
         const unsigned kcb = static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_void_t*)kc));
         const unsigned ksb = static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_void_t*)ks));
 #pragma unroll
@@ -560,23 +596,22 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
                 asm volatile("ds_read_b64 %0, %1" : "=v"(kw[kb * KK + kk]) : "v"(a) : "memory");
             }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const unsigned a = ksb + 8 * (16 * kb + 4 * q4 + e);
-                asm volatile("ds_read_b64 %0, %1" : "=v"(pw2[4 * kb + e]) : "v"(a) : "memory");
+            for (int h = 0; h < 2; ++h) {
+                const unsigned a = ksb + 8 * (16 * kb + 4 * q4) + 16 * h;
+                asm volatile("ds_read_b128 %0, %1" : "=v"(pw4[2 * kb + h]) : "v"(a) : "memory");
             }
         }
         if constexpr (KK == 4) {
             asm volatile("s_waitcnt lgkmcnt(0)"
                          : "+v"(kw[0]), "+v"(kw[1]), "+v"(kw[2]), "+v"(kw[3]), "+v"(kw[4]), "+v"(kw[5]),
-                           "+v"(kw[6]), "+v"(kw[7]), "+v"(pw2[0]), "+v"(pw2[1]), "+v"(pw2[2]), "+v"(pw2[3]),
-                           "+v"(pw2[4]), "+v"(pw2[5]), "+v"(pw2[6]), "+v"(pw2[7])
+                           "+v"(kw[6]), "+v"(kw[7]), "+v"(pw4[0]), "+v"(pw4[1]), "+v"(pw4[2]), "+v"(pw4[3])
                          :
                          : "memory");
         } else {
             static_assert(KK == 2, "head_dim 64 or 128");
             asm volatile("s_waitcnt lgkmcnt(0)"
-                         : "+v"(kw[0]), "+v"(kw[1]), "+v"(kw[2]), "+v"(kw[3]), "+v"(pw2[0]), "+v"(pw2[1]),
-                           "+v"(pw2[2]), "+v"(pw2[3]), "+v"(pw2[4]), "+v"(pw2[5]), "+v"(pw2[6]), "+v"(pw2[7])
+                         : "+v"(kw[0]), "+v"(kw[1]), "+v"(kw[2]), "+v"(kw[3]), "+v"(pw4[0]), "+v"(pw4[1]),
+                           "+v"(pw4[2]), "+v"(pw4[3])
                          :
                          : "memory");
         }
@@ -587,7 +622,11 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) ka[kb][kk] = codes8_to_bf16<FMT>(__builtin_bit_cast(uint2, kw[kb * KK + kk]));
 #pragma unroll
-            for (int e = 0; e < 4; ++e) kp[kb][e] = __builtin_bit_cast(float2, pw2[4 * kb + e]);
+            for (int h = 0; h < 2; ++h) {
+                const uint4 w = __builtin_bit_cast(uint4, pw4[2 * kb + h]);
+                kp[kb][2 * h] = make_float2(__builtin_bit_cast(float, w.x), __builtin_bit_cast(float, w.y));
+                kp[kb][2 * h + 1] = make_float2(__builtin_bit_cast(float, w.z), __builtin_bit_cast(float, w.w));
+            }
         }
         // the K stage is free once those reads are done: the next tile's K
         __builtin_amdgcn_s_waitcnt(kLgkmZero);
@@ -611,8 +650,9 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
                 }
             }
 
-        // V codes and pairs: issued before the K loads just above
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kTensorLoads));
+        // this tile's V codes (and paged, pairs): issued before the K loads
+        // just above
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kWait));
         if constexpr (FUSED) {
             if (patch) {
                 char* vcw = vc_lds + wave * CSTAGE;
@@ -624,7 +664,7 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
                             vcode[kk];
                     }
                 }
-                if (lane == 0) *reinterpret_cast<float2*>(vsz_lds + wave * TT * 8 + 8 * dp) = vpair;
+                if (lane == 0) *reinterpret_cast<float2*>(vs + 8 * dp) = vpair;
             }
         }
         // the V pairs and this lane's part of the V^T operand: for each
@@ -633,8 +673,8 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
         // by one transposed read in which lanes 2i and 2i + 1 of each 16 name
         // the two 8-byte halves of row i's chunk nb (inline assembly, as the K
         // reads above; the wait above is the one they need)
-        static_assert(4 * KB + NB <= 16, "the wait below names every result");
-        u32x2_t vpw[4 * KB];
+        static_assert(2 * KB + NB <= 16, "the wait below names every result");
+        u32x4_t vpw[2 * KB];
         u32x2_t vt[NB];
         {
             const unsigned vsb = static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_void_t*)vs));
@@ -642,9 +682,9 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const unsigned a = vsb + 8 * (16 * kb + 4 * q4 + e);
-                    asm volatile("ds_read_b64 %0, %1" : "=v"(vpw[4 * kb + e]) : "v"(a) : "memory");
+                for (int h = 0; h < 2; ++h) {
+                    const unsigned a = vsb + 8 * (16 * kb + 4 * q4) + 16 * h;
+                    asm volatile("ds_read_b128 %0, %1" : "=v"(vpw[2 * kb + h]) : "v"(a) : "memory");
                 }
             const int ti = s16 >> 1;
             const int tr = ti < 4 ? 4 * q4 + ti : 16 + 4 * q4 + (ti - 4);
@@ -655,16 +695,15 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
             }
             if constexpr (NB == 8) {
                 asm volatile("s_waitcnt lgkmcnt(0)"
-                             : "+v"(vpw[0]), "+v"(vpw[1]), "+v"(vpw[2]), "+v"(vpw[3]), "+v"(vpw[4]), "+v"(vpw[5]),
-                               "+v"(vpw[6]), "+v"(vpw[7]), "+v"(vt[0]), "+v"(vt[1]), "+v"(vt[2]), "+v"(vt[3]),
-                               "+v"(vt[4]), "+v"(vt[5]), "+v"(vt[6]), "+v"(vt[7])
+                             : "+v"(vpw[0]), "+v"(vpw[1]), "+v"(vpw[2]), "+v"(vpw[3]), "+v"(vt[0]), "+v"(vt[1]),
+                               "+v"(vt[2]), "+v"(vt[3]), "+v"(vt[4]), "+v"(vt[5]), "+v"(vt[6]), "+v"(vt[7])
                              :
                              : "memory");
             } else {
                 static_assert(NB == 4, "head_dim 64 or 128");
                 asm volatile("s_waitcnt lgkmcnt(0)"
-                             : "+v"(vpw[0]), "+v"(vpw[1]), "+v"(vpw[2]), "+v"(vpw[3]), "+v"(vpw[4]), "+v"(vpw[5]),
-                               "+v"(vpw[6]), "+v"(vpw[7]), "+v"(vt[0]), "+v"(vt[1]), "+v"(vt[2]), "+v"(vt[3])
+                             : "+v"(vpw[0]), "+v"(vpw[1]), "+v"(vpw[2]), "+v"(vpw[3]), "+v"(vt[0]), "+v"(vt[1]),
+                               "+v"(vt[2]), "+v"(vt[3])
                              :
                              : "memory");
             }
@@ -672,15 +711,21 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
         // the V stage is free once those reads are done: the next tile's V
         __builtin_amdgcn_s_waitcnt(kLgkmZero);
         load_tensor(std::false_type{}, base + kStep, tb_next);
+        if constexpr (GP) {
+            if (phase == 0) {
+                load_pair_group(std::true_type{}, base + kGrp * kStep, gsel ^ 1);
+                load_pair_group(std::false_type{}, base + kGrp * kStep, gsel ^ 1);
+            }
+        }
 
         float vstep[NS], vzp[NS];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float2 sz = __builtin_bit_cast(float2, vpw[4 * kb + e]);
-                vstep[4 * kb + e] = sz.x;
-                vzp[4 * kb + e] = sz.y;
+                const uint4 w = __builtin_bit_cast(uint4, vpw[2 * kb + e / 2]);
+                vstep[4 * kb + e] = __builtin_bit_cast(float, e % 2 ? w.z : w.x);
+                vzp[4 * kb + e] = __builtin_bit_cast(float, e % 2 ? w.w : w.y);
             }
 
         // online softmax per head (lazy reference max, as in the bf16 kernel);
@@ -736,8 +781,8 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
     // Tiles past the split are loaded anyway (zero range: no memory access), so
     // every path has the same loads in flight and the waits stay exact.
     if (base < t_end) {
-        for (;;) {
-            compute_tile(base);
+        for (int tile = 0;; ++tile) {
+            compute_tile(base, tile % kGrp, (tile / kGrp) & 1);
             base += kStep;
             if (base >= t_end) break;
         }
