@@ -540,26 +540,34 @@ __global__ void __launch_bounds__(DL / 4) mla_merge_kernel(const MlaParams p) {
 
 // ---------------------------------------------------------------------------
 // Value up-projection, out[b, h, i] = W_uv[h d_k + i, :] . x[b, h, :] +
-// b_uv[h d_k + i].  One single-wave workgroup per (head, 16 rows of d_k),
+// b_uv[h d_k + i].  One workgroup of four waves per (head, 16 rows of d_k),
 // 16 sequences per product:
 //   out^T[i, b] = sum_l W_uv[h d_k + i, l] x[b, h, l]   A = W_uv rows (16 i x 32 l),
 //                                                       B = x^T (32 l x 16 b), hi + lo
-// so each row of W_uv is read once per step; the reduction runs in two
-// independent accumulator chains.
+// Wave w takes the latent columns of a quarter of the 32-wide steps, so each
+// wave has a quarter of the loads in flight; the four partial products are
+// added through LDS in wave order (deterministic).  Each row of W_uv is read
+// once per step.
 // ---------------------------------------------------------------------------
 template <int DL>
-__global__ void __launch_bounds__(64) mla_up_kernel(const MlaParams p) {
+__global__ void __launch_bounds__(256) mla_up_kernel(const MlaParams p) {
     constexpr int KK = DL / 32;
+    constexpr int KW = KK / 4;            // 32-wide steps per wave
+    static_assert(KW >= 1 && KK % 4 == 0, "d_latent a multiple of 128");
+    __shared__ f32x4_t part[3][64];       // waves 1..3's partial products
     const int nib = p.d_k / 16;
     const int h = blockIdx.x / nib;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
     const int r16 = lane & 15, q4 = lane >> 4;
     const int i0 = 16 * (blockIdx.x - h * nib);
     if (h >= p.H) return;
-    const uint16_t* wrow = static_cast<const uint16_t*>(p.w_uv) + (static_cast<size_t>(h) * p.d_k + i0 + r16) * DL + 8 * q4;
-    uint4 wa[KK];
+    const int k0 = wave * KW;             // this wave's first 32-wide step
+    const uint16_t* wrow =
+        static_cast<const uint16_t*>(p.w_uv) + (static_cast<size_t>(h) * p.d_k + i0 + r16) * DL + 8 * q4 + 32 * k0;
+    uint4 wa[KW];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) wa[kk] = *reinterpret_cast<const uint4*>(wrow + 32 * kk);
+    for (int kk = 0; kk < KW; ++kk) wa[kk] = *reinterpret_cast<const uint4*>(wrow + 32 * kk);
     // the bias, read unconditionally (from W_uv when there is none, then
     // replaced by 0) so that no branch separates the loads from each other
     const uint16_t* bv = static_cast<const uint16_t*>(p.b_uv);
@@ -570,37 +578,42 @@ __global__ void __launch_bounds__(64) mla_up_kernel(const MlaParams p) {
     for (int b0 = 0; b0 < p.B; b0 += 16) {
         const int bq = b0 + r16;
         const bool bok = bq < p.B;
-        const float* xr = p.ctx + (static_cast<size_t>(bok ? bq : 0) * p.H + h) * DL + 8 * q4;
-        // all of the block's x rows requested at once, then its length
-        float4 xa[KK], xc[KK];
+        const float* xr = p.ctx + (static_cast<size_t>(bok ? bq : 0) * p.H + h) * DL + 8 * q4 + 32 * k0;
+        // all of the block's x pieces requested at once, then its length
+        float4 xa[KW], xc[KW];
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
+        for (int kk = 0; kk < KW; ++kk) {
             xa[kk] = *reinterpret_cast<const float4*>(xr + 32 * kk);
             xc[kk] = *reinterpret_cast<const float4*>(xr + 32 * kk + 4);
         }
         const bool empty = !bok || mla_len_lane(p, bok ? bq : b0) == 0;   // length 0: zeros
-        f32x4_t acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+        f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
+        for (int kk = 0; kk < KW; ++kk) {
             float4 a = xa[kk], c = xc[kk];
             if (!bok) a = c = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             uint4 xh, xl;
             split8(a, c, xh, xl);
-            acc[kk & 1] = mfma16(wa[kk], xh, acc[kk & 1]);
-            acc[kk & 1] = mfma16(wa[kk], xl, acc[kk & 1]);
+            acc = mfma16(wa[kk], xh, acc);
+            acc = mfma16(wa[kk], xl, acc);
         }
-        const f32x4_t r4 = acc[0] + acc[1];
-        float bias[4];
+        if (wave > 0) part[wave - 1][lane] = acc;
+        __syncthreads();
+        if (wave == 0) {
+            const f32x4_t r4 = ((acc + part[0][lane]) + part[1][lane]) + part[2][lane];
+            float bias[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) bias[e] = bv ? bf16_bits_to_f32(braw[e]) : 0.0f;
-        if (bok) {
-            float4 r;
-            r.x = empty ? 0.0f : r4[0] + bias[0];
-            r.y = empty ? 0.0f : r4[1] + bias[1];
-            r.z = empty ? 0.0f : r4[2] + bias[2];
-            r.w = empty ? 0.0f : r4[3] + bias[3];
-            *reinterpret_cast<float4*>(p.out + (static_cast<size_t>(bq) * p.H + h) * p.d_k + i0 + 4 * q4) = r;
+            for (int e = 0; e < 4; ++e) bias[e] = bv ? bf16_bits_to_f32(braw[e]) : 0.0f;
+            if (bok) {
+                float4 r;
+                r.x = empty ? 0.0f : r4[0] + bias[0];
+                r.y = empty ? 0.0f : r4[1] + bias[1];
+                r.z = empty ? 0.0f : r4[2] + bias[2];
+                r.w = empty ? 0.0f : r4[3] + bias[3];
+                *reinterpret_cast<float4*>(p.out + (static_cast<size_t>(bq) * p.H + h) * p.d_k + i0 + 4 * q4) = r;
+            }
         }
+        __syncthreads();
     }
 }
 
@@ -640,7 +653,7 @@ hipError_t launch_dl(const MlaParams& p, hipStream_t stream, const KernelTiming&
     hipLaunchKernelGGL(mla_merge_kernel<DL>, dim3(p.B * p.H), dim3(DL / 4), 0, stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(mla_up_kernel<DL>, dim3(p.H * (p.d_k / 16)), dim3(64), 0, stream, p);
+    hipLaunchKernelGGL(mla_up_kernel<DL>, dim3(p.H * (p.d_k / 16)), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
