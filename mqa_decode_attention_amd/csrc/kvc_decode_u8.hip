@@ -24,8 +24,9 @@
 //
 // Structure (as the bf16 kernel's staged-tile path): one workgroup of four
 // waves per (sequence, KV head, split); each wave streams 32-token tiles.  Per
-// tile the K codes, V codes and both pair rows go from HBM to LDS by direct
-// loads (buffer ranges ending at the split, so nothing past it is read); the K
+// tile the K codes and V codes go from HBM to LDS by direct loads (buffer
+// ranges ending at the split, so nothing past it is read), the pair rows with
+// them (paged) or four tiles' at a time in one load (contiguous); the K
 // operand is read from LDS as 8 codes per lane and converted to bf16; the V
 // operand V^T is read from the staged codes transposed (ds_read_b64_tr_b8:
 // each lane gets one column's codes of 8 token rows) and converted the same
