@@ -645,11 +645,18 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
                 for (int kk = 0; kk < KK; ++kk) acc = mfma16(ka[kb][kk], qb[hb][kk], acc);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int t = base + 16 * kb + 4 * q4 + e;
                     const float2 sz = kp[kb][e];
-                    s[hb][4 * kb + e] = t < t_end ? (acc[e] - sz.y * qsum[hb]) * (sz.x * p.scale_log2) : -INFINITY;
+                    s[hb][4 * kb + e] = (acc[e] - sz.y * qsum[hb]) * (sz.x * p.scale_log2);
                 }
             }
+        // (only a tile that reaches past the split has rows to mask)
+        if (base + TT > t_end) {
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+                for (int i = 0; i < NS; ++i)
+                    if (base + 16 * (i / 4) + 4 * q4 + i % 4 >= t_end) s[hb][i] = -INFINITY;
+        }
 
         // this tile's V codes (and paged, pairs): issued before the K loads
         // just above
