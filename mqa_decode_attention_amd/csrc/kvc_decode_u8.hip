@@ -521,10 +521,16 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
     }
 
     // sum over d of each query head (the zero-point term of the scores): this
-    // lane's 8*KK elements, then the four lanes of the head
+    // lane's 8*KK elements, then the four lanes of the head.  FP8 caches read
+    // back as decode(code) * scale: no zero-point terms at all (ZP false).
+    constexpr bool ZP = FMT == kQ8Affine;
     float qsum[HB];
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
+        if constexpr (!ZP) {
+            qsum[hb] = 0.0f;
+            continue;
+        }
         float acc = 0.0f;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
@@ -646,7 +652,8 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float2 sz = kp[kb][e];
-                    s[hb][4 * kb + e] = (acc[e] - sz.y * qsum[hb]) * (sz.x * p.scale_log2);
+                    s[hb][4 * kb + e] = ZP ? (acc[e] - sz.y * qsum[hb]) * (sz.x * p.scale_log2)
+                                           : acc[e] * (sz.x * p.scale_log2);
                 }
             }
         // (only a tile that reaches past the split has rows to mask)
@@ -767,8 +774,10 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
             for (int i = 0; i < NS / 2; ++i) {
                 ph[hb][i] = pack2_bf16(pw[2 * i], pw[2 * i + 1]);
                 pl[hb][i] = pack2_bf16(pw[2 * i] - bf16_lo(ph[hb][i]), pw[2 * i + 1] - bf16_hi(ph[hb][i]));
-                corr[hb] = fmaf(bf16_lo(ph[hb][i]) + bf16_lo(pl[hb][i]), vzp[2 * i], corr[hb]);
-                corr[hb] = fmaf(bf16_hi(ph[hb][i]) + bf16_hi(pl[hb][i]), vzp[2 * i + 1], corr[hb]);
+                if constexpr (ZP) {
+                    corr[hb] = fmaf(bf16_lo(ph[hb][i]) + bf16_lo(pl[hb][i]), vzp[2 * i], corr[hb]);
+                    corr[hb] = fmaf(bf16_hi(ph[hb][i]) + bf16_hi(pl[hb][i]), vzp[2 * i + 1], corr[hb]);
+                }
             }
             l[hb] += ps;
         }
@@ -801,9 +810,11 @@ decode_u8_kernel(const DecodeParams p, const int32_t* __restrict__ block_table, 
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
         l[hb] = sum_same_head(l[hb]);
-        const float c = sum_same_head(corr[hb]);
+        if constexpr (ZP) {
+            const float c = sum_same_head(corr[hb]);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) o[hb][nb] -= c;
+            for (int nb = 0; nb < NB; ++nb) o[hb][nb] -= c;
+        }
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
